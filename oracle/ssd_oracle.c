@@ -1,0 +1,267 @@
+/*
+ * ssd_oracle.c -- plain, slow, float64 CPU oracle for the selective state-space
+ * (SSD) scan.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark call it; the product library never links,
+ * loads or calls it, and it shares no code, header or table with the HIP path.
+ *
+ * It evaluates the recurrences exactly as defined, one time step after the
+ * other, in double precision.  No chunking, blocking or re-association: the
+ * chunked GPU algorithm is checked against this definition.
+ *
+ * Sources (page titles and sections):
+ *  - Mamba-3-Lite README, section on the classical Mamba-2 recurrence and its
+ *    complex promotion: h_t = exp(A dt) h_{t-1} + B x_t, y_t = C h_t, and the
+ *    complex form with A = A_re + i A_im, B, C complex.
+ *  - "Block Anatomy, Numerical Stability & Scaling", section 4.4 (the per-head
+ *    complex A used through exp(softplus(dt) * A)) and the Numerical Stability
+ *    doc, section 4 (softplus is ln(1 + e^x); per-step factor |a| <= 1 when
+ *    Re A <= 0).
+ *  - The real form used here is the usual Mamba-2 discretisation with the
+ *    step size on the input term as well, h_t = exp(A dt) h_{t-1} +
+ *    dt B_t x_t^T, y_t = C_t^T h_t + D x_t, A one scalar per head (the README
+ *    shorthand writes the input term as B x_t).
+ *
+ * Readings where the pages leave a step open (each is listed in the design doc):
+ *  - real form: the input term carries the step size (dt * B * x); the
+ *    complex form does not (B * x), as the complex recurrence on the README
+ *    page writes it;
+ *  - y_t reads the state after the update at step t (y_t = C h_t);
+ *  - complex readout: y = Re(sum_n C_n h_n) with no conjugation (the page's
+ *    real-GEMM expansion subtracts the imag*imag product);
+ *  - x is real in the complex form; there is no D skip in the complex form;
+ *  - dt processing: delta = clamp(softplus(dt + dt_bias), dt_min, dt_max);
+ *  - head h reads B/C group g = h / (H / G).
+ *
+ * Layouts (row-major, last index fastest):
+ *   x  (Bsz,T,H,P)  dt (Bsz,T,H)  B,C (Bsz,T,G,N)[,2]  y (Bsz,T,H,P)
+ *   h0, h_final (Bsz,H,P,N)[,2]   A (H) or (H,2)      D, dt_bias (H)
+ * x/B/C may be float32 (dtype 0) or bfloat16 bit patterns (dtype 1); they are
+ * widened exactly to double.  Outputs are double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int g_threads_used = 1;
+
+int ssd_oracle_threads_used(void) { return g_threads_used; }
+
+/* Set the OpenMP thread count for later calls (n <= 0 leaves it alone). */
+void ssd_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Read element i of an array of float32 (dtype 0) or bfloat16 (dtype 1).
+ * A bfloat16 value is the top half of a float32 bit pattern, so the
+ * widening is exact. */
+static double load_in(const void *p, size_t i, int dtype)
+{
+    if (dtype == 0)
+        return (double)((const float *)p)[i];
+    uint32_t bits = ((uint32_t)((const uint16_t *)p)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* softplus(z) = ln(1 + e^z), evaluated without overflow as
+ * max(z,0) + ln(1 + e^{-|z|}). */
+double ssd_oracle_softplus(double z)
+{
+    double m = z > 0.0 ? z : 0.0;
+    return m + log1p(exp(-fabs(z)));
+}
+
+/* Step size for one (token, head): softplus of the biased raw value, then
+ * the clamp [dt_min, dt_max]. */
+double ssd_oracle_delta(double dt_raw, double bias, double dt_min, double dt_max)
+{
+    double d = ssd_oracle_softplus(dt_raw + bias);
+    if (d < dt_min) d = dt_min;
+    if (d > dt_max) d = dt_max;
+    return d;
+}
+
+static void record_threads(void)
+{
+#ifdef _OPENMP
+    g_threads_used = omp_get_num_threads();
+#else
+    g_threads_used = 1;
+#endif
+}
+
+/*
+ * Real Mamba-2 recurrence, sequential over t, for every (b, h):
+ *   delta = clamp(softplus(dt + dt_bias))
+ *   S[p][n] <- exp(A_h * delta) * S[p][n] + delta * x[p] * B[n]
+ *   y[p]     = sum_n C[n] * S[p][n] + D_h * x[p]
+ * S starts at h0 (zeros when h0 is NULL).  state is caller-owned scratch of
+ * Bsz*H*P*N doubles.  Returns 0, or 1 on invalid sizes.
+ */
+int ssd_oracle_fwd(const void *x, const float *dt, const float *A,
+                   const void *B, const void *C, const float *D,
+                   const float *dt_bias, double dt_min, double dt_max,
+                   const float *h0, double *y, double *h_final,
+                   int Bsz, int T, int H, int P, int G, int N, int dtype,
+                   double *state /* Bsz*H*P*N doubles, caller-owned */)
+{
+    if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G)
+        return 1;
+    const int hpg = H / G;
+    const long long BH = (long long)Bsz * H;
+#pragma omp parallel
+    {
+#pragma omp single
+        record_threads();
+#pragma omp for schedule(dynamic, 1)
+        for (long long bh = 0; bh < BH; ++bh) {
+            const int b = (int)(bh / H), h = (int)(bh % H), g = h / hpg;
+            double *S = state + (size_t)bh * P * N;
+            for (int i = 0; i < P * N; ++i)
+                S[i] = h0 ? (double)h0[(size_t)bh * P * N + i] : 0.0;
+            const double Ah = (double)A[h];
+            const double Dh = D ? (double)D[h] : 0.0;
+            const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+            for (int t = 0; t < T; ++t) {
+                const size_t tok = (size_t)b * T + t;
+                const double delta =
+                    ssd_oracle_delta((double)dt[tok * H + h], bias, dt_min, dt_max);
+                const double a = exp(Ah * delta);
+                const size_t xo = (tok * H + h) * (size_t)P;
+                const size_t bo = (tok * G + g) * (size_t)N;
+                for (int p = 0; p < P; ++p) {
+                    const double xp = load_in(x, xo + p, dtype);
+                    double acc = 0.0;
+                    for (int n = 0; n < N; ++n) {
+                        double *s = &S[(size_t)p * N + n];
+                        *s = a * (*s) + delta * xp * load_in(B, bo + n, dtype);
+                        acc += load_in(C, bo + n, dtype) * (*s);
+                    }
+                    y[xo + p] = acc + Dh * xp;
+                }
+            }
+            if (h_final)
+                memcpy(h_final + (size_t)bh * P * N, S, sizeof(double) * P * N);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Complex (Mamba-3-Lite) recurrence, sequential over t, for every (b, h):
+ *   delta = clamp(softplus(dt + dt_bias))
+ *   a     = exp((alpha_h + i beta_h) * delta)
+ *   S[p][n] <- a * S[p][n] + B[n] * x[p]          (complex, no delta factor)
+ *   y[p]     = Re( sum_n C[n] * S[p][n] )          (unconjugated C)
+ * x is real float32; A, B, C, h0, h_final are (re, im) float pairs.  The
+ * complex arithmetic is written out on (re, im) doubles.  state must hold
+ * Bsz*H*P*N*2 doubles.
+ */
+int ssd_oracle_complex_fwd(const float *x, const float *dt, const float *A,
+                           const float *B, const float *C,
+                           const float *dt_bias, double dt_min, double dt_max,
+                           const float *h0, double *y, double *h_final,
+                           int Bsz, int T, int H, int P, int G, int N,
+                           double *state)
+{
+    if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G)
+        return 1;
+    const int hpg = H / G;
+    const long long BH = (long long)Bsz * H;
+#pragma omp parallel
+    {
+#pragma omp single
+        record_threads();
+#pragma omp for schedule(dynamic, 1)
+        for (long long bh = 0; bh < BH; ++bh) {
+            const int b = (int)(bh / H), h = (int)(bh % H), g = h / hpg;
+            double *S = state + (size_t)bh * P * N * 2;
+            for (int i = 0; i < P * N * 2; ++i)
+                S[i] = h0 ? (double)h0[(size_t)bh * P * N * 2 + i] : 0.0;
+            const double al = (double)A[2 * h], be = (double)A[2 * h + 1];
+            const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+            for (int t = 0; t < T; ++t) {
+                const size_t tok = (size_t)b * T + t;
+                const double delta =
+                    ssd_oracle_delta((double)dt[tok * H + h], bias, dt_min, dt_max);
+                const double mag = exp(al * delta);
+                const double are = mag * cos(be * delta), aim = mag * sin(be * delta);
+                const size_t xo = (tok * H + h) * (size_t)P;
+                const size_t bo = (tok * G + g) * (size_t)N * 2;
+                for (int p = 0; p < P; ++p) {
+                    const double xp = (double)x[xo + p];
+                    double acc = 0.0;
+                    for (int n = 0; n < N; ++n) {
+                        double *s = &S[((size_t)p * N + n) * 2];
+                        const double br = B[bo + 2 * n], bi = B[bo + 2 * n + 1];
+                        const double sr = are * s[0] - aim * s[1] + br * xp;
+                        const double si = are * s[1] + aim * s[0] + bi * xp;
+                        s[0] = sr;
+                        s[1] = si;
+                        const double cr = C[bo + 2 * n], ci = C[bo + 2 * n + 1];
+                        acc += cr * sr - ci * si; /* Re(c * s) */
+                    }
+                    y[xo + p] = acc;
+                }
+            }
+            if (h_final)
+                memcpy(h_final + (size_t)bh * P * N * 2, S, sizeof(double) * P * N * 2);
+        }
+    }
+    return 0;
+}
+
+/*
+ * One real recurrent step (single-token decode) on a float64 state held by
+ * the caller, updated in place:
+ *   h[b,h,p,n] <- exp(A_h delta) h + delta x[b,h,p] B[b,g,n]
+ *   y[b,h,p]    = sum_n C[b,g,n] h[b,h,p,n] + D_h x[b,h,p]
+ * x (Bsz,H,P), dt (Bsz,H), B/C (Bsz,G,N) are float32.
+ */
+int ssd_oracle_step(double *hstate, const float *x, const float *dt, const float *A,
+                    const float *B, const float *C, const float *D,
+                    const float *dt_bias, double dt_min, double dt_max,
+                    double *y, int Bsz, int H, int P, int G, int N)
+{
+    if (Bsz <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G)
+        return 1;
+    const int hpg = H / G;
+    const long long BH = (long long)Bsz * H;
+#pragma omp parallel
+    {
+#pragma omp single
+        record_threads();
+#pragma omp for schedule(static)
+        for (long long bh = 0; bh < BH; ++bh) {
+            const int b = (int)(bh / H), h = (int)(bh % H), g = h / hpg;
+            const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+            const double delta = ssd_oracle_delta((double)dt[bh], bias, dt_min, dt_max);
+            const double a = exp((double)A[h] * delta);
+            const double Dh = D ? (double)D[h] : 0.0;
+            const float *Bv = B + ((size_t)b * G + g) * N;
+            const float *Cv = C + ((size_t)b * G + g) * N;
+            for (int p = 0; p < P; ++p) {
+                const double xp = (double)x[(size_t)bh * P + p];
+                double *s = hstate + ((size_t)bh * P + p) * N;
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    s[n] = a * s[n] + delta * xp * (double)Bv[n];
+                    acc += (double)Cv[n] * s[n];
+                }
+                y[(size_t)bh * P + p] = acc + Dh * xp;
+            }
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs for the SSD scan and the decode step.
+
+Shared by the tests, the smoke check and the benchmark, on both sides of every
+parity comparison.  This module holds none of the scan's arithmetic: only
+random draws, the float32 -> bfloat16 encoding of inputs, and the named
+workloads.  Each generator uses one ``numpy.random.default_rng(seed)`` stream
+and draws in a fixed order (x, dt, dt_bias, A, B, C, D, h0; decode: dt_bias,
+A, D, h0, then x, dt, B, C per step), so a seed fixes every bit.
+
+Large normal tensors are drawn directly in float32
+(``Generator.standard_normal(dtype=float32)``); bfloat16 inputs are the
+round-to-nearest-even encodings of those float32 values, so the oracle and the
+GPU read identical bits.
+
+Workloads (shapes of the BitMamba-1B Mamba-2 layer -- d_inner 4096, 64 heads,
+d_state 128 -- and of the Mamba-3-Lite layer -- 16 heads, head_dim 64, 64
+complex states):
+"""
+import math
+
+import numpy as np
+
+WORKLOADS = {
+    # small fp32 case the oracle finishes in well under a second
+    "tiny_f32": dict(kind="real", Bsz=1, T=256, H=2, P=16, N=16, G=1, chunk=64,
+                     dtype="f32"),
+    # BitMamba-1B layer shape, bf16 x/B/C, fp32 dt/A/state
+    "bitmamba_bf16": dict(kind="real", Bsz=2, T=2048, H=64, P=64, N=128, G=1,
+                          chunk=256, dtype="bf16"),
+    # Mamba-3-Lite layer shape, complex64 state, per-head B/C
+    "mamba3lite_complex": dict(kind="complex", Bsz=8, T=2048, H=16, P=64, N=64,
+                               G=16, chunk=256),
+    # long sequence at the BitMamba shape: 256 chunks of 256
+    "long_bf16": dict(kind="real", Bsz=1, T=65536, H=64, P=64, N=128, G=1,
+                      chunk=256, dtype="bf16"),
+    # single-token recurrent decode at the BitMamba shape, 64 steps in place
+    "decode_f32": dict(kind="decode", Bsz=256, H=64, P=64, N=128, G=1, steps=64),
+}
+
+DT_MIN = 1e-3
+DT_MAX = 1e-1
+
+
+def f32_to_bf16_bits(a):
+    """Round float32 values to bfloat16 (nearest, ties to even); returns the
+    16-bit patterns as uint16.  Inputs here are finite."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b):
+    """Widen bfloat16 bit patterns (uint16) to float32, exactly."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(rng, shape, std=1.0):
+    z = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        z *= np.float32(std)
+    return z
+
+
+def _dt_bias(rng, H, lo=DT_MIN, hi=DT_MAX):
+    # bias b with softplus(b) = u, u log-uniform in [lo, hi]:  b = log(expm1(u))
+    u = np.exp(rng.uniform(math.log(lo), math.log(hi), size=H))
+    return np.log(np.expm1(u)).astype(np.float32)
+
+
+def make_real(Bsz, T, H, P, N, G=1, dtype="f32", seed=0, with_h0=False,
+              with_D=True, with_bias=True, a_range=(1.0, 16.0), **_ignored):
+    """Inputs of the real Mamba-2 form.
+
+    x, B, C ~ N(0,1); dt_raw ~ N(0,1); dt_bias such that softplus(dt_bias) is
+    log-uniform in [1e-3, 1e-1]; A_h = -exp(U(log a0, log a1)); D_h ~ N(0,1);
+    clamp [1e-3, 1e-1]; optional h0 ~ N(0,1).  x/B/C are float32 or bfloat16
+    bit patterns (uint16) according to ``dtype``.
+    """
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (Bsz, T, H, P))
+    dt = _normal(rng, (Bsz, T, H))
+    dt_bias = _dt_bias(rng, H) if with_bias else None
+    A = (-np.exp(rng.uniform(math.log(a_range[0]), math.log(a_range[1]), size=H))
+         ).astype(np.float32)
+    B = _normal(rng, (Bsz, T, G, N))
+    C = _normal(rng, (Bsz, T, G, N))
+    D = rng.standard_normal(H).astype(np.float32) if with_D else None
+    h0 = _normal(rng, (Bsz, H, P, N)) if with_h0 else None
+    if dtype == "bf16":
+        x, B, C = f32_to_bf16_bits(x), f32_to_bf16_bits(B), f32_to_bf16_bits(C)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return dict(kind="real", x=x, dt=dt, A=A, B=B, C=C, D=D, dt_bias=dt_bias,
+                dt_min=DT_MIN, dt_max=DT_MAX, h0=h0, dtype=dtype,
+                dims=dict(Bsz=Bsz, T=T, H=H, P=P, G=G, N=N))
+
+
+def make_complex(Bsz, T, H, P, N, G=None, seed=0, with_h0=False, **_ignored):
+    """Inputs of the complex Mamba-3-Lite form.
+
+    x ~ N(0,1) float32; dt_raw ~ N(0,1) with no bias and clamp [1e-3, 1e-1];
+    A_re = -exp(U(log 0.5, log 4)), A_im ~ U(-pi, pi); B, C complex with real
+    and imaginary parts each ~ N(0, 1/2) (variance 1/2), stored as (re, im)
+    float32 pairs; optional h0 with parts ~ N(0, 1/2).
+    """
+    if G is None:
+        G = H
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (Bsz, T, H, P))
+    dt = _normal(rng, (Bsz, T, H))
+    a_re = -np.exp(rng.uniform(math.log(0.5), math.log(4.0), size=H))
+    a_im = rng.uniform(-math.pi, math.pi, size=H)
+    A = np.stack([a_re, a_im], axis=-1).astype(np.float32)
+    s = math.sqrt(0.5)
+    B = _normal(rng, (Bsz, T, G, N, 2), s)
+    C = _normal(rng, (Bsz, T, G, N, 2), s)
+    h0 = _normal(rng, (Bsz, H, P, N, 2), s) if with_h0 else None
+    return dict(kind="complex", x=x, dt=dt, A=A, B=B, C=C, D=None, dt_bias=None,
+                dt_min=DT_MIN, dt_max=DT_MAX, h0=h0, dtype="f32",
+                dims=dict(Bsz=Bsz, T=T, H=H, P=P, G=G, N=N))
+
+
+def make_decode(Bsz, H, P, N, G=1, steps=1, seed=0, **_ignored):
+    """Inputs of the single-token decode workload.
+
+    State h ~ N(0,1) float32 (Bsz,H,P,N); A, D, dt_bias as in ``make_real``;
+    then per step x (Bsz,H,P), dt_raw (Bsz,H), B, C (Bsz,G,N), all N(0,1)
+    float32.  Clamp [1e-3, 1e-1].
+    """
+    rng = np.random.default_rng(seed)
+    dt_bias = _dt_bias(rng, H)
+    A = (-np.exp(rng.uniform(0.0, math.log(16.0), size=H))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    h0 = _normal(rng, (Bsz, H, P, N))
+    per_step = []
+    for _ in range(steps):
+        per_step.append(dict(x=_normal(rng, (Bsz, H, P)), dt=_normal(rng, (Bsz, H)),
+                             B=_normal(rng, (Bsz, G, N)), C=_normal(rng, (Bsz, G, N))))
+    return dict(kind="decode", h0=h0, A=A, D=D, dt_bias=dt_bias, dt_min=DT_MIN,
+                dt_max=DT_MAX, steps=per_step,
+                dims=dict(Bsz=Bsz, H=H, P=P, G=G, N=N))
+
+
+def make_workload(name, seed=0, **overrides):
+    """Inputs for a named workload (see WORKLOADS), with optional overrides."""
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    kind = cfg["kind"]
+    if kind == "real":
+        return make_real(seed=seed, **cfg)
+    if kind == "complex":
+        return make_complex(seed=seed, **cfg)
+    return make_decode(seed=seed, **cfg)
