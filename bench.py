@@ -1,0 +1,341 @@
+"""Benchmark of the chunked SSD forward on one MI355X.
+
+Default workload: the BitMamba-1B Mamba-2 layer shape -- batch 2, T 2048,
+64 heads, head dim 64, state 128, one B/C group, chunk 256, bf16 x/B/C with
+fp32 dt/A/state -- on seeded synthetic inputs.  One step = one call of
+ssd_chunk_fwd over the whole batch (all three kernels: chunk states,
+inter-chunk scan, chunk outputs).
+
+Timing: HIP events recorded by the library on the launch stream around each
+kernel of every timed step; ms_per_step is the mean of the per-step event
+intervals.  Between steps a 512 MiB buffer is rewritten (outside the timed
+intervals) so that the 256 MB Infinity Cache holds none of the step's inputs:
+the number is the rate with inputs resident in HBM.
+
+Prints one JSON line (rank 0): metric, value (tokens/s), roofline of the
+dominant kernel, and the float64 CPU oracle timed on a bounded sample.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/s per layer (H64 P64 N128) + % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bitmamba_bf16",
+                    choices=["bitmamba_bf16", "long_bf16", "mamba3lite_complex", "tiny_f32",
+                             "decode_f32"])
+    ap.add_argument("--no-flush", action="store_true",
+                    help="keep the Infinity Cache warm between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+class Hip:
+    """Minimal HIP event API through ctypes (the runtime torch already loaded)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e
+
+    def record(self, e, stream):
+        rc = self.lib.hipEventRecord(e, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+
+def kernel_bytes(cfg, dims):
+    """Algorithmic HBM bytes of each kernel of one chunked-forward call: every
+    array the kernel must read or write, counted once."""
+    Bsz, T, H, P, G, N, Q = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N", "Q"))
+    cplx = cfg["kind"] == "complex"
+    es = 2 if cfg.get("dtype") == "bf16" else 4          # x element
+    bs = 8 if cplx else es                                # B/C element
+    KC = 2 * N if cplx else N
+    nc = -(-T // Q)
+    x = Bsz * T * H * P * es
+    bc = Bsz * T * G * N * bs
+    dt = Bsz * T * H * 4
+    states = Bsz * nc * H * P * KC * 4
+    decay = Bsz * H * nc * 8
+    y = Bsz * T * H * P * (4 if cplx else es)
+    return {
+        "ssd_state_kernel": x + bc + dt + states + decay,
+        "ssd_pass_kernel": 2 * states + decay,
+        "ssd_scan_kernel": x + 2 * bc + dt + states + y,
+        "whole_forward": x + 2 * bc + dt + y,
+    }
+
+
+def kernel_flops(cfg, dims):
+    """Algorithmic flops: lower-triangle intra-chunk products (C.B^T per head
+    and M.X), chunk states and the C.h_in products."""
+    Bsz, T, H, P, G, N, Q = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N", "Q"))
+    KC = 2 * N if cfg["kind"] == "complex" else N
+    units = Bsz * H * (T / Q)                   # (b, chunk, h) units
+    tri = Q * (Q + 1) / 2
+    scan = units * (2 * tri * KC + 2 * tri * P + 2 * Q * KC * P)
+    state = units * 2 * Q * KC * P
+    return {"ssd_scan_kernel": scan, "ssd_state_kernel": state}
+
+
+def cpu_baseline(inp, cfg, dims, target_s):
+    """The float64 oracle on a bounded sample of the same workload: the first
+    k (batch, head) recurrences in full length, k grown until the run takes
+    about target_s seconds.  Reported as tokens/s of the whole workload's
+    token count scaled by the sampled fraction."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    H = dims["H"]
+    Bsz, T = dims["Bsz"], dims["T"]
+    total_bh = Bsz * H
+
+    def run(nh):
+        sub = dict(inp)
+        sub["x"] = np.ascontiguousarray(inp["x"][:1, :, :nh])
+        sub["dt"] = np.ascontiguousarray(inp["dt"][:1, :, :nh])
+        sub["A"] = np.ascontiguousarray(inp["A"][:nh])
+        G, N = dims["G"], dims["N"]
+        hpg = H // G
+        groups = [h // hpg for h in range(nh)]
+        sub["B"] = np.ascontiguousarray(inp["B"][:1, :, groups])
+        sub["C"] = np.ascontiguousarray(inp["C"][:1, :, groups])
+        for k in ("D", "dt_bias"):
+            sub[k] = None if inp[k] is None else np.ascontiguousarray(inp[k][:nh])
+        t0 = time.perf_counter()
+        if cfg["kind"] == "complex":
+            oracle.complex_fwd(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"],
+                               sub["dt_bias"], sub["dt_min"], sub["dt_max"], None)
+        else:
+            oracle.fwd(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["D"],
+                       sub["dt_bias"], sub["dt_min"], sub["dt_max"], None)
+        return time.perf_counter() - t0
+
+    nh = min(H, max(1, threads))
+    dt_run = run(nh)
+    while dt_run < target_s / 3 and nh < H:
+        nh = min(H, nh * 2)
+        dt_run = run(nh)
+    frac = nh / total_bh
+    tokens_per_s = (Bsz * T * frac) / dt_run
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": oracle.threads_used(),
+            "kind": "oracle",
+            "sample": f"{nh} of {total_bh} (batch, head) recurrences of the same workload, "
+                      f"full length T={T}, float64, {dt_run:.2f} s; tokens/s scaled by the "
+                      f"sampled fraction {nh}/{total_bh}"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the scan shards by batch/head with no communication; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_09_amd as ssd
+    from selective_state_space_09_amd import inputs
+
+    cfg = dict(inputs.WORKLOADS[args.workload])
+    if cfg["kind"] == "decode":
+        return bench_decode(args, cfg)
+    inp = inputs.make_workload(args.workload, seed=0)
+    Q = cfg["chunk"]
+    dims = dict(inp["dims"], Q=Q)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    d = {k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    Bsz, T, H, P, G, N = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N"))
+    cplx = cfg["kind"] == "complex"
+    y = torch.empty((Bsz, T, H, P), dtype=torch.float32 if cplx else d["x"].dtype, device=dev)
+    nbytes = ssd.ssd_workspace_size(Bsz, T, H, P, G, N, Q, cplx)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    L = ssd.lib()
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P_ = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    n_total = args.warmup + args.steps
+    evs = [[hip.event() for _ in range(4)] for _ in range(n_total)]
+    ev_arrays = [(ctypes.c_void_p * 4)(*[e.value for e in row]) for row in evs]
+
+    if cplx:
+        fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["dt_bias"]),
+                 float(d["dt_min"]), float(d["dt_max"]), None, P_(y), None,
+                 Bsz, T, H, P, G, N, Q, P_(ws), ws.numel(), sp)
+        call = lambda evarr: L.ssd_complex_chunk_fwd_ev(*fixed, evarr)
+        dtype_name = "f32"
+    else:
+        dcode = ssd.SSD_BF16 if d["x"].dtype == torch.bfloat16 else ssd.SSD_F32
+        fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["D"]),
+                 P_(d["dt_bias"]), float(d["dt_min"]), float(d["dt_max"]), None, P_(y), None,
+                 Bsz, T, H, P, G, N, Q, dcode, P_(ws), ws.numel(), sp)
+        call = lambda evarr: L.ssd_chunk_fwd_ev(*fixed, evarr)
+        dtype_name = "bf16" if dcode == ssd.SSD_BF16 else "f32"
+
+    def step(i):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        rc = call(ev_arrays[i])
+        if rc != 0:
+            raise RuntimeError(L.ssd_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.warmup, n_total):
+        step(i)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    names = ["ssd_state_kernel", "ssd_pass_kernel", "ssd_scan_kernel"]
+    per_step, per_kernel = [], {n: [] for n in names}
+    for i in range(args.warmup, n_total):
+        e = evs[i]
+        per_step.append(hip.elapsed_ms(e[0], e[3]))
+        for k, n in enumerate(names):
+            per_kernel[n].append(hip.elapsed_ms(e[k], e[k + 1]))
+    ms = float(np.mean(per_step))
+    tokens = Bsz * T
+    value = tokens / (ms / 1e3)
+    kb = kernel_bytes(cfg, dims)
+    kf = kernel_flops(cfg, dims)
+    kern = {}
+    for n in names:
+        avg = float(np.mean(per_kernel[n]))
+        gbs = kb[n] / (avg / 1e3) / 1e9
+        ent = {"avg_us": avg * 1e3, "alg_bytes": kb[n], "hbm_gbs": gbs,
+               "hbm_frac": gbs / HBM_PEAK_GBS}
+        if n in kf:
+            tf = kf[n] / (avg / 1e3) / 1e12
+            ent.update({"alg_flops": kf[n], "tflops": tf,
+                        "mfma_frac": tf / MFMA_PEAK_TFLOPS[dtype_name]})
+        kern[n] = ent
+    dom = max(names, key=lambda n: kern[n]["avg_us"])
+    k = kern[dom]
+    if "mfma_frac" in k and k["mfma_frac"] > k["hbm_frac"]:
+        roof = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_PEAK_TFLOPS[dtype_name],
+                "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": None, "kernel": dom}
+    else:
+        roof = {"bound": "hbm", "achieved": k["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": k["hbm_frac"], "traffic": None, "kernel": dom}
+    whole_gbs = kb["whole_forward"] / (ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype_name, "data": "synthetic",
+        "config": {"workload": args.workload, "batch": Bsz, "seq_len": T, "heads": H,
+                   "headdim": P, "d_state": N, "ngroups": G, "chunk": Q,
+                   "complex": cplx, "cache": "cold (Infinity Cache flushed between steps)"
+                   if flush is not None else "warm"},
+        "roofline": roof,
+        "whole_forward": {"alg_bytes": kb["whole_forward"], "hbm_gbs": whole_gbs,
+                          "hbm_frac": whole_gbs / HBM_PEAK_GBS},
+        "kernels": kern,
+        "wall_ms_per_step_incl_flush": t_wall / args.steps * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, cfg, dims, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, cfg):
+    """Decode workload: one step = one ssd_step_decode over the whole batch
+    (state 256 x 64 x 64 x 128 fp32 updated in place)."""
+    import torch
+    import selective_state_space_09_amd as ssd
+    from selective_state_space_09_amd import inputs
+    inp = inputs.make_workload("decode_f32", seed=0, steps=1)
+    dev = torch.device("cuda:0")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    h = up(inp["h0"])
+    st = inp["steps"][0]
+    x, dt, B, C = up(st["x"]), up(st["dt"]), up(st["B"]), up(st["C"])
+    A, D, bias = up(inp["A"]), up(inp["D"]), up(inp["dt_bias"])
+    Bsz, H, P, N = h.shape
+    G = B.shape[1]
+    y = torch.empty((Bsz, H, P), dtype=torch.float32, device=dev)
+    L = ssd.lib()
+    hip = Hip()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P_ = lambda t: ctypes.c_void_p(t.data_ptr())
+    args_c = (P_(h), P_(x), P_(dt), P_(A), P_(B), P_(C), P_(D), P_(bias),
+              float(inp["dt_min"]), float(inp["dt_max"]), P_(y), Bsz, H, P, G, N, sp)
+    n_total = args.warmup + args.steps
+    evs = [(hip.event(), hip.event()) for _ in range(n_total)]
+    for i in range(n_total):
+        hip.record(evs[i][0], sp)
+        rc = L.ssd_step_decode(*args_c)
+        hip.record(evs[i][1], sp)
+        if rc:
+            raise RuntimeError(L.ssd_last_error().decode())
+    torch.cuda.synchronize()
+    times = [hip.elapsed_ms(a, b) for a, b in evs[args.warmup:]]
+    ms = float(np.mean(times))
+    nbytes = 2 * h.numel() * 4 + Bsz * H * P * 8 + Bsz * H * 4 + 2 * Bsz * G * N * 4
+    gbs = nbytes / (ms / 1e3) / 1e9
+    out = {"metric": "SSD decode tokens/s (B256 H64 P64 N128)", "value": Bsz / (ms / 1e3),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "decode_f32", "batch": Bsz, "heads": H, "headdim": P,
+                      "d_state": N},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                        "kernel": "ssd_decode_kernel"}}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

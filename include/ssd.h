@@ -1,0 +1,174 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) selective state-space (SSD) scan.
+ *
+ * What is computed (page titles and sections of the sources):
+ *
+ *  Real (Mamba-2) form, one scalar A_h < 0 per head (Mamba-3-Lite README,
+ *  "classical Mamba-2 recurrence"; Block Anatomy page, section 4.4 for
+ *  exp(softplus(dt) * A); step size also on the input term, the usual
+ *  Mamba-2 discretisation):
+ *      delta_t = clamp(softplus(dt_t + dt_bias_h), dt_min, dt_max)
+ *      h_t     = exp(A_h delta_t) h_{t-1} + delta_t x_t B_t^T      (P x N)
+ *      y_t     = h_t C_t + D_h x_t
+ *
+ *  Complex (Mamba-3-Lite) form (README, the complex recurrence; Block
+ *  Anatomy section 6, the real part is returned):
+ *      h_t = exp((alpha_h + i beta_h) delta_t) h_{t-1} + x_t B_t^T  (complex)
+ *      y_t = Re(h_t C_t)          -- C is not conjugated; no D term
+ *
+ *  Both are evaluated chunkwise (chunk length Q): within a chunk through the
+ *  decay matrix L[l,s] = exp(cs_l - cs_s) 1[l >= s] and across chunks by a
+ *  linear scan of chunk-end states (Numerical Stability in Mamba-3-Lite,
+ *  section 4).  The result equals the sequential recurrence up to rounding.
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers (memory of the current HIP
+ *    device), row-major and contiguous, last index fastest.  The caller owns
+ *    every buffer; the library never allocates, frees or keeps a pointer
+ *    after the call returns.
+ *  - x, B, C, y, h0, h_final, h and workspace must be 16-byte aligned; dt, A,
+ *    D and dt_bias 4-byte aligned.
+ *  - Head h reads B/C group g = h / (H / G)  (H % G == 0).
+ *  - dt is the raw (pre-softplus) step; dt_bias may be NULL (zero bias);
+ *    dt_min/dt_max clamp the step after softplus (0 and +INFINITY disable).
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream).  The
+ *    call only enqueues work and returns; buffers must stay valid until the
+ *    stream has passed it.  Faults inside kernels surface at the caller's
+ *    next synchronisation.
+ *  - Every argument is validated before any HIP call, so a rejected call has
+ *    no effect on the device.  There is no fallback path: unsupported shapes
+ *    are errors.
+ *  - Return value: SSD_OK or one of the error codes below; ssd_last_error()
+ *    then describes the problem (thread-local, valid until the next call on
+ *    the same thread).
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+/* status codes */
+#define SSD_OK 0
+#define SSD_EINVAL 1          /* null pointer, bad size, misaligned pointer  */
+#define SSD_EUNSUPPORTED 2    /* valid but not built: P, N, chunk or dtype   */
+#define SSD_EWORKSPACE 3      /* workspace missing or smaller than required  */
+#define SSD_EHIP 4            /* a HIP launch reported an error              */
+
+/* element types of x, B, C and y in ssd_chunk_fwd */
+#define SSD_F32 0
+#define SSD_BF16 1
+
+/* Supported sizes of the chunked forwards:
+ *   P (head dim) in {16, 32, 64, 128}; N (state) in {16, 32, 64, 128} for the
+ *   real form and {16, 32, 64} for the complex form; chunk in
+ *   {32, 64, 128, 256}; any T >= 0 (a last, shorter chunk is handled as if
+ *   padded with identity steps).  The decode step takes N in
+ *   {16, 32, 64, 128, 256} and any P >= 1. */
+
+/* Version of this ABI (SSD_ABI_VERSION of the built library). */
+int ssd_abi_version(void);
+
+/* Description of the last error on this thread ("" when none). */
+const char *ssd_last_error(void);
+
+/*
+ * Bytes of device workspace ssd_chunk_fwd (is_complex = 0) or
+ * ssd_complex_chunk_fwd (is_complex = 1) needs for these sizes: the
+ * chunk-boundary states, fp32, (Bsz, nc, H, P, N) real or (Bsz, nc, H, P, 2N)
+ * complex with nc = ceil(T / chunk), plus one decay factor per (b, h, chunk).
+ * Returns 0 for sizes the library rejects.
+ */
+size_t ssd_workspace_size(int Bsz, int T, int H, int P, int G, int N, int chunk,
+                          int is_complex);
+
+/*
+ * Real chunked forward (Mamba-2 form above).
+ *   x        (Bsz, T, H, P)  dtype (SSD_F32 or SSD_BF16 bit patterns)
+ *   dt       (Bsz, T, H)     float32, raw step
+ *   A        (H)             float32, A_h (negative for a decaying scan)
+ *   B, C     (Bsz, T, G, N)  dtype
+ *   D        (H)             float32 or NULL (no skip term)
+ *   dt_bias  (H)             float32 or NULL
+ *   h0       (Bsz, H, P, N)  float32 initial state, or NULL for zeros
+ *   y        (Bsz, T, H, P)  dtype, written (bf16 rounded to nearest even
+ *                            from the fp32 accumulator)
+ *   h_final  (Bsz, H, P, N)  float32 state after token T-1, or NULL
+ *   workspace of at least ssd_workspace_size(..., 0) bytes, device memory
+ * The state and all accumulation are fp32 for both dtypes.
+ */
+int ssd_chunk_fwd(const void *x, const float *dt, const float *A, const void *B,
+                  const void *C, const float *D, const float *dt_bias,
+                  float dt_min, float dt_max, const float *h0, void *y,
+                  float *h_final, int Bsz, int T, int H, int P, int G, int N,
+                  int chunk, int dtype, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
+ * Complex chunked forward (Mamba-3-Lite form above).
+ *   x        (Bsz, T, H, P)     float32 (real token content)
+ *   dt       (Bsz, T, H)        float32, raw step
+ *   A        (H, 2)             float32 (alpha_h, beta_h) = complex64
+ *   B, C     (Bsz, T, G, N, 2)  float32 (re, im) pairs = complex64
+ *   dt_bias  (H)                float32 or NULL
+ *   h0       (Bsz, H, P, N, 2)  complex64 initial state, or NULL for zeros
+ *   y        (Bsz, T, H, P)     float32, Re(h_t C_t)
+ *   h_final  (Bsz, H, P, N, 2)  complex64 final state, or NULL
+ *   workspace of at least ssd_workspace_size(..., 1) bytes
+ */
+int ssd_complex_chunk_fwd(const float *x, const float *dt, const float *A,
+                          const float *B, const float *C, const float *dt_bias,
+                          float dt_min, float dt_max, const float *h0, float *y,
+                          float *h_final, int Bsz, int T, int H, int P, int G,
+                          int N, int chunk, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * Measurement variants of the two chunked forwards: identical arguments,
+ * kernels and results, plus `events`, an array of 4 hipEvent_t (passed as
+ * void*) recorded on `stream` before the chunk-state kernel, after it, after
+ * the inter-chunk scan and after the output kernel; or NULL (then they are
+ * the plain calls).  The caller creates and owns the events.
+ */
+int ssd_chunk_fwd_ev(const void *x, const float *dt, const float *A,
+                     const void *B, const void *C, const float *D,
+                     const float *dt_bias, float dt_min, float dt_max,
+                     const float *h0, void *y, float *h_final, int Bsz, int T,
+                     int H, int P, int G, int N, int chunk, int dtype,
+                     void *workspace, size_t workspace_bytes, void *stream,
+                     void *const *events);
+
+int ssd_complex_chunk_fwd_ev(const float *x, const float *dt, const float *A,
+                             const float *B, const float *C,
+                             const float *dt_bias, float dt_min, float dt_max,
+                             const float *h0, float *y, float *h_final, int Bsz,
+                             int T, int H, int P, int G, int N, int chunk,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream, void *const *events);
+
+/*
+ * One recurrent step of the real form for a single new token per sequence
+ * (the recurrence of the Mamba-3-Lite README applied once), in place:
+ *   h        (Bsz, H, P, N)  float32 state, read and overwritten
+ *   x        (Bsz, H, P)     float32
+ *   dt       (Bsz, H)        float32, raw step
+ *   A, D, dt_bias (H)        as in ssd_chunk_fwd (D, dt_bias may be NULL)
+ *   B, C     (Bsz, G, N)     float32
+ *   y        (Bsz, H, P)     float32, computed from the updated state
+ * Needs no workspace.
+ */
+int ssd_step_decode(float *h, const float *x, const float *dt, const float *A,
+                    const float *B, const float *C, const float *D,
+                    const float *dt_bias, float dt_min, float dt_max, float *y,
+                    int Bsz, int H, int P, int G, int N, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

@@ -1,0 +1,190 @@
+"""MI355X (gfx950) chunked selective state-space (SSD) scan.
+
+Python binding of the C ABI in ``include/ssd.h`` (library ``libssd.so`` in
+this package).  The functions keep the C names and only marshal arguments:
+tensors must already live on the GPU; PyTorch provides device memory and the
+current stream, every step of the scan runs in the library's HIP kernels.
+There is no CPU path: without the built library every call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd.so")
+
+SSD_OK, SSD_EINVAL, SSD_EUNSUPPORTED, SSD_EWORKSPACE, SSD_EHIP = 0, 1, 2, 3, 4
+SSD_F32, SSD_BF16 = 0, 1
+
+_lib = None
+
+
+class SSDError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"ssd error {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """The loaded C library (ctypes), with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.ssd_abi_version.restype = I
+    L.ssd_abi_version.argtypes = []
+    L.ssd_last_error.restype = ctypes.c_char_p
+    L.ssd_last_error.argtypes = []
+    L.ssd_workspace_size.restype = S
+    L.ssd_workspace_size.argtypes = [I] * 8
+    L.ssd_chunk_fwd.restype = I
+    L.ssd_chunk_fwd.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P,
+                                I, I, I, I, I, I, I, I, P, S, P]
+    L.ssd_complex_chunk_fwd.restype = I
+    L.ssd_complex_chunk_fwd.argtypes = [P, P, P, P, P, P, F, F, P, P, P,
+                                        I, I, I, I, I, I, I, P, S, P]
+    L.ssd_chunk_fwd_ev.restype = I
+    L.ssd_chunk_fwd_ev.argtypes = L.ssd_chunk_fwd.argtypes + [P]
+    L.ssd_complex_chunk_fwd_ev.restype = I
+    L.ssd_complex_chunk_fwd_ev.argtypes = L.ssd_complex_chunk_fwd.argtypes + [P]
+    L.ssd_step_decode.restype = I
+    L.ssd_step_decode.argtypes = [P, P, P, P, P, P, P, P, F, F, P, I, I, I, I, I, P]
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != SSD_OK:
+        raise SSDError(rc, lib().ssd_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _pairs(t):
+    return torch.view_as_real(t) if t is not None and t.is_complex() else t
+
+
+def ssd_abi_version():
+    return lib().ssd_abi_version()
+
+
+def ssd_workspace_size(Bsz, T, H, P, G, N, chunk, is_complex=False):
+    return int(lib().ssd_workspace_size(Bsz, T, H, P, G, N, chunk, int(bool(is_complex))))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return _dev(workspace, "workspace")
+
+
+def ssd_chunk_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=math.inf,
+                  h0=None, chunk=256, y=None, h_final=None, return_final_state=False,
+                  workspace=None, stream=None):
+    """Real chunked forward.  x (Bsz,T,H,P) and B, C (Bsz,T,G,N) in float32 or
+    bfloat16; dt (Bsz,T,H), A/D/dt_bias (H), h0 (Bsz,H,P,N) float32.
+    Returns y (and h_final when asked or given)."""
+    if x.dtype == torch.bfloat16:
+        dtype = SSD_BF16
+    elif x.dtype == torch.float32:
+        dtype = SSD_F32
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    _dev(x, "x")
+    _dev(B, "B", x.dtype)
+    _dev(C, "C", x.dtype)
+    _dev(dt, "dt", torch.float32)
+    _dev(A, "A", torch.float32)
+    _dev(D, "D", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    _dev(h0, "h0", torch.float32)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype)
+    if h_final is None and return_final_state:
+        h_final = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=x.device)
+    _dev(h_final, "h_final", torch.float32)
+    nbytes = ssd_workspace_size(Bsz, T, H, P, G, N, chunk, False)
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib().ssd_chunk_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                               _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0),
+                               _ptr(y), _ptr(h_final), Bsz, T, H, P, G, N, chunk, dtype,
+                               _ptr(ws), ws.numel(), _stream(stream)))
+    return (y, h_final) if h_final is not None else y
+
+
+def ssd_complex_chunk_fwd(x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=math.inf,
+                          h0=None, chunk=256, y=None, h_final=None,
+                          return_final_state=False, workspace=None, stream=None):
+    """Complex chunked forward.  x (Bsz,T,H,P) float32; A (H) complex64 or
+    (H,2) float32; B, C (Bsz,T,G,N) complex64 or (...,N,2) float32; h0
+    likewise.  Returns y = Re(h C) (and h_final as (Bsz,H,P,N,2) float32)."""
+    A, B, C, h0 = _pairs(A), _pairs(B), _pairs(C), _pairs(h0)
+    _dev(x, "x", torch.float32)
+    _dev(dt, "dt", torch.float32)
+    _dev(A, "A", torch.float32)
+    _dev(B, "B", torch.float32)
+    _dev(C, "C", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    _dev(h0, "h0", torch.float32)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", torch.float32)
+    if h_final is None and return_final_state:
+        h_final = torch.empty((Bsz, H, P, N, 2), dtype=torch.float32, device=x.device)
+    h_final = _pairs(h_final)
+    _dev(h_final, "h_final", torch.float32)
+    nbytes = ssd_workspace_size(Bsz, T, H, P, G, N, chunk, True)
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib().ssd_complex_chunk_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                       _ptr(dt_bias), float(dt_min), float(dt_max),
+                                       _ptr(h0), _ptr(y), _ptr(h_final), Bsz, T, H, P, G,
+                                       N, chunk, _ptr(ws), ws.numel(), _stream(stream)))
+    return (y, h_final) if h_final is not None else y
+
+
+def ssd_step_decode(h, x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=math.inf,
+                    y=None, stream=None):
+    """One decode step, state h (Bsz,H,P,N) float32 updated in place; x
+    (Bsz,H,P), dt (Bsz,H), B/C (Bsz,G,N).  Returns y (Bsz,H,P)."""
+    for t, n in ((h, "h"), (x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C")):
+        _dev(t, n, torch.float32)
+    _dev(D, "D", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    Bsz, H, P, N = h.shape
+    G = B.shape[1]
+    if y is None:
+        y = torch.empty((Bsz, H, P), dtype=torch.float32, device=h.device)
+    _dev(y, "y", torch.float32)
+    _check(lib().ssd_step_decode(_ptr(h), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(dt_bias), float(dt_min), float(dt_max),
+                                 _ptr(y), Bsz, H, P, G, N, _stream(stream)))
+    return y

@@ -1,0 +1,209 @@
+// C ABI of the SSD library (declared in include/ssd.h): argument validation,
+// workspace sizing and kernel dispatch.  Validation runs before any HIP call,
+// so rejected calls never touch the device.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/ssd.h"
+#include "ssd_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SSD_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool in_set(int v, const int* set, int n) {
+  for (int i = 0; i < n; ++i)
+    if (set[i] == v) return true;
+  return false;
+}
+
+const int kPs[] = {16, 32, 64, 128};
+const int kNsReal[] = {16, 32, 64, 128};
+const int kNsCplx[] = {16, 32, 64};
+const int kChunks[] = {32, 64, 128, 256};
+const int kNsDecode[] = {16, 32, 64, 128, 256};
+
+// Shape checks shared by both chunked forwards.  Returns SSD_OK or an error.
+int check_chunk_shape(int Bsz, int T, int H, int P, int G, int N, int chunk, int is_complex) {
+  if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk <= 0)
+    return fail(SSD_EINVAL, "sizes must be positive (T >= 0): Bsz=%d T=%d H=%d P=%d G=%d N=%d chunk=%d",
+                Bsz, T, H, P, G, N, chunk);
+  if (H % G != 0) return fail(SSD_EINVAL, "H=%d is not a multiple of G=%d", H, G);
+  if (!in_set(P, kPs, 4)) return fail(SSD_EUNSUPPORTED, "P=%d not in {16,32,64,128}", P);
+  if (is_complex ? !in_set(N, kNsCplx, 3) : !in_set(N, kNsReal, 4))
+    return fail(SSD_EUNSUPPORTED, "N=%d not supported (%s)", N,
+                is_complex ? "complex: {16,32,64}" : "real: {16,32,64,128}");
+  if (!in_set(chunk, kChunks, 4)) return fail(SSD_EUNSUPPORTED, "chunk=%d not in {32,64,128,256}", chunk);
+  // 32-bit grid limits and index headroom
+  const long long nc = (static_cast<long long>(T) + chunk - 1) / chunk;
+  if (nc > 2147483647LL || static_cast<long long>(H) > 65535 || Bsz > 65535)
+    return fail(SSD_EUNSUPPORTED, "grid too large: nc=%lld H=%d Bsz=%d", nc, H, Bsz);
+  return SSD_OK;
+}
+
+int check_clamp(float lo, float hi) {
+  if (!(lo >= 0.0f) || !(hi >= lo))
+    return fail(SSD_EINVAL, "need 0 <= dt_min <= dt_max (got %g, %g)", lo, hi);
+  return SSD_OK;
+}
+
+size_t workspace_bytes_for(int Bsz, int T, int H, int P, int N, int chunk, int is_complex) {
+  const int nc = (T + chunk - 1) / chunk;
+  const int KC = is_complex ? 2 * N : N;
+  const size_t floats = ssd::workspace_state_floats(Bsz, nc, H, P, KC) +
+                        ssd::workspace_decay_floats(Bsz, nc, H);
+  const size_t bytes = floats * sizeof(float);
+  return (bytes + 255) / 256 * 256 + 256;
+}
+
+int check_ptr(const void* p, const char* name, uintptr_t align, bool required) {
+  if (!p) {
+    if (required) return fail(SSD_EINVAL, "%s is NULL", name);
+    return SSD_OK;
+  }
+  if (!aligned(p, align)) return fail(SSD_EINVAL, "%s is not %u-byte aligned", name, (unsigned)align);
+  return SSD_OK;
+}
+
+#define SSD_TRY(expr)          \
+  do {                         \
+    const int rc_ = (expr);    \
+    if (rc_ != SSD_OK) return rc_; \
+  } while (0)
+
+int launch_status(hipError_t e) {
+  if (e != hipSuccess) return fail(SSD_EHIP, "HIP error: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_last_error(void) { return g_err; }
+
+size_t ssd_workspace_size(int Bsz, int T, int H, int P, int G, int N, int chunk, int is_complex) {
+  if (check_chunk_shape(Bsz, T, H, P, G, N, chunk, is_complex) != SSD_OK) return 0;
+  return workspace_bytes_for(Bsz, T, H, P, N, chunk, is_complex);
+}
+
+int ssd_chunk_fwd_ev(const void* x, const float* dt, const float* A, const void* B,
+                     const void* C, const float* D, const float* dt_bias, float dt_min,
+                     float dt_max, const float* h0, void* y, float* h_final, int Bsz, int T,
+                     int H, int P, int G, int N, int chunk, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream, void* const* events) {
+  SSD_TRY(check_chunk_shape(Bsz, T, H, P, G, N, chunk, 0));
+  if (dtype != SSD_F32 && dtype != SSD_BF16)
+    return fail(SSD_EUNSUPPORTED, "dtype=%d is neither SSD_F32 nor SSD_BF16", dtype);
+  const bool has_tokens = T > 0;
+  SSD_TRY(check_ptr(x, "x", 16, has_tokens));
+  SSD_TRY(check_ptr(dt, "dt", 4, has_tokens));
+  SSD_TRY(check_ptr(A, "A", 4, has_tokens));
+  SSD_TRY(check_ptr(B, "B", 16, has_tokens));
+  SSD_TRY(check_ptr(C, "C", 16, has_tokens));
+  SSD_TRY(check_ptr(y, "y", 16, has_tokens));
+  SSD_TRY(check_ptr(D, "D", 4, false));
+  SSD_TRY(check_ptr(dt_bias, "dt_bias", 4, false));
+  SSD_TRY(check_ptr(h0, "h0", 16, false));
+  SSD_TRY(check_ptr(h_final, "h_final", 16, false));
+  SSD_TRY(check_clamp(dt_min, dt_max));
+  const size_t need = workspace_bytes_for(Bsz, T, H, P, N, chunk, 0);
+  SSD_TRY(check_ptr(workspace, "workspace", 256, true));
+  if (workspace_bytes < need)
+    return fail(SSD_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  ssd::ChunkArgs a{x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final,
+                   Bsz, T, H, P, G, N, chunk, dtype, workspace,
+                   reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_chunk_real(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssd_chunk_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                  const float* D, const float* dt_bias, float dt_min, float dt_max,
+                  const float* h0, void* y, float* h_final, int Bsz, int T, int H, int P, int G,
+                  int N, int chunk, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return ssd_chunk_fwd_ev(x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final, Bsz, T,
+                          H, P, G, N, chunk, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssd_complex_chunk_fwd_ev(const float* x, const float* dt, const float* A, const float* B,
+                             const float* C, const float* dt_bias, float dt_min, float dt_max,
+                             const float* h0, float* y, float* h_final, int Bsz, int T, int H,
+                             int P, int G, int N, int chunk, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* events) {
+  SSD_TRY(check_chunk_shape(Bsz, T, H, P, G, N, chunk, 1));
+  const bool has_tokens = T > 0;
+  SSD_TRY(check_ptr(x, "x", 16, has_tokens));
+  SSD_TRY(check_ptr(dt, "dt", 4, has_tokens));
+  SSD_TRY(check_ptr(A, "A", 8, has_tokens));
+  SSD_TRY(check_ptr(B, "B", 16, has_tokens));
+  SSD_TRY(check_ptr(C, "C", 16, has_tokens));
+  SSD_TRY(check_ptr(y, "y", 16, has_tokens));
+  SSD_TRY(check_ptr(dt_bias, "dt_bias", 4, false));
+  SSD_TRY(check_ptr(h0, "h0", 16, false));
+  SSD_TRY(check_ptr(h_final, "h_final", 16, false));
+  SSD_TRY(check_clamp(dt_min, dt_max));
+  const size_t need = workspace_bytes_for(Bsz, T, H, P, N, chunk, 1);
+  SSD_TRY(check_ptr(workspace, "workspace", 256, true));
+  if (workspace_bytes < need)
+    return fail(SSD_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  ssd::ChunkArgs a{x, dt, A, B, C, nullptr, dt_bias, dt_min, dt_max, h0, y, h_final,
+                   Bsz, T, H, P, G, N, chunk, SSD_F32, workspace,
+                   reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_chunk_complex(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssd_complex_chunk_fwd(const float* x, const float* dt, const float* A, const float* B,
+                          const float* C, const float* dt_bias, float dt_min, float dt_max,
+                          const float* h0, float* y, float* h_final, int Bsz, int T, int H, int P,
+                          int G, int N, int chunk, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return ssd_complex_chunk_fwd_ev(x, dt, A, B, C, dt_bias, dt_min, dt_max, h0, y, h_final, Bsz,
+                                  T, H, P, G, N, chunk, workspace, workspace_bytes, stream,
+                                  nullptr);
+}
+
+int ssd_step_decode(float* h, const float* x, const float* dt, const float* A, const float* B,
+                    const float* C, const float* D, const float* dt_bias, float dt_min,
+                    float dt_max, float* y, int Bsz, int H, int P, int G, int N, void* stream) {
+  if (Bsz <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0)
+    return fail(SSD_EINVAL, "sizes must be positive: Bsz=%d H=%d P=%d G=%d N=%d", Bsz, H, P, G, N);
+  if (H % G != 0) return fail(SSD_EINVAL, "H=%d is not a multiple of G=%d", H, G);
+  if (!in_set(N, kNsDecode, 5)) return fail(SSD_EUNSUPPORTED, "N=%d not in {16,32,64,128,256}", N);
+  if (static_cast<long long>(Bsz) * H > 2147483647LL)
+    return fail(SSD_EUNSUPPORTED, "Bsz*H too large");
+  SSD_TRY(check_ptr(h, "h", 16, true));
+  SSD_TRY(check_ptr(x, "x", 4, true));
+  SSD_TRY(check_ptr(dt, "dt", 4, true));
+  SSD_TRY(check_ptr(A, "A", 4, true));
+  SSD_TRY(check_ptr(B, "B", 16, true));
+  SSD_TRY(check_ptr(C, "C", 16, true));
+  SSD_TRY(check_ptr(y, "y", 4, true));
+  SSD_TRY(check_ptr(D, "D", 4, false));
+  SSD_TRY(check_ptr(dt_bias, "dt_bias", 4, false));
+  SSD_TRY(check_clamp(dt_min, dt_max));
+  ssd::DecodeArgs a{h, x, dt, A, B, C, D, dt_bias, dt_min, dt_max, y, Bsz, H, P, G, N};
+  return launch_status(ssd::run_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

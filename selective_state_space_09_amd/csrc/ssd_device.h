@@ -1,0 +1,92 @@
+// Device-side helpers shared by the gfx950 SSD kernels: element conversion,
+// MFMA operand types, the step-size gate and the per-chunk prefix scan.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // 4 waves per workgroup in every chunk kernel
+
+// bfloat16 values travel as uint16 bit patterns (the top half of a float32).
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float load_elem(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* p, size_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+__device__ __forceinline__ void store_elem(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, size_t i, float v) {
+  p[i] = f32_to_bf16_bits(v);
+}
+
+// Step size of one token: softplus(dt + bias) = ln(1 + e^z), evaluated as
+// max(z, 0) + ln(1 + e^-|z|), then clamped to [lo, hi] (Numerical Stability
+// in Mamba-3-Lite, section 4: the gate is softplus, always positive).
+__device__ __forceinline__ float step_size(float dt, float bias, float lo, float hi) {
+  const float z = dt + bias;
+  const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+  return fminf(fmaxf(sp, lo), hi);
+}
+
+// Inclusive prefix sum of one double per thread over a 256-thread block.
+// wsum must be a __shared__ array of 4 doubles.  Contains __syncthreads().
+__device__ __forceinline__ double block_inclusive_scan(double v, double* wsum) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  if (lane == kWave - 1) wsum[wid] = v;
+  __syncthreads();
+  double add = 0.0;
+  for (int k = 0; k < wid; ++k) add += wsum[k];
+  return v + add;
+}
+
+// cos/sin of an angle given in double: reduced to [-pi, pi] in double, then
+// evaluated in float.  Angles of a 256-token chunk reach ~80 rad; reducing in
+// float would cost ~1e-5 rad of phase.
+__device__ __forceinline__ void rot_cs(double ang, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const double r = ang - two_pi * rint(ang * (1.0 / two_pi));
+  sincosf(static_cast<float>(r), &s, &c);
+}
+
+// MFMA wrappers (gfx950).  Operand layouts for the 16x16 forms, lane i,
+// q = i / 16:  A holds row i % 16, B holds column i % 16, and the k values
+// of a lane are k-group q; the accumulator holds column i % 16, rows
+// 4q .. 4q+3.  The kernels only rely on A and B sharing one k assignment.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace ssd

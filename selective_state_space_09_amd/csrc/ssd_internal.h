@@ -1,0 +1,54 @@
+// Internal interface between the C ABI (ssd_api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ssd {
+
+struct ChunkArgs {
+  const void* x;
+  const float* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* dt_bias;
+  float dt_min, dt_max;
+  const float* h0;
+  void* y;
+  float* h_final;
+  int Bsz, T, H, P, G, N, chunk, dtype;
+  void* workspace;
+  hipEvent_t* events;  // NULL, or 4 events recorded around the 3 kernels
+};
+
+struct DecodeArgs {
+  float* h;
+  const float* x;
+  const float* dt;
+  const float* A;
+  const float* B;
+  const float* C;
+  const float* D;
+  const float* dt_bias;
+  float dt_min, dt_max;
+  float* y;
+  int Bsz, H, P, G, N;
+};
+
+// floats of chunk-boundary states: (Bsz, nc, H, P, KC), KC = N or 2N
+inline size_t workspace_state_floats(int Bsz, int nc, int H, int P, int KC) {
+  return static_cast<size_t>(Bsz) * nc * H * P * KC;
+}
+
+// floats of per-chunk decay factors: (Bsz, H, nc, 2)
+inline size_t workspace_decay_floats(int Bsz, int nc, int H) {
+  return static_cast<size_t>(Bsz) * H * nc * 2;
+}
+
+hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
+hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
+hipError_t run_decode(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace ssd

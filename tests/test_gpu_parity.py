@@ -1,0 +1,308 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (max over (batch, head) of the normwise relative error
+||y - y_ref||_inf / ||y_ref||_inf, same for states): 1e-4 for float32 and
+complex64 inputs, 2e-2 for bfloat16 inputs.  Small shapes are compared in
+full; the full-size workloads in the launch configuration the benchmark
+times, on sampled heads or batch rows that the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_09_amd as ssd
+from selective_state_space_09_amd import inputs
+from _metrics import y_err, state_err
+import _gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def _oracle_real(inp):
+    return oracle.fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                      inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"])
+
+
+def _oracle_cplx(inp):
+    return oracle.complex_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                              inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"])
+
+
+def _head_slice(inp, heads):
+    """Inputs restricted to some heads, each head given its own B/C group."""
+    H, G = inp["dims"]["H"], inp["dims"]["G"]
+    groups = [h // (H // G) for h in heads]
+    out = dict(inp)
+    out["x"] = np.ascontiguousarray(inp["x"][:, :, heads])
+    out["dt"] = np.ascontiguousarray(inp["dt"][:, :, heads])
+    out["A"] = np.ascontiguousarray(inp["A"][heads])
+    out["B"] = np.ascontiguousarray(inp["B"][:, :, groups])
+    out["C"] = np.ascontiguousarray(inp["C"][:, :, groups])
+    for k in ("D", "dt_bias"):
+        out[k] = None if inp[k] is None else np.ascontiguousarray(inp[k][heads])
+    out["h0"] = None if inp["h0"] is None else np.ascontiguousarray(inp["h0"][:, heads])
+    return out
+
+
+def _print_case(**kw):
+    print("case:", kw, flush=True)
+
+
+# --------------------------------------------------------------------------
+# small shapes, compared in full
+# --------------------------------------------------------------------------
+
+REAL_CASES = [
+    # Bsz, T, H, P, N, G, Q, h0, D, bias
+    (1, 256, 2, 16, 16, 1, 64, False, True, True),
+    (2, 100, 4, 32, 64, 2, 32, True, True, True),
+    (1, 257, 2, 64, 128, 1, 128, True, False, True),
+    (1, 300, 3, 64, 32, 3, 256, False, True, False),
+    (2, 65, 2, 128, 16, 1, 64, True, True, True),
+    (1, 63, 2, 16, 128, 2, 64, False, True, True),
+    (1, 1, 2, 32, 32, 1, 32, True, True, True),
+    (1, 256, 2, 64, 64, 1, 256, True, True, True),
+    (3, 513, 4, 64, 128, 1, 256, True, True, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", REAL_CASES, ids=lambda c: "B%dT%dH%dP%dN%dG%dQ%d" % c[:7])
+def test_real_small(case, dtype):
+    Bsz, T, H, P, N, G, Q, with_h0, with_D, with_bias = case
+    _print_case(kind="real", dtype=dtype, case=case)
+    inp = inputs.make_real(Bsz, T, H, P, N, G, dtype=dtype, seed=7, with_h0=with_h0,
+                           with_D=with_D, with_bias=with_bias)
+    y, hf = _gpu.run_real(inp, Q)
+    yr, hr = _oracle_real(inp)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert y_err(y, yr) < tol
+    assert state_err(hf, hr) < tol
+
+
+COMPLEX_CASES = [
+    # Bsz, T, H, P, N, G, Q, h0
+    (1, 256, 2, 16, 16, 2, 64, False),
+    (2, 100, 4, 32, 64, 4, 32, True),
+    (1, 257, 2, 64, 64, 1, 128, True),
+    (1, 300, 2, 16, 32, 2, 256, False),
+    (2, 65, 2, 128, 16, 2, 64, True),
+    (1, 1, 2, 32, 32, 2, 32, True),
+    (2, 512, 4, 64, 64, 4, 256, True),
+]
+
+
+@pytest.mark.parametrize("case", COMPLEX_CASES, ids=lambda c: "B%dT%dH%dP%dN%dG%dQ%d" % c[:7])
+def test_complex_small(case):
+    Bsz, T, H, P, N, G, Q, with_h0 = case
+    _print_case(kind="complex", case=case)
+    inp = inputs.make_complex(Bsz, T, H, P, N, G, seed=9, with_h0=with_h0)
+    y, hf = _gpu.run_complex(inp, Q)
+    yr, hr = _oracle_cplx(inp)
+    assert y_err(y, yr) < TOL_F32
+    assert state_err(hf, hr) < TOL_F32
+
+
+def test_tiny_workload_full():
+    _print_case(workload="tiny_f32")
+    cfg = inputs.WORKLOADS["tiny_f32"]
+    inp = inputs.make_workload("tiny_f32")
+    y, hf = _gpu.run_real(inp, cfg["chunk"])
+    yr, hr = _oracle_real(inp)
+    assert y_err(y, yr) < TOL_F32
+    assert state_err(hf, hr) < TOL_F32
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+def test_empty_sequence_passes_initial_state():
+    _print_case(edge="T=0")
+    inp = inputs.make_real(1, 4, 2, 16, 16, 1, seed=3, with_h0=True)
+    for k in ("x", "dt", "B", "C"):
+        inp[k] = np.ascontiguousarray(inp[k][:, :0])
+    d = _gpu.upload(inp)
+    y, hf = ssd.ssd_chunk_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dt_bias"],
+                              d["dt_min"], d["dt_max"], d["h0"], chunk=64,
+                              return_final_state=True)
+    torch.cuda.synchronize()
+    assert y.shape[1] == 0
+    np.testing.assert_array_equal(hf.cpu().numpy(), inp["h0"])
+
+
+def test_vanishing_step_freezes_state():
+    """dt -> -100 without clamp: exp(A * softplus(dt)) rounds to 1 in fp32, the
+    state carries h0 unchanged (the fp32 boundary case of the Numerical
+    Stability doc, pitfall 6) and y = C h0 + D x."""
+    _print_case(edge="frozen")
+    inp = inputs.make_real(1, 200, 2, 32, 32, 1, seed=4, with_h0=True)
+    inp["dt"] = np.full_like(inp["dt"], -100.0)
+    inp["dt_bias"] = None
+    inp["dt_min"], inp["dt_max"] = 0.0, math.inf
+    y, hf = _gpu.run_real(inp, 64)
+    np.testing.assert_array_equal(hf, inp["h0"].astype(np.float64))
+    yr, _ = _oracle_real(inp)
+    assert y_err(y, yr) < TOL_F32
+
+
+def test_deterministic():
+    _print_case(edge="determinism")
+    inp = inputs.make_real(2, 700, 4, 64, 128, 1, dtype="bf16", seed=5, with_h0=True)
+    d = _gpu.upload(inp)
+    y1, h1 = _gpu.run_real(inp, 256, dev=d)
+    y2, h2 = _gpu.run_real(inp, 256, dev=d)
+    np.testing.assert_array_equal(y1, y2)
+    np.testing.assert_array_equal(h1, h2)
+
+
+def test_chunk_size_invariance_on_gpu():
+    """The same inputs through every supported chunk size agree with the
+    oracle and with each other."""
+    _print_case(edge="chunk sweep")
+    inp = inputs.make_real(1, 333, 2, 32, 64, 1, seed=6, with_h0=True)
+    yr, hr = _oracle_real(inp)
+    for Q in (32, 64, 128, 256):
+        y, hf = _gpu.run_real(inp, Q)
+        assert y_err(y, yr) < TOL_F32, Q
+        assert state_err(hf, hr) < TOL_F32, Q
+
+
+def test_chained_calls_equal_one_call():
+    """Prefill in two calls chained through h_final -> h0 equals one call."""
+    _print_case(edge="chaining")
+    inp = inputs.make_real(1, 400, 2, 64, 64, 1, seed=8, with_h0=True)
+    y, hf = _gpu.run_real(inp, 128)
+    first = dict(inp)
+    second = dict(inp)
+    for k in ("x", "dt", "B", "C"):
+        first[k] = np.ascontiguousarray(inp[k][:, :150])
+        second[k] = np.ascontiguousarray(inp[k][:, 150:])
+    y1, h1 = _gpu.run_real(first, 128)
+    second["h0"] = h1.astype(np.float32)
+    y2, h2 = _gpu.run_real(second, 128)
+    yr, hr = _oracle_real(inp)
+    assert y_err(np.concatenate([y1, y2], axis=1), yr) < TOL_F32
+    assert state_err(h2, hr) < TOL_F32
+
+
+def test_rejects_bad_arguments_without_launch():
+    inp = inputs.make_real(1, 64, 2, 16, 16, 1, seed=1)
+    d = _gpu.upload(inp)
+    with pytest.raises(ssd.SSDError) as e:
+        ssd.ssd_chunk_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], chunk=48)
+    assert e.value.code == ssd.SSD_EUNSUPPORTED
+
+
+# --------------------------------------------------------------------------
+# full-size workloads
+# --------------------------------------------------------------------------
+
+def test_bitmamba_workload_full():
+    _print_case(workload="bitmamba_bf16")
+    cfg = inputs.WORKLOADS["bitmamba_bf16"]
+    inp = inputs.make_workload("bitmamba_bf16")
+    y, hf = _gpu.run_real(inp, cfg["chunk"])
+    yr, hr = _oracle_real(inp)
+    assert y_err(y, yr) < TOL_BF16
+    assert state_err(hf, hr) < TOL_BF16
+
+
+def test_mamba3lite_complex_workload_full():
+    _print_case(workload="mamba3lite_complex")
+    cfg = inputs.WORKLOADS["mamba3lite_complex"]
+    inp = inputs.make_workload("mamba3lite_complex")
+    y, hf = _gpu.run_complex(inp, cfg["chunk"])
+    yr, hr = _oracle_cplx(inp)
+    assert y_err(y, yr) < TOL_F32
+    assert state_err(hf, hr) < TOL_F32
+
+
+def test_long_workload_sampled_heads():
+    _print_case(workload="long_bf16")
+    cfg = inputs.WORKLOADS["long_bf16"]
+    inp = inputs.make_workload("long_bf16")
+    d = _gpu.upload(inp)
+    y, hf = ssd.ssd_chunk_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dt_bias"],
+                              d["dt_min"], d["dt_max"], None, chunk=cfg["chunk"],
+                              return_final_state=True)
+    torch.cuda.synchronize()
+    heads = [0, 17, 42, 63]
+    ys = _gpu.to_host64(y[:, :, heads].contiguous())
+    hs = _gpu.to_host64(hf[:, heads].contiguous())
+    del d, y, hf
+    sub = _head_slice(inp, heads)
+    yr, hr = _oracle_real(sub)
+    assert y_err(ys, yr) < TOL_BF16
+    assert state_err(hs, hr) < TOL_BF16
+
+
+def test_decode_workload_64_steps():
+    _print_case(workload="decode_f32")
+    cfg = inputs.WORKLOADS["decode_f32"]
+    inp = inputs.make_workload("decode_f32")
+    rows = [0, 1, 100, 255]
+    h = _gpu.to_dev(inp["h0"])
+    A, D, bias = _gpu.to_dev(inp["A"]), _gpu.to_dev(inp["D"]), _gpu.to_dev(inp["dt_bias"])
+    href = inp["h0"][rows].astype(np.float64)
+    worst_y = worst_h = 0.0
+    for k, st in enumerate(inp["steps"]):
+        x, dt, B, C = (_gpu.to_dev(st[n]) for n in ("x", "dt", "B", "C"))
+        y = ssd.ssd_step_decode(h, x, dt, A, B, C, D, bias, inp["dt_min"], inp["dt_max"])
+        torch.cuda.synchronize()
+        yr = oracle.step(href, st["x"][rows], st["dt"][rows], inp["A"], st["B"][rows],
+                         st["C"][rows], inp["D"], inp["dt_bias"], inp["dt_min"], inp["dt_max"])
+        yg = y[rows].cpu().numpy().astype(np.float64)
+        hg = h[rows].cpu().numpy().astype(np.float64)
+        ey = state_err(yg, yr)
+        eh = state_err(hg, href)
+        worst_y, worst_h = max(worst_y, ey), max(worst_h, eh)
+        assert ey < TOL_F32, (k, ey)
+        assert eh < TOL_F32, (k, eh)
+    print("decode worst errors y=%.3g h=%.3g" % (worst_y, worst_h))
+
+
+def test_decode_small_shapes():
+    for (Bsz, H, P, N, G) in [(3, 4, 16, 16, 2), (2, 2, 5, 32, 1), (1, 3, 64, 256, 3),
+                              (4, 2, 64, 64, 2)]:
+        _print_case(kind="decode", shape=(Bsz, H, P, N, G))
+        inp = inputs.make_decode(Bsz, H, P, N, G, steps=3, seed=11)
+        h = _gpu.to_dev(inp["h0"])
+        href = inp["h0"].astype(np.float64)
+        A, D, bias = _gpu.to_dev(inp["A"]), _gpu.to_dev(inp["D"]), _gpu.to_dev(inp["dt_bias"])
+        for st in inp["steps"]:
+            x, dt, B, C = (_gpu.to_dev(st[n]) for n in ("x", "dt", "B", "C"))
+            y = ssd.ssd_step_decode(h, x, dt, A, B, C, D, bias, inp["dt_min"], inp["dt_max"])
+            torch.cuda.synchronize()
+            yr = oracle.step(href, st["x"], st["dt"], inp["A"], st["B"], st["C"], inp["D"],
+                             inp["dt_bias"], inp["dt_min"], inp["dt_max"])
+            assert state_err(y.cpu().numpy(), yr) < TOL_F32
+            assert state_err(h.cpu().numpy(), href) < TOL_F32
+
+
+def test_decode_continues_forward():
+    """A chunked prefill followed by decode steps equals the oracle over the
+    whole sequence (the forward's h_final feeds the decode state)."""
+    _print_case(edge="prefill+decode")
+    inp = inputs.make_real(2, 300, 4, 64, 128, 1, seed=12, with_h0=False)
+    T0 = 290
+    pre = dict(inp)
+    for k in ("x", "dt", "B", "C"):
+        pre[k] = np.ascontiguousarray(inp[k][:, :T0])
+    _, hf = _gpu.run_real(pre, 256)
+    h = _gpu.to_dev(hf.astype(np.float32))
+    d = _gpu.upload(inp)
+    yr, hr = _oracle_real(inp)
+    for t in range(T0, 300):
+        y = ssd.ssd_step_decode(h, d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(), d["A"],
+                                d["B"][:, t].contiguous(), d["C"][:, t].contiguous(), d["D"],
+                                d["dt_bias"], inp["dt_min"], inp["dt_max"])
+        torch.cuda.synchronize()
+        assert state_err(y.cpu().numpy(), yr[:, t]) < TOL_F32
+    assert state_err(h.cpu().numpy(), hr) < TOL_F32
