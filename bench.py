@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run one plain 256 MiB device copy (reference for the HBM "
+                         "byte counters)")
     return ap.parse_args()
 
 
@@ -285,6 +288,12 @@ def main():
         "kernels": kern,
         "wall_ms_per_step_incl_flush": t_wall / args.steps * 1e3,
     }
+    if args.copy_ref:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, dims, args.cpu_seconds)
     print(json.dumps(out), flush=True)

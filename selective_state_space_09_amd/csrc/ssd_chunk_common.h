@@ -1,0 +1,274 @@
+// Shared device code of the chunked SSD kernels (gfx950): workgroup order,
+// the per-chunk prologue (step sizes and cumulative decay exponents), register
+// staging of token slabs, and the inter-chunk state-passing kernel.
+#pragma once
+
+#include <type_traits>
+
+#include "ssd_device.h"
+#include "ssd_internal.h"
+
+namespace ssd {
+
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
+constexpr int kXCD = 8;    // XCDs of an MI355X
+
+template <typename E>
+struct Pad;
+template <>
+struct Pad<uint16_t> {
+  static constexpr int row = 8;  // bf16 elements of padding per LDS row
+};
+template <>
+struct Pad<float> {
+  static constexpr int row = 4;
+};
+
+// (b, c, h) of this workgroup under the XCD-grouped order; false for the
+// padding workgroups of the last, partial group of 8 (b, c) pairs.
+__device__ __forceinline__ bool unit_of_block(int H, int nc, int npairs, int& b, int& c, int& h) {
+  const int id = blockIdx.x;
+  const int k = id / kXCD;
+  const int j = (id % kXCD) + kXCD * (k / H);
+  h = k % H;
+  if (j >= npairs) return false;
+  b = j / nc;
+  c = j % nc;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk prologue: step sizes and cumulative decay exponents.
+//
+// Thread l < Q handles token l of the chunk (l >= Lc is padding: step 0); d is
+// its raw dt (loaded by the caller, ignored for l >= Lc).  Writes dl[l] (step
+// size), cs_hi/cs_lo[l] (double-float of the inclusive cumulative exponent:
+// A*sum(delta) real, alpha*sum(delta) complex) and, for the complex form, the
+// cosine/sine of theta_l = beta * sum(delta).  Returns this thread's
+// cumulative sum (double) and stores the chunk total in *tot.
+// ---------------------------------------------------------------------------
+template <bool CPLX>
+__device__ __forceinline__ double chunk_prologue(float dt_raw, int Lc, float a_re, float a_im,
+                                                 float bias, float lo, float hi, float* dl,
+                                                 float* cs_hi, float* cs_lo, float* cth,
+                                                 float* sth, double* wsum, double* tot, int Q) {
+  const int l = threadIdx.x;
+  const float d = l < Lc ? step_size(dt_raw, bias, lo, hi) : 0.0f;
+  const double v = CPLX ? static_cast<double>(d)
+                        : static_cast<double>(a_re) * static_cast<double>(d);
+  const double cum = block_inclusive_scan(v, wsum);  // u (complex) or A*u (real)
+  if (l < Q) {
+    dl[l] = d;
+    const double e = CPLX ? static_cast<double>(a_re) * cum : cum;
+    const float ehi = static_cast<float>(e);
+    cs_hi[l] = ehi;
+    cs_lo[l] = static_cast<float>(e - static_cast<double>(ehi));
+    if (CPLX) {
+      float c, s;
+      rot_cs(static_cast<double>(a_im) * cum, c, s);
+      cth[l] = c;
+      sth[l] = s;
+    }
+    if (l == Q - 1) *tot = cum;
+  }
+  __syncthreads();
+  return cum;
+}
+
+// exp(cs_l - cs_s) from double-float exponents.
+__device__ __forceinline__ float decay_between(float hl, float ll, float hs, float ls) {
+  return __expf((hl - hs) + (ll - ls));
+}
+
+// ---------------------------------------------------------------------------
+// An ST-token slab of one row-major array, fetched into registers as 16-byte
+// vectors: item it -> rows (RPI of them) and vector v = it % VPR of those rows.
+// Rows at or past Lc read as zero.  All loads of a slab are issued together.
+// ---------------------------------------------------------------------------
+template <int ST, int VPR, int RPI>
+struct Slab {
+  static constexpr int ITEMS = (ST / RPI) * VPR;
+  static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+  uint4 v[PER][RPI];
+
+  // base: first element of token s0 = 0 of the chunk slice, in bytes;
+  // row_bytes: stride between tokens in bytes.
+  __device__ __forceinline__ void load(const char* __restrict__ base, size_t row_bytes, int s0,
+                                       int Lc) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * kThreads;
+      const int vv = it % VPR, rg = it / VPR;
+#pragma unroll
+      for (int r = 0; r < RPI; ++r) {
+        const int s = s0 + rg * RPI + r;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (it < ITEMS && s < Lc)
+          val = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(s) * row_bytes + vv * 16);
+        v[i][r] = val;
+      }
+    }
+  }
+};
+
+// x slab -> xT[p][s - s0]  (transposed, s contiguous).  bf16: item = 2 rows x
+// 8 columns, packed as (row s, row s+1) pairs per 32-bit LDS write.
+template <int ST, int P>
+struct XSlabBF : Slab<ST, P / 8, 2> {
+  __device__ __forceinline__ void store(uint16_t* xT) const {
+    constexpr int XP = ST + Pad<uint16_t>::row;
+#pragma unroll
+    for (int i = 0; i < this->PER; ++i) {
+      const int it = threadIdx.x + i * kThreads;
+      if (it >= this->ITEMS) break;
+      const int pg = it % (P / 8), sp = it / (P / 8);
+      const uint4 r0 = this->v[i][0], r1 = this->v[i][1];
+      const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
+      const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo_pair = (a[j] & 0xFFFFu) | (b[j] << 16);
+        const uint32_t hi_pair = (a[j] >> 16) | (b[j] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(xT + (pg * 8 + 2 * j) * XP + 2 * sp) = lo_pair;
+        *reinterpret_cast<uint32_t*>(xT + (pg * 8 + 2 * j + 1) * XP + 2 * sp) = hi_pair;
+      }
+    }
+  }
+};
+
+template <int ST, int P>
+struct XSlabF32 : Slab<ST, P / 4, 1> {
+  __device__ __forceinline__ void store(float* xT) const {
+    constexpr int XP = ST + Pad<float>::row;
+#pragma unroll
+    for (int i = 0; i < this->PER; ++i) {
+      const int it = threadIdx.x + i * kThreads;
+      if (it >= this->ITEMS) break;
+      const int pg = it % (P / 4), sl = it / (P / 4);
+      const uint4 u = this->v[i][0];
+      xT[(pg * 4 + 0) * XP + sl] = __uint_as_float(u.x);
+      xT[(pg * 4 + 1) * XP + sl] = __uint_as_float(u.y);
+      xT[(pg * 4 + 2) * XP + sl] = __uint_as_float(u.z);
+      xT[(pg * 4 + 3) * XP + sl] = __uint_as_float(u.w);
+    }
+  }
+};
+
+template <typename TI, int ST, int P>
+using XSlab = typename std::conditional<std::is_same<TI, uint16_t>::value, XSlabBF<ST, P>,
+                                        XSlabF32<ST, P>>::type;
+
+// ---------------------------------------------------------------------------
+// Kernel 2: inter-chunk scan of states, in place.
+//   states[b][c][h] : S_c on entry, h_in(c) on exit.
+// Real: one thread per 4 consecutive (p, n).  Complex: one thread per 4
+// consecutive n of one p, re and im together (planar re | im in the
+// workspace; h0/h_final interleaved (re, im) as complex64).
+// ---------------------------------------------------------------------------
+template <bool CPLX, int N>
+__global__ __launch_bounds__(kThreads) void ssd_pass_kernel(
+    float* __restrict__ states, const float* __restrict__ decay, const float* __restrict__ h0,
+    float* __restrict__ h_final, int H, int P, int nc) {
+  constexpr int KC = CPLX ? 2 * N : N;
+  constexpr int PF = 4;  // chunks in flight per thread
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int e4 = blockIdx.x * kThreads + threadIdx.x;  // group of 4 elements
+  const int groups = P * N / 4;
+  if (e4 >= groups) return;
+  const int p = (e4 * 4) / N, n = (e4 * 4) % N;
+  const size_t chunk_stride = static_cast<size_t>(H) * P * KC;
+  float* base = states + (static_cast<size_t>(b) * nc * H + h) * (static_cast<size_t>(P) * KC) +
+                static_cast<size_t>(p) * KC + n;
+  const float* dc = decay + (static_cast<size_t>(b) * H + h) * nc * 2;
+  const size_t pub = ((static_cast<size_t>(b) * H + h) * P + p) * N + n;  // public (p, n) index
+
+  float4 hr = make_float4(0.f, 0.f, 0.f, 0.f), hi = hr;
+  if (h0) {
+    if (CPLX) {
+      const float4* src = reinterpret_cast<const float4*>(h0 + pub * 2);
+      const float4 u = src[0], v = src[1];
+      hr = make_float4(u.x, u.z, v.x, v.z);
+      hi = make_float4(u.y, u.w, v.y, v.w);
+    } else {
+      hr = *reinterpret_cast<const float4*>(h0 + pub);
+    }
+  }
+
+  float4 cur_r[PF], cur_i[PF];
+  float2 cur_d[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    if (j < nc) {
+      cur_r[j] = *reinterpret_cast<const float4*>(base + j * chunk_stride);
+      if (CPLX) cur_i[j] = *reinterpret_cast<const float4*>(base + j * chunk_stride + N);
+      cur_d[j] = *reinterpret_cast<const float2*>(dc + 2 * j);
+    }
+  }
+  for (int c0 = 0; c0 < nc; c0 += PF) {
+    float4 nxt_r[PF], nxt_i[PF];
+    float2 nxt_d[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int cn = c0 + PF + j;
+      if (cn < nc) {
+        nxt_r[j] = *reinterpret_cast<const float4*>(base + cn * chunk_stride);
+        if (CPLX) nxt_i[j] = *reinterpret_cast<const float4*>(base + cn * chunk_stride + N);
+        nxt_d[j] = *reinterpret_cast<const float2*>(dc + 2 * cn);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int cc = c0 + j;
+      if (cc < nc) {
+        float* slot = base + cc * chunk_stride;
+        *reinterpret_cast<float4*>(slot) = hr;
+        if (CPLX) {
+          *reinterpret_cast<float4*>(slot + N) = hi;
+          const float dr = cur_d[j].x, di = cur_d[j].y;
+          const float4 sr = cur_r[j], si = cur_i[j];
+          float4 nr, ni;
+          nr.x = dr * hr.x - di * hi.x + sr.x;
+          nr.y = dr * hr.y - di * hi.y + sr.y;
+          nr.z = dr * hr.z - di * hi.z + sr.z;
+          nr.w = dr * hr.w - di * hi.w + sr.w;
+          ni.x = dr * hi.x + di * hr.x + si.x;
+          ni.y = dr * hi.y + di * hr.y + si.y;
+          ni.z = dr * hi.z + di * hr.z + si.z;
+          ni.w = dr * hi.w + di * hr.w + si.w;
+          hr = nr;
+          hi = ni;
+        } else {
+          const float d = cur_d[j].x;
+          const float4 s = cur_r[j];
+          hr = make_float4(d * hr.x + s.x, d * hr.y + s.y, d * hr.z + s.z, d * hr.w + s.w);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      cur_r[j] = nxt_r[j];
+      if (CPLX) cur_i[j] = nxt_i[j];
+      cur_d[j] = nxt_d[j];
+    }
+  }
+  if (h_final) {
+    if (CPLX) {
+      float4* dst = reinterpret_cast<float4*>(h_final + pub * 2);
+      dst[0] = make_float4(hr.x, hi.x, hr.y, hi.y);
+      dst[1] = make_float4(hr.z, hi.z, hr.w, hi.w);
+    } else {
+      *reinterpret_cast<float4*>(h_final + pub) = hr;
+    }
+  }
+}
+
+// launch of the inter-chunk scan for one shape
+template <bool CPLX, int N>
+inline void launch_pass(float* states, const float* decay, const float* h0, float* h_final,
+                        int Bsz, int H, int P, int nc, hipStream_t st) {
+  const int groups = P * N / 4;
+  dim3 grid((groups + kThreads - 1) / kThreads, H, Bsz);
+  ssd_pass_kernel<CPLX, N><<<grid, kThreads, 0, st>>>(states, decay, h0, h_final, H, P, nc);
+}
+
+}  // namespace ssd

@@ -18,16 +18,19 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// float32 -> bfloat16, round to nearest, ties to even (finite inputs).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// float32 -> bfloat16 by the hardware conversion (v_cvt_pk_bf16_f32: round
+// to nearest, ties to even, in the default rounding mode).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
@@ -50,6 +53,14 @@ __device__ __forceinline__ float step_size(float dt, float bias, float lo, float
   const float z = dt + bias;
   const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
   return fminf(fmaxf(sp, lo), hi);
+}
+
+// Index of this wave in the workgroup, as a wave-uniform (scalar) value, so
+// that branches on it compile to scalar branches with every lane active.
+// (The gfx950 LDS transpose read exchanges data across lanes and must not run
+// under a partial or empty EXEC mask.)
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
 }
 
 // Inclusive prefix sum of one double per thread over a 256-thread block.

@@ -48,6 +48,7 @@ inline size_t workspace_decay_floats(int Bsz, int nc, int H) {
 }
 
 hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
+hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st);
 
