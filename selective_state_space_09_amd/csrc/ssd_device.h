@@ -89,6 +89,22 @@ __device__ __forceinline__ void rot_cs(double ang, float& c, float& s) {
   sincosf(static_cast<float>(r), &s, &c);
 }
 
+// Raw buffer access (gfx9 buffer descriptor, dword3 0x00020000): offsets are
+// bytes from `base`; loads at or past `bytes` return zero and stores there are
+// dropped, which bounds every access to the described range.
+typedef __amdgpu_buffer_rsrc_t buf_t;
+__device__ __forceinline__ buf_t make_buf(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(buf_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(buf_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                         r, off, 0, 0);
+}
+
 // MFMA wrappers (gfx950).  Operand layouts for the 16x16 forms, lane i,
 // q = i / 16:  A holds row i % 16, B holds column i % 16, and the k values
 // of a lane are k-group q; the accumulator holds column i % 16, rows

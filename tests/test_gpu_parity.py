@@ -306,3 +306,33 @@ def test_decode_continues_forward():
         torch.cuda.synchronize()
         assert state_err(y.cpu().numpy(), yr[:, t]) < TOL_F32
     assert state_err(h.cpu().numpy(), hr) < TOL_F32
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_steep_decay(dtype):
+    """Decay of about e^-11 per token (A = -16, steps up to 1): the decay over
+    half a 64-token sub-chunk leaves the range of the factored form, and the
+    bf16 output kernel runs those chunks in its exact mode."""
+    _print_case(edge="steep decay", dtype=dtype)
+    inp = inputs.make_real(2, 300, 4, 64, 128, 1, dtype=dtype, seed=13, with_h0=True)
+    inp["A"] = np.full_like(inp["A"], -16.0)
+    inp["dt_bias"] = np.zeros_like(inp["dt_bias"])
+    inp["dt_min"], inp["dt_max"] = 1e-3, 1.0
+    y, hf = _gpu.run_real(inp, 256)
+    yr, hr = _oracle_real(inp)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert y_err(y, yr) < tol
+    assert state_err(hf, hr) < tol
+
+
+def test_mixed_decay_modes():
+    """Chunks with gentle and with steep decay in one call (the bf16 output
+    kernel picks its mode per chunk)."""
+    _print_case(edge="mixed decay")
+    inp = inputs.make_real(1, 512, 2, 64, 64, 1, dtype="bf16", seed=14, with_h0=True)
+    inp["dt_min"], inp["dt_max"] = 1e-3, 1.0
+    inp["dt"][:, 256:] += 4.0  # second chunk: steps near 1, steep decay
+    y, hf = _gpu.run_real(inp, 256)
+    yr, hr = _oracle_real(inp)
+    assert y_err(y, yr) < TOL_BF16
+    assert state_err(hf, hr) < TOL_BF16
