@@ -3,8 +3,9 @@
 Default workload: the BitMamba-1B Mamba-2 layer shape -- batch 2, T 2048,
 64 heads, head dim 64, state 128, one B/C group, chunk 256, bf16 x/B/C with
 fp32 dt/A/state -- on seeded synthetic inputs.  One step = one call of
-ssd_chunk_fwd over the whole batch (all three kernels: chunk states,
-inter-chunk scan, chunk outputs).
+ssd_chunk_fwd over the whole batch (every kernel of the call: for bf16 the
+chunk-state walk and the chunk outputs; for fp32 and complex the chunk
+states, the inter-chunk scan and the chunk outputs).
 
 Timing: HIP events recorded by the library on the launch stream around each
 kernel of every timed step; ms_per_step is the mean of the per-step event
@@ -84,6 +85,16 @@ class Hip:
         return ms.value
 
 
+def kernel_segments(cfg):
+    """Kernels of one chunked-forward call and the event pair around each:
+    the bf16 real path walks the chunk states in one kernel; the fp32 and
+    complex paths compute chunk states, pass them between chunks, then the
+    outputs."""
+    if cfg["kind"] == "real" and cfg.get("dtype") == "bf16":
+        return {"ssd_walk_bf16_kernel": (0, 1), "ssd_scan_bf16_kernel": (2, 3)}
+    return {"ssd_state_kernel": (0, 1), "ssd_pass_kernel": (1, 2), "ssd_scan_kernel": (2, 3)}
+
+
 def kernel_bytes(cfg, dims):
     """Algorithmic HBM bytes of each kernel of one chunked-forward call: every
     array the kernel must read or write, counted once."""
@@ -99,7 +110,10 @@ def kernel_bytes(cfg, dims):
     states = Bsz * nc * H * P * KC * 4
     decay = Bsz * H * nc * 8
     y = Bsz * T * H * P * (4 if cplx else es)
+    hin16 = Bsz * nc * H * P * N * 2                      # bf16 boundary states
     return {
+        "ssd_walk_bf16_kernel": x + bc + dt + hin16,
+        "ssd_scan_bf16_kernel": x + 2 * bc + dt + hin16 + y,
         "ssd_state_kernel": x + bc + dt + states + decay,
         "ssd_pass_kernel": 2 * states + decay,
         "ssd_scan_kernel": x + 2 * bc + dt + states + y,
@@ -116,7 +130,8 @@ def kernel_flops(cfg, dims):
     tri = Q * (Q + 1) / 2
     scan = units * (2 * tri * KC + 2 * tri * P + 2 * Q * KC * P)
     state = units * 2 * Q * KC * P
-    return {"ssd_scan_kernel": scan, "ssd_state_kernel": state}
+    return {"ssd_scan_kernel": scan, "ssd_state_kernel": state,
+            "ssd_scan_bf16_kernel": scan, "ssd_walk_bf16_kernel": state}
 
 
 def cpu_baseline(inp, cfg, dims, target_s):
@@ -241,13 +256,14 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
 
-    names = ["ssd_state_kernel", "ssd_pass_kernel", "ssd_scan_kernel"]
+    segs = kernel_segments(cfg)
+    names = list(segs)
     per_step, per_kernel = [], {n: [] for n in names}
     for i in range(args.warmup, n_total):
         e = evs[i]
         per_step.append(hip.elapsed_ms(e[0], e[3]))
-        for k, n in enumerate(names):
-            per_kernel[n].append(hip.elapsed_ms(e[k], e[k + 1]))
+        for n, (k0, k1) in segs.items():
+            per_kernel[n].append(hip.elapsed_ms(e[k0], e[k1]))
     ms = float(np.mean(per_step))
     tokens = Bsz * T
     value = tokens / (ms / 1e3)

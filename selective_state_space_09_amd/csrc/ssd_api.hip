@@ -56,6 +56,15 @@ int check_chunk_shape(int Bsz, int T, int H, int P, int G, int N, int chunk, int
   const long long nc = (static_cast<long long>(T) + chunk - 1) / chunk;
   if (nc > 2147483647LL || static_cast<long long>(H) > 65535 || Bsz > 65535)
     return fail(SSD_EUNSUPPORTED, "grid too large: nc=%lld H=%d Bsz=%d", nc, H, Bsz);
+  // 1-D grids: (b, chunk) pairs rounded to whole XCD groups, times H
+  const long long pairs = (Bsz * nc + 7) / 8 * 8;
+  if (pairs * H > 2147483647LL)
+    return fail(SSD_EUNSUPPORTED, "grid too large: Bsz*nc*H = %lld workgroups", pairs * H);
+  // one chunk's token rows are addressed by 32-bit byte offsets
+  if (static_cast<long long>(chunk) * H * P * 4 > 4294967295LL ||
+      static_cast<long long>(chunk) * G * N * 8 > 4294967295LL)
+    return fail(SSD_EUNSUPPORTED, "one chunk's rows exceed 4 GiB: chunk=%d H=%d P=%d G=%d N=%d",
+                chunk, H, P, G, N);
   return SSD_OK;
 }
 

@@ -80,6 +80,26 @@ __device__ __forceinline__ double block_inclusive_scan(double v, double* wsum) {
   return v + add;
 }
 
+// Inclusive prefix sum of one float per lane over a wave, by DPP lane moves
+// (the gfx9 pattern: row shifts by 1, 2, 4, 8 inside rows of 16 lanes, then
+// the broadcasts of lane 15 and lane 31 into the upper rows).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15;
+  float t;
+  t = dpp_mov<0x111>(v); if (r >= 1) v += t;   // row_shr:1
+  t = dpp_mov<0x112>(v); if (r >= 2) v += t;   // row_shr:2
+  t = dpp_mov<0x114>(v); if (r >= 4) v += t;   // row_shr:4
+  t = dpp_mov<0x118>(v); if (r >= 8) v += t;   // row_shr:8
+  t = dpp_mov<0x142>(v); if ((lane & 31) >= 16) v += t;  // row_bcast:15
+  t = dpp_mov<0x143>(v); if (lane >= 32) v += t;         // row_bcast:31
+  return v;
+}
+
 // cos/sin of an angle given in double: reduced to [-pi, pi] in double, then
 // evaluated in float.  Angles of a 256-token chunk reach ~80 rad; reducing in
 // float would cost ~1e-5 rad of phase.
@@ -99,6 +119,13 @@ __device__ __forceinline__ buf_t make_buf(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ uint4 buf_load16(buf_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buf_load8(buf_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(buf_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v),
+                                        r, off, 0, 0);
 }
 __device__ __forceinline__ void buf_store16(buf_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
