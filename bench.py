@@ -3,15 +3,16 @@
 Default workload: the BitMamba-1B Mamba-2 layer shape -- batch 2, T 2048,
 64 heads, head dim 64, state 128, one B/C group, chunk 256, bf16 x/B/C with
 fp32 dt/A/state -- on seeded synthetic inputs.  One step = one call of
-ssd_chunk_fwd over the whole batch (every kernel of the call: for bf16 the
-chunk-state walk and the chunk outputs; for fp32 and complex the chunk
-states, the inter-chunk scan and the chunk outputs).
+ssd_chunk_fwd over the whole batch (every kernel of the call: chunk states,
+the state passing between chunks, chunk outputs).
 
 Timing: HIP events recorded by the library on the launch stream around each
 kernel of every timed step; ms_per_step is the mean of the per-step event
-intervals.  Between steps a 512 MiB buffer is rewritten (outside the timed
-intervals) so that the 256 MB Infinity Cache holds none of the step's inputs:
-the number is the rate with inputs resident in HBM.
+intervals.  Between steps a 512 MiB buffer is read (outside the timed
+intervals) so that the 256 MB Infinity Cache and the L2s hold none of the
+step's inputs: the number is the rate with inputs resident in HBM.  The flush
+reads rather than writes: a written flush would leave the cache full of dirty
+lines whose write-back the next step's first kernel would pay for.
 
 Prints one JSON line (rank 0): metric, value (tokens/s), roofline of the
 dominant kernel, and the float64 CPU oracle timed on a bounded sample.
@@ -87,11 +88,10 @@ class Hip:
 
 def kernel_segments(cfg):
     """Kernels of one chunked-forward call and the event pair around each:
-    the bf16 real path walks the chunk states in one kernel; the fp32 and
-    complex paths compute chunk states, pass them between chunks, then the
-    outputs."""
+    chunk states, the state passing between chunks, then the outputs."""
     if cfg["kind"] == "real" and cfg.get("dtype") == "bf16":
-        return {"ssd_walk_bf16_kernel": (0, 1), "ssd_scan_bf16_kernel": (2, 3)}
+        return {"ssd_state_bf16_kernel": (0, 1), "ssd_pass_bf16_kernel": (1, 2),
+                "ssd_scan_bf16_kernel": (2, 3)}
     return {"ssd_state_kernel": (0, 1), "ssd_pass_kernel": (1, 2), "ssd_scan_kernel": (2, 3)}
 
 
@@ -110,10 +110,12 @@ def kernel_bytes(cfg, dims):
     states = Bsz * nc * H * P * KC * 4
     decay = Bsz * H * nc * 8
     y = Bsz * T * H * P * (4 if cplx else es)
-    hin16 = Bsz * nc * H * P * N * 2                      # bf16 boundary states
+    st16 = Bsz * nc * H * P * N * 2                       # bf16 chunk / boundary states
+    dec = Bsz * H * nc * 4
     return {
-        "ssd_walk_bf16_kernel": x + bc + dt + hin16,
-        "ssd_scan_bf16_kernel": x + 2 * bc + dt + hin16 + y,
+        "ssd_state_bf16_kernel": x + bc + dt + st16 + dec,
+        "ssd_pass_bf16_kernel": 2 * st16 + dec,
+        "ssd_scan_bf16_kernel": x + 2 * bc + dt + st16 + y,
         "ssd_state_kernel": x + bc + dt + states + decay,
         "ssd_pass_kernel": 2 * states + decay,
         "ssd_scan_kernel": x + 2 * bc + dt + states + y,
@@ -131,7 +133,7 @@ def kernel_flops(cfg, dims):
     scan = units * (2 * tri * KC + 2 * tri * P + 2 * Q * KC * P)
     state = units * 2 * Q * KC * P
     return {"ssd_scan_kernel": scan, "ssd_state_kernel": state,
-            "ssd_scan_bf16_kernel": scan, "ssd_walk_bf16_kernel": state}
+            "ssd_scan_bf16_kernel": scan, "ssd_state_bf16_kernel": state}
 
 
 def cpu_baseline(inp, cfg, dims, target_s):
@@ -215,7 +217,7 @@ def main():
     y = torch.empty((Bsz, T, H, P), dtype=torch.float32 if cplx else d["x"].dtype, device=dev)
     nbytes = ssd.ssd_workspace_size(Bsz, T, H, P, G, N, Q, cplx)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.int32, device=dev)
     L = ssd.lib()
     hip = Hip()
     stream = torch.cuda.current_stream()
@@ -242,7 +244,7 @@ def main():
 
     def step(i):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            flush.max()  # reads 512 MiB: evicts the inputs, leaves clean lines
         rc = call(ev_arrays[i])
         if rc != 0:
             raise RuntimeError(L.ssd_last_error().decode())

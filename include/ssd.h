@@ -81,8 +81,9 @@ const char *ssd_last_error(void);
  * Bytes of device workspace ssd_chunk_fwd (is_complex = 0) or
  * ssd_complex_chunk_fwd (is_complex = 1) needs for these sizes: room for the
  * chunk-boundary states as fp32, (Bsz, nc, H, P, N) real or (Bsz, nc, H, P, 2N)
- * complex with nc = ceil(T / chunk), plus one decay factor per (b, h, chunk).
- * (The bf16 real path keeps its boundary states as bf16 and uses less of it.)
+ * complex with nc = ceil(T / chunk), plus one decay factor per (b, h, chunk),
+ * plus for the real form one (exponent, step size) float pair per token and
+ * head.  (The bf16 real path keeps its chunk and boundary states as bf16.)
  * Returns 0 for sizes the library rejects, among them any whose 1-D grid
  * would exceed 2^31 - 1 workgroups (ceil(Bsz * nc / 8) * 8 * H) or whose
  * chunk of token rows exceeds 4 GiB (chunk * H * P * 4 or chunk * G * N * 8).
@@ -136,10 +137,7 @@ int ssd_complex_chunk_fwd(const float *x, const float *dt, const float *A,
  * kernels and results, plus `events`, an array of 4 hipEvent_t (passed as
  * void*) recorded on `stream` before the chunk-state kernel, after it, after
  * the inter-chunk scan and after the output kernel; or NULL (then they are
- * the plain calls).  The bf16 real path has no separate inter-chunk scan (its
- * chunk-state kernel walks the chunks in order and writes the boundary
- * states itself): its events 1 and 2 are recorded back to back.  The caller
- * creates and owns the events.
+ * the plain calls).  The caller creates and owns the events.
  */
 int ssd_chunk_fwd_ev(const void *x, const float *dt, const float *A,
                      const void *B, const void *C, const float *D,

@@ -1,9 +1,9 @@
 // Chunked SSD forward on gfx950 for bfloat16 x, B, C (real Mamba-2 form; fp32
-// state and accumulation), in two kernels:
-//   ssd_walk_bf16_kernel  chunk-boundary states h_in(c) and the final state:
-//                         each workgroup walks the chunks of one (batch, head,
-//                         state-column group) in order;
-//   ssd_scan_bf16_kernel  chunk outputs from h_in(c), per (batch, chunk, head).
+// state and accumulation), in three kernels:
+//   ssd_state_bf16_kernel  each chunk's own state S_c and decay, per (batch,
+//                          chunk, head);
+//   ssd_pass_bf16_kernel   the boundary states h_in(c) and the final state;
+//   ssd_scan_bf16_kernel   chunk outputs from h_in(c), per (batch, chunk, head).
 // (Numerical Stability in Mamba-3-Lite, section 4: the chunkwise form with
 // L[l,s] = exp(cs_l - cs_s) 1[l >= s] inside a chunk and the chunk's total
 // log-decay carrying the state from one chunk to the next.)
@@ -43,187 +43,226 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
 }
 
 // ---------------------------------------------------------------------------
-// Chunk-boundary states, walked.  One workgroup per (batch, head, group of NG
-// state columns) runs through the chunks in order with the running state in
-// MFMA accumulators; for chunk c it writes h_in(c) and then advances
-//   h <- e^{A u_c} h + sum_s x_s (e^{A (u_c - u_s)} delta_s B_s)^T,
-// u_s = delta_1 + .. + delta_s, u_c the chunk total (the chunk's state from a
-// zero start on MFMA, contraction over the chunk's tokens, plus the decayed
-// carry: the chunkwise recurrence of the state-passing step).  After the
-// last chunk it writes the final state (fp32).  Chunk c+1's x, B and dt are
-// in flight while chunk c computes.  The column groups of one (batch, head)
-// are dispatched to one XCD, so x comes from HBM once and from that XCD's L2
-// for the other groups; the decay weights go onto this group's B columns,
-// so no group rescales the shared x.
-//
-// The exponent sums here are fp32 (a wave DPP scan): a sum of at most 256
-// positive steps carries a relative error of ~1e-6, far below the bf16
-// rounding of the weighted B.  The boundary states are stored as bf16: the
-// output kernel rounds the carried state to bf16 for its MFMA in any case.
-//
-// Tiles are transposed (D[n][p] = sum_s B~_s[n] x_s[p]): an accumulator lane
-// holds column p and four consecutive n, which is one 8-byte store of the
-// [p][n] state layout.
+// Chunk states from a zero start, one workgroup per (batch, chunk, head):
+//   S_c[p][n] = sum_s x_s[p] e^{A (u_c - u_s)} delta_s B_s[n],
+//   lambda_c  = e^{A u_c},
+// u_s = delta_1 + .. + delta_s over the chunk and u_c its total (the chunk's
+// own contribution to the state at its end, and its decay; the state-passing
+// kernel chains them).  The chunk is staged through LDS in two halves of up
+// to 128 tokens; both halves are loaded into registers at the start.  The
+// decay weight goes onto x (P columns) as it is staged.  Eight waves; wave w
+// owns n tiles 2(w%4), 2(w%4)+1 and p tiles 2(w/4), 2(w/4)+1 of the
+// transposed product D[n][p] = sum_s B_s[n] (w_s x_s[p]), so an accumulator
+// lane holds one p and four consecutive n: one 8-byte store of S_c (bf16;
+// the output kernel rounds the carried state to bf16 for its MFMA in any
+// case).  The exponent sums are fp32 (a wave DPP scan): a sum of at most 256
+// positive steps carries a relative error of ~1e-6.
 // ---------------------------------------------------------------------------
-template <int P, int N, int NG>
-__global__ __launch_bounds__(kThreads) void ssd_walk_bf16_kernel(
+template <int P, int N>
+__global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min,
-    float dt_max, const float* __restrict__ h0, uint16_t* __restrict__ hin,
-    float* __restrict__ h_final, int Bsz, int T, int H, int G, int Q, int nc) {
-  constexpr int NGRP = N / NG;
-  constexpr int QM = 256;               // largest chunk
-  constexpr int XPn = P + 16, BPn = NG + 16;
-  constexpr int PT = P / 16, NT = NG / 16;
-  constexpr int TILES = PT * NT;
-  constexpr int TPW = (TILES + 3) / 4;  // tiles per wave: tile = wave + 4 i
+    float dt_max, uint16_t* __restrict__ states, float* __restrict__ decay,
+    float2* __restrict__ tok, int T, int H, int G, int Q, int nc, int npairs) {
+  constexpr int NTHR = 512, WW = 8;
+  constexpr int HS = 128;                   // tokens per staged half
+  constexpr int XPn = P + 16, BPn = N + 16;  // pitches (bf16 elements)
+  constexpr int PT = P / 16, NT = N / 16;
+  // wave tile block: NTW n tiles x PTW p tiles
+  constexpr int NTW = NT >= 8 ? NT / 4 : (NT >= 2 ? 2 : 1);
+  constexpr int NGW = NT / NTW;             // wave groups along n
+  constexpr int PGW = WW / NGW;             // wave groups along p
+  constexpr int PTW = (PT + PGW - 1) / PGW;
 
-  __shared__ __attribute__((aligned(16))) uint16_t xt[QM * XPn];  // x_s
-  __shared__ __attribute__((aligned(16))) uint16_t bq[QM * BPn];  // w_s B_s, this column group
-  __shared__ __attribute__((aligned(16))) float wsc[QM];
-  __shared__ float wpart[4];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[HS * XPn];  // w_s x_s
+  __shared__ __attribute__((aligned(16))) uint16_t bl[HS * BPn];  // B_s
+  __shared__ __attribute__((aligned(16))) float wsc[256];
+  __shared__ float wpart[WW];
 
-  // workgroup -> (b, h, column group): groups of one (b, h) on one XCD
-  const int id = blockIdx.x;
-  const int k = id / kXCD;
-  const int unit = (id % kXCD) + kXCD * (k / NGRP);
-  const int gn = k % NGRP;
-  if (unit >= Bsz * H) return;
-  const int b = unit / H, h = unit % H;
+  int b, c, h;
+  if (!unit_of_block(H, nc, npairs, b, c, h)) return;
   const int g = h / (H / G);
-  const int n0 = gn * NG;
+  const int t0 = c * Q;
+  const int Lc = min(Q, T - t0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wid = wave_id();
+  const int ng = wid % NGW, pg = wid / NGW;
+
+  // ---- loads: dt first, then both halves of x and B ----
+  const size_t r0 = static_cast<size_t>(b) * T + t0;
+  const float dtv = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
+  const uint32_t xrow = static_cast<uint32_t>(H) * P * 2;
+  const uint32_t brow = static_cast<uint32_t>(G) * N * 2;
+  const buf_t xbuf = make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
+                              static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+  const buf_t bbuf = make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N,
+                              static_cast<uint32_t>(Lc - 1) * brow + N * 2);
+  BufSlab<HS, P / 8, NTHR> xs0, xs1;
+  BufSlab<HS, N / 8, NTHR> bs0, bs1;
+  const bool two = Q > HS;
+  xs0.load(xbuf, xrow, 0);
+  bs0.load(bbuf, brow, 0);
+  if (two) {
+    xs1.load(xbuf, xrow, HS);
+    bs1.load(bbuf, brow, HS);
+  }
   const float a_re = A[h];
   const float bias = dt_bias ? dt_bias[h] : 0.0f;
 
-  const uint32_t xrow = static_cast<uint32_t>(H) * P * 2;
-  const uint32_t brow = static_cast<uint32_t>(G) * N * 2;
-  BufSlab<QM, P / 8> xs;
-  BufSlab<QM, NG / 8> bs;
-  float dtv = 0.0f;
-  // chunk c's rows into registers (rows at or past the chunk's end read 0)
-  // (dt first: the next chunk's scan waits for it alone, the in-order load
-  // counter then leaves x and B in flight)
-  auto prefetch = [&](int c) {
-    const int t0 = c * Q, Lc = min(Q, T - t0);
-    const size_t r0 = static_cast<size_t>(b) * T + t0;
-    dtv = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
-    xs.load(make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
-                     static_cast<uint32_t>(Lc - 1) * xrow + P * 2), xrow, 0);
-    bs.load(make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N + n0,
-                     static_cast<uint32_t>(Lc - 1) * brow + NG * 2), brow, 0);
-  };
-
-  // running state: lane holds column p = pt*16 + r16, rows n = n0 + nt*16 + 4q + j
-  const size_t pub = (static_cast<size_t>(b) * H + h) * P * N;  // h0 / h_final slice
-  f32x4 hacc[TPW];
+  // ---- step sizes and running sums (thread s = token s) ----
+  const float d = tid < Lc ? step_size(dtv, bias, dt_min, dt_max) : 0.0f;
+  float u = wave_inclusive_sum(d);
+  if (lane == kWave - 1) wpart[wid] = u;
+  __syncthreads();
+  float before = 0.0f, total = 0.0f;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int tile = wid + 4 * i;
-    const int nt = tile % NT, pt = tile / NT;
-    hacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (h0 && tile < TILES)
-      hacc[i] = *reinterpret_cast<const f32x4*>(h0 + pub + (pt * 16 + r16) * N + n0 + nt * 16 + 4 * q);
+  for (int w = 0; w < WW; ++w) {
+    const float pw = wpart[w];
+    before += w < wid ? pw : 0.0f;
+    total += pw;
   }
+  u += before;
+  if (tid < 256) wsc[tid] = __expf(a_re * (total - u)) * d;
+  if (tid == 0) decay[(static_cast<size_t>(b) * H + h) * nc + c] = __expf(a_re * total);
+  // (A u_l, delta_l) of every token for the output kernel (padding: delta 0)
+  if (tid < Q) tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid] = make_float2(a_re * u, d);
+  __syncthreads();
 
-  // rows Q..127 of the tiles stay zero (the MFMA groups run over 128 rows)
-  for (int it = tid; it < (128 - min(Q, 128)) * (XPn + BPn) / 8; it += kThreads) {
-    const int r = it / ((XPn + BPn) / 8), v = it % ((XPn + BPn) / 8);
-    uint16_t* row = v < XPn / 8 ? xt + (Q + r) * XPn + v * 8 : bq + (Q + r) * BPn + (v - XPn / 8) * 8;
-    *reinterpret_cast<uint4*>(row) = make_uint4(0, 0, 0, 0);
-  }
-
-  if (nc > 0) prefetch(0);
-  for (int c = 0; c < nc; ++c) {
-    const int Lc = min(Q, T - c * Q);
-    // step sizes and their running sums u_s over the chunk (thread s = token s)
-    const float d = tid < Lc ? step_size(dtv, bias, dt_min, dt_max) : 0.0f;
-    float u = wave_inclusive_sum(d);
-    if (lane == kWave - 1) wpart[wid] = u;
-    __syncthreads();  // (also: every wave is done with the previous chunk's tiles)
-    float before = 0.0f, total = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float pw = wpart[w];
-      before += w < wid ? pw : 0.0f;
-      total += pw;
-    }
-    u += before;
-    wsc[tid] = __expf(a_re * (total - u)) * d;
-    const float lam = __expf(a_re * total);
+  // half -> LDS (x scaled by w_s; rows past the chunk are zero)
+  auto stage = [&](const BufSlab<HS, P / 8, NTHR>& xs, const BufSlab<HS, N / 8, NTHR>& bs, int s0) {
 #pragma unroll
     for (int i = 0; i < xs.PER; ++i) {
-      const int it = tid + i * kThreads;
-      const int v = it % (P / 8), s = it / (P / 8);
-      if ((xs.ITEMS % kThreads == 0 || it < xs.ITEMS) && s < Q)
-        *reinterpret_cast<uint4*>(xt + s * XPn + v * 8) = xs.v[i];
+      const int it = tid + i * NTHR;
+      const int v = it % (P / 8), sl = it / (P / 8);
+      if (xs.ITEMS % NTHR == 0 || it < xs.ITEMS)
+        *reinterpret_cast<uint4*>(xl + sl * XPn + v * 8) =
+            scale_bf16x8(xs.v[i], s0 + sl < Q ? wsc[s0 + sl] : 0.0f);
     }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < bs.PER; ++i) {
-      const int it = tid + i * kThreads;
-      const int v = it % (NG / 8), s = it / (NG / 8);
-      if ((bs.ITEMS % kThreads == 0 || it < bs.ITEMS) && s < Q)
-        *reinterpret_cast<uint4*>(bq + s * BPn + v * 8) = scale_bf16x8(bs.v[i], wsc[s]);
+      const int it = tid + i * NTHR;
+      const int v = it % (N / 8), sl = it / (N / 8);
+      if (bs.ITEMS % NTHR == 0 || it < bs.ITEMS)
+        *reinterpret_cast<uint4*>(bl + sl * BPn + v * 8) = bs.v[i];
     }
-    // h_in(c), bf16 -- issued after this chunk's loads are consumed and before
-    // the next chunk's are issued: the in-order load/store counter then never
-    // holds a prefetch behind a wait on these stores
-    uint16_t* dst = hin + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N);
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tile = wid + 4 * i;
-      if (tile >= TILES) break;
-      const int nt = tile % NT, pt = tile / NT;
-      *reinterpret_cast<uint2*>(dst + (pt * 16 + r16) * N + n0 + nt * 16 + 4 * q) =
-          make_uint2(pack_bf16x2(hacc[i][0], hacc[i][1]), pack_bf16x2(hacc[i][2], hacc[i][3]));
-    }
-    if (c + 1 < nc) prefetch(c + 1);
-    __syncthreads();
+  };
 
-    // chunk state on MFMA, 128 tokens (4 k-steps) per group: every operand
-    // read of a group is issued before its MFMAs (rows Q..127 are zero)
-    f32x4 sacc[TPW];
+  f32x4 acc[NTW][PTW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb < Q; kb += 128) {
-      uint4 af[4][TPW], bf[4][TPW];
+  for (int i = 0; i < NTW; ++i)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ks = kb + 32 * kk;
+    for (int j = 0; j < PTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one half on MFMA: contraction over its tokens, all operand reads of a
+  // 32-token step issued before the step's MFMAs
+  auto mma = [&](int rows) {
+    for (int ks = 0; ks < rows; ks += 32) {
+      uint4 af[NTW], bf[PTW];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          const int tile = wid + 4 * i;
-          const int nt = (tile < TILES ? tile : 0) % NT, pt = (tile < TILES ? tile : 0) / NT;
-          const uint2 alo = lds_tr4(bq, BPn, ks + 8 * q, nt * 16);
-          const uint2 ahi = lds_tr4(bq, BPn, ks + 8 * q + 4, nt * 16);
-          const uint2 blo = lds_tr4(xt, XPn, ks + 8 * q, pt * 16);
-          const uint2 bhi = lds_tr4(xt, XPn, ks + 8 * q + 4, pt * 16);
-          af[kk][i] = make_uint4(alo.x, alo.y, ahi.x, ahi.y);
-          bf[kk][i] = make_uint4(blo.x, blo.y, bhi.x, bhi.y);
-        }
+      for (int i = 0; i < NTW; ++i) {
+        const int nt = ng * NTW + i;
+        const uint2 lo = lds_tr4(bl, BPn, ks + 8 * q, nt * 16);
+        const uint2 hi = lds_tr4(bl, BPn, ks + 8 * q + 4, nt * 16);
+        af[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int j = 0; j < PTW; ++j) {
+        const int pt = pg * PTW + j < PT ? pg * PTW + j : 0;
+        const uint2 lo = lds_tr4(xl, XPn, ks + 8 * q, pt * 16);
+        const uint2 hi = lds_tr4(xl, XPn, ks + 8 * q + 4, pt * 16);
+        bf[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
 #pragma unroll
-        for (int i = 0; i < TPW; ++i)
-          if (wid + 4 * i < TILES)
-            sacc[i] = mfma_bf16(as_bf16x8(af[kk][i]), as_bf16x8(bf[kk][i]), sacc[i]);
+      for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int j = 0; j < PTW; ++j)
+          if (pg * PTW + j < PT) acc[i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+    }
+  };
+  const int rows0 = Q < HS ? Q : HS;
+  stage(xs0, bs0, 0);
+  __syncthreads();
+  mma(rows0);
+  if (two) {
+    __syncthreads();
+    stage(xs1, bs1, HS);
+    __syncthreads();
+    mma(Q - HS);
+  }
+
+  // S_c: lane holds p = pt*16 + r16, n = nt*16 + 4q .. +3
+  uint16_t* dst = states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N);
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int j = 0; j < PTW; ++j) {
+      const int nt = ng * NTW + i, pt = pg * PTW + j;
+      if (pt < PT)
+        *reinterpret_cast<uint2*>(dst + (pt * 16 + r16) * N + nt * 16 + 4 * q) =
+            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Inter-chunk state passing (bf16 chunk states in, bf16 boundary states out):
+//   h_in(0) = h0,  h_in(c+1) = lambda_c h_in(c) + S_c,  h_final = h_in(nc)
+// (the chunkwise recurrence of the state across chunks), fp32 running state.
+// One thread per 4 consecutive n of one p of one (batch, head); PF chunks in
+// flight.  h_in(c) overwrites S_c in place (S_c is read before it).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
+    uint16_t* __restrict__ states, const float* __restrict__ decay, const float* __restrict__ h0,
+    float* __restrict__ h_final, int H, int PN, int nc) {
+  constexpr int PF = 8;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int e4 = blockIdx.x * kThreads + threadIdx.x;  // group of 4 elements
+  if (e4 * 4 >= PN) return;
+  const size_t bh = static_cast<size_t>(b) * H + h;
+  const size_t cstride = static_cast<size_t>(H) * PN;  // between chunks of one (b, h)
+  uint16_t* base = states + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e4 * 4;
+  const float* dc = decay + bh * nc;
+  float4 hv = h0 ? *reinterpret_cast<const float4*>(h0 + bh * PN + e4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+
+  uint2 cur[PF];
+  float cd[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j)
+    if (j < nc) {
+      cur[j] = *reinterpret_cast<const uint2*>(base + j * cstride);
+      cd[j] = dc[j];
+    }
+  for (int c0 = 0; c0 < nc; c0 += PF) {
+    uint2 nxt[PF];
+    float nd[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int cn = c0 + PF + j;
+      if (cn < nc) {
+        nxt[j] = *reinterpret_cast<const uint2*>(base + cn * cstride);
+        nd[j] = dc[cn];
+      }
     }
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) hacc[i] = hacc[i] * lam + sacc[i];
-  }
-  if (h_final) {
+    for (int j = 0; j < PF; ++j) {
+      const int cc = c0 + j;
+      if (cc < nc) {
+        *reinterpret_cast<uint2*>(base + cc * cstride) =
+            make_uint2(pack_bf16x2(hv.x, hv.y), pack_bf16x2(hv.z, hv.w));
+        const float l = cd[j];
+        const uint2 s = cur[j];
+        hv.x = l * hv.x + bf16_bits_to_f32(s.x & 0xFFFFu);
+        hv.y = l * hv.y + bf16_bits_to_f32(s.x >> 16);
+        hv.z = l * hv.z + bf16_bits_to_f32(s.y & 0xFFFFu);
+        hv.w = l * hv.w + bf16_bits_to_f32(s.y >> 16);
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tile = wid + 4 * i;
-      if (tile >= TILES) break;
-      const int nt = tile % NT, pt = tile / NT;
-      *reinterpret_cast<f32x4*>(h_final + pub + (pt * 16 + r16) * N + n0 + nt * 16 + 4 * q) = hacc[i];
+    for (int j = 0; j < PF; ++j) {
+      cur[j] = nxt[j];
+      cd[j] = nd[j];
     }
   }
+  if (h_final) *reinterpret_cast<float4*>(h_final + bh * PN + e4 * 4) = hv;
 }
 
 // ---------------------------------------------------------------------------
@@ -264,11 +303,9 @@ __global__ __launch_bounds__(kThreads) void ssd_walk_bf16_kernel(
 // ---------------------------------------------------------------------------
 template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
-    const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm, const float* __restrict__ D,
-    const float* __restrict__ dt_bias, float dt_min, float dt_max,
-    const uint16_t* __restrict__ hin, uint16_t* __restrict__ y, int T, int H, int G, int Q, int nc,
-    int npairs) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm, const float* __restrict__ D,
+    const float2* __restrict__ tok, const uint16_t* __restrict__ hin, uint16_t* __restrict__ y,
+    int T, int H, int G, int Q, int nc, int npairs) {
   constexpr int QSM = 64;               // sub-chunk length (Q >= 64); Q = 32 runs one of 32
   constexpr int KCP = N < 32 ? 32 : N;  // K of G^T padded to whole 32-wide MFMA steps (zeros)
   constexpr int BP = KCP + 8;           // pitch of bt / hT rows (bf16)
@@ -284,13 +321,11 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t xh[QSM * XPn];  // x * xsc
   __shared__ __attribute__((aligned(16))) uint16_t hT[P * BP];
   __shared__ __attribute__((aligned(16))) float dl[256];
-  __shared__ __attribute__((aligned(16))) float cs_hi[256];
-  __shared__ __attribute__((aligned(16))) float cs_lo[256];
+  __shared__ __attribute__((aligned(16))) float cs[256];   // A u_l
   __shared__ __attribute__((aligned(16))) float csc[256];  // output row scale
   __shared__ __attribute__((aligned(16))) float xsc[256];  // x row scale
   __shared__ float kpre[4], kpost[4];                       // state factors per sub-chunk
   __shared__ int exact_flag;
-  __shared__ double wsum[4], tot;
 
   int b, c, h;
   if (!unit_of_block(H, nc, npairs, b, c, h)) return;
@@ -303,8 +338,9 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   const int QS = Q < QSM ? Q : QSM;
   const int nsub = Q / QS;
   const bool has_rows = 16 * wid < QS;  // waves without output rows (Q = 32) only help stage
-  const float a_re = A[h];
-  const float bias = dt_bias ? dt_bias[h] : 0.0f;
+  // per-token exponents and step sizes (from the chunk-state kernel), first
+  const float2 tv = tid < Q ? tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid]
+                            : make_float2(0.f, 0.f);
   const float Dh = D ? D[h] : 0.0f;
   if (tid == 0) exact_flag = 0;
 
@@ -322,9 +358,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   const buf_t hbuf = make_buf(hin + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
                               P * N * 2);
 
-  // ---- global loads first: dt, h_in, C rows and x/B of sub-chunk 0 ----
-  const size_t dt_base = (static_cast<size_t>(b) * T + t0) * H + h;
-  const float dt_raw = tid < Lc ? dt[dt_base + static_cast<size_t>(tid) * H] : 0.0f;
+  // ---- global loads: h_in, C rows and x/B of sub-chunk 0 ----
 
   // state tiles, transposed: lane holds column p = pt*16 + r16, rows n = nt*16 + 4q + j
   f32x4 hacc[KTW][NPT];
@@ -362,13 +396,14 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   xs.load(xbuf, xrow, 0);
   bs.load(bbuf, brow, 0);
 
-  // ---- prologue: step sizes, cumulative exponents, per-sub-chunk factors ----
-  chunk_prologue<false>(dt_raw, Lc, a_re, 0.0f, bias, dt_min, dt_max, dl, cs_hi, cs_lo, nullptr,
-                        nullptr, wsum, &tot, Q);
-  // exponent of token t as a double (t = -1: 0)
-  auto csd = [&](int t) -> double {
-    return t < 0 ? 0.0 : static_cast<double>(cs_hi[t]) + static_cast<double>(cs_lo[t]);
-  };
+  // ---- prologue: per-token values, per-sub-chunk factors ----
+  if (tid < Q) {
+    cs[tid] = tv.x;
+    dl[tid] = tv.y;
+  }
+  __syncthreads();
+  // exponent of token t (t = -1: 0)
+  auto csd = [&](int t) -> float { return t < 0 ? 0.0f : cs[t]; };
   if (tid < nsub) {
     const int j0 = tid * QS, m = j0 + QS / 2 - 1, j1 = j0 + QS - 1;
     if (csd(j0 - 1) - csd(m) > kMaxHalfSpread || csd(m) - csd(j1) > kMaxHalfSpread)
@@ -379,21 +414,21 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   const bool exact = __builtin_amdgcn_readfirstlane(exact_flag) != 0;
   if (tid < Q) {
     const int j0 = tid & ~(QS - 1), m = j0 + QS / 2 - 1, j1 = j0 + QS - 1;
-    const double e = csd(tid);
+    const float e = csd(tid);
     if (exact) {
-      csc[tid] = __expf(static_cast<float>(e - csd(j0 - 1)));
-      xsc[tid] = __expf(static_cast<float>(csd(j1) - e)) * dl[tid];
+      csc[tid] = __expf(e - csd(j0 - 1));
+      xsc[tid] = __expf(csd(j1) - e) * dl[tid];
     } else {
-      csc[tid] = __expf(static_cast<float>(e - csd(m)));
-      xsc[tid] = __expf(static_cast<float>(csd(m) - e)) * dl[tid];
+      csc[tid] = __expf(e - csd(m));
+      xsc[tid] = __expf(csd(m) - e) * dl[tid];
     }
     if (tid == j1) {
       const int j = tid / QS;
       if (exact) {
         kpre[j] = 1.0f;
-        kpost[j] = __expf(static_cast<float>(csd(j1) - csd(j0 - 1)));
+        kpost[j] = __expf(csd(j1) - csd(j0 - 1));
       } else {
-        kpre[j] = __expf(static_cast<float>(csd(m) - (j0 > 0 ? csd(m - QS) : 0.0)));
+        kpre[j] = __expf(csd(m) - (j0 > 0 ? csd(m - QS) : 0.0f));
         kpost[j] = 1.0f;
       }
     }
@@ -506,19 +541,18 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
             for (int jj = 0; jj < 4; ++jj) gb[jj] = 4 * q + jj <= r16 ? gb[jj] : 0.f;
           }
         } else {
-          const float lh = cs_hi[lrow], ll = cs_lo[lrow];
+          const float lh = cs[lrow];
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const int s0 = sj + (b0 + half) * 16 + 4 * q;
             f32x4& gv = half ? gb : ga;
-            const float4 hs = *reinterpret_cast<const float4*>(cs_hi + s0);
-            const float4 ls = *reinterpret_cast<const float4*>(cs_lo + s0);
+            const float4 hs = *reinterpret_cast<const float4*>(cs + s0);
             const float4 ds = *reinterpret_cast<const float4*>(dl + s0);
-            const float hv[4] = {hs.x, hs.y, hs.z, hs.w}, lv[4] = {ls.x, ls.y, ls.z, ls.w};
+            const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
             const float dv[4] = {ds.x, ds.y, ds.z, ds.w};
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-              gv[jj] = s0 + jj <= lrow ? gv[jj] * decay_between(lh, ll, hv[jj], lv[jj]) * dv[jj] : 0.f;
+              gv[jj] = s0 + jj <= lrow ? gv[jj] * __expf(lh - hv[jj]) * dv[jj] : 0.f;
           }
         }
         const uint4 mv = make_uint4(pack_bf16x2(ga[0], ga[1]), pack_bf16x2(ga[2], ga[3]),
@@ -589,29 +623,34 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 // ---------------------------------------------------------------------------
 template <int P, int N>
 static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st) {
-  constexpr int NG = N < 32 ? N : 32;  // state columns per walking workgroup
   const int nc = (a.T + a.chunk - 1) / a.chunk;
   const int npairs = a.Bsz * nc;
-  uint16_t* hin = static_cast<uint16_t*>(a.workspace);  // (Bsz, nc, H, P, N) bf16
+  // workspace: bf16 chunk states (Bsz, nc, H, P, N), overwritten in place by
+  // the boundary states; fp32 chunk decays (Bsz, H, nc) after the room an
+  // fp32 copy of the states would take
+  // (Bsz, nc, H, Q) (exponent, step size) pairs after the decays
+  uint16_t* states = static_cast<uint16_t*>(a.workspace);
+  float* decay = static_cast<float*>(a.workspace) + workspace_state_floats(a.Bsz, nc, a.H, P, N);
+  float2* tok = reinterpret_cast<float2*>(decay + workspace_decay_floats(a.Bsz, nc, a.H));
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
   const uint16_t* C = static_cast<const uint16_t*>(a.C);
-  const unsigned walkers = static_cast<unsigned>((a.Bsz * a.H + kXCD - 1) / kXCD) * kXCD * (N / NG);
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
   if (a.events) (void)hipEventRecord(a.events[0], st);
-  // the walk also runs for T = 0: it writes h_final = h0 (or zeros)
-  if (nc > 0 || a.h_final)
-    ssd_walk_bf16_kernel<P, N, NG><<<walkers, kThreads, 0, st>>>(
-        x, a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, a.h0, hin, a.h_final, a.Bsz, a.T, a.H,
-        a.G, a.chunk, nc);
-  if (a.events) {
-    (void)hipEventRecord(a.events[1], st);
-    (void)hipEventRecord(a.events[2], st);
+  if (nc > 0)
+    ssd_state_bf16_kernel<P, N><<<blocks, 512, 0, st>>>(
+        x, a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G,
+        a.chunk, nc, npairs);
+  if (a.events) (void)hipEventRecord(a.events[1], st);
+  if (nc > 0 || a.h_final) {
+    dim3 grid((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz);
+    ssd_pass_bf16_kernel<<<grid, kThreads, 0, st>>>(states, decay, a.h0, a.h_final, a.H, P * N, nc);
   }
+  if (a.events) (void)hipEventRecord(a.events[2], st);
   if (nc > 0)
     ssd_scan_bf16_kernel<P, N><<<blocks, kThreads, 0, st>>>(
-        x, a.dt, a.A, B, C, a.D, a.dt_bias, a.dt_min, a.dt_max, hin,
-        static_cast<uint16_t*>(a.y), a.T, a.H, a.G, a.chunk, nc, npairs);
+        x, B, C, a.D, tok, states, static_cast<uint16_t*>(a.y), a.T, a.H, a.G, a.chunk, nc,
+        npairs);
   if (a.events) (void)hipEventRecord(a.events[3], st);
   return hipGetLastError();
 }

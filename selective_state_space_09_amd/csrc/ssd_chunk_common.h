@@ -114,18 +114,18 @@ struct Slab {
 // The same slab fetched through a buffer descriptor: rows at or past the
 // described range read as zero (no per-row test).  voff: byte offset of token
 // s0 = 0 of the slab's rows in the descriptor.
-template <int ST, int VPR>
+template <int ST, int VPR, int NTHR = kThreads>
 struct BufSlab {
   static constexpr int ITEMS = ST * VPR;
-  static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+  static constexpr int PER = (ITEMS + NTHR - 1) / NTHR;
   uint4 v[PER];
 
   __device__ __forceinline__ void load(buf_t r, uint32_t row_bytes, int s0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int it = threadIdx.x + i * kThreads;
+      const int it = threadIdx.x + i * NTHR;
       const int vv = it % VPR, rg = it / VPR;
-      if (ITEMS % kThreads == 0 || it < ITEMS)
+      if (ITEMS % NTHR == 0 || it < ITEMS)
         v[i] = buf_load16(r, static_cast<uint32_t>(s0 + rg) * row_bytes + vv * 16);
     }
   }

@@ -47,6 +47,12 @@ inline size_t workspace_decay_floats(int Bsz, int nc, int H) {
   return static_cast<size_t>(Bsz) * H * nc * 2;
 }
 
+// floats of per-token (exponent, step size) pairs of the real form:
+// (Bsz, nc, H, chunk, 2)
+inline size_t workspace_token_floats(int Bsz, int nc, int H, int chunk) {
+  return static_cast<size_t>(Bsz) * nc * H * chunk * 2;
+}
+
 hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);

@@ -107,9 +107,10 @@ def test_decode_rejects():
 
 def test_workspace_size():
     L = ssd.lib()
-    # BitMamba layer shape: states (2, 8, 64, 64, 128) fp32 + decays
+    # BitMamba layer shape: states (2, 8, 64, 64, 128) fp32 + decays + the
+    # per-token (exponent, step) pairs (2, 8, 64, 256) of the real form
     n = ssd.ssd_workspace_size(2, 2048, 64, 64, 1, 128, 256, False)
-    assert n >= 2 * 8 * 64 * 64 * 128 * 4 + 2 * 64 * 8 * 8
+    assert n >= 2 * 8 * 64 * 64 * 128 * 4 + 2 * 64 * 8 * 8 + 2 * 8 * 64 * 256 * 8
     assert n % 256 == 0
     # complex doubles the state width
     nc = ssd.ssd_workspace_size(8, 2048, 16, 64, 16, 64, 256, True)
