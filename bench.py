@@ -6,9 +6,11 @@ fp32 dt/A/state -- on seeded synthetic inputs.  One step = one call of
 ssd_chunk_fwd over the whole batch (every kernel of the call: chunk states,
 the state passing between chunks, chunk outputs).
 
-Timing: HIP events recorded by the library on the launch stream around each
-kernel of every timed step; ms_per_step is the mean of the per-step event
-intervals.  Between steps a 512 MiB buffer is read (outside the timed
+Timing: HIP events bound by the library to each kernel's dispatch on the
+launch stream (a start/stop pair per kernel, every timed step); a kernel's
+time is the mean of its pair's intervals, ms_per_step the mean interval from
+the first kernel's start to the last kernel's stop (gaps between the kernels
+included).  Between steps a 512 MiB buffer is read (outside the timed
 intervals) so that the 256 MB Infinity Cache and the L2s hold none of the
 step's inputs: the number is the rate with inputs resident in HBM.  The flush
 reads rather than writes: a written flush would leave the cache full of dirty
@@ -86,13 +88,41 @@ class Hip:
         return ms.value
 
 
+def source_sha256():
+    """Hash of the library's kernel sources (file names and contents)."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "selective_state_space_09_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` (FETCH + WRITE, rocprofv3 counters
+    scaled by a plain copy of known size) from profiles/traffic_<workload>.json,
+    or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_sha256():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+
+
 def kernel_segments(cfg):
-    """Kernels of one chunked-forward call and the event pair around each:
+    """Kernels of one chunked-forward call and the event pair bound to each:
     chunk states, the state passing between chunks, then the outputs."""
     if cfg["kind"] == "real" and cfg.get("dtype") == "bf16":
-        return {"ssd_state_bf16_kernel": (0, 1), "ssd_pass_bf16_kernel": (1, 2),
-                "ssd_scan_bf16_kernel": (2, 3)}
-    return {"ssd_state_kernel": (0, 1), "ssd_pass_kernel": (1, 2), "ssd_scan_kernel": (2, 3)}
+        return {"ssd_state_bf16_kernel": (0, 1), "ssd_pass_bf16_kernel": (2, 3),
+                "ssd_scan_bf16_kernel": (4, 5)}
+    return {"ssd_state_kernel": (0, 1), "ssd_pass_kernel": (2, 3), "ssd_scan_kernel": (4, 5)}
 
 
 def kernel_bytes(cfg, dims):
@@ -112,10 +142,11 @@ def kernel_bytes(cfg, dims):
     y = Bsz * T * H * P * (4 if cplx else es)
     st16 = Bsz * nc * H * P * N * 2                       # bf16 chunk / boundary states
     dec = Bsz * H * nc * 4
+    tok = Bsz * nc * H * Q * 8                            # per-token (exponent, step) pairs
     return {
-        "ssd_state_bf16_kernel": x + bc + dt + st16 + dec,
+        "ssd_state_bf16_kernel": x + bc + dt + st16 + dec + tok,
         "ssd_pass_bf16_kernel": 2 * st16 + dec,
-        "ssd_scan_bf16_kernel": x + 2 * bc + dt + st16 + y,
+        "ssd_scan_bf16_kernel": x + 2 * bc + tok + st16 + y,
         "ssd_state_kernel": x + bc + dt + states + decay,
         "ssd_pass_kernel": 2 * states + decay,
         "ssd_scan_kernel": x + 2 * bc + dt + states + y,
@@ -225,8 +256,8 @@ def main():
     P_ = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
 
     n_total = args.warmup + args.steps
-    evs = [[hip.event() for _ in range(4)] for _ in range(n_total)]
-    ev_arrays = [(ctypes.c_void_p * 4)(*[e.value for e in row]) for row in evs]
+    evs = [[hip.event() for _ in range(6)] for _ in range(n_total)]
+    ev_arrays = [(ctypes.c_void_p * 6)(*[e.value for e in row]) for row in evs]
 
     if cplx:
         fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["dt_bias"]),
@@ -263,7 +294,7 @@ def main():
     per_step, per_kernel = [], {n: [] for n in names}
     for i in range(args.warmup, n_total):
         e = evs[i]
-        per_step.append(hip.elapsed_ms(e[0], e[3]))
+        per_step.append(hip.elapsed_ms(e[0], e[5]))
         for n, (k0, k1) in segs.items():
             per_kernel[n].append(hip.elapsed_ms(e[k0], e[k1]))
     ms = float(np.mean(per_step))
@@ -284,12 +315,13 @@ def main():
         kern[n] = ent
     dom = max(names, key=lambda n: kern[n]["avg_us"])
     k = kern[dom]
+    traffic = measured_traffic(args.workload, dom)
     if "mfma_frac" in k and k["mfma_frac"] > k["hbm_frac"]:
         roof = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_PEAK_TFLOPS[dtype_name],
-                "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": None, "kernel": dom}
+                "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": traffic, "kernel": dom}
     else:
         roof = {"bound": "hbm", "achieved": k["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": k["hbm_frac"], "traffic": None, "kernel": dom}
+                "frac": k["hbm_frac"], "traffic": traffic, "kernel": dom}
     whole_gbs = kb["whole_forward"] / (ms / 1e3) / 1e9
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
@@ -359,7 +391,8 @@ def bench_decode(args, cfg):
            "config": {"workload": "decode_f32", "batch": Bsz, "heads": H, "headdim": P,
                       "d_state": N},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                        "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": measured_traffic("decode_f32", "ssd_decode_kernel"),
                         "kernel": "ssd_decode_kernel"}}
     print(json.dumps(out), flush=True)
 

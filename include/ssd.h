@@ -134,10 +134,13 @@ int ssd_complex_chunk_fwd(const float *x, const float *dt, const float *A,
 
 /*
  * Measurement variants of the two chunked forwards: identical arguments,
- * kernels and results, plus `events`, an array of 4 hipEvent_t (passed as
- * void*) recorded on `stream` before the chunk-state kernel, after it, after
- * the inter-chunk scan and after the output kernel; or NULL (then they are
- * the plain calls).  The caller creates and owns the events.
+ * kernels and results, plus `events`, an array of 6 hipEvent_t (passed as
+ * void*): the start and stop of the chunk-state kernel, of the inter-chunk
+ * state-passing kernel and of the output kernel, in that order, each pair
+ * bound to its kernel's dispatch on `stream` (so that it times the kernel
+ * alone); a kernel that a call does not run (T = 0) has its pair recorded
+ * back to back.  NULL: the plain calls.  The caller creates and owns the
+ * events.
  */
 int ssd_chunk_fwd_ev(const void *x, const float *dt, const float *A,
                      const void *B, const void *C, const float *D,

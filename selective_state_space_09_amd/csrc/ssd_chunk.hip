@@ -697,21 +697,16 @@ static hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st) {
   const TI* B = static_cast<const TI*>(a.B);
   const TI* C = static_cast<const TI*>(a.C);
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
-  if (a.events) (void)hipEventRecord(a.events[0], st);
-  if (nc > 0) {
-    ssd_state_kernel<TI, CPLX, P, N><<<blocks, kThreads, 0, st>>>(
-        x, a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, a.T, a.H, a.G, a.chunk,
-        nc, npairs);
-  }
-  if (a.events) (void)hipEventRecord(a.events[1], st);
-  launch_pass<CPLX, N>(states, decay, a.h0, a.h_final, a.Bsz, a.H, P, nc, st);
-  if (a.events) (void)hipEventRecord(a.events[2], st);
-  if (nc > 0) {
-    ssd_scan_kernel<TI, CPLX, P, N><<<blocks, kThreads, 0, st>>>(
-        x, a.dt, a.A, B, C, a.D, a.dt_bias, a.dt_min, a.dt_max, states,
-        static_cast<TI*>(a.y), a.T, a.H, a.G, a.chunk, nc, npairs);
-  }
-  if (a.events) (void)hipEventRecord(a.events[3], st);
+  const hipEvent_t* ev = a.events;
+  launch_k(nc > 0, ssd_state_kernel<TI, CPLX, P, N>, dim3(blocks), dim3(kThreads), st, ev, x,
+           a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, a.T, a.H, a.G, a.chunk,
+           nc, npairs);
+  launch_pass<CPLX, N>(states, decay, a.h0, a.h_final, a.Bsz, a.H, P, nc, st,
+                       ev ? ev + 2 : nullptr);
+  launch_k(nc > 0, ssd_scan_kernel<TI, CPLX, P, N>, dim3(blocks), dim3(kThreads), st,
+           ev ? ev + 4 : nullptr, x, a.dt, a.A, B, C, a.D, a.dt_bias, a.dt_min, a.dt_max,
+           static_cast<const float*>(states), static_cast<TI*>(a.y), a.T, a.H, a.G, a.chunk, nc,
+           npairs);
   return hipGetLastError();
 }
 

@@ -360,19 +360,14 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 
   // ---- global loads: h_in, C rows and x/B of sub-chunk 0 ----
 
-  // state tiles, transposed: lane holds column p = pt*16 + r16, rows n = nt*16 + 4q + j
-  f32x4 hacc[KTW][NPT];
+  // h_in tiles (bf16, converted after the prologue so that nothing waits for
+  // them before every other load is in flight)
+  uint2 hv[KTW][NPT];
 #pragma unroll
-  for (int i = 0; i < KTW; ++i) {
-    const int nt = wid + 4 * i;
+  for (int i = 0; i < KTW; ++i)
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt) {
-      const uint2 v = buf_load8(hbuf, ((pt * 16 + r16) * N + nt * 16 + 4 * q) * 2);
-      hacc[i][pt] = nt < KT ? f32x4{bf16_bits_to_f32(v.x & 0xFFFFu), bf16_bits_to_f32(v.x >> 16),
-                                    bf16_bits_to_f32(v.y & 0xFFFFu), bf16_bits_to_f32(v.y >> 16)}
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+    for (int pt = 0; pt < NPT; ++pt)
+      hv[i][pt] = buf_load8(hbuf, ((pt * 16 + r16) * N + (wid + 4 * i) * 16 + 4 * q) * 2);
 
   // C rows of this wave's output tile in sub-chunk j: lane (row r16, group q)
   // holds k = ks*32 + 8q .. +7.  Rows past the chunk (and every row of the
@@ -433,6 +428,18 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       }
     }
   }
+  // state tiles, transposed: lane holds column p = pt*16 + r16, rows n = nt*16 + 4q + j
+  f32x4 hacc[KTW][NPT];
+#pragma unroll
+  for (int i = 0; i < KTW; ++i)
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) {
+      const uint2 v = hv[i][pt];
+      hacc[i][pt] = wid + 4 * i < KT
+                        ? f32x4{bf16_bits_to_f32(v.x & 0xFFFFu), bf16_bits_to_f32(v.x >> 16),
+                                bf16_bits_to_f32(v.y & 0xFFFFu), bf16_bits_to_f32(v.y >> 16)}
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   if constexpr (KCP > N) {
     // zero the K padding of bt and hT (stage stores never write it)
     for (int it = tid; it < QSM + P; it += kThreads) {
@@ -636,22 +643,18 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st) {
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
   const uint16_t* C = static_cast<const uint16_t*>(a.C);
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
-  if (a.events) (void)hipEventRecord(a.events[0], st);
-  if (nc > 0)
-    ssd_state_bf16_kernel<P, N><<<blocks, 512, 0, st>>>(
-        x, a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G,
-        a.chunk, nc, npairs);
-  if (a.events) (void)hipEventRecord(a.events[1], st);
-  if (nc > 0 || a.h_final) {
-    dim3 grid((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz);
-    ssd_pass_bf16_kernel<<<grid, kThreads, 0, st>>>(states, decay, a.h0, a.h_final, a.H, P * N, nc);
-  }
-  if (a.events) (void)hipEventRecord(a.events[2], st);
-  if (nc > 0)
-    ssd_scan_bf16_kernel<P, N><<<blocks, kThreads, 0, st>>>(
-        x, B, C, a.D, tok, states, static_cast<uint16_t*>(a.y), a.T, a.H, a.G, a.chunk, nc,
-        npairs);
-  if (a.events) (void)hipEventRecord(a.events[3], st);
+  const hipEvent_t* ev = a.events;
+  launch_k(nc > 0, ssd_state_bf16_kernel<P, N>, dim3(blocks), dim3(512), st, ev, x, a.dt, a.A,
+           B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G, a.chunk, nc,
+           npairs);
+  launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel,
+           dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
+           ev ? ev + 2 : nullptr, states, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
+           P * N, nc);
+  launch_k(nc > 0, ssd_scan_bf16_kernel<P, N>, dim3(blocks), dim3(kThreads), st,
+           ev ? ev + 4 : nullptr, x, B, C, a.D, static_cast<const float2*>(tok),
+           static_cast<const uint16_t*>(states), static_cast<uint16_t*>(a.y), a.T, a.H, a.G,
+           a.chunk, nc, npairs);
   return hipGetLastError();
 }
 

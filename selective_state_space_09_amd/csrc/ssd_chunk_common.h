@@ -3,6 +3,8 @@
 // staging of token slabs, and the inter-chunk state-passing kernel.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "ssd_device.h"
@@ -24,10 +26,12 @@ struct Pad<float> {
   static constexpr int row = 4;
 };
 
-// (b, c, h) of this workgroup under the XCD-grouped order; false for the
-// padding workgroups of the last, partial group of 8 (b, c) pairs.
-__device__ __forceinline__ bool unit_of_block(int H, int nc, int npairs, int& b, int& c, int& h) {
-  const int id = blockIdx.x;
+// (b, c, h) of work unit `id` under the XCD-grouped order: consecutive ids go
+// to consecutive XCDs, and the H heads of one (b, c) pair share an XCD (and
+// its L2, which then serves their common B and C rows).  False for the
+// padding units of the last, partial group of 8 (b, c) pairs.
+__device__ __forceinline__ bool unit_coords(int id, int H, int nc, int npairs, int& b, int& c,
+                                            int& h) {
   const int k = id / kXCD;
   const int j = (id % kXCD) + kXCD * (k / H);
   h = k % H;
@@ -35,6 +39,30 @@ __device__ __forceinline__ bool unit_of_block(int H, int nc, int npairs, int& b,
   b = j / nc;
   c = j % nc;
   return true;
+}
+__device__ __forceinline__ bool unit_of_block(int H, int nc, int npairs, int& b, int& c, int& h) {
+  return unit_coords(blockIdx.x, H, nc, npairs, b, c, h);
+}
+
+
+// Launch of one kernel of a forward call.  With a start/stop event pair
+// (ev != NULL) the events are bound to the kernel's own dispatch
+// (hipExtLaunchKernelGGL), so that they time the kernel alone; a kernel that
+// is not run (run == false) records its pair back to back.
+template <typename F, typename... Args>
+inline void launch_k(bool run, F kernel, dim3 grid, dim3 block, hipStream_t st,
+                     const hipEvent_t* ev, Args... args) {
+  if (!run) {
+    if (ev) {
+      (void)hipEventRecord(ev[0], st);
+      (void)hipEventRecord(ev[1], st);
+    }
+    return;
+  }
+  if (ev)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev[0], ev[1], 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
 }
 
 // ---------------------------------------------------------------------------
@@ -285,10 +313,11 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_kernel(
 // launch of the inter-chunk scan for one shape
 template <bool CPLX, int N>
 inline void launch_pass(float* states, const float* decay, const float* h0, float* h_final,
-                        int Bsz, int H, int P, int nc, hipStream_t st) {
+                        int Bsz, int H, int P, int nc, hipStream_t st, const hipEvent_t* ev) {
   const int groups = P * N / 4;
   dim3 grid((groups + kThreads - 1) / kThreads, H, Bsz);
-  ssd_pass_kernel<CPLX, N><<<grid, kThreads, 0, st>>>(states, decay, h0, h_final, H, P, nc);
+  launch_k(true, ssd_pass_kernel<CPLX, N>, grid, dim3(kThreads), st, ev, states, decay, h0,
+           h_final, H, P, nc);
 }
 
 }  // namespace ssd

@@ -20,7 +20,7 @@ struct ChunkArgs {
   float* h_final;
   int Bsz, T, H, P, G, N, chunk, dtype;
   void* workspace;
-  hipEvent_t* events;  // NULL, or 4 events recorded around the 3 kernels
+  hipEvent_t* events;  // NULL, or 6: start/stop of each of the 3 kernels
 };
 
 struct DecodeArgs {

@@ -123,9 +123,10 @@ def test_tiny_workload_full():
 # edge cases
 # --------------------------------------------------------------------------
 
-def test_empty_sequence_passes_initial_state():
-    _print_case(edge="T=0")
-    inp = inputs.make_real(1, 4, 2, 16, 16, 1, seed=3, with_h0=True)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_sequence_passes_initial_state(dtype):
+    _print_case(edge="T=0", dtype=dtype)
+    inp = inputs.make_real(1, 4, 2, 16, 16, 1, dtype=dtype, seed=3, with_h0=True)
     for k in ("x", "dt", "B", "C"):
         inp[k] = np.ascontiguousarray(inp[k][:, :0])
     d = _gpu.upload(inp)
@@ -190,6 +191,31 @@ def test_chained_calls_equal_one_call():
     yr, hr = _oracle_real(inp)
     assert y_err(np.concatenate([y1, y2], axis=1), yr) < TOL_F32
     assert state_err(h2, hr) < TOL_F32
+
+
+def test_workspace_contents_do_not_matter():
+    """The bf16 path keeps per-(batch, head) chunk counters in the workspace
+    (tagged per call): a workspace of random bytes gives the oracle's result,
+    and reusing it for further calls gives bit-identical results."""
+    _print_case(edge="workspace reuse", dtype="bf16")
+    inp = inputs.make_real(2, 700, 4, 64, 128, 1, dtype="bf16", seed=9, with_h0=True)
+    d = _gpu.upload(inp)
+    nbytes = ssd.ssd_workspace_size(2, 700, 4, 64, 1, 128, 256)
+    g = torch.Generator(device="cpu").manual_seed(1)
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).cuda()
+    outs = []
+    for _ in range(3):
+        y, hf = ssd.ssd_chunk_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dt_bias"],
+                                  d["dt_min"], d["dt_max"], d["h0"], chunk=256,
+                                  return_final_state=True, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((_gpu.to_host64(y), _gpu.to_host64(hf)))
+    yr, hr = _oracle_real(inp)
+    assert y_err(outs[0][0], yr) < TOL_BF16
+    assert state_err(outs[0][1], hr) < TOL_BF16
+    for y, hf in outs[1:]:
+        np.testing.assert_array_equal(y, outs[0][0])
+        np.testing.assert_array_equal(hf, outs[0][1])
 
 
 def test_rejects_bad_arguments_without_launch():
