@@ -374,9 +374,8 @@ def bench_decode(args, cfg):
     n_total = args.warmup + args.steps
     evs = [(hip.event(), hip.event()) for _ in range(n_total)]
     for i in range(n_total):
-        hip.record(evs[i][0], sp)
-        rc = L.ssd_step_decode(*args_c)
-        hip.record(evs[i][1], sp)
+        arr = (ctypes.c_void_p * 2)(evs[i][0].value, evs[i][1].value)
+        rc = L.ssd_step_decode_ev(*args_c, arr)
         if rc:
             raise RuntimeError(L.ssd_last_error().decode())
     torch.cuda.synchronize()

@@ -174,6 +174,17 @@ int ssd_step_decode(float *h, const float *x, const float *dt, const float *A,
                     const float *dt_bias, float dt_min, float dt_max, float *y,
                     int Bsz, int H, int P, int G, int N, void *stream);
 
+/*
+ * Measurement variant of ssd_step_decode: identical arguments, kernel and
+ * result, plus `events`, 2 hipEvent_t (passed as void*) bound to the decode
+ * kernel's dispatch on `stream` (start, stop), or NULL.
+ */
+int ssd_step_decode_ev(float *h, const float *x, const float *dt, const float *A,
+                       const float *B, const float *C, const float *D,
+                       const float *dt_bias, float dt_min, float dt_max, float *y,
+                       int Bsz, int H, int P, int G, int N, void *stream,
+                       void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,8 @@ def lib():
     L.ssd_complex_chunk_fwd_ev.argtypes = L.ssd_complex_chunk_fwd.argtypes + [P]
     L.ssd_step_decode.restype = I
     L.ssd_step_decode.argtypes = [P, P, P, P, P, P, P, P, F, F, P, I, I, I, I, I, P]
+    L.ssd_step_decode_ev.restype = I
+    L.ssd_step_decode_ev.argtypes = L.ssd_step_decode.argtypes + [P]
     _lib = L
     return L
 

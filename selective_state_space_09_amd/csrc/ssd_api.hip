@@ -196,6 +196,14 @@ int ssd_complex_chunk_fwd(const float* x, const float* dt, const float* A, const
 int ssd_step_decode(float* h, const float* x, const float* dt, const float* A, const float* B,
                     const float* C, const float* D, const float* dt_bias, float dt_min,
                     float dt_max, float* y, int Bsz, int H, int P, int G, int N, void* stream) {
+  return ssd_step_decode_ev(h, x, dt, A, B, C, D, dt_bias, dt_min, dt_max, y, Bsz, H, P, G, N,
+                            stream, nullptr);
+}
+
+int ssd_step_decode_ev(float* h, const float* x, const float* dt, const float* A, const float* B,
+                       const float* C, const float* D, const float* dt_bias, float dt_min,
+                       float dt_max, float* y, int Bsz, int H, int P, int G, int N, void* stream,
+                       void* const* events) {
   if (Bsz <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0)
     return fail(SSD_EINVAL, "sizes must be positive: Bsz=%d H=%d P=%d G=%d N=%d", Bsz, H, P, G, N);
   if (H % G != 0) return fail(SSD_EINVAL, "H=%d is not a multiple of G=%d", H, G);
@@ -212,7 +220,8 @@ int ssd_step_decode(float* h, const float* x, const float* dt, const float* A, c
   SSD_TRY(check_ptr(D, "D", 4, false));
   SSD_TRY(check_ptr(dt_bias, "dt_bias", 4, false));
   SSD_TRY(check_clamp(dt_min, dt_max));
-  ssd::DecodeArgs a{h, x, dt, A, B, C, D, dt_bias, dt_min, dt_max, y, Bsz, H, P, G, N};
+  ssd::DecodeArgs a{h, x, dt, A, B, C, D, dt_bias, dt_min, dt_max, y, Bsz, H, P, G, N,
+                    reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
   return launch_status(ssd::run_decode(a, static_cast<hipStream_t>(stream)));
 }
 

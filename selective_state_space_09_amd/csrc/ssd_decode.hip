@@ -7,12 +7,14 @@
 // coalesced access; the workgroup walks its P rows with 8 rows in flight per
 // thread.  The dot product with C is reduced across the row's lanes with
 // cross-lane shuffles.  The state is read once and written once: the kernel
-// is bound by HBM bandwidth.
+// is bound by HBM bandwidth.  Its loads and stores are nontemporal (each state
+// byte is touched once per step; nothing else is displaced from the caches).
 
-#include "ssd_device.h"
-#include "ssd_internal.h"
+#include "ssd_chunk_common.h"
 
 namespace ssd {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 template <int N>
 __global__ __launch_bounds__(kThreads) void ssd_decode_kernel(
@@ -43,7 +45,8 @@ __global__ __launch_bounds__(kThreads) void ssd_decode_kernel(
     for (int k = 0; k < UNR; ++k) {
       const int r = r0 + k * RPP;
       if (r < P) {
-        v[k] = *reinterpret_cast<const float4*>(hrow + static_cast<size_t>(r) * N);
+        const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(hrow + static_cast<size_t>(r) * N));
+        v[k] = make_float4(t.x, t.y, t.z, t.w);
         xv[k] = xr[r];
       }
     }
@@ -58,7 +61,8 @@ __global__ __launch_bounds__(kThreads) void ssd_decode_kernel(
         n.y = a * v[k].y + u * bv.y;
         n.z = a * v[k].z + u * bv.z;
         n.w = a * v[k].w + u * bv.w;
-        *reinterpret_cast<float4*>(hrow + static_cast<size_t>(r) * N) = n;
+        __builtin_nontemporal_store(f4v{n.x, n.y, n.z, n.w},
+                                    reinterpret_cast<f4v*>(hrow + static_cast<size_t>(r) * N));
         part = n.x * cv.x + n.y * cv.y + n.z * cv.z + n.w * cv.w;
       }
 #pragma unroll
@@ -72,9 +76,8 @@ hipError_t run_decode(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.Bsz * a.H);
 #define SSD_DECODE_CASE(NN)                                                                  \
   case NN:                                                                                   \
-    ssd_decode_kernel<NN><<<grid, kThreads, 0, st>>>(a.h, a.x, a.dt, a.A, a.B, a.C, a.D,     \
-                                                     a.dt_bias, a.dt_min, a.dt_max, a.y,     \
-                                                     a.H, a.P, a.G);                         \
+    launch_k(true, ssd_decode_kernel<NN>, grid, dim3(kThreads), st, a.events, a.h, a.x, a.dt,  \
+             a.A, a.B, a.C, a.D, a.dt_bias, a.dt_min, a.dt_max, a.y, a.H, a.P, a.G);         \
     break;
   switch (a.N) {
     SSD_DECODE_CASE(16)

@@ -35,6 +35,7 @@ struct DecodeArgs {
   float dt_min, dt_max;
   float* y;
   int Bsz, H, P, G, N;
+  hipEvent_t* events;  // NULL, or start/stop of the decode kernel
 };
 
 // floats of chunk-boundary states: (Bsz, nc, H, P, KC), KC = N or 2N
