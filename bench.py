@@ -35,7 +35,9 @@ if ROOT not in sys.path:
 
 METRIC = "SSD fwd tokens/s per layer (H64 P64 N128) + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+# dense MFMA peaks; "f32 as 3 bf16": fp32-precision products computed as three
+# bf16 products (split operands), i.e. a third of the bf16 peak
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "f32 as 3 bf16": 2500.0 / 3}
 
 
 def parse():
@@ -122,6 +124,9 @@ def kernel_segments(cfg):
     if cfg["kind"] == "real" and cfg.get("dtype") == "bf16":
         return {"ssd_state_bf16_kernel": (0, 1), "ssd_pass_bf16_kernel": (2, 3),
                 "ssd_scan_bf16_kernel": (4, 5)}
+    if cfg["kind"] == "complex":
+        return {"ssd_state_cplx_kernel": (0, 1), "ssd_pass_kernel": (2, 3),
+                "ssd_scan_cplx_kernel": (4, 5)}
     return {"ssd_state_kernel": (0, 1), "ssd_pass_kernel": (2, 3), "ssd_scan_kernel": (4, 5)}
 
 
@@ -147,6 +152,9 @@ def kernel_bytes(cfg, dims):
         "ssd_state_bf16_kernel": x + bc + dt + st16 + dec + tok,
         "ssd_pass_bf16_kernel": 2 * st16 + dec,
         "ssd_scan_bf16_kernel": x + 2 * bc + tok + st16 + y,
+        # complex: the per-token table is (exponent, cos, sin, 0), 16 bytes
+        "ssd_state_cplx_kernel": x + bc + dt + states + decay + 2 * tok,
+        "ssd_scan_cplx_kernel": x + 2 * bc + 2 * tok + states + y,
         "ssd_state_kernel": x + bc + dt + states + decay,
         "ssd_pass_kernel": 2 * states + decay,
         "ssd_scan_kernel": x + 2 * bc + dt + states + y,
@@ -164,7 +172,8 @@ def kernel_flops(cfg, dims):
     scan = units * (2 * tri * KC + 2 * tri * P + 2 * Q * KC * P)
     state = units * 2 * Q * KC * P
     return {"ssd_scan_kernel": scan, "ssd_state_kernel": state,
-            "ssd_scan_bf16_kernel": scan, "ssd_state_bf16_kernel": state}
+            "ssd_scan_bf16_kernel": scan, "ssd_state_bf16_kernel": state,
+            "ssd_scan_cplx_kernel": scan, "ssd_state_cplx_kernel": state}
 
 
 def cpu_baseline(inp, cfg, dims, target_s):
@@ -265,6 +274,7 @@ def main():
                  Bsz, T, H, P, G, N, Q, P_(ws), ws.numel(), sp)
         call = lambda evarr: L.ssd_complex_chunk_fwd_ev(*fixed, evarr)
         dtype_name = "f32"
+        peak_name = "f32 as 3 bf16"
     else:
         dcode = ssd.SSD_BF16 if d["x"].dtype == torch.bfloat16 else ssd.SSD_F32
         fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["D"]),
@@ -272,6 +282,7 @@ def main():
                  Bsz, T, H, P, G, N, Q, dcode, P_(ws), ws.numel(), sp)
         call = lambda evarr: L.ssd_chunk_fwd_ev(*fixed, evarr)
         dtype_name = "bf16" if dcode == ssd.SSD_BF16 else "f32"
+        peak_name = dtype_name
 
     def step(i):
         if flush is not None:
@@ -311,13 +322,13 @@ def main():
         if n in kf:
             tf = kf[n] / (avg / 1e3) / 1e12
             ent.update({"alg_flops": kf[n], "tflops": tf,
-                        "mfma_frac": tf / MFMA_PEAK_TFLOPS[dtype_name]})
+                        "mfma_frac": tf / MFMA_PEAK_TFLOPS[peak_name]})
         kern[n] = ent
     dom = max(names, key=lambda n: kern[n]["avg_us"])
     k = kern[dom]
     traffic = measured_traffic(args.workload, dom)
     if "mfma_frac" in k and k["mfma_frac"] > k["hbm_frac"]:
-        roof = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_PEAK_TFLOPS[dtype_name],
+        roof = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_PEAK_TFLOPS[peak_name],
                 "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": traffic, "kernel": dom}
     else:
         roof = {"bound": "hbm", "achieved": k["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -8,7 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssd.so")
-SOURCES = ["ssd_api.hip", "ssd_chunk.hip", "ssd_chunk_bf16.hip", "ssd_decode.hip"]
+SOURCES = ["ssd_api.hip", "ssd_chunk.hip", "ssd_chunk_bf16.hip", "ssd_chunk_cplx.hip",
+           "ssd_decode.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -79,7 +79,8 @@ size_t workspace_bytes_for(int Bsz, int T, int H, int P, int N, int chunk, int i
   const int KC = is_complex ? 2 * N : N;
   const size_t floats = ssd::workspace_state_floats(Bsz, nc, H, P, KC) +
                         ssd::workspace_decay_floats(Bsz, nc, H) +
-                        (is_complex ? 0 : ssd::workspace_token_floats(Bsz, nc, H, chunk));
+                        (is_complex ? ssd::workspace_cplx_token_floats(Bsz, nc, H, chunk)
+                                    : ssd::workspace_token_floats(Bsz, nc, H, chunk));
   const size_t bytes = floats * sizeof(float);
   return (bytes + 255) / 256 * 256 + 256;
 }

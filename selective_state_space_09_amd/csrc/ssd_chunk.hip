@@ -741,8 +741,5 @@ hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st) {
   return dispatch_p<float, false>(a, st);
 }
 
-hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st) {
-  return dispatch_p<float, true>(a, st);
-}
 
 }  // namespace ssd

@@ -16,23 +16,6 @@
 
 namespace ssd {
 
-typedef __attribute__((ext_vector_type(4))) short short4v;
-typedef __attribute__((address_space(3))) short4v lds_short4v;
-
-// LDS transpose read (ds_read_b64_tr_b16) of a row-major bf16 tile; call it
-// with all 64 lanes active (wave-uniform control flow only).  Lane i
-// of each 16-lane group receives the values of column col0 + (i % 16) in rows
-// row0 .. row0+3 (row0 may differ between the four groups of a wave), as four
-// bf16 in a uint2, row order.  The instruction hands lane i element (i % 4)
-// of the 8 bytes addressed by lanes 4k + i/4 (k = 0..3) of its group, so lane
-// m addresses row row0 + m/4, columns col0 + 4(m % 4) .. +3.
-__device__ __forceinline__ uint2 lds_tr4(const uint16_t* tile, int pitch, int row0, int col0) {
-  const int m = threadIdx.x & 15;
-  const uint16_t* a = tile + (row0 + (m >> 2)) * pitch + col0 + 4 * (m & 3);
-  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(const_cast<uint16_t*>(a)));
-  return __builtin_bit_cast(uint2, r);
-}
-
 __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
   const uint32_t a[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
@@ -583,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
         const float o1 = yacc[pt][1] * s2 + Dh * bf16_bits_to_f32(u.x >> 16);
         const float o2 = yacc[pt][2] * s2 + Dh * bf16_bits_to_f32(u.y & 0xFFFFu);
         const float o3 = yacc[pt][3] * s2 + Dh * bf16_bits_to_f32(u.y >> 16);
-        buf_store8(ybuf, static_cast<uint32_t>(lrow) * xrow + (pt * 16 + 4 * q) * 2,
+        buf_store8_nt(ybuf, static_cast<uint32_t>(lrow) * xrow + (pt * 16 + 4 * q) * 2,
                    make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)));
       }
     }

@@ -100,6 +100,43 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
   return v;
 }
 
+// The same in double: each DPP lane move carries the two 32-bit halves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov_d(double v) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(u & 0xFFFFFFFFull), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, (static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) |
+                                        static_cast<unsigned>(lo));
+}
+__device__ __forceinline__ double wave_inclusive_sum_d(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15;
+  double t;
+  t = dpp_mov_d<0x111>(v); if (r >= 1) v += t;
+  t = dpp_mov_d<0x112>(v); if (r >= 2) v += t;
+  t = dpp_mov_d<0x114>(v); if (r >= 4) v += t;
+  t = dpp_mov_d<0x118>(v); if (r >= 8) v += t;
+  t = dpp_mov_d<0x142>(v); if ((lane & 31) >= 16) v += t;
+  t = dpp_mov_d<0x143>(v); if (lane >= 32) v += t;
+  return v;
+}
+
+// fp32 -> bf16 hi + bf16 lo with hi + lo = v to ~2^-17 |v| (the operand split
+// of fp32 products computed as three bf16 products, hi*hi + hi*lo + lo*hi)
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  const __bf16 h = static_cast<__bf16>(v);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v - static_cast<float>(h)));
+}
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  uint16_t ah, al, bh, bl;
+  split_bf16(a, ah, al);
+  split_bf16(b, bh, bl);
+  hi = static_cast<uint32_t>(ah) | (static_cast<uint32_t>(bh) << 16);
+  lo = static_cast<uint32_t>(al) | (static_cast<uint32_t>(bl) << 16);
+}
+
 // cos/sin of an angle given in double: reduced to [-pi, pi] in double, then
 // evaluated in float.  Angles of a 256-token chunk reach ~80 rad; reducing in
 // float would cost ~1e-5 rad of phase.
@@ -127,9 +164,36 @@ __device__ __forceinline__ void buf_store8(buf_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v),
                                         r, off, 0, 0);
 }
+// Nontemporal store (cache policy bit nt): for data no later access of the
+// same kernel or the next one reads.
+__device__ __forceinline__ void buf_store8_nt(buf_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v),
+                                        r, off, 0, 2);
+}
+__device__ __forceinline__ void buf_store16_nt(buf_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                         r, off, 0, 2);
+}
 __device__ __forceinline__ void buf_store16(buf_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
                                          r, off, 0, 0);
+}
+
+typedef __attribute__((ext_vector_type(4))) short short4v;
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+// LDS transpose read (ds_read_b64_tr_b16) of a row-major bf16 tile; call it
+// with all 64 lanes active (wave-uniform control flow only).  Lane i
+// of each 16-lane group receives the values of column col0 + (i % 16) in rows
+// row0 .. row0+3 (row0 may differ between the four groups of a wave), as four
+// bf16 in a uint2, row order.  The instruction hands lane i element (i % 4)
+// of the 8 bytes addressed by lanes 4k + i/4 (k = 0..3) of its group, so lane
+// m addresses row row0 + m/4, columns col0 + 4(m % 4) .. +3.
+__device__ __forceinline__ uint2 lds_tr4(const uint16_t* tile, int pitch, int row0, int col0) {
+  const int m = threadIdx.x & 15;
+  const uint16_t* a = tile + (row0 + (m >> 2)) * pitch + col0 + 4 * (m & 3);
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(const_cast<uint16_t*>(a)));
+  return __builtin_bit_cast(uint2, r);
 }
 
 // MFMA wrappers (gfx950).  Operand layouts for the 16x16 forms, lane i,

@@ -54,6 +54,12 @@ inline size_t workspace_token_floats(int Bsz, int nc, int H, int chunk) {
   return static_cast<size_t>(Bsz) * nc * H * chunk * 2;
 }
 
+// floats of the complex form's per-token table (alpha u, cos theta, sin theta, 0):
+// (Bsz, nc, H, chunk, 4)
+inline size_t workspace_cplx_token_floats(int Bsz, int nc, int H, int chunk) {
+  return static_cast<size_t>(Bsz) * nc * H * chunk * 4;
+}
+
 hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
