@@ -32,8 +32,8 @@ namespace ssd {
 // frame of the chunk end, written as fp32 (re | im) rows for the state
 // passing; lambda_c = e^{A u_c}.  Also writes, per token, (alpha u_l,
 // cos theta_l, sin theta_l) for the output kernel.  The chunk is staged
-// through LDS in two halves of up to 128 tokens, both loaded into registers
-// at the start.  The step prefix sums are double (a DPP wave scan), so the
+// through LDS in quarters of up to 64 tokens, loaded into registers two
+// quarters ahead.  The step prefix sums are double (a DPP wave scan), so the
 // rotation angles (up to ~100 rad over a chunk) keep fp32 accuracy; they are
 // reduced modulo 2 pi in double.
 //
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
     int G, int Q, int nc, int npairs) {
   constexpr int NTHR = 512, WW = 8;
   constexpr int K = 2 * N;
-  constexpr int HS = 128;                    // tokens per staged half
+  constexpr int HS = 64;                     // tokens per staged quarter
   constexpr int XPn = P + 16, BPn = K + 16;  // pitches (bf16 elements)
   constexpr int PT = P / 16;
   constexpr int NKP = N / 16;                // k tile pairs (re, im)
@@ -80,15 +80,16 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
   const buf_t xbuf = make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
                               static_cast<uint32_t>(Lc - 1) * xrow + P * 4);
   const buf_t bbuf = make_buf(Bm + (r0 * G + g) * N * 2, static_cast<uint32_t>(Lc - 1) * brow + N * 8);
-  BufSlab<HS, P / 4, NTHR> xs0, xs1;
-  BufSlab<HS, N / 2, NTHR> bs0, bs1;
-  const bool two = Q > HS;
-  xs0.load(xbuf, xrow, 0);
-  bs0.load(bbuf, brow, 0);
-  if (two) {
-    xs1.load(xbuf, xrow, HS);
-    bs1.load(bbuf, brow, HS);
-  }
+  // two register slots: quarters 0 and 1 now, quarter i+2 once quarter i is staged
+  BufSlab<HS, P / 4, NTHR> xs[2];
+  BufSlab<HS, N / 2, NTHR> bs[2];
+  const int nq = (Q + HS - 1) / HS;  // quarters of the chunk
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (i < nq) {
+      xs[i].load(xbuf, xrow, i * HS);
+      bs[i].load(bbuf, brow, i * HS);
+    }
   const float a_re = A[2 * h], a_im = A[2 * h + 1];
   const float bias = dt_bias ? dt_bias[h] : 0.0f;
 
@@ -200,15 +201,18 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
           }
     }
   };
-  stage(xs0, bs0, 0);
-  __syncthreads();
-  mma(Q < HS ? Q : HS);
-  if (two) {
-    __syncthreads();
-    stage(xs1, bs1, HS);
-    __syncthreads();
-    mma(Q - HS);
-  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < nq) {
+      if (i > 0) __syncthreads();
+      stage(xs[i & 1], bs[i & 1], i * HS);
+      if (i + 2 < nq) {
+        xs[i & 1].load(xbuf, xrow, (i + 2) * HS);
+        bs[i & 1].load(bbuf, brow, (i + 2) * HS);
+      }
+      __syncthreads();
+      mma(Q - i * HS < HS ? Q - i * HS : HS);
+    }
 
   // S_c = e^{i theta_c} S~_c; lane: p = pt*16 + r16, n = kp*16 + 4q .. +3
   float* dst = states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * K);
@@ -242,10 +246,10 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
 // with cs = alpha u, the pivot m = j0 + QS/2 - 1, x^_s = x_s e^{cs_m - cs_s},
 // H = e^{cs_m - cs_{j0-1}} h~_j, and H updated by Bfeat^T x^ between
 // sub-chunks; exact mode (per-element exponentials, raw x, unscaled state)
-// when a half sub-chunk decays by more than e^60.  Wave w produces output
-// rows 16w .. 16w+15 of each sub-chunk (C features in registers, loaded a
-// sub-chunk ahead and rotated once the angles are known); for the state
-// update it owns k tiles w, w+4, ...
+// when a half sub-chunk decays by more than e^60.  Each 16-row block of a
+// sub-chunk is produced by 4 / (QS/16) waves, each over its share of the p
+// tiles (C features in registers, loaded a sub-chunk ahead and rotated once
+// the angles are known); for the state update wave w owns k tiles w, w+4, ...
 // ---------------------------------------------------------------------------
 template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
   constexpr int K = 2 * N;              // real features
   // sub-chunk length: 64 tokens unless the hi / lo tiles then overflow LDS
   constexpr int QSM = (2 * 64 * (K + 8) + 4 * 64 * (P + 16) + 2 * P * (K + 8)) * 2 + 6 * 1024 <=
-                              kLdsBytes ? 64 : 32;
+                              kLdsBytes / 2 ? 64 : 32;
   constexpr int BP = K + 8;             // pitch of bt / hT rows (bf16)
   constexpr int XPn = P + 16;           // pitch of the x tiles
   constexpr int NKS = K / 32;
@@ -263,6 +267,9 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
   constexpr int NPT = P / 16;
   constexpr int KT = K / 16;
   constexpr int KTW = (KT + 3) / 4;
+  constexpr int NRB = QSM / 16;                 // row blocks of a sub-chunk
+  constexpr int WPR = 4 / NRB;                  // waves per row block (p tiles split)
+  constexpr int NPW = (NPT + WPR - 1) / WPR;    // p tiles per wave in the outputs
   constexpr float kMaxHalfSpread = 60.0f;
 
   __shared__ __attribute__((aligned(16))) uint16_t bt[2][QSM * BP];   // Bfeat hi / lo
@@ -281,9 +288,10 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wid = wave_id();
+  const int rb = wid / WPR, ph = wid % WPR;     // row block, p part
   const int QS = Q < QSM ? Q : QSM;
   const int nsub = Q / QS;
-  const bool has_rows = 16 * wid < QS;
+  const bool has_rows = 16 * rb < QS;
   const size_t unit = (static_cast<size_t>(b) * nc + c) * H + h;
   const float4 tv = tid < Q ? tok[unit * Q + tid] : make_float4(0.f, 1.f, 0.f, 0.f);
   if (tid == 0) exact_flag = 0;
@@ -312,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
   // C row of this lane's output row in sub-chunk j: complex group cg holds
   // n0 .. n0+7 with n0 = cg*32 + 8q (N >= 32) or 8q mod 16 (N = 16)
   auto load_c = [&](uint4 (&cr)[NCG][4], int j) {
-    const uint32_t row = j * QS + 16 * wid + r16;
+    const uint32_t row = j * QS + 16 * rb + r16;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const int n0 = N >= 32 ? cg * 32 + 8 * q : (8 * q) % 16;
@@ -470,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
   };
   store_stage(0);
   store_state(0);
-  make_c(craw, 16 * wid + r16);
+  make_c(craw, 16 * rb + r16);
   __syncthreads();
 
   // three split-bf16 products: (ah + al)(bh + bl) without al*bl
@@ -489,28 +497,30 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
       load_c(craw, j + 1);
     }
 
-    // ---- outputs of rows sj + 16 wid .. +15 (accumulator columns) ----
+    // ---- outputs of rows sj + 16 rb .. +15 (accumulator columns), p tiles
+    // ph*NPW .. +NPW-1 ----
     if (has_rows) {
-      const int lrow = sj + 16 * wid + r16;
-      f32x4 yacc[NPT];
+      const int lrow = sj + 16 * rb + r16;
+      f32x4 yacc[NPW];
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) yacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NPW; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
+        for (int i = 0; i < NPW; ++i) {
+          const int pt = ph * NPW + i < NPT ? ph * NPW + i : 0;
           const uint4 h_h = *reinterpret_cast<const uint4*>(hT[0] + (pt * 16 + r16) * BP + ks * 32 + 8 * q);
           const uint4 h_l = *reinterpret_cast<const uint4*>(hT[1] + (pt * 16 + r16) * BP + ks * 32 + 8 * q);
-          yacc[pt] = mma3(h_h, h_l, ch[ks], cl[ks], yacc[pt]);
+          yacc[i] = mma3(h_h, h_l, ch[ks], cl[ks], yacc[i]);
         }
       if (exact) {
         const float s1 = csc[lrow];
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) yacc[pt] = yacc[pt] * s1;
+        for (int i = 0; i < NPW; ++i) yacc[i] = yacc[i] * s1;
       }
-      for (int k2 = 0; 2 * k2 <= wid; ++k2) {
+      for (int k2 = 0; 2 * k2 <= rb; ++k2) {
         const int b0 = 2 * k2, b1 = 2 * k2 + 1;
-        const bool live1 = b1 <= wid;
+        const bool live1 = b1 <= rb;
         f32x4 ga = f32x4{0.f, 0.f, 0.f, 0.f}, gb = ga;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -527,11 +537,11 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
           }
         }
         if (!exact) {
-          if (b0 == wid) {
+          if (b0 == rb) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) ga[jj] = 4 * q + jj <= r16 ? ga[jj] : 0.f;
           }
-          if (b1 == wid) {
+          if (b1 == rb) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) gb[jj] = 4 * q + jj <= r16 ? gb[jj] : 0.f;
           }
@@ -558,20 +568,23 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
         const uint16_t* xt0 = exact ? xl[0] : xh[0];
         const uint16_t* xt1 = exact ? xl[1] : xh[1];
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
+        for (int i = 0; i < NPW; ++i) {
+          const int pt = ph * NPW + i < NPT ? ph * NPW + i : 0;
           const uint2 lo0 = lds_tr4(xt0, XPn, b0 * 16 + 4 * q, pt * 16);
           const uint2 hi0 = lds_tr4(xt0, XPn, b1 * 16 + 4 * q, pt * 16);
           const uint2 lo1 = lds_tr4(xt1, XPn, b0 * 16 + 4 * q, pt * 16);
           const uint2 hi1 = lds_tr4(xt1, XPn, b1 * 16 + 4 * q, pt * 16);
-          yacc[pt] = mma3(make_uint4(lo0.x, lo0.y, hi0.x, hi0.y), make_uint4(lo1.x, lo1.y, hi1.x, hi1.y),
-                          mvh, mvl, yacc[pt]);
+          yacc[i] = mma3(make_uint4(lo0.x, lo0.y, hi0.x, hi0.y), make_uint4(lo1.x, lo1.y, hi1.x, hi1.y),
+                         mvh, mvl, yacc[i]);
         }
       }
       // row scale, y rows out (lane: row lrow, p = pt*16 + 4q .. +3)
       const float s2 = exact ? 1.0f : csc[lrow];
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-        const f32x4 o = yacc[pt] * s2;
+      for (int i = 0; i < NPW; ++i) {
+        const int pt = ph * NPW + i;
+        if (pt >= NPT) break;
+        const f32x4 o = yacc[i] * s2;
         buf_store16_nt(ybuf, static_cast<uint32_t>(lrow) * xrow + (pt * 16 + 4 * q) * 4,
                        __builtin_bit_cast(uint4, o));
       }
@@ -615,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
       store_stage(j + 1);
       store_state(j + 1);
       __syncthreads();
-      make_c(craw, (j + 1) * QS + 16 * wid + r16);
+      make_c(craw, (j + 1) * QS + 16 * rb + r16);
     }
   }
 }
