@@ -16,6 +16,14 @@
 
 namespace ssd {
 
+// eight bf16 scaled by eight factors (element i by w[i]), rounded back to bf16
+__device__ __forceinline__ uint4 scale_bf16x8_each(uint4 v, float4 w0, float4 w1) {
+  return make_uint4(pack_bf16x2(bf16_bits_to_f32(v.x & 0xFFFFu) * w0.x, bf16_bits_to_f32(v.x >> 16) * w0.y),
+                    pack_bf16x2(bf16_bits_to_f32(v.y & 0xFFFFu) * w0.z, bf16_bits_to_f32(v.y >> 16) * w0.w),
+                    pack_bf16x2(bf16_bits_to_f32(v.z & 0xFFFFu) * w1.x, bf16_bits_to_f32(v.z >> 16) * w1.y),
+                    pack_bf16x2(bf16_bits_to_f32(v.w & 0xFFFFu) * w1.z, bf16_bits_to_f32(v.w >> 16) * w1.w));
+}
+
 __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
   const uint32_t a[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
@@ -31,9 +39,9 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
 //   lambda_c  = e^{A u_c},
 // u_s = delta_1 + .. + delta_s over the chunk and u_c its total (the chunk's
 // own contribution to the state at its end, and its decay; the state-passing
-// kernel chains them).  The chunk is staged through LDS in two halves of up
-// to 128 tokens; both halves are loaded into registers at the start.  The
-// decay weight goes onto x (P columns) as it is staged.  Eight waves; wave w
+// kernel chains them).  The chunk is staged through LDS in quarters of up to
+// 64 tokens, loaded into registers two quarters ahead.  The decay weight goes
+// onto x (P columns) as it is staged.  Eight waves; wave w
 // owns n tiles 2(w%4), 2(w%4)+1 and p tiles 2(w/4), 2(w/4)+1 of the
 // transposed product D[n][p] = sum_s B_s[n] (w_s x_s[p]), so an accumulator
 // lane holds one p and four consecutive n: one 8-byte store of S_c (bf16;
@@ -48,7 +56,7 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
     float dt_max, uint16_t* __restrict__ states, float* __restrict__ decay,
     float2* __restrict__ tok, int T, int H, int G, int Q, int nc, int npairs) {
   constexpr int NTHR = 512, WW = 8;
-  constexpr int HS = 128;                   // tokens per staged half
+  constexpr int HS = 64;                    // tokens per staged quarter
   constexpr int XPn = P + 16, BPn = N + 16;  // pitches (bf16 elements)
   constexpr int PT = P / 16, NT = N / 16;
   // wave tile block: NTW n tiles x PTW p tiles
@@ -72,7 +80,7 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
   const int wid = wave_id();
   const int ng = wid % NGW, pg = wid / NGW;
 
-  // ---- loads: dt first, then both halves of x and B ----
+  // ---- loads: dt first, then the first two quarters of x and B ----
   const size_t r0 = static_cast<size_t>(b) * T + t0;
   const float dtv = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
   const uint32_t xrow = static_cast<uint32_t>(H) * P * 2;
@@ -81,15 +89,15 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
                               static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
   const buf_t bbuf = make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N,
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
-  BufSlab<HS, P / 8, NTHR> xs0, xs1;
-  BufSlab<HS, N / 8, NTHR> bs0, bs1;
-  const bool two = Q > HS;
-  xs0.load(xbuf, xrow, 0);
-  bs0.load(bbuf, brow, 0);
-  if (two) {
-    xs1.load(xbuf, xrow, HS);
-    bs1.load(bbuf, brow, HS);
-  }
+  BufSlab<HS, P / 8, NTHR> xs[2];
+  BufSlab<HS, N / 8, NTHR> bs[2];
+  const int nq = (Q + HS - 1) / HS;  // quarters of the chunk
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (i < nq) {
+      xs[i].load(xbuf, xrow, i * HS);
+      bs[i].load(bbuf, brow, i * HS);
+    }
   const float a_re = A[h];
   const float bias = dt_bias ? dt_bias[h] : 0.0f;
 
@@ -112,7 +120,7 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
   if (tid < Q) tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid] = make_float2(a_re * u, d);
   __syncthreads();
 
-  // half -> LDS (x scaled by w_s; rows past the chunk are zero)
+  // quarter -> LDS (x scaled by w_s; rows past the chunk are zero)
   auto stage = [&](const BufSlab<HS, P / 8, NTHR>& xs, const BufSlab<HS, N / 8, NTHR>& bs, int s0) {
 #pragma unroll
     for (int i = 0; i < xs.PER; ++i) {
@@ -136,7 +144,7 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
   for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int j = 0; j < PTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // one half on MFMA: contraction over its tokens, all operand reads of a
+  // one quarter on MFMA: contraction over its tokens, all operand reads of a
   // 32-token step issued before the step's MFMAs
   auto mma = [&](int rows) {
     for (int ks = 0; ks < rows; ks += 32) {
@@ -162,16 +170,18 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
           if (pg * PTW + j < PT) acc[i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
     }
   };
-  const int rows0 = Q < HS ? Q : HS;
-  stage(xs0, bs0, 0);
-  __syncthreads();
-  mma(rows0);
-  if (two) {
-    __syncthreads();
-    stage(xs1, bs1, HS);
-    __syncthreads();
-    mma(Q - HS);
-  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < nq) {
+      if (i > 0) __syncthreads();
+      stage(xs[i & 1], bs[i & 1], i * HS);
+      if (i + 2 < nq) {
+        xs[i & 1].load(xbuf, xrow, (i + 2) * HS);
+        bs[i & 1].load(bbuf, brow, (i + 2) * HS);
+      }
+      __syncthreads();
+      mma(Q - i * HS < HS ? Q - i * HS : HS);
+    }
 
   // S_c: lane holds p = pt*16 + r16, n = nt*16 + 4q .. +3
   uint16_t* dst = states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N);
@@ -261,28 +271,30 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
 // sub-chunk).
 //
 // Decay factoring.  With the pivot m = j0 + QS/2 - 1 of the sub-chunk,
-// e^{cs_l - cs_s} = e^{cs_l - cs_m} e^{cs_m - cs_s}.  The second factor scales
-// x_s once when the sub-chunk is staged (x^ = x e^{cs_m - cs_s} delta); the
-// first is common to every term of output row l, carried one included when
-// the state is kept as H = e^{cs_m - cs_{j0-1}} h_j (one factor per
-// sub-chunk), so
-//   y_l = e^{cs_l - cs_m} (C_l . H + sum_{s <= l} (C_l . B_s) x^_s) + D x_l
-// -- raw C everywhere, the causal mask only on diagonal blocks, one scale per
-// output row at the end.  The state update accumulates x^ B^T into H.  The
+// e^{cs_l - cs_s} = e^{cs_l - cs_m} e^{cs_m - cs_s}.  The second factor (times
+// delta_s) is one weight w_s per source token; the first is common to every
+// term of output row l, carried one included when the state is kept as
+// H = e^{cs_m - cs_{j0-1}} h_j (one factor per sub-chunk), so
+//   y_l = e^{cs_l - cs_m} (C_l . H + sum_{s <= l} (C_l . B_s) w_s x_s) + D x_l
+// -- raw C and raw x everywhere, the causal mask only on diagonal blocks, w_s
+// on the columns of the masked (C_l . B_s) block before it is rounded to bf16,
+// one scale per output row at the end.  The state update accumulates
+// (w_s B_s) x_s^T into H, w_s applied to the B operand in registers.  Only
+// raw x is staged, one tile that also supplies D x_l.  The
 // factors stay below e^60 when every half sub-chunk decays by at most e^60;
 // when a chunk breaks that bound the workgroup switches to exact mode
 // (per-element exponentials against raw x, the carried term scaled by
-// e^{cs_l - cs_{j0-1}}, the state kept unscaled).
+// e^{cs_l - cs_{j0-1}}, the state kept unscaled, w_s = e^{cs_j1 - cs_s} delta_s).
 //
 // The output tile is computed transposed, Y^T[p][l]: wave w owns output rows
 // l = 16w .. 16w+15 of each sub-chunk as accumulator columns, so a lane holds
 // one row l (one scale factor) and four consecutive p (one 8-byte store of y).
 // Per 32 source tokens, G^T = B_s . C_l^T on MFMA (C rows in registers,
 // prefetched a sub-chunk ahead) leaves column l in the lane, which after the
-// mask is the B operand of Y^T += X^T M^T.  For the state update wave w owns
-// n tiles w, w+4, ..: H^T[n][p] += sum_s B_s[n] x^_s[p] (operands from LDS by
-// the transpose read); a lane holds 4 consecutive n of one p and writes the
-// bf16 state tile with 8-byte stores.
+// mask and the weights is the B operand of Y^T += X^T M^T.  For the state
+// update wave w owns n tiles w, w+4, ..: H^T[n][p] += sum_s (w_s B_s[n]) x_s[p]
+// (operands from LDS by the transpose read); a lane holds 4 consecutive n of
+// one p and writes the bf16 state tile with 8-byte stores.
 // ---------------------------------------------------------------------------
 template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
@@ -301,12 +313,11 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t bt[QSM * BP];
   __shared__ __attribute__((aligned(16))) uint16_t xl[QSM * XPn];  // raw x
-  __shared__ __attribute__((aligned(16))) uint16_t xh[QSM * XPn];  // x * xsc
   __shared__ __attribute__((aligned(16))) uint16_t hT[P * BP];
   __shared__ __attribute__((aligned(16))) float dl[256];
   __shared__ __attribute__((aligned(16))) float cs[256];   // A u_l
   __shared__ __attribute__((aligned(16))) float csc[256];  // output row scale
-  __shared__ __attribute__((aligned(16))) float xsc[256];  // x row scale
+  __shared__ __attribute__((aligned(16))) float xsc[256];  // source token weight w_s
   __shared__ float kpre[4], kpost[4];                       // state factors per sub-chunk
   __shared__ int exact_flag;
 
@@ -446,10 +457,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       const int it = tid + i * kThreads;
       if (xs.ITEMS % kThreads == 0 || it < xs.ITEMS) {
         const int v = it % (P / 8), sl = it / (P / 8);
-        const int s = j * QS + sl;
-        const float w = (sl < QS && s < Q) ? xsc[s] : 0.0f;
         *reinterpret_cast<uint4*>(xl + sl * XPn + v * 8) = xs.v[i];
-        *reinterpret_cast<uint4*>(xh + sl * XPn + v * 8) = scale_bf16x8(xs.v[i], w);
       }
     }
   };
@@ -522,6 +530,10 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
         }
         // lane: column l = r16 (+16 wid), rows s = 4q + jj of blocks b0, b1
         if (!exact) {
+          const float4 wa = *reinterpret_cast<const float4*>(xsc + sj + b0 * 16 + 4 * q);
+          const float4 wb = *reinterpret_cast<const float4*>(xsc + sj + b1 * 16 + 4 * q);
+          ga = ga * f32x4{wa.x, wa.y, wa.z, wa.w};
+          gb = gb * f32x4{wb.x, wb.y, wb.z, wb.w};
           if (b0 == wid) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) ga[jj] = 4 * q + jj <= r16 ? ga[jj] : 0.f;
@@ -547,11 +559,10 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
         }
         const uint4 mv = make_uint4(pack_bf16x2(ga[0], ga[1]), pack_bf16x2(ga[2], ga[3]),
                                     pack_bf16x2(gb[0], gb[1]), pack_bf16x2(gb[2], gb[3]));
-        const uint16_t* xs_tile = exact ? xl : xh;
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
-          const uint2 lo = lds_tr4(xs_tile, XPn, b0 * 16 + 4 * q, pt * 16);
-          const uint2 hi = lds_tr4(xs_tile, XPn, b1 * 16 + 4 * q, pt * 16);
+          const uint2 lo = lds_tr4(xl, XPn, b0 * 16 + 4 * q, pt * 16);
+          const uint2 hi = lds_tr4(xl, XPn, b1 * 16 + 4 * q, pt * 16);
           yacc[pt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(mv),
                                yacc[pt]);
         }
@@ -581,18 +592,21 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
           for (int pt = 0; pt < NPT; ++pt) hacc[i][pt] = hacc[i][pt] * kp;
       }
       for (int k = 0; k < QS; k += 32) {
+        // weights of this lane's source tokens sj + k + 8q .. +7
+        const float4 w0 = *reinterpret_cast<const float4*>(xsc + sj + k + 8 * q);
+        const float4 w1 = *reinterpret_cast<const float4*>(xsc + sj + k + 8 * q + 4);
         uint4 bfr[KTW];
 #pragma unroll
         for (int i = 0; i < KTW; ++i) {
           const int nt = wid + 4 * i;
           const uint2 lo = lds_tr4(bt, BP, k + 8 * q, (nt < KT ? nt : 0) * 16);
           const uint2 hi = lds_tr4(bt, BP, k + 8 * q + 4, (nt < KT ? nt : 0) * 16);
-          bfr[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          bfr[i] = scale_bf16x8_each(make_uint4(lo.x, lo.y, hi.x, hi.y), w0, w1);
         }
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
-          const uint2 lo = lds_tr4(xh, XPn, k + 8 * q, pt * 16);
-          const uint2 hi = lds_tr4(xh, XPn, k + 8 * q + 4, pt * 16);
+          const uint2 lo = lds_tr4(xl, XPn, k + 8 * q, pt * 16);
+          const uint2 hi = lds_tr4(xl, XPn, k + 8 * q + 4, pt * 16);
           const uint4 afr = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
           for (int i = 0; i < KTW; ++i)
