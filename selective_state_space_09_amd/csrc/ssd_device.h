@@ -149,10 +149,19 @@ __device__ __forceinline__ void rot_cs(double ang, float& c, float& s) {
 // Raw buffer access (gfx9 buffer descriptor, dword3 0x00020000): offsets are
 // bytes from `base`; loads at or past `bytes` return zero and stores there are
 // dropped, which bounds every access to the described range.
+// The descriptor lives in scalar registers: base and bytes must be the same in
+// every lane of the wave.  They are taken from the first lane explicitly, so
+// that values the compiler computes in vector registers (64-bit address
+// arithmetic) do not turn each access into a per-lane loop.
 typedef __amdgpu_buffer_rsrc_t buf_t;
 __device__ __forceinline__ buf_t make_buf(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* pu = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, static_cast<short>(0),
+                                           static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           0x00020000);
 }
 __device__ __forceinline__ uint4 buf_load16(buf_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
