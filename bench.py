@@ -102,6 +102,16 @@ def source_sha256():
     return h.hexdigest()
 
 
+def copy_reference(torch, dev):
+    """One plain 256 MiB device-to-device copy: the reference the HBM byte
+    counters are scaled by."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` (FETCH + WRITE, rocprofv3 counters
     scaled by a plain copy of known size) from profiles/traffic_<workload>.json,
@@ -350,11 +360,7 @@ def main():
         "wall_ms_per_step_incl_flush": t_wall / args.steps * 1e3,
     }
     if args.copy_ref:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_reference(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, dims, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -403,7 +409,11 @@ def bench_decode(args, cfg):
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS,
                         "traffic": measured_traffic("decode_f32", "ssd_decode_kernel"),
-                        "kernel": "ssd_decode_kernel"}}
+                        "kernel": "ssd_decode_kernel"},
+           "kernels": {"ssd_decode_kernel": {"avg_us": ms * 1e3, "alg_bytes": nbytes,
+                                             "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}}}
+    if args.copy_ref:
+        copy_reference(torch, dev)
     print(json.dumps(out), flush=True)
 
 
