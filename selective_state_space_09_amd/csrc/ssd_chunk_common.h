@@ -18,12 +18,8 @@ constexpr int kXCD = 8;    // XCDs of an MI355X
 template <typename E>
 struct Pad;
 template <>
-struct Pad<uint16_t> {
-  static constexpr int row = 8;  // bf16 elements of padding per LDS row
-};
-template <>
 struct Pad<float> {
-  static constexpr int row = 4;
+  static constexpr int row = 4;  // fp32 elements of padding per LDS row
 };
 
 // (b, c, h) of work unit `id` under the XCD-grouped order: consecutive ids go
@@ -66,37 +62,26 @@ inline void launch_k(bool run, F kernel, dim3 grid, dim3 block, hipStream_t st,
 }
 
 // ---------------------------------------------------------------------------
-// Per-chunk prologue: step sizes and cumulative decay exponents.
+// Per-chunk prologue of the fp32 kernels: step sizes and cumulative decay
+// exponents.
 //
 // Thread l < Q handles token l of the chunk (l >= Lc is padding: step 0); d is
 // its raw dt (loaded by the caller, ignored for l >= Lc).  Writes dl[l] (step
-// size), cs_hi/cs_lo[l] (double-float of the inclusive cumulative exponent:
-// A*sum(delta) real, alpha*sum(delta) complex) and, for the complex form, the
-// cosine/sine of theta_l = beta * sum(delta).  Returns this thread's
-// cumulative sum (double) and stores the chunk total in *tot.
+// size) and cs_hi/cs_lo[l] (double-float of the inclusive cumulative exponent
+// A*sum(delta)).  Returns this thread's cumulative exponent (double) and
+// stores the chunk total in *tot.
 // ---------------------------------------------------------------------------
-template <bool CPLX>
-__device__ __forceinline__ double chunk_prologue(float dt_raw, int Lc, float a_re, float a_im,
-                                                 float bias, float lo, float hi, float* dl,
-                                                 float* cs_hi, float* cs_lo, float* cth,
-                                                 float* sth, double* wsum, double* tot, int Q) {
+__device__ __forceinline__ double chunk_prologue(float dt_raw, int Lc, float a_re, float bias,
+                                                 float lo, float hi, float* dl, float* cs_hi,
+                                                 float* cs_lo, double* wsum, double* tot, int Q) {
   const int l = threadIdx.x;
   const float d = l < Lc ? step_size(dt_raw, bias, lo, hi) : 0.0f;
-  const double v = CPLX ? static_cast<double>(d)
-                        : static_cast<double>(a_re) * static_cast<double>(d);
-  const double cum = block_inclusive_scan(v, wsum);  // u (complex) or A*u (real)
+  const double cum = block_inclusive_scan(static_cast<double>(a_re) * static_cast<double>(d), wsum);
   if (l < Q) {
     dl[l] = d;
-    const double e = CPLX ? static_cast<double>(a_re) * cum : cum;
-    const float ehi = static_cast<float>(e);
+    const float ehi = static_cast<float>(cum);
     cs_hi[l] = ehi;
-    cs_lo[l] = static_cast<float>(e - static_cast<double>(ehi));
-    if (CPLX) {
-      float c, s;
-      rot_cs(static_cast<double>(a_im) * cum, c, s);
-      cth[l] = c;
-      sth[l] = s;
-    }
+    cs_lo[l] = static_cast<float>(cum - static_cast<double>(ehi));
     if (l == Q - 1) *tot = cum;
   }
   __syncthreads();
@@ -159,31 +144,7 @@ struct BufSlab {
   }
 };
 
-// x slab -> xT[p][s - s0]  (transposed, s contiguous).  bf16: item = 2 rows x
-// 8 columns, packed as (row s, row s+1) pairs per 32-bit LDS write.
-template <int ST, int P>
-struct XSlabBF : Slab<ST, P / 8, 2> {
-  __device__ __forceinline__ void store(uint16_t* xT) const {
-    constexpr int XP = ST + Pad<uint16_t>::row;
-#pragma unroll
-    for (int i = 0; i < this->PER; ++i) {
-      const int it = threadIdx.x + i * kThreads;
-      if (it >= this->ITEMS) break;
-      const int pg = it % (P / 8), sp = it / (P / 8);
-      const uint4 r0 = this->v[i][0], r1 = this->v[i][1];
-      const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
-      const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo_pair = (a[j] & 0xFFFFu) | (b[j] << 16);
-        const uint32_t hi_pair = (a[j] >> 16) | (b[j] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(xT + (pg * 8 + 2 * j) * XP + 2 * sp) = lo_pair;
-        *reinterpret_cast<uint32_t*>(xT + (pg * 8 + 2 * j + 1) * XP + 2 * sp) = hi_pair;
-      }
-    }
-  }
-};
-
+// x slab -> xT[p][s - s0]  (transposed, s contiguous).
 template <int ST, int P>
 struct XSlabF32 : Slab<ST, P / 4, 1> {
   __device__ __forceinline__ void store(float* xT) const {
@@ -201,10 +162,6 @@ struct XSlabF32 : Slab<ST, P / 4, 1> {
     }
   }
 };
-
-template <typename TI, int ST, int P>
-using XSlab = typename std::conditional<std::is_same<TI, uint16_t>::value, XSlabBF<ST, P>,
-                                        XSlabF32<ST, P>>::type;
 
 // ---------------------------------------------------------------------------
 // Kernel 2: inter-chunk scan of states, in place.

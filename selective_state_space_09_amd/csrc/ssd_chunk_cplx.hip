@@ -72,7 +72,7 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
   const int wid = wave_id();
   const int kp = wid % NKP, pg = wid / NKP;
 
-  // ---- loads: dt first, then both halves of x and B ----
+  // ---- loads: dt first, then the first two quarters of x and B ----
   const size_t r0 = static_cast<size_t>(b) * T + t0;
   const float dtv = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
   const uint32_t xrow = static_cast<uint32_t>(H) * P * 4;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
   }
   __syncthreads();
 
-  // half -> LDS: x scaled by w and split; B rotated by e^{-i theta}, split
+  // quarter -> LDS: x scaled by w and split; B rotated by e^{-i theta}, split
   auto stage = [&](const BufSlab<HS, P / 4, NTHR>& xs, const BufSlab<HS, N / 2, NTHR>& bs, int s0) {
 #pragma unroll
     for (int i = 0; i < xs.PER; ++i) {

@@ -20,12 +20,8 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
-// float32 -> bfloat16 by the hardware conversion (v_cvt_pk_bf16_f32: round
-// to nearest, ties to even, in the default rounding mode).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
-
+// two float32 -> bfloat16 by the hardware conversion (v_cvt_pk_bf16_f32:
+// round to nearest, ties to even, in the default rounding mode)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;
   v[0] = static_cast<__bf16>(lo);
@@ -37,14 +33,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ float load_elem(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float load_elem(const uint16_t* p, size_t i) {
-  return bf16_bits_to_f32(p[i]);
-}
-__device__ __forceinline__ void store_elem(float* p, size_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void store_elem(uint16_t* p, size_t i, float v) {
-  p[i] = f32_to_bf16_bits(v);
-}
 
 // Step size of one token: softplus(dt + bias) = ln(1 + e^z), evaluated as
 // max(z, 0) + ln(1 + e^-|z|), then clamped to [lo, hi] (Numerical Stability
