@@ -54,6 +54,8 @@ def _load():
     lib.ssd_oracle_step.restype = I
     lib.ssd_oracle_step.argtypes = [P, P, P, P, P, P, P, P, Dd, Dd, P,
                                     I, I, I, I, I]
+    lib.ssd_oracle_complex_step.restype = I
+    lib.ssd_oracle_complex_step.argtypes = [P, P, P, P, P, P, P, Dd, Dd, P, I, I, I, I, I]
     lib.ssd_oracle_threads_used.restype = I
     lib.ssd_oracle_set_threads.argtypes = [I]
     _lib = lib
@@ -168,6 +170,30 @@ def step(h, x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=float("inf"
     rc = lib.ssd_oracle_step(_ptr(h), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                              _ptr(D), _ptr(dt_bias), float(dt_min), float(dt_max),
                              _ptr(y), Bsz, H, P, G, N)
+    if rc:
+        raise ValueError("oracle rejected the sizes")
+    return y
+
+
+def complex_step(h, x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=float("inf")):
+    """One complex decode step on a float64 state h (Bsz,H,P,N,2) of (re, im)
+    pairs, updated in place.  x (Bsz,H,P), dt (Bsz,H), A (H,2), B/C (Bsz,G,N,2)
+    float32.  Returns y = Re(C . h) (Bsz,H,P) after the update."""
+    lib = _load()
+    if h.dtype != np.float64 or not h.flags.c_contiguous or h.shape[-1] != 2:
+        raise TypeError("h must be a C-contiguous float64 (..., 2) array")
+    x = _c(x, np.float32)
+    dt = _c(dt, np.float32)
+    A = _c(A, np.float32)
+    B = _c(B, np.float32)
+    C = _c(C, np.float32)
+    dt_bias = _c(dt_bias, np.float32)
+    Bsz, H, P, N, _ = h.shape
+    G = B.shape[1]
+    y = np.empty((Bsz, H, P), np.float64)
+    rc = lib.ssd_oracle_complex_step(_ptr(h), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                     _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(y),
+                                     Bsz, H, P, G, N)
     if rc:
         raise ValueError("oracle rejected the sizes")
     return y

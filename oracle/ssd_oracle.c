@@ -265,3 +265,54 @@ int ssd_oracle_step(double *hstate, const float *x, const float *dt, const float
     }
     return 0;
 }
+
+/*
+ * One complex recurrent step (single-token decode, Mamba-3-Lite README: the
+ * complex promotion of the recurrence) on a float64 complex state held by the
+ * caller as (re, im) pairs, updated in place:
+ *   h[b,h,p,n] <- exp((alpha_h + i beta_h) delta) h + B[b,g,n] x[b,h,p]
+ *   y[b,h,p]    = Re(sum_n C[b,g,n] h[b,h,p,n])
+ * (no step factor on the input, no D, readout after the update -- the
+ * readings of the complex forward above).  x (Bsz,H,P), dt (Bsz,H) float32;
+ * A (H,2), B/C (Bsz,G,N,2) float32 (re, im); h (Bsz,H,P,N,2).
+ */
+int ssd_oracle_complex_step(double *hstate, const float *x, const float *dt, const float *A,
+                            const float *B, const float *C, const float *dt_bias,
+                            double dt_min, double dt_max, double *y,
+                            int Bsz, int H, int P, int G, int N)
+{
+    if (Bsz <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G)
+        return 1;
+    const int hpg = H / G;
+    const long long BH = (long long)Bsz * H;
+#pragma omp parallel
+    {
+#pragma omp single
+        record_threads();
+#pragma omp for schedule(static)
+        for (long long bh = 0; bh < BH; ++bh) {
+            const int b = (int)(bh / H), h = (int)(bh % H), g = h / hpg;
+            const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+            const double delta = ssd_oracle_delta((double)dt[bh], bias, dt_min, dt_max);
+            const double mag = exp((double)A[2 * h] * delta);
+            const double ar = mag * cos((double)A[2 * h + 1] * delta);
+            const double ai = mag * sin((double)A[2 * h + 1] * delta);
+            const float *Bv = B + ((size_t)b * G + g) * N * 2;
+            const float *Cv = C + ((size_t)b * G + g) * N * 2;
+            for (int p = 0; p < P; ++p) {
+                const double xp = (double)x[(size_t)bh * P + p];
+                double *s = hstate + ((size_t)bh * P + p) * N * 2;
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    const double sr = ar * s[2 * n] - ai * s[2 * n + 1] + (double)Bv[2 * n] * xp;
+                    const double si = ar * s[2 * n + 1] + ai * s[2 * n] + (double)Bv[2 * n + 1] * xp;
+                    s[2 * n] = sr;
+                    s[2 * n + 1] = si;
+                    acc += (double)Cv[2 * n] * sr - (double)Cv[2 * n + 1] * si; /* Re(c * s) */
+                }
+                y[(size_t)bh * P + p] = acc;
+            }
+        }
+    }
+    return 0;
+}

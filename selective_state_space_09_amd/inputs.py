@@ -35,6 +35,9 @@ WORKLOADS = {
                       chunk=256, dtype="bf16"),
     # single-token recurrent decode at the BitMamba shape, 64 steps in place
     "decode_f32": dict(kind="decode", Bsz=256, H=64, P=64, N=128, G=1, steps=64),
+    # complex decode at the Mamba-3-Lite head shape; 1024 sequences so that the
+    # complex64 state (537 MB) exceeds the 256 MB Infinity Cache like the real one
+    "decode_complex": dict(kind="complex_decode", Bsz=1024, H=16, P=64, N=64, G=16, steps=64),
 }
 
 DT_MIN = 1e-3
@@ -144,6 +147,31 @@ def make_decode(Bsz, H, P, N, G=1, steps=1, seed=0, **_ignored):
                 dims=dict(Bsz=Bsz, H=H, P=P, G=G, N=N))
 
 
+def make_complex_decode(Bsz, H, P, N, G=None, steps=1, seed=0, **_ignored):
+    """Inputs of the complex single-token decode workload.
+
+    State h (Bsz,H,P,N,2) with real and imaginary parts ~ N(0, 1/2) float32;
+    A as in ``make_complex``; then per step x (Bsz,H,P) ~ N(0,1), dt_raw
+    (Bsz,H) ~ N(0,1) with no bias and clamp [1e-3, 1e-1], B, C (Bsz,G,N,2)
+    with parts ~ N(0, 1/2).
+    """
+    if G is None:
+        G = H
+    rng = np.random.default_rng(seed)
+    a_re = -np.exp(rng.uniform(math.log(0.5), math.log(4.0), size=H))
+    a_im = rng.uniform(-math.pi, math.pi, size=H)
+    A = np.stack([a_re, a_im], axis=-1).astype(np.float32)
+    s = math.sqrt(0.5)
+    h0 = _normal(rng, (Bsz, H, P, N, 2), s)
+    per_step = []
+    for _ in range(steps):
+        per_step.append(dict(x=_normal(rng, (Bsz, H, P)), dt=_normal(rng, (Bsz, H)),
+                             B=_normal(rng, (Bsz, G, N, 2), s),
+                             C=_normal(rng, (Bsz, G, N, 2), s)))
+    return dict(kind="complex_decode", h0=h0, A=A, D=None, dt_bias=None, dt_min=DT_MIN,
+                dt_max=DT_MAX, steps=per_step, dims=dict(Bsz=Bsz, H=H, P=P, G=G, N=N))
+
+
 def make_workload(name, seed=0, **overrides):
     """Inputs for a named workload (see WORKLOADS), with optional overrides."""
     cfg = dict(WORKLOADS[name])
@@ -153,4 +181,6 @@ def make_workload(name, seed=0, **overrides):
         return make_real(seed=seed, **cfg)
     if kind == "complex":
         return make_complex(seed=seed, **cfg)
+    if kind == "complex_decode":
+        return make_complex_decode(seed=seed, **cfg)
     return make_decode(seed=seed, **cfg)

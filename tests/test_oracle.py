@@ -347,6 +347,66 @@ def test_decode_steps_equal_forward():
     np.testing.assert_allclose(h, hf, rtol=1e-14, atol=1e-14)
 
 
+def _cstep(h, st, inp):
+    return oracle.complex_step(h, st["x"], st["dt"], inp["A"], st["B"], st["C"], inp["dt_bias"],
+                               inp["dt_min"], inp["dt_max"])
+
+
+def test_complex_decode_steps_equal_forward():
+    """k complex decode steps from h0 give the complex forward scan's y and
+    final state over the same k tokens (groups shared by two heads)."""
+    k = 5
+    ci = _cplx(T=k, H=4, G=2, with_h0=True, seed=53)
+    y, hf = _run_cplx(ci)
+    h = ci["h0"].astype(np.float64).copy()
+    for t in range(k):
+        st = dict(x=ci["x"][:, t], dt=ci["dt"][:, t], B=ci["B"][:, t], C=ci["C"][:, t])
+        yt = _cstep(h, st, ci)
+        np.testing.assert_allclose(yt, y[:, t], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(h, hf, rtol=1e-14, atol=1e-14)
+
+
+def test_complex_decode_step_complex128():
+    """One step against numpy complex128 arithmetic written out from the
+    recurrence: h' = e^{A delta} h + B x, y = Re(sum_n C_n h'_n)."""
+    inp = inputs.make_complex_decode(2, 3, 5, 8, G=3, steps=1, seed=54)
+    st = inp["steps"][0]
+    h = inp["h0"].astype(np.float64).copy()
+    y = _cstep(h, st, inp)
+    hc = inp["h0"][..., 0].astype(np.float64) + 1j * inp["h0"][..., 1].astype(np.float64)
+    A = inp["A"][:, 0].astype(np.float64) + 1j * inp["A"][:, 1].astype(np.float64)
+    d = _forms.deltas(st["dt"], None, inp["dt_min"], inp["dt_max"])  # (Bsz, H)
+    Bc = st["B"][..., 0].astype(np.float64) + 1j * st["B"][..., 1].astype(np.float64)
+    Cc = st["C"][..., 0].astype(np.float64) + 1j * st["C"][..., 1].astype(np.float64)
+    a = np.exp(A[None, :] * d)  # (Bsz, H)
+    hn = a[:, :, None, None] * hc + Bc[:, :, None, :] * st["x"].astype(np.float64)[..., None]
+    yr = np.real(np.einsum("bhpn,bhn->bhp", hn, Cc))
+    np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(h[..., 0] + 1j * h[..., 1], hn, rtol=1e-12, atol=1e-13)
+
+
+def test_complex_decode_closed_forms():
+    """A = 0: the state gains B x exactly.  alpha = 0 and B = 0: every state
+    element keeps its modulus and turns by beta * delta."""
+    inp = inputs.make_complex_decode(1, 2, 3, 4, G=2, steps=1, seed=55)
+    st = dict(inp["steps"][0])
+    inp0 = dict(inp, A=np.zeros_like(inp["A"]))
+    h = inp["h0"].astype(np.float64).copy()
+    _cstep(h, st, inp0)
+    gain = st["B"].astype(np.float64)[:, :, None, :, :] * st["x"].astype(np.float64)[..., None, None]
+    np.testing.assert_array_equal(h, inp["h0"].astype(np.float64) + gain)
+    inp1 = dict(inp, A=np.array([[0.0, 2.5], [0.0, -0.75]], np.float32))
+    st1 = dict(st, B=np.zeros_like(st["B"]))
+    h = inp["h0"].astype(np.float64).copy()
+    _cstep(h, st1, inp1)
+    h0 = inp["h0"][..., 0].astype(np.float64) + 1j * inp["h0"][..., 1].astype(np.float64)
+    got = h[..., 0] + 1j * h[..., 1]
+    np.testing.assert_allclose(np.abs(got), np.abs(h0), rtol=1e-14)
+    d = _forms.deltas(st["dt"], None, inp["dt_min"], inp["dt_max"])[0]
+    turn = np.exp(1j * np.array([2.5, -0.75]) * d)
+    np.testing.assert_allclose(got, h0 * turn[None, :, None, None], rtol=1e-13)
+
+
 def test_empty_sequence_returns_initial_state():
     inp = _real(T=0 + 1, with_h0=True)
     for k in ("x", "dt", "B", "C"):
