@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bitmamba_bf16",
                     choices=["bitmamba_bf16", "long_bf16", "mamba3lite_complex", "tiny_f32",
-                             "decode_f32"])
+                             "decode_f32", "decode_complex"])
     ap.add_argument("--no-flush", action="store_true",
                     help="keep the Infinity Cache warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -247,7 +247,7 @@ def main():
     from selective_state_space_09_amd import inputs
 
     cfg = dict(inputs.WORKLOADS[args.workload])
-    if cfg["kind"] == "decode":
+    if cfg["kind"] in ("decode", "complex_decode"):
         return bench_decode(args, cfg)
     inp = inputs.make_workload(args.workload, seed=0)
     Q = cfg["chunk"]
@@ -367,51 +367,67 @@ def main():
 
 
 def bench_decode(args, cfg):
-    """Decode workload: one step = one ssd_step_decode over the whole batch
-    (state 256 x 64 x 64 x 128 fp32 updated in place)."""
+    """Decode workloads: one step = one decode call over the whole batch, state
+    updated in place (real: 256 x 64 x 64 x 128 fp32; complex: 1024 x 16 x 64
+    x 64 complex64, both 537 MB, above the 256 MB Infinity Cache)."""
     import torch
     import selective_state_space_09_amd as ssd
     from selective_state_space_09_amd import inputs
-    inp = inputs.make_workload("decode_f32", seed=0, steps=1)
+    cplx = cfg["kind"] == "complex_decode"
+    inp = inputs.make_workload(args.workload, seed=0, steps=1)
     dev = torch.device("cuda:0")
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     h = up(inp["h0"])
     st = inp["steps"][0]
     x, dt, B, C = up(st["x"]), up(st["dt"]), up(st["B"]), up(st["C"])
-    A, D, bias = up(inp["A"]), up(inp["D"]), up(inp["dt_bias"])
-    Bsz, H, P, N = h.shape
+    A = up(inp["A"])
+    D = None if inp["D"] is None else up(inp["D"])
+    bias = None if inp["dt_bias"] is None else up(inp["dt_bias"])
+    Bsz, H, P, N = h.shape[:4]
     G = B.shape[1]
     y = torch.empty((Bsz, H, P), dtype=torch.float32, device=dev)
     L = ssd.lib()
     hip = Hip()
     sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    P_ = lambda t: ctypes.c_void_p(t.data_ptr())
-    args_c = (P_(h), P_(x), P_(dt), P_(A), P_(B), P_(C), P_(D), P_(bias),
-              float(inp["dt_min"]), float(inp["dt_max"]), P_(y), Bsz, H, P, G, N, sp)
+    P_ = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    if cplx:
+        fn = L.ssd_complex_step_decode_ev
+        args_c = (P_(h), P_(x), P_(dt), P_(A), P_(B), P_(C), P_(bias),
+                  float(inp["dt_min"]), float(inp["dt_max"]), P_(y), Bsz, H, P, G, N, sp)
+        kernel = "ssd_complex_decode_kernel"
+    else:
+        fn = L.ssd_step_decode_ev
+        args_c = (P_(h), P_(x), P_(dt), P_(A), P_(B), P_(C), P_(D), P_(bias),
+                  float(inp["dt_min"]), float(inp["dt_max"]), P_(y), Bsz, H, P, G, N, sp)
+        kernel = "ssd_decode_kernel"
     n_total = args.warmup + args.steps
     evs = [(hip.event(), hip.event()) for _ in range(n_total)]
     for i in range(n_total):
         arr = (ctypes.c_void_p * 2)(evs[i][0].value, evs[i][1].value)
-        rc = L.ssd_step_decode_ev(*args_c, arr)
+        rc = fn(*args_c, arr)
         if rc:
             raise RuntimeError(L.ssd_last_error().decode())
     torch.cuda.synchronize()
     times = [hip.elapsed_ms(a, b) for a, b in evs[args.warmup:]]
     ms = float(np.mean(times))
-    nbytes = 2 * h.numel() * 4 + Bsz * H * P * 8 + Bsz * H * 4 + 2 * Bsz * G * N * 4
+    # algorithmic bytes: the state read and written once, x and y, dt, and B/C
+    nbytes = (2 * h.numel() * 4 + Bsz * H * P * 8 + Bsz * H * 4
+              + 2 * Bsz * G * N * (8 if cplx else 4))
     gbs = nbytes / (ms / 1e3) / 1e9
-    out = {"metric": "SSD decode tokens/s (B256 H64 P64 N128)", "value": Bsz / (ms / 1e3),
+    shape = "B1024 H16 P64 N64 complex" if cplx else "B256 H64 P64 N128"
+    out = {"metric": f"SSD {'complex ' if cplx else ''}decode tokens/s ({shape})",
+           "value": Bsz / (ms / 1e3),
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "f32", "data": "synthetic",
-           "config": {"workload": "decode_f32", "batch": Bsz, "heads": H, "headdim": P,
-                      "d_state": N},
+           "dtype": "c64" if cplx else "f32", "data": "synthetic",
+           "config": {"workload": args.workload, "batch": Bsz, "heads": H, "headdim": P,
+                      "d_state": N, "ngroups": G},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS,
-                        "traffic": measured_traffic("decode_f32", "ssd_decode_kernel"),
-                        "kernel": "ssd_decode_kernel"},
-           "kernels": {"ssd_decode_kernel": {"avg_us": ms * 1e3, "alg_bytes": nbytes,
-                                             "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}}}
+                        "traffic": measured_traffic(args.workload, kernel),
+                        "kernel": kernel},
+           "kernels": {kernel: {"avg_us": ms * 1e3, "alg_bytes": nbytes,
+                                "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}}}
     if args.copy_ref:
         copy_reference(torch, dev)
     print(json.dumps(out), flush=True)

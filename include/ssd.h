@@ -185,6 +185,41 @@ int ssd_step_decode_ev(float *h, const float *x, const float *dt, const float *A
                        int Bsz, int H, int P, int G, int N, void *stream,
                        void *const *events);
 
+/*
+ * One recurrent step of the complex form for a single new token per sequence
+ * (the complex promotion of the recurrence in the Mamba-3-Lite README applied
+ * once), in place:
+ *   h[b,h,p,n] <- exp((A_re + i A_im) delta) h[b,h,p,n] + B[b,g,n] x[b,h,p]
+ *   y[b,h,p]    = Re(sum_n C[b,g,n] h[b,h,p,n])     (after the update)
+ * with delta = clamp(softplus(dt + dt_bias)) as in ssd_chunk_fwd, no step
+ * factor on the input and no D (the conventions of ssd_complex_chunk_fwd).
+ *   h        (Bsz, H, P, N, 2)  complex64 state as float32 (re, im) pairs,
+ *                               read and overwritten; 16-byte aligned
+ *   x        (Bsz, H, P)        float32
+ *   dt       (Bsz, H)           float32, raw step
+ *   A        (H, 2)             float32 (re, im)
+ *   B, C     (Bsz, G, N, 2)     float32 (re, im); 16-byte aligned
+ *   dt_bias  (H) or NULL
+ *   y        (Bsz, H, P)        float32
+ * N must be one of 16, 32, 64, 128; any P >= 1; H a multiple of G.  Needs no
+ * workspace.  Errors as for ssd_step_decode; nothing is launched on error.
+ */
+int ssd_complex_step_decode(float *h, const float *x, const float *dt, const float *A,
+                            const float *B, const float *C, const float *dt_bias,
+                            float dt_min, float dt_max, float *y,
+                            int Bsz, int H, int P, int G, int N, void *stream);
+
+/*
+ * Measurement variant of ssd_complex_step_decode: identical arguments, kernel
+ * and result, plus `events`, 2 hipEvent_t (passed as void*) bound to the
+ * kernel's dispatch on `stream` (start, stop), or NULL.
+ */
+int ssd_complex_step_decode_ev(float *h, const float *x, const float *dt, const float *A,
+                               const float *B, const float *C, const float *dt_bias,
+                               float dt_min, float dt_max, float *y,
+                               int Bsz, int H, int P, int G, int N, void *stream,
+                               void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,6 +56,10 @@ def lib():
     L.ssd_step_decode.argtypes = [P, P, P, P, P, P, P, P, F, F, P, I, I, I, I, I, P]
     L.ssd_step_decode_ev.restype = I
     L.ssd_step_decode_ev.argtypes = L.ssd_step_decode.argtypes + [P]
+    L.ssd_complex_step_decode.restype = I
+    L.ssd_complex_step_decode.argtypes = [P, P, P, P, P, P, P, F, F, P, I, I, I, I, I, P]
+    L.ssd_complex_step_decode_ev.restype = I
+    L.ssd_complex_step_decode_ev.argtypes = L.ssd_complex_step_decode.argtypes + [P]
     _lib = L
     return L
 
@@ -189,4 +193,23 @@ def ssd_step_decode(h, x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=
     _check(lib().ssd_step_decode(_ptr(h), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                                  _ptr(D), _ptr(dt_bias), float(dt_min), float(dt_max),
                                  _ptr(y), Bsz, H, P, G, N, _stream(stream)))
+    return y
+
+
+def ssd_complex_step_decode(h, x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=math.inf,
+                            y=None, stream=None):
+    """One complex decode step, state h (Bsz,H,P,N,2) float32 (re, im) updated
+    in place; x (Bsz,H,P), dt (Bsz,H), A (H,2), B/C (Bsz,G,N,2).  Returns
+    y = Re(C . h) (Bsz,H,P)."""
+    for t, n in ((h, "h"), (x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C")):
+        _dev(t, n, torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    Bsz, H, P, N, _ = h.shape
+    G = B.shape[1]
+    if y is None:
+        y = torch.empty((Bsz, H, P), dtype=torch.float32, device=h.device)
+    _dev(y, "y", torch.float32)
+    _check(lib().ssd_complex_step_decode(_ptr(h), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                         _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(y),
+                                         Bsz, H, P, G, N, _stream(stream)))
     return y

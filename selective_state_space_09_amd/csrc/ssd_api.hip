@@ -40,6 +40,7 @@ const int kNsReal[] = {16, 32, 64, 128};
 const int kNsCplx[] = {16, 32, 64};
 const int kChunks[] = {32, 64, 128, 256};
 const int kNsDecode[] = {16, 32, 64, 128, 256};
+const int kNsCplxDecode[] = {16, 32, 64, 128};
 
 // Shape checks shared by both chunked forwards.  Returns SSD_OK or an error.
 int check_chunk_shape(int Bsz, int T, int H, int P, int G, int N, int chunk, int is_complex) {
@@ -224,6 +225,38 @@ int ssd_step_decode_ev(float* h, const float* x, const float* dt, const float* A
   ssd::DecodeArgs a{h, x, dt, A, B, C, D, dt_bias, dt_min, dt_max, y, Bsz, H, P, G, N,
                     reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
   return launch_status(ssd::run_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssd_complex_step_decode(float* h, const float* x, const float* dt, const float* A,
+                            const float* B, const float* C, const float* dt_bias, float dt_min,
+                            float dt_max, float* y, int Bsz, int H, int P, int G, int N,
+                            void* stream) {
+  return ssd_complex_step_decode_ev(h, x, dt, A, B, C, dt_bias, dt_min, dt_max, y, Bsz, H, P, G,
+                                    N, stream, nullptr);
+}
+
+int ssd_complex_step_decode_ev(float* h, const float* x, const float* dt, const float* A,
+                               const float* B, const float* C, const float* dt_bias,
+                               float dt_min, float dt_max, float* y, int Bsz, int H, int P,
+                               int G, int N, void* stream, void* const* events) {
+  if (Bsz <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0)
+    return fail(SSD_EINVAL, "sizes must be positive: Bsz=%d H=%d P=%d G=%d N=%d", Bsz, H, P, G, N);
+  if (H % G != 0) return fail(SSD_EINVAL, "H=%d is not a multiple of G=%d", H, G);
+  if (!in_set(N, kNsCplxDecode, 4)) return fail(SSD_EUNSUPPORTED, "N=%d not in {16,32,64,128}", N);
+  if (static_cast<long long>(Bsz) * H > 2147483647LL)
+    return fail(SSD_EUNSUPPORTED, "Bsz*H too large");
+  SSD_TRY(check_ptr(h, "h", 16, true));
+  SSD_TRY(check_ptr(x, "x", 4, true));
+  SSD_TRY(check_ptr(dt, "dt", 4, true));
+  SSD_TRY(check_ptr(A, "A", 4, true));
+  SSD_TRY(check_ptr(B, "B", 16, true));
+  SSD_TRY(check_ptr(C, "C", 16, true));
+  SSD_TRY(check_ptr(y, "y", 4, true));
+  SSD_TRY(check_ptr(dt_bias, "dt_bias", 4, false));
+  SSD_TRY(check_clamp(dt_min, dt_max));
+  ssd::DecodeArgs a{h, x, dt, A, B, C, nullptr, dt_bias, dt_min, dt_max, y, Bsz, H, P, G, N,
+                    reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_complex_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -64,5 +64,6 @@ hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t run_complex_decode(const DecodeArgs& a, hipStream_t st);  // D unused
 
 }  // namespace ssd

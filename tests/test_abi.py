@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ssd_chunk_fwd", "ssd_complex_chunk_fwd", "ssd_step_decode",
-              "ssd_workspace_size", "ssd_last_error", "ssd_abi_version"):
+              "ssd_complex_step_decode", "ssd_workspace_size", "ssd_last_error",
+              "ssd_abi_version"):
         assert n in names
 
 
@@ -103,6 +104,29 @@ def test_decode_rejects():
     rc = L.ssd_step_decode(None, GOOD, GOOD, GOOD, GOOD, GOOD, None, None, 0.0, 1.0, GOOD,
                            2, 4, 16, 1, 128, None)
     assert rc == ssd.SSD_EINVAL and "h is NULL" in L.ssd_last_error().decode()
+
+
+def test_complex_decode_rejects():
+    """Argument checks of the complex decode step run before any HIP call."""
+    L = ssd.lib()
+    rc = L.ssd_complex_step_decode(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, 0.0, 1.0, GOOD,
+                                   2, 4, 16, 3, 64, None)
+    assert rc == ssd.SSD_EINVAL and "multiple" in L.ssd_last_error().decode()
+    rc = L.ssd_complex_step_decode(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, 0.0, 1.0, GOOD,
+                                   2, 4, 16, 1, 256, None)
+    assert rc == ssd.SSD_EUNSUPPORTED and "N=256" in L.ssd_last_error().decode()
+    rc = L.ssd_complex_step_decode(None, GOOD, GOOD, GOOD, GOOD, GOOD, None, 0.0, 1.0, GOOD,
+                                   2, 4, 16, 1, 64, None)
+    assert rc == ssd.SSD_EINVAL and "h is NULL" in L.ssd_last_error().decode()
+    rc = L.ssd_complex_step_decode(GOOD, GOOD, GOOD, GOOD, ctypes.c_void_p(_base + 8), GOOD, None, 0.0, 1.0, GOOD,
+                                   2, 4, 16, 1, 64, None)
+    assert rc == ssd.SSD_EINVAL and "B is not 16-byte aligned" in L.ssd_last_error().decode()
+    rc = L.ssd_complex_step_decode(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, 1.0, 0.5, GOOD,
+                                   2, 4, 16, 1, 64, None)
+    assert rc == ssd.SSD_EINVAL
+    rc = L.ssd_complex_step_decode(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, 0.0, 1.0, GOOD,
+                                   0, 4, 16, 1, 64, None)
+    assert rc == ssd.SSD_EINVAL and "positive" in L.ssd_last_error().decode()
 
 
 def test_workspace_size():

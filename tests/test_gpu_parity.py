@@ -312,6 +312,77 @@ def test_decode_small_shapes():
             assert state_err(h.cpu().numpy(), href) < TOL_F32
 
 
+def _cdecode_step_dev(h, st, A, bias, inp):
+    x, dt, B, C = (_gpu.to_dev(st[n]) for n in ("x", "dt", "B", "C"))
+    y = ssd.ssd_complex_step_decode(h, x, dt, A, B, C, bias, inp["dt_min"], inp["dt_max"])
+    torch.cuda.synchronize()
+    return y
+
+
+def test_complex_decode_workload_64_steps():
+    """The complex decode workload at full size (1024 sequences, H16 P64 N64,
+    537 MB complex64 state in place), 64 consecutive steps, checked after every
+    step on sampled batch rows that the oracle advances alongside."""
+    _print_case(workload="decode_complex")
+    inp = inputs.make_workload("decode_complex")
+    rows = [0, 1, 513, 1023]
+    h = _gpu.to_dev(inp["h0"])
+    A = _gpu.to_dev(inp["A"])
+    href = np.ascontiguousarray(inp["h0"][rows].astype(np.float64))
+    worst_y = worst_h = 0.0
+    for k, st in enumerate(inp["steps"]):
+        y = _cdecode_step_dev(h, st, A, None, inp)
+        sub = {n: np.ascontiguousarray(st[n][rows]) for n in ("x", "dt", "B", "C")}
+        yr = oracle.complex_step(href, sub["x"], sub["dt"], inp["A"], sub["B"], sub["C"], None,
+                                 inp["dt_min"], inp["dt_max"])
+        ey = state_err(y[rows].cpu().numpy(), yr)
+        eh = state_err(h[rows].cpu().numpy(), href)
+        worst_y, worst_h = max(worst_y, ey), max(worst_h, eh)
+        assert ey < TOL_F32, (k, ey)
+        assert eh < TOL_F32, (k, eh)
+    print("complex decode worst errors y=%.3g h=%.3g" % (worst_y, worst_h))
+
+
+def test_complex_decode_small_shapes():
+    """Every supported N, ragged P (1 and 5 rows), shared and per-head groups,
+    a step bias, three steps each, compared in full."""
+    for (Bsz, H, P, N, G) in [(3, 4, 16, 16, 2), (2, 2, 5, 32, 1), (1, 3, 64, 128, 3),
+                              (4, 2, 64, 64, 2), (2, 2, 1, 64, 2)]:
+        _print_case(kind="complex decode", shape=(Bsz, H, P, N, G))
+        inp = inputs.make_complex_decode(Bsz, H, P, N, G, steps=3, seed=15)
+        bias = np.linspace(-1.0, 1.0, H).astype(np.float32)
+        h = _gpu.to_dev(inp["h0"])
+        href = inp["h0"].astype(np.float64)
+        A, b_dev = _gpu.to_dev(inp["A"]), _gpu.to_dev(bias)
+        for st in inp["steps"]:
+            y = _cdecode_step_dev(h, st, A, b_dev, inp)
+            yr = oracle.complex_step(href, st["x"], st["dt"], inp["A"], st["B"], st["C"], bias,
+                                     inp["dt_min"], inp["dt_max"])
+            assert state_err(y.cpu().numpy(), yr) < TOL_F32
+            assert state_err(h.cpu().numpy(), href) < TOL_F32
+
+
+def test_complex_decode_continues_forward():
+    """A chunked complex prefill followed by complex decode steps equals the
+    complex oracle over the whole sequence (the forward's h_final feeds the
+    decode state)."""
+    _print_case(edge="complex prefill+decode")
+    inp = inputs.make_complex(2, 300, 4, 64, 64, G=4, seed=16, with_h0=False)
+    T0 = 292
+    pre = dict(inp)
+    for k in ("x", "dt", "B", "C"):
+        pre[k] = np.ascontiguousarray(inp[k][:, :T0])
+    _, hf = _gpu.run_complex(pre, 256)
+    h = _gpu.to_dev(hf.astype(np.float32))
+    A = _gpu.to_dev(inp["A"])
+    yr, hr = _oracle_cplx(inp)
+    for t in range(T0, 300):
+        st = {n: np.ascontiguousarray(inp[n][:, t]) for n in ("x", "dt", "B", "C")}
+        y = _cdecode_step_dev(h, st, A, None, inp)
+        assert state_err(y.cpu().numpy(), yr[:, t]) < TOL_F32
+    assert state_err(h.cpu().numpy(), hr) < TOL_F32
+
+
 def test_decode_continues_forward():
     """A chunked prefill followed by decode steps equals the oracle over the
     whole sequence (the forward's h_final feeds the decode state)."""
