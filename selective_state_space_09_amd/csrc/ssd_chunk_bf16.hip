@@ -303,7 +303,11 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
     int T, int H, int G, int Q, int nc, int npairs) {
   constexpr int QSM = 64;               // sub-chunk length (Q >= 64); Q = 32 runs one of 32
   constexpr int KCP = N < 32 ? 32 : N;  // K of G^T padded to whole 32-wide MFMA steps (zeros)
-  constexpr int BP = KCP + 8;           // pitch of bt / hT rows (bf16)
+  // row pitches (bf16): the B tile is read by rows (16 bytes a lane) and by the
+  // transpose read (4 rows x 32 bytes a 16-lane group), so its rows start 8
+  // banks apart; the state tile is read by rows only (4 banks apart suffice)
+  constexpr int BTP = KCP + 16;
+  constexpr int HTP = KCP + 8;
   constexpr int XPn = P + 16;           // pitch of the x tiles
   constexpr int NKS = KCP / 32;
   constexpr int NPT = P / 16;
@@ -311,9 +315,9 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   constexpr int KTW = (KT + 3) / 4;     // n tiles per wave in the state update
   constexpr float kMaxHalfSpread = 60.0f;
 
-  __shared__ __attribute__((aligned(16))) uint16_t bt[QSM * BP];
+  __shared__ __attribute__((aligned(16))) uint16_t bt[QSM * BTP];
   __shared__ __attribute__((aligned(16))) uint16_t xl[QSM * XPn];  // raw x
-  __shared__ __attribute__((aligned(16))) uint16_t hT[P * BP];
+  __shared__ __attribute__((aligned(16))) uint16_t hT[P * HTP];
   __shared__ __attribute__((aligned(16))) float dl[256];
   __shared__ __attribute__((aligned(16))) float cs[256];   // A u_l
   __shared__ __attribute__((aligned(16))) float csc[256];  // output row scale
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   if constexpr (KCP > N) {
     // zero the K padding of bt and hT (stage stores never write it)
     for (int it = tid; it < QSM + P; it += kThreads) {
-      uint16_t* row = it < QSM ? bt + it * BP : hT + (it - QSM) * BP;
+      uint16_t* row = it < QSM ? bt + it * BTP : hT + (it - QSM) * HTP;
       for (int k = N; k < KCP; ++k) row[k] = 0;
     }
   }
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       const int it = tid + i * kThreads;
       if (bs.ITEMS % kThreads == 0 || it < bs.ITEMS) {
         const int v = it % (N / 8), sl = it / (N / 8);
-        *reinterpret_cast<uint4*>(bt + sl * BP + v * 8) = bs.v[i];
+        *reinterpret_cast<uint4*>(bt + sl * BTP + v * 8) = bs.v[i];
       }
     }
 #pragma unroll
@@ -471,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
         hacc[i][pt] = hacc[i][pt] * k;
-        *reinterpret_cast<uint2*>(hT + (pt * 16 + r16) * BP + nt * 16 + 4 * q) =
+        *reinterpret_cast<uint2*>(hT + (pt * 16 + r16) * HTP + nt * 16 + 4 * q) =
             make_uint2(pack_bf16x2(hacc[i][pt][0], hacc[i][pt][1]),
                        pack_bf16x2(hacc[i][pt][2], hacc[i][pt][3]));
       }
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
-          const uint4 hv = *reinterpret_cast<const uint4*>(hT + (pt * 16 + r16) * BP + ks * 32 + 8 * q);
+          const uint4 hv = *reinterpret_cast<const uint4*>(hT + (pt * 16 + r16) * HTP + ks * 32 + 8 * q);
           yacc[pt] = mfma_bf16(as_bf16x8(hv), as_bf16x8(creg[ks]), yacc[pt]);
         }
       }
@@ -518,13 +522,13 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
         f32x4 ga = f32x4{0.f, 0.f, 0.f, 0.f}, gb = ga;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const uint4 va = *reinterpret_cast<const uint4*>(bt + (b0 * 16 + r16) * BP + ks * 32 + 8 * q);
+          const uint4 va = *reinterpret_cast<const uint4*>(bt + (b0 * 16 + r16) * BTP + ks * 32 + 8 * q);
           ga = mfma_bf16(as_bf16x8(va), as_bf16x8(creg[ks]), ga);
         }
         if (live1) {
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            const uint4 vb = *reinterpret_cast<const uint4*>(bt + (b1 * 16 + r16) * BP + ks * 32 + 8 * q);
+            const uint4 vb = *reinterpret_cast<const uint4*>(bt + (b1 * 16 + r16) * BTP + ks * 32 + 8 * q);
             gb = mfma_bf16(as_bf16x8(vb), as_bf16x8(creg[ks]), gb);
           }
         }
@@ -599,8 +603,8 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < KTW; ++i) {
           const int nt = wid + 4 * i;
-          const uint2 lo = lds_tr4(bt, BP, k + 8 * q, (nt < KT ? nt : 0) * 16);
-          const uint2 hi = lds_tr4(bt, BP, k + 8 * q + 4, (nt < KT ? nt : 0) * 16);
+          const uint2 lo = lds_tr4(bt, BTP, k + 8 * q, (nt < KT ? nt : 0) * 16);
+          const uint2 hi = lds_tr4(bt, BTP, k + 8 * q + 4, (nt < KT ? nt : 0) * 16);
           bfr[i] = scale_bf16x8_each(make_uint4(lo.x, lo.y, hi.x, hi.y), w0, w1);
         }
 #pragma unroll
