@@ -34,22 +34,26 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
 }
 
 // ---------------------------------------------------------------------------
-// Chunk states from a zero start, one workgroup per (batch, chunk, head):
+// Chunk states from a zero start, one workgroup per (batch, chunk, HPW heads
+// of one group):
 //   S_c[p][n] = sum_s x_s[p] e^{A (u_c - u_s)} delta_s B_s[n],
 //   lambda_c  = e^{A u_c},
 // u_s = delta_1 + .. + delta_s over the chunk and u_c its total (the chunk's
 // own contribution to the state at its end, and its decay; the state-passing
-// kernel chains them).  The chunk is staged through LDS in quarters of up to
-// 64 tokens, loaded into registers two quarters ahead.  The decay weight goes
-// onto x (P columns) as it is staged.  Eight waves; wave w
-// owns n tiles 2(w%4), 2(w%4)+1 and p tiles 2(w/4), 2(w/4)+1 of the
-// transposed product D[n][p] = sum_s B_s[n] (w_s x_s[p]), so an accumulator
-// lane holds one p and four consecutive n: one 8-byte store of S_c (bf16;
-// the output kernel rounds the carried state to bf16 for its MFMA in any
-// case).  The exponent sums are fp32 (a wave DPP scan): a sum of at most 256
-// positive steps carries a relative error of ~1e-6.
+// kernel chains them).  The heads of a workgroup share their B rows: B is
+// staged once and its MFMA operands are read once for all of them (HPW = 2
+// when the heads of a group pair up, which also halves the grid so that one
+// round of workgroups covers it at the BitMamba shape).  The chunk is staged
+// through LDS in quarters of up to 64 tokens, loaded into registers two
+// quarters ahead.  The decay weight goes onto x (P columns) as it is staged.
+// Eight waves; wave w owns n tiles 2(w%4), 2(w%4)+1 and p tiles 2(w/4),
+// 2(w/4)+1 of the transposed product D[n][p] = sum_s B_s[n] (w_s x_s[p]) of
+// every head, so an accumulator lane holds one p and four consecutive n: one
+// 8-byte store of S_c (bf16; the output kernel rounds the carried state to
+// bf16 for its MFMA in any case).  The exponent sums are fp32 (a wave DPP
+// scan): a sum of at most 256 positive steps carries a relative error of ~1e-6.
 // ---------------------------------------------------------------------------
-template <int P, int N>
+template <int P, int N, int HPW>
 __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min,
@@ -65,14 +69,15 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
   constexpr int PGW = WW / NGW;             // wave groups along p
   constexpr int PTW = (PT + PGW - 1) / PGW;
 
-  __shared__ __attribute__((aligned(16))) uint16_t xl[HS * XPn];  // w_s x_s
-  __shared__ __attribute__((aligned(16))) uint16_t bl[HS * BPn];  // B_s
-  __shared__ __attribute__((aligned(16))) float wsc[256];
-  __shared__ float wpart[WW];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[HPW][HS * XPn];  // w_s x_s per head
+  __shared__ __attribute__((aligned(16))) uint16_t bl[HS * BPn];       // B_s
+  __shared__ __attribute__((aligned(16))) float wsc[HPW][256];
+  __shared__ float wpart[HPW][WW];
 
-  int b, c, h;
-  if (!unit_of_block(H, nc, npairs, b, c, h)) return;
-  const int g = h / (H / G);
+  int b, c, hp;
+  if (!unit_of_block(H / HPW, nc, npairs, b, c, hp)) return;
+  const int h0 = hp * HPW;  // first head of the workgroup
+  const int g = h0 / (H / G);
   const int t0 = c * Q;
   const int Lc = min(Q, T - t0);
   const int tid = threadIdx.x;
@@ -82,73 +87,92 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
 
   // ---- loads: dt first, then the first two quarters of x and B ----
   const size_t r0 = static_cast<size_t>(b) * T + t0;
-  const float dtv = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
+  float dtv[HPW];
+#pragma unroll
+  for (int e = 0; e < HPW; ++e) dtv[e] = tid < Lc ? dt[(r0 + tid) * H + h0 + e] : 0.0f;
   const uint32_t xrow = static_cast<uint32_t>(H) * P * 2;
   const uint32_t brow = static_cast<uint32_t>(G) * N * 2;
-  const buf_t xbuf = make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
-                              static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+  buf_t xbuf[HPW];
+#pragma unroll
+  for (int e = 0; e < HPW; ++e)
+    xbuf[e] = make_buf(x + r0 * H * P + static_cast<size_t>(h0 + e) * P,
+                       static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
   const buf_t bbuf = make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N,
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
-  BufSlab<HS, P / 8, NTHR> xs[2];
+  BufSlab<HS, P / 8, NTHR> xs[2][HPW];
   BufSlab<HS, N / 8, NTHR> bs[2];
   const int nq = (Q + HS - 1) / HS;  // quarters of the chunk
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     if (i < nq) {
-      xs[i].load(xbuf, xrow, i * HS);
+#pragma unroll
+      for (int e = 0; e < HPW; ++e) xs[i][e].load(xbuf[e], xrow, i * HS);
       bs[i].load(bbuf, brow, i * HS);
     }
-  const float a_re = A[h];
-  const float bias = dt_bias ? dt_bias[h] : 0.0f;
 
-  // ---- step sizes and running sums (thread s = token s) ----
-  const float d = tid < Lc ? step_size(dtv, bias, dt_min, dt_max) : 0.0f;
-  float u = wave_inclusive_sum(d);
-  if (lane == kWave - 1) wpart[wid] = u;
-  __syncthreads();
-  float before = 0.0f, total = 0.0f;
+  // ---- step sizes and running sums (thread s = token s), per head ----
+  float dd[HPW], uu[HPW];
 #pragma unroll
-  for (int w = 0; w < WW; ++w) {
-    const float pw = wpart[w];
-    before += w < wid ? pw : 0.0f;
-    total += pw;
+  for (int e = 0; e < HPW; ++e) {
+    const float bias = dt_bias ? dt_bias[h0 + e] : 0.0f;
+    dd[e] = tid < Lc ? step_size(dtv[e], bias, dt_min, dt_max) : 0.0f;
+    uu[e] = wave_inclusive_sum(dd[e]);
+    if (lane == kWave - 1) wpart[e][wid] = uu[e];
   }
-  u += before;
-  if (tid < 256) wsc[tid] = __expf(a_re * (total - u)) * d;
-  if (tid == 0) decay[(static_cast<size_t>(b) * H + h) * nc + c] = __expf(a_re * total);
-  // (A u_l, delta_l) of every token for the output kernel (padding: delta 0)
-  if (tid < Q) tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid] = make_float2(a_re * u, d);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < HPW; ++e) {
+    const int h = h0 + e;
+    const float a_re = A[h];
+    float before = 0.0f, total = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WW; ++w) {
+      const float pw = wpart[e][w];
+      before += w < wid ? pw : 0.0f;
+      total += pw;
+    }
+    const float u = uu[e] + before;
+    if (tid < 256) wsc[e][tid] = __expf(a_re * (total - u)) * dd[e];
+    if (tid == 0) decay[(static_cast<size_t>(b) * H + h) * nc + c] = __expf(a_re * total);
+    // (A u_l, delta_l) of every token for the output kernel (padding: delta 0)
+    if (tid < Q) tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid] = make_float2(a_re * u, dd[e]);
+  }
   __syncthreads();
 
   // quarter -> LDS (x scaled by w_s; rows past the chunk are zero)
-  auto stage = [&](const BufSlab<HS, P / 8, NTHR>& xs, const BufSlab<HS, N / 8, NTHR>& bs, int s0) {
+  auto stage = [&](const BufSlab<HS, P / 8, NTHR> (&xsq)[HPW], const BufSlab<HS, N / 8, NTHR>& bsq,
+                   int s0) {
 #pragma unroll
-    for (int i = 0; i < xs.PER; ++i) {
-      const int it = tid + i * NTHR;
-      const int v = it % (P / 8), sl = it / (P / 8);
-      if (xs.ITEMS % NTHR == 0 || it < xs.ITEMS)
-        *reinterpret_cast<uint4*>(xl + sl * XPn + v * 8) =
-            scale_bf16x8(xs.v[i], s0 + sl < Q ? wsc[s0 + sl] : 0.0f);
-    }
+    for (int e = 0; e < HPW; ++e)
 #pragma unroll
-    for (int i = 0; i < bs.PER; ++i) {
+      for (int i = 0; i < xsq[e].PER; ++i) {
+        const int it = tid + i * NTHR;
+        const int v = it % (P / 8), sl = it / (P / 8);
+        if (xsq[e].ITEMS % NTHR == 0 || it < xsq[e].ITEMS)
+          *reinterpret_cast<uint4*>(xl[e] + sl * XPn + v * 8) =
+              scale_bf16x8(xsq[e].v[i], s0 + sl < Q ? wsc[e][s0 + sl] : 0.0f);
+      }
+#pragma unroll
+    for (int i = 0; i < bsq.PER; ++i) {
       const int it = tid + i * NTHR;
       const int v = it % (N / 8), sl = it / (N / 8);
-      if (bs.ITEMS % NTHR == 0 || it < bs.ITEMS)
-        *reinterpret_cast<uint4*>(bl + sl * BPn + v * 8) = bs.v[i];
+      if (bsq.ITEMS % NTHR == 0 || it < bsq.ITEMS)
+        *reinterpret_cast<uint4*>(bl + sl * BPn + v * 8) = bsq.v[i];
     }
   };
 
-  f32x4 acc[NTW][PTW];
+  f32x4 acc[HPW][NTW][PTW];
 #pragma unroll
-  for (int i = 0; i < NTW; ++i)
+  for (int e = 0; e < HPW; ++e)
 #pragma unroll
-    for (int j = 0; j < PTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int j = 0; j < PTW; ++j) acc[e][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // one quarter on MFMA: contraction over its tokens, all operand reads of a
-  // 32-token step issued before the step's MFMAs
+  // 32-token step issued before the step's MFMAs; the B operands serve every head
   auto mma = [&](int rows) {
     for (int ks = 0; ks < rows; ks += 32) {
-      uint4 af[NTW], bf[PTW];
+      uint4 af[NTW], bf[HPW][PTW];
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
         const int nt = ng * NTW + i;
@@ -157,17 +181,22 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
         af[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
 #pragma unroll
-      for (int j = 0; j < PTW; ++j) {
-        const int pt = pg * PTW + j < PT ? pg * PTW + j : 0;
-        const uint2 lo = lds_tr4(xl, XPn, ks + 8 * q, pt * 16);
-        const uint2 hi = lds_tr4(xl, XPn, ks + 8 * q + 4, pt * 16);
-        bf[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
+      for (int e = 0; e < HPW; ++e)
 #pragma unroll
-      for (int i = 0; i < NTW; ++i)
+        for (int j = 0; j < PTW; ++j) {
+          const int pt = pg * PTW + j < PT ? pg * PTW + j : 0;
+          const uint2 lo = lds_tr4(xl[e], XPn, ks + 8 * q, pt * 16);
+          const uint2 hi = lds_tr4(xl[e], XPn, ks + 8 * q + 4, pt * 16);
+          bf[e][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
 #pragma unroll
-        for (int j = 0; j < PTW; ++j)
-          if (pg * PTW + j < PT) acc[i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+      for (int e = 0; e < HPW; ++e)
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+#pragma unroll
+          for (int j = 0; j < PTW; ++j)
+            if (pg * PTW + j < PT)
+              acc[e][i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bf[e][j]), acc[e][i][j]);
     }
   };
 #pragma unroll
@@ -176,7 +205,8 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
       if (i > 0) __syncthreads();
       stage(xs[i & 1], bs[i & 1], i * HS);
       if (i + 2 < nq) {
-        xs[i & 1].load(xbuf, xrow, (i + 2) * HS);
+#pragma unroll
+        for (int e = 0; e < HPW; ++e) xs[i & 1][e].load(xbuf[e], xrow, (i + 2) * HS);
         bs[i & 1].load(bbuf, brow, (i + 2) * HS);
       }
       __syncthreads();
@@ -184,16 +214,20 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
     }
 
   // S_c: lane holds p = pt*16 + r16, n = nt*16 + 4q .. +3
-  uint16_t* dst = states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N);
 #pragma unroll
-  for (int i = 0; i < NTW; ++i)
+  for (int e = 0; e < HPW; ++e) {
+    uint16_t* dst = states + ((static_cast<size_t>(b) * nc + c) * H + h0 + e) * (static_cast<size_t>(P) * N);
 #pragma unroll
-    for (int j = 0; j < PTW; ++j) {
-      const int nt = ng * NTW + i, pt = pg * PTW + j;
-      if (pt < PT)
-        *reinterpret_cast<uint2*>(dst + (pt * 16 + r16) * N + nt * 16 + 4 * q) =
-            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
-    }
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int j = 0; j < PTW; ++j) {
+        const int nt = ng * NTW + i, pt = pg * PTW + j;
+        if (pt < PT)
+          *reinterpret_cast<uint2*>(dst + (pt * 16 + r16) * N + nt * 16 + 4 * q) =
+              make_uint2(pack_bf16x2(acc[e][i][j][0], acc[e][i][j][1]),
+                         pack_bf16x2(acc[e][i][j][2], acc[e][i][j][3]));
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -645,9 +679,15 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st) {
   const uint16_t* C = static_cast<const uint16_t*>(a.C);
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
   const hipEvent_t* ev = a.events;
-  launch_k(nc > 0, ssd_state_bf16_kernel<P, N>, dim3(blocks), dim3(512), st, ev, x, a.dt, a.A,
-           B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G, a.chunk, nc,
-           npairs);
+  // chunk states: two heads per workgroup when the heads of a group pair up
+  if ((a.H / a.G) % 2 == 0)
+    launch_k(nc > 0, ssd_state_bf16_kernel<P, N, 2>, dim3(blocks / 2), dim3(512), st, ev, x, a.dt,
+             a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G, a.chunk,
+             nc, npairs);
+  else
+    launch_k(nc > 0, ssd_state_bf16_kernel<P, N, 1>, dim3(blocks), dim3(512), st, ev, x, a.dt,
+             a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G, a.chunk,
+             nc, npairs);
   launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel,
            dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
            ev ? ev + 2 : nullptr, states, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
