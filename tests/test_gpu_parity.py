@@ -69,6 +69,11 @@ REAL_CASES = [
     (1, 1, 2, 32, 32, 1, 32, True, True, True),
     (1, 256, 2, 64, 64, 1, 256, True, True, True),
     (3, 513, 4, 64, 128, 1, 256, True, True, True),
+    # 16 chunks: the last size whose boundary states the bf16 output kernel
+    # forms itself; 17 and 18 chunks: the state-passing kernel
+    (1, 1024, 2, 64, 128, 1, 64, True, True, True),
+    (2, 1100, 2, 64, 128, 1, 64, True, True, True),
+    (1, 2100, 4, 32, 64, 2, 128, False, True, True),
 ]
 
 
@@ -194,9 +199,9 @@ def test_chained_calls_equal_one_call():
 
 
 def test_workspace_contents_do_not_matter():
-    """The bf16 path keeps per-(batch, head) chunk counters in the workspace
-    (tagged per call): a workspace of random bytes gives the oracle's result,
-    and reusing it for further calls gives bit-identical results."""
+    """The bf16 path keeps chunk states, decays and per-token tables in the
+    workspace: a workspace of random bytes gives the oracle's result, and
+    reusing it for further calls gives bit-identical results."""
     _print_case(edge="workspace reuse", dtype="bf16")
     inp = inputs.make_real(2, 700, 4, 64, 128, 1, dtype="bf16", seed=9, with_h0=True)
     d = _gpu.upload(inp)
