@@ -56,6 +56,8 @@ def _load():
                                     I, I, I, I, I]
     lib.ssd_oracle_complex_step.restype = I
     lib.ssd_oracle_complex_step.argtypes = [P, P, P, P, P, P, P, Dd, Dd, P, I, I, I, I, I]
+    lib.ssd_oracle_conv1d.restype = I
+    lib.ssd_oracle_conv1d.argtypes = [P, ctypes.c_longlong, P, P, P, I, P, P, I, I, I, I, I]
     lib.ssd_oracle_threads_used.restype = I
     lib.ssd_oracle_set_threads.argtypes = [I]
     _lib = lib
@@ -197,3 +199,43 @@ def complex_step(h, x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=float("inf"
     if rc:
         raise ValueError("oracle rejected the sizes")
     return y
+
+
+def conv1d(xbc, w, bias=None, state_in=None, act=1, ch=None):
+    """Depthwise causal convolution.  xbc (Bsz,T,ld) float32 or uint16
+    (bfloat16 bits), of which channels 0..ch-1 are used (ch = ld by default);
+    w (ch,K) float32, bias (ch) or None, state_in (Bsz,K-1,ch) float32 or
+    None; act 1 = SiLU, 0 = none.  Returns (out (Bsz,T,ch), state_out
+    (Bsz,K-1,ch)) as float64."""
+    lib = _load()
+    if xbc.dtype == np.uint16:
+        dtype = 1
+    elif xbc.dtype == np.float32:
+        dtype = 0
+    else:
+        raise TypeError("xbc must be float32 or uint16 bfloat16 bits")
+    xbc = _c(xbc, xbc.dtype)
+    w = _c(w, np.float32)
+    bias = _c(bias, np.float32)
+    state_in = _c(state_in, np.float32)
+    Bsz, T, ld = xbc.shape
+    ch = ld if ch is None else int(ch)
+    K = w.shape[1]
+    if w.shape[0] != ch:
+        raise ValueError("w must be (ch, K)")
+    out = np.empty((Bsz, T, ch), np.float64)
+    st = np.empty((Bsz, K - 1, ch), np.float64)
+    rc = lib.ssd_oracle_conv1d(_ptr(xbc), ld, _ptr(w), _ptr(bias), _ptr(state_in), int(act),
+                               _ptr(out), _ptr(st), Bsz, T, ch, K, dtype)
+    if rc:
+        raise ValueError("oracle rejected the sizes")
+    return out, st
+
+
+def conv1d_step(state, xt, w, bias=None, act=1):
+    """One decode step of the convolution: the segment of length 1.  state
+    (Bsz,K-1,ch) float32 inputs that preceded the token, xt (Bsz,ch) float32.
+    Returns (out (Bsz,ch), new state (Bsz,K-1,ch)) as float64."""
+    xt = np.ascontiguousarray(xt, np.float32)
+    out, st = conv1d(xt[:, None, :], w, bias, state, act)
+    return out[:, 0, :], st

@@ -316,3 +316,70 @@ int ssd_oracle_complex_step(double *hstate, const float *x, const float *dt, con
     }
     return 0;
 }
+
+/*
+ * Depthwise causal convolution of the Mamba-1/2 layer (Mamba-3-Lite block
+ * page, section 5.1 "Zero causal convolution": before the scan, each channel's
+ * value at position t is replaced by a learned combination of that channel's
+ * values at positions t-K+1 .. t, K = 4).  Written out as the definition:
+ *
+ *   v[b,t,c]   = bias[c] + sum_{j=0..K-1} w[c,j] * in[b, t-K+1+j, c]
+ *   out[b,t,c] = act ? v / (1 + exp(-v)) : v        (SiLU when act = 1)
+ *
+ * where in[b,p,c] for p < 0 is state_in[b, K-1+p, c] (the inputs that preceded
+ * this segment; zero when state_in is NULL).  state_out[b,j,c] receives the raw
+ * input at position T-K+1+j (j = 0..K-2), taken from state_in when that
+ * position is negative, so that a sequence cut into segments gives the same
+ * output as the whole.
+ *
+ *   xbc (Bsz,T,ld) of dtype 0 (float32) or 1 (bfloat16 bits), channels
+ *   0..Ch-1 of each row used; w (Ch,K), bias (Ch) or NULL, state_in/state_out
+ *   (Bsz,K-1,Ch) or NULL; out (Bsz,T,Ch) double.
+ *
+ * Readings: the bias and the SiLU are those of the usual Mamba-2 layer (the
+ * pages name only the learned combination); the state holds raw inputs.
+ */
+int ssd_oracle_conv1d(const void *xbc, long long ld, const float *w, const float *bias,
+                      const float *state_in, int act, double *out, double *state_out,
+                      int Bsz, int T, int Ch, int K, int dtype)
+{
+    if (Bsz <= 0 || T < 0 || Ch <= 0 || K <= 0 || ld < Ch)
+        return 1;
+    const long long BC = (long long)Bsz * Ch;
+#pragma omp parallel
+    {
+#pragma omp single
+        record_threads();
+#pragma omp for schedule(static)
+        for (long long bc = 0; bc < BC; ++bc) {
+            const int b = (int)(bc / Ch), c = (int)(bc % Ch);
+            for (int t = 0; t < T; ++t) {
+                double v = bias ? (double)bias[c] : 0.0;
+                for (int j = 0; j < K; ++j) {
+                    const long long p = (long long)t - (K - 1) + j;
+                    double in;
+                    if (p >= 0)
+                        in = load_in(xbc, ((size_t)b * T + (size_t)p) * (size_t)ld + c, dtype);
+                    else
+                        in = state_in ? (double)state_in[((size_t)b * (K - 1) + (K - 1 + p)) * Ch + c] : 0.0;
+                    v += (double)w[(size_t)c * K + j] * in;
+                }
+                if (act == 1)
+                    v = v / (1.0 + exp(-v));
+                out[((size_t)b * T + t) * Ch + c] = v;
+            }
+            if (state_out) {
+                for (int j = 0; j < K - 1; ++j) {
+                    const long long p = (long long)T - (K - 1) + j;
+                    double in;
+                    if (p >= 0)
+                        in = load_in(xbc, ((size_t)b * T + (size_t)p) * (size_t)ld + c, dtype);
+                    else
+                        in = state_in ? (double)state_in[((size_t)b * (K - 1) + (K - 1 + p)) * Ch + c] : 0.0;
+                    state_out[((size_t)b * (K - 1) + j) * Ch + c] = in;
+                }
+            }
+        }
+    }
+    return 0;
+}

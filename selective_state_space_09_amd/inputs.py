@@ -38,6 +38,14 @@ WORKLOADS = {
     # complex decode at the Mamba-3-Lite head shape; 1024 sequences so that the
     # complex64 state (537 MB) exceeds the 256 MB Infinity Cache like the real one
     "decode_complex": dict(kind="complex_decode", Bsz=1024, H=16, P=64, N=64, G=16, steps=64),
+    # depthwise causal conv (K = 4, SiLU) of the BitMamba layer over its x|B|C
+    # channels (4096 + 128 + 128), read from the in_proj output row (width
+    # 2*4096 + 2*128 + 64 = 8512: z, x, B, C, dt) and split into the scan's inputs
+    "conv_bf16": dict(kind="conv", Bsz=2, T=2048, HP=4096, GN=128, ld=8512, K=4,
+                      dtype="bf16"),
+    # its single-token step at the decode batch of decode_f32, 64 steps in place
+    "conv_decode_f32": dict(kind="conv_decode", Bsz=256, HP=4096, GN=128, ld=8512, K=4,
+                            steps=64),
 }
 
 DT_MIN = 1e-3
@@ -172,6 +180,48 @@ def make_complex_decode(Bsz, H, P, N, G=None, steps=1, seed=0, **_ignored):
                 dt_max=DT_MAX, steps=per_step, dims=dict(Bsz=Bsz, H=H, P=P, G=G, N=N))
 
 
+def make_conv(Bsz, T, HP, GN, ld=None, K=4, dtype="f32", seed=0, with_state=True,
+              with_bias=True, **_ignored):
+    """Inputs of the depthwise causal convolution over the x|B|C channels
+    (Ch = HP + 2*GN).
+
+    xbc (Bsz,T,ld) ~ N(0,1) (channels Ch..ld-1 of each row belong to other
+    slices of the projection and are never read); w (Ch,K) and bias (Ch)
+    ~ U(-1/sqrt(K), 1/sqrt(K)) (the usual fan-in bound of a depthwise conv);
+    state_in (Bsz,K-1,Ch) ~ N(0,1) float32.  xbc is float32 or bfloat16 bits.
+    """
+    Ch = HP + 2 * GN
+    ld = Ch if ld is None else ld
+    rng = np.random.default_rng(seed)
+    xbc = _normal(rng, (Bsz, T, ld))
+    bound = 1.0 / math.sqrt(K)
+    w = rng.uniform(-bound, bound, size=(Ch, K)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, size=Ch).astype(np.float32) if with_bias else None
+    state_in = _normal(rng, (Bsz, K - 1, Ch)) if with_state else None
+    if dtype == "bf16":
+        xbc = f32_to_bf16_bits(xbc)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return dict(kind="conv", xbc=xbc, w=w, bias=bias, state_in=state_in, dtype=dtype,
+                dims=dict(Bsz=Bsz, T=T, HP=HP, GN=GN, ld=ld, K=K))
+
+
+def make_conv_decode(Bsz, HP, GN, ld=None, K=4, steps=1, seed=0, **_ignored):
+    """Inputs of the convolution's single-token step: w, bias and the state
+    (Bsz,K-1,Ch) as in ``make_conv``, then per step a row xt (Bsz,ld) ~ N(0,1)
+    float32."""
+    Ch = HP + 2 * GN
+    ld = Ch if ld is None else ld
+    rng = np.random.default_rng(seed)
+    bound = 1.0 / math.sqrt(K)
+    w = rng.uniform(-bound, bound, size=(Ch, K)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, size=Ch).astype(np.float32)
+    state0 = _normal(rng, (Bsz, K - 1, Ch))
+    per_step = [_normal(rng, (Bsz, ld)) for _ in range(steps)]
+    return dict(kind="conv_decode", w=w, bias=bias, state0=state0, steps=per_step,
+                dims=dict(Bsz=Bsz, HP=HP, GN=GN, ld=ld, K=K))
+
+
 def make_workload(name, seed=0, **overrides):
     """Inputs for a named workload (see WORKLOADS), with optional overrides."""
     cfg = dict(WORKLOADS[name])
@@ -183,4 +233,8 @@ def make_workload(name, seed=0, **overrides):
         return make_complex(seed=seed, **cfg)
     if kind == "complex_decode":
         return make_complex_decode(seed=seed, **cfg)
+    if kind == "conv":
+        return make_conv(seed=seed, **cfg)
+    if kind == "conv_decode":
+        return make_conv_decode(seed=seed, **cfg)
     return make_decode(seed=seed, **cfg)

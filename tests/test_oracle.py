@@ -414,3 +414,97 @@ def test_empty_sequence_returns_initial_state():
     y, hf = _run_real(inp)
     assert y.shape[1] == 0
     np.testing.assert_array_equal(hf, inp["h0"].astype(np.float64))
+
+
+# ---- depthwise causal convolution (Mamba-3-Lite block page, section 5.1) ----
+
+def _conv_in(**kw):
+    base = dict(Bsz=2, T=11, HP=8, GN=4, K=4, dtype="f32", seed=5)
+    base.update(kw)
+    return inputs.make_conv(**base)
+
+
+def test_conv_matches_numpy_convolve():
+    """Zero state, no activation: each channel is numpy's full discrete
+    convolution with the reversed taps, cut to the first T outputs, plus the
+    bias."""
+    d = _conv_in(with_state=False)
+    out, _ = oracle.conv1d(d["xbc"], d["w"], d["bias"], None, act=0)
+    Bsz, T, Ch = out.shape
+    for b in range(Bsz):
+        for c in range(Ch):
+            ref = np.convolve(d["xbc"][b, :, c].astype(np.float64),
+                              d["w"][c, ::-1].astype(np.float64))[:T] + float(d["bias"][c])
+            np.testing.assert_allclose(out[b, :, c], ref, rtol=0, atol=1e-12)
+
+
+def test_conv_silu_closed_form():
+    """Identity taps (only the current position), no bias: the output is
+    SiLU of the input, v * sigmoid(v) with scipy's logistic function."""
+    import scipy.special
+    d = _conv_in(with_bias=False)
+    K = d["w"].shape[1]
+    w = np.zeros_like(d["w"])
+    w[:, K - 1] = 1.0
+    out, _ = oracle.conv1d(d["xbc"], w, None, d["state_in"], act=1)
+    v = d["xbc"].astype(np.float64)
+    np.testing.assert_allclose(out, v * scipy.special.expit(v), rtol=1e-14, atol=1e-300)
+    z, _ = oracle.conv1d(np.zeros((1, 3, 2), np.float32), w[:2], None, None, act=1)
+    assert np.all(z == 0.0)
+
+
+def test_conv_delay_reads_state():
+    """Only the oldest tap set: the output is the input delayed by K-1
+    positions, the first K-1 outputs being the state that preceded the
+    segment, in order."""
+    d = _conv_in()
+    K = d["w"].shape[1]
+    w = np.zeros_like(d["w"])
+    w[:, 0] = 1.0
+    out, _ = oracle.conv1d(d["xbc"], w, None, d["state_in"], act=0)
+    full = np.concatenate([d["state_in"], d["xbc"]], axis=1).astype(np.float64)
+    np.testing.assert_array_equal(out, full[:, :out.shape[1]])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("cut", [0, 1, 2, 3, 7, 11])
+def test_conv_segments_chain(dtype, cut):
+    """A sequence cut anywhere (also inside the first K-1 positions) and run
+    as two segments, the second starting from the first one's state_out,
+    gives the whole sequence's output and final state; state_out is the last
+    K-1 raw inputs."""
+    d = _conv_in(dtype=dtype)
+    x = d["xbc"]
+    whole, st = oracle.conv1d(x, d["w"], d["bias"], d["state_in"], act=1)
+    o1, s1 = oracle.conv1d(np.ascontiguousarray(x[:, :cut]), d["w"], d["bias"], d["state_in"], act=1)
+    o2, s2 = oracle.conv1d(np.ascontiguousarray(x[:, cut:]), d["w"], d["bias"],
+                           s1.astype(np.float32), act=1)
+    np.testing.assert_array_equal(np.concatenate([o1, o2], axis=1), whole)
+    np.testing.assert_array_equal(s2, st)
+    xf = inputs.bf16_bits_to_f32(x) if dtype == "bf16" else x
+    np.testing.assert_array_equal(st, xf[:, -3:].astype(np.float64))
+
+
+def test_conv_row_stride_ignores_other_columns():
+    """Channels past ch of each row (other slices of the projection) are not
+    read: changing them changes nothing."""
+    d = _conv_in(ld=20)
+    a, sa = oracle.conv1d(d["xbc"], d["w"], d["bias"], d["state_in"], act=1, ch=16)
+    x2 = d["xbc"].copy()
+    x2[:, :, 16:] = 1e30
+    b, sb = oracle.conv1d(x2, d["w"], d["bias"], d["state_in"], act=1, ch=16)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(sa, sb)
+
+
+def test_conv_step_equals_prefill():
+    """Steps of one token chained through the state reproduce the prefill of
+    the whole segment."""
+    d = _conv_in(T=6)
+    whole, st = oracle.conv1d(d["xbc"], d["w"], d["bias"], d["state_in"], act=1)
+    s = d["state_in"]
+    for t in range(6):
+        o, s64 = oracle.conv1d_step(s, d["xbc"][:, t], d["w"], d["bias"], act=1)
+        np.testing.assert_array_equal(o, whole[:, t])
+        s = s64.astype(np.float32)
+    np.testing.assert_array_equal(s, st.astype(np.float32))
