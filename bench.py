@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bitmamba_bf16",
                     choices=["bitmamba_bf16", "long_bf16", "mamba3lite_complex", "tiny_f32",
-                             "decode_f32", "decode_complex"])
+                             "decode_f32", "decode_complex", "conv_bf16", "conv_decode_f32"])
     ap.add_argument("--no-flush", action="store_true",
                     help="keep the Infinity Cache warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -90,12 +90,28 @@ class Hip:
         return ms.value
 
 
-def source_sha256():
-    """Hash of the library's kernel sources (file names and contents)."""
+# Device code behind each workload's kernels: the kernel file and the device
+# headers every kernel file includes.  A traffic record stays valid while these
+# files hash the same.
+DEVICE_HEADERS = ["ssd_chunk_common.h", "ssd_device.h"]
+KERNEL_SOURCES = {
+    "bitmamba_bf16": ["ssd_chunk_bf16.hip"],
+    "long_bf16": ["ssd_chunk_bf16.hip"],
+    "tiny_f32": ["ssd_chunk.hip"],
+    "mamba3lite_complex": ["ssd_chunk_cplx.hip"],
+    "decode_f32": ["ssd_decode.hip"],
+    "decode_complex": ["ssd_decode.hip"],
+    "conv_bf16": ["ssd_conv.hip"],
+    "conv_decode_f32": ["ssd_conv.hip"],
+}
+
+
+def source_sha256(workload):
+    """Hash of the device sources of a workload's kernels (names and contents)."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "selective_state_space_09_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in sorted(KERNEL_SOURCES[workload] + DEVICE_HEADERS):
         h.update(f.encode())
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
@@ -122,7 +138,7 @@ def measured_traffic(workload, kernel):
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_sha256():
+    if rec.get("source_sha256") != source_sha256(workload):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k["fetch_bytes"] + k["write_bytes"]
@@ -269,6 +285,8 @@ def main():
     cfg = dict(inputs.WORKLOADS[args.workload])
     if cfg["kind"] in ("decode", "complex_decode"):
         return bench_decode(args, cfg)
+    if cfg["kind"] in ("conv", "conv_decode"):
+        return bench_conv(args, cfg)
     inp = inputs.make_workload(args.workload, seed=0)
     Q = cfg["chunk"]
     dims = dict(inp["dims"], Q=Q)
@@ -472,6 +490,123 @@ def bench_decode(args, cfg):
     if args.copy_ref:
         copy_reference(torch, dev)
     print(json.dumps(out), flush=True)
+
+
+def bench_conv(args, cfg):
+    """Convolution workloads.  conv_bf16: one step = one ssd_conv1d_fwd call
+    over the whole batch (B2 T2048, 4352 channels read from 8512-wide rows,
+    split into x/B/C).  conv_decode_f32: one step = one ssd_conv1d_step over
+    256 sequences, state in place.  The 512 MiB flush read runs between steps
+    in both (the step's data would otherwise sit in the Infinity Cache)."""
+    import torch
+    import selective_state_space_09_amd as ssd
+    from selective_state_space_09_amd import inputs
+    decode = cfg["kind"] == "conv_decode"
+    inp = inputs.make_workload(args.workload, seed=0, **({"steps": 1} if decode else {}))
+    dims = inp["dims"]
+    Bsz, HP, GN, ld = dims["Bsz"], dims["HP"], dims["GN"], dims["ld"]
+    Ch = HP + 2 * GN
+    T = 1 if decode else dims["T"]
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    w, bias = up(inp["w"]), up(inp["bias"])
+    L = ssd.lib()
+    hip = Hip()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P_ = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    if decode:
+        state = up(inp["state0"])
+        xt = up(inp["steps"][0])
+        x = torch.empty((Bsz, HP), dtype=torch.float32, device=dev)
+        B = torch.empty((Bsz, GN), dtype=torch.float32, device=dev)
+        C = torch.empty_like(B)
+        fn = L.ssd_conv1d_step_ev
+        args_c = (P_(state), P_(xt), ld, P_(w), P_(bias), 1, P_(x), P_(B), P_(C),
+                  Bsz, HP, GN, 4, sp)
+        kernel, es = "ssd_conv1d_step_kernel", 4
+        # state read and written, the token row's channels read, x|B|C written
+        nbytes = 2 * Bsz * 3 * Ch * 4 + 2 * Bsz * Ch * 4 + Ch * 20
+        dtype_name = "f32"
+    else:
+        xbc = up(inp["xbc"])
+        si = up(inp["state_in"])
+        so = torch.empty_like(si)
+        x = torch.empty((Bsz, T, HP), dtype=xbc.dtype, device=dev)
+        B = torch.empty((Bsz, T, GN), dtype=xbc.dtype, device=dev)
+        C = torch.empty_like(B)
+        dcode = ssd.SSD_BF16 if xbc.dtype == torch.bfloat16 else ssd.SSD_F32
+        es = 2 if dcode == ssd.SSD_BF16 else 4
+        fn = L.ssd_conv1d_fwd_ev
+        args_c = (P_(xbc), ld, P_(w), P_(bias), P_(si), 1, P_(x), P_(B), P_(C), P_(so),
+                  Bsz, T, HP, GN, 4, dcode, sp)
+        kernel = "ssd_conv1d_kernel"
+        # the used channels of every row read once, x|B|C written once, taps,
+        # bias and both states
+        nbytes = 2 * Bsz * T * Ch * es + Ch * 20 + 2 * Bsz * 3 * Ch * 4
+        dtype_name = "bf16" if es == 2 else "f32"
+    n_total = args.warmup + args.steps
+    evs = [(hip.event(), hip.event()) for _ in range(n_total)]
+    for i in range(n_total):
+        if flush is not None:
+            flush.max()
+        arr = (ctypes.c_void_p * 2)(evs[i][0].value, evs[i][1].value)
+        rc = fn(*args_c, arr)
+        if rc:
+            raise RuntimeError(L.ssd_last_error().decode())
+    torch.cuda.synchronize()
+    times = [hip.elapsed_ms(a, b) for a, b in evs[args.warmup:]]
+    ms = float(np.mean(times))
+    gbs = nbytes / (ms / 1e3) / 1e9
+    tokens = Bsz * T
+    out = {"metric": (f"conv1d {'decode step' if decode else 'fwd'} tokens/s "
+                      f"(k=4 SiLU over x|B|C, {Ch} channels)"),
+           "value": tokens / (ms / 1e3),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": dtype_name, "data": "synthetic",
+           "config": {"workload": args.workload, "batch": Bsz, "seq_len": T, "channels": Ch,
+                      "x_channels": HP, "bc_channels": GN, "row_stride": ld, "kernel_size": 4,
+                      "cache": "cold (Infinity Cache flushed between steps)"
+                      if flush is not None else "warm"},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": measured_traffic(args.workload, kernel),
+                        "kernel": kernel},
+           "kernels": {kernel: {"avg_us": ms * 1e3, "alg_bytes": nbytes,
+                                "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}}}
+    if args.copy_ref:
+        copy_reference(torch, dev)
+    if not decode and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_conv(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_conv(inp, target_s):
+    """The float64 oracle convolution over the whole workload, repeated until
+    about target_s/3 seconds have passed (one pass takes well under a second)."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    dims = inp["dims"]
+    Ch = dims["HP"] + 2 * dims["GN"]
+    reps, total = 0, 0.0
+    while total < target_s / 3:
+        t0 = time.perf_counter()
+        oracle.conv1d(inp["xbc"], inp["w"], inp["bias"], inp["state_in"], act=1, ch=Ch)
+        total += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * dims["Bsz"] * dims["T"] / total, "unit": "tokens/s",
+            "cores": oracle.threads_used(), "kind": "oracle",
+            "sample": f"the whole workload ({dims['Bsz']} x {dims['T']} tokens x {Ch} channels), "
+                      f"float64, {reps} passes in {total:.2f} s"}
 
 
 if __name__ == "__main__":

@@ -220,6 +220,74 @@ int ssd_complex_step_decode_ev(float *h, const float *x, const float *dt, const 
                                int Bsz, int H, int P, int G, int N, void *stream,
                                void *const *events);
 
+/*
+ * Depthwise causal convolution of the Mamba-2 layer (Mamba-3-Lite block page,
+ * section 5.1 "Zero causal convolution": before the scan, Mamba-1/2 replace
+ * each channel's value at position t by a learned combination of that
+ * channel's values at positions t-3 .. t).  Over the Ch = HP + 2*GN channels
+ * x|B|C of each token row:
+ *   v[b,t,c]   = bias[c] + sum_{j=0..3} w[c,j] * in[b, t-3+j, c]
+ *   out[b,t,c] = act ? v / (1 + exp(-v)) : v          (act 1 = SiLU)
+ * where in[b,p,c] for p < 0 is state_in[b, 3+p, c].  out is split into the
+ * three contiguous inputs of ssd_chunk_fwd: channels [0, HP) to x, [HP,
+ * HP+GN) to B, [HP+GN, Ch) to C.
+ *   xbc        (Bsz, T, ld) elements of `dtype` (SSD_F32 or SSD_BF16);
+ *              channels 0..Ch-1 of each row are read, the rest never (the
+ *              in_proj output row can be passed at the offset of its x slice)
+ *   w          (Ch, 4) float32 taps, oldest position first
+ *   bias       (Ch) float32, or NULL (zero)
+ *   state_in   (Bsz, 3, Ch) float32: raw inputs at positions -3, -2, -1, or
+ *              NULL (zeros: a fresh sequence)
+ *   x          (Bsz, T, HP) `dtype`        = (Bsz, T, H, P) of the scan
+ *   B, C       (Bsz, T, GN) `dtype`        = (Bsz, T, G, N); NULL if GN = 0
+ *   state_out  (Bsz, 3, Ch) float32: raw inputs at positions T-3 .. T-1 (from
+ *              state_in where negative), the state_in of the next segment or
+ *              of ssd_conv1d_step; or NULL.  Must not overlap state_in.
+ * K (kernel size) must be 4.  HP, GN and ld must be multiples of 8 (bf16) or
+ * 4 (fp32), ld >= Ch; xbc, x, B, C, w, bias and both states 16-byte aligned.
+ * T = 0 is allowed (only state_out is written).  Arithmetic in float32, one
+ * rounding to `dtype` on output.  Outputs must not overlap inputs.  Needs no
+ * workspace.  Errors: SSD_EINVAL (bad pointer, size, alignment, overlapping
+ * states), SSD_EUNSUPPORTED (K, dtype, channel counts, sizes past the 32-bit
+ * addressing of one batch entry's rows), SSD_EHIP; nothing runs on error.
+ */
+int ssd_conv1d_fwd(const void *xbc, long long ld, const float *w, const float *bias,
+                   const float *state_in, int act, void *x, void *B, void *C,
+                   float *state_out, int Bsz, int T, int HP, int GN, int K, int dtype,
+                   void *stream);
+
+/*
+ * Measurement variant of ssd_conv1d_fwd: identical arguments, kernel and
+ * result, plus `events`, 2 hipEvent_t (passed as void*) bound to the kernel's
+ * dispatch on `stream` (start, stop), or NULL.
+ */
+int ssd_conv1d_fwd_ev(const void *xbc, long long ld, const float *w, const float *bias,
+                      const float *state_in, int act, void *x, void *B, void *C,
+                      float *state_out, int Bsz, int T, int HP, int GN, int K, int dtype,
+                      void *stream, void *const *events);
+
+/*
+ * One decode step of the convolution (the segment of one token), in place:
+ *   state  (Bsz, 3, Ch) float32, read as positions t-3 .. t-1 and overwritten
+ *          with t-2 .. t (the state_out layout of ssd_conv1d_fwd)
+ *   xt     (Bsz, ld) float32 token rows (channels 0..Ch-1 read)
+ *   w, bias, act as in ssd_conv1d_fwd
+ *   x      (Bsz, HP), B, C (Bsz, GN) float32: the inputs of ssd_step_decode
+ * HP, GN and ld must be multiples of 4; pointers 16-byte aligned; K = 4.
+ * Errors as for ssd_conv1d_fwd.
+ */
+int ssd_conv1d_step(float *state, const float *xt, long long ld, const float *w,
+                    const float *bias, int act, float *x, float *B, float *C,
+                    int Bsz, int HP, int GN, int K, void *stream);
+
+/*
+ * Measurement variant of ssd_conv1d_step, with 2 hipEvent_t (start, stop)
+ * bound to the kernel's dispatch, or NULL.
+ */
+int ssd_conv1d_step_ev(float *state, const float *xt, long long ld, const float *w,
+                       const float *bias, int act, float *x, float *B, float *C,
+                       int Bsz, int HP, int GN, int K, void *stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,15 @@ def lib():
     L.ssd_complex_step_decode.argtypes = [P, P, P, P, P, P, P, F, F, P, I, I, I, I, I, P]
     L.ssd_complex_step_decode_ev.restype = I
     L.ssd_complex_step_decode_ev.argtypes = L.ssd_complex_step_decode.argtypes + [P]
+    LL = ctypes.c_longlong
+    L.ssd_conv1d_fwd.restype = I
+    L.ssd_conv1d_fwd.argtypes = [P, LL, P, P, P, I, P, P, P, P, I, I, I, I, I, I, P]
+    L.ssd_conv1d_fwd_ev.restype = I
+    L.ssd_conv1d_fwd_ev.argtypes = L.ssd_conv1d_fwd.argtypes + [P]
+    L.ssd_conv1d_step.restype = I
+    L.ssd_conv1d_step.argtypes = [P, P, LL, P, P, I, P, P, P, I, I, I, I, P]
+    L.ssd_conv1d_step_ev.restype = I
+    L.ssd_conv1d_step_ev.argtypes = L.ssd_conv1d_step.argtypes + [P]
     _lib = L
     return L
 
@@ -213,3 +222,84 @@ def ssd_complex_step_decode(h, x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=
                                          _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(y),
                                          Bsz, H, P, G, N, _stream(stream)))
     return y
+
+
+def _rows(t, name, ndim):
+    """A GPU tensor whose last dimension is contiguous and whose rows are
+    evenly spaced (a column slice of a wider row-major tensor is accepted).
+    Returns the row stride in elements."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() == ndim and t.numel() == 0:
+        return t.shape[-1]  # nothing is read
+    if t.dim() != ndim or t.stride(-1) != 1:
+        raise ValueError(f"{name} must have {ndim} dims with a contiguous last dim")
+    ld = t.stride(-2)
+    if ndim == 3 and t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) != t.shape[1] * ld:
+        raise ValueError(f"{name}: batch entries must follow each other (stride T*ld)")
+    return ld
+
+
+def ssd_conv1d_fwd(xbc, w, HP, GN, bias=None, state_in=None, act=1, x=None, B=None, C=None,
+                   state_out=None, stream=None):
+    """Depthwise causal convolution (kernel 4) over the Ch = HP + 2*GN
+    channels of xbc (Bsz,T,Ch) -- contiguous or a column slice of wider rows,
+    float32 or bfloat16 -- split into x (Bsz,T,HP), B and C (Bsz,T,GN).
+    w (Ch,4), bias (Ch), state_in/state_out (Bsz,3,Ch) float32.  act 1 = SiLU.
+    Returns (x, B, C, state_out); state_out is allocated when not given."""
+    ld = _rows(xbc, "xbc", 3)
+    Bsz, T, Ch = xbc.shape
+    if Ch != HP + 2 * GN:
+        raise ValueError(f"xbc has {Ch} channels, HP + 2*GN = {HP + 2 * GN}")
+    if xbc.dtype == torch.bfloat16:
+        dtype = SSD_BF16
+    elif xbc.dtype == torch.float32:
+        dtype = SSD_F32
+    else:
+        raise TypeError("xbc must be float32 or bfloat16")
+    _dev(w, "w", torch.float32)
+    _dev(bias, "bias", torch.float32)
+    _dev(state_in, "state_in", torch.float32)
+    dev = xbc.device
+    if x is None:
+        x = torch.empty((Bsz, T, HP), dtype=xbc.dtype, device=dev)
+    if B is None:
+        B = torch.empty((Bsz, T, GN), dtype=xbc.dtype, device=dev)
+    if C is None:
+        C = torch.empty((Bsz, T, GN), dtype=xbc.dtype, device=dev)
+    if state_out is None:
+        state_out = torch.empty((Bsz, 3, Ch), dtype=torch.float32, device=dev)
+    for t, n in ((x, "x"), (B, "B"), (C, "C")):
+        _dev(t, n, xbc.dtype)
+    _dev(state_out, "state_out", torch.float32)
+    _check(lib().ssd_conv1d_fwd(_ptr(xbc), ld, _ptr(w), _ptr(bias), _ptr(state_in), int(act),
+                                _ptr(x), _ptr(B), _ptr(C), _ptr(state_out), Bsz, T, HP, GN,
+                                w.shape[1], dtype, _stream(stream)))
+    return x, B, C, state_out
+
+
+def ssd_conv1d_step(state, xt, w, HP, GN, bias=None, act=1, x=None, B=None, C=None,
+                    stream=None):
+    """One decode step of the convolution on the float32 state (Bsz,3,Ch),
+    updated in place; xt (Bsz,Ch) float32, contiguous or a column slice.
+    Returns x (Bsz,HP), B, C (Bsz,GN) float32."""
+    _dev(state, "state", torch.float32)
+    ld = _rows(xt, "xt", 2)
+    if xt.dtype != torch.float32:
+        raise TypeError("xt must be float32")
+    _dev(w, "w", torch.float32)
+    _dev(bias, "bias", torch.float32)
+    Bsz = xt.shape[0]
+    dev = xt.device
+    if x is None:
+        x = torch.empty((Bsz, HP), dtype=torch.float32, device=dev)
+    if B is None:
+        B = torch.empty((Bsz, GN), dtype=torch.float32, device=dev)
+    if C is None:
+        C = torch.empty((Bsz, GN), dtype=torch.float32, device=dev)
+    for t, n in ((x, "x"), (B, "B"), (C, "C")):
+        _dev(t, n, torch.float32)
+    _check(lib().ssd_conv1d_step(_ptr(state), _ptr(xt), ld, _ptr(w), _ptr(bias), int(act),
+                                 _ptr(x), _ptr(B), _ptr(C), Bsz, HP, GN, w.shape[1],
+                                 _stream(stream)))
+    return x, B, C

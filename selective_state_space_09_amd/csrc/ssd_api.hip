@@ -260,3 +260,101 @@ int ssd_complex_step_decode_ev(float* h, const float* x, const float* dt, const 
 }
 
 }  // extern "C"
+
+// ---- depthwise causal convolution ----
+
+namespace {
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return a && b && x < y + nb && y < x + na;
+}
+
+// Checks shared by the prefill and the step.  V = channels per 16-byte vector.
+int check_conv_common(int Bsz, int HP, int GN, long long ld, int K, int act, int V) {
+  if (Bsz <= 0 || HP <= 0 || GN < 0)
+    return fail(SSD_EINVAL, "sizes must be positive (GN >= 0): Bsz=%d HP=%d GN=%d", Bsz, HP, GN);
+  if (K != 4) return fail(SSD_EUNSUPPORTED, "K=%d: only kernel size 4 is built", K);
+  if (act != 0 && act != 1) return fail(SSD_EINVAL, "act=%d not in {0, 1}", act);
+  if (HP % V != 0 || GN % V != 0)
+    return fail(SSD_EUNSUPPORTED, "HP=%d and GN=%d must be multiples of %d", HP, GN, V);
+  const long long Ch = static_cast<long long>(HP) + 2LL * GN;
+  if (Ch > 2147483647LL / 4) return fail(SSD_EUNSUPPORTED, "too many channels: %lld", Ch);
+  if (ld < Ch) return fail(SSD_EINVAL, "ld=%lld is smaller than HP + 2*GN = %lld", ld, Ch);
+  if (ld % V != 0) return fail(SSD_EINVAL, "ld=%lld is not a multiple of %d", ld, V);
+  if (ld > 2147483647LL) return fail(SSD_EUNSUPPORTED, "ld=%lld too large", ld);
+  if (Bsz > 65535) return fail(SSD_EUNSUPPORTED, "Bsz=%d above 65535", Bsz);
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_conv1d_fwd(const void* xbc, long long ld, const float* w, const float* bias,
+                   const float* state_in, int act, void* x, void* B, void* C, float* state_out,
+                   int Bsz, int T, int HP, int GN, int K, int dtype, void* stream) {
+  return ssd_conv1d_fwd_ev(xbc, ld, w, bias, state_in, act, x, B, C, state_out, Bsz, T, HP, GN,
+                           K, dtype, stream, nullptr);
+}
+
+int ssd_conv1d_fwd_ev(const void* xbc, long long ld, const float* w, const float* bias,
+                      const float* state_in, int act, void* x, void* B, void* C, float* state_out,
+                      int Bsz, int T, int HP, int GN, int K, int dtype, void* stream,
+                      void* const* events) {
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_EUNSUPPORTED, "dtype=%d", dtype);
+  const int V = dtype == SSD_BF16 ? 8 : 4;
+  const long long es = dtype == SSD_BF16 ? 2 : 4;
+  if (T < 0) return fail(SSD_EINVAL, "T=%d is negative", T);
+  SSD_TRY(check_conv_common(Bsz, HP, GN, ld, K, act, V));
+  // one batch entry's rows (and a run of tokens past T) are addressed by
+  // 32-bit byte offsets; runs of 4 x 16 tokens fill grid.y
+  const int tt = ssd::conv_tokens_per_thread();
+  if ((static_cast<long long>(T) + tt) * ld * es > 4294967295LL - 16)
+    return fail(SSD_EUNSUPPORTED, "one batch entry's rows exceed 4 GiB: T=%d ld=%lld", T, ld);
+  if ((static_cast<long long>(T) + 4LL * tt - 1) / (4LL * tt) > 65535)
+    return fail(SSD_EUNSUPPORTED, "T=%d too long", T);
+  const bool has_tokens = T > 0;
+  SSD_TRY(check_ptr(xbc, "xbc", 16, has_tokens));
+  SSD_TRY(check_ptr(w, "w", 16, true));
+  SSD_TRY(check_ptr(bias, "bias", 16, false));
+  SSD_TRY(check_ptr(state_in, "state_in", 16, false));
+  SSD_TRY(check_ptr(state_out, "state_out", 16, false));
+  SSD_TRY(check_ptr(x, "x", 16, has_tokens));
+  SSD_TRY(check_ptr(B, "B", 16, has_tokens && GN > 0));
+  SSD_TRY(check_ptr(C, "C", 16, has_tokens && GN > 0));
+  const size_t Ch = static_cast<size_t>(HP) + 2 * static_cast<size_t>(GN);
+  const size_t sbytes = static_cast<size_t>(Bsz) * 3 * Ch * 4;
+  if (overlaps(state_in, sbytes, state_out, sbytes))
+    return fail(SSD_EINVAL, "state_in and state_out overlap");
+  ssd::ConvArgs a{xbc, static_cast<int>(ld), w, bias, state_in, state_out, act, x, B, C,
+                  Bsz, T, HP, GN, dtype,
+                  reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_conv1d(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssd_conv1d_step(float* state, const float* xt, long long ld, const float* w,
+                    const float* bias, int act, float* x, float* B, float* C, int Bsz, int HP,
+                    int GN, int K, void* stream) {
+  return ssd_conv1d_step_ev(state, xt, ld, w, bias, act, x, B, C, Bsz, HP, GN, K, stream,
+                            nullptr);
+}
+
+int ssd_conv1d_step_ev(float* state, const float* xt, long long ld, const float* w,
+                       const float* bias, int act, float* x, float* B, float* C, int Bsz, int HP,
+                       int GN, int K, void* stream, void* const* events) {
+  SSD_TRY(check_conv_common(Bsz, HP, GN, ld, K, act, 4));
+  SSD_TRY(check_ptr(state, "state", 16, true));
+  SSD_TRY(check_ptr(xt, "xt", 16, true));
+  SSD_TRY(check_ptr(w, "w", 16, true));
+  SSD_TRY(check_ptr(bias, "bias", 16, false));
+  SSD_TRY(check_ptr(x, "x", 16, true));
+  SSD_TRY(check_ptr(B, "B", 16, GN > 0));
+  SSD_TRY(check_ptr(C, "C", 16, GN > 0));
+  ssd::ConvArgs a{xt, static_cast<int>(ld), w, bias, nullptr, state, act, x, B, C,
+                  Bsz, 1, HP, GN, SSD_F32,
+                  reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_conv1d_step(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -38,6 +38,21 @@ struct DecodeArgs {
   hipEvent_t* events;  // NULL, or start/stop of the decode kernel
 };
 
+struct ConvArgs {
+  const void* xbc;         // (Bsz, T, ld) rows; the step: (Bsz, ld) float32
+  int ld;                  // elements between consecutive token rows
+  const float* w;          // (Ch, 4)
+  const float* bias;       // (Ch) or NULL
+  const float* state_in;   // (Bsz, 3, Ch) or NULL (prefill only)
+  float* state_out;        // (Bsz, 3, Ch) or NULL; the step's state, in place
+  int act;                 // 1 = SiLU
+  void* x;                 // (Bsz, T, HP)
+  void* B;                 // (Bsz, T, GN)
+  void* C;                 // (Bsz, T, GN)
+  int Bsz, T, HP, GN, dtype;
+  hipEvent_t* events;      // NULL, or start/stop of the kernel
+};
+
 // floats of chunk-boundary states: (Bsz, nc, H, P, KC), KC = N or 2N
 inline size_t workspace_state_floats(int Bsz, int nc, int H, int P, int KC) {
   return static_cast<size_t>(Bsz) * nc * H * P * KC;
@@ -65,5 +80,8 @@ hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t run_complex_decode(const DecodeArgs& a, hipStream_t st);  // D unused
+hipError_t run_conv1d(const ConvArgs& a, hipStream_t st);
+hipError_t run_conv1d_step(const ConvArgs& a, hipStream_t st);  // float32, T = 1
+int conv_tokens_per_thread();
 
 }  // namespace ssd

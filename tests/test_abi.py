@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ssd_chunk_fwd", "ssd_complex_chunk_fwd", "ssd_step_decode",
               "ssd_complex_step_decode", "ssd_workspace_size", "ssd_last_error",
-              "ssd_abi_version"):
+              "ssd_abi_version", "ssd_conv1d_fwd", "ssd_conv1d_step"):
         assert n in names
 
 
@@ -127,6 +127,49 @@ def test_complex_decode_rejects():
     rc = L.ssd_complex_step_decode(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, 0.0, 1.0, GOOD,
                                    0, 4, 16, 1, 64, None)
     assert rc == ssd.SSD_EINVAL and "positive" in L.ssd_last_error().decode()
+
+
+def _conv(**over):
+    a = dict(xbc=GOOD, ld=48, w=GOOD, bias=None, si=None, act=1, x=GOOD, B=GOOD, C=GOOD,
+             so=None, Bsz=2, T=40, HP=32, GN=8, K=4, dtype=1)
+    a.update(over)
+    L = ssd.lib()
+    rc = L.ssd_conv1d_fwd(a["xbc"], a["ld"], a["w"], a["bias"], a["si"], a["act"], a["x"],
+                          a["B"], a["C"], a["so"], a["Bsz"], a["T"], a["HP"], a["GN"], a["K"],
+                          a["dtype"], None)
+    return rc, L.ssd_last_error().decode()
+
+
+def test_conv_rejects():
+    """Argument checks of the convolution run before any HIP call."""
+    assert _conv(K=3) == (ssd.SSD_EUNSUPPORTED, "K=3: only kernel size 4 is built")
+    rc, msg = _conv(HP=36)  # not a multiple of 8 for bf16
+    assert rc == ssd.SSD_EUNSUPPORTED and "multiples of 8" in msg
+    rc, msg = _conv(ld=40)  # ld < HP + 2*GN = 48
+    assert rc == ssd.SSD_EINVAL and "smaller" in msg
+    rc, msg = _conv(ld=52)
+    assert rc == ssd.SSD_EINVAL and "multiple of 8" in msg
+    rc, msg = _conv(act=2)
+    assert rc == ssd.SSD_EINVAL and "act" in msg
+    rc, msg = _conv(dtype=5)
+    assert rc == ssd.SSD_EUNSUPPORTED
+    rc, msg = _conv(T=-1)
+    assert rc == ssd.SSD_EINVAL
+    rc, msg = _conv(x=MISALIGNED)
+    assert rc == ssd.SSD_EINVAL and "x is not 16-byte aligned" in msg
+    rc, msg = _conv(w=None)
+    assert rc == ssd.SSD_EINVAL and "w is NULL" in msg
+    # the two states may not overlap (here: same buffer)
+    rc, msg = _conv(si=GOOD, so=ctypes.c_void_p(_base + 256))
+    assert rc == ssd.SSD_EINVAL and "overlap" in msg
+    # rows of one batch entry past 4 GiB
+    rc, msg = _conv(T=1 << 26, ld=64)
+    assert rc == ssd.SSD_EUNSUPPORTED
+    L = ssd.lib()
+    rc = L.ssd_conv1d_step(GOOD, GOOD, 48, GOOD, None, 1, GOOD, GOOD, GOOD, 2, 30, 9, 4, None)
+    assert rc == ssd.SSD_EUNSUPPORTED and "multiples of 4" in L.ssd_last_error().decode()
+    rc = L.ssd_conv1d_step(None, GOOD, 48, GOOD, None, 1, GOOD, GOOD, GOOD, 2, 32, 8, 4, None)
+    assert rc == ssd.SSD_EINVAL and "state is NULL" in L.ssd_last_error().decode()
 
 
 def test_workspace_size():

@@ -1,0 +1,195 @@
+"""GPU parity of the depthwise causal convolution (prefill and decode step)
+against the float64 oracle, through the C ABI.
+
+Bars, elementwise: float32 outputs within 2e-5 + 2e-6 |ref| (float32
+accumulation of 4 products, a bias and the SiLU); bfloat16 outputs within
+2^-8 |ref| + 2e-5 (one rounding to bfloat16 of that float32 value).  Both are
+far inside the normwise 1e-4 / 2e-2 of the scan.  The carried state holds raw
+inputs, so it must match bit for bit.  Every case compares every element,
+also at the BitMamba layer shape the benchmark times (the oracle finishes it
+in well under a second).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_09_amd as ssd
+from selective_state_space_09_amd import inputs
+import _gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _bar(dtype):
+    return (2.0 ** -8, 2e-5) if dtype == "bf16" else (2e-6, 2e-5)
+
+
+def _check(got, ref, dtype, what):
+    rel, ab = _bar(dtype)
+    err = np.abs(got - ref)
+    lim = rel * np.abs(ref) + ab
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, (f"{what}: {len(bad)} elements outside the bar, first at "
+                           f"{tuple(bad[0])}: got {got[tuple(bad[0])]}, ref {ref[tuple(bad[0])]}")
+
+
+def _split(out, HP, GN):
+    return out[..., :HP], out[..., HP:HP + GN], out[..., HP + GN:]
+
+
+def _run_gpu(d, act, ld_view=None):
+    """Uploads xbc (as a column slice of wider rows when ld_view is given) and
+    runs the prefill.  Returns x, B, C, state_out as float64 numpy."""
+    Bsz, T, ld = d["xbc"].shape
+    HP, GN = d["dims"]["HP"], d["dims"]["GN"]
+    Ch = HP + 2 * GN
+    xb = _gpu.to_dev(d["xbc"])
+    if ld_view is None:
+        xin = xb[:, :, :Ch] if ld > Ch else xb
+    else:
+        # the rows of a wider projection output, the conv channels at column 8
+        wide = torch.zeros((Bsz, T, ld_view), dtype=xb.dtype, device=xb.device)
+        wide[:, :, 8:8 + Ch] = xb[:, :, :Ch]
+        xin = wide[:, :, 8:8 + Ch]
+    w = _gpu.to_dev(d["w"])
+    bias = _gpu.to_dev(d["bias"])
+    si = _gpu.to_dev(d["state_in"])
+    x, B, C, so = ssd.ssd_conv1d_fwd(xin, w, HP, GN, bias=bias, state_in=si, act=act)
+    torch.cuda.synchronize()
+    return _gpu.to_host64(x), _gpu.to_host64(B), _gpu.to_host64(C), _gpu.to_host64(so)
+
+
+CASES = [
+    # Bsz, T, HP, GN, ld, dtype, act, with_state, with_bias
+    (2, 40, 32, 8, 48, "bf16", 1, True, True),       # ragged T: 3 runs of 16
+    (1, 1, 8, 8, 24, "f32", 0, True, False),          # one token, window from the state
+    (3, 2, 16, 0, 16, "f32", 1, True, True),          # no B/C channels, T < 3
+    (1, 3, 16, 8, 32, "bf16", 1, True, True),         # T = 3
+    (2, 200, 96, 16, 136, "bf16", 1, False, True),    # fresh sequence, ld > Ch
+    (1, 70, 512, 64, 704, "bf16", 1, True, True),     # 80 vectors: 2 channel blocks, ragged
+    (2, 65, 512, 64, 640, "f32", 1, True, True),      # 160 vectors: 3 blocks; 5 runs
+    (1, 257, 64, 32, 128, "f32", 0, True, True),      # runs across 5 workgroups, no SiLU
+]
+
+
+@pytest.mark.parametrize("Bsz,T,HP,GN,ld,dtype,act,ws,wb", CASES)
+def test_conv_small(Bsz, T, HP, GN, ld, dtype, act, ws, wb):
+    d = inputs.make_conv(Bsz, T, HP, GN, ld=ld, dtype=dtype, seed=T + HP, with_state=ws,
+                         with_bias=wb)
+    print(f"conv case Bsz={Bsz} T={T} HP={HP} GN={GN} ld={ld} {dtype} act={act}", flush=True)
+    Ch = HP + 2 * GN
+    ref, rst = oracle.conv1d(d["xbc"], d["w"], d["bias"], d["state_in"], act=act, ch=Ch)
+    x, B, C, so = _run_gpu(d, act)
+    rx, rB, rC = _split(ref, HP, GN)
+    _check(x, rx, dtype, "x")
+    if GN:
+        _check(B, rB, dtype, "B")
+        _check(C, rC, dtype, "C")
+    np.testing.assert_array_equal(so, rst)
+
+
+def test_conv_empty_sequence_copies_state():
+    d = inputs.make_conv(2, 0, 32, 8, dtype="bf16", seed=3)
+    ref, rst = oracle.conv1d(d["xbc"], d["w"], d["bias"], d["state_in"], act=1)
+    x, B, C, so = _run_gpu(d, 1)
+    assert x.size == 0
+    np.testing.assert_array_equal(so, rst)
+    np.testing.assert_array_equal(so, d["state_in"].astype(np.float64))
+
+
+def test_conv_row_slice_of_projection():
+    """xbc given as a column slice of wider rows (the in_proj output): the
+    binding passes the row stride, and the other columns are not read."""
+    d = inputs.make_conv(2, 33, 64, 16, dtype="bf16", seed=11)
+    ref, rst = oracle.conv1d(d["xbc"], d["w"], d["bias"], d["state_in"], act=1)
+    x, B, C, so = _run_gpu(d, 1, ld_view=136)
+    rx, rB, rC = _split(ref, 64, 16)
+    _check(x, rx, "bf16", "x")
+    _check(B, rB, "bf16", "B")
+    _check(C, rC, "bf16", "C")
+    np.testing.assert_array_equal(so, rst)
+
+
+def test_conv_workload_full():
+    """The benchmark's workload (BitMamba layer: 4096 + 2x128 channels read
+    from 8512-wide rows, B2 T2048, bf16, SiLU), every element."""
+    cfg = inputs.WORKLOADS["conv_bf16"]
+    d = inputs.make_workload("conv_bf16", seed=0)
+    HP, GN = cfg["HP"], cfg["GN"]
+    ref, rst = oracle.conv1d(d["xbc"], d["w"], d["bias"], d["state_in"], act=1, ch=HP + 2 * GN)
+    x, B, C, so = _run_gpu(d, 1)
+    rx, rB, rC = _split(ref, HP, GN)
+    _check(x, rx, "bf16", "x")
+    _check(B, rB, "bf16", "B")
+    _check(C, rC, "bf16", "C")
+    np.testing.assert_array_equal(so, rst)
+
+
+def test_conv_decode_workload_64_steps():
+    """The decode workload (256 sequences, BitMamba channels, 64 steps in
+    place on the float32 state), every output of every step and the state."""
+    cfg = inputs.WORKLOADS["conv_decode_f32"]
+    d = inputs.make_workload("conv_decode_f32", seed=0)
+    HP, GN, ld = cfg["HP"], cfg["GN"], cfg["ld"]
+    Ch = HP + 2 * GN
+    w, bias = _gpu.to_dev(d["w"]), _gpu.to_dev(d["bias"])
+    state = _gpu.to_dev(d["state0"])
+    ref_state = d["state0"].copy()
+    for k, xt in enumerate(d["steps"]):
+        xd = _gpu.to_dev(xt)[:, :Ch]
+        x, B, C = ssd.ssd_conv1d_step(state, xd, w, HP, GN, bias=bias, act=1)
+        out, st = oracle.conv1d(np.ascontiguousarray(xt[:, None, :]), d["w"], d["bias"],
+                                ref_state, act=1, ch=Ch)
+        out = out[:, 0]
+        ref_state = st.astype(np.float32)
+        rx, rB, rC = _split(out, HP, GN)
+        torch.cuda.synchronize()
+        _check(_gpu.to_host64(x), rx, "f32", f"x step {k}")
+        _check(_gpu.to_host64(B), rB, "f32", f"B step {k}")
+        _check(_gpu.to_host64(C), rC, "f32", f"C step {k}")
+    np.testing.assert_array_equal(_gpu.to_host64(state), ref_state.astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_prefill_then_steps(dtype):
+    """A prefill segment, its state handed to the step, then single tokens:
+    the outputs equal the oracle's over the whole sequence."""
+    HP, GN, T0, steps = 64, 16, 37, 6
+    Ch = HP + 2 * GN
+    d = inputs.make_conv(2, T0 + steps, HP, GN, dtype=dtype, seed=21)
+    ref, rst = oracle.conv1d(d["xbc"], d["w"], d["bias"], d["state_in"], act=1)
+    pre = dict(d, xbc=np.ascontiguousarray(d["xbc"][:, :T0]))
+    x, B, C, so = _run_gpu(pre, 1)
+    _check(x, ref[:, :T0, :HP], dtype, "prefill x")
+    xs = inputs.bf16_bits_to_f32(d["xbc"]) if dtype == "bf16" else d["xbc"]
+    state = _gpu.to_dev(so.astype(np.float32))
+    w, bias = _gpu.to_dev(d["w"]), _gpu.to_dev(d["bias"])
+    for k in range(steps):
+        xt = _gpu.to_dev(np.ascontiguousarray(xs[:, T0 + k]))
+        x, B, C = ssd.ssd_conv1d_step(state, xt, w, HP, GN, bias=bias, act=1)
+        torch.cuda.synchronize()
+        _check(_gpu.to_host64(x), ref[:, T0 + k, :HP], "f32", f"step {k} x")
+        _check(_gpu.to_host64(C), ref[:, T0 + k, HP + GN:], "f32", f"step {k} C")
+    np.testing.assert_array_equal(_gpu.to_host64(state), rst)
+
+
+def test_conv_feeds_the_scan():
+    """The conv's x, B, C (bf16) are the scan's inputs as laid out: the scan
+    run on them on the GPU matches the oracle scan of the same values."""
+    H, P, G, N, T = 4, 32, 1, 64, 300
+    d = inputs.make_conv(1, T, H * P, G * N, dtype="bf16", seed=5)
+    xb = _gpu.to_dev(d["xbc"])
+    x, B, C, _ = ssd.ssd_conv1d_fwd(xb, _gpu.to_dev(d["w"]), H * P, G * N,
+                                    bias=_gpu.to_dev(d["bias"]), state_in=_gpu.to_dev(d["state_in"]))
+    r = inputs.make_real(1, T, H, P, N, G=G, dtype="bf16", seed=6)
+    dt, A, D, bias = (_gpu.to_dev(r[k]) for k in ("dt", "A", "D", "dt_bias"))
+    xs, Bs, Cs = x.view(1, T, H, P), B.view(1, T, G, N), C.view(1, T, G, N)
+    y = ssd.ssd_chunk_fwd(xs, dt, A, Bs, Cs, D, bias, r["dt_min"], r["dt_max"], None, chunk=64)
+    torch.cuda.synchronize()
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    yr, _ = oracle.fwd(bits(xs), r["dt"], r["A"], bits(Bs), bits(Cs), r["D"], r["dt_bias"],
+                       r["dt_min"], r["dt_max"], None)
+    yg = _gpu.to_host64(y)
+    err = np.abs(yg - yr).max() / np.abs(yr).max()
+    assert err < 2e-2, err
