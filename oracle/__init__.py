@@ -58,6 +58,9 @@ def _load():
     lib.ssd_oracle_complex_step.argtypes = [P, P, P, P, P, P, P, Dd, Dd, P, I, I, I, I, I]
     lib.ssd_oracle_conv1d.restype = I
     lib.ssd_oracle_conv1d.argtypes = [P, ctypes.c_longlong, P, P, P, I, P, P, I, I, I, I, I]
+    lib.ssd_oracle_bwd.restype = I
+    lib.ssd_oracle_bwd.argtypes = [P, P, P, P, P, P, P, Dd, Dd, P, P, P,
+                                   P, P, P, P, P, P, P, P, I, I, I, I, I, I, I]
     lib.ssd_oracle_threads_used.restype = I
     lib.ssd_oracle_set_threads.argtypes = [I]
     _lib = lib
@@ -239,3 +242,41 @@ def conv1d_step(state, xt, w, bias=None, act=1):
     xt = np.ascontiguousarray(xt, np.float32)
     out, st = conv1d(xt[:, None, :], w, bias, state, act)
     return out[:, 0, :], st
+
+
+def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=float("inf"),
+        h0=None, dh_final=None, want_dh0=True):
+    """Gradient of loss = sum(dy * y) + <dh_final, h_final> of the real
+    recurrence (same inputs and dtype rules as ``fwd``; dy has x's shape and
+    dtype, dh_final (Bsz,H,P,N) float32 or None).  Returns a dict of float64
+    arrays: dx, ddt, dA, dB, dC, dD, ddt_bias, dh0 (None unless want_dh0)."""
+    lib = _load()
+    if x.dtype == np.uint16:
+        dtype = 1
+    elif x.dtype == np.float32:
+        dtype = 0
+    else:
+        raise TypeError("x must be float32 or uint16 bfloat16 bits")
+    x = _c(x, x.dtype)
+    B = _c(B, x.dtype)
+    C = _c(C, x.dtype)
+    dy = _c(dy, x.dtype)
+    dt = _c(dt, np.float32)
+    A = _c(A, np.float32)
+    D = _c(D, np.float32)
+    dt_bias = _c(dt_bias, np.float32)
+    h0 = _c(h0, np.float32)
+    dh_final = _c(dh_final, np.float32)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    out = dict(dx=np.empty((Bsz, T, H, P)), ddt=np.empty((Bsz, T, H)), dA=np.empty(H),
+               dB=np.empty((Bsz, T, G, N)), dC=np.empty((Bsz, T, G, N)), dD=np.empty(H),
+               ddt_bias=np.empty(H), dh0=np.empty((Bsz, H, P, N)) if want_dh0 else None)
+    rc = lib.ssd_oracle_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                            _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0), _ptr(dy),
+                            _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+                            _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                            _ptr(out["ddt_bias"]), _ptr(out["dh0"]), Bsz, T, H, P, G, N, dtype)
+    if rc:
+        raise ValueError("oracle rejected the sizes" if rc == 1 else "oracle out of memory")
+    return out

@@ -41,6 +41,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -382,4 +383,162 @@ int ssd_oracle_conv1d(const void *xbc, long long ld, const float *w, const float
         }
     }
     return 0;
+}
+
+/*
+ * Reverse-mode derivative of the real recurrence (ssd_oracle_fwd) for the
+ * scalar   loss = sum_t dy_t . y_t + <dh_final, h_final>,
+ * by the adjoint recurrence run backwards in time (the definition of the
+ * gradient of the recurrence of the Mamba-3-Lite README's classical Mamba-2
+ * form, with the step size on the input term and y_t read after the update).
+ * For every (b, h), with a_t = exp(A_h delta_t), u_t = delta_t x_t B_t^T:
+ *   G = dh_final                       (adjoint of h_{T-1}; 0 when NULL)
+ *   for t = T-1 .. 0:
+ *     G        += dy_t C_t^T           (y_t = h_t C_t + D x_t)
+ *     dC_t     += h_t^T dy_t
+ *     dx_t      = delta_t G B_t + D dy_t
+ *     dB_t     += delta_t G^T x_t
+ *     ddelta_t  = <G, x_t B_t^T> + A_h a_t <G, h_{t-1}>
+ *     dA_h     += delta_t a_t <G, h_{t-1}>
+ *     dD_h     += dy_t . x_t
+ *     ddt_t     = ddelta_t softplus'(z_t) [dt_min <= softplus(z_t) <= dt_max]
+ *     ddt_bias_h += ddt_t
+ *     G         = a_t G                (adjoint of h_{t-1})
+ *   dh0 = G.
+ * z_t = dt_t + dt_bias_h; softplus'(z) = 1 / (1 + e^-z); the clamp passes the
+ * derivative on its closed interval and stops it outside.  dB and dC sum over
+ * the heads of a group.  dy has the dtype of x.  Outputs are double: dx, dy-
+ * shaped (Bsz,T,H,P); ddt (Bsz,T,H); dB, dC (Bsz,T,G,N); dA, dD, ddt_bias (H);
+ * dh0 (Bsz,H,P,N) or NULL.  The states h_0 .. h_{T-1} of one (b, h) are kept
+ * (T P N doubles per thread).
+ */
+int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B,
+                   const void *C, const float *D, const float *dt_bias, double dt_min,
+                   double dt_max, const float *h0, const void *dy, const float *dh_final,
+                   double *dx, double *ddt, double *dA, double *dB, double *dC, double *dD,
+                   double *ddt_bias, double *dh0, int Bsz, int T, int H, int P, int G, int N,
+                   int dtype)
+{
+    if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G)
+        return 1;
+    const int hpg = H / G;
+    const size_t PN = (size_t)P * N;
+    memset(dB, 0, sizeof(double) * (size_t)Bsz * T * G * N);
+    memset(dC, 0, sizeof(double) * (size_t)Bsz * T * G * N);
+    int fail = 0;
+    /* per head: sums over the batch, reduced after the parallel loop */
+    double *pA = calloc((size_t)Bsz * H, sizeof(double));
+    double *pD = calloc((size_t)Bsz * H, sizeof(double));
+    double *pbias = calloc((size_t)Bsz * H, sizeof(double));
+    if (!pA || !pD || !pbias) {
+        free(pA); free(pD); free(pbias);
+        return 2;
+    }
+    const long long BG = (long long)Bsz * G;
+#pragma omp parallel
+    {
+#pragma omp single
+        record_threads();
+        double *hist = malloc(sizeof(double) * ((size_t)T + 1) * PN);
+        double *Gm = malloc(sizeof(double) * PN);
+        double *dlt = malloc(sizeof(double) * ((size_t)T + 1));
+        if (!hist || !Gm || !dlt) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic)
+        for (long long bg = 0; bg < BG; ++bg) {
+            if (!hist || !Gm || !dlt)
+                continue;
+            const int b = (int)(bg / G), g = (int)(bg % G);
+            for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+                const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+                const double Ah = (double)A[h];
+                const double Dh = D ? (double)D[h] : 0.0;
+                /* forward: hist[0] = h0, hist[t+1] = h_t */
+                for (size_t i = 0; i < PN; ++i)
+                    hist[i] = h0 ? (double)h0[((size_t)b * H + h) * PN + i] : 0.0;
+                for (int t = 0; t < T; ++t) {
+                    const size_t row = (size_t)b * T + t;
+                    const double delta = ssd_oracle_delta((double)dt[row * H + h], bias, dt_min, dt_max);
+                    dlt[t] = delta;
+                    const double a = exp(Ah * delta);
+                    const double *hp = hist + (size_t)t * PN;
+                    double *hn = hist + ((size_t)t + 1) * PN;
+                    for (int p = 0; p < P; ++p) {
+                        const double xp = load_in(x, (row * H + h) * P + p, dtype);
+                        for (int n = 0; n < N; ++n)
+                            hn[(size_t)p * N + n] = a * hp[(size_t)p * N + n] +
+                                delta * xp * load_in(B, (row * G + g) * N + n, dtype);
+                    }
+                }
+                /* backward */
+                for (size_t i = 0; i < PN; ++i)
+                    Gm[i] = dh_final ? (double)dh_final[((size_t)b * H + h) * PN + i] : 0.0;
+                for (int t = T - 1; t >= 0; --t) {
+                    const size_t row = (size_t)b * T + t;
+                    const double delta = dlt[t];
+                    const double a = exp(Ah * delta);
+                    const double *ht = hist + ((size_t)t + 1) * PN;
+                    const double *hprev = hist + (size_t)t * PN;
+                    /* G += dy_t C_t^T ; dC_t += h_t^T dy_t */
+                    for (int p = 0; p < P; ++p) {
+                        const double dyp = load_in(dy, (row * H + h) * P + p, dtype);
+                        for (int n = 0; n < N; ++n) {
+                            Gm[(size_t)p * N + n] += dyp * load_in(C, (row * G + g) * N + n, dtype);
+                            dC[(row * G + g) * N + n] += ht[(size_t)p * N + n] * dyp;
+                        }
+                    }
+                    double gx_b = 0.0, g_hprev = 0.0, dyx = 0.0;
+                    for (int p = 0; p < P; ++p) {
+                        const double xp = load_in(x, (row * H + h) * P + p, dtype);
+                        const double dyp = load_in(dy, (row * H + h) * P + p, dtype);
+                        double gb = 0.0;
+                        for (int n = 0; n < N; ++n) {
+                            const double bn = load_in(B, (row * G + g) * N + n, dtype);
+                            const double gv = Gm[(size_t)p * N + n];
+                            gb += gv * bn;
+                            dB[(row * G + g) * N + n] += delta * gv * xp;
+                            g_hprev += gv * hprev[(size_t)p * N + n];
+                        }
+                        dx[(row * H + h) * P + p] = delta * gb + Dh * dyp;
+                        gx_b += xp * gb;
+                        dyx += dyp * xp;
+                    }
+                    const double ddelta = gx_b + Ah * a * g_hprev;
+                    pA[(size_t)b * H + h] += delta * a * g_hprev;
+                    pD[(size_t)b * H + h] += dyx;
+                    const double z = (double)dt[row * H + h] + bias;
+                    const double sp = ssd_oracle_softplus(z);
+                    const double pass = (sp >= dt_min && sp <= dt_max) ? 1.0 : 0.0;
+                    const double d = ddelta * pass / (1.0 + exp(-z));
+                    ddt[row * H + h] = d;
+                    pbias[(size_t)b * H + h] += d;
+                    for (size_t i = 0; i < PN; ++i)
+                        Gm[i] *= a;
+                }
+                if (dh0)
+                    for (size_t i = 0; i < PN; ++i)
+                        dh0[((size_t)b * H + h) * PN + i] = Gm[i];
+            }
+        }
+        free(hist);
+        free(Gm);
+        free(dlt);
+    }
+    for (int h = 0; h < H; ++h) {
+        double sa = 0.0, sd = 0.0, sb = 0.0;
+        for (int b = 0; b < Bsz; ++b) {
+            sa += pA[(size_t)b * H + h];
+            sd += pD[(size_t)b * H + h];
+            sb += pbias[(size_t)b * H + h];
+        }
+        dA[h] = sa;
+        dD[h] = sd;
+        ddt_bias[h] = sb;
+    }
+    free(pA);
+    free(pD);
+    free(pbias);
+    return fail ? 2 : 0;
 }

@@ -508,3 +508,83 @@ def test_conv_step_equals_prefill():
         np.testing.assert_array_equal(o, whole[:, t])
         s = s64.astype(np.float32)
     np.testing.assert_array_equal(s, st.astype(np.float32))
+
+
+# ---- backward of the real recurrence (oracle.bwd), pinned by finite
+# differences of the pinned forward ----
+
+def _loss(inp, dy, dhf):
+    y, hf = oracle.fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                       inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"])
+    return float(np.sum(dy.astype(np.float64) * y) + np.sum(dhf.astype(np.float64) * hf))
+
+
+def _bwd_case(G, seed):
+    inp = _real(Bsz=2, T=7, H=2, P=3, N=4, G=G, seed=seed, with_h0=True)
+    rng = np.random.default_rng(seed + 100)
+    dy = rng.standard_normal(inp["x"].shape).astype(np.float32)
+    dhf = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    # no step within reach of a clamp bound: the loss is smooth at every
+    # perturbation below
+    z = inp["dt"].astype(np.float64) + inp["dt_bias"].astype(np.float64)
+    sp = np.logaddexp(0.0, z)
+    assert np.min(np.abs(sp - inp["dt_min"])) > 1e-3 * inp["dt_min"]
+    assert np.min(np.abs(sp - inp["dt_max"])) > 1e-3 * inp["dt_max"]
+    assert np.any(sp > inp["dt_max"]) and np.any(sp < inp["dt_max"])  # both branches occur
+    return inp, dy, dhf
+
+
+@pytest.mark.parametrize("G,seed", [(1, 3), (2, 5)])
+def test_bwd_matches_finite_differences(G, seed):
+    """Every gradient of every input element against the central difference
+    of the forward oracle (perturbation 2^-12, exact in float32; the loss is
+    linear in x, B, C, D, h0, so there the difference is exact up to rounding,
+    and smooth in dt, A, dt_bias)."""
+    inp, dy, dhf = _bwd_case(G, seed)
+    g = oracle.bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], dy, inp["D"],
+                   inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
+    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+             "dt_bias": "ddt_bias", "h0": "dh0"}
+    eps = 2.0 ** -12
+    for k, gk in names.items():
+        base = inp[k]
+        fd = np.empty(base.shape)
+        for idx in np.ndindex(base.shape):
+            hi, lo = dict(inp), dict(inp)
+            hi[k] = base.copy()
+            lo[k] = base.copy()
+            hi[k][idx] += np.float32(eps)
+            lo[k][idx] -= np.float32(eps)
+            step = float(hi[k][idx]) - float(lo[k][idx])
+            fd[idx] = (_loss(hi, dy, dhf) - _loss(lo, dy, dhf)) / step
+        got = g[gk]
+        scale = np.abs(fd).max()
+        np.testing.assert_allclose(got, fd, rtol=2e-5, atol=2e-6 * scale, err_msg=k)
+
+
+def test_bwd_bf16_equals_widened_f32():
+    """bfloat16 inputs are read as the float32 values they widen to."""
+    inp = _real(Bsz=1, T=9, H=2, P=3, N=4, G=1, seed=8, dtype="bf16", with_h0=True)
+    rng = np.random.default_rng(9)
+    dy = inputs.f32_to_bf16_bits(rng.standard_normal(inp["x"].shape).astype(np.float32))
+    dhf = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    w = inputs.bf16_bits_to_f32
+    a = oracle.bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], dy, inp["D"],
+                   inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
+    b = oracle.bwd(w(inp["x"]), inp["dt"], inp["A"], w(inp["B"]), w(inp["C"]), w(dy), inp["D"],
+                   inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_bwd_clamped_steps_pass_no_gradient_to_dt():
+    """A step clamped by dt_max (or dt_min) does not move with dt: its ddt is
+    exactly zero, and the others are not."""
+    inp, dy, dhf = _bwd_case(1, 3)
+    g = oracle.bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], dy, inp["D"],
+                   inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
+    sp = np.logaddexp(0.0, inp["dt"].astype(np.float64) + inp["dt_bias"].astype(np.float64))
+    clamped = (sp > inp["dt_max"]) | (sp < inp["dt_min"])
+    assert np.all(g["ddt"][clamped] == 0.0)
+    assert np.all(g["ddt"][~clamped] != 0.0)
+    np.testing.assert_allclose(g["ddt_bias"], g["ddt"].sum(axis=(0, 1)), rtol=1e-12)
