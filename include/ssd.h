@@ -288,6 +288,55 @@ int ssd_conv1d_step_ev(float *state, const float *xt, long long ld, const float 
                        const float *bias, int act, float *x, float *B, float *C,
                        int Bsz, int HP, int GN, int K, void *stream, void *const *events);
 
+/*
+ * Backward of ssd_chunk_fwd for the real form: the gradient of
+ *   loss = sum_{b,t,h,p} dy[b,t,h,p] y[b,t,h,p] + <dh_final, h_final>
+ * with respect to every input (reverse-mode derivative of the recurrence of
+ * the Mamba-3-Lite README's classical Mamba-2 form, evaluated chunkwise as in
+ * Numerical Stability in Mamba-3-Lite, section 4).  The forward's chunk
+ * states are recomputed inside the call; y is not needed.
+ *   inputs      x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0 exactly as given
+ *               to ssd_chunk_fwd; dy (Bsz,T,H,P) in x's dtype; dh_final
+ *               (Bsz,H,P,N) float32 or NULL (zero)
+ *   dx          (Bsz,T,H,P) x's dtype
+ *   ddt         (Bsz,T,H) float32, gradient of the raw dt (zero where the
+ *               step is clamped: the clamp passes the derivative on its closed
+ *               interval only)
+ *   dB, dC      (Bsz,T,G,N) float32, summed over the heads of each group
+ *   dA, dD, ddt_bias  (H) float32, summed over batch and tokens (written even
+ *               when D or dt_bias is NULL)
+ *   dh0         (Bsz,H,P,N) float32, or NULL (not written)
+ *   workspace   ssd_bwd_workspace_size(...) bytes, 256-byte aligned
+ * Built for dtype SSD_BF16 with P in {32, 64}, N in {64, 128}, chunk in
+ * {64, 128, 256} (SSD_EUNSUPPORTED otherwise, including SSD_F32).  dB, dC,
+ * dh0, h0 and dh_final 16-byte aligned.  Outputs are overwritten, not
+ * accumulated, and must not overlap inputs.  Errors as for ssd_chunk_fwd.
+ */
+size_t ssd_bwd_workspace_size(int Bsz, int T, int H, int P, int G, int N, int chunk);
+
+int ssd_chunk_bwd(const void *x, const float *dt, const float *A, const void *B,
+                  const void *C, const float *D, const float *dt_bias, float dt_min,
+                  float dt_max, const float *h0, const void *dy, const float *dh_final,
+                  void *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                  float *ddt_bias, float *dh0, int Bsz, int T, int H, int P, int G, int N,
+                  int chunk, int dtype, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
+ * Measurement variant of ssd_chunk_bwd: identical arguments, kernels and
+ * result, plus `events`, 20 hipEvent_t (passed as void*): a start/stop pair
+ * bound to each of the 10 kernels' dispatches in order (chunk states, state
+ * passing, adjoint chunk states, adjoint passing, dx/dB blocks, dC blocks,
+ * chunk constants of da, step-size gradients, dB sum, dC sum), or NULL.
+ */
+int ssd_chunk_bwd_ev(const void *x, const float *dt, const float *A, const void *B,
+                     const void *C, const float *D, const float *dt_bias, float dt_min,
+                     float dt_max, const float *h0, const void *dy, const float *dh_final,
+                     void *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                     float *ddt_bias, float *dh0, int Bsz, int T, int H, int P, int G, int N,
+                     int chunk, int dtype, void *workspace, size_t workspace_bytes,
+                     void *stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

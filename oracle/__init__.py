@@ -60,7 +60,7 @@ def _load():
     lib.ssd_oracle_conv1d.argtypes = [P, ctypes.c_longlong, P, P, P, I, P, P, I, I, I, I, I]
     lib.ssd_oracle_bwd.restype = I
     lib.ssd_oracle_bwd.argtypes = [P, P, P, P, P, P, P, Dd, Dd, P, P, P,
-                                   P, P, P, P, P, P, P, P, I, I, I, I, I, I, I]
+                                   P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I]
     lib.ssd_oracle_threads_used.restype = I
     lib.ssd_oracle_set_threads.argtypes = [I]
     _lib = lib
@@ -249,7 +249,8 @@ def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=float("inf"
     """Gradient of loss = sum(dy * y) + <dh_final, h_final> of the real
     recurrence (same inputs and dtype rules as ``fwd``; dy has x's shape and
     dtype, dh_final (Bsz,H,P,N) float32 or None).  Returns a dict of float64
-    arrays: dx, ddt, dA, dB, dC, dD, ddt_bias, dh0 (None unless want_dh0)."""
+    arrays: dx, ddt, dA, dB, dC, dD, ddt_bias, dh0 (None unless want_dh0), and
+    da (Bsz,T,H), the gradient of each step's log-decay A_h delta_t."""
     lib = _load()
     if x.dtype == np.uint16:
         dtype = 1
@@ -271,12 +272,14 @@ def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=float("inf"
     G, N = B.shape[2], B.shape[3]
     out = dict(dx=np.empty((Bsz, T, H, P)), ddt=np.empty((Bsz, T, H)), dA=np.empty(H),
                dB=np.empty((Bsz, T, G, N)), dC=np.empty((Bsz, T, G, N)), dD=np.empty(H),
-               ddt_bias=np.empty(H), dh0=np.empty((Bsz, H, P, N)) if want_dh0 else None)
+               ddt_bias=np.empty(H), dh0=np.empty((Bsz, H, P, N)) if want_dh0 else None,
+               da=np.empty((Bsz, T, H)))
     rc = lib.ssd_oracle_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                             _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0), _ptr(dy),
                             _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
                             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
-                            _ptr(out["ddt_bias"]), _ptr(out["dh0"]), Bsz, T, H, P, G, N, dtype)
+                            _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(out["da"]),
+                            Bsz, T, H, P, G, N, dtype)
     if rc:
         raise ValueError("oracle rejected the sizes" if rc == 1 else "oracle out of memory")
     return out

@@ -409,15 +409,18 @@ int ssd_oracle_conv1d(const void *xbc, long long ld, const float *w, const float
  * derivative on its closed interval and stops it outside.  dB and dC sum over
  * the heads of a group.  dy has the dtype of x.  Outputs are double: dx, dy-
  * shaped (Bsz,T,H,P); ddt (Bsz,T,H); dB, dC (Bsz,T,G,N); dA, dD, ddt_bias (H);
- * dh0 (Bsz,H,P,N) or NULL.  The states h_0 .. h_{T-1} of one (b, h) are kept
- * (T P N doubles per thread).
+ * dh0 (Bsz,H,P,N) or NULL; da (Bsz,T,H) or NULL receives the gradient of
+ * the step's log-decay A_h delta_t, a_t <G, h_{t-1}> (dA_h sums delta_t da_t).
+ * The states h_0 .. h_{T-1} of one (b, h) are kept
+ * (T P N doubles per thread); each thread sums dB and dC over its heads
+ * and the sums are added at the end.
  */
 int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B,
                    const void *C, const float *D, const float *dt_bias, double dt_min,
                    double dt_max, const float *h0, const void *dy, const float *dh_final,
                    double *dx, double *ddt, double *dA, double *dB, double *dC, double *dD,
-                   double *ddt_bias, double *dh0, int Bsz, int T, int H, int P, int G, int N,
-                   int dtype)
+                   double *ddt_bias, double *dh0, double *da, int Bsz, int T, int H, int P,
+                   int G, int N, int dtype)
 {
     if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G)
         return 1;
@@ -434,7 +437,8 @@ int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B
         free(pA); free(pD); free(pbias);
         return 2;
     }
-    const long long BG = (long long)Bsz * G;
+    const long long BH = (long long)Bsz * H;
+    const size_t nbc = (size_t)Bsz * T * G * N;
 #pragma omp parallel
     {
 #pragma omp single
@@ -442,16 +446,20 @@ int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B
         double *hist = malloc(sizeof(double) * ((size_t)T + 1) * PN);
         double *Gm = malloc(sizeof(double) * PN);
         double *dlt = malloc(sizeof(double) * ((size_t)T + 1));
-        if (!hist || !Gm || !dlt) {
+        /* this thread's sums over its heads of dB and dC */
+        double *dBt = calloc(nbc ? nbc : 1, sizeof(double));
+        double *dCt = calloc(nbc ? nbc : 1, sizeof(double));
+        const int ok = hist && Gm && dlt && dBt && dCt;
+        if (!ok) {
 #pragma omp atomic write
             fail = 1;
         }
 #pragma omp for schedule(dynamic)
-        for (long long bg = 0; bg < BG; ++bg) {
-            if (!hist || !Gm || !dlt)
+        for (long long bh = 0; bh < BH; ++bh) {
+            if (!ok)
                 continue;
-            const int b = (int)(bg / G), g = (int)(bg % G);
-            for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+            const int b = (int)(bh / H), h = (int)(bh % H), g = h / hpg;
+            {
                 const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
                 const double Ah = (double)A[h];
                 const double Dh = D ? (double)D[h] : 0.0;
@@ -486,7 +494,7 @@ int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B
                         const double dyp = load_in(dy, (row * H + h) * P + p, dtype);
                         for (int n = 0; n < N; ++n) {
                             Gm[(size_t)p * N + n] += dyp * load_in(C, (row * G + g) * N + n, dtype);
-                            dC[(row * G + g) * N + n] += ht[(size_t)p * N + n] * dyp;
+                            dCt[(row * G + g) * N + n] += ht[(size_t)p * N + n] * dyp;
                         }
                     }
                     double gx_b = 0.0, g_hprev = 0.0, dyx = 0.0;
@@ -498,7 +506,7 @@ int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B
                             const double bn = load_in(B, (row * G + g) * N + n, dtype);
                             const double gv = Gm[(size_t)p * N + n];
                             gb += gv * bn;
-                            dB[(row * G + g) * N + n] += delta * gv * xp;
+                            dBt[(row * G + g) * N + n] += delta * gv * xp;
                             g_hprev += gv * hprev[(size_t)p * N + n];
                         }
                         dx[(row * H + h) * P + p] = delta * gb + Dh * dyp;
@@ -506,6 +514,8 @@ int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B
                         dyx += dyp * xp;
                     }
                     const double ddelta = gx_b + Ah * a * g_hprev;
+                    if (da)
+                        da[row * H + h] = a * g_hprev;
                     pA[(size_t)b * H + h] += delta * a * g_hprev;
                     pD[(size_t)b * H + h] += dyx;
                     const double z = (double)dt[row * H + h] + bias;
@@ -522,9 +532,18 @@ int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B
                         dh0[((size_t)b * H + h) * PN + i] = Gm[i];
             }
         }
+#pragma omp critical
+        if (ok) {
+            for (size_t i = 0; i < nbc; ++i) {
+                dB[i] += dBt[i];
+                dC[i] += dCt[i];
+            }
+        }
         free(hist);
         free(Gm);
         free(dlt);
+        free(dBt);
+        free(dCt);
     }
     for (int h = 0; h < H; ++h) {
         double sa = 0.0, sd = 0.0, sb = 0.0;

@@ -61,6 +61,13 @@ def lib():
     L.ssd_complex_step_decode_ev.restype = I
     L.ssd_complex_step_decode_ev.argtypes = L.ssd_complex_step_decode.argtypes + [P]
     LL = ctypes.c_longlong
+    L.ssd_bwd_workspace_size.restype = S
+    L.ssd_bwd_workspace_size.argtypes = [I] * 7
+    L.ssd_chunk_bwd.restype = I
+    L.ssd_chunk_bwd.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P,
+                                P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, S, P]
+    L.ssd_chunk_bwd_ev.restype = I
+    L.ssd_chunk_bwd_ev.argtypes = L.ssd_chunk_bwd.argtypes + [P]
     L.ssd_conv1d_fwd.restype = I
     L.ssd_conv1d_fwd.argtypes = [P, LL, P, P, P, I, P, P, P, P, I, I, I, I, I, I, P]
     L.ssd_conv1d_fwd_ev.restype = I
@@ -303,3 +310,39 @@ def ssd_conv1d_step(state, xt, w, HP, GN, bias=None, act=1, x=None, B=None, C=No
                                  _ptr(x), _ptr(B), _ptr(C), Bsz, HP, GN, w.shape[1],
                                  _stream(stream)))
     return x, B, C
+
+
+def ssd_bwd_workspace_size(Bsz, T, H, P, G, N, chunk):
+    return int(lib().ssd_bwd_workspace_size(Bsz, T, H, P, G, N, chunk))
+
+
+def ssd_chunk_bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=math.inf,
+                  h0=None, dh_final=None, chunk=256, want_dh0=True, workspace=None, stream=None):
+    """Gradient of sum(dy * y) + <dh_final, h_final> of ssd_chunk_fwd (real
+    form, bfloat16 x/B/C/dy).  Returns a dict: dx (x's dtype), ddt, dA, dB,
+    dC, dD, ddt_bias and dh0 (float32; dh0 None unless want_dh0)."""
+    for t, n in ((x, "x"), (B, "B"), (C, "C"), (dy, "dy")):
+        _dev(t, n, torch.bfloat16)
+    for t, n in ((dt, "dt"), (A, "A")):
+        _dev(t, n, torch.float32)
+    for t, n in ((D, "D"), (dt_bias, "dt_bias"), (h0, "h0"), (dh_final, "dh_final")):
+        _dev(t, n, torch.float32)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty((Bsz, T, H), **f32),
+               dA=torch.empty(H, **f32), dB=torch.empty((Bsz, T, G, N), **f32),
+               dC=torch.empty((Bsz, T, G, N), **f32), dD=torch.empty(H, **f32),
+               ddt_bias=torch.empty(H, **f32),
+               dh0=torch.empty((Bsz, H, P, N), **f32) if want_dh0 else None)
+    nbytes = ssd_bwd_workspace_size(Bsz, T, H, P, G, N, chunk)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().ssd_chunk_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                               _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0), _ptr(dy),
+                               _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]),
+                               _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                               _ptr(out["dD"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]),
+                               Bsz, T, H, P, G, N, chunk, SSD_BF16, _ptr(ws), ws.numel(),
+                               _stream(stream)))
+    return out

@@ -9,7 +9,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 SOURCES = ["ssd_api.hip", "ssd_chunk.hip", "ssd_chunk_bf16.hip", "ssd_chunk_cplx.hip",
-           "ssd_decode.hip", "ssd_conv.hip"]
+           "ssd_decode.hip", "ssd_conv.hip", "ssd_bwd_bf16.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -1,0 +1,924 @@
+// Backward of the chunked SSD, real Mamba-2 form, bfloat16 x, B, C and dy
+// (fp32 accumulation, fp32 gradients except dx), on gfx950.
+//
+// Gradient of  loss = sum_t dy_t . y_t + <dh_final, h_final>  for
+//   h_t = e^{A delta_t} h_{t-1} + delta_t x_t B_t^T,  y_t = h_t C_t + D x_t
+// (the classical Mamba-2 recurrence of the Mamba-3-Lite README, evaluated
+// chunkwise as in Numerical Stability in Mamba-3-Lite, section 4).  Inside a
+// chunk (cs_l the inclusive cumulative log-decay, tot its total) the adjoint
+// of the state is
+//   dh_s = sum_{l >= s} e^{cs_l - cs_s} C_l^T dy_l + e^{tot - cs_s} R_c,
+// R_c the adjoint at the chunk's end (from the later chunks and dh_final),
+// carried across chunks by R_{c-1} = e^{tot_c} R_c + G_c with
+// G_c = sum_l e^{cs_l} C_l^T dy_l.  Then, per head,
+//   v_s   = dh_s B_s       = sum_{l>=s} e^{cs_l-cs_s} (C_l.B_s) dy_l + e^{tot-cs_s} R_c B_s
+//   dx_s  = delta_s v_s + D dy_s
+//   dB_s += delta_s dh_s^T x_s
+//         = delta_s [ sum_{l>=s} e^{cs_l-cs_s} (dy_l.x_s) C_l + e^{tot-cs_s} R_c^T x_s ]
+//   dC_l += h_l^T dy_l     = sum_{s<=l} e^{cs_l-cs_s} delta_s (dy_l.x_s) B_s + e^{cs_l} H_in^T dy_l
+// (dB and dC summed over the heads of a group), and for the step sizes
+//   ddelta_t = A da_t + x_t . v_t,   dA = sum_t delta_t da_t,   dD = sum_t dy_t . x_t,
+// with da_t = <dh_t, e^{A delta_t} h_{t-1}> the gradient of the step's
+// log-decay, taken apart inside the chunk into terms that each decay away
+// from t (so that none of them is a long sum of terms that cancel):
+//   da_t = sum_{s < t <= l} e^{cs_l-cs_s} delta_s (C_l.B_s)(dy_l.x_s)      (box)
+//        + sum_{l >= t} e^{cs_l} C_l . (H_in^T dy_l)                      (f1)
+//        + sum_{s < t} e^{tot-cs_s} delta_s x_s . (R_c B_s)               (f2)
+//        + e^{tot} <R_c, H_in>.
+// The pieces:
+//   forward recompute   chunk states, boundary states h_in(c) and the
+//                       per-token (cs, delta) table (the forward's kernels)
+//   ssd_adj_state       G_c per (batch, chunk, head), MFMA over tokens
+//   ssd_adj_pass        R_c in place over G_c, dh0
+//   ssd_bwd_dxdb        per (batch, chunk, 64-token column block s, head
+//                       group): v, dx, x.v, dy.x, f2, the block's share of
+//                       the box, and dB summed over the group
+//   ssd_bwd_dc          per (batch, chunk, 64-token row block l, head group):
+//                       dC summed over the group, f1 per head
+//   ssd_bwd_anchor      per (chunk, head, batch): e^{tot} <R_c, H_in>
+//   ssd_bwd_dt          per head: the prefix / suffix sums of f2 / f1 inside
+//                       each chunk (fp64), da, ddt, dA, ddt_bias, dD
+//   ssd_bwd_reduce      sums of the head-group partials of dB and dC.
+// Every factor e^{cs_l - cs_s} (l >= s), e^{cs_l} and e^{tot - cs_s} is at
+// most 1 (A < 0), so each is evaluated directly per element.
+
+#include "ssd_chunk_common.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kBlk = 64;  // tokens per row / column block
+
+// 16-byte LDS row read (8 bf16): an MFMA A or B operand whose k runs along a row
+__device__ __forceinline__ uint4 lds_row8(const uint16_t* tile, int pitch, int row, int col) {
+  return *reinterpret_cast<const uint4*>(tile + row * pitch + col);
+}
+
+// the 8 bf16 of v times f, rounded back to bf16
+__device__ __forceinline__ uint4 scale8(uint4 v, float f) {
+  const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = pack_bf16x2(bf16_bits_to_f32(a[j] & 0xFFFFu) * f, bf16_bits_to_f32(a[j] >> 16) * f);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Copies `rows` rows of `VPR` 16-byte vectors from a buffer (row r at byte
+// r * row_bytes) into an LDS tile of pitch `pitch` bf16; rows past the
+// buffer's range arrive as zero.  256 threads.
+template <int VPR, int ROWS>
+__device__ __forceinline__ void stage_rows(uint16_t* tile, int pitch, buf_t src, uint32_t row_bytes,
+                                           int row0) {
+  constexpr int ITEMS = VPR * ROWS;
+#pragma unroll
+  for (int it0 = 0; it0 < ITEMS; it0 += kThreads) {
+    const int it = it0 + static_cast<int>(threadIdx.x);
+    if (ITEMS % kThreads == 0 || it < ITEMS) {
+      const int v = it % VPR, r = it / VPR;
+      *reinterpret_cast<uint4*>(tile + r * pitch + v * 8) =
+          buf_load16(src, static_cast<uint32_t>(row0 + r) * row_bytes + v * 16);
+    }
+  }
+}
+
+// row-wise sum over the 16 lanes of a lane group (lanes with the same i / 16)
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1, kWave);
+  v += __shfl_xor(v, 2, kWave);
+  v += __shfl_xor(v, 4, kWave);
+  v += __shfl_xor(v, 8, kWave);
+  return v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// G_c[p][n] = sum_l e^{cs_l} dy_l[p] C_l[n], one workgroup per (batch, chunk,
+// head), computed transposed (D[n][p], contraction over tokens on MFMA with
+// operands from the LDS transpose read) so that a lane holds one p and four
+// consecutive n: 8-byte bf16 stores in the (P, N) layout of the states.
+// ---------------------------------------------------------------------------
+template <int P, int N>
+__global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ Cm,
+    const float2* __restrict__ tok, uint16_t* __restrict__ adj, int T, int H, int G, int Q, int nc,
+    int npairs) {
+  constexpr int YP = P + 16, CP = N + 16;
+  constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4;  // wave w: n tiles w, w+4, ..
+  __shared__ __attribute__((aligned(16))) uint16_t yl[kBlk * YP];  // e^{cs_l} dy_l
+  __shared__ __attribute__((aligned(16))) uint16_t cl[kBlk * CP];  // C_l
+  __shared__ float wl[256];
+
+  int b, c, h;
+  if (!unit_of_block(H, nc, npairs, b, c, h)) return;
+  const int g = h / (H / G);
+  const int t0 = c * Q;
+  const int Lc = min(Q, T - t0);
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int wid = wave_id();
+  const size_t r0 = static_cast<size_t>(b) * T + t0;
+  const float2* tk = tok + ((static_cast<size_t>(b) * nc + c) * H + h) * Q;
+  if (tid < Q) wl[tid] = tid < Lc ? __expf(tk[tid].x) : 0.0f;
+  const uint32_t yrow = static_cast<uint32_t>(H) * P * 2, crow = static_cast<uint32_t>(G) * N * 2;
+  const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
+                              static_cast<uint32_t>(Lc - 1) * yrow + P * 2);
+  const buf_t cbuf = make_buf(Cm + r0 * G * N + static_cast<size_t>(g) * N,
+                              static_cast<uint32_t>(Lc - 1) * crow + N * 2);
+  f32x4 acc[NTW][PT];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int j = 0; j < PT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int l0 = 0; l0 < Lc; l0 += kBlk) {
+    __syncthreads();  // wl written / previous block consumed
+    stage_rows<N / 8, kBlk>(cl, CP, cbuf, crow, l0);
+    // dy rows scaled by e^{cs_l}
+#pragma unroll
+    for (int it0 = 0; it0 < kBlk * (P / 8); it0 += kThreads) {
+      const int it = it0 + tid;
+      if ((kBlk * (P / 8)) % kThreads == 0 || it < kBlk * (P / 8)) {
+        const int v = it % (P / 8), r = it / (P / 8);
+        const float w = l0 + r < Q ? wl[l0 + r] : 0.0f;
+        *reinterpret_cast<uint4*>(yl + r * YP + v * 8) =
+            scale8(buf_load16(ybuf, static_cast<uint32_t>(l0 + r) * yrow + v * 16), w);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kBlk; ks += 32) {
+      uint4 af[NTW], bf[PT];
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) {
+        const int nt = wid + 4 * i;
+        const uint2 lo = lds_tr4(cl, CP, ks + 8 * q, nt * 16);
+        const uint2 hi = lds_tr4(cl, CP, ks + 8 * q + 4, nt * 16);
+        af[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const uint2 lo = lds_tr4(yl, YP, ks + 8 * q, j * 16);
+        const uint2 hi = lds_tr4(yl, YP, ks + 8 * q + 4, j * 16);
+        bf[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+#pragma unroll
+      for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int j = 0; j < PT; ++j) acc[i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+    }
+  }
+  uint16_t* dst = adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N);
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int nt = wid + 4 * i;
+      *reinterpret_cast<uint2*>(dst + (j * 16 + r16) * N + nt * 16 + 4 * q) =
+          make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Adjoint passing, last chunk first:  R_{nc-1} = dh_final,
+// R_{c-1} = lambda_c R_c + G_c,  dh0 = R_{-1}.  R_c overwrites G_c in place
+// (bf16); the running adjoint is fp32.  One thread per 4 consecutive n.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void ssd_adj_pass_kernel(
+    uint16_t* __restrict__ adj, const float* __restrict__ decay, const float* __restrict__ dh_final,
+    float* __restrict__ dh0, int H, int PN, int nc) {
+  constexpr int PF = 8;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int e4 = blockIdx.x * kThreads + threadIdx.x;
+  if (e4 * 4 >= PN) return;
+  const size_t bh = static_cast<size_t>(b) * H + h;
+  const size_t cstride = static_cast<size_t>(H) * PN;
+  uint16_t* base = adj + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e4 * 4;
+  const float* dc = decay + bh * nc;
+  float4 r = dh_final ? *reinterpret_cast<const float4*>(dh_final + bh * PN + e4 * 4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c1 = nc; c1 > 0; c1 -= PF) {  // chunks c1-1 down to c1-PF
+    uint2 gv[PF];
+    float ld[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int cc = c1 - 1 - j;
+      if (cc >= 0) {
+        gv[j] = *reinterpret_cast<const uint2*>(base + cc * cstride);
+        ld[j] = dc[cc];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int cc = c1 - 1 - j;
+      if (cc >= 0) {
+        *reinterpret_cast<uint2*>(base + cc * cstride) =
+            make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+        const float l = ld[j];
+        r.x = l * r.x + bf16_bits_to_f32(gv[j].x & 0xFFFFu);
+        r.y = l * r.y + bf16_bits_to_f32(gv[j].x >> 16);
+        r.z = l * r.z + bf16_bits_to_f32(gv[j].y & 0xFFFFu);
+        r.w = l * r.w + bf16_bits_to_f32(gv[j].y >> 16);
+      }
+    }
+  }
+  if (dh0) *reinterpret_cast<float4*>(dh0 + bh * PN + e4 * 4) = r;
+}
+
+// Work unit of the two block kernels: (b, chunk, 64-token block, head group),
+// in the XCD-grouped order of the forward (the head groups of one (b, chunk,
+// block) share an XCD and its L2, which serves their common B and C rows).
+struct BlockUnit {
+  int b, c, blk, hg;
+};
+__device__ __forceinline__ bool block_unit(int ngroups, int nc, int nb, int Bsz, BlockUnit& u) {
+  int b, cj, hg;
+  if (!unit_coords(blockIdx.x, ngroups, nc * nb, Bsz * nc * nb, b, cj, hg)) return false;
+  u.b = b;
+  u.c = cj / nb;
+  u.blk = cj % nb;
+  u.hg = hg;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Column blocks: per (batch, chunk, block j of source tokens s, group of HPG
+// heads of one B/C group).  Wave w owns the 16 tokens s of tile w of the block
+// and, per head, accumulates
+//   v[s][p]  = e^{tot-cs_s} (B_s . R_c[p]) + sum_{l >= s} M[l][s] dy_l[p]
+//   dB[s][n] += delta_s e^{tot-cs_s} (x_s R_c)[n] + sum_{l >= s} W[l][s] C_l[n]
+// with M[l][s] = e^{cs_l-cs_s} (C_l.B_s) and W[l][s] = e^{cs_l-cs_s} delta_s
+// (dy_l.x_s) for l >= s.  The rows l run over 64-token blocks, last first
+// (the diagonal block last, so that its dy rows are in LDS for dx); C_l.B_s
+// and dy_l.x_s are MFMA tiles whose lane holds one s and four l, which after
+// the mask and decay are the A operands (rows s, contraction over l) of the
+// products with dy and C, read from LDS by the transpose read.  The same
+// fp32 tiles give the box terms ee[l][s] = e^{cs_l-cs_s} delta_s (C_l.B_s)
+// (dy_l.x_s): a suffix scan down each column (lanes, lane groups, then the
+// later l blocks) and a masked sum over the block's columns s < t give the
+// block's share of box_t for every t.  Per head: dx (bf16), x.v, dy.x, f2 and
+// the box shares; after the group: dB.
+// ---------------------------------------------------------------------------
+template <int P, int N>
+__global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ dy, const float* __restrict__ D, const float2* __restrict__ tok,
+    const uint16_t* __restrict__ adj, uint16_t* __restrict__ dx, float* __restrict__ xv,
+    float* __restrict__ dyx, float* __restrict__ f2o, float* __restrict__ boxp,
+    float* __restrict__ dBp, int Bsz, int T, int H, int G, int Q, int nc, int HPG) {
+  constexpr int XP = P + 16, NP = N + 16;
+  constexpr int PT = P / 16, NT = N / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[kBlk * NP];  // C rows of the l block
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[kBlk * XP];  // dy rows of the l block
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBlk * NP];  // B rows of the s block
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[kBlk * XP];  // x rows of the s block
+  __shared__ __attribute__((aligned(16))) uint16_t Rs[P * NP];     // R_c of the head
+  __shared__ float2 tk[256];
+  __shared__ float boxs[4][kBlk];  // per wave: box share of each row of the l block
+
+  const int nb = (Q + kBlk - 1) / kBlk;
+  const int hpg = H / G;
+  BlockUnit u;
+  if (!block_unit(H / HPG, nc, nb, Bsz, u)) return;
+  const int b = u.b, c = u.c, j = u.blk;
+  const size_t BTH = static_cast<size_t>(Bsz) * T * H;
+  const int h0 = u.hg * HPG, g = h0 / hpg, hgl = (h0 % hpg) / HPG;
+  const int t0 = c * Q, Lc = min(Q, T - t0), s0 = j * kBlk;
+  if (s0 >= Lc) return;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int w = wave_id();
+  const size_t r0 = static_cast<size_t>(b) * T + t0;
+  const uint32_t xrow = static_cast<uint32_t>(H) * P * 2, brow = static_cast<uint32_t>(G) * N * 2;
+  const buf_t bbuf = make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N,
+                              static_cast<uint32_t>(Lc - 1) * brow + N * 2);
+  const buf_t cbuf = make_buf(Cm + r0 * G * N + static_cast<size_t>(g) * N,
+                              static_cast<uint32_t>(Lc - 1) * brow + N * 2);
+  stage_rows<N / 8, kBlk>(Bs, NP, bbuf, brow, s0);
+
+  f32x4 dB[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) dB[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int sl = s0 + 16 * w + r16;  // this lane's source token (A rows, score columns)
+  const int nlb = (Lc - s0 + kBlk - 1) / kBlk;
+
+  for (int e = 0; e < HPG; ++e) {
+    const int h = h0 + e;
+    const buf_t xbuf = make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
+                                static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+    const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
+                                static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+    const buf_t rbuf = make_buf(adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
+                                static_cast<uint32_t>(P) * N * 2);
+    __syncthreads();  // previous head done with Xs, Rs, tk, Ys, Cs
+    stage_rows<P / 8, kBlk>(Xs, XP, xbuf, xrow, s0);
+    stage_rows<N / 8, P>(Rs, NP, rbuf, N * 2, 0);
+    if (tid < Q) tk[tid] = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
+    __syncthreads();
+    const float tot = tk[Q - 1].x;
+    const float cs_s = tk[sl].x, dl_s = tk[sl].y;
+
+    // boundary part of v: e^{tot-cs_s} B_s R^T, rows s = 16w + 4q + i of the tile
+    f32x4 v[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) v[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < N; ks += 32) {
+      const uint4 a = lds_row8(Bs, NP, 16 * w + r16, ks + 8 * q);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+        v[pt] = mfma_bf16(as_bf16x8(a), as_bf16x8(lds_row8(Rs, NP, pt * 16 + r16, ks + 8 * q)), v[pt]);
+    }
+    float fr[4];  // e^{tot-cs_s} of the accumulator rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fr[i] = __expf(tot - tk[s0 + 16 * w + 4 * q + i].x);
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[pt][i] *= fr[i];
+    // f2_s = delta_s x_s . (e^{tot-cs_s} R_c B_s): the R part of x.v, before the rest
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sr = 16 * w + 4 * q + i;
+      float part = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) part += bf16_bits_to_f32(Xs[sr * XP + pt * 16 + r16]) * v[pt][i];
+      part = sum16(part);
+      if (r16 == 0 && s0 + sr < Lc) f2o[(r0 + s0 + sr) * H + h] = tk[s0 + sr].y * part;
+    }
+    // boundary part of dB: delta_s e^{tot-cs_s} x_s R (A rows s = this lane's sl)
+    {
+      const float f2 = dl_s * __expf(tot - cs_s);
+#pragma unroll
+      for (int ks = 0; ks < P; ks += 32) {
+        const uint4 a = scale8(lds_row8(Xs, XP, 16 * w + r16, ks + 8 * q), f2);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint2 lo = lds_tr4(Rs, NP, ks + 8 * q, nt * 16);
+          const uint2 hi = lds_tr4(Rs, NP, ks + 8 * q + 4, nt * 16);
+          dB[nt] = mfma_bf16(as_bf16x8(a), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dB[nt]);
+        }
+      }
+    }
+
+    float car = 0.0f;  // sum over the later l blocks of this column's box terms
+    for (int lb = nlb - 1; lb >= 0; --lb) {
+      const int l0 = s0 + lb * kBlk;
+      __syncthreads();
+      stage_rows<N / 8, kBlk>(Cs, NP, cbuf, brow, l0);
+      stage_rows<P / 8, kBlk>(Ys, XP, ybuf, xrow, l0);
+      __syncthreads();
+      // score tiles of this wave's 16 columns s: lane holds s = sl, l = l0 + 16 lt + 4q + i
+      f32x4 s1[4], s2[4];
+#pragma unroll
+      for (int lt = 0; lt < 4; ++lt) {
+        s1[lt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s2[lt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < N; ks += 32) {
+        const uint4 bb = lds_row8(Bs, NP, 16 * w + r16, ks + 8 * q);
+#pragma unroll
+        for (int lt = 0; lt < 4; ++lt)
+          s1[lt] = mfma_bf16(as_bf16x8(lds_row8(Cs, NP, lt * 16 + r16, ks + 8 * q)), as_bf16x8(bb), s1[lt]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < P; ks += 32) {
+        const uint4 xx = lds_row8(Xs, XP, 16 * w + r16, ks + 8 * q);
+#pragma unroll
+        for (int lt = 0; lt < 4; ++lt)
+          s2[lt] = mfma_bf16(as_bf16x8(lds_row8(Ys, XP, lt * 16 + r16, ks + 8 * q)), as_bf16x8(xx), s2[lt]);
+      }
+      // mask and decay -> bf16 A operands; k slot of lane group q: l = 16 lt + 4q + i
+      uint32_t am[4][2], aw[4][2];
+      float ee[4][4];  // box terms e^{cs_l-cs_s} delta_s (C_l.B_s)(dy_l.x_s), fp32
+#pragma unroll
+      for (int lt = 0; lt < 4; ++lt) {
+        float mv[4], wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int l = l0 + 16 * lt + 4 * q + i;
+          const bool ok = l >= sl && l < Lc && sl < Lc;
+          const float d = ok ? __expf(tk[l < Q ? l : Q - 1].x - cs_s) : 0.0f;
+          mv[i] = d * s1[lt][i];
+          wv[i] = d * dl_s * s2[lt][i];
+          ee[lt][i] = wv[i] * s1[lt][i];
+        }
+        am[lt][0] = pack_bf16x2(mv[0], mv[1]);
+        am[lt][1] = pack_bf16x2(mv[2], mv[3]);
+        aw[lt][0] = pack_bf16x2(wv[0], wv[1]);
+        aw[lt][1] = pack_bf16x2(wv[2], wv[3]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint4 Am = make_uint4(am[2 * kk][0], am[2 * kk][1], am[2 * kk + 1][0], am[2 * kk + 1][1]);
+        const uint4 Aw = make_uint4(aw[2 * kk][0], aw[2 * kk][1], aw[2 * kk + 1][0], aw[2 * kk + 1][1]);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const uint2 lo = lds_tr4(Ys, XP, 32 * kk + 4 * q, pt * 16);
+          const uint2 hi = lds_tr4(Ys, XP, 32 * kk + 16 + 4 * q, pt * 16);
+          v[pt] = mfma_bf16(as_bf16x8(Am), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), v[pt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint2 lo = lds_tr4(Cs, NP, 32 * kk + 4 * q, nt * 16);
+          const uint2 hi = lds_tr4(Cs, NP, 32 * kk + 16 + 4 * q, nt * 16);
+          dB[nt] = mfma_bf16(as_bf16x8(Aw), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dB[nt]);
+        }
+      }
+      // box: K_s(t) = sum_{l >= t} ee[l][s] down this lane's column s (rows of the
+      // block: 16 lt + 4 q + i, lane group q), then for every row t the sum over
+      // the columns s < t of the workgroup's block
+      float tt[4];
+#pragma unroll
+      for (int lt = 0; lt < 4; ++lt) {
+        ee[lt][2] += ee[lt][3];
+        ee[lt][1] += ee[lt][2];
+        ee[lt][0] += ee[lt][1];
+        const float g0 = __shfl(ee[lt][0], r16, kWave), g1 = __shfl(ee[lt][0], r16 + 16, kWave);
+        const float g2 = __shfl(ee[lt][0], r16 + 32, kWave), g3 = __shfl(ee[lt][0], r16 + 48, kWave);
+        const float after = (q < 1 ? g1 : 0.0f) + (q < 2 ? g2 : 0.0f) + (q < 3 ? g3 : 0.0f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ee[lt][i] += after;
+        tt[lt] = g0 + g1 + g2 + g3;
+      }
+      {
+        float later = car;
+#pragma unroll
+        for (int lt = 3; lt >= 0; --lt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ee[lt][i] += later;
+          later += tt[lt];
+        }
+        car = later;
+      }
+#pragma unroll
+      for (int lt = 0; lt < 4; ++lt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * lt + 4 * q + i;
+          const float part = sum16(sl < l0 + row ? ee[lt][i] : 0.0f);
+          if (r16 == 0) boxs[w][row] = part;
+        }
+      __syncthreads();
+      if (tid < kBlk && l0 + tid < Lc)
+        boxp[static_cast<size_t>(j) * BTH + (r0 + l0 + tid) * H + h] =
+            boxs[0][tid] + boxs[1][tid] + boxs[2][tid] + boxs[3][tid];
+    }
+
+    // outputs of head h: lane holds p = 16 pt + r16 of rows s = s0 + 16w + 4q + i;
+    // Ys now holds the dy rows of the s block (the last l block was the diagonal)
+    const float Dh = D ? D[h] : 0.0f;
+    const buf_t dxbuf = make_buf(dx + r0 * H * P + static_cast<size_t>(h) * P,
+                                 static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sr = 16 * w + 4 * q + i;  // row within the block
+      const float dls = tk[s0 + sr].y;
+      float pxv = 0.0f, pdx = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const int p = pt * 16 + r16;
+        const float xe = bf16_bits_to_f32(Xs[sr * XP + p]);
+        const float ye = bf16_bits_to_f32(Ys[sr * XP + p]);
+        pxv += xe * v[pt][i];
+        pdx += xe * ye;
+        const float gx = dls * v[pt][i] + Dh * ye;
+        const uint32_t off = (static_cast<uint32_t>(s0 + sr) * xrow + p * 2);
+        __builtin_amdgcn_raw_buffer_store_b16(
+            __builtin_bit_cast(unsigned short, static_cast<__bf16>(gx)), dxbuf, off, 0, 0);
+      }
+      pxv = sum16(pxv);
+      pdx = sum16(pdx);
+      if (r16 == 0 && s0 + sr < Lc) {
+        xv[(r0 + s0 + sr) * H + h] = pxv;
+        dyx[(r0 + s0 + sr) * H + h] = pdx;
+      }
+    }
+  }
+
+  // dB of the head group: lane holds n = 16 nt + r16 of rows s = s0 + 16w + 4q + i
+  float* dst = dBp + ((static_cast<size_t>(hgl) * Bsz + b) * T + t0) * G * N + static_cast<size_t>(g) * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = s0 + 16 * w + 4 * q + i;
+    if (s < Lc) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) dst[static_cast<size_t>(s) * G * N + nt * 16 + r16] = dB[nt][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row blocks: per (batch, chunk, block i of target tokens l, group of HPG
+// heads).  Wave w owns the 16 tokens l of tile w and, per head, accumulates
+//   dC_h[l][n] = e^{cs_l} (dy_l H_in)[n] + sum_{s <= l} W[l][s] B_s[n],
+//   W[l][s] = e^{cs_l - cs_s} delta_s (dy_l . x_s),
+// the scores computed transposed (x_s . dy_l: a lane holds one l and four s,
+// the A operand of the product with B).  Per head: f1_l = C_l . (the H_in
+// part of dC_h[l]); after the group: dC.
+// ---------------------------------------------------------------------------
+template <int P, int N>
+__global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ dy, const float2* __restrict__ tok,
+    const uint16_t* __restrict__ states, float* __restrict__ f1o, float* __restrict__ dCp, int Bsz,
+    int T, int H, int G, int Q, int nc, int HPG) {
+  constexpr int XP = P + 16, NP = N + 16;
+  constexpr int NT = N / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[kBlk * XP];  // x rows of the s block
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBlk * NP];  // B rows of the s block
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[kBlk * XP];  // dy rows of the l block
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[P * NP];     // h_in(c) of the head
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[kBlk * NP];  // C rows of the l block
+  __shared__ float2 tk[256];
+
+  const int nb = (Q + kBlk - 1) / kBlk;
+  const int hpg = H / G;
+  BlockUnit u;
+  if (!block_unit(H / HPG, nc, nb, Bsz, u)) return;
+  const int b = u.b, c = u.c, ib = u.blk;
+  const int h0 = u.hg * HPG, g = h0 / hpg, hgl = (h0 % hpg) / HPG;
+  const int t0 = c * Q, Lc = min(Q, T - t0), l0 = ib * kBlk;
+  if (l0 >= Lc) return;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int w = wave_id();
+  const size_t r0 = static_cast<size_t>(b) * T + t0;
+  const uint32_t xrow = static_cast<uint32_t>(H) * P * 2, brow = static_cast<uint32_t>(G) * N * 2;
+  const buf_t bbuf = make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N,
+                              static_cast<uint32_t>(Lc - 1) * brow + N * 2);
+  const buf_t cbuf = make_buf(Cm + r0 * G * N + static_cast<size_t>(g) * N,
+                              static_cast<uint32_t>(Lc - 1) * brow + N * 2);
+  stage_rows<N / 8, kBlk>(Cs, NP, cbuf, brow, l0);
+
+  f32x4 dCg[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) dCg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ll = l0 + 16 * w + r16;  // this lane's target token (A rows)
+
+  for (int e = 0; e < HPG; ++e) {
+    const int h = h0 + e;
+    const buf_t xbuf = make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
+                                static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+    const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
+                                static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+    const buf_t hbuf = make_buf(states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
+                                static_cast<uint32_t>(P) * N * 2);
+    __syncthreads();
+    stage_rows<P / 8, kBlk>(Ys, XP, ybuf, xrow, l0);
+    stage_rows<N / 8, P>(Hs, NP, hbuf, N * 2, 0);
+    if (tid < Q) tk[tid] = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
+    __syncthreads();
+    const float cs_l = tk[ll < Q ? ll : Q - 1].x;
+
+    // boundary: e^{cs_l} dy_l H_in (A rows l = this lane's ll)
+    f32x4 dC[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dC[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const float f = __expf(cs_l);
+#pragma unroll
+      for (int ks = 0; ks < P; ks += 32) {
+        const uint4 a = scale8(lds_row8(Ys, XP, 16 * w + r16, ks + 8 * q), f);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint2 lo = lds_tr4(Hs, NP, ks + 8 * q, nt * 16);
+          const uint2 hi = lds_tr4(Hs, NP, ks + 8 * q + 4, nt * 16);
+          dC[nt] = mfma_bf16(as_bf16x8(a), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dC[nt]);
+        }
+      }
+    }
+    // f1_l = e^{cs_l} C_l . (H_in^T dy_l): the H_in part of C_l . dC_h[l]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lr = 16 * w + 4 * q + i;
+      float pd = 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pd += bf16_bits_to_f32(Cs[lr * NP + nt * 16 + r16]) * dC[nt][i];
+      pd = sum16(pd);
+      if (r16 == 0 && l0 + lr < Lc) f1o[(r0 + l0 + lr) * H + h] = pd;
+    }
+    for (int sb = 0; sb <= ib; ++sb) {
+      const int s0 = sb * kBlk;
+      __syncthreads();
+      stage_rows<P / 8, kBlk>(Xs, XP, xbuf, xrow, s0);
+      stage_rows<N / 8, kBlk>(Bs, NP, bbuf, brow, s0);
+      __syncthreads();
+      // transposed scores: lane holds l = ll, s = s0 + 16 st + 4q + i
+      f32x4 st2[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) st2[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < P; ks += 32) {
+        const uint4 yy = lds_row8(Ys, XP, 16 * w + r16, ks + 8 * q);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          st2[st] = mfma_bf16(as_bf16x8(lds_row8(Xs, XP, st * 16 + r16, ks + 8 * q)), as_bf16x8(yy), st2[st]);
+      }
+      uint32_t aw[4][2];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = s0 + 16 * st + 4 * q + i;
+          const bool ok = ll >= s && ll < Lc && s < Lc;
+          const float2 ts = tk[s];
+          wv[i] = ok ? __expf(cs_l - ts.x) * ts.y * st2[st][i] : 0.0f;
+        }
+        aw[st][0] = pack_bf16x2(wv[0], wv[1]);
+        aw[st][1] = pack_bf16x2(wv[2], wv[3]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint4 Aw = make_uint4(aw[2 * kk][0], aw[2 * kk][1], aw[2 * kk + 1][0], aw[2 * kk + 1][1]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint2 lo = lds_tr4(Bs, NP, 32 * kk + 4 * q, nt * 16);
+          const uint2 hi = lds_tr4(Bs, NP, 32 * kk + 16 + 4 * q, nt * 16);
+          dC[nt] = mfma_bf16(as_bf16x8(Aw), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dC[nt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dCg[nt][i] += dC[nt][i];
+  }
+
+  float* dst = dCp + ((static_cast<size_t>(hgl) * Bsz + b) * T + t0) * G * N + static_cast<size_t>(g) * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int l = l0 + 16 * w + 4 * q + i;
+    if (l < Lc) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) dst[static_cast<size_t>(l) * G * N + nt * 16 + r16] = dCg[nt][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk constants: e^{tot_c} <R_c, H_in(c)> (the term of da shared by every
+// step of chunk c), one workgroup per (chunk, head, batch).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void ssd_bwd_const_kernel(
+    const uint16_t* __restrict__ adj, const uint16_t* __restrict__ states,
+    const float* __restrict__ decay, double* __restrict__ cst, int H, int PN, int nc) {
+  __shared__ double ws4[4];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
+  const size_t bh = static_cast<size_t>(b) * H + h;
+  const size_t slot = ((static_cast<size_t>(b) * nc + c) * H + h) * PN;
+  double s = 0.0;
+  for (int i = tid * 8; i < PN; i += kThreads * 8) {
+    const uint4 rv = *reinterpret_cast<const uint4*>(adj + slot + i);
+    const uint4 hv = *reinterpret_cast<const uint4*>(states + slot + i);
+    const uint32_t ra[4] = {rv.x, rv.y, rv.z, rv.w}, ha[4] = {hv.x, hv.y, hv.z, hv.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc = fmaf(bf16_bits_to_f32(ra[k] & 0xFFFFu), bf16_bits_to_f32(ha[k] & 0xFFFFu), acc);
+      acc = fmaf(bf16_bits_to_f32(ra[k] >> 16), bf16_bits_to_f32(ha[k] >> 16), acc);
+    }
+    s += acc;
+  }
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (lane == 0) ws4[wid] = s;
+  __syncthreads();
+  if (tid == 0)
+    cst[bh * nc + c] = static_cast<double>(decay[bh * nc + c]) * (ws4[0] + ws4[1] + ws4[2] + ws4[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Step-size gradients, one workgroup per head, batch entries and chunks in
+// turn (thread l = token l of the chunk):
+//   da_l = box_l + sum_{l' >= l} f1_l' + sum_{s < l} f2_s + e^{tot} <R_c, H_in>
+// (fp64 block scans: f1 summed from the chunk's end, f2 from its start), then
+// ddelta_l = A da_l + x_l.v_l, ddt_l = ddelta_l sigmoid(z_l) [lo <= sp <= hi],
+// and the per-head sums dA, ddt_bias, dD over the batch.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
+    const float* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
+    float dt_min, float dt_max, const float* __restrict__ f1, const float* __restrict__ f2,
+    const float* __restrict__ boxp, const float* __restrict__ xv, const float* __restrict__ dyx,
+    const double* __restrict__ cst, float* __restrict__ ddt, float* __restrict__ dA,
+    float* __restrict__ ddt_bias, float* __restrict__ dD, int Bsz, int T, int H, int Q, int nc) {
+  __shared__ double wsum[4];
+  __shared__ double red[3][4];
+  __shared__ double sfx[kThreads];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
+  const float a_re = A[h];
+  const float bias = dt_bias ? dt_bias[h] : 0.0f;
+  const size_t BTH = static_cast<size_t>(Bsz) * T * H;
+  double sA = 0.0, sBias = 0.0, sD = 0.0;
+  for (int b = 0; b < Bsz; ++b) {
+    for (int c = 0; c < nc; ++c) {
+      const int t = c * Q + tid;
+      const bool in = tid < Q && t < T;
+      const size_t row = (static_cast<size_t>(b) * T + (in ? t : 0)) * H + h;
+      const double f1v = in ? static_cast<double>(f1[row]) : 0.0;
+      const double f2v = in ? static_cast<double>(f2[row]) : 0.0;
+      // f1 summed from the chunk's end: thread k scans token 255 - k
+      sfx[tid] = f1v;
+      __syncthreads();
+      const double rev = block_inclusive_scan(sfx[kThreads - 1 - tid], wsum);
+      __syncthreads();
+      sfx[kThreads - 1 - tid] = rev;
+      __syncthreads();
+      const double f1_suffix = sfx[tid];
+      const double f2_prefix = block_inclusive_scan(f2v, wsum) - f2v;
+      __syncthreads();
+      if (in) {
+        double box = 0.0;
+        for (int jb = 0; jb <= tid / kBlk; ++jb) box += boxp[static_cast<size_t>(jb) * BTH + row];
+        const double da = box + f1_suffix + f2_prefix + cst[(static_cast<size_t>(b) * H + h) * nc + c];
+        const float z = dt[row] + bias;
+        const float d = step_size(dt[row], bias, dt_min, dt_max);
+        const float xvt = xv[row];
+        const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+        const bool pass = sp >= dt_min && sp <= dt_max;
+        const double dd = static_cast<double>(a_re) * da + xvt;
+        const double gz = pass ? dd / (1.0 + exp(-static_cast<double>(z))) : 0.0;
+        ddt[row] = static_cast<float>(gz);
+        sA += static_cast<double>(d) * da;
+        sBias += gz;
+        sD += dyx[row];
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    sA += __shfl_xor(sA, o, kWave);
+    sBias += __shfl_xor(sBias, o, kWave);
+    sD += __shfl_xor(sD, o, kWave);
+  }
+  if (lane == 0) {
+    red[0][wid] = sA;
+    red[1][wid] = sBias;
+    red[2][wid] = sD;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    dA[h] = static_cast<float>(red[0][0] + red[0][1] + red[0][2] + red[0][3]);
+    ddt_bias[h] = static_cast<float>(red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+    dD[h] = static_cast<float>(red[2][0] + red[2][1] + red[2][2] + red[2][3]);
+  }
+}
+
+// dB (or dC) = sum of the nparts head-group partials, float4 at a time
+__global__ __launch_bounds__(kThreads) void ssd_bwd_reduce_kernel(const float* __restrict__ part,
+                                                                  float* __restrict__ out,
+                                                                  size_t n4, int nparts) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n4) return;
+  const float4* p = reinterpret_cast<const float4*>(part);
+  float4 s = p[i];
+  for (int k = 1; k < nparts; ++k) {
+    const float4 v = p[i + k * n4];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  reinterpret_cast<float4*>(out)[i] = s;
+}
+
+// heads per workgroup of the block kernels: the largest divisor of H/G up to 16
+int bwd_heads_per_group(int H, int G) {
+  const int hpg = H / G;
+  for (int d = hpg < 16 ? hpg : 16; d >= 1; --d)
+    if (hpg % d == 0) return d;
+  return 1;
+}
+
+// workspace layout of the backward, after the forward's own (states, decays,
+// token table): the adjoint states (bf16); f1, f2, x.v, dy.x (fp32 per token
+// and head); the box shares of the column blocks (fp32, one per block); the
+// chunk constants of da (fp64); the dB and dC partials (fp32)
+struct BwdLayout {
+  size_t fwd, adj, f1, f2, xv, dyx, box, cst, dBp, dCp, total;
+};
+static BwdLayout bwd_layout(int Bsz, int T, int H, int P, int G, int N, int chunk) {
+  const int nc = (T + chunk - 1) / chunk;
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  BwdLayout L{};
+  const size_t fwd_floats = workspace_state_floats(Bsz, nc, H, P, N) + workspace_decay_floats(Bsz, nc, H) +
+                            workspace_token_floats(Bsz, nc, H, chunk);
+  size_t o = up(fwd_floats * 4);
+  L.fwd = 0;
+  L.adj = o;
+  o += up(static_cast<size_t>(Bsz) * nc * H * P * N * 2);
+  const size_t tok = static_cast<size_t>(Bsz) * T * H * 4;
+  L.f1 = o;
+  o += up(tok);
+  L.f2 = o;
+  o += up(tok);
+  L.xv = o;
+  o += up(tok);
+  L.dyx = o;
+  o += up(tok);
+  L.box = o;
+  o += up(tok * ((chunk + kBlk - 1) / kBlk));
+  L.cst = o;
+  o += up(static_cast<size_t>(Bsz) * H * nc * 8);
+  const int nparts = (H / G) / bwd_heads_per_group(H, G);
+  const size_t part = static_cast<size_t>(nparts) * Bsz * T * G * N * 4;
+  L.dBp = o;
+  o += up(part);
+  L.dCp = o;
+  o += up(part);
+  L.total = o + 256;
+  return L;
+}
+
+size_t bwd_workspace_bytes(int Bsz, int T, int H, int P, int G, int N, int chunk) {
+  return bwd_layout(Bsz, T, H, P, G, N, chunk).total;
+}
+
+template <int P, int N>
+static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+  const int Q = a.chunk;
+  const int nc = (a.T + Q - 1) / Q;
+  const BwdLayout L = bwd_layout(a.Bsz, a.T, a.H, P, a.G, N, Q);
+  char* ws = static_cast<char*>(a.workspace);
+  const hipEvent_t* ev = a.events;
+  // forward recompute: chunk states -> boundary states, decays, token table
+  ChunkArgs f{};
+  f.x = a.x;
+  f.dt = a.dt;
+  f.A = a.A;
+  f.B = a.B;
+  f.C = a.C;
+  f.dt_bias = a.dt_bias;
+  f.dt_min = a.dt_min;
+  f.dt_max = a.dt_max;
+  f.h0 = a.h0;
+  f.Bsz = a.Bsz;
+  f.T = a.T;
+  f.H = a.H;
+  f.P = P;
+  f.G = a.G;
+  f.N = N;
+  f.chunk = Q;
+  f.dtype = 1;
+  f.workspace = ws;
+  f.events = const_cast<hipEvent_t*>(ev);
+  hipError_t e = run_chunk_states_bf16(f, st);
+  if (e != hipSuccess) return e;
+  const uint16_t* states = reinterpret_cast<const uint16_t*>(ws);
+  const float* decay = reinterpret_cast<const float*>(ws) + workspace_state_floats(a.Bsz, nc, a.H, P, N);
+  const float2* tok = reinterpret_cast<const float2*>(decay + workspace_decay_floats(a.Bsz, nc, a.H));
+  uint16_t* adj = reinterpret_cast<uint16_t*>(ws + L.adj);
+  float* f1 = reinterpret_cast<float*>(ws + L.f1);
+  float* f2 = reinterpret_cast<float*>(ws + L.f2);
+  float* box = reinterpret_cast<float*>(ws + L.box);
+  float* xv = reinterpret_cast<float*>(ws + L.xv);
+  float* dyx = reinterpret_cast<float*>(ws + L.dyx);
+  float* dBp = reinterpret_cast<float*>(ws + L.dBp);
+  float* dCp = reinterpret_cast<float*>(ws + L.dCp);
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* B = static_cast<const uint16_t*>(a.B);
+  const uint16_t* C = static_cast<const uint16_t*>(a.C);
+  const uint16_t* dy = static_cast<const uint16_t*>(a.dy);
+  const int npairs = a.Bsz * nc;
+  const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
+  launch_k(nc > 0, ssd_adj_state_kernel<P, N>, dim3(blocks), dim3(kThreads), st, ev ? ev + 4 : nullptr,
+           dy, C, tok, adj, a.T, a.H, a.G, Q, nc, npairs);
+  launch_k(true, ssd_adj_pass_kernel, dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
+           dim3(kThreads), st, ev ? ev + 6 : nullptr, adj, decay, a.dh_final, a.dh0, a.H, P * N, nc);
+  const int HPG = bwd_heads_per_group(a.H, a.G);
+  const int nb = (Q + kBlk - 1) / kBlk;
+  const int bpairs = a.Bsz * nc * nb;
+  const unsigned bblocks = static_cast<unsigned>((bpairs + kXCD - 1) / kXCD) * kXCD * (a.H / HPG);
+  launch_k(nc > 0, ssd_bwd_dxdb_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 8 : nullptr,
+           x, B, C, dy, a.D, tok, static_cast<const uint16_t*>(adj), static_cast<uint16_t*>(a.dx), xv,
+           dyx, f2, box, dBp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
+  launch_k(nc > 0, ssd_bwd_dc_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 10 : nullptr,
+           x, B, C, dy, tok, states, f1, dCp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
+  double* cst = reinterpret_cast<double*>(ws + L.cst);
+  launch_k(nc > 0, ssd_bwd_const_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
+           ev ? ev + 12 : nullptr, static_cast<const uint16_t*>(adj), states, decay, cst, a.H, P * N,
+           nc);
+  launch_k(true, ssd_bwd_dt_kernel, dim3(a.H), dim3(kThreads), st, ev ? ev + 14 : nullptr, a.dt, a.A,
+           a.dt_bias, a.dt_min, a.dt_max, static_cast<const float*>(f1), static_cast<const float*>(f2),
+           static_cast<const float*>(box), static_cast<const float*>(xv), static_cast<const float*>(dyx),
+           static_cast<const double*>(cst), a.ddt, a.dA, a.ddt_bias, a.dD, a.Bsz, a.T, a.H, Q, nc);
+  const size_t n4 = static_cast<size_t>(a.Bsz) * a.T * a.G * N / 4;
+  const int nparts = (a.H / a.G) / HPG;
+  const unsigned rblocks = static_cast<unsigned>((n4 + kThreads - 1) / kThreads);
+  launch_k(n4 > 0, ssd_bwd_reduce_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(kThreads), st,
+           ev ? ev + 16 : nullptr, static_cast<const float*>(dBp), a.dB, n4, nparts);
+  launch_k(n4 > 0, ssd_bwd_reduce_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(kThreads), st,
+           ev ? ev + 18 : nullptr, static_cast<const float*>(dCp), a.dC, n4, nparts);
+  return hipGetLastError();
+}
+
+hipError_t run_chunk_bwd_bf16(const BwdArgs& a, hipStream_t st) {
+  if (a.P == 64 && a.N == 128) return launch_bwd<64, 128>(a, st);
+  if (a.P == 64 && a.N == 64) return launch_bwd<64, 64>(a, st);
+  if (a.P == 32 && a.N == 64) return launch_bwd<32, 64>(a, st);
+  if (a.P == 32 && a.N == 128) return launch_bwd<32, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssd

@@ -664,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 template <int P, int N>
-static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st) {
+static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output = true) {
   const int nc = (a.T + a.chunk - 1) / a.chunk;
   const int npairs = a.Bsz * nc;
   // workspace: bf16 chunk states (Bsz, nc, H, P, N), overwritten in place by
@@ -692,6 +692,7 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st) {
            dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
            ev ? ev + 2 : nullptr, states, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
            P * N, nc);
+  if (!with_output) return hipGetLastError();
   launch_k(nc > 0, ssd_scan_bf16_kernel<P, N>, dim3(blocks), dim3(kThreads), st,
            ev ? ev + 4 : nullptr, x, B, C, a.D, static_cast<const float2*>(tok),
            static_cast<const uint16_t*>(states), static_cast<uint16_t*>(a.y), a.T, a.H, a.G,
@@ -700,26 +701,32 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st) {
 }
 
 template <int P>
-static hipError_t dispatch_bf16_n(const ChunkArgs& a, hipStream_t st) {
+static hipError_t dispatch_bf16_n(const ChunkArgs& a, hipStream_t st, bool with_output) {
   switch (a.N) {
-    case 16: return launch_bf16<P, 16>(a, st);
-    case 32: return launch_bf16<P, 32>(a, st);
-    case 64: return launch_bf16<P, 64>(a, st);
-    case 128: return launch_bf16<P, 128>(a, st);
+    case 16: return launch_bf16<P, 16>(a, st, with_output);
+    case 32: return launch_bf16<P, 32>(a, st, with_output);
+    case 64: return launch_bf16<P, 64>(a, st, with_output);
+    case 128: return launch_bf16<P, 128>(a, st, with_output);
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st) {
+static hipError_t dispatch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output) {
   switch (a.P) {
-    case 16: return dispatch_bf16_n<16>(a, st);
-    case 32: return dispatch_bf16_n<32>(a, st);
-    case 64: return dispatch_bf16_n<64>(a, st);
-    case 128: return dispatch_bf16_n<128>(a, st);
+    case 16: return dispatch_bf16_n<16>(a, st, with_output);
+    case 32: return dispatch_bf16_n<32>(a, st, with_output);
+    case 64: return dispatch_bf16_n<64>(a, st, with_output);
+    case 128: return dispatch_bf16_n<128>(a, st, with_output);
     default: break;
   }
   return hipErrorInvalidValue;
 }
+
+hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st) { return dispatch_bf16(a, st, true); }
+
+// the chunk states, boundary states, decays, token table and h_final of a
+// forward call without its outputs (the backward recomputes these)
+hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st) { return dispatch_bf16(a, st, false); }
 
 }  // namespace ssd

@@ -53,6 +53,31 @@ struct ConvArgs {
   hipEvent_t* events;      // NULL, or start/stop of the kernel
 };
 
+struct BwdArgs {
+  const void* x;
+  const float* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* dt_bias;
+  float dt_min, dt_max;
+  const float* h0;
+  const void* dy;
+  const float* dh_final;
+  void* dx;
+  float* ddt;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;
+  float* ddt_bias;
+  float* dh0;
+  int Bsz, T, H, P, G, N, chunk;
+  void* workspace;
+  hipEvent_t* events;  // NULL, or 20: start/stop of each of the 10 kernels
+};
+
 // floats of chunk-boundary states: (Bsz, nc, H, P, KC), KC = N or 2N
 inline size_t workspace_state_floats(int Bsz, int nc, int H, int P, int KC) {
   return static_cast<size_t>(Bsz) * nc * H * P * KC;
@@ -80,6 +105,10 @@ hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t run_complex_decode(const DecodeArgs& a, hipStream_t st);  // D unused
+hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st);  // state + pass kernels only
+hipError_t run_chunk_bwd_bf16(const BwdArgs& a, hipStream_t st);
+size_t bwd_workspace_bytes(int Bsz, int T, int H, int P, int G, int N, int chunk);
+int bwd_heads_per_group(int H, int G);
 hipError_t run_conv1d(const ConvArgs& a, hipStream_t st);
 hipError_t run_conv1d_step(const ConvArgs& a, hipStream_t st);  // float32, T = 1
 int conv_tokens_per_thread();

@@ -563,7 +563,8 @@ def test_bwd_matches_finite_differences(G, seed):
 
 
 def test_bwd_bf16_equals_widened_f32():
-    """bfloat16 inputs are read as the float32 values they widen to."""
+    """bfloat16 inputs are read as the float32 values they widen to (dB and dC
+    sum over heads in thread order: equal up to that reassociation)."""
     inp = _real(Bsz=1, T=9, H=2, P=3, N=4, G=1, seed=8, dtype="bf16", with_h0=True)
     rng = np.random.default_rng(9)
     dy = inputs.f32_to_bf16_bits(rng.standard_normal(inp["x"].shape).astype(np.float32))
@@ -574,7 +575,7 @@ def test_bwd_bf16_equals_widened_f32():
     b = oracle.bwd(w(inp["x"]), inp["dt"], inp["A"], w(inp["B"]), w(inp["C"]), w(dy), inp["D"],
                    inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
     for k in a:
-        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+        np.testing.assert_allclose(a[k], b[k], rtol=1e-13, atol=1e-300, err_msg=k)
 
 
 def test_bwd_clamped_steps_pass_no_gradient_to_dt():
@@ -588,3 +589,14 @@ def test_bwd_clamped_steps_pass_no_gradient_to_dt():
     assert np.all(g["ddt"][clamped] == 0.0)
     assert np.all(g["ddt"][~clamped] != 0.0)
     np.testing.assert_allclose(g["ddt_bias"], g["ddt"].sum(axis=(0, 1)), rtol=1e-12)
+
+
+def test_bwd_log_decay_gradient_sums_to_dA():
+    """da_t, the gradient of the step's log-decay A delta_t, is what dA sums:
+    dA_h = sum_{b,t} delta_t da_t (dA itself is pinned by finite differences)."""
+    inp, dy, dhf = _bwd_case(1, 3)
+    g = oracle.bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], dy, inp["D"],
+                   inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
+    d = np.clip(np.logaddexp(0.0, inp["dt"].astype(np.float64) + inp["dt_bias"]),
+                inp["dt_min"], inp["dt_max"])
+    np.testing.assert_allclose(g["dA"], (d * g["da"]).sum(axis=(0, 1)), rtol=1e-12)
