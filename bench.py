@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bitmamba_bf16",
                     choices=["bitmamba_bf16", "long_bf16", "mamba3lite_complex", "tiny_f32",
-                             "decode_f32", "decode_complex", "conv_bf16", "conv_decode_f32"])
+                             "decode_f32", "decode_complex", "conv_bf16", "conv_decode_f32",
+                             "bwd_bf16"])
     ap.add_argument("--no-flush", action="store_true",
                     help="keep the Infinity Cache warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -103,6 +104,7 @@ KERNEL_SOURCES = {
     "decode_complex": ["ssd_decode.hip"],
     "conv_bf16": ["ssd_conv.hip"],
     "conv_decode_f32": ["ssd_conv.hip"],
+    "bwd_bf16": ["ssd_bwd_bf16.hip", "ssd_chunk_bf16.hip"],
 }
 
 
@@ -287,6 +289,8 @@ def main():
         return bench_decode(args, cfg)
     if cfg["kind"] in ("conv", "conv_decode"):
         return bench_conv(args, cfg)
+    if cfg["kind"] == "bwd":
+        return bench_bwd(args, cfg)
     inp = inputs.make_workload(args.workload, seed=0)
     Q = cfg["chunk"]
     dims = dict(inp["dims"], Q=Q)
@@ -607,6 +611,169 @@ def cpu_baseline_conv(inp, target_s):
             "cores": oracle.threads_used(), "kind": "oracle",
             "sample": f"the whole workload ({dims['Bsz']} x {dims['T']} tokens x {Ch} channels), "
                       f"float64, {reps} passes in {total:.2f} s"}
+
+
+BWD_KERNELS = ["ssd_state_bf16_kernel", "ssd_pass_bf16_kernel", "ssd_adj_state_kernel",
+               "ssd_adj_pass_kernel", "ssd_bwd_dxdb_kernel", "ssd_bwd_dc_kernel",
+               "ssd_bwd_const_kernel", "ssd_bwd_dt_kernel", "ssd_bwd_dt_sum_kernel",
+               "ssd_bwd_reduce_kernel(dB)", "ssd_bwd_reduce_kernel(dC)"]
+
+
+def bwd_kernel_costs(dims, nparts):
+    """Algorithmic HBM bytes and MFMA flops of each kernel of one backward
+    call (bf16 x/B/C/dy; every array a kernel must read or write counted once;
+    flops: the lower-triangle in-chunk products and the boundary products)."""
+    Bsz, T, H, P, G, N, Q = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N", "Q"))
+    nc = -(-T // Q)
+    nb = -(-Q // 64)
+    x = Bsz * T * H * P * 2                 # x, dy, dx (bf16)
+    bc = Bsz * T * G * N * 2                # B or C (bf16)
+    st = Bsz * nc * H * P * N * 2           # bf16 chunk / boundary / adjoint states
+    tok = Bsz * nc * H * Q * 8              # (cs, delta) per token
+    dec = Bsz * H * nc * 4
+    pt = Bsz * T * H * 4                    # one fp32 value per token and head
+    part = nparts * Bsz * T * G * N * 4     # fp32 head-group partials of dB or dC
+    out = Bsz * T * G * N * 4               # dB or dC
+    units = Bsz * nc * H
+    tri = Q * (Q + 1) / 2
+    return {
+        "ssd_state_bf16_kernel": (x + bc + Bsz * T * H * 4 + st + dec + tok, units * 2 * Q * P * N),
+        "ssd_pass_bf16_kernel": (2 * st + dec, 0),
+        "ssd_adj_state_kernel": (x + bc + tok + st, units * 2 * Q * P * N),
+        "ssd_adj_pass_kernel": (2 * st + dec, 0),
+        # x, dy, B, C, tok, R in; dx, x.v, dy.x, f2, box shares, dB partials out
+        "ssd_bwd_dxdb_kernel": (3 * x + 2 * bc + tok + st + 3 * pt + pt * (nb + 1) / 2 + part,
+                                units * (2 * tri * P * 2 + 2 * tri * N + 2 * Q * N * P * 2)
+                                + Bsz * nc * G * 2 * tri * N),
+        # x, dy, B, C, tok, h_in in; f1, dC partials out
+        "ssd_bwd_dc_kernel": (2 * x + 2 * bc + tok + st + pt + part,
+                              units * (2 * tri * P + 2 * tri * N + 2 * Q * P * N)),
+        "ssd_bwd_const_kernel": (2 * st + dec, 0),
+        "ssd_bwd_dt_kernel": (Bsz * T * H * 4 + 5 * pt + pt * (nb + 1) / 2, 0),
+        "ssd_bwd_dt_sum_kernel": (Bsz * H * nc * 24 + H * 12, 0),
+        "ssd_bwd_reduce_kernel(dB)": (part + out, 0),
+        "ssd_bwd_reduce_kernel(dC)": (part + out, 0),
+        "whole_backward": (4 * x + 2 * bc + Bsz * T * H * 8 + 2 * out, 0),
+    }
+
+
+def bench_bwd(args, cfg):
+    """Backward workload: one step = one ssd_chunk_bwd call over the whole
+    batch (B2 T2048 H64 P64 N128, bf16 x/B/C/dy; the forward's chunk states
+    recomputed inside the call), the 512 MiB flush read between steps."""
+    import torch
+    import selective_state_space_09_amd as ssd
+    from selective_state_space_09_amd import inputs
+    inp = inputs.make_workload(args.workload, seed=0)
+    Q = cfg["chunk"]
+    dims = dict(inp["dims"], Q=Q)
+    Bsz, T, H, P, G, N = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N"))
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    d = {k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    f32 = dict(dtype=torch.float32, device=dev)
+    dx = torch.empty_like(d["x"])
+    ddt = torch.empty((Bsz, T, H), **f32)
+    dA, dD, dbias = (torch.empty(H, **f32) for _ in range(3))
+    dB = torch.empty((Bsz, T, G, N), **f32)
+    dC = torch.empty_like(dB)
+    nbytes = ssd.ssd_bwd_workspace_size(Bsz, T, H, P, G, N, Q)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    L = ssd.lib()
+    hip = Hip()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P_ = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["D"]),
+             P_(d["dt_bias"]), float(d["dt_min"]), float(d["dt_max"]), None, P_(d["dy"]), None,
+             P_(dx), P_(ddt), P_(dA), P_(dB), P_(dC), P_(dD), P_(dbias), None,
+             Bsz, T, H, P, G, N, Q, ssd.SSD_BF16, P_(ws), ws.numel(), sp)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(L.ssd_last_error().decode())
+
+    n_total = args.warmup + args.steps
+    step_evs = [(hip.event(), hip.event()) for _ in range(n_total)]
+    for i in range(n_total):
+        if flush is not None:
+            flush.max()
+        a, b = step_evs[i]
+        hip.lib.hipEventRecord(a, sp)
+        check(L.ssd_chunk_bwd(*fixed))
+        hip.lib.hipEventRecord(b, sp)
+    torch.cuda.synchronize()
+    per_step = [hip.elapsed_ms(*step_evs[i]) for i in range(args.warmup, n_total)]
+    n_kern = max(10, args.steps // 2)
+    evs = [[hip.event() for _ in range(22)] for _ in range(n_kern)]
+    for i in range(n_kern):
+        if flush is not None:
+            flush.max()
+        arr = (ctypes.c_void_p * 22)(*[e.value for e in evs[i]])
+        check(L.ssd_chunk_bwd_ev(*fixed, arr))
+    torch.cuda.synchronize()
+    nparts = (H // G) // max(k for k in range(1, min(4, H // G) + 1) if (H // G) % k == 0)
+    costs = bwd_kernel_costs(dims, nparts)
+    kern = {}
+    for k, name in enumerate(BWD_KERNELS):
+        avg = float(np.mean([hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in evs]))
+        nb_, fl = costs[name]
+        gbs = nb_ / (avg / 1e3) / 1e9
+        ent = {"avg_us": avg * 1e3, "alg_bytes": nb_, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        if fl:
+            tf = fl / (avg / 1e3) / 1e12
+            ent.update({"alg_flops": fl, "tflops": tf, "mfma_frac": tf / MFMA_PEAK_TFLOPS["bf16"]})
+        kern[name] = ent
+    ms = float(np.mean(per_step))
+    dom = max(kern, key=lambda n: kern[n]["avg_us"])
+    k = kern[dom]
+    traffic = measured_traffic(args.workload, dom)
+    if "mfma_frac" in k and k["mfma_frac"] > k["hbm_frac"]:
+        roof = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_PEAK_TFLOPS["bf16"],
+                "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": traffic, "kernel": dom}
+    else:
+        roof = {"bound": "hbm", "achieved": k["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": k["hbm_frac"], "traffic": traffic, "kernel": dom}
+    whole = costs["whole_backward"][0]
+    out = {
+        "metric": "SSD bwd tokens/s per layer (H64 P64 N128, bf16)", "value": Bsz * T / (ms / 1e3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": Bsz, "seq_len": T, "heads": H,
+                   "headdim": P, "d_state": N, "ngroups": G, "chunk": Q,
+                   "cache": "cold (Infinity Cache flushed between steps)"
+                   if flush is not None else "warm"},
+        "roofline": roof,
+        "whole_backward": {"alg_bytes": whole, "hbm_gbs": whole / (ms / 1e3) / 1e9,
+                           "hbm_frac": whole / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "kernels": kern,
+    }
+    if args.copy_ref:
+        copy_reference(torch, dev)
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        oracle.set_threads(threads)
+        reps, total = 0, 0.0
+        while total < args.cpu_seconds / 3:
+            t0 = time.perf_counter()
+            oracle.bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["dy"], inp["D"],
+                       inp["dt_bias"], inp["dt_min"], inp["dt_max"], None, None, want_dh0=False)
+            total += time.perf_counter() - t0
+            reps += 1
+        out["cpu_baseline"] = {
+            "value": reps * Bsz * T / total, "unit": "tokens/s", "cores": oracle.threads_used(),
+            "kind": "oracle",
+            "sample": f"the whole workload (float64 adjoint recurrence), {reps} passes in {total:.2f} s"}
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -324,10 +324,11 @@ int ssd_chunk_bwd(const void *x, const float *dt, const float *A, const void *B,
 
 /*
  * Measurement variant of ssd_chunk_bwd: identical arguments, kernels and
- * result, plus `events`, 20 hipEvent_t (passed as void*): a start/stop pair
- * bound to each of the 10 kernels' dispatches in order (chunk states, state
+ * result, plus `events`, 22 hipEvent_t (passed as void*): a start/stop pair
+ * bound to each of the 11 kernels' dispatches in order (chunk states, state
  * passing, adjoint chunk states, adjoint passing, dx/dB blocks, dC blocks,
- * chunk constants of da, step-size gradients, dB sum, dC sum), or NULL.
+ * chunk constants of da, step-size gradients per chunk, their sums per head,
+ * dB sum, dC sum), or NULL.
  */
 int ssd_chunk_bwd_ev(const void *x, const float *dt, const float *A, const void *B,
                      const void *C, const float *D, const float *dt_bias, float dt_min,

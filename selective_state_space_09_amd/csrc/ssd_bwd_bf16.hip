@@ -36,8 +36,10 @@
 //   ssd_bwd_dc          per (batch, chunk, 64-token row block l, head group):
 //                       dC summed over the group, f1 per head
 //   ssd_bwd_anchor      per (chunk, head, batch): e^{tot} <R_c, H_in>
-//   ssd_bwd_dt          per head: the prefix / suffix sums of f2 / f1 inside
-//                       each chunk (fp64), da, ddt, dA, ddt_bias, dD
+//   ssd_bwd_dt          per (chunk, head, batch): the prefix / suffix sums of
+//                       f2 / f1 inside the chunk (fp64), da, ddt, the chunk's
+//                       shares of dA, ddt_bias, dD
+//   ssd_bwd_dt_sum      dA, ddt_bias, dD: the sums of the shares
 //   ssd_bwd_reduce      sums of the head-group partials of dB and dC.
 // Every factor e^{cs_l - cs_s} (l >= s), e^{cs_l} and e^{tot - cs_s} is at
 // most 1 (A < 0), so each is evaluated directly per element.
@@ -690,79 +692,88 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_const_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Step-size gradients, one workgroup per head, batch entries and chunks in
-// turn (thread l = token l of the chunk):
+// Step-size gradients, one workgroup per (chunk, head, batch), thread l =
+// token l of the chunk:
 //   da_l = box_l + sum_{l' >= l} f1_l' + sum_{s < l} f2_s + e^{tot} <R_c, H_in>
 // (fp64 block scans: f1 summed from the chunk's end, f2 from its start), then
-// ddelta_l = A da_l + x_l.v_l, ddt_l = ddelta_l sigmoid(z_l) [lo <= sp <= hi],
-// and the per-head sums dA, ddt_bias, dD over the batch.
+// ddelta_l = A da_l + x_l.v_l, ddt_l = ddelta_l sigmoid(z_l) [lo <= sp <= hi];
+// the chunk's shares of dA, ddt_bias and dD go to `part` (fp64).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
     const float* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
     float dt_min, float dt_max, const float* __restrict__ f1, const float* __restrict__ f2,
     const float* __restrict__ boxp, const float* __restrict__ xv, const float* __restrict__ dyx,
-    const double* __restrict__ cst, float* __restrict__ ddt, float* __restrict__ dA,
-    float* __restrict__ ddt_bias, float* __restrict__ dD, int Bsz, int T, int H, int Q, int nc) {
+    const double* __restrict__ cst, float* __restrict__ ddt, double* __restrict__ part, int Bsz,
+    int T, int H, int Q, int nc) {
   __shared__ double wsum[4];
   __shared__ double red[3][4];
   __shared__ double sfx[kThreads];
-  const int h = blockIdx.x;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
   const float a_re = A[h];
   const float bias = dt_bias ? dt_bias[h] : 0.0f;
   const size_t BTH = static_cast<size_t>(Bsz) * T * H;
+  const size_t bhc = (static_cast<size_t>(b) * H + h) * nc + c;
+  const int t = c * Q + tid;
+  const bool in = tid < Q && t < T;
+  const size_t row = (static_cast<size_t>(b) * T + (in ? t : 0)) * H + h;
+  const double f1v = in ? static_cast<double>(f1[row]) : 0.0;
+  const double f2v = in ? static_cast<double>(f2[row]) : 0.0;
+  // f1 summed from the chunk's end: thread k scans token 255 - k
+  sfx[tid] = f1v;
+  __syncthreads();
+  const double rev = block_inclusive_scan(sfx[kThreads - 1 - tid], wsum);
+  __syncthreads();
+  sfx[kThreads - 1 - tid] = rev;
+  __syncthreads();
+  const double f1_suffix = sfx[tid];
+  const double f2_prefix = block_inclusive_scan(f2v, wsum) - f2v;
   double sA = 0.0, sBias = 0.0, sD = 0.0;
-  for (int b = 0; b < Bsz; ++b) {
-    for (int c = 0; c < nc; ++c) {
-      const int t = c * Q + tid;
-      const bool in = tid < Q && t < T;
-      const size_t row = (static_cast<size_t>(b) * T + (in ? t : 0)) * H + h;
-      const double f1v = in ? static_cast<double>(f1[row]) : 0.0;
-      const double f2v = in ? static_cast<double>(f2[row]) : 0.0;
-      // f1 summed from the chunk's end: thread k scans token 255 - k
-      sfx[tid] = f1v;
-      __syncthreads();
-      const double rev = block_inclusive_scan(sfx[kThreads - 1 - tid], wsum);
-      __syncthreads();
-      sfx[kThreads - 1 - tid] = rev;
-      __syncthreads();
-      const double f1_suffix = sfx[tid];
-      const double f2_prefix = block_inclusive_scan(f2v, wsum) - f2v;
-      __syncthreads();
-      if (in) {
-        double box = 0.0;
-        for (int jb = 0; jb <= tid / kBlk; ++jb) box += boxp[static_cast<size_t>(jb) * BTH + row];
-        const double da = box + f1_suffix + f2_prefix + cst[(static_cast<size_t>(b) * H + h) * nc + c];
-        const float z = dt[row] + bias;
-        const float d = step_size(dt[row], bias, dt_min, dt_max);
-        const float xvt = xv[row];
-        const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
-        const bool pass = sp >= dt_min && sp <= dt_max;
-        const double dd = static_cast<double>(a_re) * da + xvt;
-        const double gz = pass ? dd / (1.0 + exp(-static_cast<double>(z))) : 0.0;
-        ddt[row] = static_cast<float>(gz);
-        sA += static_cast<double>(d) * da;
-        sBias += gz;
-        sD += dyx[row];
-      }
-    }
+  if (in) {
+    double box = 0.0;
+    for (int jb = 0; jb <= tid / kBlk; ++jb) box += boxp[static_cast<size_t>(jb) * BTH + row];
+    const double da = box + f1_suffix + f2_prefix + cst[bhc];
+    const float z = dt[row] + bias;
+    const float d = step_size(dt[row], bias, dt_min, dt_max);
+    const float xvt = xv[row];
+    const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+    const bool pass = sp >= dt_min && sp <= dt_max;
+    const double dd = static_cast<double>(a_re) * da + xvt;
+    const double gz = pass ? dd / (1.0 + exp(-static_cast<double>(z))) : 0.0;
+    ddt[row] = static_cast<float>(gz);
+    sA = static_cast<double>(d) * da;
+    sBias = gz;
+    sD = dyx[row];
   }
   for (int o = 32; o > 0; o >>= 1) {
     sA += __shfl_xor(sA, o, kWave);
     sBias += __shfl_xor(sBias, o, kWave);
     sD += __shfl_xor(sD, o, kWave);
   }
+  __syncthreads();
   if (lane == 0) {
     red[0][wid] = sA;
     red[1][wid] = sBias;
     red[2][wid] = sD;
   }
   __syncthreads();
-  if (tid == 0) {
-    dA[h] = static_cast<float>(red[0][0] + red[0][1] + red[0][2] + red[0][3]);
-    ddt_bias[h] = static_cast<float>(red[1][0] + red[1][1] + red[1][2] + red[1][3]);
-    dD[h] = static_cast<float>(red[2][0] + red[2][1] + red[2][2] + red[2][3]);
-  }
+  if (tid < 3) part[bhc * 3 + tid] = red[tid][0] + red[tid][1] + red[tid][2] + red[tid][3];
+}
+
+// dA, ddt_bias, dD: per head, the sums of the chunk shares over batch and chunks
+__global__ __launch_bounds__(kThreads) void ssd_bwd_dt_sum_kernel(
+    const double* __restrict__ part, float* __restrict__ dA, float* __restrict__ ddt_bias,
+    float* __restrict__ dD, int Bsz, int H, int nc) {
+  const int h = blockIdx.x * kThreads + threadIdx.x;
+  if (h >= H) return;
+  double s[3] = {0.0, 0.0, 0.0};
+  for (int b = 0; b < Bsz; ++b)
+    for (int c = 0; c < nc; ++c)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) s[k] += part[(((static_cast<size_t>(b) * H + h) * nc + c) * 3) + k];
+  dA[h] = static_cast<float>(s[0]);
+  ddt_bias[h] = static_cast<float>(s[1]);
+  dD[h] = static_cast<float>(s[2]);
 }
 
 // dB (or dC) = sum of the nparts head-group partials, float4 at a time
@@ -783,10 +794,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_reduce_kernel(const float* _
   reinterpret_cast<float4*>(out)[i] = s;
 }
 
-// heads per workgroup of the block kernels: the largest divisor of H/G up to 16
+// heads per workgroup of the block kernels: the largest divisor of H/G up to
+// 4 (1024 workgroups per block kernel at the BitMamba shape; more heads per
+// workgroup share staging but leave too few workgroups to fill the CUs)
+constexpr int kMaxHeadsPerWG = 4;
 int bwd_heads_per_group(int H, int G) {
   const int hpg = H / G;
-  for (int d = hpg < 16 ? hpg : 16; d >= 1; --d)
+  for (int d = hpg < kMaxHeadsPerWG ? hpg : kMaxHeadsPerWG; d >= 1; --d)
     if (hpg % d == 0) return d;
   return 1;
 }
@@ -796,7 +810,7 @@ int bwd_heads_per_group(int H, int G) {
 // and head); the box shares of the column blocks (fp32, one per block); the
 // chunk constants of da (fp64); the dB and dC partials (fp32)
 struct BwdLayout {
-  size_t fwd, adj, f1, f2, xv, dyx, box, cst, dBp, dCp, total;
+  size_t fwd, adj, f1, f2, xv, dyx, box, cst, dtp, dBp, dCp, total;
 };
 static BwdLayout bwd_layout(int Bsz, int T, int H, int P, int G, int N, int chunk) {
   const int nc = (T + chunk - 1) / chunk;
@@ -821,6 +835,8 @@ static BwdLayout bwd_layout(int Bsz, int T, int H, int P, int G, int N, int chun
   o += up(tok * ((chunk + kBlk - 1) / kBlk));
   L.cst = o;
   o += up(static_cast<size_t>(Bsz) * H * nc * 8);
+  L.dtp = o;
+  o += up(static_cast<size_t>(Bsz) * H * nc * 3 * 8);
   const int nparts = (H / G) / bwd_heads_per_group(H, G);
   const size_t part = static_cast<size_t>(nparts) * Bsz * T * G * N * 4;
   L.dBp = o;
@@ -899,17 +915,22 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   launch_k(nc > 0, ssd_bwd_const_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
            ev ? ev + 12 : nullptr, static_cast<const uint16_t*>(adj), states, decay, cst, a.H, P * N,
            nc);
-  launch_k(true, ssd_bwd_dt_kernel, dim3(a.H), dim3(kThreads), st, ev ? ev + 14 : nullptr, a.dt, a.A,
-           a.dt_bias, a.dt_min, a.dt_max, static_cast<const float*>(f1), static_cast<const float*>(f2),
-           static_cast<const float*>(box), static_cast<const float*>(xv), static_cast<const float*>(dyx),
-           static_cast<const double*>(cst), a.ddt, a.dA, a.ddt_bias, a.dD, a.Bsz, a.T, a.H, Q, nc);
+  double* dtp = reinterpret_cast<double*>(ws + L.dtp);
+  launch_k(nc > 0, ssd_bwd_dt_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
+           ev ? ev + 14 : nullptr, a.dt, a.A, a.dt_bias, a.dt_min, a.dt_max, static_cast<const float*>(f1),
+           static_cast<const float*>(f2), static_cast<const float*>(box), static_cast<const float*>(xv),
+           static_cast<const float*>(dyx), static_cast<const double*>(cst), a.ddt, dtp, a.Bsz, a.T, a.H,
+           Q, nc);
+  launch_k(true, ssd_bwd_dt_sum_kernel, dim3((a.H + kThreads - 1) / kThreads), dim3(kThreads), st,
+           ev ? ev + 16 : nullptr, static_cast<const double*>(dtp), a.dA, a.ddt_bias, a.dD, a.Bsz, a.H,
+           nc);
   const size_t n4 = static_cast<size_t>(a.Bsz) * a.T * a.G * N / 4;
   const int nparts = (a.H / a.G) / HPG;
   const unsigned rblocks = static_cast<unsigned>((n4 + kThreads - 1) / kThreads);
   launch_k(n4 > 0, ssd_bwd_reduce_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(kThreads), st,
-           ev ? ev + 16 : nullptr, static_cast<const float*>(dBp), a.dB, n4, nparts);
+           ev ? ev + 18 : nullptr, static_cast<const float*>(dBp), a.dB, n4, nparts);
   launch_k(n4 > 0, ssd_bwd_reduce_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(kThreads), st,
-           ev ? ev + 18 : nullptr, static_cast<const float*>(dCp), a.dC, n4, nparts);
+           ev ? ev + 20 : nullptr, static_cast<const float*>(dCp), a.dC, n4, nparts);
   return hipGetLastError();
 }
 

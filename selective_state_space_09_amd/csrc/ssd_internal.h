@@ -75,7 +75,7 @@ struct BwdArgs {
   float* dh0;
   int Bsz, T, H, P, G, N, chunk;
   void* workspace;
-  hipEvent_t* events;  // NULL, or 20: start/stop of each of the 10 kernels
+  hipEvent_t* events;  // NULL, or 22: start/stop of each of the 11 kernels
 };
 
 // floats of chunk-boundary states: (Bsz, nc, H, P, KC), KC = N or 2N

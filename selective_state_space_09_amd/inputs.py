@@ -12,6 +12,9 @@ Large normal tensors are drawn directly in float32
 round-to-nearest-even encodings of those float32 values, so the oracle and the
 GPU read identical bits.
 
+The backward workload adds dy ~ N(0,1) (bfloat16), drawn from a second
+stream (seed + 1) after the forward inputs.
+
 Workloads (shapes of the BitMamba-1B Mamba-2 layer -- d_inner 4096, 64 heads,
 d_state 128 -- and of the Mamba-3-Lite layer -- 16 heads, head_dim 64, 64
 complex states):
@@ -38,6 +41,10 @@ WORKLOADS = {
     # complex decode at the Mamba-3-Lite head shape; 1024 sequences so that the
     # complex64 state (537 MB) exceeds the 256 MB Infinity Cache like the real one
     "decode_complex": dict(kind="complex_decode", Bsz=1024, H=16, P=64, N=64, G=16, steps=64),
+    # backward of the chunked scan at the BitMamba layer shape (gradient of a
+    # loss through y: seeded dy, no h0, no dh_final)
+    "bwd_bf16": dict(kind="bwd", Bsz=2, T=2048, H=64, P=64, N=128, G=1, chunk=256,
+                     dtype="bf16"),
     # depthwise causal conv (K = 4, SiLU) of the BitMamba layer over its x|B|C
     # channels (4096 + 128 + 128), read from the in_proj output row (width
     # 2*4096 + 2*128 + 64 = 8512: z, x, B, C, dt) and split into the scan's inputs
@@ -235,6 +242,14 @@ def make_workload(name, seed=0, **overrides):
         return make_complex_decode(seed=seed, **cfg)
     if kind == "conv":
         return make_conv(seed=seed, **cfg)
+    if kind == "bwd":
+        inp = make_real(seed=seed, **cfg)
+        rng = np.random.default_rng(seed + 1)
+        d = inp["dims"]
+        dy = _normal(rng, (d["Bsz"], d["T"], d["H"], d["P"]))
+        inp["dy"] = f32_to_bf16_bits(dy) if cfg.get("dtype") == "bf16" else dy
+        inp["kind"] = "bwd"
+        return inp
     if kind == "conv_decode":
         return make_conv_decode(seed=seed, **cfg)
     return make_decode(seed=seed, **cfg)

@@ -122,7 +122,7 @@ CASES = [
     (1, 327, 3, 64, 64, 1, 128, False, False, True, True),    # odd head count, 3 chunks
     (1, 17, 2, 64, 128, 1, 256, True, True, False, False),    # one short chunk, no D / bias
     (1, 1, 2, 32, 128, 1, 64, True, True, True, True),        # a single token
-    (1, 200, 32, 64, 128, 1, 256, True, True, True, True),    # 2 head groups of 16: partial sums
+    (1, 200, 32, 64, 128, 1, 256, True, True, True, True),    # 8 head groups of 4: partial sums
     (2, 513, 4, 32, 128, 4, 256, True, False, True, True),    # per-head groups, ragged third chunk
 ]
 
@@ -152,8 +152,8 @@ def test_bwd_empty_sequence():
 
 
 def test_bwd_workload_full():
-    """The benchmark's shape (B2 T2048 H64 P64 N128, chunk 256, four groups of
-    16 heads per B/C group), every gradient element."""
+    """The benchmark's shape (B2 T2048 H64 P64 N128, chunk 256, sixteen groups
+    of 4 heads per B/C group), every gradient element."""
     inp = inputs.make_workload("bitmamba_bf16", seed=0, with_h0=True)
     dy = _dy(inp, 7)
     dhf = _dhf(inp, 7)
