@@ -85,6 +85,17 @@ __device__ __forceinline__ void stage_rows(uint16_t* tile, int pitch, buf_t src,
   }
 }
 
+// writes rows held in registers (a BufSlab of the same shape) into an LDS tile
+template <int ROWS, int VPR>
+__device__ __forceinline__ void put_rows(uint16_t* tile, int pitch, const BufSlab<ROWS, VPR, kThreads>& q) {
+#pragma unroll
+  for (int i = 0; i < q.PER; ++i) {
+    const int it = static_cast<int>(threadIdx.x) + i * kThreads;
+    if (q.ITEMS % kThreads == 0 || it < q.ITEMS)
+      *reinterpret_cast<uint4*>(tile + (it / VPR) * pitch + (it % VPR) * 8) = q.v[i];
+  }
+}
+
 // row-wise sum over the 16 lanes of a lane group (lanes with the same i / 16)
 __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 1, kWave);
@@ -557,11 +568,19 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
 #pragma unroll
   for (int i = 0; i < NT; ++i) dCg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ll = l0 + 16 * w + r16;  // this lane's target token (A rows)
+  auto xbufh = [&](int hh) {
+    return make_buf(x + r0 * H * P + static_cast<size_t>(hh) * P,
+                    static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+  };
+  // the x and B rows of the next s block, loaded one block ahead (the last
+  // block of a head loads the first block of the next head)
+  BufSlab<kBlk, P / 8, kThreads> xq;
+  BufSlab<kBlk, N / 8, kThreads> bq;
+  xq.load(xbufh(h0), xrow, 0);
+  bq.load(bbuf, brow, 0);
 
   for (int e = 0; e < HPG; ++e) {
     const int h = h0 + e;
-    const buf_t xbuf = make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
-                                static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
     const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
                                 static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
     const buf_t hbuf = make_buf(states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
@@ -603,8 +622,15 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
     for (int sb = 0; sb <= ib; ++sb) {
       const int s0 = sb * kBlk;
       __syncthreads();
-      stage_rows<P / 8, kBlk>(Xs, XP, xbuf, xrow, s0);
-      stage_rows<N / 8, kBlk>(Bs, NP, bbuf, brow, s0);
+      put_rows(Xs, XP, xq);
+      put_rows(Bs, NP, bq);
+      if (sb < ib) {
+        xq.load(xbufh(h), xrow, s0 + kBlk);
+        bq.load(bbuf, brow, s0 + kBlk);
+      } else if (e + 1 < HPG) {
+        xq.load(xbufh(h + 1), xrow, 0);
+        bq.load(bbuf, brow, 0);
+      }
       __syncthreads();
       // transposed scores: lane holds l = ll, s = s0 + 16 st + 4q + i
       f32x4 st2[4];
