@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--workload", default="bitmamba_bf16",
                     choices=["bitmamba_bf16", "long_bf16", "mamba3lite_complex", "tiny_f32",
                              "decode_f32", "decode_complex", "conv_bf16", "conv_decode_f32",
-                             "bwd_bf16"])
+                             "bwd_bf16", "mamba3lite_packed"])
     ap.add_argument("--no-flush", action="store_true",
                     help="keep the Infinity Cache warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,6 +105,7 @@ KERNEL_SOURCES = {
     "conv_bf16": ["ssd_conv.hip"],
     "conv_decode_f32": ["ssd_conv.hip"],
     "bwd_bf16": ["ssd_bwd_bf16.hip", "ssd_chunk_bf16.hip"],
+    "mamba3lite_packed": ["ssd_chunk_cplx.hip"],
 }
 
 
@@ -152,7 +153,7 @@ def kernel_segments(cfg):
     if cfg["kind"] == "real" and cfg.get("dtype") == "bf16":
         return {"ssd_state_bf16_kernel": (0, 1), "ssd_pass_bf16_kernel": (2, 3),
                 "ssd_scan_bf16_kernel": (4, 5)}
-    if cfg["kind"] == "complex":
+    if cfg["kind"] in ("complex", "complex_packed"):
         return {"ssd_state_cplx_kernel": (0, 1), "ssd_pass_kernel": (2, 3),
                 "ssd_scan_cplx_kernel": (4, 5)}
     return {"ssd_state_kernel": (0, 1), "ssd_pass_kernel": (2, 3), "ssd_scan_kernel": (4, 5)}
@@ -162,7 +163,7 @@ def kernel_bytes(cfg, dims):
     """Algorithmic HBM bytes of each kernel of one chunked-forward call: every
     array the kernel must read or write, counted once."""
     Bsz, T, H, P, G, N, Q = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N", "Q"))
-    cplx = cfg["kind"] == "complex"
+    cplx = cfg["kind"] in ("complex", "complex_packed")
     es = 2 if cfg.get("dtype") == "bf16" else 4          # x element
     bs = 8 if cplx else es                                # B/C element
     KC = 2 * N if cplx else N
@@ -194,7 +195,7 @@ def kernel_flops(cfg, dims):
     """Algorithmic flops: lower-triangle intra-chunk products (C.B^T per head
     and M.X), chunk states and the C.h_in products."""
     Bsz, T, H, P, G, N, Q = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N", "Q"))
-    KC = 2 * N if cfg["kind"] == "complex" else N
+    KC = 2 * N if cfg["kind"] in ("complex", "complex_packed") else N
     units = Bsz * H * (T / Q)                   # (b, chunk, h) units
     tri = Q * (Q + 1) / 2
     scan = units * (2 * tri * KC + 2 * tri * P + 2 * Q * KC * P)
@@ -229,7 +230,7 @@ def cpu_baseline(inp, cfg, dims, target_s):
         for k in ("D", "dt_bias"):
             sub[k] = None if inp[k] is None else np.ascontiguousarray(inp[k][:nh])
         t0 = time.perf_counter()
-        if cfg["kind"] == "complex":
+        if cfg["kind"] in ("complex", "complex_packed"):
             oracle.complex_fwd(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"],
                                sub["dt_bias"], sub["dt_min"], sub["dt_max"], None)
         else:
@@ -239,7 +240,7 @@ def cpu_baseline(inp, cfg, dims, target_s):
 
     def run_full():
         t0 = time.perf_counter()
-        if cfg["kind"] == "complex":
+        if cfg["kind"] in ("complex", "complex_packed"):
             oracle.complex_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
                                inp["dt_bias"], inp["dt_min"], inp["dt_max"], None)
         else:
@@ -305,7 +306,8 @@ def main():
 
     d = {k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
     Bsz, T, H, P, G, N = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N"))
-    cplx = cfg["kind"] == "complex"
+    cplx = cfg["kind"] in ("complex", "complex_packed")
+    packed = cfg["kind"] == "complex_packed"
     y = torch.empty((Bsz, T, H, P), dtype=torch.float32 if cplx else d["x"].dtype, device=dev)
     nbytes = ssd.ssd_workspace_size(Bsz, T, H, P, G, N, Q, cplx)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -326,7 +328,16 @@ def main():
     evs = [[hip.event() for _ in range(6)] for _ in range(n_kern)]
     ev_arrays = [(ctypes.c_void_p * 6)(*[e.value for e in row]) for row in evs]
 
-    if cplx:
+    if packed:
+        # x, B, C, dt read in place from the in_proj rows (Bsz, T, H(P+4N+1))
+        proj = d["proj"]
+        fixed = (P_(proj), proj.shape[2], P_(d["A"]), P_(d["dt_bias"]), float(d["dt_min"]),
+                 float(d["dt_max"]), None, P_(y), None, Bsz, T, H, P, N, Q, P_(ws), ws.numel(), sp)
+        call = lambda evarr: L.ssd_complex_chunk_fwd_packed_ev(*fixed, evarr)
+        plain = lambda: L.ssd_complex_chunk_fwd_packed(*fixed)
+        dtype_name = "f32"
+        peak_name = "f32 as 3 bf16"
+    elif cplx:
         fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["dt_bias"]),
                  float(d["dt_min"]), float(d["dt_max"]), None, P_(y), None,
                  Bsz, T, H, P, G, N, Q, P_(ws), ws.numel(), sp)
@@ -413,7 +424,8 @@ def main():
         "dtype": dtype_name, "data": "synthetic",
         "config": {"workload": args.workload, "batch": Bsz, "seq_len": T, "heads": H,
                    "headdim": P, "d_state": N, "ngroups": G, "chunk": Q,
-                   "complex": cplx, "cache": "cold (Infinity Cache flushed between steps)"
+                   "complex": cplx, "inputs": "in_proj rows, read in place" if packed else
+                   "separate arrays", "cache": "cold (Infinity Cache flushed between steps)"
                    if flush is not None else "warm"},
         "roofline": roof,
         "whole_forward": {"alg_bytes": kb["whole_forward"], "hbm_gbs": whole_gbs,

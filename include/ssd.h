@@ -338,6 +338,35 @@ int ssd_chunk_bwd_ev(const void *x, const float *dt, const float *A, const void 
                      int chunk, int dtype, void *workspace, size_t workspace_bytes,
                      void *stream, void *const *events);
 
+/*
+ * ssd_complex_chunk_fwd reading its inputs in place from the rows of the
+ * Mamba-3-Lite in_proj output (block page, sections 4.1-4.2: one row of
+ * width H(D + 4N + 1) per token, head-major slices, float32 after the casts):
+ *   proj[b,t, 0 .. HP)             x      (head h at h*P, P = D)
+ *   proj[b,t, HP + h*N + n]        Re B   proj[b,t, HP + HN + h*N + n]   Im B
+ *   proj[b,t, HP + 2HN + h*N + n]  Re C   proj[b,t, HP + 3HN + h*N + n]  Im C
+ *   proj[b,t, HP + 4HN + h]        dt
+ * with HP = H*P, HN = H*N; per-head B and C (G = H).  Rows are `ld` floats
+ * apart (ld >= H(P + 4N + 1), a multiple of 4; any columns past the slices
+ * are not read); proj 16-byte aligned.  Nothing is copied: the kernels read
+ * the planar real and imaginary slices directly.  Everything else (A,
+ * dt_bias, clamp, h0, y, h_final, the workspace of
+ * ssd_workspace_size(..., is_complex = 1), errors) as ssd_complex_chunk_fwd.
+ */
+int ssd_complex_chunk_fwd_packed(const float *proj, long long ld, const float *A,
+                                 const float *dt_bias, float dt_min, float dt_max,
+                                 const float *h0, float *y, float *h_final, int Bsz, int T,
+                                 int H, int P, int N, int chunk, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* Measurement variant of ssd_complex_chunk_fwd_packed (6 events, as
+ * ssd_complex_chunk_fwd_ev). */
+int ssd_complex_chunk_fwd_packed_ev(const float *proj, long long ld, const float *A,
+                                    const float *dt_bias, float dt_min, float dt_max,
+                                    const float *h0, float *y, float *h_final, int Bsz, int T,
+                                    int H, int P, int N, int chunk, void *workspace,
+                                    size_t workspace_bytes, void *stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

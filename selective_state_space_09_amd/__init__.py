@@ -61,6 +61,10 @@ def lib():
     L.ssd_complex_step_decode_ev.restype = I
     L.ssd_complex_step_decode_ev.argtypes = L.ssd_complex_step_decode.argtypes + [P]
     LL = ctypes.c_longlong
+    L.ssd_complex_chunk_fwd_packed.restype = I
+    L.ssd_complex_chunk_fwd_packed.argtypes = [P, LL, P, P, F, F, P, P, P, I, I, I, I, I, I, P, S, P]
+    L.ssd_complex_chunk_fwd_packed_ev.restype = I
+    L.ssd_complex_chunk_fwd_packed_ev.argtypes = L.ssd_complex_chunk_fwd_packed.argtypes + [P]
     L.ssd_bwd_workspace_size.restype = S
     L.ssd_bwd_workspace_size.argtypes = [I] * 7
     L.ssd_chunk_bwd.restype = I
@@ -346,3 +350,36 @@ def ssd_chunk_bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=m
                                Bsz, T, H, P, G, N, chunk, SSD_BF16, _ptr(ws), ws.numel(),
                                _stream(stream)))
     return out
+
+
+def ssd_complex_chunk_fwd_packed(proj, A, H, P, N, dt_bias=None, dt_min=0.0, dt_max=math.inf,
+                                 h0=None, chunk=256, return_final_state=False, y=None,
+                                 workspace=None, stream=None):
+    """Complex chunked forward reading x, B, C and dt in place from the
+    in_proj output rows proj (Bsz, T, W) float32, W >= H*(P + 4N + 1): slices
+    [x | B_re | B_im | C_re | C_im | dt], head-major, per-head B/C.  proj may
+    be a column slice of wider rows (its row stride is passed).  Returns y
+    (Bsz,T,H,P) float32 (and h_final (Bsz,H,P,N,2) if return_final_state)."""
+    ld = _rows(proj, "proj", 3)
+    if proj.dtype != torch.float32:
+        raise TypeError("proj must be float32")
+    Bsz, T, W = proj.shape
+    if W < H * (P + 4 * N + 1):
+        raise ValueError(f"proj rows have {W} columns, need {H * (P + 4 * N + 1)}")
+    A = _pairs(A)
+    _dev(A, "A", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    h0 = _pairs(h0)
+    _dev(h0, "h0", torch.float32)
+    dev = proj.device
+    if y is None:
+        y = torch.empty((Bsz, T, H, P), dtype=torch.float32, device=dev)
+    _dev(y, "y", torch.float32)
+    hf = torch.empty((Bsz, H, P, N, 2), dtype=torch.float32, device=dev) if return_final_state else None
+    nbytes = ssd_workspace_size(Bsz, T, H, P, H, N, chunk, True)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().ssd_complex_chunk_fwd_packed(_ptr(proj), ld, _ptr(A), _ptr(dt_bias),
+                                              float(dt_min), float(dt_max), _ptr(h0), _ptr(y),
+                                              _ptr(hf), Bsz, T, H, P, N, chunk, _ptr(ws),
+                                              ws.numel(), _stream(stream)))
+    return (y, hf) if return_final_state else y

@@ -195,6 +195,46 @@ int ssd_complex_chunk_fwd(const float* x, const float* dt, const float* A, const
                                   nullptr);
 }
 
+int ssd_complex_chunk_fwd_packed_ev(const float* proj, long long ld, const float* A,
+                                    const float* dt_bias, float dt_min, float dt_max,
+                                    const float* h0, float* y, float* h_final, int Bsz, int T,
+                                    int H, int P, int N, int chunk, void* workspace,
+                                    size_t workspace_bytes, void* stream, void* const* events) {
+  SSD_TRY(check_chunk_shape(Bsz, T, H, P, H, N, chunk, 1));
+  const long long width = static_cast<long long>(H) * (P + 4LL * N + 1);
+  if (ld < width)
+    return fail(SSD_EINVAL, "ld=%lld is smaller than H*(P+4N+1) = %lld", ld, width);
+  if (ld % 4 != 0) return fail(SSD_EINVAL, "ld=%lld is not a multiple of 4 floats", ld);
+  if (static_cast<long long>(chunk) * ld * 4 > 4294967295LL - 16)
+    return fail(SSD_EUNSUPPORTED, "one chunk's rows exceed 4 GiB: chunk=%d ld=%lld", chunk, ld);
+  const bool has_tokens = T > 0;
+  SSD_TRY(check_ptr(proj, "proj", 16, has_tokens));
+  SSD_TRY(check_ptr(A, "A", 8, has_tokens));
+  SSD_TRY(check_ptr(y, "y", 16, has_tokens));
+  SSD_TRY(check_ptr(dt_bias, "dt_bias", 4, false));
+  SSD_TRY(check_ptr(h0, "h0", 16, false));
+  SSD_TRY(check_ptr(h_final, "h_final", 16, false));
+  SSD_TRY(check_clamp(dt_min, dt_max));
+  const size_t need = workspace_bytes_for(Bsz, T, H, P, N, chunk, 1);
+  SSD_TRY(check_ptr(workspace, "workspace", 256, true));
+  if (workspace_bytes < need)
+    return fail(SSD_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  ssd::ChunkArgs a{proj, nullptr, A, nullptr, nullptr, nullptr, dt_bias, dt_min, dt_max, h0, y,
+                   h_final, Bsz, T, H, P, H, N, chunk, SSD_F32, workspace,
+                   reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_chunk_complex_packed(a, static_cast<int>(ld),
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+int ssd_complex_chunk_fwd_packed(const float* proj, long long ld, const float* A,
+                                 const float* dt_bias, float dt_min, float dt_max, const float* h0,
+                                 float* y, float* h_final, int Bsz, int T, int H, int P, int N,
+                                 int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_complex_chunk_fwd_packed_ev(proj, ld, A, dt_bias, dt_min, dt_max, h0, y, h_final, Bsz,
+                                         T, H, P, N, chunk, workspace, workspace_bytes, stream,
+                                         nullptr);
+}
+
 int ssd_step_decode(float* h, const float* x, const float* dt, const float* A, const float* B,
                     const float* C, const float* D, const float* dt_bias, float dt_min,
                     float dt_max, float* y, int Bsz, int H, int P, int G, int N, void* stream) {

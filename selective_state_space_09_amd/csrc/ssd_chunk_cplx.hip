@@ -24,6 +24,20 @@
 
 namespace ssd {
 
+// Where a token row's inputs live.  Separate arrays: x (Bsz,T,H,P), B and C
+// (Bsz,T,G,N) of (re, im) pairs, dt (Bsz,T,H).  Packed (PACKED = true): one
+// row of the in_proj output per token, `ld` floats apart, head-major slices
+// [x | B_re | B_im | C_re | C_im | dt] of widths H*P, H*N (x4) and H (the
+// Mamba-3-Lite block page, section 4.2), G = H.
+struct CplxRows {
+  const float* x;   // x of token 0, head 0 (separate: x; packed: the row base)
+  const float* B;   // separate: B; packed: the B_re slice (B_im at +im_off)
+  const float* C;   // separate: C; packed: the C_re slice (C_im at +im_off)
+  const float* dt;  // separate: dt; packed: the dt slice
+  int ld;           // packed: floats between token rows
+  int im_off;       // packed: floats from a re slice to its im slice (H*N)
+};
+
 // ---------------------------------------------------------------------------
 // Chunk states from a zero start, one workgroup (8 waves) per (batch, chunk,
 // head):
@@ -42,12 +56,11 @@ namespace ssd {
 // pg*PTW + PTW-1 for pg = w / NKP, so that an accumulator lane holds both
 // parts of 4 consecutive n of one p for the final rotation.
 // ---------------------------------------------------------------------------
-template <int P, int N>
+template <int P, int N, bool PACKED>
 __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
-    const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
-    const float* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min, float dt_max,
-    float* __restrict__ states, float* __restrict__ decay, float4* __restrict__ tok, int T, int H,
-    int G, int Q, int nc, int npairs) {
+    CplxRows in, const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min,
+    float dt_max, float* __restrict__ states, float* __restrict__ decay, float4* __restrict__ tok,
+    int T, int H, int G, int Q, int nc, int npairs) {
   constexpr int NTHR = 512, WW = 8;
   constexpr int K = 2 * N;
   constexpr int HS = 64;                     // tokens per staged quarter
@@ -74,21 +87,30 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
 
   // ---- loads: dt first, then the first two quarters of x and B ----
   const size_t r0 = static_cast<size_t>(b) * T + t0;
-  const float dtv = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
-  const uint32_t xrow = static_cast<uint32_t>(H) * P * 4;
-  const uint32_t brow = static_cast<uint32_t>(G) * N * 8;
-  const buf_t xbuf = make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
+  const size_t drow = PACKED ? static_cast<size_t>(in.ld) : static_cast<size_t>(H);
+  const float dtv = tid < Lc ? in.dt[(r0 + tid) * drow + h] : 0.0f;
+  const uint32_t xrow = PACKED ? static_cast<uint32_t>(in.ld) * 4 : static_cast<uint32_t>(H) * P * 4;
+  const uint32_t brow = PACKED ? static_cast<uint32_t>(in.ld) * 4 : static_cast<uint32_t>(G) * N * 8;
+  const buf_t xbuf = make_buf(in.x + r0 * (xrow / 4) + static_cast<size_t>(h) * P,
                               static_cast<uint32_t>(Lc - 1) * xrow + P * 4);
-  const buf_t bbuf = make_buf(Bm + (r0 * G + g) * N * 2, static_cast<uint32_t>(Lc - 1) * brow + N * 8);
+  // separate: (re, im) pairs, 16 bytes = 2 complex; packed: the re slice (and
+  // the im slice in bbi), 16 bytes = 4 parts
+  const size_t bcol = PACKED ? static_cast<size_t>(g) * N : static_cast<size_t>(g) * N * 2;
+  const buf_t bbuf = make_buf(in.B + r0 * (brow / 4) + bcol,
+                              static_cast<uint32_t>(Lc - 1) * brow + N * (PACKED ? 4 : 8));
+  const buf_t bbi = make_buf(in.B + (PACKED ? in.im_off : 0) + r0 * (brow / 4) + bcol,
+                             static_cast<uint32_t>(Lc - 1) * brow + N * 4);
+  constexpr int BV = PACKED ? N / 4 : N / 2;  // 16-byte vectors per row (per part if packed)
   // two register slots: quarters 0 and 1 now, quarter i+2 once quarter i is staged
   BufSlab<HS, P / 4, NTHR> xs[2];
-  BufSlab<HS, N / 2, NTHR> bs[2];
+  BufSlab<HS, BV, NTHR> bs[2], bsi[PACKED ? 2 : 1];
   const int nq = (Q + HS - 1) / HS;  // quarters of the chunk
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     if (i < nq) {
       xs[i].load(xbuf, xrow, i * HS);
       bs[i].load(bbuf, brow, i * HS);
+      if constexpr (PACKED) bsi[i].load(bbi, brow, i * HS);
     }
   const float a_re = A[2 * h], a_im = A[2 * h + 1];
   const float bias = dt_bias ? dt_bias[h] : 0.0f;
@@ -126,7 +148,8 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
   __syncthreads();
 
   // quarter -> LDS: x scaled by w and split; B rotated by e^{-i theta}, split
-  auto stage = [&](const BufSlab<HS, P / 4, NTHR>& xs, const BufSlab<HS, N / 2, NTHR>& bs, int s0) {
+  auto stage = [&](const BufSlab<HS, P / 4, NTHR>& xs, const BufSlab<HS, BV, NTHR>& bs,
+                   const BufSlab<HS, BV, NTHR>& bsi, int s0) {
 #pragma unroll
     for (int i = 0; i < xs.PER; ++i) {
       const int it = tid + i * NTHR;
@@ -144,20 +167,40 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
 #pragma unroll
     for (int i = 0; i < bs.PER; ++i) {
       const int it = tid + i * NTHR;
-      const int v = it % (N / 2), sl = it / (N / 2);
+      const int v = it % BV, sl = it / BV;
       if (bs.ITEMS % NTHR == 0 || it < bs.ITEMS) {
         const int s = s0 + sl < Q ? s0 + sl : 0;
         const float co = cth[s], si = sth[s];
-        const uint4 r = bs.v[i];  // (re, im) of n = 2v, 2v+1
-        const float b0r = __uint_as_float(r.x), b0i = __uint_as_float(r.y);
-        const float b1r = __uint_as_float(r.z), b1i = __uint_as_float(r.w);
-        uint32_t rh, rl, ih, il;
-        split_bf16x2(b0r * co + b0i * si, b1r * co + b1i * si, rh, rl);  // B'_re
-        split_bf16x2(b0i * co - b0r * si, b1i * co - b1r * si, ih, il);  // B'_im
-        *reinterpret_cast<uint32_t*>(bh[0] + sl * BPn + 2 * v) = rh;
-        *reinterpret_cast<uint32_t*>(bh[1] + sl * BPn + 2 * v) = rl;
-        *reinterpret_cast<uint32_t*>(bh[0] + sl * BPn + N + 2 * v) = ih;
-        *reinterpret_cast<uint32_t*>(bh[1] + sl * BPn + N + 2 * v) = il;
+        if constexpr (PACKED) {
+          const uint4 r = bs.v[i], m = bsi.v[i];  // re and im of n = 4v .. 4v+3
+          const float br[4] = {__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
+                               __uint_as_float(r.w)};
+          const float bi[4] = {__uint_as_float(m.x), __uint_as_float(m.y), __uint_as_float(m.z),
+                               __uint_as_float(m.w)};
+          uint32_t rh[2], rl[2], ih[2], il[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            split_bf16x2(br[2 * k] * co + bi[2 * k] * si, br[2 * k + 1] * co + bi[2 * k + 1] * si,
+                         rh[k], rl[k]);  // B'_re
+            split_bf16x2(bi[2 * k] * co - br[2 * k] * si, bi[2 * k + 1] * co - br[2 * k + 1] * si,
+                         ih[k], il[k]);  // B'_im
+          }
+          *reinterpret_cast<uint2*>(bh[0] + sl * BPn + 4 * v) = make_uint2(rh[0], rh[1]);
+          *reinterpret_cast<uint2*>(bh[1] + sl * BPn + 4 * v) = make_uint2(rl[0], rl[1]);
+          *reinterpret_cast<uint2*>(bh[0] + sl * BPn + N + 4 * v) = make_uint2(ih[0], ih[1]);
+          *reinterpret_cast<uint2*>(bh[1] + sl * BPn + N + 4 * v) = make_uint2(il[0], il[1]);
+        } else {
+          const uint4 r = bs.v[i];  // (re, im) of n = 2v, 2v+1
+          const float b0r = __uint_as_float(r.x), b0i = __uint_as_float(r.y);
+          const float b1r = __uint_as_float(r.z), b1i = __uint_as_float(r.w);
+          uint32_t rh, rl, ih, il;
+          split_bf16x2(b0r * co + b0i * si, b1r * co + b1i * si, rh, rl);  // B'_re
+          split_bf16x2(b0i * co - b0r * si, b1i * co - b1r * si, ih, il);  // B'_im
+          *reinterpret_cast<uint32_t*>(bh[0] + sl * BPn + 2 * v) = rh;
+          *reinterpret_cast<uint32_t*>(bh[1] + sl * BPn + 2 * v) = rl;
+          *reinterpret_cast<uint32_t*>(bh[0] + sl * BPn + N + 2 * v) = ih;
+          *reinterpret_cast<uint32_t*>(bh[1] + sl * BPn + N + 2 * v) = il;
+        }
       }
     }
   };
@@ -205,10 +248,11 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
   for (int i = 0; i < 4; ++i)
     if (i < nq) {
       if (i > 0) __syncthreads();
-      stage(xs[i & 1], bs[i & 1], i * HS);
+      stage(xs[i & 1], bs[i & 1], bsi[PACKED ? (i & 1) : 0], i * HS);
       if (i + 2 < nq) {
         xs[i & 1].load(xbuf, xrow, (i + 2) * HS);
         bs[i & 1].load(bbuf, brow, (i + 2) * HS);
+        if constexpr (PACKED) bsi[i & 1].load(bbi, brow, (i + 2) * HS);
       }
       __syncthreads();
       mma(Q - i * HS < HS ? Q - i * HS : HS);
@@ -251,11 +295,10 @@ __global__ __launch_bounds__(512) void ssd_state_cplx_kernel(
 // tiles (C features in registers, loaded a sub-chunk ahead and rotated once
 // the angles are known); for the state update wave w owns k tiles w, w+4, ...
 // ---------------------------------------------------------------------------
-template <int P, int N>
+template <int P, int N, bool PACKED>
 __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
-    const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ Cm,
-    const float4* __restrict__ tok, const float* __restrict__ hin, float* __restrict__ y, int T,
-    int H, int G, int Q, int nc, int npairs) {
+    CplxRows in, const float4* __restrict__ tok, const float* __restrict__ hin,
+    float* __restrict__ y, int T, int H, int G, int Q, int nc, int npairs) {
   constexpr int K = 2 * N;              // real features
   // sub-chunk length: 64 tokens unless the hi / lo tiles then overflow LDS
   constexpr int QSM = (2 * 64 * (K + 8) + 4 * 64 * (P + 16) + 2 * P * (K + 8)) * 2 + 6 * 1024 <=
@@ -297,16 +340,22 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
   if (tid == 0) exact_flag = 0;
 
   // ---- buffer descriptors (rows >= Lc read as zero, stores there dropped) ----
-  const size_t xy0 = (static_cast<size_t>(b) * T + t0) * H * P + static_cast<size_t>(h) * P;
-  const uint32_t xrow = static_cast<uint32_t>(H) * P * 4;
-  const uint32_t xbytes = static_cast<uint32_t>(Lc - 1) * xrow + P * 4;
-  const buf_t xbuf = make_buf(x + xy0, xbytes);
-  const buf_t ybuf = make_buf(y + xy0, xbytes);
-  const size_t bc0 = ((static_cast<size_t>(b) * T + t0) * G + g) * N * 2;
-  const uint32_t brow = static_cast<uint32_t>(G) * N * 8;
-  const uint32_t bbytes = static_cast<uint32_t>(Lc - 1) * brow + N * 8;
-  const buf_t bbuf = make_buf(Bm + bc0, bbytes);
-  const buf_t cbuf = make_buf(Cm + bc0, bbytes);
+  const size_t r0 = static_cast<size_t>(b) * T + t0;
+  const size_t xy0 = r0 * H * P + static_cast<size_t>(h) * P;
+  const uint32_t yrow = static_cast<uint32_t>(H) * P * 4;
+  const uint32_t xrow = PACKED ? static_cast<uint32_t>(in.ld) * 4 : yrow;
+  const buf_t xbuf = make_buf(in.x + r0 * (xrow / 4) + static_cast<size_t>(h) * P,
+                              static_cast<uint32_t>(Lc - 1) * xrow + P * 4);
+  const buf_t ybuf = make_buf(y + xy0, static_cast<uint32_t>(Lc - 1) * yrow + P * 4);
+  // separate: (re, im) pairs; packed: the re slices (im slices in bbi, cbi)
+  const uint32_t brow = PACKED ? static_cast<uint32_t>(in.ld) * 4 : static_cast<uint32_t>(G) * N * 8;
+  const size_t bc0 = r0 * (brow / 4) + (PACKED ? static_cast<size_t>(g) * N : static_cast<size_t>(g) * N * 2);
+  const uint32_t bbytes = static_cast<uint32_t>(Lc - 1) * brow + N * (PACKED ? 4 : 8);
+  const buf_t bbuf = make_buf(in.B + bc0, bbytes);
+  const buf_t cbuf = make_buf(in.C + bc0, bbytes);
+  const buf_t bbi = make_buf(in.B + (PACKED ? in.im_off : 0) + bc0, bbytes);
+  const buf_t cbi = make_buf(in.C + (PACKED ? in.im_off : 0) + bc0, bbytes);
+  constexpr int BV = PACKED ? N / 4 : N / 2;  // 16-byte vectors per row (per part if packed)
   const buf_t hbuf = make_buf(hin + unit * (static_cast<size_t>(P) * K), P * K * 4);
 
   // ---- every load first: h_in tiles, C rows, x / B of sub-chunk 0 ----
@@ -318,22 +367,32 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
       hv[i][pt] = buf_load16(hbuf, ((pt * 16 + r16) * K + (wid + 4 * i) * 16 + 4 * q) * 4);
 
   // C row of this lane's output row in sub-chunk j: complex group cg holds
-  // n0 .. n0+7 with n0 = cg*32 + 8q (N >= 32) or 8q mod 16 (N = 16)
+  // n0 .. n0+7 with n0 = cg*32 + 8q (N >= 32) or 8q mod 16 (N = 16); as four
+  // (re, im) pair vectors (separate) or two re and two im vectors (packed)
   auto load_c = [&](uint4 (&cr)[NCG][4], int j) {
     const uint32_t row = j * QS + 16 * rb + r16;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const int n0 = N >= 32 ? cg * 32 + 8 * q : (8 * q) % 16;
+      if constexpr (PACKED) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) cr[cg][v] = buf_load16(cbuf, row * brow + (n0 + 2 * v) * 8);
+        for (int v = 0; v < 2; ++v) {
+          cr[cg][v] = buf_load16(cbuf, row * brow + (n0 + 4 * v) * 4);
+          cr[cg][2 + v] = buf_load16(cbi, row * brow + (n0 + 4 * v) * 4);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cr[cg][v] = buf_load16(cbuf, row * brow + (n0 + 2 * v) * 8);
+      }
     }
   };
   uint4 craw[NCG][4];
   load_c(craw, 0);
   BufSlab<QSM, P / 4> xs;
-  BufSlab<QSM, N / 2> bs;
+  BufSlab<QSM, BV> bs, bsi;
   xs.load(xbuf, xrow, 0);
   bs.load(bbuf, brow, 0);
+  if constexpr (PACKED) bsi.load(bbi, brow, 0);
 
   // ---- prologue: per-token values, per-sub-chunk factors ----
   if (tid < Q) {
@@ -387,17 +446,37 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
     const float co = cth[lrow], si = sth[lrow];
     float re[NCG][8], im[NCG][8];
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg)
+    for (int cg = 0; cg < NCG; ++cg) {
+      float a[8], bi[8];  // C re and im of n0 .. n0+7
+      if constexpr (PACKED) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint4 r = cr[cg][v];
-        const float a0 = __uint_as_float(r.x), b0 = __uint_as_float(r.y);
-        const float a1 = __uint_as_float(r.z), b1 = __uint_as_float(r.w);
-        re[cg][2 * v] = a0 * co - b0 * si;
-        im[cg][2 * v] = -(a0 * si + b0 * co);
-        re[cg][2 * v + 1] = a1 * co - b1 * si;
-        im[cg][2 * v + 1] = -(a1 * si + b1 * co);
+        for (int v = 0; v < 2; ++v) {
+          const uint4 r = cr[cg][v], m = cr[cg][2 + v];
+          a[4 * v] = __uint_as_float(r.x);
+          a[4 * v + 1] = __uint_as_float(r.y);
+          a[4 * v + 2] = __uint_as_float(r.z);
+          a[4 * v + 3] = __uint_as_float(r.w);
+          bi[4 * v] = __uint_as_float(m.x);
+          bi[4 * v + 1] = __uint_as_float(m.y);
+          bi[4 * v + 2] = __uint_as_float(m.z);
+          bi[4 * v + 3] = __uint_as_float(m.w);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 r = cr[cg][v];
+          a[2 * v] = __uint_as_float(r.x);
+          bi[2 * v] = __uint_as_float(r.y);
+          a[2 * v + 1] = __uint_as_float(r.z);
+          bi[2 * v + 1] = __uint_as_float(r.w);
+        }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        re[cg][e] = a[e] * co - bi[e] * si;
+        im[cg][e] = -(a[e] * si + bi[e] * co);
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int cg = N >= 32 ? ks % NCG : 0;
@@ -419,19 +498,39 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
     for (int i = 0; i < bs.PER; ++i) {
       const int it = tid + i * kThreads;
       if (bs.ITEMS % kThreads == 0 || it < bs.ITEMS) {
-        const int v = it % (N / 2), sl = it / (N / 2);
+        const int v = it % BV, sl = it / BV;
         const int s = j * QS + sl < Q ? j * QS + sl : 0;
         const float co = cth[s], si = sth[s];
-        const uint4 r = bs.v[i];
-        const float b0r = __uint_as_float(r.x), b0i = __uint_as_float(r.y);
-        const float b1r = __uint_as_float(r.z), b1i = __uint_as_float(r.w);
-        uint32_t rh, rl, ih, il;
-        split_bf16x2(b0r * co + b0i * si, b1r * co + b1i * si, rh, rl);
-        split_bf16x2(b0i * co - b0r * si, b1i * co - b1r * si, ih, il);
-        *reinterpret_cast<uint32_t*>(bt[0] + sl * BP + 2 * v) = rh;
-        *reinterpret_cast<uint32_t*>(bt[1] + sl * BP + 2 * v) = rl;
-        *reinterpret_cast<uint32_t*>(bt[0] + sl * BP + N + 2 * v) = ih;
-        *reinterpret_cast<uint32_t*>(bt[1] + sl * BP + N + 2 * v) = il;
+        if constexpr (PACKED) {
+          const uint4 r = bs.v[i], m = bsi.v[i];  // re and im of n = 4v .. 4v+3
+          const float br[4] = {__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
+                               __uint_as_float(r.w)};
+          const float bi[4] = {__uint_as_float(m.x), __uint_as_float(m.y), __uint_as_float(m.z),
+                               __uint_as_float(m.w)};
+          uint32_t rh[2], rl[2], ih[2], il[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            split_bf16x2(br[2 * k] * co + bi[2 * k] * si, br[2 * k + 1] * co + bi[2 * k + 1] * si,
+                         rh[k], rl[k]);
+            split_bf16x2(bi[2 * k] * co - br[2 * k] * si, bi[2 * k + 1] * co - br[2 * k + 1] * si,
+                         ih[k], il[k]);
+          }
+          *reinterpret_cast<uint2*>(bt[0] + sl * BP + 4 * v) = make_uint2(rh[0], rh[1]);
+          *reinterpret_cast<uint2*>(bt[1] + sl * BP + 4 * v) = make_uint2(rl[0], rl[1]);
+          *reinterpret_cast<uint2*>(bt[0] + sl * BP + N + 4 * v) = make_uint2(ih[0], ih[1]);
+          *reinterpret_cast<uint2*>(bt[1] + sl * BP + N + 4 * v) = make_uint2(il[0], il[1]);
+        } else {
+          const uint4 r = bs.v[i];
+          const float b0r = __uint_as_float(r.x), b0i = __uint_as_float(r.y);
+          const float b1r = __uint_as_float(r.z), b1i = __uint_as_float(r.w);
+          uint32_t rh, rl, ih, il;
+          split_bf16x2(b0r * co + b0i * si, b1r * co + b1i * si, rh, rl);
+          split_bf16x2(b0i * co - b0r * si, b1i * co - b1r * si, ih, il);
+          *reinterpret_cast<uint32_t*>(bt[0] + sl * BP + 2 * v) = rh;
+          *reinterpret_cast<uint32_t*>(bt[1] + sl * BP + 2 * v) = rl;
+          *reinterpret_cast<uint32_t*>(bt[0] + sl * BP + N + 2 * v) = ih;
+          *reinterpret_cast<uint32_t*>(bt[1] + sl * BP + N + 2 * v) = il;
+        }
       }
     }
 #pragma unroll
@@ -494,6 +593,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
     if (more) {
       xs.load(xbuf, xrow, sj + QS);
       bs.load(bbuf, brow, sj + QS);
+      if constexpr (PACKED) bsi.load(bbi, brow, sj + QS);
       load_c(craw, j + 1);
     }
 
@@ -585,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
         const int pt = ph * NPW + i;
         if (pt >= NPT) break;
         const f32x4 o = yacc[i] * s2;
-        buf_store16_nt(ybuf, static_cast<uint32_t>(lrow) * xrow + (pt * 16 + 4 * q) * 4,
+        buf_store16_nt(ybuf, static_cast<uint32_t>(lrow) * yrow + (pt * 16 + 4 * q) * 4,
                        __builtin_bit_cast(uint4, o));
       }
     }
@@ -634,8 +734,8 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <int P, int N>
-static hipError_t launch_cplx(const ChunkArgs& a, hipStream_t st) {
+template <int P, int N, bool PACKED>
+static hipError_t launch_cplx(const ChunkArgs& a, const CplxRows& in, hipStream_t st) {
   constexpr int K = 2 * N;
   const int nc = (a.T + a.chunk - 1) / a.chunk;
   const int npairs = a.Bsz * nc;
@@ -645,41 +745,55 @@ static hipError_t launch_cplx(const ChunkArgs& a, hipStream_t st) {
   float* states = static_cast<float*>(a.workspace);
   float* decay = states + workspace_state_floats(a.Bsz, nc, a.H, P, K);
   float4* tok = reinterpret_cast<float4*>(decay + (workspace_decay_floats(a.Bsz, nc, a.H) + 3) / 4 * 4);
-  const float* x = static_cast<const float*>(a.x);
-  const float* B = static_cast<const float*>(a.B);
-  const float* C = static_cast<const float*>(a.C);
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
   const hipEvent_t* ev = a.events;
-  launch_k(nc > 0, ssd_state_cplx_kernel<P, N>, dim3(blocks), dim3(512), st, ev, x, a.dt, a.A, B,
+  launch_k(nc > 0, ssd_state_cplx_kernel<P, N, PACKED>, dim3(blocks), dim3(512), st, ev, in, a.A,
            a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G, a.chunk, nc, npairs);
   launch_pass<true, N>(states, decay, a.h0, a.h_final, a.Bsz, a.H, P, nc, st, ev ? ev + 2 : nullptr);
-  launch_k(nc > 0, ssd_scan_cplx_kernel<P, N>, dim3(blocks), dim3(kThreads), st,
-           ev ? ev + 4 : nullptr, x, B, C, static_cast<const float4*>(tok),
+  launch_k(nc > 0, ssd_scan_cplx_kernel<P, N, PACKED>, dim3(blocks), dim3(kThreads), st,
+           ev ? ev + 4 : nullptr, in, static_cast<const float4*>(tok),
            static_cast<const float*>(states), static_cast<float*>(a.y), a.T, a.H, a.G, a.chunk, nc,
            npairs);
   return hipGetLastError();
 }
 
-template <int P>
-static hipError_t dispatch_cplx_n(const ChunkArgs& a, hipStream_t st) {
+template <int P, bool PACKED>
+static hipError_t dispatch_cplx_n(const ChunkArgs& a, const CplxRows& in, hipStream_t st) {
   switch (a.N) {
-    case 16: return launch_cplx<P, 16>(a, st);
-    case 32: return launch_cplx<P, 32>(a, st);
-    case 64: return launch_cplx<P, 64>(a, st);
+    case 16: return launch_cplx<P, 16, PACKED>(a, in, st);
+    case 32: return launch_cplx<P, 32, PACKED>(a, in, st);
+    case 64: return launch_cplx<P, 64, PACKED>(a, in, st);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool PACKED>
+static hipError_t dispatch_cplx(const ChunkArgs& a, const CplxRows& in, hipStream_t st) {
+  switch (a.P) {
+    case 16: return dispatch_cplx_n<16, PACKED>(a, in, st);
+    case 32: return dispatch_cplx_n<32, PACKED>(a, in, st);
+    case 64: return dispatch_cplx_n<64, PACKED>(a, in, st);
+    case 128: return dispatch_cplx_n<128, PACKED>(a, in, st);
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st) {
-  switch (a.P) {
-    case 16: return dispatch_cplx_n<16>(a, st);
-    case 32: return dispatch_cplx_n<32>(a, st);
-    case 64: return dispatch_cplx_n<64>(a, st);
-    case 128: return dispatch_cplx_n<128>(a, st);
-    default: break;
-  }
-  return hipErrorInvalidValue;
+  const CplxRows in{static_cast<const float*>(a.x), static_cast<const float*>(a.B),
+                    static_cast<const float*>(a.C), a.dt, 0, 0};
+  return dispatch_cplx<false>(a, in, st);
+}
+
+// Packed rows: a.x is the in_proj output (Bsz, T, ld) of head-major slices
+// [x | B_re | B_im | C_re | C_im | dt]; G = H.
+hipError_t run_chunk_complex_packed(const ChunkArgs& a, int ld, hipStream_t st) {
+  const float* base = static_cast<const float*>(a.x);
+  const size_t HP = static_cast<size_t>(a.H) * a.P, HN = static_cast<size_t>(a.H) * a.N;
+  const CplxRows in{base, base + HP, base + HP + 2 * HN, base + HP + 4 * HN, ld,
+                    static_cast<int>(HN)};
+  return dispatch_cplx<true>(a, in, st);
 }
 
 }  // namespace ssd

@@ -103,6 +103,8 @@ inline size_t workspace_cplx_token_floats(int Bsz, int nc, int H, int chunk) {
 hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
+// a.x = the in_proj rows (Bsz, T, ld): [x | B_re | B_im | C_re | C_im | dt], G = H
+hipError_t run_chunk_complex_packed(const ChunkArgs& a, int ld, hipStream_t st);
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t run_complex_decode(const DecodeArgs& a, hipStream_t st);  // D unused
 hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st);  // state + pass kernels only

@@ -41,6 +41,10 @@ WORKLOADS = {
     # complex decode at the Mamba-3-Lite head shape; 1024 sequences so that the
     # complex64 state (537 MB) exceeds the 256 MB Infinity Cache like the real one
     "decode_complex": dict(kind="complex_decode", Bsz=1024, H=16, P=64, N=64, G=16, steps=64),
+    # the Mamba-3-Lite layer read in place from its in_proj output rows (width
+    # H(D + 4N + 1) = 16 * 321 = 5136: x, B_re, B_im, C_re, C_im, dt)
+    "mamba3lite_packed": dict(kind="complex_packed", Bsz=8, T=2048, H=16, P=64, N=64,
+                              chunk=256),
     # backward of the chunked scan at the BitMamba layer shape (gradient of a
     # loss through y: seeded dy, no h0, no dh_final)
     "bwd_bf16": dict(kind="bwd", Bsz=2, T=2048, H=64, P=64, N=128, G=1, chunk=256,
@@ -141,6 +145,27 @@ def make_complex(Bsz, T, H, P, N, G=None, seed=0, with_h0=False, **_ignored):
                 dims=dict(Bsz=Bsz, T=T, H=H, P=P, G=G, N=N))
 
 
+def pack_complex_rows(inp, ld=None):
+    """The inputs of ``make_complex`` (per-head B/C) laid out as in_proj
+    output rows (Bsz, T, ld) float32: head-major slices x (H*P), B_re, B_im,
+    C_re, C_im (H*N each), dt (H); columns past them are zero.  Layout only."""
+    d = inp["dims"]
+    Bsz, T, H, P, N = d["Bsz"], d["T"], d["H"], d["P"], d["N"]
+    if d["G"] != H:
+        raise ValueError("packed rows carry per-head B and C (G = H)")
+    W = H * (P + 4 * N + 1)
+    ld = W if ld is None else ld
+    proj = np.zeros((Bsz, T, ld), np.float32)
+    HP, HN = H * P, H * N
+    proj[:, :, :HP] = inp["x"].reshape(Bsz, T, HP)
+    proj[:, :, HP:HP + HN] = inp["B"][..., 0].reshape(Bsz, T, HN)
+    proj[:, :, HP + HN:HP + 2 * HN] = inp["B"][..., 1].reshape(Bsz, T, HN)
+    proj[:, :, HP + 2 * HN:HP + 3 * HN] = inp["C"][..., 0].reshape(Bsz, T, HN)
+    proj[:, :, HP + 3 * HN:HP + 4 * HN] = inp["C"][..., 1].reshape(Bsz, T, HN)
+    proj[:, :, HP + 4 * HN:W] = inp["dt"]
+    return proj
+
+
 def make_decode(Bsz, H, P, N, G=1, steps=1, seed=0, **_ignored):
     """Inputs of the single-token decode workload.
 
@@ -238,6 +263,11 @@ def make_workload(name, seed=0, **overrides):
         return make_real(seed=seed, **cfg)
     if kind == "complex":
         return make_complex(seed=seed, **cfg)
+    if kind == "complex_packed":
+        inp = make_complex(seed=seed, **cfg)
+        inp["proj"] = pack_complex_rows(inp, cfg.get("ld"))
+        inp["kind"] = "complex_packed"
+        return inp
     if kind == "complex_decode":
         return make_complex_decode(seed=seed, **cfg)
     if kind == "conv":

@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ssd_chunk_fwd", "ssd_complex_chunk_fwd", "ssd_step_decode",
               "ssd_complex_step_decode", "ssd_workspace_size", "ssd_last_error",
-              "ssd_abi_version", "ssd_conv1d_fwd", "ssd_conv1d_step"):
+              "ssd_abi_version", "ssd_conv1d_fwd", "ssd_conv1d_step", "ssd_chunk_bwd",
+              "ssd_bwd_workspace_size", "ssd_complex_chunk_fwd_packed"):
         assert n in names
 
 
@@ -192,3 +193,22 @@ def test_python_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         ssd.ssd_chunk_fwd(x, torch.zeros(1, 4, 2), torch.zeros(2), torch.zeros(1, 4, 1, 16),
                           torch.zeros(1, 4, 1, 16))
+
+
+def test_complex_packed_rejects():
+    """Argument checks of the packed-row complex forward (H=2, P=16, N=16:
+    rows need H*(P+4N+1) = 162 floats)."""
+    L = ssd.lib()
+
+    def call(ld=164, proj=GOOD, H=2, P=16, N=16, chunk=64):
+        rc = L.ssd_complex_chunk_fwd_packed(proj, ld, GOOD, None, 0.0, 1.0, None, GOOD, None,
+                                            1, 64, H, P, N, chunk, GOOD, 1 << 30, None)
+        return rc, L.ssd_last_error().decode()
+    rc, msg = call(ld=160)
+    assert rc == ssd.SSD_EINVAL and "smaller" in msg
+    rc, msg = call(ld=162)
+    assert rc == ssd.SSD_EINVAL and "multiple of 4" in msg
+    rc, msg = call(proj=MISALIGNED)
+    assert rc == ssd.SSD_EINVAL and "proj is not 16-byte aligned" in msg
+    rc, msg = call(N=128)
+    assert rc == ssd.SSD_EUNSUPPORTED
