@@ -615,7 +615,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
         const float o1 = yacc[pt][1] * s2 + Dh * bf16_bits_to_f32(u.x >> 16);
         const float o2 = yacc[pt][2] * s2 + Dh * bf16_bits_to_f32(u.y & 0xFFFFu);
         const float o3 = yacc[pt][3] * s2 + Dh * bf16_bits_to_f32(u.y >> 16);
-        buf_store8_nt(ybuf, static_cast<uint32_t>(lrow) * xrow + (pt * 16 + 4 * q) * 2,
+        buf_store8(ybuf, static_cast<uint32_t>(lrow) * xrow + (pt * 16 + 4 * q) * 2,
                    make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)));
       }
     }

@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
         const int pt = ph * NPW + i;
         if (pt >= NPT) break;
         const f32x4 o = yacc[i] * s2;
-        buf_store16_nt(ybuf, static_cast<uint32_t>(lrow) * yrow + (pt * 16 + 4 * q) * 4,
+        buf_store16(ybuf, static_cast<uint32_t>(lrow) * yrow + (pt * 16 + 4 * q) * 4,
                        __builtin_bit_cast(uint4, o));
       }
     }
