@@ -348,7 +348,7 @@ int ssd_conv1d_fwd_ev(const void* xbc, long long ld, const float* w, const float
   if (T < 0) return fail(SSD_EINVAL, "T=%d is negative", T);
   SSD_TRY(check_conv_common(Bsz, HP, GN, ld, K, act, V));
   // one batch entry's rows (and a run of tokens past T) are addressed by
-  // 32-bit byte offsets; runs of 4 x 16 tokens fill grid.y
+  // 32-bit byte offsets; blocks of 4 runs of tokens fill grid.y
   const int tt = ssd::conv_tokens_per_thread();
   if ((static_cast<long long>(T) + tt) * ld * es > 4294967295LL - 16)
     return fail(SSD_EUNSUPPORTED, "one batch entry's rows exceed 4 GiB: T=%d ld=%lld", T, ld);

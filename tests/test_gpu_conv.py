@@ -62,14 +62,14 @@ def _run_gpu(d, act, ld_view=None):
 
 CASES = [
     # Bsz, T, HP, GN, ld, dtype, act, with_state, with_bias
-    (2, 40, 32, 8, 48, "bf16", 1, True, True),       # ragged T: 3 runs of 16
+    (2, 44, 32, 8, 48, "bf16", 1, True, True),       # ragged T: 6 runs of 8, the last short
     (1, 1, 8, 8, 24, "f32", 0, True, False),          # one token, window from the state
     (3, 2, 16, 0, 16, "f32", 1, True, True),          # no B/C channels, T < 3
     (1, 3, 16, 8, 32, "bf16", 1, True, True),         # T = 3
     (2, 200, 96, 16, 136, "bf16", 1, False, True),    # fresh sequence, ld > Ch
     (1, 70, 512, 64, 704, "bf16", 1, True, True),     # 80 vectors: 2 channel blocks, ragged
-    (2, 65, 512, 64, 640, "f32", 1, True, True),      # 160 vectors: 3 blocks; 5 runs
-    (1, 257, 64, 32, 128, "f32", 0, True, True),      # runs across 5 workgroups, no SiLU
+    (2, 65, 512, 64, 640, "f32", 1, True, True),      # 160 vectors: 3 blocks; 9 runs
+    (1, 257, 64, 32, 128, "f32", 0, True, True),      # 33 runs over 9 workgroups, no SiLU
 ]
 
 
