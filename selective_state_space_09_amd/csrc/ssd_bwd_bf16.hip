@@ -35,7 +35,7 @@
 //                       the box, and dB summed over the group
 //   ssd_bwd_dc          per (batch, chunk, 64-token row block l, head group):
 //                       dC summed over the group, f1 per head
-//   ssd_bwd_anchor      per (chunk, head, batch): e^{tot} <R_c, H_in>
+//   ssd_bwd_const       per (chunk, head, batch): e^{tot} <R_c, H_in>
 //   ssd_bwd_dt          per (chunk, head, batch): the prefix / suffix sums of
 //                       f2 / f1 inside the chunk (fp64), da, ddt, the chunk's
 //                       shares of dA, ddt_bias, dD
@@ -834,7 +834,8 @@ int bwd_heads_per_group(int H, int G) {
 // workspace layout of the backward, after the forward's own (states, decays,
 // token table): the adjoint states (bf16); f1, f2, x.v, dy.x (fp32 per token
 // and head); the box shares of the column blocks (fp32, one per block); the
-// chunk constants of da (fp64); the dB and dC partials (fp32)
+// chunk constants of da and the chunk shares of dA, ddt_bias, dD (fp64); the
+// dB and dC partials (fp32)
 struct BwdLayout {
   size_t fwd, adj, f1, f2, xv, dyx, box, cst, dtp, dBp, dCp, total;
 };

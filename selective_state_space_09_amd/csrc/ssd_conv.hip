@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void ssd_conv1d_kernel(
   // a block whose vectors all lie in x issues one store per token; the block
   // holding the x|B|C boundary issues three, each lane's offset in range for
   // one of them
-  const bool all_x = (blockIdx.x + 1) * kWave * V <= HP;
+  const bool all_x = static_cast<int>(blockIdx.x + 1) * kWave * V <= HP;
   const bool in_x = active && c0 < HP;
   const bool in_b = active && c0 >= HP && c0 < HP + GN;
   const bool in_c = active && c0 >= HP + GN;
