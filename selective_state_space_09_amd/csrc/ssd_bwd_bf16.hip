@@ -96,13 +96,36 @@ __device__ __forceinline__ void put_rows(uint16_t* tile, int pitch, const BufSla
   }
 }
 
-// row-wise sum over the 16 lanes of a lane group (lanes with the same i / 16)
+// lane move by a DPP row shift; lanes whose source lies outside their row of
+// 16 read zero, so that v + shr<n>(v) folds into one v_add_f32_dpp
+template <int CTRL>
+__device__ __forceinline__ float shr0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// sum over the 16 lanes of a lane group (lanes with the same i / 16), left in
+// the group's last lane (r16 = 15): an inclusive scan by DPP row shifts, four
+// VALU adds (cross-lane shuffles go through the LDS crossbar and cost far more)
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, kWave);
-  v += __shfl_xor(v, 2, kWave);
-  v += __shfl_xor(v, 4, kWave);
-  v += __shfl_xor(v, 8, kWave);
+  v += shr0<0x111>(v);  // row_shr:1
+  v += shr0<0x112>(v);  // row_shr:2
+  v += shr0<0x114>(v);  // row_shr:4
+  v += shr0<0x118>(v);  // row_shr:8
   return v;
+}
+
+// Per column r16, the values a_k of the four lane groups k (rows of 16 lanes):
+// the sum over the groups after this lane's group q and the sum over all four.
+// The gfx950 row swaps exchange rows 2m <-> 2m+1 (permlane16) and the wave's
+// halves (permlane32); each returns the even (first) and odd (second) side.
+__device__ __forceinline__ void group_suffix(float a, int q, float& after, float& total) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  const float ev = __uint_as_float(p[0]), od = __uint_as_float(p[1]);  // a_{q&~1}, a_{q|1}
+  const float pair = ev + od;
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+  const float lo = __uint_as_float(h[0]), hi = __uint_as_float(h[1]);  // groups 0+1, groups 2+3
+  after = ((q & 1) ? 0.0f : od) + (q < 2 ? hi : 0.0f);
+  total = lo + hi;
 }
 
 }  // namespace
@@ -288,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kBlk * XP];  // x rows of the s block
   __shared__ __attribute__((aligned(16))) uint16_t Rs[P * NP];     // R_c of the head
   __shared__ float2 tk[256];
-  __shared__ float boxs[4][kBlk];  // per wave: box share of each row of the l block
+  __shared__ float boxs[2][4][kBlk];  // per l-block parity and wave: box share of each row
 
   const int nb = (Q + kBlk - 1) / kBlk;
   const int hpg = H / G;
@@ -357,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) part += bf16_bits_to_f32(Xs[sr * XP + pt * 16 + r16]) * v[pt][i];
       part = sum16(part);
-      if (r16 == 0 && s0 + sr < Lc) f2o[(r0 + s0 + sr) * H + h] = tk[s0 + sr].y * part;
+      if (r16 == 15 && s0 + sr < Lc) f2o[(r0 + s0 + sr) * H + h] = tk[s0 + sr].y * part;
     }
     // boundary part of dB: delta_s e^{tot-cs_s} x_s R (A rows s = this lane's sl)
     {
@@ -375,9 +398,18 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     }
 
     float car = 0.0f;  // sum over the later l blocks of this column's box terms
+    // the four waves' box shares of l block lb, summed into the block's partial
+    // (once every wave has written boxs[lb & 1], i.e. after the next barrier)
+    auto flush_box = [&](int lb) {
+      const int l0 = s0 + lb * kBlk;
+      const float(*bx)[kBlk] = boxs[lb & 1];
+      if (tid < kBlk && l0 + tid < Lc)
+        boxp[static_cast<size_t>(j) * BTH + (r0 + l0 + tid) * H + h] = bx[0][tid] + bx[1][tid] + bx[2][tid] + bx[3][tid];
+    };
     for (int lb = nlb - 1; lb >= 0; --lb) {
       const int l0 = s0 + lb * kBlk;
       __syncthreads();
+      if (lb + 1 < nlb) flush_box(lb + 1);
       stage_rows<N / 8, kBlk>(Cs, NP, cbuf, brow, l0);
       stage_rows<P / 8, kBlk>(Ys, XP, ybuf, xrow, l0);
       __syncthreads();
@@ -448,12 +480,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
         ee[lt][2] += ee[lt][3];
         ee[lt][1] += ee[lt][2];
         ee[lt][0] += ee[lt][1];
-        const float g0 = __shfl(ee[lt][0], r16, kWave), g1 = __shfl(ee[lt][0], r16 + 16, kWave);
-        const float g2 = __shfl(ee[lt][0], r16 + 32, kWave), g3 = __shfl(ee[lt][0], r16 + 48, kWave);
-        const float after = (q < 1 ? g1 : 0.0f) + (q < 2 ? g2 : 0.0f) + (q < 3 ? g3 : 0.0f);
+        float after;
+        group_suffix(ee[lt][0], q, after, tt[lt]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ee[lt][i] += after;
-        tt[lt] = g0 + g1 + g2 + g3;
       }
       {
         float later = car;
@@ -471,13 +501,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * lt + 4 * q + i;
           const float part = sum16(sl < l0 + row ? ee[lt][i] : 0.0f);
-          if (r16 == 0) boxs[w][row] = part;
+          if (r16 == 15) boxs[lb & 1][w][row] = part;
         }
-      __syncthreads();
-      if (tid < kBlk && l0 + tid < Lc)
-        boxp[static_cast<size_t>(j) * BTH + (r0 + l0 + tid) * H + h] =
-            boxs[0][tid] + boxs[1][tid] + boxs[2][tid] + boxs[3][tid];
     }
+    __syncthreads();
+    flush_box(0);
 
     // outputs of head h: lane holds p = 16 pt + r16 of rows s = s0 + 16w + 4q + i;
     // Ys now holds the dy rows of the s block (the last l block was the diagonal)
@@ -503,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
       }
       pxv = sum16(pxv);
       pdx = sum16(pdx);
-      if (r16 == 0 && s0 + sr < Lc) {
+      if (r16 == 15 && s0 + sr < Lc) {
         xv[(r0 + s0 + sr) * H + h] = pxv;
         dyx[(r0 + s0 + sr) * H + h] = pdx;
       }
@@ -617,7 +645,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) pd += bf16_bits_to_f32(Cs[lr * NP + nt * 16 + r16]) * dC[nt][i];
       pd = sum16(pd);
-      if (r16 == 0 && l0 + lr < Lc) f1o[(r0 + l0 + lr) * H + h] = pd;
+      if (r16 == 15 && l0 + lr < Lc) f1o[(r0 + l0 + lr) * H + h] = pd;
     }
     for (int sb = 0; sb <= ib; ++sb) {
       const int s0 = sb * kBlk;
