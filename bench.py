@@ -653,15 +653,15 @@ def bwd_kernel_costs(dims, nparts):
         "ssd_pass_bf16_kernel": (2 * st + dec, 0),
         "ssd_adj_state_kernel": (x + bc + tok + st, units * 2 * Q * P * N),
         "ssd_adj_pass_kernel": (2 * st + dec, 0),
-        # x, dy, B, C, tok, R in; dx, x.v, dy.x, f2, box shares, dB partials out
-        "ssd_bwd_dxdb_kernel": (3 * x + 2 * bc + tok + st + 3 * pt + pt * (nb + 1) / 2 + part,
+        # x, dy, B, C, tok, R in; dx, x.v, dy.x, f2, col, row shares, dB partials out
+        "ssd_bwd_dxdb_kernel": (3 * x + 2 * bc + tok + st + 4 * pt + pt * (nb + 1) / 2 + part,
                                 units * (2 * tri * P * 2 + 2 * tri * N + 2 * Q * N * P * 2)
                                 + Bsz * nc * G * 2 * tri * N),
         # x, dy, B, C, tok, h_in in; f1, dC partials out
         "ssd_bwd_dc_kernel": (2 * x + 2 * bc + tok + st + pt + part,
                               units * (2 * tri * P + 2 * tri * N + 2 * Q * P * N)),
         "ssd_bwd_const_kernel": (2 * st + dec, 0),
-        "ssd_bwd_dt_kernel": (Bsz * T * H * 4 + 5 * pt + pt * (nb + 1) / 2, 0),
+        "ssd_bwd_dt_kernel": (Bsz * T * H * 4 + 6 * pt + pt * (nb + 1) / 2, 0),
         "ssd_bwd_dt_sum_kernel": (Bsz * H * nc * 24 + H * 12, 0),
         "ssd_bwd_reduce_kernel(dB)": (part + out, 0),
         "ssd_bwd_reduce_kernel(dC)": (part + out, 0),

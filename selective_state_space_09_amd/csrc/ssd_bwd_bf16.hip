@@ -21,23 +21,29 @@
 // with da_t = <dh_t, e^{A delta_t} h_{t-1}> the gradient of the step's
 // log-decay, taken apart inside the chunk into terms that each decay away
 // from t (so that none of them is a long sum of terms that cancel):
-//   da_t = sum_{s < t <= l} e^{cs_l-cs_s} delta_s (C_l.B_s)(dy_l.x_s)      (box)
+//   da_t = sum_{s < t <= l} E[l][s]                                       (box)
 //        + sum_{l >= t} e^{cs_l} C_l . (H_in^T dy_l)                      (f1)
 //        + sum_{s < t} e^{tot-cs_s} delta_s x_s . (R_c B_s)               (f2)
-//        + e^{tot} <R_c, H_in>.
+//        + e^{tot} <R_c, H_in>,
+// E[l][s] = e^{cs_l-cs_s} delta_s (C_l.B_s)(dy_l.x_s).  Stepping t by one
+// moves column t into the box and row t out of it, so that
+//   box_t = sum_{u < t} (col_u - row_u),  col_u = sum_{l > u} E[l][u],
+//   row_u = sum_{s < u} E[u][s]
+// (strictly below the diagonal; each of col_u, row_u and their difference
+// is made of the terms next to the diagonal, so the scan stays well scaled).
 // The pieces:
 //   forward recompute   chunk states, boundary states h_in(c) and the
 //                       per-token (cs, delta) table (the forward's kernels)
 //   ssd_adj_state       G_c per (batch, chunk, head), MFMA over tokens
 //   ssd_adj_pass        R_c in place over G_c, dh0
 //   ssd_bwd_dxdb        per (batch, chunk, 64-token column block s, head
-//                       group): v, dx, x.v, dy.x, f2, the block's share of
-//                       the box, and dB summed over the group
+//                       group): v, dx, x.v, dy.x, f2, col, the block's
+//                       share of row, and dB summed over the group
 //   ssd_bwd_dc          per (batch, chunk, 64-token row block l, head group):
 //                       dC summed over the group, f1 per head
 //   ssd_bwd_const       per (chunk, head, batch): e^{tot} <R_c, H_in>
 //   ssd_bwd_dt          per (chunk, head, batch): the prefix / suffix sums of
-//                       f2 / f1 inside the chunk (fp64), da, ddt, the chunk's
+//                       col - row, f2 / f1 inside the chunk (fp64), da, ddt, the chunk's
 //                       shares of dA, ddt_bias, dD
 //   ssd_bwd_dt_sum      dA, ddt_bias, dD: the sums of the shares
 //   ssd_bwd_reduce      sums of the head-group partials of dB and dC.
@@ -51,6 +57,7 @@ namespace ssd {
 namespace {
 
 constexpr int kBlk = 64;  // tokens per row / column block
+constexpr float kLog2e = 1.4426950408889634f;
 
 // 16-byte LDS row read (8 bf16): an MFMA A or B operand whose k runs along a row
 __device__ __forceinline__ uint4 lds_row8(const uint16_t* tile, int pitch, int row, int col) {
@@ -114,18 +121,40 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-// Per column r16, the values a_k of the four lane groups k (rows of 16 lanes):
-// the sum over the groups after this lane's group q and the sum over all four.
-// The gfx950 row swaps exchange rows 2m <-> 2m+1 (permlane16) and the wave's
-// halves (permlane32); each returns the even (first) and odd (second) side.
-__device__ __forceinline__ void group_suffix(float a, int q, float& after, float& total) {
+// Per column r16, the sum of the values of the four lane groups (rows of 16
+// lanes), in every lane.  The gfx950 row swaps exchange rows 2m <-> 2m+1
+// (permlane16) and the wave's halves (permlane32); each returns the even
+// (first) and the odd (second) side.
+__device__ __forceinline__ float group_total(float a) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  const float ev = __uint_as_float(p[0]), od = __uint_as_float(p[1]);  // a_{q&~1}, a_{q|1}
-  const float pair = ev + od;
+  const float pair = __uint_as_float(p[0]) + __uint_as_float(p[1]);
   const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
-  const float lo = __uint_as_float(h[0]), hi = __uint_as_float(h[1]);  // groups 0+1, groups 2+3
-  after = ((q & 1) ? 0.0f : od) + (q < 2 ? hi : 0.0f);
-  total = lo + hi;
+  return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
+// lane permutation inside rows of 16 by DPP (every source lane valid)
+template <int CTRL>
+__device__ __forceinline__ float dperm(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sixteen values per lane, summed over the 16 lanes of each lane group: lane
+// r16 returns the sum of value k = r16.  Butterfly over the partners r ^ 8,
+// r ^ 4, r ^ 2, r ^ 1 (row_ror:8; quad_perm [3,2,1,0] then row_half_mirror;
+// quad_perm [2,3,0,1]; quad_perm [1,0,3,2]): at each step a lane keeps the
+// half of its values whose index bit equals its own lane bit and adds the
+// partner's copy of that half.
+__device__ __forceinline__ float transpose_sum16(const float (&v)[16]) {
+  const int r = threadIdx.x & 15;
+  float a[8], c[4], e[2];
+  const bool b3 = r & 8, b2 = r & 4, b1 = r & 2, b0 = r & 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = (b3 ? v[k + 8] : v[k]) + dperm<0x128>(b3 ? v[k] : v[k + 8]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = (b2 ? a[k + 4] : a[k]) + dperm<0x141>(dperm<0x1B>(b2 ? a[k] : a[k + 4]));
+#pragma unroll
+  for (int k = 0; k < 2; ++k) e[k] = (b1 ? c[k + 2] : c[k]) + dperm<0x4E>(b1 ? c[k] : c[k + 2]);
+  return (b0 ? e[1] : e[0]) + dperm<0xB1>(b0 ? e[0] : e[1]);
 }
 
 }  // namespace
@@ -290,19 +319,20 @@ __device__ __forceinline__ bool block_unit(int ngroups, int nc, int nb, int Bsz,
 // and dy_l.x_s are MFMA tiles whose lane holds one s and four l, which after
 // the mask and decay are the A operands (rows s, contraction over l) of the
 // products with dy and C, read from LDS by the transpose read.  The same
-// fp32 tiles give the box terms ee[l][s] = e^{cs_l-cs_s} delta_s (C_l.B_s)
-// (dy_l.x_s): a suffix scan down each column (lanes, lane groups, then the
-// later l blocks) and a masked sum over the block's columns s < t give the
-// block's share of box_t for every t.  Per head: dx (bf16), x.v, dy.x, f2 and
-// the box shares; after the group: dB.
+// fp32 tiles give the box terms E[l][s] (l > s): each lane sums its column
+// over the l blocks (col_s, once per head), and a transposing reduction over
+// the 16 columns of each lane group gives the rows' sums (the block's share of
+// row_l).  Blocks off the diagonal and inside the chunk need no mask.  Per
+// head: dx (bf16), x.v, dy.x, f2, col and the row shares; after the group: dB.
 // ---------------------------------------------------------------------------
 template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dy, const float* __restrict__ D, const float2* __restrict__ tok,
     const uint16_t* __restrict__ adj, uint16_t* __restrict__ dx, float* __restrict__ xv,
-    float* __restrict__ dyx, float* __restrict__ f2o, float* __restrict__ boxp,
-    float* __restrict__ dBp, int Bsz, int T, int H, int G, int Q, int nc, int HPG) {
+    float* __restrict__ dyx, float* __restrict__ f2o, float* __restrict__ colp,
+    float* __restrict__ rowp, float* __restrict__ dBp, int Bsz, int T, int H, int G, int Q, int nc,
+    int HPG) {
   constexpr int XP = P + 16, NP = N + 16;
   constexpr int PT = P / 16, NT = N / 16;
   __shared__ __attribute__((aligned(16))) uint16_t Cs[kBlk * NP];  // C rows of the l block
@@ -310,8 +340,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kBlk * NP];  // B rows of the s block
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kBlk * XP];  // x rows of the s block
   __shared__ __attribute__((aligned(16))) uint16_t Rs[P * NP];     // R_c of the head
-  __shared__ float2 tk[256];
-  __shared__ float boxs[2][4][kBlk];  // per l-block parity and wave: box share of each row
+  __shared__ __attribute__((aligned(16))) float cs2[256];  // cs_l log2(e) of the chunk's tokens
+  __shared__ float dlt[256];                               // delta_l
+  __shared__ float rows[2][4][kBlk];  // per l-block parity and wave: row share of each row l
 
   const int nb = (Q + kBlk - 1) / kBlk;
   const int hpg = H / G;
@@ -346,13 +377,18 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
                                 static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
     const buf_t rbuf = make_buf(adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
                                 static_cast<uint32_t>(P) * N * 2);
-    __syncthreads();  // previous head done with Xs, Rs, tk, Ys, Cs
+    __syncthreads();  // previous head done with Xs, Rs, cs2, dlt, Ys, Cs
     stage_rows<P / 8, kBlk>(Xs, XP, xbuf, xrow, s0);
     stage_rows<N / 8, P>(Rs, NP, rbuf, N * 2, 0);
-    if (tid < Q) tk[tid] = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
+    if (tid < Q) {
+      const float2 t2 = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
+      cs2[tid] = t2.x * kLog2e;
+      dlt[tid] = t2.y;
+    }
     __syncthreads();
-    const float tot = tk[Q - 1].x;
-    const float cs_s = tk[sl].x, dl_s = tk[sl].y;
+    // every decay factor below is 2^(cs2_l - cs2_s) <= 1 (l >= s)
+    const float tot = cs2[Q - 1];
+    const float cs_s = cs2[sl], dl_s = dlt[sl];
 
     // boundary part of v: e^{tot-cs_s} B_s R^T, rows s = 16w + 4q + i of the tile
     f32x4 v[PT];
@@ -367,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     }
     float fr[4];  // e^{tot-cs_s} of the accumulator rows
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fr[i] = __expf(tot - tk[s0 + 16 * w + 4 * q + i].x);
+    for (int i = 0; i < 4; ++i) fr[i] = __builtin_amdgcn_exp2f(tot - cs2[s0 + 16 * w + 4 * q + i]);
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -380,11 +416,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) part += bf16_bits_to_f32(Xs[sr * XP + pt * 16 + r16]) * v[pt][i];
       part = sum16(part);
-      if (r16 == 15 && s0 + sr < Lc) f2o[(r0 + s0 + sr) * H + h] = tk[s0 + sr].y * part;
+      if (r16 == 15 && s0 + sr < Lc) f2o[(r0 + s0 + sr) * H + h] = dlt[s0 + sr] * part;
     }
     // boundary part of dB: delta_s e^{tot-cs_s} x_s R (A rows s = this lane's sl)
     {
-      const float f2 = dl_s * __expf(tot - cs_s);
+      const float f2 = dl_s * __builtin_amdgcn_exp2f(tot - cs_s);
 #pragma unroll
       for (int ks = 0; ks < P; ks += 32) {
         const uint4 a = scale8(lds_row8(Xs, XP, 16 * w + r16, ks + 8 * q), f2);
@@ -397,19 +433,19 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
       }
     }
 
-    float car = 0.0f;  // sum over the later l blocks of this column's box terms
-    // the four waves' box shares of l block lb, summed into the block's partial
-    // (once every wave has written boxs[lb & 1], i.e. after the next barrier)
-    auto flush_box = [&](int lb) {
+    float col = 0.0f;  // this lane's rows of sum_{l > s} E[l][s], column s = sl
+    // the four waves' shares of row_l of l block lb, summed into the block's
+    // share (once every wave has written rows[lb & 1], i.e. after the next barrier)
+    auto flush_rows = [&](int lb) {
       const int l0 = s0 + lb * kBlk;
-      const float(*bx)[kBlk] = boxs[lb & 1];
+      const float(*rw)[kBlk] = rows[lb & 1];
       if (tid < kBlk && l0 + tid < Lc)
-        boxp[static_cast<size_t>(j) * BTH + (r0 + l0 + tid) * H + h] = bx[0][tid] + bx[1][tid] + bx[2][tid] + bx[3][tid];
+        rowp[static_cast<size_t>(j) * BTH + (r0 + l0 + tid) * H + h] = rw[0][tid] + rw[1][tid] + rw[2][tid] + rw[3][tid];
     };
     for (int lb = nlb - 1; lb >= 0; --lb) {
       const int l0 = s0 + lb * kBlk;
       __syncthreads();
-      if (lb + 1 < nlb) flush_box(lb + 1);
+      if (lb + 1 < nlb) flush_rows(lb + 1);
       stage_rows<N / 8, kBlk>(Cs, NP, cbuf, brow, l0);
       stage_rows<P / 8, kBlk>(Ys, XP, ybuf, xrow, l0);
       __syncthreads();
@@ -434,26 +470,47 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
         for (int lt = 0; lt < 4; ++lt)
           s2[lt] = mfma_bf16(as_bf16x8(lds_row8(Ys, XP, lt * 16 + r16, ks + 8 * q)), as_bf16x8(xx), s2[lt]);
       }
-      // mask and decay -> bf16 A operands; k slot of lane group q: l = 16 lt + 4q + i
+      // mask and decay -> bf16 A operands (k slot of lane group q: l = 16 lt + 4q + i)
+      // and the fp32 box terms E[l][s] (l > s only)
       uint32_t am[4][2], aw[4][2];
-      float ee[4][4];  // box terms e^{cs_l-cs_s} delta_s (C_l.B_s)(dy_l.x_s), fp32
+      float ee[16];
+      auto decay = [&](auto masked) {
 #pragma unroll
-      for (int lt = 0; lt < 4; ++lt) {
-        float mv[4], wv[4];
+        for (int lt = 0; lt < 4; ++lt) {
+          const int lb4 = l0 + 16 * lt + 4 * q;
+          float mv[4], wv[4];
+          if constexpr (decltype(masked)::value) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int l = l0 + 16 * lt + 4 * q + i;
-          const bool ok = l >= sl && l < Lc && sl < Lc;
-          const float d = ok ? __expf(tk[l < Q ? l : Q - 1].x - cs_s) : 0.0f;
-          mv[i] = d * s1[lt][i];
-          wv[i] = d * dl_s * s2[lt][i];
-          ee[lt][i] = wv[i] * s1[lt][i];
+            for (int i = 0; i < 4; ++i) {
+              const int l = lb4 + i;
+              const bool ok = l >= sl && l < Lc;
+              const float d = ok ? __builtin_amdgcn_exp2f(cs2[min(l, Q - 1)] - cs_s) : 0.0f;
+              mv[i] = d * s1[lt][i];
+              wv[i] = d * dl_s * s2[lt][i];
+              ee[4 * lt + i] = l > sl ? wv[i] * s1[lt][i] : 0.0f;
+            }
+          } else {
+            const float4 c4 = *reinterpret_cast<const float4*>(cs2 + lb4);
+            const float cl[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float d = __builtin_amdgcn_exp2f(cl[i] - cs_s);
+              mv[i] = d * s1[lt][i];
+              wv[i] = d * dl_s * s2[lt][i];
+              ee[4 * lt + i] = wv[i] * s1[lt][i];
+            }
+          }
+          am[lt][0] = pack_bf16x2(mv[0], mv[1]);
+          am[lt][1] = pack_bf16x2(mv[2], mv[3]);
+          aw[lt][0] = pack_bf16x2(wv[0], wv[1]);
+          aw[lt][1] = pack_bf16x2(wv[2], wv[3]);
         }
-        am[lt][0] = pack_bf16x2(mv[0], mv[1]);
-        am[lt][1] = pack_bf16x2(mv[2], mv[3]);
-        aw[lt][0] = pack_bf16x2(wv[0], wv[1]);
-        aw[lt][1] = pack_bf16x2(wv[2], wv[3]);
-      }
+      };
+      // off the diagonal block (every l > every s) and inside the chunk: no mask
+      if (lb > 0 && l0 + kBlk <= Lc)
+        decay(std::false_type{});
+      else
+        decay(std::true_type{});
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const uint4 Am = make_uint4(am[2 * kk][0], am[2 * kk][1], am[2 * kk + 1][0], am[2 * kk + 1][1]);
@@ -471,41 +528,22 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
           dB[nt] = mfma_bf16(as_bf16x8(Aw), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dB[nt]);
         }
       }
-      // box: K_s(t) = sum_{l >= t} ee[l][s] down this lane's column s (rows of the
-      // block: 16 lt + 4 q + i, lane group q), then for every row t the sum over
-      // the columns s < t of the workgroup's block
-      float tt[4];
-#pragma unroll
-      for (int lt = 0; lt < 4; ++lt) {
-        ee[lt][2] += ee[lt][3];
-        ee[lt][1] += ee[lt][2];
-        ee[lt][0] += ee[lt][1];
-        float after;
-        group_suffix(ee[lt][0], q, after, tt[lt]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ee[lt][i] += after;
-      }
+      // column sums (per lane) and the rows' sums over the 16 columns of the
+      // lane group: lane r16 gets value 4 lt + i = r16, i.e. row 16 (r16 / 4) + 4q + r16 % 4
       {
-        float later = car;
+        float cp[4];
 #pragma unroll
-        for (int lt = 3; lt >= 0; --lt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ee[lt][i] += later;
-          later += tt[lt];
-        }
-        car = later;
+        for (int lt = 0; lt < 4; ++lt) cp[lt] = (ee[4 * lt] + ee[4 * lt + 1]) + (ee[4 * lt + 2] + ee[4 * lt + 3]);
+        col += (cp[0] + cp[1]) + (cp[2] + cp[3]);
       }
-#pragma unroll
-      for (int lt = 0; lt < 4; ++lt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * lt + 4 * q + i;
-          const float part = sum16(sl < l0 + row ? ee[lt][i] : 0.0f);
-          if (r16 == 15) boxs[lb & 1][w][row] = part;
-        }
+      rows[lb & 1][w][16 * (r16 >> 2) + 4 * q + (r16 & 3)] = transpose_sum16(ee);
     }
     __syncthreads();
-    flush_box(0);
+    flush_rows(0);
+    {
+      const float ct = group_total(col);
+      if (q == 0 && sl < Lc) colp[(r0 + sl) * H + h] = ct;
+    }
 
     // outputs of head h: lane holds p = 16 pt + r16 of rows s = s0 + 16w + 4q + i;
     // Ys now holds the dy rows of the s block (the last l block was the diagonal)
@@ -515,7 +553,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int sr = 16 * w + 4 * q + i;  // row within the block
-      const float dls = tk[s0 + sr].y;
+      const float dls = dlt[s0 + sr];
       float pxv = 0.0f, pdx = 0.0f;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
@@ -748,15 +786,18 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_const_kernel(
 // ---------------------------------------------------------------------------
 // Step-size gradients, one workgroup per (chunk, head, batch), thread l =
 // token l of the chunk:
-//   da_l = box_l + sum_{l' >= l} f1_l' + sum_{s < l} f2_s + e^{tot} <R_c, H_in>
-// (fp64 block scans: f1 summed from the chunk's end, f2 from its start), then
+//   da_l = box_l + sum_{l' >= l} f1_l' + sum_{s < l} f2_s + e^{tot} <R_c, H_in>,
+//   box_l = sum_{u < l} (col_u - row_u)
+// (fp64 block scans: f1 summed from the chunk's end, f2 and col - row from its
+// start; row_u is the sum of the column blocks' shares), then
 // ddelta_l = A da_l + x_l.v_l, ddt_l = ddelta_l sigmoid(z_l) [lo <= sp <= hi];
 // the chunk's shares of dA, ddt_bias and dD go to `part` (fp64).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
     const float* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
     float dt_min, float dt_max, const float* __restrict__ f1, const float* __restrict__ f2,
-    const float* __restrict__ boxp, const float* __restrict__ xv, const float* __restrict__ dyx,
+    const float* __restrict__ colp, const float* __restrict__ rowp, const float* __restrict__ xv,
+    const float* __restrict__ dyx,
     const double* __restrict__ cst, float* __restrict__ ddt, double* __restrict__ part, int Bsz,
     int T, int H, int Q, int nc) {
   __shared__ double wsum[4];
@@ -773,6 +814,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
   const size_t row = (static_cast<size_t>(b) * T + (in ? t : 0)) * H + h;
   const double f1v = in ? static_cast<double>(f1[row]) : 0.0;
   const double f2v = in ? static_cast<double>(f2[row]) : 0.0;
+  double gv = 0.0;  // col_u - row_u of this token
+  if (in) {
+    gv = colp[row];
+    for (int jb = 0; jb <= tid / kBlk; ++jb) gv -= rowp[static_cast<size_t>(jb) * BTH + row];
+  }
   // f1 summed from the chunk's end: thread k scans token 255 - k
   sfx[tid] = f1v;
   __syncthreads();
@@ -782,10 +828,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
   __syncthreads();
   const double f1_suffix = sfx[tid];
   const double f2_prefix = block_inclusive_scan(f2v, wsum) - f2v;
+  __syncthreads();
+  const double box = block_inclusive_scan(gv, wsum) - gv;
   double sA = 0.0, sBias = 0.0, sD = 0.0;
   if (in) {
-    double box = 0.0;
-    for (int jb = 0; jb <= tid / kBlk; ++jb) box += boxp[static_cast<size_t>(jb) * BTH + row];
     const double da = box + f1_suffix + f2_prefix + cst[bhc];
     const float z = dt[row] + bias;
     const float d = step_size(dt[row], bias, dt_min, dt_max);
@@ -860,12 +906,12 @@ int bwd_heads_per_group(int H, int G) {
 }
 
 // workspace layout of the backward, after the forward's own (states, decays,
-// token table): the adjoint states (bf16); f1, f2, x.v, dy.x (fp32 per token
-// and head); the box shares of the column blocks (fp32, one per block); the
+// token table): the adjoint states (bf16); f1, f2, x.v, dy.x, col (fp32 per
+// token and head); the row shares of the column blocks (fp32, one per block); the
 // chunk constants of da and the chunk shares of dA, ddt_bias, dD (fp64); the
 // dB and dC partials (fp32)
 struct BwdLayout {
-  size_t fwd, adj, f1, f2, xv, dyx, box, cst, dtp, dBp, dCp, total;
+  size_t fwd, adj, f1, f2, xv, dyx, col, row, cst, dtp, dBp, dCp, total;
 };
 static BwdLayout bwd_layout(int Bsz, int T, int H, int P, int G, int N, int chunk) {
   const int nc = (T + chunk - 1) / chunk;
@@ -886,7 +932,9 @@ static BwdLayout bwd_layout(int Bsz, int T, int H, int P, int G, int N, int chun
   o += up(tok);
   L.dyx = o;
   o += up(tok);
-  L.box = o;
+  L.col = o;
+  o += up(tok);
+  L.row = o;
   o += up(tok * ((chunk + kBlk - 1) / kBlk));
   L.cst = o;
   o += up(static_cast<size_t>(Bsz) * H * nc * 8);
@@ -942,7 +990,8 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   uint16_t* adj = reinterpret_cast<uint16_t*>(ws + L.adj);
   float* f1 = reinterpret_cast<float*>(ws + L.f1);
   float* f2 = reinterpret_cast<float*>(ws + L.f2);
-  float* box = reinterpret_cast<float*>(ws + L.box);
+  float* col = reinterpret_cast<float*>(ws + L.col);
+  float* rowp = reinterpret_cast<float*>(ws + L.row);
   float* xv = reinterpret_cast<float*>(ws + L.xv);
   float* dyx = reinterpret_cast<float*>(ws + L.dyx);
   float* dBp = reinterpret_cast<float*>(ws + L.dBp);
@@ -963,7 +1012,7 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const unsigned bblocks = static_cast<unsigned>((bpairs + kXCD - 1) / kXCD) * kXCD * (a.H / HPG);
   launch_k(nc > 0, ssd_bwd_dxdb_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 8 : nullptr,
            x, B, C, dy, a.D, tok, static_cast<const uint16_t*>(adj), static_cast<uint16_t*>(a.dx), xv,
-           dyx, f2, box, dBp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
+           dyx, f2, col, rowp, dBp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
   launch_k(nc > 0, ssd_bwd_dc_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 10 : nullptr,
            x, B, C, dy, tok, states, f1, dCp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
   double* cst = reinterpret_cast<double*>(ws + L.cst);
@@ -973,7 +1022,8 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   double* dtp = reinterpret_cast<double*>(ws + L.dtp);
   launch_k(nc > 0, ssd_bwd_dt_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
            ev ? ev + 14 : nullptr, a.dt, a.A, a.dt_bias, a.dt_min, a.dt_max, static_cast<const float*>(f1),
-           static_cast<const float*>(f2), static_cast<const float*>(box), static_cast<const float*>(xv),
+           static_cast<const float*>(f2), static_cast<const float*>(col), static_cast<const float*>(rowp),
+           static_cast<const float*>(xv),
            static_cast<const float*>(dyx), static_cast<const double*>(cst), a.ddt, dtp, a.Bsz, a.T, a.H,
            Q, nc);
   launch_k(true, ssd_bwd_dt_sum_kernel, dim3((a.H + kThreads - 1) / kThreads), dim3(kThreads), st,
