@@ -610,7 +610,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ys[kBlk * XP];  // dy rows of the l block
   __shared__ __attribute__((aligned(16))) uint16_t Hs[P * NP];     // h_in(c) of the head
   __shared__ __attribute__((aligned(16))) uint16_t Cs[kBlk * NP];  // C rows of the l block
-  __shared__ float2 tk[256];
+  __shared__ __attribute__((aligned(16))) float cs2[256];  // cs_s log2(e) of the chunk's tokens
+  __shared__ __attribute__((aligned(16))) float dlt[256];  // delta_s
 
   const int nb = (Q + kBlk - 1) / kBlk;
   const int hpg = H / G;
@@ -654,16 +655,21 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
     __syncthreads();
     stage_rows<P / 8, kBlk>(Ys, XP, ybuf, xrow, l0);
     stage_rows<N / 8, P>(Hs, NP, hbuf, N * 2, 0);
-    if (tid < Q) tk[tid] = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
+    if (tid < Q) {
+      const float2 t2 = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
+      cs2[tid] = t2.x * kLog2e;
+      dlt[tid] = t2.y;
+    }
     __syncthreads();
-    const float cs_l = tk[ll < Q ? ll : Q - 1].x;
+    // every decay factor below is 2^(cs2_l - cs2_s) <= 1 (s <= l)
+    const float cs_l = cs2[ll < Lc ? ll : Lc - 1];
 
     // boundary: e^{cs_l} dy_l H_in (A rows l = this lane's ll)
     f32x4 dC[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) dC[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      const float f = __expf(cs_l);
+      const float f = __builtin_amdgcn_exp2f(cs_l);
 #pragma unroll
       for (int ks = 0; ks < P; ks += 32) {
         const uint4 a = scale8(lds_row8(Ys, XP, 16 * w + r16, ks + 8 * q), f);
@@ -710,19 +716,34 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
           st2[st] = mfma_bf16(as_bf16x8(lds_row8(Xs, XP, st * 16 + r16, ks + 8 * q)), as_bf16x8(yy), st2[st]);
       }
       uint32_t aw[4][2];
+      auto decay = [&](auto masked) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        float wv[4];
+        for (int st = 0; st < 4; ++st) {
+          const int sb4 = s0 + 16 * st + 4 * q;
+          const float4 c4 = *reinterpret_cast<const float4*>(cs2 + sb4);
+          const float4 d4 = *reinterpret_cast<const float4*>(dlt + sb4);
+          const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+          float wv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = s0 + 16 * st + 4 * q + i;
-          const bool ok = ll >= s && ll < Lc && s < Lc;
-          const float2 ts = tk[s];
-          wv[i] = ok ? __expf(cs_l - ts.x) * ts.y * st2[st][i] : 0.0f;
+          for (int i = 0; i < 4; ++i) {
+            const float v = __builtin_amdgcn_exp2f(cs_l - cv[i]) * dv[i] * st2[st][i];
+            if constexpr (decltype(masked)::value) {
+              const int s = sb4 + i;
+              wv[i] = (ll >= s && ll < Lc && s < Lc) ? v : 0.0f;
+            } else {
+              wv[i] = v;
+            }
+          }
+          aw[st][0] = pack_bf16x2(wv[0], wv[1]);
+          aw[st][1] = pack_bf16x2(wv[2], wv[3]);
         }
-        aw[st][0] = pack_bf16x2(wv[0], wv[1]);
-        aw[st][1] = pack_bf16x2(wv[2], wv[3]);
-      }
+      };
+      // blocks below the diagonal: every s < every l, no mask (rows l past
+      // the chunk's end hold zero dy, so their scores are zero, and are not stored)
+      if (sb < ib)
+        decay(std::false_type{});
+      else
+        decay(std::true_type{});
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const uint4 Aw = make_uint4(aw[2 * kk][0], aw[2 * kk][1], aw[2 * kk + 1][0], aw[2 * kk + 1][1]);
