@@ -367,9 +367,13 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wid = wave_id();  // wave-uniform (SGPR): tile branches stay scalar
+  // the output row tile of this wave, rotated by the workgroup index: the tiles
+  // late in a sub-chunk carry more of the causal block, and rotation spreads
+  // them over the SIMDs of a CU instead of loading one SIMD in every workgroup
+  const int rw = __builtin_amdgcn_readfirstlane((wid + static_cast<int>(blockIdx.x)) & 3);
   const int QS = Q < QSM ? Q : QSM;
   const int nsub = Q / QS;
-  const bool has_rows = 16 * wid < QS;  // waves without output rows (Q = 32) only help stage
+  const bool has_rows = 16 * rw < QS;  // waves without output rows (Q = 32) only help stage
   // per-token exponents and step sizes (from the chunk-state kernel), first
   const float2 tv = tid < Q ? tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid]
                             : make_float2(0.f, 0.f);
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   // the K padding (N = 16) is zeroed by an out-of-range offset, not by a
   // select on the loaded value, so the prefetch is not waited for here.
   auto load_c = [&](uint4 (&cr)[NKS], int j) {
-    const uint32_t row = j * QS + 16 * wid + r16;
+    const uint32_t row = j * QS + 16 * rw + r16;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int k0 = ks * 32 + 8 * q;
@@ -528,9 +532,9 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       load_c(cnext, j + 1);
     }
 
-    // ---- outputs of rows sj + 16 wid .. +15 (accumulator columns) ----
+    // ---- outputs of rows sj + 16 rw .. +15 (accumulator columns) ----
     if (has_rows) {
-      const int lrow = sj + 16 * wid + r16;  // this lane's output row
+      const int lrow = sj + 16 * rw + r16;  // this lane's output row
       f32x4 yacc[NPT];
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) yacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -549,10 +553,10 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
         for (int pt = 0; pt < NPT; ++pt) yacc[pt] = yacc[pt] * s1;
       }
       // intra-chunk: source blocks b0 = 2k2, b1 = 2k2+1 (16 tokens each);
-      // block wid is the diagonal one
-      for (int k2 = 0; 2 * k2 <= wid; ++k2) {
+      // block rw is the diagonal one
+      for (int k2 = 0; 2 * k2 <= rw; ++k2) {
         const int b0 = 2 * k2, b1 = 2 * k2 + 1;
-        const bool live1 = b1 <= wid;
+        const bool live1 = b1 <= rw;
         f32x4 ga = f32x4{0.f, 0.f, 0.f, 0.f}, gb = ga;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -566,17 +570,17 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
             gb = mfma_bf16(as_bf16x8(vb), as_bf16x8(creg[ks]), gb);
           }
         }
-        // lane: column l = r16 (+16 wid), rows s = 4q + jj of blocks b0, b1
+        // lane: column l = r16 (+16 rw), rows s = 4q + jj of blocks b0, b1
         if (!exact) {
           const float4 wa = *reinterpret_cast<const float4*>(xsc + sj + b0 * 16 + 4 * q);
           const float4 wb = *reinterpret_cast<const float4*>(xsc + sj + b1 * 16 + 4 * q);
           ga = ga * f32x4{wa.x, wa.y, wa.z, wa.w};
           gb = gb * f32x4{wb.x, wb.y, wb.z, wb.w};
-          if (b0 == wid) {
+          if (b0 == rw) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) ga[jj] = 4 * q + jj <= r16 ? ga[jj] : 0.f;
           }
-          if (b1 == wid) {
+          if (b1 == rw) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) gb[jj] = 4 * q + jj <= r16 ? gb[jj] : 0.f;
           }
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       const float s2 = exact ? 1.0f : csc[lrow];
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
-        const uint2 u = *reinterpret_cast<const uint2*>(xl + (16 * wid + r16) * XPn + pt * 16 + 4 * q);
+        const uint2 u = *reinterpret_cast<const uint2*>(xl + (16 * rw + r16) * XPn + pt * 16 + 4 * q);
         const float o0 = yacc[pt][0] * s2 + Dh * bf16_bits_to_f32(u.x & 0xFFFFu);
         const float o1 = yacc[pt][1] * s2 + Dh * bf16_bits_to_f32(u.x >> 16);
         const float o2 = yacc[pt][2] * s2 + Dh * bf16_bits_to_f32(u.y & 0xFFFFu);
