@@ -821,9 +821,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
     const float* __restrict__ dyx,
     const double* __restrict__ cst, float* __restrict__ ddt, double* __restrict__ part, int Bsz,
     int T, int H, int Q, int nc) {
-  __shared__ double wsum[4];
+  __shared__ double wsum[3][4];
   __shared__ double red[3][4];
-  __shared__ double sfx[kThreads];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
   const float a_re = A[h];
@@ -840,17 +839,25 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
     gv = colp[row];
     for (int jb = 0; jb <= tid / kBlk; ++jb) gv -= rowp[static_cast<size_t>(jb) * BTH + row];
   }
-  // f1 summed from the chunk's end: thread k scans token 255 - k
-  sfx[tid] = f1v;
+  // one fp64 block scan of (f1, f2, col - row): DPP wave scans, then the
+  // preceding waves' totals; f1's suffix is its total less the prefix before l
+  double sc[3] = {f1v, f2v, gv};
+#pragma unroll
+  for (int k = 0; k < 3; ++k) sc[k] = wave_inclusive_sum_d(sc[k]);
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) wsum[k][wid] = sc[k];
+  }
   __syncthreads();
-  const double rev = block_inclusive_scan(sfx[kThreads - 1 - tid], wsum);
-  __syncthreads();
-  sfx[kThreads - 1 - tid] = rev;
-  __syncthreads();
-  const double f1_suffix = sfx[tid];
-  const double f2_prefix = block_inclusive_scan(f2v, wsum) - f2v;
-  __syncthreads();
-  const double box = block_inclusive_scan(gv, wsum) - gv;
+  double before[3] = {0.0, 0.0, 0.0};
+  for (int w = 0; w < wid; ++w) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) before[k] += wsum[k][w];
+  }
+  const double f1_total = (wsum[0][0] + wsum[0][1]) + (wsum[0][2] + wsum[0][3]);
+  const double f1_suffix = f1_total - (sc[0] + before[0]) + f1v;
+  const double f2_prefix = sc[1] + before[1] - f2v;
+  const double box = sc[2] + before[2] - gv;
   double sA = 0.0, sBias = 0.0, sD = 0.0;
   if (in) {
     const double da = box + f1_suffix + f2_prefix + cst[bhc];
@@ -866,13 +873,11 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
     sBias = gz;
     sD = dyx[row];
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    sA += __shfl_xor(sA, o, kWave);
-    sBias += __shfl_xor(sBias, o, kWave);
-    sD += __shfl_xor(sD, o, kWave);
-  }
-  __syncthreads();
-  if (lane == 0) {
+  // wave sums by DPP scans (the total lands in the last lane)
+  sA = wave_inclusive_sum_d(sA);
+  sBias = wave_inclusive_sum_d(sBias);
+  sD = wave_inclusive_sum_d(sD);
+  if (lane == kWave - 1) {
     red[0][wid] = sA;
     red[1][wid] = sBias;
     red[2][wid] = sD;
