@@ -291,18 +291,29 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_pass_kernel(
   if (dh0) *reinterpret_cast<float4*>(dh0 + bh * PN + e4 * 4) = r;
 }
 
-// Work unit of the two block kernels: (b, chunk, 64-token block, head group),
-// in the XCD-grouped order of the forward (the head groups of one (b, chunk,
-// block) share an XCD and its L2, which serves their common B and C rows).
+// Work unit of the two block kernels: (b, chunk, 64-token block, head group).
+// A unit's work grows with its block's distance from the chunk's end (column
+// blocks) or start (row blocks), so the workgroups go out heaviest block
+// first (the longest-first order keeps the tail short); inside one block
+// rank, the XCD-grouped order of the forward (the head groups of one (b,
+// chunk, block) share an XCD and its L2, which serves their common B and C
+// rows).  `units_per_rank` workgroups per block rank.
 struct BlockUnit {
   int b, c, blk, hg;
 };
-__device__ __forceinline__ bool block_unit(int ngroups, int nc, int nb, int Bsz, BlockUnit& u) {
-  int b, cj, hg;
-  if (!unit_coords(blockIdx.x, ngroups, nc * nb, Bsz * nc * nb, b, cj, hg)) return false;
+__host__ __device__ inline int units_per_rank(int ngroups, int nc, int Bsz) {
+  return (Bsz * nc + kXCD - 1) / kXCD * kXCD * ngroups;
+}
+__device__ __forceinline__ bool block_unit(int ngroups, int nc, int nb, int Bsz, bool heavy_last_block,
+                                           BlockUnit& u) {
+  const int per = units_per_rank(ngroups, nc, Bsz);
+  const int rank = static_cast<int>(blockIdx.x) / per;
+  int b, c, hg;
+  if (rank >= nb || !unit_coords(static_cast<int>(blockIdx.x) % per, ngroups, nc, Bsz * nc, b, c, hg))
+    return false;
   u.b = b;
-  u.c = cj / nb;
-  u.blk = cj % nb;
+  u.c = c;
+  u.blk = heavy_last_block ? nb - 1 - rank : rank;
   u.hg = hg;
   return true;
 }
@@ -347,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
   const int nb = (Q + kBlk - 1) / kBlk;
   const int hpg = H / G;
   BlockUnit u;
-  if (!block_unit(H / HPG, nc, nb, Bsz, u)) return;
+  if (!block_unit(H / HPG, nc, nb, Bsz, false, u)) return;  // column block 0 carries the most rows
   const int b = u.b, c = u.c, j = u.blk;
   const size_t BTH = static_cast<size_t>(Bsz) * T * H;
   const int h0 = u.hg * HPG, g = h0 / hpg, hgl = (h0 % hpg) / HPG;
@@ -616,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
   const int nb = (Q + kBlk - 1) / kBlk;
   const int hpg = H / G;
   BlockUnit u;
-  if (!block_unit(H / HPG, nc, nb, Bsz, u)) return;
+  if (!block_unit(H / HPG, nc, nb, Bsz, true, u)) return;  // the last row block carries the most columns
   const int b = u.b, c = u.c, ib = u.blk;
   const int h0 = u.hg * HPG, g = h0 / hpg, hgl = (h0 % hpg) / HPG;
   const int t0 = c * Q, Lc = min(Q, T - t0), l0 = ib * kBlk;
@@ -1034,8 +1045,7 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
            dim3(kThreads), st, ev ? ev + 6 : nullptr, adj, decay, a.dh_final, a.dh0, a.H, P * N, nc);
   const int HPG = bwd_heads_per_group(a.H, a.G);
   const int nb = (Q + kBlk - 1) / kBlk;
-  const int bpairs = a.Bsz * nc * nb;
-  const unsigned bblocks = static_cast<unsigned>((bpairs + kXCD - 1) / kXCD) * kXCD * (a.H / HPG);
+  const unsigned bblocks = static_cast<unsigned>(nb) * units_per_rank(a.H / HPG, nc, a.Bsz);
   launch_k(nc > 0, ssd_bwd_dxdb_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 8 : nullptr,
            x, B, C, dy, a.D, tok, static_cast<const uint16_t*>(adj), static_cast<uint16_t*>(a.dx), xv,
            dyx, f2, col, rowp, dBp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
