@@ -348,6 +348,13 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   constexpr int KT = N / 16;            // n tiles of the state
   constexpr int KTW = (KT + 3) / 4;     // n tiles per wave in the state update
   constexpr float kMaxHalfSpread = 60.0f;
+  // Output tiles in pairs (P >= 32): tile pt covers p = 32 (pt / 2) + 4 (pt % 2)
+  // + 8 (r / 4) + r % 4 for its MFMA row r, so that a lane's accumulator rows of
+  // the two tiles of a pair are 8 consecutive p (one 16-byte y store)
+  constexpr bool kPairP = NPT % 2 == 0;
+  auto prow = [](int pt, int r) {
+    return kPairP ? 32 * (pt >> 1) + 4 * (pt & 1) + 8 * (r >> 2) + (r & 3) : pt * 16 + r;
+  };
 
   __shared__ __attribute__((aligned(16))) uint16_t bt[QSM * BTP];
   __shared__ __attribute__((aligned(16))) uint16_t xl[QSM * XPn];  // raw x
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
-          const uint4 hv = *reinterpret_cast<const uint4*>(hT + (pt * 16 + r16) * HTP + ks * 32 + 8 * q);
+          const uint4 hv = *reinterpret_cast<const uint4*>(hT + prow(pt, r16) * HTP + ks * 32 + 8 * q);
           yacc[pt] = mfma_bf16(as_bf16x8(hv), as_bf16x8(creg[ks]), yacc[pt]);
         }
       }
@@ -603,15 +610,35 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
                                     pack_bf16x2(gb[0], gb[1]), pack_bf16x2(gb[2], gb[3]));
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
-          const uint2 lo = lds_tr4(xl, XPn, b0 * 16 + 4 * q, pt * 16);
-          const uint2 hi = lds_tr4(xl, XPn, b1 * 16 + 4 * q, pt * 16);
+          const uint2 lo = kPairP ? lds_tr4s<8>(xl, XPn, b0 * 16 + 4 * q, 32 * (pt >> 1) + 4 * (pt & 1))
+                                  : lds_tr4(xl, XPn, b0 * 16 + 4 * q, pt * 16);
+          const uint2 hi = kPairP ? lds_tr4s<8>(xl, XPn, b1 * 16 + 4 * q, 32 * (pt >> 1) + 4 * (pt & 1))
+                                  : lds_tr4(xl, XPn, b1 * 16 + 4 * q, pt * 16);
           yacc[pt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(mv),
                                yacc[pt]);
         }
       }
-      // row scale, + D x_l, y rows out (lane: row lrow, columns pt*16 + 4q .. +3;
-      // rows past Lc are dropped by the descriptor)
+      // row scale, + D x_l, y rows out (lane: row lrow; rows past Lc are dropped
+      // by the descriptor).  Paired tiles: columns 32 hh + 8q .. +7, one 16-byte
+      // store per pair; else columns pt*16 + 4q .. +3
       const float s2 = exact ? 1.0f : csc[lrow];
+      if constexpr (kPairP) {
+#pragma unroll
+        for (int hh = 0; hh < NPT / 2; ++hh) {
+          const uint4 u = *reinterpret_cast<const uint4*>(xl + (16 * rw + r16) * XPn + hh * 32 + 8 * q);
+          const uint32_t xw[4] = {u.x, u.y, u.z, u.w};
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t w2 = xw[e >> 1];
+            const float xv = bf16_bits_to_f32((e & 1) ? (w2 >> 16) : (w2 & 0xFFFFu));
+            o[e] = yacc[2 * hh + (e >> 2)][e & 3] * s2 + Dh * xv;
+          }
+          buf_store16(ybuf, static_cast<uint32_t>(lrow) * xrow + (hh * 32 + 8 * q) * 2,
+                      make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                 pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])));
+        }
+      } else {
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
         const uint2 u = *reinterpret_cast<const uint2*>(xl + (16 * rw + r16) * XPn + pt * 16 + 4 * q);
@@ -621,6 +648,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
         const float o3 = yacc[pt][3] * s2 + Dh * bf16_bits_to_f32(u.y >> 16);
         buf_store8(ybuf, static_cast<uint32_t>(lrow) * xrow + (pt * 16 + 4 * q) * 2,
                    make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)));
+      }
       }
     }
 

@@ -193,6 +193,17 @@ __device__ __forceinline__ uint2 lds_tr4(const uint16_t* tile, int pitch, int ro
   return __builtin_bit_cast(uint2, r);
 }
 
+// The same read with the four 4-column pieces of each row CS columns apart:
+// lane i receives column col0 + CS (i / 4) + i % 4 of rows row0 .. row0+3
+// (CS = 4 is lds_tr4).
+template <int CS>
+__device__ __forceinline__ uint2 lds_tr4s(const uint16_t* tile, int pitch, int row0, int col0) {
+  const int m = threadIdx.x & 15;
+  const uint16_t* a = tile + (row0 + (m >> 2)) * pitch + col0 + CS * (m & 3);
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(const_cast<uint16_t*>(a)));
+  return __builtin_bit_cast(uint2, r);
+}
+
 // MFMA wrappers (gfx950).  Operand layouts for the 16x16 forms, lane i,
 // q = i / 16:  A holds row i % 16, B holds column i % 16, and the k values
 // of a lane are k-group q; the accumulator holds column i % 16, rows
