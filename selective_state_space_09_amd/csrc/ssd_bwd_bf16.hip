@@ -346,6 +346,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     int HPG) {
   constexpr int XP = P + 16, NP = N + 16;
   constexpr int PT = P / 16, NT = N / 16;
+  static_assert(P % 32 == 0, "v tiles go in pairs of 16 p");
   __shared__ __attribute__((aligned(16))) uint16_t Cs[kBlk * NP];  // C rows of the l block
   __shared__ __attribute__((aligned(16))) uint16_t Ys[kBlk * XP];  // dy rows of the l block
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kBlk * NP];  // B rows of the s block
@@ -401,33 +402,47 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     const float tot = cs2[Q - 1];
     const float cs_s = cs2[sl], dl_s = dlt[sl];
 
-    // boundary part of v: e^{tot-cs_s} B_s R^T, rows s = 16w + 4q + i of the tile
+    // v transposed, v^T[p][s]: a lane holds column s = sl and, per tile pt, the
+    // rows p = vp(pt, 4q + i).  The tiles go in pairs with permuted p (the pair
+    // hh covers p = 32 hh .. 32 hh + 31; MFMA row r of its tile (hh, half) is
+    // p = 32 hh + 4 half + 8 (r / 4) + r % 4), so that a lane's rows of a pair
+    // are the 8 consecutive p = 32 hh + 8q .. +7: 16-byte accesses of dx, x, dy.
+    auto vp = [](int pt, int r) { return 32 * (pt >> 1) + 4 * (pt & 1) + 8 * (r >> 2) + (r & 3); };
+    const int sr = 16 * w + r16;  // this lane's row s within the block
+    // boundary part: e^{tot-cs_s} R_c[p] . B_s
     f32x4 v[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) v[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < N; ks += 32) {
-      const uint4 a = lds_row8(Bs, NP, 16 * w + r16, ks + 8 * q);
+      const uint4 bb = lds_row8(Bs, NP, sr, ks + 8 * q);
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt)
-        v[pt] = mfma_bf16(as_bf16x8(a), as_bf16x8(lds_row8(Rs, NP, pt * 16 + r16, ks + 8 * q)), v[pt]);
+        v[pt] = mfma_bf16(as_bf16x8(lds_row8(Rs, NP, vp(pt, r16), ks + 8 * q)), as_bf16x8(bb), v[pt]);
     }
-    float fr[4];  // e^{tot-cs_s} of the accumulator rows
+    {
+      const float fr = __builtin_amdgcn_exp2f(tot - cs_s);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fr[i] = __builtin_amdgcn_exp2f(tot - cs2[s0 + 16 * w + 4 * q + i]);
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[pt][i] *= fr[i];
-    // f2_s = delta_s x_s . (e^{tot-cs_s} R_c B_s): the R part of x.v, before the rest
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sr = 16 * w + 4 * q + i;
+      for (int pt = 0; pt < PT; ++pt) v[pt] = v[pt] * fr;
+    }
+    // x_s . v_s over this lane's 8 p of pair hh (x . the R part of v: f2; later x . v)
+    auto xdot = [&](const uint16_t* rowp) {
       float part = 0.0f;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) part += bf16_bits_to_f32(Xs[sr * XP + pt * 16 + r16]) * v[pt][i];
-      part = sum16(part);
-      if (r16 == 15 && s0 + sr < Lc) f2o[(r0 + s0 + sr) * H + h] = dlt[s0 + sr] * part;
+      for (int hh = 0; hh < PT / 2; ++hh) {
+        const uint4 u = *reinterpret_cast<const uint4*>(rowp + hh * 32 + 8 * q);
+        const uint32_t xw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          part += bf16_bits_to_f32((e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu)) *
+                  v[2 * hh + (e >> 2)][e & 3];
+      }
+      return part;
+    };
+    // f2_s = delta_s x_s . (e^{tot-cs_s} R_c B_s): the R part of x.v, before the rest
+    {
+      const float part = group_total(xdot(Xs + sr * XP));
+      if (q == 0 && sl < Lc) f2o[(r0 + sl) * H + h] = dl_s * part;
     }
     // boundary part of dB: delta_s e^{tot-cs_s} x_s R (A rows s = this lane's sl)
     {
@@ -528,9 +543,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
         const uint4 Aw = make_uint4(aw[2 * kk][0], aw[2 * kk][1], aw[2 * kk + 1][0], aw[2 * kk + 1][1]);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-          const uint2 lo = lds_tr4(Ys, XP, 32 * kk + 4 * q, pt * 16);
-          const uint2 hi = lds_tr4(Ys, XP, 32 * kk + 16 + 4 * q, pt * 16);
-          v[pt] = mfma_bf16(as_bf16x8(Am), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), v[pt]);
+          const int c0 = 32 * (pt >> 1) + 4 * (pt & 1);
+          const uint2 lo = lds_tr4s<8>(Ys, XP, 32 * kk + 4 * q, c0);
+          const uint2 hi = lds_tr4s<8>(Ys, XP, 32 * kk + 16 + 4 * q, c0);
+          v[pt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(Am), v[pt]);
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -556,33 +572,37 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
       if (q == 0 && sl < Lc) colp[(r0 + sl) * H + h] = ct;
     }
 
-    // outputs of head h: lane holds p = 16 pt + r16 of rows s = s0 + 16w + 4q + i;
+    // outputs of head h: lane holds row s = sl, p = 32 hh + 8q .. +7 of each pair;
     // Ys now holds the dy rows of the s block (the last l block was the diagonal)
     const float Dh = D ? D[h] : 0.0f;
     const buf_t dxbuf = make_buf(dx + r0 * H * P + static_cast<size_t>(h) * P,
                                  static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sr = 16 * w + 4 * q + i;  // row within the block
-      const float dls = dlt[s0 + sr];
+    {
       float pxv = 0.0f, pdx = 0.0f;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        const int p = pt * 16 + r16;
-        const float xe = bf16_bits_to_f32(Xs[sr * XP + p]);
-        const float ye = bf16_bits_to_f32(Ys[sr * XP + p]);
-        pxv += xe * v[pt][i];
-        pdx += xe * ye;
-        const float gx = dls * v[pt][i] + Dh * ye;
-        const uint32_t off = (static_cast<uint32_t>(s0 + sr) * xrow + p * 2);
-        __builtin_amdgcn_raw_buffer_store_b16(
-            __builtin_bit_cast(unsigned short, static_cast<__bf16>(gx)), dxbuf, off, 0, 0);
+      for (int hh = 0; hh < PT / 2; ++hh) {
+        const uint4 ux = *reinterpret_cast<const uint4*>(Xs + sr * XP + hh * 32 + 8 * q);
+        const uint4 uy = *reinterpret_cast<const uint4*>(Ys + sr * XP + hh * 32 + 8 * q);
+        const uint32_t xw[4] = {ux.x, ux.y, ux.z, ux.w}, yw[4] = {uy.x, uy.y, uy.z, uy.w};
+        float gx[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xe = bf16_bits_to_f32((e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu));
+          const float ye = bf16_bits_to_f32((e & 1) ? (yw[e >> 1] >> 16) : (yw[e >> 1] & 0xFFFFu));
+          const float ve = v[2 * hh + (e >> 2)][e & 3];
+          pxv += xe * ve;
+          pdx += xe * ye;
+          gx[e] = dl_s * ve + Dh * ye;
+        }
+        buf_store16(dxbuf, static_cast<uint32_t>(sl) * xrow + (hh * 32 + 8 * q) * 2,
+                    make_uint4(pack_bf16x2(gx[0], gx[1]), pack_bf16x2(gx[2], gx[3]),
+                               pack_bf16x2(gx[4], gx[5]), pack_bf16x2(gx[6], gx[7])));
       }
-      pxv = sum16(pxv);
-      pdx = sum16(pdx);
-      if (r16 == 15 && s0 + sr < Lc) {
-        xv[(r0 + s0 + sr) * H + h] = pxv;
-        dyx[(r0 + s0 + sr) * H + h] = pdx;
+      pxv = group_total(pxv);
+      pdx = group_total(pdx);
+      if (q == 0 && sl < Lc) {
+        xv[(r0 + sl) * H + h] = pxv;
+        dyx[(r0 + sl) * H + h] = pdx;
       }
     }
   }
