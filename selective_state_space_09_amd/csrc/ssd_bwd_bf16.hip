@@ -328,8 +328,10 @@ __device__ __forceinline__ bool block_unit(int ngroups, int nc, int nb, int Bsz,
 // (dy_l.x_s) for l >= s.  The rows l run over 64-token blocks, last first
 // (the diagonal block last, so that its dy rows are in LDS for dx); C_l.B_s
 // and dy_l.x_s are MFMA tiles whose lane holds one s and four l, which after
-// the mask and decay are the A operands (rows s, contraction over l) of the
-// products with dy and C, read from LDS by the transpose read.  The same
+// the mask and decay are the B operands (columns s, contraction over l) of the
+// transposed products v^T += dy^T M and dB^T += C^T W, whose A operands (dy and
+// C) come from LDS by the transpose read: a lane ends with one s of v and dB
+// and runs of consecutive p or n (16-byte stores of dx and the dB partials).  The same
 // fp32 tiles give the box terms E[l][s] (l > s): each lane sums its column
 // over the l blocks (col_s, once per head), and a transposing reduction over
 // the 16 columns of each lane group gives the rows' sums (the block's share of
@@ -375,10 +377,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
   stage_rows<N / 8, kBlk>(Bs, NP, bbuf, brow, s0);
 
-  f32x4 dB[NT];
+  f32x4 dB[NT];  // dB^T[n][s]: lane holds column s = sl, rows n = 16 nt + 4q + i
 #pragma unroll
   for (int i = 0; i < NT; ++i) dB[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int sl = s0 + 16 * w + r16;  // this lane's source token (A rows, score columns)
+  const int sl = s0 + 16 * w + r16;  // this lane's source token (score, v^T and dB^T columns)
   const int nlb = (Lc - s0 + kBlk - 1) / kBlk;
 
   for (int e = 0; e < HPG; ++e) {
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
       const float part = group_total(xdot(Xs + sr * XP));
       if (q == 0 && sl < Lc) f2o[(r0 + sl) * H + h] = dl_s * part;
     }
-    // boundary part of dB: delta_s e^{tot-cs_s} x_s R (A rows s = this lane's sl)
+    // boundary part of dB: delta_s e^{tot-cs_s} (x_s R)[n] (B columns s = this lane's sl)
     {
       const float f2 = dl_s * __builtin_amdgcn_exp2f(tot - cs_s);
 #pragma unroll
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
         for (int nt = 0; nt < NT; ++nt) {
           const uint2 lo = lds_tr4(Rs, NP, ks + 8 * q, nt * 16);
           const uint2 hi = lds_tr4(Rs, NP, ks + 8 * q + 4, nt * 16);
-          dB[nt] = mfma_bf16(as_bf16x8(a), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dB[nt]);
+          dB[nt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(a), dB[nt]);
         }
       }
     }
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
         for (int nt = 0; nt < NT; ++nt) {
           const uint2 lo = lds_tr4(Cs, NP, 32 * kk + 4 * q, nt * 16);
           const uint2 hi = lds_tr4(Cs, NP, 32 * kk + 16 + 4 * q, nt * 16);
-          dB[nt] = mfma_bf16(as_bf16x8(Aw), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dB[nt]);
+          dB[nt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(Aw), dB[nt]);
         }
       }
       // column sums (per lane) and the rows' sums over the 16 columns of the
@@ -607,15 +609,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     }
   }
 
-  // dB of the head group: lane holds n = 16 nt + r16 of rows s = s0 + 16w + 4q + i
+  // dB of the head group, computed transposed: lane holds row s = sl and
+  // n = 16 nt + 4q .. +3 (one 16-byte store per tile)
   float* dst = dBp + ((static_cast<size_t>(hgl) * Bsz + b) * T + t0) * G * N + static_cast<size_t>(g) * N;
+  if (sl < Lc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = s0 + 16 * w + 4 * q + i;
-    if (s < Lc) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) dst[static_cast<size_t>(s) * G * N + nt * 16 + r16] = dB[nt][i];
-    }
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f32x4*>(dst + static_cast<size_t>(sl) * G * N + nt * 16 + 4 * q) = dB[nt];
   }
 }
 
@@ -624,9 +624,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
 // heads).  Wave w owns the 16 tokens l of tile w and, per head, accumulates
 //   dC_h[l][n] = e^{cs_l} (dy_l H_in)[n] + sum_{s <= l} W[l][s] B_s[n],
 //   W[l][s] = e^{cs_l - cs_s} delta_s (dy_l . x_s),
-// the scores computed transposed (x_s . dy_l: a lane holds one l and four s,
-// the A operand of the product with B).  Per head: f1_l = C_l . (the H_in
-// part of dC_h[l]); after the group: dC.
+// the scores computed transposed (x_s . dy_l: a lane holds one l and four s),
+// which after the decay are the B operand of dC^T += B^T W^T, so that a lane
+// ends with one row l of dC and 4 consecutive n per tile (16-byte stores).
+// Per head: f1_l = C_l . (the H_in part of dC_h[l]); after the group: dC.
 // ---------------------------------------------------------------------------
 template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
   f32x4 dCg[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) dCg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ll = l0 + 16 * w + r16;  // this lane's target token (A rows)
+  const int ll = l0 + 16 * w + r16;  // this lane's target token (score and dC^T columns)
   auto xbufh = [&](int hh) {
     return make_buf(x + r0 * H * P + static_cast<size_t>(hh) * P,
                     static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
@@ -695,7 +696,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
     // every decay factor below is 2^(cs2_l - cs2_s) <= 1 (s <= l)
     const float cs_l = cs2[ll < Lc ? ll : Lc - 1];
 
-    // boundary: e^{cs_l} dy_l H_in (A rows l = this lane's ll)
+    // dC_h computed transposed, dC^T[n][l]: lane holds column l = ll, rows
+    // n = 16 nt + 4q + i.  Boundary: e^{cs_l} (dy_l H_in)[n] (B columns l = ll)
     f32x4 dC[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) dC[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -708,19 +710,21 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
         for (int nt = 0; nt < NT; ++nt) {
           const uint2 lo = lds_tr4(Hs, NP, ks + 8 * q, nt * 16);
           const uint2 hi = lds_tr4(Hs, NP, ks + 8 * q + 4, nt * 16);
-          dC[nt] = mfma_bf16(as_bf16x8(a), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dC[nt]);
+          dC[nt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(a), dC[nt]);
         }
       }
     }
     // f1_l = e^{cs_l} C_l . (H_in^T dy_l): the H_in part of C_l . dC_h[l]
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lr = 16 * w + 4 * q + i;
+    {
       float pd = 0.0f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) pd += bf16_bits_to_f32(Cs[lr * NP + nt * 16 + r16]) * dC[nt][i];
-      pd = sum16(pd);
-      if (r16 == 15 && l0 + lr < Lc) f1o[(r0 + l0 + lr) * H + h] = pd;
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint2 cc = *reinterpret_cast<const uint2*>(Cs + (16 * w + r16) * NP + nt * 16 + 4 * q);
+        pd += bf16_bits_to_f32(cc.x & 0xFFFFu) * dC[nt][0] + bf16_bits_to_f32(cc.x >> 16) * dC[nt][1] +
+              bf16_bits_to_f32(cc.y & 0xFFFFu) * dC[nt][2] + bf16_bits_to_f32(cc.y >> 16) * dC[nt][3];
+      }
+      pd = group_total(pd);
+      if (q == 0 && ll < Lc) f1o[(r0 + ll) * H + h] = pd;
     }
     for (int sb = 0; sb <= ib; ++sb) {
       const int s0 = sb * kBlk;
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
         for (int nt = 0; nt < NT; ++nt) {
           const uint2 lo = lds_tr4(Bs, NP, 32 * kk + 4 * q, nt * 16);
           const uint2 hi = lds_tr4(Bs, NP, 32 * kk + 16 + 4 * q, nt * 16);
-          dC[nt] = mfma_bf16(as_bf16x8(Aw), as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), dC[nt]);
+          dC[nt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(Aw), dC[nt]);
         }
       }
     }
@@ -792,14 +796,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
       for (int i = 0; i < 4; ++i) dCg[nt][i] += dC[nt][i];
   }
 
+  // lane holds row l = ll, n = 16 nt + 4q .. +3: one 16-byte store per tile
   float* dst = dCp + ((static_cast<size_t>(hgl) * Bsz + b) * T + t0) * G * N + static_cast<size_t>(g) * N;
+  if (ll < Lc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int l = l0 + 16 * w + 4 * q + i;
-    if (l < Lc) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) dst[static_cast<size_t>(l) * G * N + nt * 16 + r16] = dCg[nt][i];
-    }
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f32x4*>(dst + static_cast<size_t>(ll) * G * N + nt * 16 + 4 * q) = dCg[nt];
   }
 }
 
