@@ -163,7 +163,9 @@ __device__ __forceinline__ float transpose_sum16(const float (&v)[16]) {
 // G_c[p][n] = sum_l e^{cs_l} dy_l[p] C_l[n], one workgroup per (batch, chunk,
 // head), computed transposed (D[n][p], contraction over tokens on MFMA with
 // operands from the LDS transpose read) so that a lane holds one p and four
-// consecutive n: 8-byte bf16 stores in the (P, N) layout of the states.
+// consecutive n: 8-byte bf16 stores in the (P, N) layout of the states.  With
+// two n tiles per wave they go in pairs with permuted n (the transpose read's
+// 4-column pieces 8 apart): 8 consecutive n, 16-byte stores.
 // ---------------------------------------------------------------------------
 template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
@@ -171,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
     const float2* __restrict__ tok, uint16_t* __restrict__ adj, int T, int H, int G, int Q, int nc,
     int npairs) {
   constexpr int YP = P + 16, CP = N + 16;
-  constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4;  // wave w: n tiles w, w+4, ..
+  constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4;  // n tiles per wave
+  constexpr bool kPairN = NTW % 2 == 0;  // wave w: n tiles NTW w + i (paired), else w, w + 4, ..
   __shared__ __attribute__((aligned(16))) uint16_t yl[kBlk * YP];  // e^{cs_l} dy_l
   __shared__ __attribute__((aligned(16))) uint16_t cl[kBlk * CP];  // C_l
   __shared__ float wl[256];
@@ -217,9 +220,10 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
       uint4 af[NTW], bf[PT];
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
-        const int nt = wid + 4 * i;
-        const uint2 lo = lds_tr4(cl, CP, ks + 8 * q, nt * 16);
-        const uint2 hi = lds_tr4(cl, CP, ks + 8 * q + 4, nt * 16);
+        const int nt = kPairN ? NTW * wid + i : wid + 4 * i;
+        const int c0 = kPairN ? 32 * (nt >> 1) + 4 * (nt & 1) : nt * 16;
+        const uint2 lo = kPairN ? lds_tr4s<8>(cl, CP, ks + 8 * q, c0) : lds_tr4(cl, CP, ks + 8 * q, c0);
+        const uint2 hi = kPairN ? lds_tr4s<8>(cl, CP, ks + 8 * q + 4, c0) : lds_tr4(cl, CP, ks + 8 * q + 4, c0);
         af[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
 #pragma unroll
@@ -235,14 +239,27 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
     }
   }
   uint16_t* dst = adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N);
+  if constexpr (kPairN) {
 #pragma unroll
-  for (int i = 0; i < NTW; ++i)
+    for (int i = 0; i < NTW; i += 2)
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int nt = wid + 4 * i;
-      *reinterpret_cast<uint2*>(dst + (j * 16 + r16) * N + nt * 16 + 4 * q) =
-          make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
-    }
+      for (int j = 0; j < PT; ++j) {
+        const int m = (NTW * wid + i) >> 1;  // n = 32 m + 8q .. +7
+        *reinterpret_cast<uint4*>(dst + (j * 16 + r16) * N + 32 * m + 8 * q) =
+            make_uint4(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]),
+                       pack_bf16x2(acc[i + 1][j][0], acc[i + 1][j][1]),
+                       pack_bf16x2(acc[i + 1][j][2], acc[i + 1][j][3]));
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int nt = wid + 4 * i;
+        *reinterpret_cast<uint2*>(dst + (j * 16 + r16) * N + nt * 16 + 4 * q) =
+            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -68,6 +68,10 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
   constexpr int NGW = NT / NTW;             // wave groups along n
   constexpr int PGW = WW / NGW;             // wave groups along p
   constexpr int PTW = (PT + PGW - 1) / PGW;
+  // a wave's n tiles in pairs (NTW even): tile (pair m, half) covers n = 32 m +
+  // 4 half + 8 (r / 4) + r % 4 for its MFMA row r, so a lane's rows of the pair
+  // are 8 consecutive n (one 16-byte store of S_c)
+  constexpr bool kPairN = NTW % 2 == 0;
 
   __shared__ __attribute__((aligned(16))) uint16_t xl[HPW][HS * XPn];  // w_s x_s per head
   __shared__ __attribute__((aligned(16))) uint16_t bl[HS * BPn];       // B_s
@@ -176,8 +180,9 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
         const int nt = ng * NTW + i;
-        const uint2 lo = lds_tr4(bl, BPn, ks + 8 * q, nt * 16);
-        const uint2 hi = lds_tr4(bl, BPn, ks + 8 * q + 4, nt * 16);
+        const int c0 = kPairN ? 32 * (nt >> 1) + 4 * (nt & 1) : nt * 16;
+        const uint2 lo = kPairN ? lds_tr4s<8>(bl, BPn, ks + 8 * q, c0) : lds_tr4(bl, BPn, ks + 8 * q, c0);
+        const uint2 hi = kPairN ? lds_tr4s<8>(bl, BPn, ks + 8 * q + 4, c0) : lds_tr4(bl, BPn, ks + 8 * q + 4, c0);
         af[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
 #pragma unroll
@@ -213,20 +218,35 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
       mma(Q - i * HS < HS ? Q - i * HS : HS);
     }
 
-  // S_c: lane holds p = pt*16 + r16, n = nt*16 + 4q .. +3
+  // S_c: lane holds p = pt*16 + r16 and, per pair of n tiles, n = 32 m + 8q .. +7
+  // (else per tile n = nt*16 + 4q .. +3)
 #pragma unroll
   for (int e = 0; e < HPW; ++e) {
     uint16_t* dst = states + ((static_cast<size_t>(b) * nc + c) * H + h0 + e) * (static_cast<size_t>(P) * N);
 #pragma unroll
-    for (int i = 0; i < NTW; ++i)
+    for (int j = 0; j < PTW; ++j) {
+      const int pt = pg * PTW + j;
+      if (pt >= PT) continue;
+      if constexpr (kPairN) {
 #pragma unroll
-      for (int j = 0; j < PTW; ++j) {
-        const int nt = ng * NTW + i, pt = pg * PTW + j;
-        if (pt < PT)
+        for (int i = 0; i < NTW; i += 2) {
+          const int m = (ng * NTW + i) >> 1;
+          *reinterpret_cast<uint4*>(dst + (pt * 16 + r16) * N + 32 * m + 8 * q) =
+              make_uint4(pack_bf16x2(acc[e][i][j][0], acc[e][i][j][1]),
+                         pack_bf16x2(acc[e][i][j][2], acc[e][i][j][3]),
+                         pack_bf16x2(acc[e][i + 1][j][0], acc[e][i + 1][j][1]),
+                         pack_bf16x2(acc[e][i + 1][j][2], acc[e][i + 1][j][3]));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+          const int nt = ng * NTW + i;
           *reinterpret_cast<uint2*>(dst + (pt * 16 + r16) * N + nt * 16 + 4 * q) =
               make_uint2(pack_bf16x2(acc[e][i][j][0], acc[e][i][j][1]),
                          pack_bf16x2(acc[e][i][j][2], acc[e][i][j][3]));
+        }
       }
+    }
   }
 }
 
