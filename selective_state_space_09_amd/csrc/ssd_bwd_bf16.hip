@@ -103,24 +103,6 @@ __device__ __forceinline__ void put_rows(uint16_t* tile, int pitch, const BufSla
   }
 }
 
-// lane move by a DPP row shift; lanes whose source lies outside their row of
-// 16 read zero, so that v + shr<n>(v) folds into one v_add_f32_dpp
-template <int CTRL>
-__device__ __forceinline__ float shr0(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
-}
-
-// sum over the 16 lanes of a lane group (lanes with the same i / 16), left in
-// the group's last lane (r16 = 15): an inclusive scan by DPP row shifts, four
-// VALU adds (cross-lane shuffles go through the LDS crossbar and cost far more)
-__device__ __forceinline__ float sum16(float v) {
-  v += shr0<0x111>(v);  // row_shr:1
-  v += shr0<0x112>(v);  // row_shr:2
-  v += shr0<0x114>(v);  // row_shr:4
-  v += shr0<0x118>(v);  // row_shr:8
-  return v;
-}
-
 // Per column r16, the sum of the values of the four lane groups (rows of 16
 // lanes), in every lane.  The gfx950 row swaps exchange rows 2m <-> 2m+1
 // (permlane16) and the wave's halves (permlane32); each returns the even
