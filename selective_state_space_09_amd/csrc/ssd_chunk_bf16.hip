@@ -346,7 +346,8 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
 // Per 32 source tokens, G^T = B_s . C_l^T on MFMA (C rows in registers,
 // prefetched a sub-chunk ahead) leaves column l in the lane, which after the
 // mask and the weights is the B operand of Y^T += X^T M^T.  For the state
-// update wave w owns n tiles w, w+4, ..: H^T[n][p] += sum_s (w_s B_s[n]) x_s[p]
+// update wave w owns n tiles 2w, 2w+1 with N = 128 (paired, permuted n), else
+// w, w+4, ..: H^T[n][p] += sum_s (w_s B_s[n]) x_s[p]
 // (operands from LDS by the transpose read); a lane holds 4 consecutive n of
 // one p and writes the bf16 state tile with 8-byte stores.
 // ---------------------------------------------------------------------------
@@ -375,6 +376,11 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   auto prow = [](int pt, int r) {
     return kPairP ? 32 * (pt >> 1) + 4 * (pt & 1) + 8 * (r >> 2) + (r & 3) : pt * 16 + r;
   };
+  // State tiles of a wave: n tiles 2w, 2w+1 paired with permuted n when there
+  // are eight (N = 128; a lane's rows of the pair are the 8 consecutive
+  // n = 32w + 8q .. +7: 16-byte loads of h_in and stores of its bf16 copy),
+  // else n tiles w, w + 4, ..
+  constexpr bool kPairS = KT == 8;
 
   __shared__ __attribute__((aligned(16))) uint16_t bt[QSM * BTP];
   __shared__ __attribute__((aligned(16))) uint16_t xl[QSM * XPn];  // raw x
@@ -427,10 +433,17 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   // them before every other load is in flight)
   uint2 hv[KTW][NPT];
 #pragma unroll
-  for (int i = 0; i < KTW; ++i)
+  for (int pt = 0; pt < NPT; ++pt) {
+    if constexpr (kPairS) {
+      const uint4 u = buf_load16(hbuf, ((pt * 16 + r16) * N + 32 * wid + 8 * q) * 2);
+      hv[0][pt] = make_uint2(u.x, u.y);
+      hv[1][pt] = make_uint2(u.z, u.w);
+    } else {
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt)
-      hv[i][pt] = buf_load8(hbuf, ((pt * 16 + r16) * N + (wid + 4 * i) * 16 + 4 * q) * 2);
+      for (int i = 0; i < KTW; ++i)
+        hv[i][pt] = buf_load8(hbuf, ((pt * 16 + r16) * N + (wid + 4 * i) * 16 + 4 * q) * 2);
+    }
+  }
 
   // C rows of this wave's output tile in sub-chunk j: lane (row r16, group q)
   // holds k = ks*32 + 8q .. +7.  Rows past the chunk (and every row of the
@@ -498,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
       const uint2 v = hv[i][pt];
-      hacc[i][pt] = wid + 4 * i < KT
+      hacc[i][pt] = kPairS || wid + 4 * i < KT
                         ? f32x4{bf16_bits_to_f32(v.x & 0xFFFFu), bf16_bits_to_f32(v.x >> 16),
                                 bf16_bits_to_f32(v.y & 0xFFFFu), bf16_bits_to_f32(v.y >> 16)}
                         : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -533,6 +546,17 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   // scale the state by kpre[j] and write its bf16 copy hT[p][n]
   auto store_state = [&](int j) {
     const float k = kpre[j];
+    if constexpr (kPairS) {
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        hacc[0][pt] = hacc[0][pt] * k;
+        hacc[1][pt] = hacc[1][pt] * k;
+        *reinterpret_cast<uint4*>(hT + (pt * 16 + r16) * HTP + 32 * wid + 8 * q) =
+            make_uint4(pack_bf16x2(hacc[0][pt][0], hacc[0][pt][1]), pack_bf16x2(hacc[0][pt][2], hacc[0][pt][3]),
+                       pack_bf16x2(hacc[1][pt][0], hacc[1][pt][1]), pack_bf16x2(hacc[1][pt][2], hacc[1][pt][3]));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KTW; ++i) {
       const int nt = wid + 4 * i;
@@ -689,8 +713,10 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < KTW; ++i) {
           const int nt = wid + 4 * i;
-          const uint2 lo = lds_tr4(bt, BTP, k + 8 * q, (nt < KT ? nt : 0) * 16);
-          const uint2 hi = lds_tr4(bt, BTP, k + 8 * q + 4, (nt < KT ? nt : 0) * 16);
+          const uint2 lo = kPairS ? lds_tr4s<8>(bt, BTP, k + 8 * q, 32 * wid + 4 * i)
+                                  : lds_tr4(bt, BTP, k + 8 * q, (nt < KT ? nt : 0) * 16);
+          const uint2 hi = kPairS ? lds_tr4s<8>(bt, BTP, k + 8 * q + 4, 32 * wid + 4 * i)
+                                  : lds_tr4(bt, BTP, k + 8 * q + 4, (nt < KT ? nt : 0) * 16);
           bfr[i] = scale_bf16x8_each(make_uint4(lo.x, lo.y, hi.x, hi.y), w0, w1);
         }
 #pragma unroll
@@ -700,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
           const uint4 afr = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
           for (int i = 0; i < KTW; ++i)
-            if (wid + 4 * i < KT)
+            if (kPairS || wid + 4 * i < KT)
               hacc[i][pt] = mfma_bf16(as_bf16x8(bfr[i]), as_bf16x8(afr), hacc[i][pt]);
         }
       }
