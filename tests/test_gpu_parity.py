@@ -69,8 +69,8 @@ REAL_CASES = [
     (1, 1, 2, 32, 32, 1, 32, True, True, True),
     (1, 256, 2, 64, 64, 1, 256, True, True, True),
     (3, 513, 4, 64, 128, 1, 256, True, True, True),
-    # 16 chunks: the last size whose boundary states the bf16 output kernel
-    # forms itself; 17 and 18 chunks: the state-passing kernel
+    # 16, 17 and 18 chunks: the state-passing kernels keep 8 chunks in flight
+    # per thread, so these cover two whole groups and a ragged third
     (1, 1024, 2, 64, 128, 1, 64, True, True, True),
     (2, 1100, 2, 64, 128, 1, 64, True, True, True),
     (1, 2100, 4, 32, 64, 2, 128, False, True, True),
