@@ -342,7 +342,9 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
 //
 // The output tile is computed transposed, Y^T[p][l]: wave w owns output rows
 // l = 16w .. 16w+15 of each sub-chunk as accumulator columns, so a lane holds
-// one row l (one scale factor) and four consecutive p (one 8-byte store of y).
+// one row l (one scale factor) and four consecutive p of each tile; the
+// tiles go in pairs with permuted p (P >= 32), so a lane holds 8 consecutive p
+// of a pair: one 16-byte store of y.
 // Per 32 source tokens, G^T = B_s . C_l^T on MFMA (C rows in registers,
 // prefetched a sub-chunk ahead) leaves column l in the lane, which after the
 // mask and the weights is the B operand of Y^T += X^T M^T.  For the state
