@@ -254,38 +254,48 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
 // Inter-chunk state passing (bf16 chunk states in, bf16 boundary states out):
 //   h_in(0) = h0,  h_in(c+1) = lambda_c h_in(c) + S_c,  h_final = h_in(nc)
 // (the chunkwise recurrence of the state across chunks), fp32 running state.
-// One thread per 4 consecutive n of one p of one (batch, head); PF chunks in
-// flight.  h_in(c) overwrites S_c in place (S_c is read before it).
+// One thread per 8 consecutive n of one p of one (batch, head) (16-byte
+// accesses); PF chunks in flight.  h_in(c) overwrites S_c in place (S_c is
+// read before it).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
     uint16_t* __restrict__ states, const float* __restrict__ decay, const float* __restrict__ h0,
     float* __restrict__ h_final, int H, int PN, int nc) {
   constexpr int PF = 8;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int e4 = blockIdx.x * kThreads + threadIdx.x;  // group of 4 elements
-  if (e4 * 4 >= PN) return;
+  const int e8 = blockIdx.x * kThreads + threadIdx.x;  // group of 8 elements
+  if (e8 * 8 >= PN) return;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t cstride = static_cast<size_t>(H) * PN;  // between chunks of one (b, h)
-  uint16_t* base = states + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e4 * 4;
+  uint16_t* base = states + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e8 * 8;
   const float* dc = decay + bh * nc;
-  float4 hv = h0 ? *reinterpret_cast<const float4*>(h0 + bh * PN + e4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float hv[8];
+  if (h0) {
+    const float4 a = *reinterpret_cast<const float4*>(h0 + bh * PN + e8 * 8);
+    const float4 c4 = *reinterpret_cast<const float4*>(h0 + bh * PN + e8 * 8 + 4);
+    hv[0] = a.x; hv[1] = a.y; hv[2] = a.z; hv[3] = a.w;
+    hv[4] = c4.x; hv[5] = c4.y; hv[6] = c4.z; hv[7] = c4.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) hv[k] = 0.0f;
+  }
 
-  uint2 cur[PF];
+  uint4 cur[PF];
   float cd[PF];
 #pragma unroll
   for (int j = 0; j < PF; ++j)
     if (j < nc) {
-      cur[j] = *reinterpret_cast<const uint2*>(base + j * cstride);
+      cur[j] = *reinterpret_cast<const uint4*>(base + j * cstride);
       cd[j] = dc[j];
     }
   for (int c0 = 0; c0 < nc; c0 += PF) {
-    uint2 nxt[PF];
+    uint4 nxt[PF];
     float nd[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int cn = c0 + PF + j;
       if (cn < nc) {
-        nxt[j] = *reinterpret_cast<const uint2*>(base + cn * cstride);
+        nxt[j] = *reinterpret_cast<const uint4*>(base + cn * cstride);
         nd[j] = dc[cn];
       }
     }
@@ -293,14 +303,16 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
     for (int j = 0; j < PF; ++j) {
       const int cc = c0 + j;
       if (cc < nc) {
-        *reinterpret_cast<uint2*>(base + cc * cstride) =
-            make_uint2(pack_bf16x2(hv.x, hv.y), pack_bf16x2(hv.z, hv.w));
+        *reinterpret_cast<uint4*>(base + cc * cstride) =
+            make_uint4(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
+                       pack_bf16x2(hv[6], hv[7]));
         const float l = cd[j];
-        const uint2 s = cur[j];
-        hv.x = l * hv.x + bf16_bits_to_f32(s.x & 0xFFFFu);
-        hv.y = l * hv.y + bf16_bits_to_f32(s.x >> 16);
-        hv.z = l * hv.z + bf16_bits_to_f32(s.y & 0xFFFFu);
-        hv.w = l * hv.w + bf16_bits_to_f32(s.y >> 16);
+        const uint32_t sw[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          hv[2 * k] = l * hv[2 * k] + bf16_bits_to_f32(sw[k] & 0xFFFFu);
+          hv[2 * k + 1] = l * hv[2 * k + 1] + bf16_bits_to_f32(sw[k] >> 16);
+        }
       }
     }
 #pragma unroll
@@ -309,7 +321,10 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
       cd[j] = nd[j];
     }
   }
-  if (h_final) *reinterpret_cast<float4*>(h_final + bh * PN + e4 * 4) = hv;
+  if (h_final) {
+    *reinterpret_cast<float4*>(h_final + bh * PN + e8 * 8) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    *reinterpret_cast<float4*>(h_final + bh * PN + e8 * 8 + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -769,7 +784,7 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_outp
              a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G, a.chunk,
              nc, npairs);
   launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel,
-           dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
+           dim3((P * N / 8 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
            ev ? ev + 2 : nullptr, states, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
            P * N, nc);
   if (!with_output) return hipGetLastError();
