@@ -868,8 +868,14 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
   const double f2v = in ? static_cast<double>(f2[row]) : 0.0;
   double gv = 0.0;  // col_u - row_u of this token
   if (in) {
-    gv = colp[row];
-    for (int jb = 0; jb <= tid / kBlk; ++jb) gv -= rowp[static_cast<size_t>(jb) * BTH + row];
+    // the shares of the column blocks jb <= this token's block (at most 4:
+    // Q <= 256), all loads issued together
+    float rs[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) rs[jb] = jb <= tid / kBlk ? rowp[static_cast<size_t>(jb) * BTH + row] : 0.0f;
+    gv = static_cast<double>(colp[row]);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) gv -= rs[jb];
   }
   // one fp64 block scan of (f1, f2, col - row): DPP wave scans, then the
   // preceding waves' totals; f1's suffix is its total less the prefix before l
