@@ -507,11 +507,14 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
           const int lb4 = l0 + 16 * lt + 4 * q;
           float mv[4], wv[4];
           if constexpr (decltype(masked)::value) {
+            // lb4 + 3 < 256: in the table; entries past the chunk are selected away
+            const float4 c4 = *reinterpret_cast<const float4*>(cs2 + lb4);
+            const float cl[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int l = lb4 + i;
               const bool ok = l >= sl && l < Lc;
-              const float d = ok ? __builtin_amdgcn_exp2f(cs2[min(l, Q - 1)] - cs_s) : 0.0f;
+              const float d = ok ? __builtin_amdgcn_exp2f(cl[i] - cs_s) : 0.0f;
               mv[i] = d * s1[lt][i];
               wv[i] = d * dl_s * s2[lt][i];
               ee[4 * lt + i] = l > sl ? wv[i] * s1[lt][i] : 0.0f;
