@@ -35,9 +35,8 @@ if ROOT not in sys.path:
 
 METRIC = "SSD fwd tokens/s per layer (H64 P64 N128) + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
-# dense MFMA peaks; "f32 as 3 bf16": fp32-precision products computed as three
-# bf16 products (split operands), i.e. a third of the bf16 peak
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "f32 as 3 bf16": 2500.0 / 3}
+# dense MFMA peaks (MI355X datasheet)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
 def parse():
@@ -121,7 +120,7 @@ def source_sha256(workload):
     return h.hexdigest()
 
 
-def copy_reference(torch, dev):
+def copy_counter_reference(torch, dev):
     """One plain 256 MiB device-to-device copy: the reference the HBM byte
     counters are scaled by."""
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -159,9 +158,10 @@ def kernel_segments(cfg):
     return {"ssd_state_kernel": (0, 1), "ssd_pass_kernel": (2, 3), "ssd_scan_kernel": (4, 5)}
 
 
-def kernel_bytes(cfg, dims):
-    """Algorithmic HBM bytes of each kernel of one chunked-forward call: every
-    array the kernel must read or write, counted once."""
+def own_io_bytes(cfg, dims):
+    """Bytes each kernel of one chunked-forward call reads or writes, every
+    array once, workspace arrays (chunk states, token tables) included.  This
+    is a kernel's own traffic, not the algorithmic figure the roofline uses."""
     Bsz, T, H, P, G, N, Q = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N", "Q"))
     cplx = cfg["kind"] in ("complex", "complex_packed")
     es = 2 if cfg.get("dtype") == "bf16" else 4          # x element
@@ -187,22 +187,75 @@ def kernel_bytes(cfg, dims):
         "ssd_state_kernel": x + bc + dt + states + decay,
         "ssd_pass_kernel": 2 * states + decay,
         "ssd_scan_kernel": x + 2 * bc + dt + states + y,
-        "whole_forward": x + 2 * bc + dt + y,
     }
 
 
-def kernel_flops(cfg, dims):
-    """Algorithmic flops: lower-triangle intra-chunk products (C.B^T per head
-    and M.X), chunk states and the C.h_in products."""
+def algorithmic_bytes(cfg, dims):
+    """The whole forward's algorithmic HBM bytes: x, dt, B, C read once and y
+    written once (17.15 KB per token at the BitMamba layer shape)."""
+    Bsz, T, H, P, G, N = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N"))
+    cplx = cfg["kind"] in ("complex", "complex_packed")
+    es = 2 if cfg.get("dtype") == "bf16" else 4
+    bs = 8 if cplx else es
+    return (Bsz * T * H * P * es + 2 * Bsz * T * G * N * bs + Bsz * T * H * 4
+            + Bsz * T * H * P * (4 if cplx else es))
+
+
+def algorithmic_flops(cfg, dims):
+    """Algorithmic matrix flops of one forward, per kernel: the lower
+    triangle of the in-chunk scores C.B^T (once per (batch, chunk, group):
+    heads of a group share it) and of (scores o L).(delta x), the chunk
+    states (2QNP per (batch, chunk, head)) and the carried-state readout
+    C.h_in (2QNP).  Complex, rotation-factored: real products with K = 2N
+    features, no delta factor."""
     Bsz, T, H, P, G, N, Q = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N", "Q"))
     KC = 2 * N if cfg["kind"] in ("complex", "complex_packed") else N
-    units = Bsz * H * (T / Q)                   # (b, chunk, h) units
+    nch = T / Q                                  # chunks (fractional tail as a fraction)
     tri = Q * (Q + 1) / 2
-    scan = units * (2 * tri * KC + 2 * tri * P + 2 * Q * KC * P)
+    units = Bsz * nch * H
+    gunits = Bsz * nch * G
     state = units * 2 * Q * KC * P
-    return {"ssd_scan_kernel": scan, "ssd_state_kernel": state,
-            "ssd_scan_bf16_kernel": scan, "ssd_state_bf16_kernel": state,
-            "ssd_scan_cplx_kernel": scan, "ssd_state_cplx_kernel": state}
+    scan = gunits * 2 * tri * KC + units * (2 * tri * P + 2 * Q * KC * P)
+    return {"ssd_state_kernel": state, "ssd_state_bf16_kernel": state, "ssd_state_cplx_kernel": state,
+            "ssd_scan_kernel": scan, "ssd_scan_bf16_kernel": scan, "ssd_scan_cplx_kernel": scan,
+            "whole_forward": state + scan}
+
+
+def copy_reference(torch, dev, nbytes, flush, reps=10):
+    """A plain device copy moving `nbytes` in all (nbytes/2 read, nbytes/2
+    written), cold (the same flush read before each), timed by HIP events on
+    the current stream: the achievable-HBM reference at the workload's own
+    size.  Returns (median GB/s, bytes moved)."""
+    n = max(1 << 20, int(nbytes) // 2) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    times = []
+    for _ in range(reps + 2):
+        if flush is not None:
+            flush.max()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times[2:]))
+    del src, dst
+    return 2 * n / (ms / 1e3) / 1e9, 2 * n
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (or platform.processor)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(inp, cfg, dims, target_s):
@@ -259,17 +312,33 @@ def cpu_baseline(inp, cfg, dims, target_s):
         while total < target_s:
             total += run_full()
             reps += 1
-        return {"value": reps * Bsz * T / total, "unit": "tokens/s",
-                "cores": oracle.threads_used(), "kind": "oracle",
-                "sample": f"the whole workload ({total_bh} (batch, head) recurrences, T={T}), "
-                          f"float64, {reps} passes in {total:.2f} s"}
-    frac = nh / total_bh
-    tokens_per_s = (Bsz * T * frac) / dt_run
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": oracle.threads_used(),
-            "kind": "oracle",
-            "sample": f"{nh} of {total_bh} (batch, head) recurrences of the same workload, "
-                      f"full length T={T}, float64, {dt_run:.2f} s; tokens/s scaled by the "
-                      f"sampled fraction {nh}/{total_bh}"}
+        out = {"value": reps * Bsz * T / total, "unit": "tokens/s",
+               "cores": oracle.threads_used(), "kind": "oracle",
+               "sample": f"the whole workload ({total_bh} (batch, head) recurrences, T={T}), "
+                         f"float64, {reps} passes in {total:.2f} s"}
+    else:
+        frac = nh / total_bh
+        out = {"value": (Bsz * T * frac) / dt_run, "unit": "tokens/s",
+               "cores": oracle.threads_used(), "kind": "oracle",
+               "sample": f"{nh} of {total_bh} (batch, head) recurrences of the same workload, "
+                         f"full length T={T}, float64, {dt_run:.2f} s; tokens/s scaled by the "
+                         f"sampled fraction {nh}/{total_bh}"}
+    # one thread: (batch, head) recurrences one after another for about a
+    # quarter of the target time
+    oracle.set_threads(1)
+    reps, total = 0, 0.0
+    while total < target_s / 4 and reps < 4 * H:
+        total += run(1)
+        reps += 1
+    oracle.set_threads(threads)
+    out["cpu_model"] = cpu_model()
+    # the workload's Bsz*T tokens take Bsz*H recurrences of T steps: tokens/s
+    # = T / (H * seconds per recurrence)
+    out["one_thread"] = {"value": reps * T / (H * total), "unit": "tokens/s", "cores": 1,
+                         "sample": f"{reps} runs of one (batch, head) recurrence of T={T} "
+                                   f"steps in {total:.2f} s; scaled by the workload's {H} "
+                                   f"recurrences per token"}
+    return out
 
 
 def main():
@@ -335,16 +404,16 @@ def main():
                  float(d["dt_max"]), None, P_(y), None, Bsz, T, H, P, N, Q, P_(ws), ws.numel(), sp)
         call = lambda evarr: L.ssd_complex_chunk_fwd_packed_ev(*fixed, evarr)
         plain = lambda: L.ssd_complex_chunk_fwd_packed(*fixed)
-        dtype_name = "f32"
-        peak_name = "f32 as 3 bf16"
+        dtype_name = "bf16x3"
+        peak_name = "bf16"
     elif cplx:
         fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["dt_bias"]),
                  float(d["dt_min"]), float(d["dt_max"]), None, P_(y), None,
                  Bsz, T, H, P, G, N, Q, P_(ws), ws.numel(), sp)
         call = lambda evarr: L.ssd_complex_chunk_fwd_ev(*fixed, evarr)
         plain = lambda: L.ssd_complex_chunk_fwd(*fixed)
-        dtype_name = "f32"
-        peak_name = "f32 as 3 bf16"
+        dtype_name = "bf16x3"
+        peak_name = "bf16"
     else:
         dcode = ssd.SSD_BF16 if d["x"].dtype == torch.bfloat16 else ssd.SSD_F32
         fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["D"]),
@@ -394,32 +463,48 @@ def main():
     ms = float(np.mean(per_step))
     tokens = Bsz * T
     value = tokens / (ms / 1e3)
-    kb = kernel_bytes(cfg, dims)
-    kf = kernel_flops(cfg, dims)
+    own = own_io_bytes(cfg, dims)
+    kf = algorithmic_flops(cfg, dims)
+    alg = algorithmic_bytes(cfg, dims)
+    # complex products run as three bf16 products each (split operands)
+    flop_mult = 3 if cplx else 1
     kern = {}
     for n in names:
         avg = float(np.mean(per_kernel[n]))
-        gbs = kb[n] / (avg / 1e3) / 1e9
-        ent = {"avg_us": avg * 1e3, "alg_bytes": kb[n], "hbm_gbs": gbs,
-               "hbm_frac": gbs / HBM_PEAK_GBS}
+        ent = {"avg_us": avg * 1e3, "own_io_bytes": own[n],
+               "own_io_gbs": own[n] / (avg / 1e3) / 1e9}
         if n in kf:
-            tf = kf[n] / (avg / 1e3) / 1e12
-            ent.update({"alg_flops": kf[n], "tflops": tf,
-                        "mfma_frac": tf / MFMA_PEAK_TFLOPS[peak_name]})
+            tf = kf[n] * flop_mult / (avg / 1e3) / 1e12
+            ent.update({"alg_flops": kf[n], "mfma_executed_flops": kf[n] * flop_mult,
+                        "mfma_tflops": tf, "mfma_frac": tf / MFMA_PEAK_TFLOPS[peak_name]})
         kern[n] = ent
     dom = max(names, key=lambda n: kern[n]["avg_us"])
-    k = kern[dom]
+    dom_s = kern[dom]["avg_us"] / 1e6
     traffic = measured_traffic(args.workload, dom)
-    if "mfma_frac" in k and k["mfma_frac"] > k["hbm_frac"]:
-        roof = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_PEAK_TFLOPS[peak_name],
-                "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": traffic, "kernel": dom}
-    else:
-        roof = {"bound": "hbm", "achieved": k["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": k["hbm_frac"], "traffic": traffic, "kernel": dom}
-    whole_gbs = kb["whole_forward"] / (ms / 1e3) / 1e9
+    achieved = alg / dom_s / 1e9
+    copy_gbs, copy_bytes = copy_reference(torch, dev, alg, flush)
+    # the roofline: the whole forward's algorithmic bytes (x, dt, B, C in, y
+    # out, once) over the dominant kernel's launch time, against 8 TB/s
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
+            "alg_bytes": alg, "launch_us": dom_s * 1e6,
+            "frac_of_copy": achieved / copy_gbs}
+    if dom in kf:
+        tf = kf[dom] * flop_mult / dom_s / 1e12
+        roof["mfma"] = {"alg_flops": kf[dom], "executed_flops": kf[dom] * flop_mult,
+                        "executed_dtype": "bf16x3" if cplx else dtype_name,
+                        "tflops": tf, "peak": MFMA_PEAK_TFLOPS[peak_name], "unit": "TFLOP/s",
+                        "frac": tf / MFMA_PEAK_TFLOPS[peak_name]}
+        if cplx:
+            f32e = kf[dom] / dom_s / 1e12
+            roof["mfma"]["fp32_equivalent"] = {"tflops": f32e, "peak": MFMA_PEAK_TFLOPS["f32"],
+                                               "frac": f32e / MFMA_PEAK_TFLOPS["f32"]}
+    e2e = alg / (ms / 1e3) / 1e9
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(np.min(per_step)),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype_name, "data": "synthetic",
         "config": {"workload": args.workload, "batch": Bsz, "seq_len": T, "heads": H,
@@ -428,14 +513,17 @@ def main():
                    "separate arrays", "cache": "cold (Infinity Cache flushed between steps)"
                    if flush is not None else "warm"},
         "roofline": roof,
-        "whole_forward": {"alg_bytes": kb["whole_forward"], "hbm_gbs": whole_gbs,
-                          "hbm_frac": whole_gbs / HBM_PEAK_GBS},
+        "end_to_end": {"alg_bytes": alg, "gbs": e2e, "frac": e2e / HBM_PEAK_GBS,
+                       "alg_flops": kf["whole_forward"], "frac_of_copy": e2e / copy_gbs},
+        "achievable_hbm": {"kernel": "device copy (torch copy_)", "bytes_moved": copy_bytes,
+                           "gbs": copy_gbs, "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+                           "cache": "cold" if flush is not None else "warm"},
         "kernels": kern,
         "wall_ms_per_step_incl_flush": t_wall / args.steps * 1e3,
         "ms_per_step_with_kernel_events": float(np.mean(per_step_ev)),
     }
     if args.copy_ref:
-        copy_reference(torch, dev)
+        copy_counter_reference(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, dims, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -504,7 +592,7 @@ def bench_decode(args, cfg):
            "kernels": {kernel: {"avg_us": ms * 1e3, "alg_bytes": nbytes,
                                 "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}}}
     if args.copy_ref:
-        copy_reference(torch, dev)
+        copy_counter_reference(torch, dev)
     print(json.dumps(out), flush=True)
 
 
@@ -599,7 +687,7 @@ def bench_conv(args, cfg):
            "kernels": {kernel: {"avg_us": ms * 1e3, "alg_bytes": nbytes,
                                 "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}}}
     if args.copy_ref:
-        copy_reference(torch, dev)
+        copy_counter_reference(torch, dev)
     if not decode and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_conv(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -665,7 +753,8 @@ def bwd_kernel_costs(dims, nparts):
         "ssd_bwd_dt_sum_kernel": (Bsz * H * nc * 24 + H * 12, 0),
         "ssd_bwd_reduce_kernel(dB)": (part + out, 0),
         "ssd_bwd_reduce_kernel(dC)": (part + out, 0),
-        "whole_backward": (4 * x + 2 * bc + Bsz * T * H * 8 + 2 * out, 0),
+        # x, dy in and dx out; B, C in; dt in and ddt out; dB, dC out (fp32)
+        "whole_backward": (3 * x + 2 * bc + Bsz * T * H * 8 + 2 * out, 0),
     }
 
 
@@ -737,23 +826,27 @@ def bench_bwd(args, cfg):
     for k, name in enumerate(BWD_KERNELS):
         avg = float(np.mean([hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in evs]))
         nb_, fl = costs[name]
-        gbs = nb_ / (avg / 1e3) / 1e9
-        ent = {"avg_us": avg * 1e3, "alg_bytes": nb_, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        ent = {"avg_us": avg * 1e3, "own_io_bytes": nb_, "own_io_gbs": nb_ / (avg / 1e3) / 1e9}
         if fl:
             tf = fl / (avg / 1e3) / 1e12
-            ent.update({"alg_flops": fl, "tflops": tf, "mfma_frac": tf / MFMA_PEAK_TFLOPS["bf16"]})
+            ent.update({"alg_flops": fl, "mfma_tflops": tf,
+                        "mfma_frac": tf / MFMA_PEAK_TFLOPS["bf16"]})
         kern[name] = ent
     ms = float(np.mean(per_step))
     dom = max(kern, key=lambda n: kern[n]["avg_us"])
-    k = kern[dom]
+    dom_s = kern[dom]["avg_us"] / 1e6
     traffic = measured_traffic(args.workload, dom)
-    if "mfma_frac" in k and k["mfma_frac"] > k["hbm_frac"]:
-        roof = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_PEAK_TFLOPS["bf16"],
-                "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": traffic, "kernel": dom}
-    else:
-        roof = {"bound": "hbm", "achieved": k["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": k["hbm_frac"], "traffic": traffic, "kernel": dom}
+    # the roofline: the whole backward's algorithmic bytes (x, dt, B, C, dy in,
+    # dx, ddt, dB, dC out, once) over the dominant kernel's launch time
     whole = costs["whole_backward"][0]
+    achieved = whole / dom_s / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
+            "alg_bytes": whole, "launch_us": dom_s * 1e6}
+    if "alg_flops" in kern[dom]:
+        roof["mfma"] = {"alg_flops": kern[dom]["alg_flops"], "tflops": kern[dom]["mfma_tflops"],
+                        "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                        "frac": kern[dom]["mfma_frac"]}
     out = {
         "metric": "SSD bwd tokens/s per layer (H64 P64 N128, bf16)", "value": Bsz * T / (ms / 1e3),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -763,13 +856,15 @@ def bench_bwd(args, cfg):
                    "headdim": P, "d_state": N, "ngroups": G, "chunk": Q,
                    "cache": "cold (Infinity Cache flushed between steps)"
                    if flush is not None else "warm"},
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(np.min(per_step)),
         "roofline": roof,
-        "whole_backward": {"alg_bytes": whole, "hbm_gbs": whole / (ms / 1e3) / 1e9,
-                           "hbm_frac": whole / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "end_to_end": {"alg_bytes": whole, "gbs": whole / (ms / 1e3) / 1e9,
+                       "frac": whole / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "kernels": kern,
     }
     if args.copy_ref:
-        copy_reference(torch, dev)
+        copy_counter_reference(torch, dev)
     if not args.no_cpu_baseline:
         import oracle
         threads = len(os.sched_getaffinity(0))

@@ -67,7 +67,7 @@ extern "C" {
 /* Supported sizes of the chunked forwards:
  *   P (head dim) in {16, 32, 64, 128}; N (state) in {16, 32, 64, 128} for the
  *   real form and {16, 32, 64} for the complex form; chunk in
- *   {32, 64, 128, 256}; any T >= 0 (a last, shorter chunk is handled as if
+ *   {16, 32, 64, 128, 256}; any T >= 0 (a last, shorter chunk is handled as if
  *   padded with identity steps).  The decode step takes N in
  *   {16, 32, 64, 128, 256} and any P >= 1. */
 

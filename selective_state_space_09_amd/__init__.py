@@ -105,6 +105,24 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _expect(t, name, shape, ref=None):
+    """Shape (and, given a reference tensor, device) check of an optional
+    argument, done before anything reaches the library: a tensor of the wrong
+    shape would make the kernels read or write outside its allocation."""
+    if t is None:
+        return
+    shape = tuple(int(s) for s in shape)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if ref is not None and t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _ndim(t, name, n):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -134,6 +152,19 @@ def ssd_chunk_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=math.
     """Real chunked forward.  x (Bsz,T,H,P) and B, C (Bsz,T,G,N) in float32 or
     bfloat16; dt (Bsz,T,H), A/D/dt_bias (H), h0 (Bsz,H,P,N) float32.
     Returns y (and h_final when asked or given)."""
+    _ndim(x, "x", 4)
+    _ndim(B, "B", 4)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _expect(B, "B", (Bsz, T, G, N), x)
+    _expect(C, "C", (Bsz, T, G, N), x)
+    _expect(dt, "dt", (Bsz, T, H), x)
+    _expect(A, "A", (H,), x)
+    _expect(D, "D", (H,), x)
+    _expect(dt_bias, "dt_bias", (H,), x)
+    _expect(h0, "h0", (Bsz, H, P, N), x)
+    _expect(y, "y", (Bsz, T, H, P), x)
+    _expect(h_final, "h_final", (Bsz, H, P, N), x)
     if x.dtype == torch.bfloat16:
         dtype = SSD_BF16
     elif x.dtype == torch.float32:
@@ -148,8 +179,6 @@ def ssd_chunk_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=math.
     _dev(D, "D", torch.float32)
     _dev(dt_bias, "dt_bias", torch.float32)
     _dev(h0, "h0", torch.float32)
-    Bsz, T, H, P = x.shape
-    G, N = B.shape[2], B.shape[3]
     if y is None:
         y = torch.empty_like(x)
     _dev(y, "y", x.dtype)
@@ -172,6 +201,19 @@ def ssd_complex_chunk_fwd(x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=math.
     (H,2) float32; B, C (Bsz,T,G,N) complex64 or (...,N,2) float32; h0
     likewise.  Returns y = Re(h C) (and h_final as (Bsz,H,P,N,2) float32)."""
     A, B, C, h0 = _pairs(A), _pairs(B), _pairs(C), _pairs(h0)
+    y, h_final = _pairs(y), _pairs(h_final)
+    _ndim(x, "x", 4)
+    _ndim(B, "B", 5)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _expect(B, "B", (Bsz, T, G, N, 2), x)
+    _expect(C, "C", (Bsz, T, G, N, 2), x)
+    _expect(dt, "dt", (Bsz, T, H), x)
+    _expect(A, "A", (H, 2), x)
+    _expect(dt_bias, "dt_bias", (H,), x)
+    _expect(h0, "h0", (Bsz, H, P, N, 2), x)
+    _expect(y, "y", (Bsz, T, H, P), x)
+    _expect(h_final, "h_final", (Bsz, H, P, N, 2), x)
     _dev(x, "x", torch.float32)
     _dev(dt, "dt", torch.float32)
     _dev(A, "A", torch.float32)
@@ -179,8 +221,6 @@ def ssd_complex_chunk_fwd(x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=math.
     _dev(C, "C", torch.float32)
     _dev(dt_bias, "dt_bias", torch.float32)
     _dev(h0, "h0", torch.float32)
-    Bsz, T, H, P = x.shape
-    G, N = B.shape[2], B.shape[3]
     if y is None:
         y = torch.empty_like(x)
     _dev(y, "y", torch.float32)
@@ -201,12 +241,22 @@ def ssd_step_decode(h, x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=
                     y=None, stream=None):
     """One decode step, state h (Bsz,H,P,N) float32 updated in place; x
     (Bsz,H,P), dt (Bsz,H), B/C (Bsz,G,N).  Returns y (Bsz,H,P)."""
+    _ndim(h, "h", 4)
+    _ndim(B, "B", 3)
+    Bsz, H, P, N = h.shape
+    G = B.shape[1]
+    _expect(x, "x", (Bsz, H, P), h)
+    _expect(dt, "dt", (Bsz, H), h)
+    _expect(A, "A", (H,), h)
+    _expect(B, "B", (Bsz, G, N), h)
+    _expect(C, "C", (Bsz, G, N), h)
+    _expect(D, "D", (H,), h)
+    _expect(dt_bias, "dt_bias", (H,), h)
+    _expect(y, "y", (Bsz, H, P), h)
     for t, n in ((h, "h"), (x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C")):
         _dev(t, n, torch.float32)
     _dev(D, "D", torch.float32)
     _dev(dt_bias, "dt_bias", torch.float32)
-    Bsz, H, P, N = h.shape
-    G = B.shape[1]
     if y is None:
         y = torch.empty((Bsz, H, P), dtype=torch.float32, device=h.device)
     _dev(y, "y", torch.float32)
@@ -221,11 +271,22 @@ def ssd_complex_step_decode(h, x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=
     """One complex decode step, state h (Bsz,H,P,N,2) float32 (re, im) updated
     in place; x (Bsz,H,P), dt (Bsz,H), A (H,2), B/C (Bsz,G,N,2).  Returns
     y = Re(C . h) (Bsz,H,P)."""
+    h, A, B, C = _pairs(h), _pairs(A), _pairs(B), _pairs(C)
+    _ndim(h, "h", 5)
+    _ndim(B, "B", 4)
+    Bsz, H, P, N, _ = h.shape
+    G = B.shape[1]
+    _expect(h, "h", (Bsz, H, P, N, 2))
+    _expect(x, "x", (Bsz, H, P), h)
+    _expect(dt, "dt", (Bsz, H), h)
+    _expect(A, "A", (H, 2), h)
+    _expect(B, "B", (Bsz, G, N, 2), h)
+    _expect(C, "C", (Bsz, G, N, 2), h)
+    _expect(dt_bias, "dt_bias", (H,), h)
+    _expect(y, "y", (Bsz, H, P), h)
     for t, n in ((h, "h"), (x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C")):
         _dev(t, n, torch.float32)
     _dev(dt_bias, "dt_bias", torch.float32)
-    Bsz, H, P, N, _ = h.shape
-    G = B.shape[1]
     if y is None:
         y = torch.empty((Bsz, H, P), dtype=torch.float32, device=h.device)
     _dev(y, "y", torch.float32)
@@ -258,10 +319,20 @@ def ssd_conv1d_fwd(xbc, w, HP, GN, bias=None, state_in=None, act=1, x=None, B=No
     float32 or bfloat16 -- split into x (Bsz,T,HP), B and C (Bsz,T,GN).
     w (Ch,4), bias (Ch), state_in/state_out (Bsz,3,Ch) float32.  act 1 = SiLU.
     Returns (x, B, C, state_out); state_out is allocated when not given."""
-    ld = _rows(xbc, "xbc", 3)
+    _ndim(xbc, "xbc", 3)
     Bsz, T, Ch = xbc.shape
     if Ch != HP + 2 * GN:
         raise ValueError(f"xbc has {Ch} channels, HP + 2*GN = {HP + 2 * GN}")
+    _ndim(w, "w", 2)
+    K = w.shape[1]
+    _expect(w, "w", (Ch, K), xbc)
+    _expect(bias, "bias", (Ch,), xbc)
+    _expect(state_in, "state_in", (Bsz, K - 1, Ch), xbc)
+    _expect(state_out, "state_out", (Bsz, K - 1, Ch), xbc)
+    _expect(x, "x", (Bsz, T, HP), xbc)
+    _expect(B, "B", (Bsz, T, GN), xbc)
+    _expect(C, "C", (Bsz, T, GN), xbc)
+    ld = _rows(xbc, "xbc", 3)
     if xbc.dtype == torch.bfloat16:
         dtype = SSD_BF16
     elif xbc.dtype == torch.float32:
@@ -294,6 +365,18 @@ def ssd_conv1d_step(state, xt, w, HP, GN, bias=None, act=1, x=None, B=None, C=No
     """One decode step of the convolution on the float32 state (Bsz,3,Ch),
     updated in place; xt (Bsz,Ch) float32, contiguous or a column slice.
     Returns x (Bsz,HP), B, C (Bsz,GN) float32."""
+    _ndim(xt, "xt", 2)
+    _ndim(w, "w", 2)
+    Bsz, Ch = xt.shape
+    if Ch != HP + 2 * GN:
+        raise ValueError(f"xt has {Ch} channels, HP + 2*GN = {HP + 2 * GN}")
+    K = w.shape[1]
+    _expect(w, "w", (Ch, K), xt)
+    _expect(bias, "bias", (Ch,), xt)
+    _expect(state, "state", (Bsz, K - 1, Ch), xt)
+    _expect(x, "x", (Bsz, HP), xt)
+    _expect(B, "B", (Bsz, GN), xt)
+    _expect(C, "C", (Bsz, GN), xt)
     _dev(state, "state", torch.float32)
     ld = _rows(xt, "xt", 2)
     if xt.dtype != torch.float32:
@@ -325,14 +408,25 @@ def ssd_chunk_bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=m
     """Gradient of sum(dy * y) + <dh_final, h_final> of ssd_chunk_fwd (real
     form, bfloat16 x/B/C/dy).  Returns a dict: dx (x's dtype), ddt, dA, dB,
     dC, dD, ddt_bias and dh0 (float32; dh0 None unless want_dh0)."""
+    _ndim(x, "x", 4)
+    _ndim(B, "B", 4)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _expect(B, "B", (Bsz, T, G, N), x)
+    _expect(C, "C", (Bsz, T, G, N), x)
+    _expect(dy, "dy", (Bsz, T, H, P), x)
+    _expect(dt, "dt", (Bsz, T, H), x)
+    _expect(A, "A", (H,), x)
+    _expect(D, "D", (H,), x)
+    _expect(dt_bias, "dt_bias", (H,), x)
+    _expect(h0, "h0", (Bsz, H, P, N), x)
+    _expect(dh_final, "dh_final", (Bsz, H, P, N), x)
     for t, n in ((x, "x"), (B, "B"), (C, "C"), (dy, "dy")):
         _dev(t, n, torch.bfloat16)
     for t, n in ((dt, "dt"), (A, "A")):
         _dev(t, n, torch.float32)
     for t, n in ((D, "D"), (dt_bias, "dt_bias"), (h0, "h0"), (dh_final, "dh_final")):
         _dev(t, n, torch.float32)
-    Bsz, T, H, P = x.shape
-    G, N = B.shape[2], B.shape[3]
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dx=torch.empty_like(x), ddt=torch.empty((Bsz, T, H), **f32),
@@ -360,16 +454,20 @@ def ssd_complex_chunk_fwd_packed(proj, A, H, P, N, dt_bias=None, dt_min=0.0, dt_
     [x | B_re | B_im | C_re | C_im | dt], head-major, per-head B/C.  proj may
     be a column slice of wider rows (its row stride is passed).  Returns y
     (Bsz,T,H,P) float32 (and h_final (Bsz,H,P,N,2) if return_final_state)."""
-    ld = _rows(proj, "proj", 3)
-    if proj.dtype != torch.float32:
-        raise TypeError("proj must be float32")
+    _ndim(proj, "proj", 3)
     Bsz, T, W = proj.shape
     if W < H * (P + 4 * N + 1):
         raise ValueError(f"proj rows have {W} columns, need {H * (P + 4 * N + 1)}")
-    A = _pairs(A)
+    A, h0, y = _pairs(A), _pairs(h0), _pairs(y)
+    _expect(A, "A", (H, 2), proj)
+    _expect(dt_bias, "dt_bias", (H,), proj)
+    _expect(h0, "h0", (Bsz, H, P, N, 2), proj)
+    _expect(y, "y", (Bsz, T, H, P), proj)
+    ld = _rows(proj, "proj", 3)
+    if proj.dtype != torch.float32:
+        raise TypeError("proj must be float32")
     _dev(A, "A", torch.float32)
     _dev(dt_bias, "dt_bias", torch.float32)
-    h0 = _pairs(h0)
     _dev(h0, "h0", torch.float32)
     dev = proj.device
     if y is None:

@@ -38,7 +38,7 @@ bool in_set(int v, const int* set, int n) {
 const int kPs[] = {16, 32, 64, 128};
 const int kNsReal[] = {16, 32, 64, 128};
 const int kNsCplx[] = {16, 32, 64};
-const int kChunks[] = {32, 64, 128, 256};
+const int kChunks[] = {16, 32, 64, 128, 256};
 const int kNsDecode[] = {16, 32, 64, 128, 256};
 const int kNsCplxDecode[] = {16, 32, 64, 128};
 
@@ -52,7 +52,7 @@ int check_chunk_shape(int Bsz, int T, int H, int P, int G, int N, int chunk, int
   if (is_complex ? !in_set(N, kNsCplx, 3) : !in_set(N, kNsReal, 4))
     return fail(SSD_EUNSUPPORTED, "N=%d not supported (%s)", N,
                 is_complex ? "complex: {16,32,64}" : "real: {16,32,64,128}");
-  if (!in_set(chunk, kChunks, 4)) return fail(SSD_EUNSUPPORTED, "chunk=%d not in {32,64,128,256}", chunk);
+  if (!in_set(chunk, kChunks, 5)) return fail(SSD_EUNSUPPORTED, "chunk=%d not in {16,32,64,128,256}", chunk);
   // 32-bit grid limits and index headroom
   const long long nc = (static_cast<long long>(T) + chunk - 1) / chunk;
   if (nc > 2147483647LL || static_cast<long long>(H) > 65535 || Bsz > 65535)

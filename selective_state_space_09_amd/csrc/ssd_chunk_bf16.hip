@@ -485,10 +485,10 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   bs.load(bbuf, brow, 0);
 
   // ---- prologue: per-token values, per-sub-chunk factors ----
-  if (tid < Q) {
-    cs[tid] = tv.x;
-    dl[tid] = tv.y;
-  }
+  // (entries past the chunk are zero: with chunk 16 the diagonal block pair
+  // reads the weights of tokens 16..31 into a product it then discards)
+  cs[tid] = tid < Q ? tv.x : 0.0f;
+  dl[tid] = tid < Q ? tv.y : 0.0f;
   __syncthreads();
   // exponent of token t (t = -1: 0)
   auto csd = [&](int t) -> float { return t < 0 ? 0.0f : cs[t]; };
@@ -500,6 +500,8 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   __syncthreads();
   // uniform over the workgroup; scalar so that its branches keep EXEC whole
   const bool exact = __builtin_amdgcn_readfirstlane(exact_flag) != 0;
+  csc[tid] = 0.0f;
+  xsc[tid] = 0.0f;
   if (tid < Q) {
     const int j0 = tid & ~(QS - 1), m = j0 + QS / 2 - 1, j1 = j0 + QS - 1;
     const float e = csd(tid);

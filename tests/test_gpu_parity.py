@@ -15,7 +15,7 @@ import torch
 import oracle
 import selective_state_space_09_amd as ssd
 from selective_state_space_09_amd import inputs
-from _metrics import y_err, state_err
+from _metrics import y_err, state_err, report
 import _gpu
 
 pytestmark = pytest.mark.gpu
@@ -74,6 +74,9 @@ REAL_CASES = [
     (1, 1024, 2, 64, 128, 1, 64, True, True, True),
     (2, 1100, 2, 64, 128, 1, 64, True, True, True),
     (1, 2100, 4, 32, 64, 2, 128, False, True, True),
+    # chunk 16: one output row tile per chunk, many chunks
+    (2, 200, 2, 64, 128, 1, 16, True, True, True),
+    (1, 37, 3, 32, 16, 3, 16, False, True, True),
 ]
 
 
@@ -87,8 +90,8 @@ def test_real_small(case, dtype):
     y, hf = _gpu.run_real(inp, Q)
     yr, hr = _oracle_real(inp)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    assert y_err(y, yr) < tol
-    assert state_err(hf, hr) < tol
+    assert report("y", y, yr) < tol
+    assert report("h_final", hf, hr, "state") < tol
 
 
 COMPLEX_CASES = [
@@ -100,6 +103,8 @@ COMPLEX_CASES = [
     (2, 65, 2, 128, 16, 2, 64, True),
     (1, 1, 2, 32, 32, 2, 32, True),
     (2, 512, 4, 64, 64, 4, 256, True),
+    (1, 150, 2, 64, 64, 2, 16, True),
+    (2, 33, 2, 32, 32, 1, 16, False),
 ]
 
 
@@ -110,8 +115,8 @@ def test_complex_small(case):
     inp = inputs.make_complex(Bsz, T, H, P, N, G, seed=9, with_h0=with_h0)
     y, hf = _gpu.run_complex(inp, Q)
     yr, hr = _oracle_cplx(inp)
-    assert y_err(y, yr) < TOL_F32
-    assert state_err(hf, hr) < TOL_F32
+    assert report("y", y, yr) < TOL_F32
+    assert report("h_final", hf, hr, "state") < TOL_F32
 
 
 def test_tiny_workload_full():
@@ -120,8 +125,8 @@ def test_tiny_workload_full():
     inp = inputs.make_workload("tiny_f32")
     y, hf = _gpu.run_real(inp, cfg["chunk"])
     yr, hr = _oracle_real(inp)
-    assert y_err(y, yr) < TOL_F32
-    assert state_err(hf, hr) < TOL_F32
+    assert report("y", y, yr) < TOL_F32
+    assert report("h_final", hf, hr, "state") < TOL_F32
 
 
 # --------------------------------------------------------------------------
@@ -155,7 +160,7 @@ def test_vanishing_step_freezes_state():
     y, hf = _gpu.run_real(inp, 64)
     np.testing.assert_array_equal(hf, inp["h0"].astype(np.float64))
     yr, _ = _oracle_real(inp)
-    assert y_err(y, yr) < TOL_F32
+    assert report("y", y, yr) < TOL_F32
 
 
 def test_deterministic():
@@ -174,10 +179,10 @@ def test_chunk_size_invariance_on_gpu():
     _print_case(edge="chunk sweep")
     inp = inputs.make_real(1, 333, 2, 32, 64, 1, seed=6, with_h0=True)
     yr, hr = _oracle_real(inp)
-    for Q in (32, 64, 128, 256):
+    for Q in (16, 32, 64, 128, 256):
         y, hf = _gpu.run_real(inp, Q)
-        assert y_err(y, yr) < TOL_F32, Q
-        assert state_err(hf, hr) < TOL_F32, Q
+        assert report("y Q=%d" % Q, y, yr) < TOL_F32, Q
+        assert report("h_final Q=%d" % Q, hf, hr, "state") < TOL_F32, Q
 
 
 def test_chained_calls_equal_one_call():
@@ -194,8 +199,8 @@ def test_chained_calls_equal_one_call():
     second["h0"] = h1.astype(np.float32)
     y2, h2 = _gpu.run_real(second, 128)
     yr, hr = _oracle_real(inp)
-    assert y_err(np.concatenate([y1, y2], axis=1), yr) < TOL_F32
-    assert state_err(h2, hr) < TOL_F32
+    assert report("y", np.concatenate([y1, y2], axis=1), yr) < TOL_F32
+    assert report("state", h2, hr, "state") < TOL_F32
 
 
 def test_workspace_contents_do_not_matter():
@@ -216,8 +221,8 @@ def test_workspace_contents_do_not_matter():
         torch.cuda.synchronize()
         outs.append((_gpu.to_host64(y), _gpu.to_host64(hf)))
     yr, hr = _oracle_real(inp)
-    assert y_err(outs[0][0], yr) < TOL_BF16
-    assert state_err(outs[0][1], hr) < TOL_BF16
+    assert report("y", outs[0][0], yr) < TOL_BF16
+    assert report("state", outs[0][1], hr, "state") < TOL_BF16
     for y, hf in outs[1:]:
         np.testing.assert_array_equal(y, outs[0][0])
         np.testing.assert_array_equal(hf, outs[0][1])
@@ -241,8 +246,8 @@ def test_bitmamba_workload_full():
     inp = inputs.make_workload("bitmamba_bf16")
     y, hf = _gpu.run_real(inp, cfg["chunk"])
     yr, hr = _oracle_real(inp)
-    assert y_err(y, yr) < TOL_BF16
-    assert state_err(hf, hr) < TOL_BF16
+    assert report("y", y, yr) < TOL_BF16
+    assert report("h_final", hf, hr, "state") < TOL_BF16
 
 
 def test_mamba3lite_complex_workload_full():
@@ -251,8 +256,8 @@ def test_mamba3lite_complex_workload_full():
     inp = inputs.make_workload("mamba3lite_complex")
     y, hf = _gpu.run_complex(inp, cfg["chunk"])
     yr, hr = _oracle_cplx(inp)
-    assert y_err(y, yr) < TOL_F32
-    assert state_err(hf, hr) < TOL_F32
+    assert report("y", y, yr) < TOL_F32
+    assert report("h_final", hf, hr, "state") < TOL_F32
 
 
 def test_long_workload_sampled_heads():
@@ -264,14 +269,16 @@ def test_long_workload_sampled_heads():
                               d["dt_min"], d["dt_max"], None, chunk=cfg["chunk"],
                               return_final_state=True)
     torch.cuda.synchronize()
-    heads = [0, 17, 42, 63]
+    # 16 of the 64 heads: every fourth, offset so both ends and the middle
+    # of the head range (and both halves of each XCD group) are covered
+    heads = [0, 5, 9, 13, 17, 21, 26, 30, 33, 37, 42, 46, 50, 54, 59, 63]
     ys = _gpu.to_host64(y[:, :, heads].contiguous())
     hs = _gpu.to_host64(hf[:, heads].contiguous())
     del d, y, hf
     sub = _head_slice(inp, heads)
     yr, hr = _oracle_real(sub)
-    assert y_err(ys, yr) < TOL_BF16
-    assert state_err(hs, hr) < TOL_BF16
+    assert report("y (16 heads)", ys, yr) < TOL_BF16
+    assert report("h_final (16 heads)", hs, hr, "state") < TOL_BF16
 
 
 def test_decode_workload_64_steps():
@@ -313,8 +320,8 @@ def test_decode_small_shapes():
             torch.cuda.synchronize()
             yr = oracle.step(href, st["x"], st["dt"], inp["A"], st["B"], st["C"], inp["D"],
                              inp["dt_bias"], inp["dt_min"], inp["dt_max"])
-            assert state_err(y.cpu().numpy(), yr) < TOL_F32
-            assert state_err(h.cpu().numpy(), href) < TOL_F32
+            assert report("y", y.cpu().numpy(), yr, "state") < TOL_F32
+            assert report("state", h.cpu().numpy(), href, "state") < TOL_F32
 
 
 def _cdecode_step_dev(h, st, A, bias, inp):
@@ -363,8 +370,8 @@ def test_complex_decode_small_shapes():
             y = _cdecode_step_dev(h, st, A, b_dev, inp)
             yr = oracle.complex_step(href, st["x"], st["dt"], inp["A"], st["B"], st["C"], bias,
                                      inp["dt_min"], inp["dt_max"])
-            assert state_err(y.cpu().numpy(), yr) < TOL_F32
-            assert state_err(h.cpu().numpy(), href) < TOL_F32
+            assert report("y", y.cpu().numpy(), yr, "state") < TOL_F32
+            assert report("state", h.cpu().numpy(), href, "state") < TOL_F32
 
 
 def test_complex_decode_continues_forward():
@@ -384,8 +391,8 @@ def test_complex_decode_continues_forward():
     for t in range(T0, 300):
         st = {n: np.ascontiguousarray(inp[n][:, t]) for n in ("x", "dt", "B", "C")}
         y = _cdecode_step_dev(h, st, A, None, inp)
-        assert state_err(y.cpu().numpy(), yr[:, t]) < TOL_F32
-    assert state_err(h.cpu().numpy(), hr) < TOL_F32
+        assert report("y", y.cpu().numpy(), yr[:, t], "state") < TOL_F32
+    assert report("state", h.cpu().numpy(), hr, "state") < TOL_F32
 
 
 def test_decode_continues_forward():
@@ -406,8 +413,8 @@ def test_decode_continues_forward():
                                 d["B"][:, t].contiguous(), d["C"][:, t].contiguous(), d["D"],
                                 d["dt_bias"], inp["dt_min"], inp["dt_max"])
         torch.cuda.synchronize()
-        assert state_err(y.cpu().numpy(), yr[:, t]) < TOL_F32
-    assert state_err(h.cpu().numpy(), hr) < TOL_F32
+        assert report("y", y.cpu().numpy(), yr[:, t], "state") < TOL_F32
+    assert report("state", h.cpu().numpy(), hr, "state") < TOL_F32
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -423,8 +430,8 @@ def test_steep_decay(dtype):
     y, hf = _gpu.run_real(inp, 256)
     yr, hr = _oracle_real(inp)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
-    assert y_err(y, yr) < tol
-    assert state_err(hf, hr) < tol
+    assert report("y", y, yr) < tol
+    assert report("state", hf, hr, "state") < tol
 
 
 def test_mixed_decay_modes():
@@ -436,5 +443,5 @@ def test_mixed_decay_modes():
     inp["dt"][:, 256:] += 4.0  # second chunk: steps near 1, steep decay
     y, hf = _gpu.run_real(inp, 256)
     yr, hr = _oracle_real(inp)
-    assert y_err(y, yr) < TOL_BF16
-    assert state_err(hf, hr) < TOL_BF16
+    assert report("y", y, yr) < TOL_BF16
+    assert report("state", hf, hr, "state") < TOL_BF16
