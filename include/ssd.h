@@ -133,6 +133,32 @@ int ssd_complex_chunk_fwd(const float *x, const float *dt, const float *A,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * Allocation-free variant of ssd_chunk_fwd, for callers that cannot call
+ * hipMalloc or take a workspace argument: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid device allocation.  Same
+ * arguments, kernels and results as ssd_chunk_fwd without the workspace:
+ * the chunk states, decays and per-token tables live in a scratch array of
+ * SSD_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call there).  The call allocates nothing.
+ *   - A shape whose workspace (ssd_workspace_size(..., 0)) exceeds
+ *     SSD_NOALLOC_SCRATCH_BYTES is rejected with SSD_EWORKSPACE before any
+ *     HIP call.
+ *   - Every call on one GPU shares that GPU's scratch array; calls whose
+ *     work overlaps on one GPU (two streams, two host threads) race on it.
+ *     Calls on one stream are ordered and safe.
+ *   - The scratch contents left by an earlier call do not matter (nothing
+ *     in it must start at zero).
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int ssd_chunk_fwd_noalloc(const void *x, const float *dt, const float *A,
+                          const void *B, const void *C, const float *D,
+                          const float *dt_bias, float dt_min, float dt_max,
+                          const float *h0, void *y, float *h_final, int Bsz,
+                          int T, int H, int P, int G, int N, int chunk,
+                          int dtype, void *stream);
+
+/*
  * Measurement variants of the two chunked forwards: identical arguments,
  * kernels and results, plus `events`, an array of 6 hipEvent_t (passed as
  * void*): the start and stop of the chunk-state kernel, of the inter-chunk

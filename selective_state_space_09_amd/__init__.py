@@ -48,6 +48,9 @@ def lib():
     L.ssd_complex_chunk_fwd.restype = I
     L.ssd_complex_chunk_fwd.argtypes = [P, P, P, P, P, P, F, F, P, P, P,
                                         I, I, I, I, I, I, I, P, S, P]
+    L.ssd_chunk_fwd_noalloc.restype = I
+    L.ssd_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P,
+                                        I, I, I, I, I, I, I, I, P]
     L.ssd_chunk_fwd_ev.restype = I
     L.ssd_chunk_fwd_ev.argtypes = L.ssd_chunk_fwd.argtypes + [P]
     L.ssd_complex_chunk_fwd_ev.restype = I
@@ -191,6 +194,46 @@ def ssd_chunk_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=math.
                                _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0),
                                _ptr(y), _ptr(h_final), Bsz, T, H, P, G, N, chunk, dtype,
                                _ptr(ws), ws.numel(), _stream(stream)))
+    return (y, h_final) if h_final is not None else y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def ssd_chunk_fwd_noalloc(x, dt, A, B, C, y, D=None, dt_bias=None, dt_min=0.0,
+                          dt_max=math.inf, h0=None, h_final=None, chunk=256, stream=None):
+    """ssd_chunk_fwd without a workspace: the library's per-GPU scratch array
+    holds the chunk states (shapes whose workspace exceeds 64 MiB are
+    rejected).  The caller passes y (and h_final when wanted); nothing is
+    allocated.  Calls that overlap on one GPU race on the scratch array."""
+    _ndim(x, "x", 4)
+    _ndim(B, "B", 4)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _expect(B, "B", (Bsz, T, G, N), x)
+    _expect(C, "C", (Bsz, T, G, N), x)
+    _expect(dt, "dt", (Bsz, T, H), x)
+    _expect(A, "A", (H,), x)
+    _expect(D, "D", (H,), x)
+    _expect(dt_bias, "dt_bias", (H,), x)
+    _expect(h0, "h0", (Bsz, H, P, N), x)
+    _expect(y, "y", (Bsz, T, H, P), x)
+    _expect(h_final, "h_final", (Bsz, H, P, N), x)
+    if x.dtype == torch.bfloat16:
+        dtype = SSD_BF16
+    elif x.dtype == torch.float32:
+        dtype = SSD_F32
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    for t, n in ((x, "x"), (B, "B"), (C, "C"), (y, "y")):
+        _dev(t, n, x.dtype)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D"), (dt_bias, "dt_bias"), (h0, "h0"),
+                 (h_final, "h_final")):
+        _dev(t, n, torch.float32)
+    _check(lib().ssd_chunk_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0),
+                                       _ptr(y), _ptr(h_final), Bsz, T, H, P, G, N, chunk, dtype,
+                                       _stream(stream)))
     return (y, h_final) if h_final is not None else y
 
 

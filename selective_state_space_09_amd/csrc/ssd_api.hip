@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/ssd.h"
 #include "ssd_internal.h"
 
@@ -119,11 +121,15 @@ size_t ssd_workspace_size(int Bsz, int T, int H, int P, int G, int N, int chunk,
   return workspace_bytes_for(Bsz, T, H, P, N, chunk, is_complex);
 }
 
-int ssd_chunk_fwd_ev(const void* x, const float* dt, const float* A, const void* B,
-                     const void* C, const float* D, const float* dt_bias, float dt_min,
-                     float dt_max, const float* h0, void* y, float* h_final, int Bsz, int T,
-                     int H, int P, int G, int N, int chunk, int dtype, void* workspace,
-                     size_t workspace_bytes, void* stream, void* const* events) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of the real chunked forward other than the workspace.
+int check_real_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                   const float* D, const float* dt_bias, float dt_min, float dt_max,
+                   const float* h0, const void* y, const float* h_final, int Bsz, int T, int H,
+                   int P, int G, int N, int chunk, int dtype) {
   SSD_TRY(check_chunk_shape(Bsz, T, H, P, G, N, chunk, 0));
   if (dtype != SSD_F32 && dtype != SSD_BF16)
     return fail(SSD_EUNSUPPORTED, "dtype=%d is neither SSD_F32 nor SSD_BF16", dtype);
@@ -138,7 +144,20 @@ int ssd_chunk_fwd_ev(const void* x, const float* dt, const float* A, const void*
   SSD_TRY(check_ptr(dt_bias, "dt_bias", 4, false));
   SSD_TRY(check_ptr(h0, "h0", 16, false));
   SSD_TRY(check_ptr(h_final, "h_final", 16, false));
-  SSD_TRY(check_clamp(dt_min, dt_max));
+  return check_clamp(dt_min, dt_max);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_chunk_fwd_ev(const void* x, const float* dt, const float* A, const void* B,
+                     const void* C, const float* D, const float* dt_bias, float dt_min,
+                     float dt_max, const float* h0, void* y, float* h_final, int Bsz, int T,
+                     int H, int P, int G, int N, int chunk, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream, void* const* events) {
+  SSD_TRY(check_real_fwd(x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final, Bsz, T, H,
+                         P, G, N, chunk, dtype));
   const size_t need = workspace_bytes_for(Bsz, T, H, P, N, chunk, 0);
   SSD_TRY(check_ptr(workspace, "workspace", 256, true));
   if (workspace_bytes < need)
@@ -156,6 +175,67 @@ int ssd_chunk_fwd(const void* x, const float* dt, const float* A, const void* B,
                   void* stream) {
   return ssd_chunk_fwd_ev(x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final, Bsz, T,
                           H, P, G, N, chunk, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free forward ----
+
+// Scratch memory of ssd_chunk_fwd_noalloc.  Each GPU the library runs on
+// holds its own copy of this array (at its own address) until the process
+// ends.  Host code never uses the array's name as a device address: the
+// address is looked up per device (hipGetSymbolAddress) and kept below.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up on the
+// first call there.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSD_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SSD_EUNSUPPORTED, "device %d: the scratch table holds %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SSD_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_chunk_fwd_noalloc(const void* x, const float* dt, const float* A, const void* B,
+                          const void* C, const float* D, const float* dt_bias, float dt_min,
+                          float dt_max, const float* h0, void* y, float* h_final, int Bsz,
+                          int T, int H, int P, int G, int N, int chunk, int dtype,
+                          void* stream) {
+  SSD_TRY(check_real_fwd(x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final, Bsz, T, H,
+                         P, G, N, chunk, dtype));
+  const size_t need = workspace_bytes_for(Bsz, T, H, P, N, chunk, 0);
+  if (need > SSD_NOALLOC_SCRATCH_BYTES)
+    return fail(SSD_EWORKSPACE,
+                "this shape needs %zu bytes of scratch; the allocation-free forward holds %llu "
+                "(use ssd_chunk_fwd with a workspace)",
+                need, static_cast<unsigned long long>(SSD_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  SSD_TRY(scratch_of_current_device(&ws));
+  ssd::ChunkArgs a{x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final,
+                   Bsz, T, H, P, G, N, chunk, dtype, ws, nullptr};
+  return launch_status(ssd::run_chunk_real(a, static_cast<hipStream_t>(stream)));
 }
 
 int ssd_complex_chunk_fwd_ev(const float* x, const float* dt, const float* A, const float* B,

@@ -212,3 +212,30 @@ def test_complex_packed_rejects():
     assert rc == ssd.SSD_EINVAL and "proj is not 16-byte aligned" in msg
     rc, msg = call(N=128)
     assert rc == ssd.SSD_EUNSUPPORTED
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_without_device_use():
+    """The allocation-free forward refuses a shape whose workspace exceeds its
+    64 MiB scratch array, before any HIP call (this host has no GPU), and
+    names the limit."""
+    L = ssd.lib()
+    # B1 T65536 H64 P64 N128 (the long workload): ~540 MB of chunk states
+    rc = L.ssd_chunk_fwd_noalloc(GOOD, GOOD, GOOD, GOOD, GOOD, None, None, 0.0, 1.0, None, GOOD,
+                                 None, 1, 65536, 64, 64, 1, 128, 256, ssd.SSD_BF16, None)
+    msg = L.ssd_last_error().decode()
+    assert rc == ssd.SSD_EWORKSPACE, (rc, msg)
+    assert str(64 << 20) in msg and "scratch" in msg
+    assert ssd.ssd_workspace_size(1, 65536, 64, 64, 1, 128, 256) > ssd.NOALLOC_SCRATCH_BYTES
+    # the same argument checks as ssd_chunk_fwd run first
+    rc = L.ssd_chunk_fwd_noalloc(GOOD, GOOD, GOOD, GOOD, GOOD, None, None, 0.0, 1.0, None, GOOD,
+                                 None, 1, 64, 2, 16, 1, 16, 48, ssd.SSD_BF16, None)
+    assert rc == ssd.SSD_EUNSUPPORTED
+    rc = L.ssd_chunk_fwd_noalloc(GOOD, GOOD, GOOD, MISALIGNED, GOOD, None, None, 0.0, 1.0, None,
+                                 GOOD, None, 1, 64, 2, 16, 1, 16, 64, ssd.SSD_BF16, None)
+    assert rc == ssd.SSD_EINVAL and "B is not 16-byte aligned" in L.ssd_last_error().decode()
+
+
+def test_noalloc_scratch_covers_the_bitmamba_shape():
+    """The BitMamba layer shape (B2 T2048 H64 P64 N128, chunk 256) fits the
+    allocation-free forward's scratch array."""
+    assert ssd.ssd_workspace_size(2, 2048, 64, 64, 1, 128, 256) <= ssd.NOALLOC_SCRATCH_BYTES
