@@ -77,6 +77,9 @@ int check_clamp(float lo, float hi) {
   return SSD_OK;
 }
 
+// Workspace of a chunked forward.  The real form covers both of its paths
+// (float32: per-chunk fp32 states, decays and token table; bfloat16: the
+// segment layout of ssd_internal.h), since the size query takes no dtype.
 size_t workspace_bytes_for(int Bsz, int T, int H, int P, int N, int chunk, int is_complex) {
   const int nc = (T + chunk - 1) / chunk;
   const int KC = is_complex ? 2 * N : N;
@@ -84,7 +87,12 @@ size_t workspace_bytes_for(int Bsz, int T, int H, int P, int N, int chunk, int i
                         ssd::workspace_decay_floats(Bsz, nc, H) +
                         (is_complex ? ssd::workspace_cplx_token_floats(Bsz, nc, H, chunk)
                                     : ssd::workspace_token_floats(Bsz, nc, H, chunk));
-  const size_t bytes = floats * sizeof(float);
+  size_t bytes = floats * sizeof(float);
+  if (!is_complex) {
+    const size_t b16 =
+        ssd::bf16_fwd_layout(Bsz, nc, H, P, N, chunk, ssd::bf16_segment_chunks(Bsz, nc, H, chunk)).total;
+    if (b16 > bytes) bytes = b16;
+  }
   return (bytes + 255) / 256 * 256 + 256;
 }
 

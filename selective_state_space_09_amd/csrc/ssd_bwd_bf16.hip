@@ -984,9 +984,7 @@ static BwdLayout bwd_layout(int Bsz, int T, int H, int P, int G, int N, int chun
   const int nc = (T + chunk - 1) / chunk;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   BwdLayout L{};
-  const size_t fwd_floats = workspace_state_floats(Bsz, nc, H, P, N) + workspace_decay_floats(Bsz, nc, H) +
-                            workspace_token_floats(Bsz, nc, H, chunk);
-  size_t o = up(fwd_floats * 4);
+  size_t o = up(bf16_fwd_layout(Bsz, nc, H, P, N, chunk, 1).total);
   L.fwd = 0;
   L.adj = o;
   o += up(static_cast<size_t>(Bsz) * nc * H * P * N * 2);
@@ -1051,9 +1049,10 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   f.events = const_cast<hipEvent_t*>(ev);
   hipError_t e = run_chunk_states_bf16(f, st);
   if (e != hipSuccess) return e;
-  const uint16_t* states = reinterpret_cast<const uint16_t*>(ws);
-  const float* decay = reinterpret_cast<const float*>(ws) + workspace_state_floats(a.Bsz, nc, a.H, P, N);
-  const float2* tok = reinterpret_cast<const float2*>(decay + workspace_decay_floats(a.Bsz, nc, a.H));
+  const Bf16FwdLayout FL = bf16_fwd_layout(a.Bsz, nc, a.H, P, N, Q, 1);
+  const uint16_t* states = reinterpret_cast<const uint16_t*>(ws + FL.Hin);  // h_in(c), bf16
+  const float* decay = reinterpret_cast<const float*>(ws + FL.decay);
+  const float2* tok = reinterpret_cast<const float2*>(ws + FL.tok);
   uint16_t* adj = reinterpret_cast<uint16_t*>(ws + L.adj);
   float* f1 = reinterpret_cast<float*>(ws + L.f1);
   float* f2 = reinterpret_cast<float*>(ws + L.f2);

@@ -1,16 +1,30 @@
 // Chunked SSD forward on gfx950 for bfloat16 x, B, C (real Mamba-2 form; fp32
 // state and accumulation), in three kernels:
-//   ssd_state_bf16_kernel  each chunk's own state S_c and decay, per (batch,
-//                          chunk, head);
-//   ssd_pass_bf16_kernel   the boundary states h_in(c) and the final state;
-//   ssd_scan_bf16_kernel   chunk outputs from h_in(c), per (batch, chunk, head).
+//   ssd_state_bf16_kernel  the end state of each segment of K chunks from a
+//                          zero start, and its decay, per (batch, segment,
+//                          head pair);
+//   ssd_pass_bf16_kernel   the states entering each segment and the final
+//                          state;
+//   ssd_scan_bf16_kernel   the outputs of a segment from the state entering
+//                          it, per (batch, segment, head).
 // (Numerical Stability in Mamba-3-Lite, section 4: the chunkwise form with
 // L[l,s] = exp(cs_l - cs_s) 1[l >= s] inside a chunk and the chunk's total
 // log-decay carrying the state from one chunk to the next.)
 //
-// Both kernels stage token rows into LDS in their natural row-major layout
-// (16-byte stores) and read MFMA operands whose contraction runs over tokens
+// A segment is K consecutive chunks of one (batch, head) (the workspace
+// layout and the choice of K are in ssd_internal.h): both chunk kernels walk
+// its chunks in order and carry the state between them in fp32 matrix-core
+// accumulators, so states go through memory only at segment ends.  Cumulative
+// decay exponents restart at every chunk (each exponent difference the
+// kernels form lies inside one chunk, or is a chunk total), so K does not
+// change the arithmetic's accuracy; results equal those of K = 1 up to
+// rounding order.
+//
+// Token rows are staged into LDS in their natural row-major layout (16-byte
+// stores); matrix-core operands whose contraction runs over tokens are read
 // with the gfx950 LDS transpose read ds_read_b64_tr_b16.
+
+#include <type_traits>
 
 #include "ssd_chunk_common.h"
 
@@ -33,32 +47,34 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+template <int S>
+using Slot = std::integral_constant<int, S>;
+
 // ---------------------------------------------------------------------------
-// Chunk states from a zero start, one workgroup per (batch, chunk, HPW heads
-// of one group):
-//   S_c[p][n] = sum_s x_s[p] e^{A (u_c - u_s)} delta_s B_s[n],
-//   lambda_c  = e^{A u_c},
-// u_s = delta_1 + .. + delta_s over the chunk and u_c its total (the chunk's
-// own contribution to the state at its end, and its decay; the state-passing
-// kernel chains them).  The heads of a workgroup share their B rows: B is
-// staged once and its MFMA operands are read once for all of them (HPW = 2
-// when the heads of a group pair up, which also halves the grid so that one
-// round of workgroups covers it at the BitMamba shape).  The chunk is staged
-// through LDS in quarters of up to 64 tokens, loaded into registers two
-// quarters ahead.  The decay weight goes onto x (P columns) as it is staged.
-// Eight waves; wave w owns n tiles 2(w%4), 2(w%4)+1 and p tiles 2(w/4),
-// 2(w/4)+1 of the transposed product D[n][p] = sum_s B_s[n] (w_s x_s[p]) of
-// every head, so an accumulator lane holds one p and four consecutive n: one
-// 8-byte store of S_c (bf16; the output kernel rounds the carried state to
-// bf16 for its MFMA in any case).  The exponent sums are fp32 (a wave DPP
-// scan): a sum of at most 256 positive steps carries a relative error of ~1e-6.
+// Segment end states from a zero start, one workgroup per (batch, segment,
+// HPW heads of one group).  For each chunk c of the segment, with u_s = delta_1
+// + .. + delta_s over the chunk and u_c its total:
+//   S_c[p][n] = sum_s x_s[p] e^{A (u_c - u_s)} delta_s B_s[n],  lambda_c = e^{A u_c}
+// and the segment's state S = lambda_c S + S_c chunk by chunk (fp32, in the
+// accumulators), its decay the product of the lambda_c.  The heads of a
+// workgroup share their B rows: B is staged once and its MFMA operands are
+// read once for all of them (HPW = 2 when the heads of a group pair up).  The
+// segment is staged through LDS in quarters of up to 64 tokens (a quarter
+// never spans two chunks), loaded into registers two quarters ahead.  The
+// decay weight goes onto x (P columns) as it is staged.  Eight waves; wave w
+// owns n tiles 2(w%4), 2(w%4)+1 and p tiles 2(w/4), 2(w/4)+1 of the
+// transposed product D[n][p] = sum_s B_s[n] (w_s x_s[p]) of every head, so an
+// accumulator lane holds one p and, per pair of n tiles, 8 consecutive n (two
+// 16-byte stores of the fp32 state).  The exponent sums are fp32 (a wave DPP
+// scan): a sum of at most 256 positive steps carries a relative error of
+// ~1e-6.  Each chunk's (A u_l, delta_l) per token goes to the token table.
 // ---------------------------------------------------------------------------
 template <int P, int N, int HPW>
-__global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
+__global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min,
-    float dt_max, uint16_t* __restrict__ states, float* __restrict__ decay,
-    float2* __restrict__ tok, int T, int H, int G, int Q, int nc, int npairs) {
+    float dt_max, float* __restrict__ states, float* __restrict__ decay,
+    float2* __restrict__ tok, int T, int H, int G, int Q, int nc, int K, int nseg, int npairs) {
   constexpr int NTHR = 512, WW = 8;
   constexpr int HS = 64;                    // tokens per staged quarter
   constexpr int XPn = P + 16, BPn = N + 16;  // pitches (bf16 elements)
@@ -70,7 +86,7 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
   constexpr int PTW = (PT + PGW - 1) / PGW;
   // a wave's n tiles in pairs (NTW even): tile (pair m, half) covers n = 32 m +
   // 4 half + 8 (r / 4) + r % 4 for its MFMA row r, so a lane's rows of the pair
-  // are 8 consecutive n (one 16-byte store of S_c)
+  // are 8 consecutive n
   constexpr bool kPairN = NTW % 2 == 0;
 
   __shared__ __attribute__((aligned(16))) uint16_t xl[HPW][HS * XPn];  // w_s x_s per head
@@ -78,70 +94,105 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float wsc[HPW][256];
   __shared__ float wpart[HPW][WW];
 
-  int b, c, hp;
-  if (!unit_of_block(H / HPW, nc, npairs, b, c, hp)) return;
+  int b, sg, hp;
+  if (!unit_of_block(H / HPW, nseg, npairs, b, sg, hp)) return;
   const int h0 = hp * HPW;  // first head of the workgroup
   const int g = h0 / (H / G);
-  const int t0 = c * Q;
-  const int Lc = min(Q, T - t0);
+  const int c0 = sg * K;                    // first chunk of the segment
+  const int nck = min(K, nc - c0);          // chunks of the segment
+  const int ts = c0 * Q;                    // first token
+  const int Ls = min(nck * Q, T - ts);      // tokens of the segment
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wid = wave_id();
   const int ng = wid % NGW, pg = wid / NGW;
 
-  // ---- loads: dt first, then the first two quarters of x and B ----
-  const size_t r0 = static_cast<size_t>(b) * T + t0;
+  // ---- loads: dt of the first chunk, then the first two quarters ----
+  const size_t r0 = static_cast<size_t>(b) * T + ts;
   float dtv[HPW];
+  auto load_dt = [&](int kc) {
+    const int lc = min(Q, Ls - kc * Q);
 #pragma unroll
-  for (int e = 0; e < HPW; ++e) dtv[e] = tid < Lc ? dt[(r0 + tid) * H + h0 + e] : 0.0f;
+    for (int e = 0; e < HPW; ++e)
+      dtv[e] = tid < lc ? dt[(r0 + static_cast<size_t>(kc) * Q + tid) * H + h0 + e] : 0.0f;
+  };
+  load_dt(0);
   const uint32_t xrow = static_cast<uint32_t>(H) * P * 2;
   const uint32_t brow = static_cast<uint32_t>(G) * N * 2;
   buf_t xbuf[HPW];
 #pragma unroll
   for (int e = 0; e < HPW; ++e)
     xbuf[e] = make_buf(x + r0 * H * P + static_cast<size_t>(h0 + e) * P,
-                       static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+                       static_cast<uint32_t>(Ls - 1) * xrow + P * 2);
   const buf_t bbuf = make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N,
-                              static_cast<uint32_t>(Lc - 1) * brow + N * 2);
+                              static_cast<uint32_t>(Ls - 1) * brow + N * 2);
   BufSlab<HS, P / 8, NTHR> xs[2][HPW];
   BufSlab<HS, N / 8, NTHR> bs[2];
-  const int nq = (Q + HS - 1) / HS;  // quarters of the chunk
+  // quarters: Q >= 64 splits every chunk into Q / 64 of them; a shorter chunk
+  // is one quarter (its segment has one chunk)
+  const int QR = Q < HS ? Q : HS;           // tokens per quarter
+  const int nqc = Q < HS ? 1 : Q / HS;      // quarters per chunk
+  const int nq = nck * nqc;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     if (i < nq) {
 #pragma unroll
-      for (int e = 0; e < HPW; ++e) xs[i][e].load(xbuf[e], xrow, i * HS);
-      bs[i].load(bbuf, brow, i * HS);
+      for (int e = 0; e < HPW; ++e) xs[i][e].load(xbuf[e], xrow, i * QR);
+      bs[i].load(bbuf, brow, i * QR);
     }
 
-  // ---- step sizes and running sums (thread s = token s), per head ----
-  float dd[HPW], uu[HPW];
+  f32x4 acc[HPW][NTW][PTW];
 #pragma unroll
-  for (int e = 0; e < HPW; ++e) {
-    const float bias = dt_bias ? dt_bias[h0 + e] : 0.0f;
-    dd[e] = tid < Lc ? step_size(dtv[e], bias, dt_min, dt_max) : 0.0f;
-    uu[e] = wave_inclusive_sum(dd[e]);
-    if (lane == kWave - 1) wpart[e][wid] = uu[e];
-  }
-  __syncthreads();
+  for (int e = 0; e < HPW; ++e)
 #pragma unroll
-  for (int e = 0; e < HPW; ++e) {
-    const int h = h0 + e;
-    const float a_re = A[h];
-    float before = 0.0f, total = 0.0f;
+    for (int i = 0; i < NTW; ++i)
 #pragma unroll
-    for (int w = 0; w < WW; ++w) {
-      const float pw = wpart[e][w];
-      before += w < wid ? pw : 0.0f;
-      total += pw;
+      for (int j = 0; j < PTW; ++j) acc[e][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lam_seg[HPW];
+#pragma unroll
+  for (int e = 0; e < HPW; ++e) lam_seg[e] = 1.0f;
+
+  // ---- chunk kc: step sizes, running sums (thread s = token s), weights to
+  // the chunk end, token table, decay; the carried state decays over the chunk
+  auto chunk_start = [&](int kc) {
+    const int lc = min(Q, Ls - kc * Q);
+    float dd[HPW], uu[HPW];
+#pragma unroll
+    for (int e = 0; e < HPW; ++e) {
+      const float bias = dt_bias ? dt_bias[h0 + e] : 0.0f;
+      dd[e] = tid < lc ? step_size(dtv[e], bias, dt_min, dt_max) : 0.0f;
+      uu[e] = wave_inclusive_sum(dd[e]);
+      if (lane == kWave - 1) wpart[e][wid] = uu[e];
     }
-    const float u = uu[e] + before;
-    if (tid < 256) wsc[e][tid] = __expf(a_re * (total - u)) * dd[e];
-    if (tid == 0) decay[(static_cast<size_t>(b) * H + h) * nc + c] = __expf(a_re * total);
-    // (A u_l, delta_l) of every token for the output kernel (padding: delta 0)
-    if (tid < Q) tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid] = make_float2(a_re * u, dd[e]);
-  }
-  __syncthreads();
+    if (kc + 1 < nck) load_dt(kc + 1);
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < HPW; ++e) {
+      const int h = h0 + e;
+      const float a_re = A[h];
+      float before = 0.0f, total = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WW; ++w) {
+        const float pw = wpart[e][w];
+        before += w < wid ? pw : 0.0f;
+        total += pw;
+      }
+      const float u = uu[e] + before;
+      if (tid < 256) wsc[e][tid] = __expf(a_re * (total - u)) * dd[e];
+      const float lam = __expf(a_re * total);
+      lam_seg[e] *= lam;
+      // (A u_l, delta_l) of every token for the output kernel (padding: delta 0)
+      if (tid < Q)
+        tok[((static_cast<size_t>(b) * nc + c0 + kc) * H + h) * Q + tid] = make_float2(a_re * u, dd[e]);
+      if (kc > 0) {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+#pragma unroll
+          for (int j = 0; j < PTW; ++j) acc[e][i][j] = acc[e][i][j] * lam;
+      }
+    }
+    __syncthreads();
+  };
 
   // quarter -> LDS (x scaled by w_s; rows past the chunk are zero)
   auto stage = [&](const BufSlab<HS, P / 8, NTHR> (&xsq)[HPW], const BufSlab<HS, N / 8, NTHR>& bsq,
@@ -165,13 +216,6 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
     }
   };
 
-  f32x4 acc[HPW][NTW][PTW];
-#pragma unroll
-  for (int e = 0; e < HPW; ++e)
-#pragma unroll
-    for (int i = 0; i < NTW; ++i)
-#pragma unroll
-      for (int j = 0; j < PTW; ++j) acc[e][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // one quarter on MFMA: contraction over its tokens, all operand reads of a
   // 32-token step issued before the step's MFMAs; the B operands serve every head
   auto mma = [&](int rows) {
@@ -180,9 +224,9 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
         const int nt = ng * NTW + i;
-        const int c0 = kPairN ? 32 * (nt >> 1) + 4 * (nt & 1) : nt * 16;
-        const uint2 lo = kPairN ? lds_tr4s<8>(bl, BPn, ks + 8 * q, c0) : lds_tr4(bl, BPn, ks + 8 * q, c0);
-        const uint2 hi = kPairN ? lds_tr4s<8>(bl, BPn, ks + 8 * q + 4, c0) : lds_tr4(bl, BPn, ks + 8 * q + 4, c0);
+        const int cc = kPairN ? 32 * (nt >> 1) + 4 * (nt & 1) : nt * 16;
+        const uint2 lo = kPairN ? lds_tr4s<8>(bl, BPn, ks + 8 * q, cc) : lds_tr4(bl, BPn, ks + 8 * q, cc);
+        const uint2 hi = kPairN ? lds_tr4s<8>(bl, BPn, ks + 8 * q + 4, cc) : lds_tr4(bl, BPn, ks + 8 * q + 4, cc);
         af[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
 #pragma unroll
@@ -204,25 +248,34 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
               acc[e][i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bf[e][j]), acc[e][i][j]);
     }
   };
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i < nq) {
-      if (i > 0) __syncthreads();
-      stage(xs[i & 1], bs[i & 1], i * HS);
-      if (i + 2 < nq) {
-#pragma unroll
-        for (int e = 0; e < HPW; ++e) xs[i & 1][e].load(xbuf[e], xrow, (i + 2) * HS);
-        bs[i & 1].load(bbuf, brow, (i + 2) * HS);
-      }
-      __syncthreads();
-      mma(Q - i * HS < HS ? Q - i * HS : HS);
-    }
 
-  // S_c: lane holds p = pt*16 + r16 and, per pair of n tiles, n = 32 m + 8q .. +7
-  // (else per tile n = nt*16 + 4q .. +3)
+  // quarter gi of the segment through register slot S of the ring
+  auto quarter = [&](auto slot, int gi) {
+    constexpr int S = decltype(slot)::value;
+    const int kc = gi / nqc, qi = gi - kc * nqc;
+    if (qi == 0)
+      chunk_start(kc);  // its barriers also end the previous quarter's use of the tiles
+    else
+      __syncthreads();
+    stage(xs[S], bs[S], qi * HS);
+    if (gi + 2 < nq) {
+#pragma unroll
+      for (int e = 0; e < HPW; ++e) xs[S][e].load(xbuf[e], xrow, (gi + 2) * QR);
+      bs[S].load(bbuf, brow, (gi + 2) * QR);
+    }
+    __syncthreads();
+    mma(QR);
+  };
+  for (int gi = 0; gi < nq; gi += 2) {
+    quarter(Slot<0>{}, gi);
+    if (gi + 1 < nq) quarter(Slot<1>{}, gi + 1);
+  }
+
+  // segment state: lane holds p = pt*16 + r16 and, per pair of n tiles,
+  // n = 32 m + 8q .. +7 (else per tile n = nt*16 + 4q .. +3)
 #pragma unroll
   for (int e = 0; e < HPW; ++e) {
-    uint16_t* dst = states + ((static_cast<size_t>(b) * nc + c) * H + h0 + e) * (static_cast<size_t>(P) * N);
+    float* dst = states + ((static_cast<size_t>(b) * nseg + sg) * H + h0 + e) * (static_cast<size_t>(P) * N);
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
       const int pt = pg * PTW + j;
@@ -231,44 +284,45 @@ __global__ __launch_bounds__(512) void ssd_state_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < NTW; i += 2) {
           const int m = (ng * NTW + i) >> 1;
-          *reinterpret_cast<uint4*>(dst + (pt * 16 + r16) * N + 32 * m + 8 * q) =
-              make_uint4(pack_bf16x2(acc[e][i][j][0], acc[e][i][j][1]),
-                         pack_bf16x2(acc[e][i][j][2], acc[e][i][j][3]),
-                         pack_bf16x2(acc[e][i + 1][j][0], acc[e][i + 1][j][1]),
-                         pack_bf16x2(acc[e][i + 1][j][2], acc[e][i + 1][j][3]));
+          float* o = dst + (pt * 16 + r16) * N + 32 * m + 8 * q;
+          *reinterpret_cast<float4*>(o) = __builtin_bit_cast(float4, acc[e][i][j]);
+          *reinterpret_cast<float4*>(o + 4) = __builtin_bit_cast(float4, acc[e][i + 1][j]);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
           const int nt = ng * NTW + i;
-          *reinterpret_cast<uint2*>(dst + (pt * 16 + r16) * N + nt * 16 + 4 * q) =
-              make_uint2(pack_bf16x2(acc[e][i][j][0], acc[e][i][j][1]),
-                         pack_bf16x2(acc[e][i][j][2], acc[e][i][j][3]));
+          *reinterpret_cast<float4*>(dst + (pt * 16 + r16) * N + nt * 16 + 4 * q) =
+              __builtin_bit_cast(float4, acc[e][i][j]);
         }
       }
     }
+    if (tid == 0) decay[(static_cast<size_t>(b) * H + h0 + e) * nseg + sg] = lam_seg[e];
   }
 }
 
 // ---------------------------------------------------------------------------
-// Inter-chunk state passing (bf16 chunk states in, bf16 boundary states out):
-//   h_in(0) = h0,  h_in(c+1) = lambda_c h_in(c) + S_c,  h_final = h_in(nc)
-// (the chunkwise recurrence of the state across chunks), fp32 running state.
-// One thread per 8 consecutive n of one p of one (batch, head) (16-byte
-// accesses); PF chunks in flight.  h_in(c) overwrites S_c in place (S_c is
-// read before it).
+// State passing between segments (fp32 segment states in, bf16 boundary
+// states out):
+//   h_in(0) = h0,  h_in(s+1) = lambda_s h_in(s) + S_s,  h_final = h_in(nseg)
+// (the chunkwise recurrence of the state across chunks, applied to segments),
+// fp32 running state.  One thread per 8 consecutive n of one p of one (batch,
+// head): 32-byte reads of S, 16-byte writes of the bf16 copy; PF segments in
+// flight.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
-    uint16_t* __restrict__ states, const float* __restrict__ decay, const float* __restrict__ h0,
-    float* __restrict__ h_final, int H, int PN, int nc) {
-  constexpr int PF = 8;
+    const float* __restrict__ S, uint16_t* __restrict__ hin, const float* __restrict__ decay,
+    const float* __restrict__ h0, float* __restrict__ h_final, int H, int PN, int nseg) {
+  constexpr int PF = 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const int e8 = blockIdx.x * kThreads + threadIdx.x;  // group of 8 elements
   if (e8 * 8 >= PN) return;
   const size_t bh = static_cast<size_t>(b) * H + h;
-  const size_t cstride = static_cast<size_t>(H) * PN;  // between chunks of one (b, h)
-  uint16_t* base = states + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e8 * 8;
-  const float* dc = decay + bh * nc;
+  const size_t sstride = static_cast<size_t>(H) * PN;  // between segments of one (b, h)
+  const size_t off = static_cast<size_t>(b) * nseg * sstride + h * static_cast<size_t>(PN) + e8 * 8;
+  const float* sp = S + off;
+  uint16_t* hp = hin + off;
+  const float* dc = decay + bh * nseg;
   float hv[8];
   if (h0) {
     const float4 a = *reinterpret_cast<const float4*>(h0 + bh * PN + e8 * 8);
@@ -280,44 +334,45 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
     for (int k = 0; k < 8; ++k) hv[k] = 0.0f;
   }
 
-  uint4 cur[PF];
+  float4 cur[PF][2];
   float cd[PF];
 #pragma unroll
   for (int j = 0; j < PF; ++j)
-    if (j < nc) {
-      cur[j] = *reinterpret_cast<const uint4*>(base + j * cstride);
+    if (j < nseg) {
+      cur[j][0] = *reinterpret_cast<const float4*>(sp + j * sstride);
+      cur[j][1] = *reinterpret_cast<const float4*>(sp + j * sstride + 4);
       cd[j] = dc[j];
     }
-  for (int c0 = 0; c0 < nc; c0 += PF) {
-    uint4 nxt[PF];
+  for (int s0 = 0; s0 < nseg; s0 += PF) {
+    float4 nxt[PF][2];
     float nd[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int cn = c0 + PF + j;
-      if (cn < nc) {
-        nxt[j] = *reinterpret_cast<const uint4*>(base + cn * cstride);
-        nd[j] = dc[cn];
+      const int sn = s0 + PF + j;
+      if (sn < nseg) {
+        nxt[j][0] = *reinterpret_cast<const float4*>(sp + sn * sstride);
+        nxt[j][1] = *reinterpret_cast<const float4*>(sp + sn * sstride + 4);
+        nd[j] = dc[sn];
       }
     }
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int cc = c0 + j;
-      if (cc < nc) {
-        *reinterpret_cast<uint4*>(base + cc * cstride) =
+      const int ss = s0 + j;
+      if (ss < nseg) {
+        *reinterpret_cast<uint4*>(hp + ss * sstride) =
             make_uint4(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
                        pack_bf16x2(hv[6], hv[7]));
         const float l = cd[j];
-        const uint32_t sw[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+        const float sv[8] = {cur[j][0].x, cur[j][0].y, cur[j][0].z, cur[j][0].w,
+                             cur[j][1].x, cur[j][1].y, cur[j][1].z, cur[j][1].w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          hv[2 * k] = l * hv[2 * k] + bf16_bits_to_f32(sw[k] & 0xFFFFu);
-          hv[2 * k + 1] = l * hv[2 * k + 1] + bf16_bits_to_f32(sw[k] >> 16);
-        }
+        for (int k = 0; k < 8; ++k) hv[k] = l * hv[k] + sv[k];
       }
     }
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      cur[j] = nxt[j];
+      cur[j][0] = nxt[j][0];
+      cur[j][1] = nxt[j][1];
       cd[j] = nd[j];
     }
   }
@@ -328,9 +383,12 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Chunk outputs.  The workgroup walks its chunk in sub-chunks of QS = 64
-// tokens and carries the state across them in MFMA accumulators; for
-// sub-chunk j (tokens j0..j1, state h_j at its start, h_0 = h_in(c)):
+// Segment outputs.  The workgroup walks its segment in sub-chunks of QS = 64
+// tokens (QS = chunk for chunks below 64; a sub-chunk never spans two chunks)
+// and carries the state across them -- and across the chunk boundaries inside
+// the segment -- in MFMA accumulators; for sub-chunk j (tokens j0..j1 of its
+// chunk, state h_j at its start, h_0 = the state entering the segment, cs the
+// cumulative decay exponent of the chunk, cs_{j0-1} = 0 at a chunk start):
 //   y_l     = e^{cs_l - cs_{j0-1}} C_l . h_j                      (carried)
 //           + sum_{j0 <= s <= l} (C_l . B_s) e^{cs_l - cs_s} delta_s x_s
 //           + D x_l
@@ -343,44 +401,56 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
 // e^{cs_l - cs_s} = e^{cs_l - cs_m} e^{cs_m - cs_s}.  The second factor (times
 // delta_s) is one weight w_s per source token; the first is common to every
 // term of output row l, carried one included when the state is kept as
-// H = e^{cs_m - cs_{j0-1}} h_j (one factor per sub-chunk), so
-//   y_l = e^{cs_l - cs_m} (C_l . H + sum_{s <= l} (C_l . B_s) w_s x_s) + D x_l
+// H_j = sigma_j h_j with sigma_j = e^{cs_m - cs_{j0-1}}, so
+//   y_l = e^{cs_l - cs_m} (C_l . H_j + sum_{s <= l} (C_l . B_s) w_s x_s
+//                          + D e^{cs_m - cs_l} x_l)
 // -- raw C and raw x everywhere, the causal mask only on diagonal blocks, w_s
 // on the columns of the masked (C_l . B_s) block before it is rounded to bf16,
-// one scale per output row at the end.  The state update accumulates
-// (w_s B_s) x_s^T into H, w_s applied to the B operand in registers.  Only
-// raw x is staged, one tile that also supplies D x_l.  The
-// factors stay below e^60 when every half sub-chunk decays by at most e^60;
-// when a chunk breaks that bound the workgroup switches to exact mode
-// (per-element exponentials against raw x, the carried term scaled by
-// e^{cs_l - cs_{j0-1}}, the state kept unscaled, w_s = e^{cs_j1 - cs_s} delta_s).
+// D x_l as one more term on the block's diagonal, one scale per output row at
+// the end.  The state update accumulates (w_s B_s) x_s^T into H, w_s applied
+// to the B operand in registers, which leaves tau_j h_{j+1} with tau_j =
+// e^{cs_m - cs_j1}; the next sub-chunk starts by scaling the accumulators by
+// sigma_{j+1} / tau_j (<= 1, the decay from one pivot to the next).  The
+// factors stay below e^60 when every half sub-chunk decays by at most e^60; a
+// sub-chunk that breaks this runs in exact mode (per-element exponentials
+// against raw x, the carried term scaled by e^{cs_l - cs_{j0-1}}, the state
+// unscaled: sigma = tau = 1, w_s = e^{cs_j1 - cs_s} delta_s, the state scaled
+// by e^{cs_j1 - cs_{j0-1}} before its update).  The pivot-to-pivot factor
+// sigma_{j+1} / tau_j can be as small as e^-120, below fp32's range, while the
+// state it produces is not: it is applied as its two factors in turn when
+// their product would underflow.  Wave 0 computes each
+// sub-chunk's factors from the token table one sub-chunk ahead, into one of
+// two LDS sets.
 //
 // The output tile is computed transposed, Y^T[p][l]: wave w owns output rows
-// l = 16w .. 16w+15 of each sub-chunk as accumulator columns, so a lane holds
-// one row l (one scale factor) and four consecutive p of each tile; the
-// tiles go in pairs with permuted p (P >= 32), so a lane holds 8 consecutive p
-// of a pair: one 16-byte store of y.
+// l = 16w .. 16w+15 of each sub-chunk (rotated by workgroup) as accumulator
+// columns, so a lane holds one row l (one scale factor) and four consecutive p
+// of each tile; the tiles go in pairs with permuted p (P >= 32), so a lane
+// holds 8 consecutive p of a pair: one 16-byte store of y.
 // Per 32 source tokens, G^T = B_s . C_l^T on MFMA (C rows in registers,
 // prefetched a sub-chunk ahead) leaves column l in the lane, which after the
 // mask and the weights is the B operand of Y^T += X^T M^T.  For the state
 // update wave w owns n tiles 2w, 2w+1 with N = 128 (paired, permuted n), else
-// w, w+4, ..: H^T[n][p] += sum_s (w_s B_s[n]) x_s[p]
-// (operands from LDS by the transpose read); a lane holds 4 consecutive n of
-// one p and writes the bf16 state tile with 8-byte stores.
+// w, w+4, ..: H^T[n][p] += sum_s (w_s B_s[n]) x_s[p] (operands from LDS by the
+// transpose read); a lane holds 4 consecutive n of one p.
 // ---------------------------------------------------------------------------
-template <int P, int N>
-__global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm, const float* __restrict__ D,
-    const float2* __restrict__ tok, const uint16_t* __restrict__ hin, uint16_t* __restrict__ y,
-    int T, int H, int G, int Q, int nc, int npairs) {
-  constexpr int QSM = 64;               // sub-chunk length (Q >= 64); Q = 32 runs one of 32
+// MULTI: the segment may hold several chunks (K > 1).  The single-chunk build
+// keeps three workgroups per CU (<= 168 VGPRs); the per-chunk factor step in
+// the loop of the multi-chunk build needs more registers, and it runs at two
+// per CU rather than spill (T65536: 454 us against 488 us spilled at three).
+template <int P, int N, bool MULTI>
+__global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const float* __restrict__ D, const float2* __restrict__ tok, const uint16_t* __restrict__ hin,
+    uint16_t* __restrict__ y, int T, int H, int G, int Q, int nc, int K, int nseg, int npairs) {
+  constexpr int QSM = 64;               // sub-chunk length (Q >= 64); a shorter chunk is one
   constexpr int KCP = N < 32 ? 32 : N;  // K of G^T padded to whole 32-wide MFMA steps (zeros)
   // row pitches (bf16): the B tile is read by rows (16 bytes a lane) and by the
   // transpose read (4 rows x 32 bytes a 16-lane group), so its rows start 8
   // banks apart; the state tile is read by rows only (4 banks apart suffice)
   constexpr int BTP = KCP + 16;
   constexpr int HTP = KCP + 8;
-  constexpr int XPn = P + 16;           // pitch of the x tiles
+  constexpr int XPn = P + 16;           // pitch of the x tile
   constexpr int NKS = KCP / 32;
   constexpr int NPT = P / 16;
   constexpr int KT = N / 16;            // n tiles of the state
@@ -402,18 +472,26 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t bt[QSM * BTP];
   __shared__ __attribute__((aligned(16))) uint16_t xl[QSM * XPn];  // raw x
   __shared__ __attribute__((aligned(16))) uint16_t hT[P * HTP];
-  __shared__ __attribute__((aligned(16))) float dl[256];
-  __shared__ __attribute__((aligned(16))) float cs[256];   // A u_l
-  __shared__ __attribute__((aligned(16))) float csc[256];  // output row scale
-  __shared__ __attribute__((aligned(16))) float xsc[256];  // source token weight w_s
-  __shared__ float kpre[4], kpost[4];                       // state factors per sub-chunk
-  __shared__ int exact_flag;
+  // per token of the current chunk: exponent, step size, output row scale,
+  // source weight, diagonal D term; per sub-chunk of the chunk: the state's two
+  // scale factors before it and its scale before the update, exact mode; the
+  // scale the state carries after the chunk's last update
+  __shared__ __attribute__((aligned(16))) float tcs[256];
+  __shared__ __attribute__((aligned(16))) float tdl[256];
+  __shared__ __attribute__((aligned(16))) float tcsc[256];
+  __shared__ __attribute__((aligned(16))) float txsc[256];
+  __shared__ __attribute__((aligned(16))) float tdsc[256];
+  __shared__ float skp1[256 / QSM], skp2[256 / QSM], skpost[256 / QSM];
+  __shared__ int sexact[256 / QSM];
+  __shared__ float stau_last;
 
-  int b, c, h;
-  if (!unit_of_block(H, nc, npairs, b, c, h)) return;
+  int b, sg, h;
+  if (!unit_of_block(H, nseg, npairs, b, sg, h)) return;
   const int g = h / (H / G);
-  const int t0 = c * Q;
-  const int Lc = min(Q, T - t0);
+  const int c0 = sg * K;
+  const int nck = min(K, nc - c0);
+  const int ts = c0 * Q;
+  const int Ls = min(nck * Q, T - ts);
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wid = wave_id();  // wave-uniform (SGPR): tile branches stay scalar
@@ -422,32 +500,35 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   // them over the SIMDs of a CU instead of loading one SIMD in every workgroup
   const int rw = __builtin_amdgcn_readfirstlane((wid + static_cast<int>(blockIdx.x)) & 3);
   const int QS = Q < QSM ? Q : QSM;
-  const int nsub = Q / QS;
-  const bool has_rows = 16 * rw < QS;  // waves without output rows (Q = 32) only help stage
-  // per-token exponents and step sizes (from the chunk-state kernel), first
-  const float2 tv = tid < Q ? tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid]
-                            : make_float2(0.f, 0.f);
+  const int nsc = Q / QS;               // sub-chunks per chunk
+  const int nsub = nck * nsc;
+  const bool has_rows = 16 * rw < QS;   // waves without output rows (Q < 64) only help stage
   const float Dh = D ? D[h] : 0.0f;
-  if (tid == 0) exact_flag = 0;
 
-  // ---- buffer descriptors of this chunk's slices (rows >= Lc read as zero) ----
-  const size_t xy0 = (static_cast<size_t>(b) * T + t0) * H * P + static_cast<size_t>(h) * P;
+  // ---- buffer descriptors of this segment's slices (rows >= Ls read as zero) ----
+  const size_t xy0 = (static_cast<size_t>(b) * T + ts) * H * P + static_cast<size_t>(h) * P;
   const uint32_t xrow = static_cast<uint32_t>(H) * P * 2;
-  const uint32_t xbytes = Lc > 0 ? static_cast<uint32_t>(Lc - 1) * xrow + P * 2 : 0;
+  const uint32_t xbytes = Ls > 0 ? static_cast<uint32_t>(Ls - 1) * xrow + P * 2 : 0;
   const buf_t xbuf = make_buf(x + xy0, xbytes);
   const buf_t ybuf = make_buf(y + xy0, xbytes);
-  const size_t bc0 = (static_cast<size_t>(b) * T + t0) * G * N + static_cast<size_t>(g) * N;
+  const size_t bc0 = (static_cast<size_t>(b) * T + ts) * G * N + static_cast<size_t>(g) * N;
   const uint32_t brow = static_cast<uint32_t>(G) * N * 2;
-  const uint32_t bbytes = Lc > 0 ? static_cast<uint32_t>(Lc - 1) * brow + N * 2 : 0;
+  const uint32_t bbytes = Ls > 0 ? static_cast<uint32_t>(Ls - 1) * brow + N * 2 : 0;
   const buf_t bbuf = make_buf(Bm + bc0, bbytes);
   const buf_t cbuf = make_buf(Cm + bc0, bbytes);
-  const buf_t hbuf = make_buf(hin + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
+  const buf_t hbuf = make_buf(hin + ((static_cast<size_t>(b) * nseg + sg) * H + h) * (static_cast<size_t>(P) * N),
                               P * N * 2);
+  // token table entry of token tid of chunk kc of the segment
+  auto load_tok = [&](int kc) -> float2 {
+    return tid < Q ? tok[((static_cast<size_t>(b) * nc + c0 + kc) * H + h) * Q + tid]
+                   : make_float2(0.f, 0.f);
+  };
 
-  // ---- global loads: h_in, C rows and x/B of sub-chunk 0 ----
+  // ---- global loads: token table, h_in, C rows and x/B of sub-chunk 0 ----
+  float2 tv = load_tok(0);
 
-  // h_in tiles (bf16, converted after the prologue so that nothing waits for
-  // them before every other load is in flight)
+  // h_in tiles (bf16, converted after the first factors so that nothing waits
+  // for them before every other load is in flight)
   uint2 hv[KTW][NPT];
 #pragma unroll
   for (int pt = 0; pt < NPT; ++pt) {
@@ -463,8 +544,8 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   }
 
   // C rows of this wave's output tile in sub-chunk j: lane (row r16, group q)
-  // holds k = ks*32 + 8q .. +7.  Rows past the chunk (and every row of the
-  // waves without output rows, Q = 32) read as zero through the descriptor;
+  // holds k = ks*32 + 8q .. +7.  Rows past the segment (and every row of the
+  // waves without output rows, Q < 64) read as zero through the descriptor;
   // the K padding (N = 16) is zeroed by an out-of-range offset, not by a
   // select on the loaded value, so the prefetch is not waited for here.
   auto load_c = [&](uint4 (&cr)[NKS], int j) {
@@ -484,45 +565,70 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   xs.load(xbuf, xrow, 0);
   bs.load(bbuf, brow, 0);
 
-  // ---- prologue: per-token values, per-sub-chunk factors ----
-  // (entries past the chunk are zero: with chunk 16 the diagonal block pair
-  // reads the weights of tokens 16..31 into a product it then discards)
-  cs[tid] = tid < Q ? tv.x : 0.0f;
-  dl[tid] = tid < Q ? tv.y : 0.0f;
-  __syncthreads();
-  // exponent of token t (t = -1: 0)
-  auto csd = [&](int t) -> float { return t < 0 ? 0.0f : cs[t]; };
-  if (tid < nsub) {
-    const int j0 = tid * QS, m = j0 + QS / 2 - 1, j1 = j0 + QS - 1;
-    if (csd(j0 - 1) - csd(m) > kMaxHalfSpread || csd(m) - csd(j1) > kMaxHalfSpread)
-      atomicOr(&exact_flag, 1);
-  }
-  __syncthreads();
-  // uniform over the workgroup; scalar so that its branches keep EXEC whole
-  const bool exact = __builtin_amdgcn_readfirstlane(exact_flag) != 0;
-  csc[tid] = 0.0f;
-  xsc[tid] = 0.0f;
-  if (tid < Q) {
-    const int j0 = tid & ~(QS - 1), m = j0 + QS / 2 - 1, j1 = j0 + QS - 1;
-    const float e = csd(tid);
-    if (exact) {
-      csc[tid] = __expf(e - csd(j0 - 1));
-      xsc[tid] = __expf(csd(j1) - e) * dl[tid];
-    } else {
-      csc[tid] = __expf(e - csd(m));
-      xsc[tid] = __expf(csd(m) - e) * dl[tid];
-    }
-    if (tid == j1) {
-      const int j = tid / QS;
-      if (exact) {
-        kpre[j] = 1.0f;
-        kpost[j] = __expf(csd(j1) - csd(j0 - 1));
+  // ---- factors of chunk kc's tokens and sub-chunks (every thread; t: token
+  // tid's table entry).  Contains two barriers; the first also ends every
+  // use of the previous chunk's factors.
+  auto chunk_factors = [&](float2 t, bool first) {
+    // scale after the previous chunk's last update (the segment's entering
+    // state is unscaled)
+    const float tau_in = first ? 1.0f : stau_last;
+    tcs[tid] = tid < Q ? t.x : 0.0f;
+    tdl[tid] = tid < Q ? t.y : 0.0f;
+    __syncthreads();
+    const int jl = tid / QS, j0 = jl * QS, m = j0 + QS / 2 - 1, j1 = j0 + QS - 1;
+    // exponents around sub-chunk jb (in the chunk's frame): before its first
+    // token, at its pivot, at its last token; and whether it runs exact
+    auto sub_exps = [&](int jb, float& st, float& cm, float& ce) {
+      st = jb > 0 ? tcs[jb * QS - 1] : 0.0f;
+      cm = tcs[jb * QS + QS / 2 - 1];
+      ce = tcs[jb * QS + QS - 1];
+      return st - cm > kMaxHalfSpread || cm - ce > kMaxHalfSpread;
+    };
+    if (tid < Q) {
+      float start, cm, ce;
+      const bool exact = sub_exps(jl, start, cm, ce);
+      const float e = t.x;
+      float sigma, tau, kpost;
+      if (!exact) {
+        const float w = __expf(cm - e);
+        tcsc[tid] = __expf(e - cm);
+        txsc[tid] = w * t.y;
+        tdsc[tid] = Dh * w;
+        sigma = __expf(cm - start);
+        tau = __expf(cm - ce);
+        kpost = 1.0f;
       } else {
-        kpre[j] = __expf(csd(m) - (j0 > 0 ? csd(m - QS) : 0.0f));
-        kpost[j] = 1.0f;
+        tcsc[tid] = __expf(e - start);
+        txsc[tid] = __expf(ce - e) * t.y;
+        tdsc[tid] = Dh;
+        sigma = 1.0f;
+        tau = 1.0f;
+        kpost = __expf(ce - start);
       }
+      if (tid == j1) {
+        float tau_prev = tau_in;
+        if (jl > 0) {
+          float s1, m1, e1;
+          tau_prev = sub_exps(jl - 1, s1, m1, e1) ? 1.0f : __expf(m1 - e1);
+        }
+        // sigma / tau_prev, as two factors each >= e^-60: their product (the
+        // decay from one pivot to the next) can fall below fp32's range while
+        // the state it scales to stays representable
+        skp1[jl] = 1.0f / tau_prev;
+        skp2[jl] = sigma;
+        skpost[jl] = kpost;
+        sexact[jl] = exact ? 1 : 0;
+        if (jl == nsc - 1) stau_last = tau;
+      }
+    } else {
+      tcsc[tid] = 0.0f;
+      txsc[tid] = 0.0f;
+      tdsc[tid] = 0.0f;
     }
-  }
+    __syncthreads();
+  };
+  chunk_factors(tv, true);
+
   // state tiles, transposed: lane holds column p = pt*16 + r16, rows n = nt*16 + 4q + j
   f32x4 hacc[KTW][NPT];
 #pragma unroll
@@ -544,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
   }
   __syncthreads();
 
-  auto store_stage = [&](int j) {
+  auto store_stage = [&]() {
 #pragma unroll
     for (int i = 0; i < bs.PER; ++i) {
       const int it = tid + i * kThreads;
@@ -562,9 +668,17 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       }
     }
   };
-  // scale the state by kpre[j] and write its bf16 copy hT[p][n]
-  auto store_state = [&](int j) {
-    const float k = kpre[j];
+  // scale the state by the sub-chunk's factors and write its bf16 copy hT[p][n]
+  auto store_state = [&](int jl) {
+    const float k1 = skp1[jl], k2 = skp2[jl];
+    const float k12 = k1 * k2;
+    if (k12 < 0x1p-100f) {  // uniform: the two factors one after the other
+#pragma unroll
+      for (int i = 0; i < KTW; ++i)
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) hacc[i][pt] = hacc[i][pt] * k1;
+    }
+    const float k = k12 < 0x1p-100f ? k2 : k12;
     if constexpr (kPairS) {
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
@@ -589,22 +703,31 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       }
     }
   };
-  store_stage(0);
+  store_stage();
   store_state(0);
   __syncthreads();
 
   for (int j = 0; j < nsub; ++j) {
-    const int sj = j * QS;  // first token of the sub-chunk
+    const int kc = j / nsc, jl = j - kc * nsc;  // chunk, sub-chunk within it
+    const int sl0 = jl * QS;                    // its first token in the chunk
+    const int sj = j * QS;                      // its first token in the segment
     const bool more = j + 1 < nsub;
+    const bool next_chunk = more && jl == nsc - 1;
+    // uniform over the workgroup; scalar so that its branches keep EXEC whole
+    const bool exact = __builtin_amdgcn_readfirstlane(sexact[jl]) != 0;
+    float2 tvn = make_float2(0.f, 0.f);
     if (more) {
       xs.load(xbuf, xrow, sj + QS);
       bs.load(bbuf, brow, sj + QS);
       load_c(cnext, j + 1);
+      if constexpr (MULTI) {
+        if (next_chunk) tvn = load_tok(kc + 1);
+      }
     }
 
     // ---- outputs of rows sj + 16 rw .. +15 (accumulator columns) ----
     if (has_rows) {
-      const int lrow = sj + 16 * rw + r16;  // this lane's output row
+      const int lr = 16 * rw + r16;  // this lane's output row in the sub-chunk
       f32x4 yacc[NPT];
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) yacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -613,15 +736,16 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
-          const uint4 hv = *reinterpret_cast<const uint4*>(hT + prow(pt, r16) * HTP + ks * 32 + 8 * q);
-          yacc[pt] = mfma_bf16(as_bf16x8(hv), as_bf16x8(creg[ks]), yacc[pt]);
+          const uint4 hvv = *reinterpret_cast<const uint4*>(hT + prow(pt, r16) * HTP + ks * 32 + 8 * q);
+          yacc[pt] = mfma_bf16(as_bf16x8(hvv), as_bf16x8(creg[ks]), yacc[pt]);
         }
       }
+      const float rsc = tcsc[sl0 + lr];  // row scale (exact mode: the carried term's)
       if (exact) {
-        const float s1 = csc[lrow];
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) yacc[pt] = yacc[pt] * s1;
+        for (int pt = 0; pt < NPT; ++pt) yacc[pt] = yacc[pt] * rsc;
       }
+      const float dterm = tdsc[sl0 + lr];
       // intra-chunk: source blocks b0 = 2k2, b1 = 2k2+1 (16 tokens each);
       // block rw is the diagonal one
       for (int k2 = 0; 2 * k2 <= rw; ++k2) {
@@ -640,33 +764,41 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
             gb = mfma_bf16(as_bf16x8(vb), as_bf16x8(creg[ks]), gb);
           }
         }
-        // lane: column l = r16 (+16 rw), rows s = 4q + jj of blocks b0, b1
+        // lane: column l = r16 (+16 rw), rows s = 4q + jj of blocks b0, b1; on
+        // the diagonal block the mask, and the D term on its diagonal
         if (!exact) {
-          const float4 wa = *reinterpret_cast<const float4*>(xsc + sj + b0 * 16 + 4 * q);
-          const float4 wb = *reinterpret_cast<const float4*>(xsc + sj + b1 * 16 + 4 * q);
+          const float4 wa = *reinterpret_cast<const float4*>(&txsc[sl0 + b0 * 16 + 4 * q]);
+          const float4 wb = *reinterpret_cast<const float4*>(&txsc[sl0 + b1 * 16 + 4 * q]);
           ga = ga * f32x4{wa.x, wa.y, wa.z, wa.w};
           gb = gb * f32x4{wb.x, wb.y, wb.z, wb.w};
-          if (b0 == rw) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) ga[jj] = 4 * q + jj <= r16 ? ga[jj] : 0.f;
-          }
-          if (b1 == rw) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) gb[jj] = 4 * q + jj <= r16 ? gb[jj] : 0.f;
-          }
         } else {
-          const float lh = cs[lrow];
+          const float lh = tcs[sl0 + lr];
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const int s0 = sj + (b0 + half) * 16 + 4 * q;
+            const int s0 = (b0 + half) * 16 + 4 * q;
             f32x4& gv = half ? gb : ga;
-            const float4 hs = *reinterpret_cast<const float4*>(cs + s0);
-            const float4 ds = *reinterpret_cast<const float4*>(dl + s0);
-            const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
+            const float4 hs = *reinterpret_cast<const float4*>(&tcs[sl0 + s0]);
+            const float4 ds = *reinterpret_cast<const float4*>(&tdl[sl0 + s0]);
+            const float hsv[4] = {hs.x, hs.y, hs.z, hs.w};
             const float dv[4] = {ds.x, ds.y, ds.z, ds.w};
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-              gv[jj] = s0 + jj <= lrow ? gv[jj] * __expf(lh - hv[jj]) * dv[jj] : 0.f;
+              gv[jj] = s0 + jj <= lr ? gv[jj] * __expf(lh - hsv[jj]) * dv[jj] : 0.f;
+          }
+        }
+        // (selects and an add, no per-lane branches)
+        if (b0 == rw) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float keep = 4 * q + jj <= r16 ? ga[jj] : 0.f;
+            ga[jj] = keep + (4 * q + jj == r16 ? dterm : 0.f);
+          }
+        }
+        if (b1 == rw) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float keep = 4 * q + jj <= r16 ? gb[jj] : 0.f;
+            gb[jj] = keep + (4 * q + jj == r16 ? dterm : 0.f);
           }
         }
         const uint4 mv = make_uint4(pack_bf16x2(ga[0], ga[1]), pack_bf16x2(ga[2], ga[3]),
@@ -681,53 +813,44 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
                                yacc[pt]);
         }
       }
-      // row scale, + D x_l, y rows out (lane: row lrow; rows past Lc are dropped
-      // by the descriptor).  Paired tiles: columns 32 hh + 8q .. +7, one 16-byte
+      // row scale, y rows out (lane: row sj + lr; rows past Ls are dropped by
+      // the descriptor).  Paired tiles: columns 32 hh + 8q .. +7, one 16-byte
       // store per pair; else columns pt*16 + 4q .. +3
-      const float s2 = exact ? 1.0f : csc[lrow];
+      const float s2 = exact ? 1.0f : rsc;
+      const uint32_t yoff = static_cast<uint32_t>(sj + lr) * xrow;
       if constexpr (kPairP) {
 #pragma unroll
         for (int hh = 0; hh < NPT / 2; ++hh) {
-          const uint4 u = *reinterpret_cast<const uint4*>(xl + (16 * rw + r16) * XPn + hh * 32 + 8 * q);
-          const uint32_t xw[4] = {u.x, u.y, u.z, u.w};
-          float o[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t w2 = xw[e >> 1];
-            const float xv = bf16_bits_to_f32((e & 1) ? (w2 >> 16) : (w2 & 0xFFFFu));
-            o[e] = yacc[2 * hh + (e >> 2)][e & 3] * s2 + Dh * xv;
-          }
-          buf_store16(ybuf, static_cast<uint32_t>(lrow) * xrow + (hh * 32 + 8 * q) * 2,
-                      make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                 pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])));
+          const f32x4 o0 = yacc[2 * hh] * s2, o1 = yacc[2 * hh + 1] * s2;
+          buf_store16(ybuf, yoff + (hh * 32 + 8 * q) * 2,
+                      make_uint4(pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3]),
+                                 pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])));
         }
       } else {
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-        const uint2 u = *reinterpret_cast<const uint2*>(xl + (16 * rw + r16) * XPn + pt * 16 + 4 * q);
-        const float o0 = yacc[pt][0] * s2 + Dh * bf16_bits_to_f32(u.x & 0xFFFFu);
-        const float o1 = yacc[pt][1] * s2 + Dh * bf16_bits_to_f32(u.x >> 16);
-        const float o2 = yacc[pt][2] * s2 + Dh * bf16_bits_to_f32(u.y & 0xFFFFu);
-        const float o3 = yacc[pt][3] * s2 + Dh * bf16_bits_to_f32(u.y >> 16);
-        buf_store8(ybuf, static_cast<uint32_t>(lrow) * xrow + (pt * 16 + 4 * q) * 2,
-                   make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)));
-      }
+        for (int pt = 0; pt < NPT; ++pt) {
+          const f32x4 o = yacc[pt] * s2;
+          buf_store8(ybuf, yoff + (pt * 16 + 4 * q) * 2,
+                     make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])));
+        }
       }
     }
 
     // ---- state update to the start of the next sub-chunk ----
     if (more) {
       if (exact) {
-        const float kp = kpost[j];
+        const float kp = skpost[jl];
 #pragma unroll
         for (int i = 0; i < KTW; ++i)
 #pragma unroll
           for (int pt = 0; pt < NPT; ++pt) hacc[i][pt] = hacc[i][pt] * kp;
       }
-      for (int k = 0; k < QS; k += 32) {
-        // weights of this lane's source tokens sj + k + 8q .. +7
-        const float4 w0 = *reinterpret_cast<const float4*>(xsc + sj + k + 8 * q);
-        const float4 w1 = *reinterpret_cast<const float4*>(xsc + sj + k + 8 * q + 4);
+      // (only chunks of 64 tokens and more have a next sub-chunk: QS = QSM)
+#pragma unroll
+      for (int k = 0; k < QSM; k += 32) {
+        // weights of this lane's source tokens k + 8q .. +7
+        const float4 w0 = *reinterpret_cast<const float4*>(&txsc[sl0 + k + 8 * q]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&txsc[sl0 + k + 8 * q + 4]);
         uint4 bfr[KTW];
 #pragma unroll
         for (int i = 0; i < KTW; ++i) {
@@ -750,8 +873,11 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
         }
       }
       __syncthreads();  // every wave is done with this sub-chunk's tiles
-      store_stage(j + 1);
-      store_state(j + 1);
+      store_stage();
+      if constexpr (MULTI) {
+        if (next_chunk) chunk_factors(tvn, false);  // the chunk's factors replace the last one's
+      }
+      store_state(next_chunk ? 0 : jl + 1);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) creg[ks] = cnext[ks];
       __syncthreads();
@@ -761,69 +887,80 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 template <int P, int N>
-static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output = true) {
+static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output, int K) {
   const int nc = (a.T + a.chunk - 1) / a.chunk;
-  const int npairs = a.Bsz * nc;
-  // workspace: bf16 chunk states (Bsz, nc, H, P, N), overwritten in place by
-  // the boundary states; fp32 chunk decays (Bsz, H, nc) after the room an
-  // fp32 copy of the states would take
-  // (Bsz, nc, H, Q) (exponent, step size) pairs after the decays
-  uint16_t* states = static_cast<uint16_t*>(a.workspace);
-  float* decay = static_cast<float*>(a.workspace) + workspace_state_floats(a.Bsz, nc, a.H, P, N);
-  float2* tok = reinterpret_cast<float2*>(decay + workspace_decay_floats(a.Bsz, nc, a.H));
+  const int nseg = (nc + K - 1) / K;
+  const int npairs = a.Bsz * nseg;
+  const Bf16FwdLayout L = bf16_fwd_layout(a.Bsz, nc, a.H, P, N, a.chunk, K);
+  char* ws = static_cast<char*>(a.workspace);
+  float* S = reinterpret_cast<float*>(ws + L.S);
+  uint16_t* hin = reinterpret_cast<uint16_t*>(ws + L.Hin);
+  float* decay = reinterpret_cast<float*>(ws + L.decay);
+  float2* tok = reinterpret_cast<float2*>(ws + L.tok);
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
   const uint16_t* C = static_cast<const uint16_t*>(a.C);
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
   const hipEvent_t* ev = a.events;
-  // chunk states: two heads per workgroup when the heads of a group pair up
+  // segment states: two heads per workgroup when the heads of a group pair up
   if ((a.H / a.G) % 2 == 0)
     launch_k(nc > 0, ssd_state_bf16_kernel<P, N, 2>, dim3(blocks / 2), dim3(512), st, ev, x, a.dt,
-             a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G, a.chunk,
-             nc, npairs);
+             a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, decay, tok, a.T, a.H, a.G, a.chunk, nc, K,
+             nseg, npairs);
   else
     launch_k(nc > 0, ssd_state_bf16_kernel<P, N, 1>, dim3(blocks), dim3(512), st, ev, x, a.dt,
-             a.A, B, a.dt_bias, a.dt_min, a.dt_max, states, decay, tok, a.T, a.H, a.G, a.chunk,
-             nc, npairs);
+             a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, decay, tok, a.T, a.H, a.G, a.chunk, nc, K,
+             nseg, npairs);
   launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel,
            dim3((P * N / 8 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
-           ev ? ev + 2 : nullptr, states, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
-           P * N, nc);
+           ev ? ev + 2 : nullptr, static_cast<const float*>(S), hin, static_cast<const float*>(decay),
+           a.h0, a.h_final, a.H, P * N, nseg);
   if (!with_output) return hipGetLastError();
-  launch_k(nc > 0, ssd_scan_bf16_kernel<P, N>, dim3(blocks), dim3(kThreads), st,
-           ev ? ev + 4 : nullptr, x, B, C, a.D, static_cast<const float2*>(tok),
-           static_cast<const uint16_t*>(states), static_cast<uint16_t*>(a.y), a.T, a.H, a.G,
-           a.chunk, nc, npairs);
+  // the kernel walks several chunks only when K > 1 (a separate build: the
+  // per-chunk factor step inside its loop costs registers)
+  if (K > 1)
+    launch_k(nc > 0, ssd_scan_bf16_kernel<P, N, true>, dim3(blocks), dim3(kThreads), st,
+             ev ? ev + 4 : nullptr, x, B, C, a.D, static_cast<const float2*>(tok),
+             static_cast<const uint16_t*>(hin), static_cast<uint16_t*>(a.y), a.T, a.H, a.G,
+             a.chunk, nc, K, nseg, npairs);
+  else
+    launch_k(nc > 0, ssd_scan_bf16_kernel<P, N, false>, dim3(blocks), dim3(kThreads), st,
+             ev ? ev + 4 : nullptr, x, B, C, a.D, static_cast<const float2*>(tok),
+             static_cast<const uint16_t*>(hin), static_cast<uint16_t*>(a.y), a.T, a.H, a.G,
+             a.chunk, nc, K, nseg, npairs);
   return hipGetLastError();
 }
 
 template <int P>
-static hipError_t dispatch_bf16_n(const ChunkArgs& a, hipStream_t st, bool with_output) {
+static hipError_t dispatch_bf16_n(const ChunkArgs& a, hipStream_t st, bool with_output, int K) {
   switch (a.N) {
-    case 16: return launch_bf16<P, 16>(a, st, with_output);
-    case 32: return launch_bf16<P, 32>(a, st, with_output);
-    case 64: return launch_bf16<P, 64>(a, st, with_output);
-    case 128: return launch_bf16<P, 128>(a, st, with_output);
+    case 16: return launch_bf16<P, 16>(a, st, with_output, K);
+    case 32: return launch_bf16<P, 32>(a, st, with_output, K);
+    case 64: return launch_bf16<P, 64>(a, st, with_output, K);
+    case 128: return launch_bf16<P, 128>(a, st, with_output, K);
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
-static hipError_t dispatch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output) {
+static hipError_t dispatch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output, int K) {
   switch (a.P) {
-    case 16: return dispatch_bf16_n<16>(a, st, with_output);
-    case 32: return dispatch_bf16_n<32>(a, st, with_output);
-    case 64: return dispatch_bf16_n<64>(a, st, with_output);
-    case 128: return dispatch_bf16_n<128>(a, st, with_output);
+    case 16: return dispatch_bf16_n<16>(a, st, with_output, K);
+    case 32: return dispatch_bf16_n<32>(a, st, with_output, K);
+    case 64: return dispatch_bf16_n<64>(a, st, with_output, K);
+    case 128: return dispatch_bf16_n<128>(a, st, with_output, K);
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st) { return dispatch_bf16(a, st, true); }
+hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st) {
+  const int nc = (a.T + a.chunk - 1) / a.chunk;
+  return dispatch_bf16(a, st, true, bf16_segment_chunks(a.Bsz, nc, a.H, a.chunk));
+}
 
-// the chunk states, boundary states, decays, token table and h_final of a
-// forward call without its outputs (the backward recomputes these)
-hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st) { return dispatch_bf16(a, st, false); }
+// the per-chunk boundary states, decays, token table and h_final of a forward
+// call without its outputs (the backward recomputes these)
+hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st) { return dispatch_bf16(a, st, false, 1); }
 
 }  // namespace ssd

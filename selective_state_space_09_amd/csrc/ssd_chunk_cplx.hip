@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t xl[2][QSM * XPn];  // raw x hi / lo (exact mode)
   __shared__ __attribute__((aligned(16))) uint16_t hT[2][P * BP];     // H hi / lo
   __shared__ __attribute__((aligned(16))) float cs[256], cth[256], sth[256], csc[256], xsc[256];
-  __shared__ float kpre[256 / QSM], kpost[256 / QSM];
+  __shared__ float kpre[256 / QSM], kpre2[256 / QSM], kpost[256 / QSM];
   __shared__ int exact_flag;
 
   int b, c, h;
@@ -423,9 +423,14 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
       const int j = tid / QS;
       if (exact) {
         kpre[j] = 1.0f;
+        kpre2[j] = 1.0f;
         kpost[j] = __expf(csd(j1) - csd(j0 - 1));
       } else {
-        kpre[j] = __expf(csd(m) - (j0 > 0 ? csd(m - QS) : 0.0f));
+        // e^{cs_m - cs_{m-QS}} as two factors each >= e^-60 (before and after
+        // the sub-chunk boundary): their product can fall below fp32's range
+        // while the state it scales to stays representable
+        kpre[j] = j0 > 0 ? __expf(csd(j0 - 1) - csd(m - QS)) : 1.0f;
+        kpre2[j] = __expf(csd(m) - csd(j0 - 1));
         kpost[j] = 1.0f;
       }
     }
@@ -559,13 +564,16 @@ __global__ __launch_bounds__(kThreads) void ssd_scan_cplx_kernel(
   };
   // scale the state by kpre[j] and write its split copy hT[p][k]
   auto store_state = [&](int j) {
-    const float kk = kpre[j];
+    const float k1 = kpre[j], k2 = kpre2[j];
+    const bool two = k1 * k2 < 0x1p-100f;  // uniform: the factors one after the other
+    const float kk = two ? k2 : k1 * k2;
 #pragma unroll
     for (int i = 0; i < KTW; ++i) {
       const int nt = wid + 4 * i;
       if (nt >= KT) break;
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
+        if (two) hacc[i][pt] = hacc[i][pt] * k1;
         hacc[i][pt] = hacc[i][pt] * kk;
         uint32_t h0, l0, h1, l1;
         split_bf16x2(hacc[i][pt][0], hacc[i][pt][1], h0, l0);

@@ -100,6 +100,55 @@ inline size_t workspace_cplx_token_floats(int Bsz, int nc, int H, int chunk) {
   return static_cast<size_t>(Bsz) * nc * H * chunk * 4;
 }
 
+// ---------------------------------------------------------------------------
+// Workspace of the bfloat16 real forward.  A workgroup of its chunk-state and
+// output kernels walks a segment of K consecutive chunks of one (batch, head)
+// and carries the state across them, so states are kept at segment ends only:
+//   S     fp32 (Bsz, nseg, H, P, N)  each segment's own end state from zero
+//   Hin   bf16 (Bsz, nseg, H, P, N)  the state entering each segment (the
+//                                    output kernel's matrix-core operand)
+//   decay fp32 (Bsz, H, nseg)        each segment's decay factor
+//   tok   float2 (Bsz, nc, H, chunk) per token: A u_l (cumulative step from
+//                                    the chunk start times A) and delta_l
+// nseg = ceil(nc / K).  K is 1 while the (batch, chunk, head) units fill the
+// chip on their own, else the largest power of two (<= 16) that leaves at
+// least kSegTargetUnits workgroups; chunks below 64 tokens always use K = 1.
+// ---------------------------------------------------------------------------
+#ifndef SSD_SEG_TARGET_UNITS
+#define SSD_SEG_TARGET_UNITS 2048
+#endif
+constexpr long long kSegTargetUnits = SSD_SEG_TARGET_UNITS;
+
+inline int bf16_segment_chunks(int Bsz, int nc, int H, int chunk) {
+  if (chunk < 64) return 1;
+  const long long units = static_cast<long long>(Bsz) * nc * H;
+  int K = 1;
+  while (K < 16 && 2 * K <= nc && units / (2LL * K) >= kSegTargetUnits) K *= 2;
+  return K;
+}
+
+struct Bf16FwdLayout {
+  size_t S, Hin, decay, tok, total;  // byte offsets, total bytes
+};
+
+inline Bf16FwdLayout bf16_fwd_layout(int Bsz, int nc, int H, int P, int N, int chunk, int K) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const int nseg = (nc + K - 1) / K;
+  const size_t st = static_cast<size_t>(Bsz) * nseg * H * P * N;
+  Bf16FwdLayout L{};
+  size_t o = 0;
+  L.S = o;
+  o += up(st * 4);
+  L.Hin = o;
+  o += up(st * 2);
+  L.decay = o;
+  o += up(static_cast<size_t>(Bsz) * H * nseg * 4);
+  L.tok = o;
+  o += up(static_cast<size_t>(Bsz) * nc * H * chunk * 8);
+  L.total = o;
+  return L;
+}
+
 hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
@@ -107,7 +156,9 @@ hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex_packed(const ChunkArgs& a, int ld, hipStream_t st);
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t run_complex_decode(const DecodeArgs& a, hipStream_t st);  // D unused
-hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st);  // state + pass kernels only
+// state + pass kernels only, one chunk per segment (K = 1: per-chunk boundary
+// states, decays and the token table in bf16_fwd_layout(..., 1))
+hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_bwd_bf16(const BwdArgs& a, hipStream_t st);
 size_t bwd_workspace_bytes(int Bsz, int T, int H, int P, int G, int N, int chunk);
 int bwd_heads_per_group(int H, int G);

@@ -445,3 +445,84 @@ def test_mixed_decay_modes():
     yr, hr = _oracle_real(inp)
     assert report("y", y, yr) < TOL_BF16
     assert report("state", hf, hr, "state") < TOL_BF16
+
+
+# --------------------------------------------------------------------------
+# bf16 segments: output and state workgroups that walk several chunks
+# --------------------------------------------------------------------------
+
+def _segment_chunks(Bsz, T, H, Q, target=2048):
+    """Chunks per workgroup the bf16 forward picks for a shape (the rule the
+    library states with its workspace layout): 1 below 64-token chunks, else
+    the largest power of two <= 16 leaving >= `target` workgroups."""
+    nc = -(-T // Q)
+    if Q < 64:
+        return 1
+    K = 1
+    while K < 16 and 2 * K <= nc and (Bsz * nc * H) // (2 * K) >= target:
+        K *= 2
+    return K
+
+
+SEGMENT_CASES = [
+    # Bsz, T, H, P, N, G, Q, h0, steep
+    (2, 2048, 64, 16, 16, 1, 64, True, False),     # K = 2
+    (4, 4000, 64, 16, 32, 2, 64, True, False),     # K = 4, ragged last segment and chunk
+    (1, 8192, 64, 32, 64, 1, 64, False, False),    # K = 4
+    (4, 2100, 64, 16, 16, 1, 64, True, True),      # K = 4, exact-mode sub-chunks mixed in
+    (1, 16384, 64, 16, 16, 1, 128, True, False),   # K = 4 at chunk 128
+    (1, 70000, 64, 16, 16, 4, 256, True, True),    # K = 8 at chunk 256, steep, ragged
+]
+
+
+@pytest.mark.parametrize("case", SEGMENT_CASES, ids=lambda c: "B%dT%dH%dP%dN%dG%dQ%d" % c[:7])
+def test_real_segments(case):
+    Bsz, T, H, P, N, G, Q, with_h0, steep = case
+    K = _segment_chunks(Bsz, T, H, Q)
+    _print_case(kind="segments", K=K, case=case)
+    assert K > 1
+    inp = inputs.make_real(Bsz, T, H, P, N, G, dtype="bf16", seed=17, with_h0=with_h0)
+    if steep:
+        # every second chunk with steps near 1 on a fast head: decays of e^-16
+        # per token, sub-chunks in exact mode next to factored ones
+        inp["dt_min"], inp["dt_max"] = 1e-3, 1.0
+        inp["A"][: H // 2] = -16.0
+        nc = -(-T // Q)
+        for c in range(1, nc, 2):
+            inp["dt"][:, c * Q:(c + 1) * Q] += 4.0
+    y, hf = _gpu.run_real(inp, Q)
+    yr, hr = _oracle_real(inp)
+    assert report("y", y, yr) < TOL_BF16
+    assert report("h_final", hf, hr, "state") < TOL_BF16
+
+
+@pytest.mark.parametrize("shape", [(1, 300, 2, 64, 128, 1, 256), (4, 4096, 64, 16, 16, 1, 256)],
+                         ids=["K1", "K2"])
+def test_pivot_gap_below_fp32_range(shape):
+    """A decay of e^-1.8 per token (A = -18, every step 0.1): each half
+    sub-chunk decays by e^-57.6, inside the factored form's e^60 bound, so no
+    sub-chunk runs in exact mode, while the decay from one sub-chunk pivot to
+    the next, e^-115, is below fp32's range.  The state entering each
+    sub-chunk still carries a large share of its first outputs (e^-1.8)."""
+    Bsz, T, H, P, N, G, Q = shape
+    _print_case(edge="pivot gap", shape=shape, K=_segment_chunks(Bsz, T, H, Q))
+    inp = inputs.make_real(Bsz, T, H, P, N, G, dtype="bf16", seed=18, with_h0=True)
+    inp["A"] = np.full_like(inp["A"], -18.0)
+    inp["dt_min"], inp["dt_max"] = 0.1, 0.1
+    y, hf = _gpu.run_real(inp, Q)
+    yr, hr = _oracle_real(inp)
+    assert report("y", y, yr) < TOL_BF16
+    assert report("h_final", hf, hr, "state") < TOL_BF16
+
+
+def test_complex_pivot_gap_below_fp32_range():
+    """The complex form with Re A = -18 and every step 0.1: the same
+    pivot-to-pivot decay of e^-115 in its sub-chunk walk."""
+    _print_case(edge="complex pivot gap")
+    inp = inputs.make_complex(2, 300, 2, 64, 64, 2, seed=19, with_h0=True)
+    inp["A"][:, 0] = -18.0
+    inp["dt_min"], inp["dt_max"] = 0.1, 0.1
+    y, hf = _gpu.run_complex(inp, 256)
+    yr, hr = _oracle_cplx(inp)
+    assert report("y", y, yr) < TOL_F32
+    assert report("h_final", hf, hr, "state") < TOL_F32
