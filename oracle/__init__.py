@@ -283,3 +283,34 @@ def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=float("inf"
     if rc:
         raise ValueError("oracle rejected the sizes" if rc == 1 else "oracle out of memory")
     return out
+
+
+def _widen(a):
+    """float64 view of float32 values or of bfloat16 bit patterns (uint16)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def linear(x, W):
+    """A bias-free linear layer on the last axis, in float64: out[..., o] =
+    sum_i W[o, i] x[..., i] (the convention of the block's Linear layers:
+    W is (out_features, in_features)).  x, W: float32 or bfloat16 bit
+    patterns.  (Block Anatomy, section 6, rows 9-10: MIMO and out_proj are
+    single bias-free Linear layers; a matrix product is the one step.)"""
+    xw = _widen(x)
+    Ww = _widen(W)
+    if Ww.ndim != 2 or Ww.shape[1] != xw.shape[-1]:
+        raise ValueError(f"W {Ww.shape} does not take x's last axis {xw.shape[-1]}")
+    return xw @ Ww.T
+
+
+def mimo(y, W):
+    """The MIMO head mixer: y (Bsz, T, H, P) flattened per token to H*P
+    features head-major (feature h*P + p, the plain reshape of the block's
+    walkthrough), mixed by W (H*P, H*P), reshaped back to (Bsz, T, H, P).
+    (Block Anatomy, section 6, row 9; identity W leaves y unchanged.)"""
+    y = np.asarray(y)
+    Bsz, T, H, P = y.shape
+    return linear(y.reshape(Bsz, T, H * P), W).reshape(Bsz, T, H, P)

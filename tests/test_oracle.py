@@ -600,3 +600,94 @@ def test_bwd_log_decay_gradient_sums_to_dA():
     d = np.clip(np.logaddexp(0.0, inp["dt"].astype(np.float64) + inp["dt_bias"]),
                 inp["dt_min"], inp["dt_max"])
     np.testing.assert_allclose(g["dA"], (d * g["da"]).sum(axis=(0, 1)), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# MIMO head mixer and the bias-free linear layers (Block Anatomy, section 6,
+# rows 9-10)
+# --------------------------------------------------------------------------
+
+def _mimo_y(Bsz=2, T=5, H=4, P=3, seed=31):
+    return np.random.default_rng(seed).standard_normal((Bsz, T, H, P)).astype(np.float32)
+
+
+def test_mimo_identity_leaves_y_unchanged():
+    y = _mimo_y()
+    HP = y.shape[2] * y.shape[3]
+    np.testing.assert_array_equal(oracle.mimo(y, np.eye(HP, dtype=np.float32)), y.astype(np.float64))
+
+
+def test_mimo_head_permutation_permutes_heads():
+    """W = (permutation of heads) x I_P moves head perm[h]'s features to head
+    h: fails a d-major flatten or a transposed W."""
+    y = _mimo_y(H=5, P=3)
+    H, P = 5, 3
+    perm = [3, 0, 4, 1, 2]
+    W = np.zeros((H * P, H * P), np.float32)
+    for h in range(H):
+        for p in range(P):
+            W[h * P + p, perm[h] * P + p] = 1.0
+    z = oracle.mimo(y, W)
+    for h in range(H):
+        np.testing.assert_array_equal(z[:, :, h, :], y[:, :, perm[h], :].astype(np.float64))
+
+
+def test_mimo_single_entry_moves_one_feature():
+    """W with one entry c at (out = h_o*P + p_o, in = h_i*P + p_i): output
+    feature (h_o, p_o) is c times input feature (h_i, p_i), everything else 0."""
+    y = _mimo_y(H=4, P=3)
+    H, P = 4, 3
+    W = np.zeros((H * P, H * P), np.float32)
+    W[2 * P + 1, 0 * P + 2] = 2.5
+    z = oracle.mimo(y, W)
+    ref = np.zeros_like(z)
+    ref[:, :, 2, 1] = 2.5 * y[:, :, 0, 2].astype(np.float64)
+    np.testing.assert_array_equal(z, ref)
+
+
+def test_mimo_block_diagonal_mixes_within_heads_only():
+    """A block-diagonal W (one P x P block per head) mixes features inside
+    each head: each head's output depends on that head's input alone."""
+    H, P = 3, 4
+    rng = np.random.default_rng(5)
+    blocks = rng.standard_normal((H, P, P)).astype(np.float32)
+    W = np.zeros((H * P, H * P), np.float32)
+    for h in range(H):
+        W[h * P:(h + 1) * P, h * P:(h + 1) * P] = blocks[h]
+    y = _mimo_y(H=H, P=P)
+    z = oracle.mimo(y, W)
+    y2 = y.copy()
+    y2[:, :, 1, :] += 10.0   # perturb head 1 only
+    z2 = oracle.mimo(y2, W)
+    np.testing.assert_array_equal(z2[:, :, 0, :], z[:, :, 0, :])
+    np.testing.assert_array_equal(z2[:, :, 2, :], z[:, :, 2, :])
+    # head 1 follows its own block: the change is blocks[1] applied to the
+    # change of head 1's input (as stored in float32)
+    dy = y2[:, :, 1, :].astype(np.float64) - y[:, :, 1, :].astype(np.float64)
+    np.testing.assert_allclose(z2[:, :, 1, :] - z[:, :, 1, :],
+                               dy @ blocks[1].astype(np.float64).T, rtol=1e-9, atol=1e-9)
+
+
+def test_linear_reads_bf16_bits_exactly():
+    """bfloat16 bit patterns are widened exactly: W = 1.5 (0x3FC0) and x =
+    -0.375 (0xBEC0) give -0.5625 with no rounding."""
+    x = np.full((3, 64), 0xBEC0, np.uint16)
+    W = np.zeros((2, 64), np.uint16)
+    W[1, 7] = 0x3FC0
+    z = oracle.linear(x, W)
+    np.testing.assert_array_equal(z[:, 0], 0.0)
+    np.testing.assert_array_equal(z[:, 1], -0.5625)
+
+
+def test_linear_out_proj_shape_and_composition():
+    """out_proj after MIMO is the composition of the two maps: applying W_mimo
+    then W_out equals applying the product W_out W_mimo (float64, exact up to
+    rounding order)."""
+    rng = np.random.default_rng(7)
+    y = _mimo_y(H=2, P=4)
+    Wm = rng.standard_normal((8, 8)).astype(np.float32)
+    Wo = rng.standard_normal((6, 8)).astype(np.float32)
+    two = oracle.linear(oracle.mimo(y, Wm).reshape(2, 5, 8), Wo)
+    one = y.reshape(2, 5, 8).astype(np.float64) @ (Wo.astype(np.float64) @ Wm.astype(np.float64)).T
+    assert two.shape == (2, 5, 6)
+    np.testing.assert_allclose(two, one, rtol=1e-12, atol=1e-12)
