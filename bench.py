@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--workload", default="bitmamba_bf16",
                     choices=["bitmamba_bf16", "long_bf16", "mamba3lite_complex", "tiny_f32",
                              "decode_f32", "decode_complex", "conv_bf16", "conv_decode_f32",
-                             "bwd_bf16", "mamba3lite_packed"])
+                             "bwd_bf16", "mamba3lite_packed", "mimo_bf16"])
     ap.add_argument("--no-flush", action="store_true",
                     help="keep the Infinity Cache warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,6 +105,7 @@ KERNEL_SOURCES = {
     "conv_decode_f32": ["ssd_conv.hip"],
     "bwd_bf16": ["ssd_bwd_bf16.hip", "ssd_chunk_bf16.hip"],
     "mamba3lite_packed": ["ssd_chunk_cplx.hip"],
+    "mimo_bf16": ["ssd_linear.hip"],
 }
 
 
@@ -361,6 +362,8 @@ def main():
         return bench_conv(args, cfg)
     if cfg["kind"] == "bwd":
         return bench_bwd(args, cfg)
+    if cfg["kind"] == "mimo":
+        return bench_mimo(args, cfg)
     inp = inputs.make_workload(args.workload, seed=0)
     Q = cfg["chunk"]
     dims = dict(inp["dims"], Q=Q)
@@ -880,6 +883,81 @@ def bench_bwd(args, cfg):
             "value": reps * Bsz * T / total, "unit": "tokens/s", "cores": oracle.threads_used(),
             "kind": "oracle",
             "sample": f"the whole workload (float64 adjoint recurrence), {reps} passes in {total:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
+def bench_mimo(args, cfg):
+    """MIMO head mixer: one step = one ssd_mimo_fwd over the whole batch (B8
+    T2048, 1024 features per token, fp32 y in, bf16 W and z), the 512 MiB
+    flush read between steps.  Roofline: the matrix cores (2 M K N flops
+    against the bf16 dense peak), with the HBM figure beside it."""
+    import torch
+    import selective_state_space_09_amd as ssd
+    from selective_state_space_09_amd import inputs
+    inp = inputs.make_workload(args.workload, seed=0)
+    d = inp["dims"]
+    Bsz, T, H, P = d["Bsz"], d["T"], d["H"], d["P"]
+    dev = torch.device("cuda:0")
+    y = torch.from_numpy(inp["y"]).to(dev)
+    W = torch.from_numpy(inp["W"].view(np.int16)).view(torch.bfloat16).to(dev)
+    z = torch.empty((Bsz, T, H, P), dtype=torch.bfloat16, device=dev)
+    L = ssd.lib()
+    hip = Hip()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    M, K = Bsz * T, H * P
+    n_total = args.warmup + args.steps
+    evs = [(hip.event(), hip.event()) for _ in range(n_total)]
+    for i in range(n_total):
+        if flush is not None:
+            flush.max()
+        arr = (ctypes.c_void_p * 2)(evs[i][0].value, evs[i][1].value)
+        rc = L.ssd_linear_fwd_ev(ctypes.c_void_p(y.data_ptr()), ssd.SSD_F32,
+                                 ctypes.c_void_p(W.data_ptr()), ctypes.c_void_p(z.data_ptr()),
+                                 ssd.SSD_BF16, M, K, K, sp, arr)
+        if rc:
+            raise RuntimeError(L.ssd_last_error().decode())
+    torch.cuda.synchronize()
+    times = [hip.elapsed_ms(a, b) for a, b in evs[args.warmup:]]
+    ms = float(np.mean(times))
+    flops = 2.0 * M * K * K
+    nbytes = M * K * 4 + K * K * 2 + M * K * 2
+    tf = flops / (ms / 1e3) / 1e12
+    gbs = nbytes / (ms / 1e3) / 1e9
+    out = {"metric": "MIMO head mixer tokens/s (B8 T2048 H16 P64, 1024 x 1024 bf16 weight)",
+           "value": M / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms,
+           "ms_per_step_median": float(np.median(times)), "ms_per_step_min": float(np.min(times)),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": args.workload, "batch": Bsz, "seq_len": T, "heads": H,
+                      "headdim": P, "features": K, "x_dtype": "f32", "out_dtype": "bf16",
+                      "cache": "cold (Infinity Cache flushed between steps)"
+                      if flush is not None else "warm"},
+           "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS["bf16"],
+                        "unit": "TFLOP/s", "frac": tf / MFMA_PEAK_TFLOPS["bf16"],
+                        "traffic": measured_traffic(args.workload, "ssd_linear_kernel"),
+                        "kernel": "ssd_linear_kernel", "alg_flops": flops,
+                        "launch_us": ms * 1e3,
+                        "hbm": {"alg_bytes": nbytes, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS}},
+           "kernels": {"ssd_linear_kernel": {"avg_us": ms * 1e3, "alg_bytes": nbytes,
+                                             "alg_flops": flops}}}
+    if args.copy_ref:
+        copy_counter_reference(torch, dev)
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 256
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < args.cpu_seconds / 4:
+            oracle.mimo(inp["y"][:1, :rows], inp["W"])
+            reps += 1
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": reps * rows / el, "unit": "tokens/s",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "cpu_model": cpu_model(),
+                               "sample": f"{reps} passes over {rows} token rows (float64 numpy "
+                                         f"matrix product) in {el:.2f} s"}
     print(json.dumps(out), flush=True)
 
 

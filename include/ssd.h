@@ -393,6 +393,41 @@ int ssd_complex_chunk_fwd_packed_ev(const float *proj, long long ld, const float
                                     int H, int P, int N, int chunk, void *workspace,
                                     size_t workspace_bytes, void *stream, void *const *events);
 
+/*
+ * Bias-free linear layer z = x W^T row by row (z[m][n] = sum_k x[m][k] W[n][k],
+ * W stored (out_features, in_features)) on the matrix cores: bf16 operands,
+ * fp32 accumulation.  These are the MIMO head mixer and out_proj of the
+ * Mamba-3-Lite block (Block Anatomy, Numerical Stability & Scaling, section
+ * 6, rows 9-10: single bias-free Linear layers, run in bf16 under autocast).
+ *   x  (M, K)     x_dtype SSD_F32 (rounded to bf16, nearest even, as it is
+ *                 read) or SSD_BF16
+ *   W  (Nout, K)  bf16
+ *   z  (M, Nout)  z_dtype SSD_F32, or SSD_BF16 (rounded to nearest even from
+ *                 the fp32 sum)
+ * K a multiple of 64 (>= 64), Nout a multiple of 128 (>= 128), M >= 0.  x, W
+ * and z are caller-owned device memory, 16-byte aligned; no workspace.
+ * Errors: SSD_EINVAL for null/misaligned pointers or negative sizes,
+ * SSD_EUNSUPPORTED for K, Nout off those multiples, a bad dtype or a grid
+ * beyond 32 bits; validated before any HIP call.
+ */
+int ssd_linear_fwd(const void *x, int x_dtype, const void *W, void *z,
+                   int z_dtype, int M, int K, int Nout, void *stream);
+
+/* The same with a start/stop hipEvent_t pair (events[0], events[1]) bound to
+ * the kernel's dispatch, for measurement. */
+int ssd_linear_fwd_ev(const void *x, int x_dtype, const void *W, void *z,
+                      int z_dtype, int M, int K, int Nout, void *stream,
+                      void *const *events);
+
+/*
+ * The MIMO head mixer (Block Anatomy, section 6, row 9): y (Bsz, T, H, P), the
+ * scan output, read per token as H*P features head-major (feature h*P + p:
+ * the plain flatten of (H, P)), mixed by W (H*P, H*P): z (Bsz, T, H, P) =
+ * ssd_linear_fwd(y as (Bsz*T, H*P), W).  H*P must be a multiple of 128.
+ */
+int ssd_mimo_fwd(const void *y, int y_dtype, const void *W, void *z,
+                 int z_dtype, int Bsz, int T, int H, int P, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -79,6 +79,12 @@ def lib():
     L.ssd_conv1d_fwd.argtypes = [P, LL, P, P, P, I, P, P, P, P, I, I, I, I, I, I, P]
     L.ssd_conv1d_fwd_ev.restype = I
     L.ssd_conv1d_fwd_ev.argtypes = L.ssd_conv1d_fwd.argtypes + [P]
+    L.ssd_linear_fwd.restype = I
+    L.ssd_linear_fwd.argtypes = [P, I, P, P, I, I, I, I, P]
+    L.ssd_linear_fwd_ev.restype = I
+    L.ssd_linear_fwd_ev.argtypes = L.ssd_linear_fwd.argtypes + [P]
+    L.ssd_mimo_fwd.restype = I
+    L.ssd_mimo_fwd.argtypes = [P, I, P, P, I, I, I, I, I, P]
     L.ssd_conv1d_step.restype = I
     L.ssd_conv1d_step.argtypes = [P, P, LL, P, P, I, P, P, P, I, I, I, I, P]
     L.ssd_conv1d_step_ev.restype = I
@@ -524,3 +530,52 @@ def ssd_complex_chunk_fwd_packed(proj, A, H, P, N, dt_bias=None, dt_min=0.0, dt_
                                               _ptr(hf), Bsz, T, H, P, N, chunk, _ptr(ws),
                                               ws.numel(), _stream(stream)))
     return (y, hf) if return_final_state else y
+
+
+def _dcode(dtype, name):
+    if dtype == torch.bfloat16:
+        return SSD_BF16
+    if dtype == torch.float32:
+        return SSD_F32
+    raise TypeError(f"{name} must be float32 or bfloat16, got {dtype}")
+
+
+def ssd_linear_fwd(x, W, z=None, out_dtype=torch.bfloat16, stream=None):
+    """Bias-free linear layer z = x W^T on the last axis: x (..., K) float32 or
+    bfloat16, W (Nout, K) bfloat16, z (..., Nout) in out_dtype (bf16 matrix
+    products, fp32 accumulation).  K % 64 == 0, Nout % 128 == 0."""
+    _ndim(W, "W", 2)
+    Nout, K = W.shape
+    if x.dim() < 1 or x.shape[-1] != K:
+        raise ValueError(f"x has shape {tuple(x.shape)}, its last axis must be K={K}")
+    if z is not None:
+        _expect(z, "z", tuple(x.shape[:-1]) + (Nout,), x)
+    xd = _dcode(x.dtype, "x")
+    _dev(x, "x")
+    _dev(W, "W", torch.bfloat16)
+    if z is None:
+        z = torch.empty(tuple(x.shape[:-1]) + (Nout,), dtype=out_dtype, device=x.device)
+    zd = _dcode(z.dtype, "z")
+    _dev(z, "z")
+    M = x.numel() // K
+    _check(lib().ssd_linear_fwd(_ptr(x), xd, _ptr(W), _ptr(z), zd, M, K, Nout, _stream(stream)))
+    return z
+
+
+def ssd_mimo_fwd(y, W, z=None, out_dtype=torch.bfloat16, stream=None):
+    """MIMO head mixer: y (Bsz, T, H, P) float32 or bfloat16, read per token as
+    H*P features head-major; W (H*P, H*P) bfloat16; returns z (Bsz, T, H, P)
+    in out_dtype.  H*P % 128 == 0."""
+    _ndim(y, "y", 4)
+    Bsz, T, H, P = y.shape
+    _expect(W, "W", (H * P, H * P), y)
+    _expect(z, "z", (Bsz, T, H, P), y)
+    yd = _dcode(y.dtype, "y")
+    _dev(y, "y")
+    _dev(W, "W", torch.bfloat16)
+    if z is None:
+        z = torch.empty((Bsz, T, H, P), dtype=out_dtype, device=y.device)
+    zd = _dcode(z.dtype, "z")
+    _dev(z, "z")
+    _check(lib().ssd_mimo_fwd(_ptr(y), yd, _ptr(W), _ptr(z), zd, Bsz, T, H, P, _stream(stream)))
+    return z

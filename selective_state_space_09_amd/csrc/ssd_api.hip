@@ -559,3 +559,49 @@ int ssd_chunk_bwd_ev(const void* x, const float* dt, const float* A, const void*
 }
 
 }  // extern "C"
+
+// ---- bias-free linear layers (MIMO, out_proj) ----
+
+extern "C" {
+
+int ssd_linear_fwd_ev(const void* x, int x_dtype, const void* W, void* z, int z_dtype, int M,
+                      int K, int Nout, void* stream, void* const* events) {
+  if (M < 0 || K <= 0 || Nout <= 0)
+    return fail(SSD_EINVAL, "sizes must be positive (M >= 0): M=%d K=%d Nout=%d", M, K, Nout);
+  if (K % 64 != 0) return fail(SSD_EUNSUPPORTED, "K=%d is not a multiple of 64", K);
+  if (Nout % 128 != 0) return fail(SSD_EUNSUPPORTED, "Nout=%d is not a multiple of 128", Nout);
+  if ((x_dtype != SSD_F32 && x_dtype != SSD_BF16) || (z_dtype != SSD_F32 && z_dtype != SSD_BF16))
+    return fail(SSD_EUNSUPPORTED, "x_dtype=%d z_dtype=%d: each must be SSD_F32 or SSD_BF16",
+                x_dtype, z_dtype);
+  // one block of 128 rows (x and z) and W are addressed by 32-bit byte offsets
+  if (128LL * K * 4 > 4294967295LL || 128LL * Nout * 4 > 4294967295LL ||
+      static_cast<long long>(Nout) * K * 2 > 4294967295LL)
+    return fail(SSD_EUNSUPPORTED, "K=%d Nout=%d too large", K, Nout);
+  const long long mblocks = (static_cast<long long>(M) + 127) / 128;
+  if ((mblocks + 7) / 8 * 8 * (Nout / 128) > 2147483647LL)
+    return fail(SSD_EUNSUPPORTED, "grid too large: M=%d Nout=%d", M, Nout);
+  SSD_TRY(check_ptr(x, "x", 16, M > 0));
+  SSD_TRY(check_ptr(W, "W", 16, true));
+  SSD_TRY(check_ptr(z, "z", 16, M > 0));
+  ssd::LinearArgs a{x, x_dtype, static_cast<const uint16_t*>(W), z, z_dtype, M, K, Nout,
+                    reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_linear(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssd_linear_fwd(const void* x, int x_dtype, const void* W, void* z, int z_dtype, int M, int K,
+                   int Nout, void* stream) {
+  return ssd_linear_fwd_ev(x, x_dtype, W, z, z_dtype, M, K, Nout, stream, nullptr);
+}
+
+int ssd_mimo_fwd(const void* y, int y_dtype, const void* W, void* z, int z_dtype, int Bsz, int T,
+                 int H, int P, void* stream) {
+  if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0)
+    return fail(SSD_EINVAL, "sizes must be positive (T >= 0): Bsz=%d T=%d H=%d P=%d", Bsz, T, H, P);
+  const long long M = static_cast<long long>(Bsz) * T, HP = static_cast<long long>(H) * P;
+  if (M > 2147483647LL || HP > 2147483647LL)
+    return fail(SSD_EUNSUPPORTED, "Bsz*T=%lld or H*P=%lld too large", M, HP);
+  return ssd_linear_fwd_ev(y, y_dtype, W, z, z_dtype, static_cast<int>(M), static_cast<int>(HP),
+                           static_cast<int>(HP), stream, nullptr);
+}
+
+}  // extern "C"

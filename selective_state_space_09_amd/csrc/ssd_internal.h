@@ -78,6 +78,16 @@ struct BwdArgs {
   hipEvent_t* events;  // NULL, or 22: start/stop of each of the 11 kernels
 };
 
+struct LinearArgs {
+  const void* x;        // (M, K), fp32 (x_dtype 0) or bf16 (1)
+  int x_dtype;
+  const uint16_t* W;    // (Nout, K) bf16
+  void* z;              // (M, Nout), fp32 (z_dtype 0) or bf16 (1)
+  int z_dtype;
+  int M, K, Nout;
+  hipEvent_t* events;   // NULL, or start/stop of the kernel
+};
+
 // floats of chunk-boundary states: (Bsz, nc, H, P, KC), KC = N or 2N
 inline size_t workspace_state_floats(int Bsz, int nc, int H, int P, int KC) {
   return static_cast<size_t>(Bsz) * nc * H * P * KC;
@@ -163,6 +173,7 @@ hipError_t run_chunk_bwd_bf16(const BwdArgs& a, hipStream_t st);
 size_t bwd_workspace_bytes(int Bsz, int T, int H, int P, int G, int N, int chunk);
 int bwd_heads_per_group(int H, int G);
 hipError_t run_conv1d(const ConvArgs& a, hipStream_t st);
+hipError_t run_linear(const LinearArgs& a, hipStream_t st);  // K % 64 == 0, Nout % 128 == 0
 hipError_t run_conv1d_step(const ConvArgs& a, hipStream_t st);  // float32, T = 1
 int conv_tokens_per_thread();
 

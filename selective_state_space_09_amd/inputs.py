@@ -57,6 +57,9 @@ WORKLOADS = {
     # its single-token step at the decode batch of decode_f32, 64 steps in place
     "conv_decode_f32": dict(kind="conv_decode", Bsz=256, HP=4096, GN=128, ld=8512, K=4,
                             steps=64),
+    # the MIMO head mixer after the Mamba-3-Lite scan: its fp32 output y (B8 T2048,
+    # H16 P64 -> 1024 features per token) times a bf16 (1024, 1024) weight, bf16 out
+    "mimo_bf16": dict(kind="mimo", Bsz=8, T=2048, H=16, P=64),
 }
 
 DT_MIN = 1e-3
@@ -282,4 +285,21 @@ def make_workload(name, seed=0, **overrides):
         return inp
     if kind == "conv_decode":
         return make_conv_decode(seed=seed, **cfg)
+    if kind == "mimo":
+        return make_mimo(seed=seed, **cfg)
     return make_decode(seed=seed, **cfg)
+
+
+def make_mimo(Bsz, T, H, P, seed=0, identity=False, **_ignored):
+    """MIMO inputs: y (Bsz, T, H, P) ~ N(0, 1) float32 (the scan output) and W
+    (H*P, H*P) as bfloat16 bits, N(0, 1/(H*P)) (a mixed, trained-like weight;
+    the block initialises it to the identity, identity=True)."""
+    rng = np.random.default_rng(seed)
+    y = _normal(rng, (Bsz, T, H, P))
+    HP = H * P
+    if identity:
+        W = np.eye(HP, dtype=np.float32)
+    else:
+        W = _normal(rng, (HP, HP), 1.0 / math.sqrt(HP))
+    return {"kind": "mimo", "y": y, "W": f32_to_bf16_bits(W),
+            "dims": dict(Bsz=Bsz, T=T, H=H, P=P)}
