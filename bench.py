@@ -731,7 +731,7 @@ def bwd_kernel_costs(dims, nparts):
     nb = -(-Q // 64)
     x = Bsz * T * H * P * 2                 # x, dy, dx (bf16)
     bc = Bsz * T * G * N * 2                # B or C (bf16)
-    st = Bsz * nc * H * P * N * 2           # bf16 chunk / boundary / adjoint states
+    st = Bsz * nc * H * P * N * 4           # fp32 chunk / boundary / adjoint states
     tok = Bsz * nc * H * Q * 8              # (cs, delta) per token
     dec = Bsz * H * nc * 4
     pt = Bsz * T * H * 4                    # one fp32 value per token and head

@@ -31,8 +31,14 @@
 //   row_u = sum_{s < u} E[u][s]
 // (strictly below the diagonal; each of col_u, row_u and their difference
 // is made of the terms next to the diagonal, so the scan stays well scaled).
+// The terms of da_t and x_t . v_t cancel (their magnitudes can sum to tens
+// of times the result), so everything that feeds them is fp32-accurate: the
+// boundary states h_in(c), G_c and R_c are fp32, and a product of an fp32
+// operand with bf16 data is taken as two bf16 products (the operand split
+// into bf16 hi + lo).  Only dx, dB and dC's own products, which no gradient
+// subtracts from, use single bf16 operands.
 // The pieces:
-//   forward recompute   chunk states, boundary states h_in(c) and the
+//   forward recompute   chunk states, boundary states h_in(c) (fp32) and the
 //                       per-token (cs, delta) table (the forward's kernels)
 //   ssd_adj_state       G_c per (batch, chunk, head), MFMA over tokens
 //   ssd_adj_pass        R_c in place over G_c, dh0
@@ -64,14 +70,39 @@ __device__ __forceinline__ uint4 lds_row8(const uint16_t* tile, int pitch, int r
   return *reinterpret_cast<const uint4*>(tile + row * pitch + col);
 }
 
-// the 8 bf16 of v times f, rounded back to bf16
-__device__ __forceinline__ uint4 scale8(uint4 v, float f) {
+// The 8 bf16 of v times f as an unevaluated pair of bf16 vectors hi + lo
+// (hi = f v rounded, lo = the rest rounded): ~2^-17 relative, so that a
+// matrix product with an exact bf16 operand, taken as two products, is
+// accurate to fp32 level.
+__device__ __forceinline__ void split8(uint4 v, float f, uint4& hi, uint4& lo) {
   const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = pack_bf16x2(bf16_bits_to_f32(a[j] & 0xFFFFu) * f, bf16_bits_to_f32(a[j] >> 16) * f);
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  for (int j = 0; j < 4; ++j) split_bf16x2(bf16_bits_to_f32(a[j] & 0xFFFFu) * f, bf16_bits_to_f32(a[j] >> 16) * f, h[j], l[j]);
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Copies an fp32 (ROWS, 8 * VPR) tile from a buffer (row r at byte r *
+// row_bytes) into two LDS bf16 tiles of pitch `pitch`: its leading part
+// round(v) into `hi` and the remainder round(v - round(v)) into `lo`.
+template <int VPR, int ROWS>
+__device__ __forceinline__ void stage_rows_split(uint16_t* hi, uint16_t* lo, int pitch, buf_t src,
+                                                 uint32_t row_bytes) {
+  constexpr int ITEMS = 2 * VPR * ROWS;  // 16-byte (4-float) pieces
+#pragma unroll
+  for (int it0 = 0; it0 < ITEMS; it0 += kThreads) {
+    const int it = it0 + static_cast<int>(threadIdx.x);
+    if (ITEMS % kThreads == 0 || it < ITEMS) {
+      const int v = it % (2 * VPR), r = it / (2 * VPR);
+      const uint4 u = buf_load16(src, static_cast<uint32_t>(r) * row_bytes + v * 16);
+      uint32_t h0, l0, h1, l1;
+      split_bf16x2(__uint_as_float(u.x), __uint_as_float(u.y), h0, l0);
+      split_bf16x2(__uint_as_float(u.z), __uint_as_float(u.w), h1, l1);
+      *reinterpret_cast<uint2*>(hi + r * pitch + v * 4) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(lo + r * pitch + v * 4) = make_uint2(l0, l1);
+    }
+  }
 }
 
 // Copies `rows` rows of `VPR` 16-byte vectors from a buffer (row r at byte
@@ -142,22 +173,26 @@ __device__ __forceinline__ float transpose_sum16(const float (&v)[16]) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// G_c[p][n] = sum_l e^{cs_l} dy_l[p] C_l[n], one workgroup per (batch, chunk,
-// head), computed transposed (D[n][p], contraction over tokens on MFMA with
-// operands from the LDS transpose read) so that a lane holds one p and four
-// consecutive n: 8-byte bf16 stores in the (P, N) layout of the states.  With
-// two n tiles per wave they go in pairs with permuted n (the transpose read's
-// 4-column pieces 8 apart): 8 consecutive n, 16-byte stores.
+// G_c[p][n] = sum_l e^{cs_l} dy_l[p] C_l[n] (fp32), one workgroup per (batch,
+// chunk, head), computed transposed (D[n][p], contraction over tokens on MFMA
+// with operands from the LDS transpose read) so that a lane holds one p and
+// four consecutive n.  The weighted rows e^{cs_l} dy_l are split into bf16
+// hi + lo (two products with the exact bf16 C): G and the adjoint states
+// built from it feed the step-size gradient, whose terms cancel (the sum of
+// their magnitudes is tens of times the result), so they are kept to fp32
+// accuracy.  With two n tiles per wave they go in pairs with permuted n (the
+// transpose read's 4-column pieces 8 apart): 8 consecutive n, 32-byte stores.
 // ---------------------------------------------------------------------------
 template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ Cm,
-    const float2* __restrict__ tok, uint16_t* __restrict__ adj, int T, int H, int G, int Q, int nc,
+    const float2* __restrict__ tok, float* __restrict__ adj, int T, int H, int G, int Q, int nc,
     int npairs) {
   constexpr int YP = P + 16, CP = N + 16;
   constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4;  // n tiles per wave
   constexpr bool kPairN = NTW % 2 == 0;  // wave w: n tiles NTW w + i (paired), else w, w + 4, ..
-  __shared__ __attribute__((aligned(16))) uint16_t yl[kBlk * YP];  // e^{cs_l} dy_l
+  __shared__ __attribute__((aligned(16))) uint16_t yl[kBlk * YP];  // e^{cs_l} dy_l, hi
+  __shared__ __attribute__((aligned(16))) uint16_t ylo[kBlk * YP];  // and lo
   __shared__ __attribute__((aligned(16))) uint16_t cl[kBlk * CP];  // C_l
   __shared__ float wl[256];
 
@@ -192,14 +227,16 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
       if ((kBlk * (P / 8)) % kThreads == 0 || it < kBlk * (P / 8)) {
         const int v = it % (P / 8), r = it / (P / 8);
         const float w = l0 + r < Q ? wl[l0 + r] : 0.0f;
-        *reinterpret_cast<uint4*>(yl + r * YP + v * 8) =
-            scale8(buf_load16(ybuf, static_cast<uint32_t>(l0 + r) * yrow + v * 16), w);
+        uint4 hi, lo;
+        split8(buf_load16(ybuf, static_cast<uint32_t>(l0 + r) * yrow + v * 16), w, hi, lo);
+        *reinterpret_cast<uint4*>(yl + r * YP + v * 8) = hi;
+        *reinterpret_cast<uint4*>(ylo + r * YP + v * 8) = lo;
       }
     }
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < kBlk; ks += 32) {
-      uint4 af[NTW], bf[PT];
+      uint4 af[NTW], bf[PT], bfl[PT];
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
         const int nt = kPairN ? NTW * wid + i : wid + 4 * i;
@@ -213,24 +250,29 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
         const uint2 lo = lds_tr4(yl, YP, ks + 8 * q, j * 16);
         const uint2 hi = lds_tr4(yl, YP, ks + 8 * q + 4, j * 16);
         bf[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        const uint2 lo2 = lds_tr4(ylo, YP, ks + 8 * q, j * 16);
+        const uint2 hi2 = lds_tr4(ylo, YP, ks + 8 * q + 4, j * 16);
+        bfl[j] = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
       }
 #pragma unroll
       for (int i = 0; i < NTW; ++i)
 #pragma unroll
-        for (int j = 0; j < PT; ++j) acc[i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+        for (int j = 0; j < PT; ++j) {
+          acc[i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j]);
+          acc[i][j] = mfma_bf16(as_bf16x8(af[i]), as_bf16x8(bfl[j]), acc[i][j]);
+        }
     }
   }
-  uint16_t* dst = adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N);
+  float* dst = adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N);
   if constexpr (kPairN) {
 #pragma unroll
     for (int i = 0; i < NTW; i += 2)
 #pragma unroll
       for (int j = 0; j < PT; ++j) {
         const int m = (NTW * wid + i) >> 1;  // n = 32 m + 8q .. +7
-        *reinterpret_cast<uint4*>(dst + (j * 16 + r16) * N + 32 * m + 8 * q) =
-            make_uint4(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]),
-                       pack_bf16x2(acc[i + 1][j][0], acc[i + 1][j][1]),
-                       pack_bf16x2(acc[i + 1][j][2], acc[i + 1][j][3]));
+        float* o = dst + (j * 16 + r16) * N + 32 * m + 8 * q;
+        *reinterpret_cast<f32x4*>(o) = acc[i][j];
+        *reinterpret_cast<f32x4*>(o + 4) = acc[i + 1][j];
       }
   } else {
 #pragma unroll
@@ -238,8 +280,7 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
 #pragma unroll
       for (int j = 0; j < PT; ++j) {
         const int nt = wid + 4 * i;
-        *reinterpret_cast<uint2*>(dst + (j * 16 + r16) * N + nt * 16 + 4 * q) =
-            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+        *reinterpret_cast<f32x4*>(dst + (j * 16 + r16) * N + nt * 16 + 4 * q) = acc[i][j];
       }
   }
 }
@@ -247,10 +288,10 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
 // ---------------------------------------------------------------------------
 // Adjoint passing, last chunk first:  R_{nc-1} = dh_final,
 // R_{c-1} = lambda_c R_c + G_c,  dh0 = R_{-1}.  R_c overwrites G_c in place
-// (bf16); the running adjoint is fp32.  One thread per 4 consecutive n.
+// (fp32, after G_c is consumed).  One thread per 4 consecutive n.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ssd_adj_pass_kernel(
-    uint16_t* __restrict__ adj, const float* __restrict__ decay, const float* __restrict__ dh_final,
+    float* __restrict__ adj, const float* __restrict__ decay, const float* __restrict__ dh_final,
     float* __restrict__ dh0, int H, int PN, int nc) {
   constexpr int PF = 8;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -258,18 +299,18 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_pass_kernel(
   if (e4 * 4 >= PN) return;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t cstride = static_cast<size_t>(H) * PN;
-  uint16_t* base = adj + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e4 * 4;
+  float* base = adj + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e4 * 4;
   const float* dc = decay + bh * nc;
   float4 r = dh_final ? *reinterpret_cast<const float4*>(dh_final + bh * PN + e4 * 4)
                       : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c1 = nc; c1 > 0; c1 -= PF) {  // chunks c1-1 down to c1-PF
-    uint2 gv[PF];
+    float4 gv[PF];
     float ld[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int cc = c1 - 1 - j;
       if (cc >= 0) {
-        gv[j] = *reinterpret_cast<const uint2*>(base + cc * cstride);
+        gv[j] = *reinterpret_cast<const float4*>(base + cc * cstride);
         ld[j] = dc[cc];
       }
     }
@@ -277,13 +318,13 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_pass_kernel(
     for (int j = 0; j < PF; ++j) {
       const int cc = c1 - 1 - j;
       if (cc >= 0) {
-        *reinterpret_cast<uint2*>(base + cc * cstride) =
-            make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+        const float4 hold = r;
         const float l = ld[j];
-        r.x = l * r.x + bf16_bits_to_f32(gv[j].x & 0xFFFFu);
-        r.y = l * r.y + bf16_bits_to_f32(gv[j].x >> 16);
-        r.z = l * r.z + bf16_bits_to_f32(gv[j].y & 0xFFFFu);
-        r.w = l * r.w + bf16_bits_to_f32(gv[j].y >> 16);
+        r.x = l * r.x + gv[j].x;
+        r.y = l * r.y + gv[j].y;
+        r.z = l * r.z + gv[j].z;
+        r.w = l * r.w + gv[j].w;
+        *reinterpret_cast<float4*>(base + cc * cstride) = hold;
       }
     }
   }
@@ -330,7 +371,11 @@ __device__ __forceinline__ bool block_unit(int ngroups, int nc, int nb, int Bsz,
 // the mask and decay are the B operands (columns s, contraction over l) of the
 // transposed products v^T += dy^T M and dB^T += C^T W, whose A operands (dy and
 // C) come from LDS by the transpose read: a lane ends with one s of v and dB
-// and runs of consecutive p or n (16-byte stores of dx and the dB partials).  The same
+// and runs of consecutive p or n (16-byte stores of dx and the dB partials).
+// v feeds x.v and f2, which enter the step-size gradient where its terms cancel,
+// so its products are fp32-accurate: R_c (fp32) is staged as bf16 hi + lo and
+// M as hi + lo, each product taken twice; W (which only reaches dB) is one bf16
+// operand.  The same
 // fp32 tiles give the box terms E[l][s] (l > s): each lane sums its column
 // over the l blocks (col_s, once per head), and a transposing reduction over
 // the 16 columns of each lane group gives the rows' sums (the block's share of
@@ -341,18 +386,20 @@ template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dy, const float* __restrict__ D, const float2* __restrict__ tok,
-    const uint16_t* __restrict__ adj, uint16_t* __restrict__ dx, float* __restrict__ xv,
+    const float* __restrict__ adj, uint16_t* __restrict__ dx, float* __restrict__ xv,
     float* __restrict__ dyx, float* __restrict__ f2o, float* __restrict__ colp,
     float* __restrict__ rowp, float* __restrict__ dBp, int Bsz, int T, int H, int G, int Q, int nc,
     int HPG) {
   constexpr int XP = P + 16, NP = N + 16;
   constexpr int PT = P / 16, NT = N / 16;
   static_assert(P % 32 == 0, "v tiles go in pairs of 16 p");
-  __shared__ __attribute__((aligned(16))) uint16_t Cs[kBlk * NP];  // C rows of the l block
+  static_assert(P <= kBlk, "R_c's lo part is staged in the C tile");
+  // C rows of the l block; before the l blocks of a head, the lo part of R_c
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[kBlk * NP];
   __shared__ __attribute__((aligned(16))) uint16_t Ys[kBlk * XP];  // dy rows of the l block
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kBlk * NP];  // B rows of the s block
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kBlk * XP];  // x rows of the s block
-  __shared__ __attribute__((aligned(16))) uint16_t Rs[P * NP];     // R_c of the head
+  __shared__ __attribute__((aligned(16))) uint16_t Rs[P * NP];     // R_c of the head, hi part
   __shared__ __attribute__((aligned(16))) float cs2[256];  // cs_l log2(e) of the chunk's tokens
   __shared__ float dlt[256];                               // delta_l
   __shared__ float rows[2][4][kBlk];  // per l-block parity and wave: row share of each row l
@@ -389,10 +436,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
                                 static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
     const buf_t rbuf = make_buf(adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
-                                static_cast<uint32_t>(P) * N * 2);
+                                static_cast<uint32_t>(P) * N * 4);
     __syncthreads();  // previous head done with Xs, Rs, cs2, dlt, Ys, Cs
     stage_rows<P / 8, kBlk>(Xs, XP, xbuf, xrow, s0);
-    stage_rows<N / 8, P>(Rs, NP, rbuf, N * 2, 0);
+    stage_rows_split<N / 8, P>(Rs, Cs, NP, rbuf, N * 4);
     if (tid < Q) {
       const float2 t2 = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
       cs2[tid] = t2.x * kLog2e;
@@ -418,8 +465,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     for (int ks = 0; ks < N; ks += 32) {
       const uint4 bb = lds_row8(Bs, NP, sr, ks + 8 * q);
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
+      for (int pt = 0; pt < PT; ++pt) {
         v[pt] = mfma_bf16(as_bf16x8(lds_row8(Rs, NP, vp(pt, r16), ks + 8 * q)), as_bf16x8(bb), v[pt]);
+        v[pt] = mfma_bf16(as_bf16x8(lds_row8(Cs, NP, vp(pt, r16), ks + 8 * q)), as_bf16x8(bb), v[pt]);
+      }
     }
     {
       const float fr = __builtin_amdgcn_exp2f(tot - cs_s);
@@ -445,19 +494,28 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
       const float part = group_total(xdot(Xs + sr * XP));
       if (q == 0 && sl < Lc) f2o[(r0 + sl) * H + h] = dl_s * part;
     }
-    // boundary part of dB: delta_s e^{tot-cs_s} (x_s R)[n] (B columns s = this lane's sl)
+    // boundary part of dB: delta_s e^{tot-cs_s} (x_s R)[n] (B columns s = this lane's sl),
+    // x_s R from the exact x rows and both parts of R, scaled in fp32
     {
-      const float f2 = dl_s * __builtin_amdgcn_exp2f(tot - cs_s);
+      f32x4 xr[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) xr[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < P; ks += 32) {
-        const uint4 a = scale8(lds_row8(Xs, XP, 16 * w + r16, ks + 8 * q), f2);
+        const uint4 a = lds_row8(Xs, XP, 16 * w + r16, ks + 8 * q);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const uint2 lo = lds_tr4(Rs, NP, ks + 8 * q, nt * 16);
           const uint2 hi = lds_tr4(Rs, NP, ks + 8 * q + 4, nt * 16);
-          dB[nt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(a), dB[nt]);
+          xr[nt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(a), xr[nt]);
+          const uint2 lo2 = lds_tr4(Cs, NP, ks + 8 * q, nt * 16);
+          const uint2 hi2 = lds_tr4(Cs, NP, ks + 8 * q + 4, nt * 16);
+          xr[nt] = mfma_bf16(as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y)), as_bf16x8(a), xr[nt]);
         }
       }
+      const float f2 = dl_s * __builtin_amdgcn_exp2f(tot - cs_s);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) dB[nt] += xr[nt] * f2;
     }
 
     float col = 0.0f;  // this lane's rows of sum_{l > s} E[l][s], column s = sl
@@ -499,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
       }
       // mask and decay -> bf16 A operands (k slot of lane group q: l = 16 lt + 4q + i)
       // and the fp32 box terms E[l][s] (l > s only)
-      uint32_t am[4][2], aw[4][2];
+      uint32_t am[4][2], aml[4][2], aw[4][2];
       float ee[16];
       auto decay = [&](auto masked) {
 #pragma unroll
@@ -530,8 +588,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
               ee[4 * lt + i] = wv[i] * s1[lt][i];
             }
           }
-          am[lt][0] = pack_bf16x2(mv[0], mv[1]);
-          am[lt][1] = pack_bf16x2(mv[2], mv[3]);
+          split_bf16x2(mv[0], mv[1], am[lt][0], aml[lt][0]);
+          split_bf16x2(mv[2], mv[3], am[lt][1], aml[lt][1]);
           aw[lt][0] = pack_bf16x2(wv[0], wv[1]);
           aw[lt][1] = pack_bf16x2(wv[2], wv[3]);
         }
@@ -544,13 +602,16 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const uint4 Am = make_uint4(am[2 * kk][0], am[2 * kk][1], am[2 * kk + 1][0], am[2 * kk + 1][1]);
+        const uint4 Aml = make_uint4(aml[2 * kk][0], aml[2 * kk][1], aml[2 * kk + 1][0], aml[2 * kk + 1][1]);
         const uint4 Aw = make_uint4(aw[2 * kk][0], aw[2 * kk][1], aw[2 * kk + 1][0], aw[2 * kk + 1][1]);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
           const int c0 = 32 * (pt >> 1) + 4 * (pt & 1);
           const uint2 lo = lds_tr4s<8>(Ys, XP, 32 * kk + 4 * q, c0);
           const uint2 hi = lds_tr4s<8>(Ys, XP, 32 * kk + 16 + 4 * q, c0);
-          v[pt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(Am), v[pt]);
+          const bf16x8 yt = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          v[pt] = mfma_bf16(yt, as_bf16x8(Am), v[pt]);
+          v[pt] = mfma_bf16(yt, as_bf16x8(Aml), v[pt]);
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -630,19 +691,24 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
 // which after the decay are the B operand of dC^T += B^T W^T, so that a lane
 // ends with one row l of dC and 4 consecutive n per tile (16-byte stores).
 // Per head: f1_l = C_l . (the H_in part of dC_h[l]); after the group: dC.
+// f1 enters the step-size gradient where its terms cancel, so the H_in part
+// is fp32-accurate: H_in (fp32) is staged as bf16 hi + lo, multiplied by the
+// exact dy rows, and the product scaled by e^{cs_l} in fp32.
 // ---------------------------------------------------------------------------
 template <int P, int N>
 __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dy, const float2* __restrict__ tok,
-    const uint16_t* __restrict__ states, float* __restrict__ f1o, float* __restrict__ dCp, int Bsz,
+    const float* __restrict__ states, float* __restrict__ f1o, float* __restrict__ dCp, int Bsz,
     int T, int H, int G, int Q, int nc, int HPG) {
   constexpr int XP = P + 16, NP = N + 16;
   constexpr int NT = N / 16;
+  static_assert(P <= kBlk, "h_in's lo part is staged in the B tile");
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kBlk * XP];  // x rows of the s block
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBlk * NP];  // B rows of the s block
+  // B rows of the s block; before the s blocks of a head, the lo part of h_in(c)
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBlk * NP];
   __shared__ __attribute__((aligned(16))) uint16_t Ys[kBlk * XP];  // dy rows of the l block
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[P * NP];     // h_in(c) of the head
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[P * NP];     // h_in(c) of the head, hi part
   __shared__ __attribute__((aligned(16))) uint16_t Cs[kBlk * NP];  // C rows of the l block
   __shared__ __attribute__((aligned(16))) float cs2[256];  // cs_s log2(e) of the chunk's tokens
   __shared__ __attribute__((aligned(16))) float dlt[256];  // delta_s
@@ -685,10 +751,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
     const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
                                 static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
     const buf_t hbuf = make_buf(states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
-                                static_cast<uint32_t>(P) * N * 2);
+                                static_cast<uint32_t>(P) * N * 4);
     __syncthreads();
     stage_rows<P / 8, kBlk>(Ys, XP, ybuf, xrow, l0);
-    stage_rows<N / 8, P>(Hs, NP, hbuf, N * 2, 0);
+    stage_rows_split<N / 8, P>(Hs, Bs, NP, hbuf, N * 4);
     if (tid < Q) {
       const float2 t2 = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
       cs2[tid] = t2.x * kLog2e;
@@ -704,17 +770,22 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) dC[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      const float f = __builtin_amdgcn_exp2f(cs_l);
 #pragma unroll
       for (int ks = 0; ks < P; ks += 32) {
-        const uint4 a = scale8(lds_row8(Ys, XP, 16 * w + r16, ks + 8 * q), f);
+        const uint4 a = lds_row8(Ys, XP, 16 * w + r16, ks + 8 * q);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const uint2 lo = lds_tr4(Hs, NP, ks + 8 * q, nt * 16);
           const uint2 hi = lds_tr4(Hs, NP, ks + 8 * q + 4, nt * 16);
           dC[nt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(a), dC[nt]);
+          const uint2 lo2 = lds_tr4(Bs, NP, ks + 8 * q, nt * 16);
+          const uint2 hi2 = lds_tr4(Bs, NP, ks + 8 * q + 4, nt * 16);
+          dC[nt] = mfma_bf16(as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y)), as_bf16x8(a), dC[nt]);
         }
       }
+      const float f = __builtin_amdgcn_exp2f(cs_l);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) dC[nt] = dC[nt] * f;
     }
     // f1_l = e^{cs_l} C_l . (H_in^T dy_l): the H_in part of C_l . dC_h[l]
     {
@@ -809,10 +880,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
 
 // ---------------------------------------------------------------------------
 // Chunk constants: e^{tot_c} <R_c, H_in(c)> (the term of da shared by every
-// step of chunk c), one workgroup per (chunk, head, batch).
+// step of chunk c), fp32 states, one workgroup per (chunk, head, batch).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ssd_bwd_const_kernel(
-    const uint16_t* __restrict__ adj, const uint16_t* __restrict__ states,
+    const float* __restrict__ adj, const float* __restrict__ states,
     const float* __restrict__ decay, double* __restrict__ cst, int H, int PN, int nc) {
   __shared__ double ws4[4];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -821,15 +892,18 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_const_kernel(
   const size_t slot = ((static_cast<size_t>(b) * nc + c) * H + h) * PN;
   double s = 0.0;
   for (int i = tid * 8; i < PN; i += kThreads * 8) {
-    const uint4 rv = *reinterpret_cast<const uint4*>(adj + slot + i);
-    const uint4 hv = *reinterpret_cast<const uint4*>(states + slot + i);
-    const uint32_t ra[4] = {rv.x, rv.y, rv.z, rv.w}, ha[4] = {hv.x, hv.y, hv.z, hv.w};
-    float acc = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc = fmaf(bf16_bits_to_f32(ra[k] & 0xFFFFu), bf16_bits_to_f32(ha[k] & 0xFFFFu), acc);
-      acc = fmaf(bf16_bits_to_f32(ra[k] >> 16), bf16_bits_to_f32(ha[k] >> 16), acc);
-    }
+    const float4 r0 = *reinterpret_cast<const float4*>(adj + slot + i);
+    const float4 r1 = *reinterpret_cast<const float4*>(adj + slot + i + 4);
+    const float4 h0v = *reinterpret_cast<const float4*>(states + slot + i);
+    const float4 h1v = *reinterpret_cast<const float4*>(states + slot + i + 4);
+    float acc = r0.x * h0v.x;
+    acc = fmaf(r0.y, h0v.y, acc);
+    acc = fmaf(r0.z, h0v.z, acc);
+    acc = fmaf(r0.w, h0v.w, acc);
+    acc = fmaf(r1.x, h1v.x, acc);
+    acc = fmaf(r1.y, h1v.y, acc);
+    acc = fmaf(r1.z, h1v.z, acc);
+    acc = fmaf(r1.w, h1v.w, acc);
     s += acc;
   }
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
@@ -973,7 +1047,7 @@ int bwd_heads_per_group(int H, int G) {
 }
 
 // workspace layout of the backward, after the forward's own (states, decays,
-// token table): the adjoint states (bf16); f1, f2, x.v, dy.x, col (fp32 per
+// token table): the adjoint states (fp32); f1, f2, x.v, dy.x, col (fp32 per
 // token and head); the row shares of the column blocks (fp32, one per block); the
 // chunk constants of da and the chunk shares of dA, ddt_bias, dD (fp64); the
 // dB and dC partials (fp32)
@@ -987,7 +1061,7 @@ static BwdLayout bwd_layout(int Bsz, int T, int H, int P, int G, int N, int chun
   size_t o = up(bf16_fwd_layout(Bsz, nc, H, P, N, chunk, 1).total);
   L.fwd = 0;
   L.adj = o;
-  o += up(static_cast<size_t>(Bsz) * nc * H * P * N * 2);
+  o += up(static_cast<size_t>(Bsz) * nc * H * P * N * 4);
   const size_t tok = static_cast<size_t>(Bsz) * T * H * 4;
   L.f1 = o;
   o += up(tok);
@@ -1050,10 +1124,11 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   hipError_t e = run_chunk_states_bf16(f, st);
   if (e != hipSuccess) return e;
   const Bf16FwdLayout FL = bf16_fwd_layout(a.Bsz, nc, a.H, P, N, Q, 1);
-  const uint16_t* states = reinterpret_cast<const uint16_t*>(ws + FL.Hin);  // h_in(c), bf16
+  // h_in(c) in fp32 (the recompute leaves it over the chunk states)
+  const float* states = reinterpret_cast<const float*>(ws + FL.S);
   const float* decay = reinterpret_cast<const float*>(ws + FL.decay);
   const float2* tok = reinterpret_cast<const float2*>(ws + FL.tok);
-  uint16_t* adj = reinterpret_cast<uint16_t*>(ws + L.adj);
+  float* adj = reinterpret_cast<float*>(ws + L.adj);
   float* f1 = reinterpret_cast<float*>(ws + L.f1);
   float* f2 = reinterpret_cast<float*>(ws + L.f2);
   float* col = reinterpret_cast<float*>(ws + L.col);
@@ -1076,13 +1151,13 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const int nb = (Q + kBlk - 1) / kBlk;
   const unsigned bblocks = static_cast<unsigned>(nb) * units_per_rank(a.H / HPG, nc, a.Bsz);
   launch_k(nc > 0, ssd_bwd_dxdb_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 8 : nullptr,
-           x, B, C, dy, a.D, tok, static_cast<const uint16_t*>(adj), static_cast<uint16_t*>(a.dx), xv,
+           x, B, C, dy, a.D, tok, static_cast<const float*>(adj), static_cast<uint16_t*>(a.dx), xv,
            dyx, f2, col, rowp, dBp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
   launch_k(nc > 0, ssd_bwd_dc_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 10 : nullptr,
            x, B, C, dy, tok, states, f1, dCp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
   double* cst = reinterpret_cast<double*>(ws + L.cst);
   launch_k(nc > 0, ssd_bwd_const_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
-           ev ? ev + 12 : nullptr, static_cast<const uint16_t*>(adj), states, decay, cst, a.H, P * N,
+           ev ? ev + 12 : nullptr, static_cast<const float*>(adj), states, decay, cst, a.H, P * N,
            nc);
   double* dtp = reinterpret_cast<double*>(ws + L.dtp);
   launch_k(nc > 0, ssd_bwd_dt_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,

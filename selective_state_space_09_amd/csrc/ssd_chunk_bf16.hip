@@ -50,6 +50,11 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
 template <int S>
 using Slot = std::integral_constant<int, S>;
 
+#ifndef SSD_STATE_PAIR_HEADS
+#define SSD_STATE_PAIR_HEADS 1
+#endif
+constexpr bool kStatePairHeads = SSD_STATE_PAIR_HEADS;
+
 // ---------------------------------------------------------------------------
 // Segment end states from a zero start, one workgroup per (batch, segment,
 // HPW heads of one group).  For each chunk c of the segment, with u_s = delta_1
@@ -302,16 +307,19 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// State passing between segments (fp32 segment states in, bf16 boundary
-// states out):
+// State passing between segments (fp32 segment states in, boundary states
+// out):
 //   h_in(0) = h0,  h_in(s+1) = lambda_s h_in(s) + S_s,  h_final = h_in(nseg)
 // (the chunkwise recurrence of the state across chunks, applied to segments),
-// fp32 running state.  One thread per 8 consecutive n of one p of one (batch,
-// head): 32-byte reads of S, 16-byte writes of the bf16 copy; PF segments in
-// flight.
+// fp32 running state.  The boundary states go out as the bf16 copy the output
+// kernel multiplies with (KEEP32 = false), or in fp32 over the segment states
+// they were made from (KEEP32 = true: for consumers that need them exact).
+// One thread per 8 consecutive n of one p of one (batch, head): 32-byte reads
+// of S, 16-byte writes of the bf16 copy; PF segments in flight.
 // ---------------------------------------------------------------------------
+template <bool KEEP32>
 __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
-    const float* __restrict__ S, uint16_t* __restrict__ hin, const float* __restrict__ decay,
+    float* __restrict__ S, uint16_t* __restrict__ hin, const float* __restrict__ decay,
     const float* __restrict__ h0, float* __restrict__ h_final, int H, int PN, int nseg) {
   constexpr int PF = 4;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t sstride = static_cast<size_t>(H) * PN;  // between segments of one (b, h)
   const size_t off = static_cast<size_t>(b) * nseg * sstride + h * static_cast<size_t>(PN) + e8 * 8;
-  const float* sp = S + off;
+  float* sp = S + off;
   uint16_t* hp = hin + off;
   const float* dc = decay + bh * nseg;
   float hv[8];
@@ -359,14 +367,24 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
     for (int j = 0; j < PF; ++j) {
       const int ss = s0 + j;
       if (ss < nseg) {
-        *reinterpret_cast<uint4*>(hp + ss * sstride) =
-            make_uint4(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
-                       pack_bf16x2(hv[6], hv[7]));
+        if constexpr (!KEEP32)
+          *reinterpret_cast<uint4*>(hp + ss * sstride) =
+              make_uint4(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
+                         pack_bf16x2(hv[6], hv[7]));
         const float l = cd[j];
         const float sv[8] = {cur[j][0].x, cur[j][0].y, cur[j][0].z, cur[j][0].w,
                              cur[j][1].x, cur[j][1].y, cur[j][1].z, cur[j][1].w};
+        float hold[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) hv[k] = l * hv[k] + sv[k];
+        for (int k = 0; k < 8; ++k) {
+          hold[k] = hv[k];
+          hv[k] = l * hv[k] + sv[k];
+        }
+        if constexpr (KEEP32) {
+          // the fp32 state entering segment ss over its own S (already consumed)
+          *reinterpret_cast<float4*>(sp + ss * sstride) = make_float4(hold[0], hold[1], hold[2], hold[3]);
+          *reinterpret_cast<float4*>(sp + ss * sstride + 4) = make_float4(hold[4], hold[5], hold[6], hold[7]);
+        }
       }
     }
 #pragma unroll
@@ -903,7 +921,7 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_outp
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
   const hipEvent_t* ev = a.events;
   // segment states: two heads per workgroup when the heads of a group pair up
-  if ((a.H / a.G) % 2 == 0)
+  if (kStatePairHeads && (a.H / a.G) % 2 == 0)
     launch_k(nc > 0, ssd_state_bf16_kernel<P, N, 2>, dim3(blocks / 2), dim3(512), st, ev, x, a.dt,
              a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, decay, tok, a.T, a.H, a.G, a.chunk, nc, K,
              nseg, npairs);
@@ -911,10 +929,18 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_outp
     launch_k(nc > 0, ssd_state_bf16_kernel<P, N, 1>, dim3(blocks), dim3(512), st, ev, x, a.dt,
              a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, decay, tok, a.T, a.H, a.G, a.chunk, nc, K,
              nseg, npairs);
-  launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel,
-           dim3((P * N / 8 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
-           ev ? ev + 2 : nullptr, static_cast<const float*>(S), hin, static_cast<const float*>(decay),
-           a.h0, a.h_final, a.H, P * N, nseg);
+  // without the outputs (the backward's recompute, K = 1) the fp32 boundary
+  // states are kept too, over the chunk states
+  if (with_output)
+    launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel<false>,
+             dim3((P * N / 8 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
+             ev ? ev + 2 : nullptr, S, hin, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
+             P * N, nseg);
+  else
+    launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel<true>,
+             dim3((P * N / 8 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
+             ev ? ev + 2 : nullptr, S, hin, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
+             P * N, nseg);
   if (!with_output) return hipGetLastError();
   // the kernel walks several chunks only when K > 1 (a separate build: the
   // per-chunk factor step inside its loop costs registers)
@@ -959,8 +985,9 @@ hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st) {
   return dispatch_bf16(a, st, true, bf16_segment_chunks(a.Bsz, nc, a.H, a.chunk));
 }
 
-// the per-chunk boundary states, decays, token table and h_final of a forward
-// call without its outputs (the backward recomputes these)
+// the per-chunk boundary states (fp32 over S, and their bf16 copies), decays,
+// token table and h_final of a forward call without its outputs (the backward
+// recomputes these)
 hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st) { return dispatch_bf16(a, st, false, 1); }
 
 }  // namespace ssd

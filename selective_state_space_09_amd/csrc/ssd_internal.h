@@ -167,7 +167,8 @@ hipError_t run_chunk_complex_packed(const ChunkArgs& a, int ld, hipStream_t st);
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t run_complex_decode(const DecodeArgs& a, hipStream_t st);  // D unused
 // state + pass kernels only, one chunk per segment (K = 1: per-chunk boundary
-// states, decays and the token table in bf16_fwd_layout(..., 1))
+// states, decays and the token table in bf16_fwd_layout(..., 1); the S region
+// then holds the fp32 boundary states h_in(c))
 hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_bwd_bf16(const BwdArgs& a, hipStream_t st);
 size_t bwd_workspace_bytes(int Bsz, int T, int H, int P, int G, int N, int chunk);

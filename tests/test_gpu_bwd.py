@@ -2,16 +2,18 @@
 the float64 oracle (oracle.bwd), through the C ABI.
 
 Bar: the bfloat16 tolerance of the scan, 2e-2 normwise -- max |got - ref| /
-max |ref| over each (batch, head) for dx and dh0, over each (batch, group)
-for dB and dC, over the heads for dD.  Where a gradient is a sum of terms that
-cancel, the error is measured against the magnitude of those terms (the usual
-error measure of a sum):
-  ddt_t = sigmoid(z_t) (A da_t + x_t.v_t): normwise per (batch, head) against
-          max_t of sigmoid(z_t)|A da_t| + |ddt_t - sigmoid(z_t) A da_t| (the
-          two summands; a lone token's ddt can be 300 times smaller than them);
-  dA, ddt_bias (sums over every token; sum |delta_t da_t| exceeds |dA| 20-40
-          times on these inputs): |got - ref| <= 2e-2 sum_{b,t} |delta_t da_t|
-          (resp. the summands of every ddt_t), per head.
+max |ref| over each (batch, head) for dx, dh0 and ddt, over each (batch,
+group) for dB and dC, over the heads for dD, dA and ddt_bias.  dA, ddt_bias
+and ddt are sums of terms that cancel (sum |delta_t da_t| exceeds |dA| 20-40
+times on these inputs, and a lone token's ddt can be 300 times smaller than
+its two summands), so the kernels form everything that feeds them to fp32
+accuracy; the plain normwise bar holds for them too.  Their errors against the
+magnitude of those terms (the usual error measure of a sum) are printed and
+held to the same bar:
+  ddt_t = sigmoid(z_t) (A da_t + x_t.v_t): per (batch, head) against max_t of
+          sigmoid(z_t)|A da_t| + |ddt_t - sigmoid(z_t) A da_t|;
+  dA, ddt_bias: |got - ref| <= 2e-2 sum_{b,t} |delta_t da_t| (resp. the
+          summands of every ddt_t), per head.
 Every case compares every element, the full B2 T2048 H64 P64 N128 workload
 included (the oracle computes it in about two seconds).
 """
@@ -97,20 +99,20 @@ def _ddt_err(got, ref, inp):
 
 def _compare(got, ref, inp, what=""):
     dl = _deltas(inp)
-    info = {"dA plain": _nerr(got["dA"], ref["dA"], None),
-            "ddt_bias plain": _nerr(got["ddt_bias"], ref["ddt_bias"], None),
-            "ddt plain": _nerr(got["ddt"], ref["ddt"], (0, 2))}
     checks = {
         "dx": _nerr(got["dx"], ref["dx"], (0, 2)),
-        "ddt": _ddt_err(got["ddt"], ref, inp),
+        "ddt": _nerr(got["ddt"], ref["ddt"], (0, 2)),
         "dB": _nerr(got["dB"], ref["dB"], (0, 2)),
         "dC": _nerr(got["dC"], ref["dC"], (0, 2)),
-        "dA": _sum_err(got["dA"], ref["dA"], dl * ref["da"]),
+        "dA": _nerr(got["dA"], ref["dA"], None),
         "dD": _nerr(got["dD"], ref["dD"], None),
-        "ddt_bias": _sum_err(got["ddt_bias"], ref["ddt_bias"], _ddt_mag(ref, inp)),
+        "ddt_bias": _nerr(got["ddt_bias"], ref["ddt_bias"], None),
         "dh0": _nerr(got["dh0"], ref["dh0"], (0, 1)),
+        "ddt vs summands": _ddt_err(got["ddt"], ref, inp),
+        "dA vs summands": _sum_err(got["dA"], ref["dA"], dl * ref["da"]),
+        "ddt_bias vs summands": _sum_err(got["ddt_bias"], ref["ddt_bias"], _ddt_mag(ref, inp)),
     }
-    print(what, {k: f"{v:.2e}" for k, v in {**checks, **info}.items()}, flush=True)
+    print(what, {k: f"{v:.2e}" for k, v in checks.items()}, flush=True)
     bad = {k: v for k, v in checks.items() if not v <= TOL}
     assert not bad, f"{what}: {bad}"
 
