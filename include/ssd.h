@@ -4,7 +4,7 @@
  * What is computed (page titles and sections of the sources):
  *
  *  Real (Mamba-2) form, one scalar A_h < 0 per head (Mamba-3-Lite README,
- *  "classical Mamba-2 recurrence"; Block Anatomy page, section 4.4 for
+ *  its statement of the Mamba-2 recurrence; Block Anatomy page, section 4.4 for
  *  exp(softplus(dt) * A); step size also on the input term, the usual
  *  Mamba-2 discretisation):
  *      delta_t = clamp(softplus(dt_t + dt_bias_h), dt_min, dt_max)
@@ -398,7 +398,8 @@ int ssd_complex_chunk_fwd_packed_ev(const float *proj, long long ld, const float
  * W stored (out_features, in_features)) on the matrix cores: bf16 operands,
  * fp32 accumulation.  These are the MIMO head mixer and out_proj of the
  * Mamba-3-Lite block (Block Anatomy, Numerical Stability & Scaling, section
- * 6, rows 9-10: single bias-free Linear layers, run in bf16 under autocast).
+ * 6, rows 9-10: single bias-free Linear layers; Numerical Stability in
+ * Mamba-3-Lite, section 3.1: projection GEMMs run in bf16 under autocast).
  *   x  (M, K)     x_dtype SSD_F32 (rounded to bf16, nearest even, as it is
  *                 read) or SSD_BF16
  *   W  (Nout, K)  bf16

@@ -3,8 +3,8 @@
 // block's Linear layers store it).  The MIMO head mixer is this map on the
 // scan output flattened per token to H*P features, head-major, with W of
 // (H*P, H*P); out_proj is the same map with W of (d_model, H*P) (Block
-// Anatomy, section 6, rows 9-10; these projections run in bf16 under the
-// pages' autocast, with fp32 accumulation).
+// Anatomy, section 6, rows 9-10; Numerical Stability in Mamba-3-Lite, section
+// 3.1: these projections run in bf16 under autocast, fp32 accumulation).
 //
 // One workgroup per 128 x 128 output tile (4 waves, 2 x 2, each 64 x 64), K in
 // steps of 64 staged through LDS (rows K-contiguous for both operands, so the
