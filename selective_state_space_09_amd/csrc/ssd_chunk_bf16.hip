@@ -50,6 +50,19 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float w) {
 template <int S>
 using Slot = std::integral_constant<int, S>;
 
+// The k slots of a 32-token step of an MFMA contraction over tokens whose two
+// operands both come from the LDS transpose read: lane group q takes the rows
+// (tokens) kSlotRow(q, 0) .. +3 and kSlotRow(q, 1) .. +3.  S4: rows 4q and
+// 16 + 4q, so that the four groups of a half-wave read 8 consecutive rows,
+// which the transpose read serves without bank conflicts at these pitches;
+// otherwise rows 8q and 8q + 4 (groups 8 rows apart: 2-way conflicts), which
+// the single-chunk builds keep: measured faster there (the other form made
+// the single-chunk output kernel spill at its 168-register bound).
+template <bool S4>
+__host__ __device__ constexpr int kSlotRow(int q, int half) {
+  return S4 ? 4 * q + 16 * half : 8 * q + 4 * half;
+}
+
 #ifndef SSD_STATE_PAIR_HEADS
 #define SSD_STATE_PAIR_HEADS 1
 #endif
@@ -74,7 +87,8 @@ constexpr bool kStatePairHeads = SSD_STATE_PAIR_HEADS;
 // scan): a sum of at most 256 positive steps carries a relative error of
 // ~1e-6.  Each chunk's (A u_l, delta_l) per token goes to the token table.
 // ---------------------------------------------------------------------------
-template <int P, int N, int HPW>
+// S4: the k slots of the contraction over tokens (see kSlotRow)
+template <int P, int N, int HPW, bool S4>
 __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min,
@@ -230,8 +244,9 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
       for (int i = 0; i < NTW; ++i) {
         const int nt = ng * NTW + i;
         const int cc = kPairN ? 32 * (nt >> 1) + 4 * (nt & 1) : nt * 16;
-        const uint2 lo = kPairN ? lds_tr4s<8>(bl, BPn, ks + 8 * q, cc) : lds_tr4(bl, BPn, ks + 8 * q, cc);
-        const uint2 hi = kPairN ? lds_tr4s<8>(bl, BPn, ks + 8 * q + 4, cc) : lds_tr4(bl, BPn, ks + 8 * q + 4, cc);
+        const int r0 = ks + kSlotRow<S4>(q, 0), r1 = ks + kSlotRow<S4>(q, 1);
+        const uint2 lo = kPairN ? lds_tr4s<8>(bl, BPn, r0, cc) : lds_tr4(bl, BPn, r0, cc);
+        const uint2 hi = kPairN ? lds_tr4s<8>(bl, BPn, r1, cc) : lds_tr4(bl, BPn, r1, cc);
         af[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
 #pragma unroll
@@ -239,8 +254,8 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < PTW; ++j) {
           const int pt = pg * PTW + j < PT ? pg * PTW + j : 0;
-          const uint2 lo = lds_tr4(xl[e], XPn, ks + 8 * q, pt * 16);
-          const uint2 hi = lds_tr4(xl[e], XPn, ks + 8 * q + 4, pt * 16);
+          const uint2 lo = lds_tr4(xl[e], XPn, ks + kSlotRow<S4>(q, 0), pt * 16);
+          const uint2 hi = lds_tr4(xl[e], XPn, ks + kSlotRow<S4>(q, 1), pt * 16);
           bf[e][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
 #pragma unroll
@@ -575,13 +590,31 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
       cr[ks] = buf_load16(cbuf, off);
     }
   };
+  // x, B and C rows of the sub-chunks ahead, in registers.  The single-chunk
+  // build loads one sub-chunk ahead (slot 0 for x and B; C in creg, the next
+  // in cnext).  The multi-chunk build runs at two workgroups per CU with
+  // registers to spare and loads two ahead through a two-slot ring: sub-chunk
+  // j's x, B and C in slot j % 2 (C rows of the sub-chunk being computed stay
+  // in its slot until its outputs are done).
+  constexpr int NSLOT = MULTI ? 2 : 1;
   uint4 creg[NKS], cnext[NKS];
-  load_c(creg, 0);
-
-  BufSlab<QSM, P / 8> xs;
-  BufSlab<QSM, N / 8> bs;
-  xs.load(xbuf, xrow, 0);
-  bs.load(bbuf, brow, 0);
+  uint4 cslot[NSLOT][NKS];
+  BufSlab<QSM, P / 8> xsl[NSLOT];
+  BufSlab<QSM, N / 8> bsl[NSLOT];
+  if constexpr (MULTI) {
+    load_c(cslot[0], 0);
+    xsl[0].load(xbuf, xrow, 0);
+    bsl[0].load(bbuf, brow, 0);
+    if (nsub > 1) {
+      load_c(cslot[1], 1);
+      xsl[1].load(xbuf, xrow, QS);
+      bsl[1].load(bbuf, brow, QS);
+    }
+  } else {
+    load_c(creg, 0);
+    xsl[0].load(xbuf, xrow, 0);
+    bsl[0].load(bbuf, brow, 0);
+  }
 
   // ---- factors of chunk kc's tokens and sub-chunks (every thread; t: token
   // tid's table entry).  Contains two barriers; the first also ends every
@@ -668,7 +701,8 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
   }
   __syncthreads();
 
-  auto store_stage = [&]() {
+  // x and B rows of a slot into the LDS tiles
+  auto store_stage = [&](const BufSlab<QSM, P / 8>& xs, const BufSlab<QSM, N / 8>& bs) {
 #pragma unroll
     for (int i = 0; i < bs.PER; ++i) {
       const int it = tid + i * kThreads;
@@ -721,11 +755,14 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
       }
     }
   };
-  store_stage();
+  store_stage(xsl[0], bsl[0]);
   store_state(0);
   __syncthreads();
 
-  for (int j = 0; j < nsub; ++j) {
+  // one sub-chunk: its outputs, then (unless it is the last) the state update
+  // and the staging of the next sub-chunk.  S: the slot of sub-chunk j.
+  auto step = [&](auto S, int j) {
+    constexpr int slot = decltype(S)::value;
     const int kc = j / nsc, jl = j - kc * nsc;  // chunk, sub-chunk within it
     const int sl0 = jl * QS;                    // its first token in the chunk
     const int sj = j * QS;                      // its first token in the segment
@@ -734,14 +771,26 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
     // uniform over the workgroup; scalar so that its branches keep EXEC whole
     const bool exact = __builtin_amdgcn_readfirstlane(sexact[jl]) != 0;
     float2 tvn = make_float2(0.f, 0.f);
-    if (more) {
-      xs.load(xbuf, xrow, sj + QS);
-      bs.load(bbuf, brow, sj + QS);
-      load_c(cnext, j + 1);
-      if constexpr (MULTI) {
-        if (next_chunk) tvn = load_tok(kc + 1);
+    if constexpr (MULTI) {
+      if (j + 2 < nsub) {
+        xsl[slot].load(xbuf, xrow, sj + 2 * QS);
+        bsl[slot].load(bbuf, brow, sj + 2 * QS);
+      }
+      if (next_chunk) tvn = load_tok(kc + 1);
+    } else {
+      if (more) {
+        xsl[0].load(xbuf, xrow, sj + QS);
+        bsl[0].load(bbuf, brow, sj + QS);
+        load_c(cnext, j + 1);
       }
     }
+    // C rows of this sub-chunk
+    auto& cr = [&]() -> uint4(&)[NKS] {
+      if constexpr (MULTI)
+        return cslot[slot];
+      else
+        return creg;
+    }();
 
     // ---- outputs of rows sj + 16 rw .. +15 (accumulator columns) ----
     if (has_rows) {
@@ -755,7 +804,7 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
           const uint4 hvv = *reinterpret_cast<const uint4*>(hT + prow(pt, r16) * HTP + ks * 32 + 8 * q);
-          yacc[pt] = mfma_bf16(as_bf16x8(hvv), as_bf16x8(creg[ks]), yacc[pt]);
+          yacc[pt] = mfma_bf16(as_bf16x8(hvv), as_bf16x8(cr[ks]), yacc[pt]);
         }
       }
       const float rsc = tcsc[sl0 + lr];  // row scale (exact mode: the carried term's)
@@ -773,13 +822,13 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const uint4 va = *reinterpret_cast<const uint4*>(bt + (b0 * 16 + r16) * BTP + ks * 32 + 8 * q);
-          ga = mfma_bf16(as_bf16x8(va), as_bf16x8(creg[ks]), ga);
+          ga = mfma_bf16(as_bf16x8(va), as_bf16x8(cr[ks]), ga);
         }
         if (live1) {
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const uint4 vb = *reinterpret_cast<const uint4*>(bt + (b1 * 16 + r16) * BTP + ks * 32 + 8 * q);
-            gb = mfma_bf16(as_bf16x8(vb), as_bf16x8(creg[ks]), gb);
+            gb = mfma_bf16(as_bf16x8(vb), as_bf16x8(cr[ks]), gb);
           }
         }
         // lane: column l = r16 (+16 rw), rows s = 4q + jj of blocks b0, b1; on
@@ -854,6 +903,10 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
       }
     }
 
+    if constexpr (MULTI) {
+      if (j + 2 < nsub) load_c(cslot[slot], j + 2);
+    }
+
     // ---- state update to the start of the next sub-chunk ----
     if (more) {
       if (exact) {
@@ -866,23 +919,25 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
       // (only chunks of 64 tokens and more have a next sub-chunk: QS = QSM)
 #pragma unroll
       for (int k = 0; k < QSM; k += 32) {
-        // weights of this lane's source tokens k + 8q .. +7
-        const float4 w0 = *reinterpret_cast<const float4*>(&txsc[sl0 + k + 8 * q]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&txsc[sl0 + k + 8 * q + 4]);
+        // weights of this lane's source tokens (its two k slots, kSlotRow)
+        constexpr int kHalf = kSlotRow<MULTI>(0, 1);  // row offset of the second half
+        const int r0 = k + kSlotRow<MULTI>(q, 0), r1 = r0 + kHalf;
+        const float4 w0 = *reinterpret_cast<const float4*>(&txsc[sl0 + k + kSlotRow<MULTI>(q, 0)]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&txsc[sl0 + k + kSlotRow<MULTI>(q, 0) + kHalf]);
         uint4 bfr[KTW];
 #pragma unroll
         for (int i = 0; i < KTW; ++i) {
           const int nt = wid + 4 * i;
-          const uint2 lo = kPairS ? lds_tr4s<8>(bt, BTP, k + 8 * q, 32 * wid + 4 * i)
-                                  : lds_tr4(bt, BTP, k + 8 * q, (nt < KT ? nt : 0) * 16);
-          const uint2 hi = kPairS ? lds_tr4s<8>(bt, BTP, k + 8 * q + 4, 32 * wid + 4 * i)
-                                  : lds_tr4(bt, BTP, k + 8 * q + 4, (nt < KT ? nt : 0) * 16);
+          const uint2 lo = kPairS ? lds_tr4s<8>(bt, BTP, r0, 32 * wid + 4 * i)
+                                  : lds_tr4(bt, BTP, r0, (nt < KT ? nt : 0) * 16);
+          const uint2 hi = kPairS ? lds_tr4s<8>(bt, BTP, r1, 32 * wid + 4 * i)
+                                  : lds_tr4(bt, BTP, r1, (nt < KT ? nt : 0) * 16);
           bfr[i] = scale_bf16x8_each(make_uint4(lo.x, lo.y, hi.x, hi.y), w0, w1);
         }
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
-          const uint2 lo = lds_tr4(xl, XPn, k + 8 * q, pt * 16);
-          const uint2 hi = lds_tr4(xl, XPn, k + 8 * q + 4, pt * 16);
+          const uint2 lo = lds_tr4(xl, XPn, r0, pt * 16);
+          const uint2 hi = lds_tr4(xl, XPn, r1, pt * 16);
           const uint4 afr = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
           for (int i = 0; i < KTW; ++i)
@@ -891,15 +946,25 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
         }
       }
       __syncthreads();  // every wave is done with this sub-chunk's tiles
-      store_stage();
+      store_stage(xsl[MULTI ? 1 - slot : 0], bsl[MULTI ? 1 - slot : 0]);
       if constexpr (MULTI) {
         if (next_chunk) chunk_factors(tvn, false);  // the chunk's factors replace the last one's
       }
       store_state(next_chunk ? 0 : jl + 1);
+      if constexpr (!MULTI) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) creg[ks] = cnext[ks];
+        for (int ks = 0; ks < NKS; ++ks) creg[ks] = cnext[ks];
+      }
       __syncthreads();
     }
+  };
+  if constexpr (MULTI) {
+    for (int j = 0; j < nsub; j += 2) {
+      step(Slot<0>{}, j);
+      if (j + 1 < nsub) step(Slot<1>{}, j + 1);
+    }
+  } else {
+    for (int j = 0; j < nsub; ++j) step(Slot<0>{}, j);
   }
 }
 
@@ -921,14 +986,21 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_outp
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
   const hipEvent_t* ev = a.events;
   // segment states: two heads per workgroup when the heads of a group pair up
-  if (kStatePairHeads && (a.H / a.G) % 2 == 0)
-    launch_k(nc > 0, ssd_state_bf16_kernel<P, N, 2>, dim3(blocks / 2), dim3(512), st, ev, x, a.dt,
-             a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, decay, tok, a.T, a.H, a.G, a.chunk, nc, K,
-             nseg, npairs);
+  auto state = [&](auto hpw, auto s4) {
+    constexpr int HPW = decltype(hpw)::value;
+    launch_k(nc > 0, ssd_state_bf16_kernel<P, N, HPW, decltype(s4)::value>, dim3(blocks / HPW), dim3(512),
+             st, ev, x, a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, decay, tok, a.T, a.H, a.G,
+             a.chunk, nc, K, nseg, npairs);
+  };
+  const bool pair = kStatePairHeads && (a.H / a.G) % 2 == 0;
+  if (pair && K > 1)
+    state(Slot<2>{}, std::true_type{});
+  else if (pair)
+    state(Slot<2>{}, std::false_type{});
+  else if (K > 1)
+    state(Slot<1>{}, std::true_type{});
   else
-    launch_k(nc > 0, ssd_state_bf16_kernel<P, N, 1>, dim3(blocks), dim3(512), st, ev, x, a.dt,
-             a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, decay, tok, a.T, a.H, a.G, a.chunk, nc, K,
-             nseg, npairs);
+    state(Slot<1>{}, std::false_type{});
   // without the outputs (the backward's recompute, K = 1) the fp32 boundary
   // states are kept too, over the chunk states
   if (with_output)
