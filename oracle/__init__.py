@@ -61,6 +61,9 @@ def _load():
     lib.ssd_oracle_bwd.restype = I
     lib.ssd_oracle_bwd.argtypes = [P, P, P, P, P, P, P, Dd, Dd, P, P, P,
                                    P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I]
+    lib.ssd_oracle_complex_bwd.restype = I
+    lib.ssd_oracle_complex_bwd.argtypes = [P, P, P, P, P, P, Dd, Dd, P, P, P,
+                                           P, P, P, P, P, P, P, P, I, I, I, I, I, I]
     lib.ssd_oracle_threads_used.restype = I
     lib.ssd_oracle_set_threads.argtypes = [I]
     _lib = lib
@@ -280,6 +283,41 @@ def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=float("inf"
                             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
                             _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(out["da"]),
                             Bsz, T, H, P, G, N, dtype)
+    if rc:
+        raise ValueError("oracle rejected the sizes" if rc == 1 else "oracle out of memory")
+    return out
+
+
+def complex_bwd(x, dt, A, B, C, dy, dt_bias=None, dt_min=0.0, dt_max=float("inf"),
+                h0=None, dh_final=None, want_dh0=True):
+    """Gradient of loss = sum(dy * y) + <dh_final, h_final>_R of the complex
+    recurrence (inputs as ``complex_fwd``; dy (Bsz,T,H,P) float32, dh_final
+    (Bsz,H,P,N,2) float32 or None).  Complex gradients come as (d/d re, d/d im)
+    pairs.  Returns a dict of float64 arrays: dx, ddt, dA (H,2), dB, dC
+    (Bsz,T,G,N,2), ddt_bias, dh0 (None unless want_dh0) and q (Bsz,T,H,2), the
+    gradient of each step's complex exponent A delta_t."""
+    lib = _load()
+    x = _c(x, np.float32)
+    dt = _c(dt, np.float32)
+    A = _c(A, np.float32)
+    B = _c(B, np.float32)
+    C = _c(C, np.float32)
+    dy = _c(dy, np.float32)
+    dt_bias = _c(dt_bias, np.float32)
+    h0 = _c(h0, np.float32)
+    dh_final = _c(dh_final, np.float32)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    out = dict(dx=np.empty((Bsz, T, H, P)), ddt=np.empty((Bsz, T, H)), dA=np.empty((H, 2)),
+               dB=np.empty((Bsz, T, G, N, 2)), dC=np.empty((Bsz, T, G, N, 2)),
+               ddt_bias=np.empty(H), dh0=np.empty((Bsz, H, P, N, 2)) if want_dh0 else None,
+               q=np.empty((Bsz, T, H, 2)))
+    rc = lib.ssd_oracle_complex_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(dt_bias),
+                                    float(dt_min), float(dt_max), _ptr(h0), _ptr(dy),
+                                    _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]),
+                                    _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                                    _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(out["q"]),
+                                    Bsz, T, H, P, G, N)
     if rc:
         raise ValueError("oracle rejected the sizes" if rc == 1 else "oracle out of memory")
     return out

@@ -561,3 +561,178 @@ int ssd_oracle_bwd(const void *x, const float *dt, const float *A, const void *B
     free(pbias);
     return fail ? 2 : 0;
 }
+
+/*
+ * Gradient of  loss = sum_t dy_t . y_t + <dh_final, h_final>_R  through the
+ * complex recurrence of ssd_oracle_complex_fwd (Mamba-3-Lite README, the
+ * complex recurrence; Block Anatomy, section 7, pitfall 7: the gradient of
+ * the complex A is complex).  <u, v>_R = sum Re(conj(u) v), the real inner
+ * product of the arrays as (re, im) pairs.  Every complex gradient is
+ * returned as (dL/d re, dL/d im).  The reverse-mode derivative, one step at a
+ * time from the last token:
+ *   G      = dL/dh_t  (starts as dh_final, gains dy_t conj(C_t) at step t,
+ *            and reaches h_{t-1} as conj(a_t) G)
+ *   dx_t   = Re(sum_n conj(G[p][n]) B_t[n])
+ *   dB_t   = sum_p x_t[p] G[p][n]          dC_t = sum_p dy_t[p] conj(h_t[p][n])
+ *   q_t    = conj(a_t) sum G conj(h_{t-1})  (the gradient of the step's
+ *            exponent A delta_t)
+ *   dA    += delta_t q_t,   d delta_t = Re(A conj(q_t)),   dh0 = G after t = 0,
+ * and the clamp and softplus of the step size as in ssd_oracle_bwd.
+ * Layouts as ssd_oracle_complex_fwd; outputs double: dx (Bsz,T,H,P), ddt
+ * (Bsz,T,H), dA (H,2), dB/dC (Bsz,T,G,N,2), ddt_bias (H), dh0 (Bsz,H,P,N,2)
+ * (may be NULL), q (Bsz,T,H,2) (may be NULL).
+ */
+int ssd_oracle_complex_bwd(const float *x, const float *dt, const float *A, const float *B,
+                           const float *C, const float *dt_bias, double dt_min, double dt_max,
+                           const float *h0, const float *dy, const float *dh_final,
+                           double *dx, double *ddt, double *dA, double *dB, double *dC,
+                           double *ddt_bias, double *dh0, double *qout, int Bsz, int T, int H,
+                           int P, int G, int N)
+{
+    if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G)
+        return 1;
+    const int hpg = H / G;
+    const size_t PN2 = (size_t)P * N * 2;
+    const size_t nbc = (size_t)Bsz * T * G * N * 2;
+    memset(dB, 0, sizeof(double) * nbc);
+    memset(dC, 0, sizeof(double) * nbc);
+    int fail = 0;
+    double *pA = calloc((size_t)Bsz * H * 2, sizeof(double));
+    double *pbias = calloc((size_t)Bsz * H, sizeof(double));
+    if (!pA || !pbias) {
+        free(pA); free(pbias);
+        return 2;
+    }
+    const long long BH = (long long)Bsz * H;
+#pragma omp parallel
+    {
+#pragma omp single
+        record_threads();
+        double *hist = malloc(sizeof(double) * ((size_t)T + 1) * PN2);
+        double *Gm = malloc(sizeof(double) * PN2);
+        double *dlt = malloc(sizeof(double) * ((size_t)T + 1));
+        double *dBt = calloc(nbc ? nbc : 1, sizeof(double));
+        double *dCt = calloc(nbc ? nbc : 1, sizeof(double));
+        const int ok = hist && Gm && dlt && dBt && dCt;
+        if (!ok) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic)
+        for (long long bh = 0; bh < BH; ++bh) {
+            if (!ok)
+                continue;
+            const int b = (int)(bh / H), h = (int)(bh % H), g = h / hpg;
+            const double al = (double)A[2 * h], be = (double)A[2 * h + 1];
+            const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+            /* forward: hist[0] = h0, hist[t+1] = h_t */
+            for (size_t i = 0; i < PN2; ++i)
+                hist[i] = h0 ? (double)h0[(size_t)bh * PN2 + i] : 0.0;
+            for (int t = 0; t < T; ++t) {
+                const size_t row = (size_t)b * T + t;
+                const double delta = ssd_oracle_delta((double)dt[row * H + h], bias, dt_min, dt_max);
+                dlt[t] = delta;
+                const double mag = exp(al * delta);
+                const double ar = mag * cos(be * delta), ai = mag * sin(be * delta);
+                const double *hp = hist + (size_t)t * PN2;
+                double *hn = hist + ((size_t)t + 1) * PN2;
+                const size_t bo = (row * G + g) * (size_t)N * 2;
+                for (int p = 0; p < P; ++p) {
+                    const double xp = (double)x[(row * H + h) * P + p];
+                    for (int n = 0; n < N; ++n) {
+                        const size_t e = ((size_t)p * N + n) * 2;
+                        hn[e] = ar * hp[e] - ai * hp[e + 1] + xp * B[bo + 2 * n];
+                        hn[e + 1] = ar * hp[e + 1] + ai * hp[e] + xp * B[bo + 2 * n + 1];
+                    }
+                }
+            }
+            /* backward */
+            for (size_t i = 0; i < PN2; ++i)
+                Gm[i] = dh_final ? (double)dh_final[(size_t)bh * PN2 + i] : 0.0;
+            for (int t = T - 1; t >= 0; --t) {
+                const size_t row = (size_t)b * T + t;
+                const double delta = dlt[t];
+                const double mag = exp(al * delta);
+                const double ar = mag * cos(be * delta), ai = mag * sin(be * delta);
+                const double *ht = hist + ((size_t)t + 1) * PN2;
+                const double *hprev = hist + (size_t)t * PN2;
+                const size_t bo = (row * G + g) * (size_t)N * 2;
+                /* G += dy_t conj(C_t);  dC_t += dy_t conj(h_t) */
+                for (int p = 0; p < P; ++p) {
+                    const double dyp = (double)dy[(row * H + h) * P + p];
+                    for (int n = 0; n < N; ++n) {
+                        const size_t e = ((size_t)p * N + n) * 2;
+                        Gm[e] += dyp * C[bo + 2 * n];
+                        Gm[e + 1] -= dyp * C[bo + 2 * n + 1];
+                        dCt[bo + 2 * n] += dyp * ht[e];
+                        dCt[bo + 2 * n + 1] -= dyp * ht[e + 1];
+                    }
+                }
+                double gar = 0.0, gai = 0.0; /* sum G conj(h_{t-1}) */
+                for (int p = 0; p < P; ++p) {
+                    const double xp = (double)x[(row * H + h) * P + p];
+                    double acc = 0.0;
+                    for (int n = 0; n < N; ++n) {
+                        const size_t e = ((size_t)p * N + n) * 2;
+                        const double gr = Gm[e], gi = Gm[e + 1];
+                        acc += gr * B[bo + 2 * n] + gi * B[bo + 2 * n + 1]; /* Re(conj(G) B) */
+                        dBt[bo + 2 * n] += xp * gr;
+                        dBt[bo + 2 * n + 1] += xp * gi;
+                        gar += gr * hprev[e] + gi * hprev[e + 1];
+                        gai += gi * hprev[e] - gr * hprev[e + 1];
+                    }
+                    dx[(row * H + h) * P + p] = acc;
+                }
+                /* q = conj(a) Ga */
+                const double qr = ar * gar + ai * gai, qi = ar * gai - ai * gar;
+                if (qout) {
+                    qout[(row * H + h) * 2] = qr;
+                    qout[(row * H + h) * 2 + 1] = qi;
+                }
+                pA[((size_t)b * H + h) * 2] += delta * qr;
+                pA[((size_t)b * H + h) * 2 + 1] += delta * qi;
+                const double ddelta = al * qr + be * qi; /* Re(A conj(q)) */
+                const double z = (double)dt[row * H + h] + bias;
+                const double sp = ssd_oracle_softplus(z);
+                const double pass = (sp >= dt_min && sp <= dt_max) ? 1.0 : 0.0;
+                const double d = ddelta * pass / (1.0 + exp(-z));
+                ddt[row * H + h] = d;
+                pbias[(size_t)b * H + h] += d;
+                /* G reaches h_{t-1}: G <- conj(a) G */
+                for (size_t e = 0; e < PN2; e += 2) {
+                    const double gr = Gm[e], gi = Gm[e + 1];
+                    Gm[e] = ar * gr + ai * gi;
+                    Gm[e + 1] = ar * gi - ai * gr;
+                }
+            }
+            if (dh0)
+                memcpy(dh0 + (size_t)bh * PN2, Gm, sizeof(double) * PN2);
+        }
+#pragma omp critical
+        if (ok) {
+            for (size_t i = 0; i < nbc; ++i) {
+                dB[i] += dBt[i];
+                dC[i] += dCt[i];
+            }
+        }
+        free(hist);
+        free(Gm);
+        free(dlt);
+        free(dBt);
+        free(dCt);
+    }
+    for (int h = 0; h < H; ++h) {
+        double sr = 0.0, si = 0.0, sb = 0.0;
+        for (int b = 0; b < Bsz; ++b) {
+            sr += pA[((size_t)b * H + h) * 2];
+            si += pA[((size_t)b * H + h) * 2 + 1];
+            sb += pbias[(size_t)b * H + h];
+        }
+        dA[2 * h] = sr;
+        dA[2 * h + 1] = si;
+        ddt_bias[h] = sb;
+    }
+    free(pA);
+    free(pbias);
+    return fail ? 2 : 0;
+}

@@ -691,3 +691,99 @@ def test_linear_out_proj_shape_and_composition():
     one = y.reshape(2, 5, 8).astype(np.float64) @ (Wo.astype(np.float64) @ Wm.astype(np.float64)).T
     assert two.shape == (2, 5, 6)
     np.testing.assert_allclose(two, one, rtol=1e-12, atol=1e-12)
+
+
+# ---- backward of the complex recurrence (oracle.complex_bwd), pinned by
+# finite differences of the pinned complex forward ----
+
+def _closs(inp, dy, dhf):
+    y, hf = oracle.complex_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                               inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"])
+    return float(np.sum(dy.astype(np.float64) * y) + np.sum(dhf.astype(np.float64) * hf))
+
+
+def _cbwd_case(G, seed):
+    inp = _cplx(Bsz=2, T=6, H=2, P=3, N=4, G=G, seed=seed, with_h0=True)
+    # a bias that puts most steps inside the clamp range, some above it
+    inp["dt_bias"] = np.full(2, -2.5, np.float32)
+    rng = np.random.default_rng(seed + 200)
+    dy = rng.standard_normal(inp["x"].shape).astype(np.float32)
+    dhf = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    z = inp["dt"].astype(np.float64) + inp["dt_bias"].astype(np.float64)
+    sp = np.logaddexp(0.0, z)
+    assert np.min(np.abs(sp - inp["dt_min"])) > 1e-3 * inp["dt_min"]
+    assert np.min(np.abs(sp - inp["dt_max"])) > 1e-3 * inp["dt_max"]
+    assert np.any(sp > inp["dt_max"]) and np.any(sp < inp["dt_max"])  # both branches occur
+    return inp, dy, dhf
+
+
+@pytest.mark.parametrize("G,seed", [(2, 3), (1, 6)])
+def test_complex_bwd_matches_finite_differences(G, seed):
+    """Every gradient of every input element -- real and imaginary parts of
+    A, B, C and h0 separately -- against the central difference of the complex
+    forward oracle (perturbation 2^-12, exact in float32)."""
+    inp, dy, dhf = _cbwd_case(G, seed)
+    g = oracle.complex_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], dy,
+                           inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
+    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC",
+             "dt_bias": "ddt_bias", "h0": "dh0"}
+    eps = 2.0 ** -12
+    for k, gk in names.items():
+        base = inp[k]
+        fd = np.empty(base.shape)
+        for idx in np.ndindex(base.shape):
+            hi, lo = dict(inp), dict(inp)
+            hi[k] = base.copy()
+            lo[k] = base.copy()
+            hi[k][idx] += np.float32(eps)
+            lo[k][idx] -= np.float32(eps)
+            step = float(hi[k][idx]) - float(lo[k][idx])
+            fd[idx] = (_closs(hi, dy, dhf) - _closs(lo, dy, dhf)) / step
+        scale = np.abs(fd).max()
+        np.testing.assert_allclose(g[gk], fd, rtol=2e-5, atol=2e-6 * scale, err_msg=k)
+
+
+def test_complex_bwd_exponent_gradient_identities():
+    """q_t, the gradient of the step's complex exponent A delta_t, is what dA
+    sums (dA_h = sum_{b,t} delta_t q_t), and its real part along A gives the
+    step-size gradient: ddt_t = Re(A conj(q_t)) sigmoid(z_t) inside the clamp,
+    0 outside (dA and ddt are pinned by finite differences above)."""
+    inp, dy, dhf = _cbwd_case(2, 3)
+    g = oracle.complex_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], dy,
+                           inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
+    z = inp["dt"].astype(np.float64) + inp["dt_bias"].astype(np.float64)
+    sp = np.logaddexp(0.0, z)
+    d = np.clip(sp, inp["dt_min"], inp["dt_max"])
+    q = g["q"][..., 0] + 1j * g["q"][..., 1]
+    dA = (d[..., None] * g["q"]).sum(axis=(0, 1))
+    np.testing.assert_allclose(g["dA"], dA, rtol=1e-12, atol=1e-12 * np.abs(dA).max())
+    A = inp["A"][:, 0].astype(np.float64) + 1j * inp["A"][:, 1].astype(np.float64)
+    inside = (sp >= inp["dt_min"]) & (sp <= inp["dt_max"])
+    want = np.where(inside, np.real(A[None, None, :] * np.conj(q)) / (1.0 + np.exp(-z)), 0.0)
+    np.testing.assert_allclose(g["ddt"], want, rtol=1e-12, atol=1e-14)
+
+
+def test_complex_bwd_without_rotation_is_two_real_recurrences():
+    """With A_im = 0 and real B, C, h0 the complex recurrence is the real one
+    without the step size on its input term; feeding the real oracle x / delta
+    (so that its delta x B is x B) gives the same dB, dC (real parts) and dh0,
+    and imaginary parts exactly zero."""
+    inp = _cplx(Bsz=1, T=8, H=2, P=3, N=4, G=2, seed=11, with_h0=True)
+    inp["A"][:, 1] = 0.0
+    for k in ("B", "C", "h0"):
+        inp[k][..., 1] = 0.0
+    rng = np.random.default_rng(12)
+    dy = rng.standard_normal(inp["x"].shape).astype(np.float32)
+    dhf = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    dhf[..., 1] = 0.0
+    g = oracle.complex_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], dy,
+                           inp["dt_bias"], inp["dt_min"], inp["dt_max"], inp["h0"], dhf)
+    d = np.clip(np.logaddexp(0.0, inp["dt"].astype(np.float64)), inp["dt_min"], inp["dt_max"])
+    xr = (inp["x"].astype(np.float64) / d[..., None]).astype(np.float32)
+    # x / delta is rounded to float32 once: compare at that rounding
+    gr = oracle.bwd(xr, inp["dt"], inp["A"][:, 0].copy(), inp["B"][..., 0].copy(),
+                    inp["C"][..., 0].copy(), dy, None, None, inp["dt_min"], inp["dt_max"],
+                    inp["h0"][..., 0].copy(), dhf[..., 0].copy())
+    for k in ("dB", "dC", "dh0"):
+        np.testing.assert_array_equal(g[k][..., 1], 0.0)
+        np.testing.assert_allclose(g[k][..., 0], gr[k], rtol=1e-5, atol=1e-6 * np.abs(gr[k]).max())
