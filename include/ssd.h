@@ -334,11 +334,15 @@ int ssd_conv1d_step_ev(float *state, const float *xt, long long ld, const float 
  *   dh0         (Bsz,H,P,N) float32, or NULL (not written)
  *   workspace   ssd_bwd_workspace_size(...) bytes, 256-byte aligned
  * Built for dtype SSD_BF16 with P in {32, 64}, N in {64, 128}, chunk in
- * {64, 128, 256} (SSD_EUNSUPPORTED otherwise, including SSD_F32).  dB, dC,
- * dh0, h0 and dh_final 16-byte aligned.  Outputs are overwritten, not
+ * {64, 128, 256}, and for dtype SSD_F32 (x, B, C, dy and dx float32; fp32
+ * matrix products) with P in {32, 64}, N in {32, 64, 128} and chunk 64
+ * (SSD_EUNSUPPORTED otherwise; the fp32 backward has no measurement events).
+ * dB, dC, dh0, h0 and dh_final 16-byte aligned.  Outputs are overwritten, not
  * accumulated, and must not overlap inputs.  Errors as for ssd_chunk_fwd.
+ * Workspace: ssd_bwd_workspace_size (SSD_BF16) or ssd_bwd_workspace_size_f32.
  */
 size_t ssd_bwd_workspace_size(int Bsz, int T, int H, int P, int G, int N, int chunk);
+size_t ssd_bwd_workspace_size_f32(int Bsz, int T, int H, int P, int G, int N);
 
 int ssd_chunk_bwd(const void *x, const float *dt, const float *A, const void *B,
                   const void *C, const float *D, const float *dt_bias, float dt_min,
@@ -363,6 +367,35 @@ int ssd_chunk_bwd_ev(const void *x, const float *dt, const float *A, const void 
                      float *ddt_bias, float *dh0, int Bsz, int T, int H, int P, int G, int N,
                      int chunk, int dtype, void *workspace, size_t workspace_bytes,
                      void *stream, void *const *events);
+
+/*
+ * Backward of ssd_complex_chunk_fwd (Mamba-3-Lite README, the complex
+ * recurrence; Block Anatomy, section 7, pitfall 7: the gradient of the complex
+ * A is complex): the gradient of
+ *   loss = sum_t dy_t . y_t + sum Re(conj(dh_final) h_final)
+ * with respect to every input.  Complex arrays as ssd_complex_chunk_fwd,
+ * (re, im) float32 pairs; every complex gradient is returned as
+ * (dL/d re, dL/d im).
+ *   dy          (Bsz,T,H,P) float32;  dh_final (Bsz,H,P,N,2), or NULL (zero)
+ *   dx          (Bsz,T,H,P)   ddt (Bsz,T,H)   dA (H,2)   ddt_bias (H)
+ *   dB, dC      (Bsz,T,G,N,2), summed over the heads of each group
+ *   dh0         (Bsz,H,P,N,2), or NULL (not written)
+ * Computed in the sequence-wide rotated frame, where the complex recurrence is
+ * two real ones with one real decay, with fp32 matrix products and fp64
+ * angles and scans.  P in {32, 64}, N in {16, 32, 64}, chunk 64
+ * (SSD_EUNSUPPORTED otherwise).  x, B, C, dy, dx, dB, dC, h0, dh_final, dh0
+ * 16-byte aligned, A and dA 8-byte aligned.  Outputs are overwritten and
+ * must not overlap inputs.  Workspace: ssd_complex_bwd_workspace_size bytes,
+ * 256-byte aligned.  Errors as for ssd_complex_chunk_fwd.
+ */
+size_t ssd_complex_bwd_workspace_size(int Bsz, int T, int H, int P, int G, int N);
+
+int ssd_complex_chunk_bwd(const float *x, const float *dt, const float *A, const float *B,
+                          const float *C, const float *dt_bias, float dt_min, float dt_max,
+                          const float *h0, const float *dy, const float *dh_final, float *dx,
+                          float *ddt, float *dA, float *dB, float *dC, float *ddt_bias,
+                          float *dh0, int Bsz, int T, int H, int P, int G, int N, int chunk,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * ssd_complex_chunk_fwd reading its inputs in place from the rows of the

@@ -75,6 +75,13 @@ def lib():
                                 P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, S, P]
     L.ssd_chunk_bwd_ev.restype = I
     L.ssd_chunk_bwd_ev.argtypes = L.ssd_chunk_bwd.argtypes + [P]
+    L.ssd_bwd_workspace_size_f32.restype = S
+    L.ssd_bwd_workspace_size_f32.argtypes = [I] * 6
+    L.ssd_complex_bwd_workspace_size.restype = S
+    L.ssd_complex_bwd_workspace_size.argtypes = [I] * 6
+    L.ssd_complex_chunk_bwd.restype = I
+    L.ssd_complex_chunk_bwd.argtypes = [P, P, P, P, P, P, F, F, P, P, P, P, P, P, P, P, P, P,
+                                        I, I, I, I, I, I, I, P, S, P]
     L.ssd_conv1d_fwd.restype = I
     L.ssd_conv1d_fwd.argtypes = [P, LL, P, P, P, I, P, P, P, P, I, I, I, I, I, I, P]
     L.ssd_conv1d_fwd_ev.restype = I
@@ -452,11 +459,20 @@ def ssd_bwd_workspace_size(Bsz, T, H, P, G, N, chunk):
     return int(lib().ssd_bwd_workspace_size(Bsz, T, H, P, G, N, chunk))
 
 
+def ssd_bwd_workspace_size_f32(Bsz, T, H, P, G, N):
+    return int(lib().ssd_bwd_workspace_size_f32(Bsz, T, H, P, G, N))
+
+
+def ssd_complex_bwd_workspace_size(Bsz, T, H, P, G, N):
+    return int(lib().ssd_complex_bwd_workspace_size(Bsz, T, H, P, G, N))
+
+
 def ssd_chunk_bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=math.inf,
                   h0=None, dh_final=None, chunk=256, want_dh0=True, workspace=None, stream=None):
     """Gradient of sum(dy * y) + <dh_final, h_final> of ssd_chunk_fwd (real
-    form, bfloat16 x/B/C/dy).  Returns a dict: dx (x's dtype), ddt, dA, dB,
-    dC, dD, ddt_bias and dh0 (float32; dh0 None unless want_dh0)."""
+    form; x/B/C/dy all bfloat16, or all float32 with chunk 64).  Returns a
+    dict: dx (x's dtype), ddt, dA, dB, dC, dD, ddt_bias and dh0 (float32; dh0
+    None unless want_dh0)."""
     _ndim(x, "x", 4)
     _ndim(B, "B", 4)
     Bsz, T, H, P = x.shape
@@ -470,8 +486,9 @@ def ssd_chunk_bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=m
     _expect(dt_bias, "dt_bias", (H,), x)
     _expect(h0, "h0", (Bsz, H, P, N), x)
     _expect(dh_final, "dh_final", (Bsz, H, P, N), x)
+    xdt = _dcode(x.dtype, "x")
     for t, n in ((x, "x"), (B, "B"), (C, "C"), (dy, "dy")):
-        _dev(t, n, torch.bfloat16)
+        _dev(t, n, torch.bfloat16 if xdt == SSD_BF16 else torch.float32)
     for t, n in ((dt, "dt"), (A, "A")):
         _dev(t, n, torch.float32)
     for t, n in ((D, "D"), (dt_bias, "dt_bias"), (h0, "h0"), (dh_final, "dh_final")):
@@ -483,15 +500,57 @@ def ssd_chunk_bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, dt_min=0.0, dt_max=m
                dC=torch.empty((Bsz, T, G, N), **f32), dD=torch.empty(H, **f32),
                ddt_bias=torch.empty(H, **f32),
                dh0=torch.empty((Bsz, H, P, N), **f32) if want_dh0 else None)
-    nbytes = ssd_bwd_workspace_size(Bsz, T, H, P, G, N, chunk)
+    nbytes = (ssd_bwd_workspace_size(Bsz, T, H, P, G, N, chunk) if xdt == SSD_BF16
+              else ssd_bwd_workspace_size_f32(Bsz, T, H, P, G, N))
     ws = _workspace(nbytes, dev, workspace)
     _check(lib().ssd_chunk_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0), _ptr(dy),
                                _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]),
                                _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
                                _ptr(out["dD"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]),
-                               Bsz, T, H, P, G, N, chunk, SSD_BF16, _ptr(ws), ws.numel(),
+                               Bsz, T, H, P, G, N, chunk, xdt, _ptr(ws), ws.numel(),
                                _stream(stream)))
+    return out
+
+
+def ssd_complex_chunk_bwd(x, dt, A, B, C, dy, dt_bias=None, dt_min=0.0, dt_max=math.inf,
+                          h0=None, dh_final=None, chunk=64, want_dh0=True, workspace=None,
+                          stream=None):
+    """Gradient of sum(dy * y) + <dh_final, h_final> of ssd_complex_chunk_fwd
+    (float32 x and dy, complex64 A/B/C/h0/dh_final as (re, im) pairs, chunk
+    64).  Complex gradients come as (d/d re, d/d im) pairs.  Returns a dict:
+    dx, ddt, dA (H,2), dB, dC (Bsz,T,G,N,2), ddt_bias, dh0 (Bsz,H,P,N,2; None
+    unless want_dh0), all float32."""
+    A, B, C, h0, dh_final = _pairs(A), _pairs(B), _pairs(C), _pairs(h0), _pairs(dh_final)
+    _ndim(x, "x", 4)
+    _ndim(B, "B", 5)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _expect(B, "B", (Bsz, T, G, N, 2), x)
+    _expect(C, "C", (Bsz, T, G, N, 2), x)
+    _expect(dy, "dy", (Bsz, T, H, P), x)
+    _expect(dt, "dt", (Bsz, T, H), x)
+    _expect(A, "A", (H, 2), x)
+    _expect(dt_bias, "dt_bias", (H,), x)
+    _expect(h0, "h0", (Bsz, H, P, N, 2), x)
+    _expect(dh_final, "dh_final", (Bsz, H, P, N, 2), x)
+    for t, n in ((x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C"), (dy, "dy"),
+                 (dt_bias, "dt_bias"), (h0, "h0"), (dh_final, "dh_final")):
+        _dev(t, n, torch.float32)
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty((Bsz, T, H, P), **f32), ddt=torch.empty((Bsz, T, H), **f32),
+               dA=torch.empty((H, 2), **f32), dB=torch.empty((Bsz, T, G, N, 2), **f32),
+               dC=torch.empty((Bsz, T, G, N, 2), **f32), ddt_bias=torch.empty(H, **f32),
+               dh0=torch.empty((Bsz, H, P, N, 2), **f32) if want_dh0 else None)
+    ws = _workspace(ssd_complex_bwd_workspace_size(Bsz, T, H, P, G, N), dev, workspace)
+    _check(lib().ssd_complex_chunk_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                       _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0),
+                                       _ptr(dy), _ptr(dh_final), _ptr(out["dx"]),
+                                       _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                                       _ptr(out["dC"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]),
+                                       Bsz, T, H, P, G, N, chunk, _ptr(ws), ws.numel(),
+                                       _stream(stream)))
     return out
 
 

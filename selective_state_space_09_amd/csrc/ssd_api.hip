@@ -516,12 +516,18 @@ int ssd_chunk_bwd_ev(const void* x, const float* dt, const float* A, const void*
                      void* workspace, size_t workspace_bytes, void* stream,
                      void* const* events) {
   SSD_TRY(check_chunk_shape(Bsz, T, H, P, G, N, chunk, 0));
-  if (dtype == SSD_F32)
-    return fail(SSD_EUNSUPPORTED, "the backward is built for bfloat16 x, B, C and dy only");
-  if (dtype != SSD_BF16) return fail(SSD_EUNSUPPORTED, "dtype=%d", dtype);
-  if (!((P == 64 || P == 32) && (N == 64 || N == 128)))
-    return fail(SSD_EUNSUPPORTED, "backward: (P, N) = (%d, %d) not in {32, 64} x {64, 128}", P, N);
-  if (chunk < 64) return fail(SSD_EUNSUPPORTED, "backward: chunk=%d not in {64, 128, 256}", chunk);
+  const bool f32 = dtype == SSD_F32;
+  if (dtype != SSD_BF16 && !f32) return fail(SSD_EUNSUPPORTED, "dtype=%d", dtype);
+  if (f32) {
+    if (!((P == 64 || P == 32) && (N == 32 || N == 64 || N == 128)))
+      return fail(SSD_EUNSUPPORTED, "fp32 backward: (P, N) = (%d, %d) not in {32, 64} x {32, 64, 128}", P,
+                  N);
+    if (chunk != 64) return fail(SSD_EUNSUPPORTED, "fp32 backward: chunk=%d, must be 64", chunk);
+  } else {
+    if (!((P == 64 || P == 32) && (N == 64 || N == 128)))
+      return fail(SSD_EUNSUPPORTED, "backward: (P, N) = (%d, %d) not in {32, 64} x {64, 128}", P, N);
+    if (chunk < 64) return fail(SSD_EUNSUPPORTED, "backward: chunk=%d not in {64, 128, 256}", chunk);
+  }
   const bool has_tokens = T > 0;
   SSD_TRY(check_ptr(x, "x", 16, has_tokens));
   SSD_TRY(check_ptr(dt, "dt", 4, has_tokens));
@@ -547,7 +553,8 @@ int ssd_chunk_bwd_ev(const void* x, const float* dt, const float* A, const void*
   const long long bpairs = (static_cast<long long>(Bsz) * nc * (chunk / 64) + 7) / 8 * 8;
   if (bpairs * (H / hpg) > 2147483647LL)
     return fail(SSD_EUNSUPPORTED, "grid too large for the backward");
-  const size_t need = ssd::bwd_workspace_bytes(Bsz, T, H, P, G, N, chunk);
+  const size_t need = f32 ? ssd::bwd_f32_workspace_bytes(Bsz, T, H, P, G, N, false)
+                          : ssd::bwd_workspace_bytes(Bsz, T, H, P, G, N, chunk);
   if (!workspace || workspace_bytes < need)
     return fail(SSD_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : static_cast<size_t>(0));
@@ -555,7 +562,60 @@ int ssd_chunk_bwd_ev(const void* x, const float* dt, const float* A, const void*
   ssd::BwdArgs a{x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, dy, dh_final, dx, ddt, dA, dB,
                  dC, dD, ddt_bias, dh0, Bsz, T, H, P, G, N, chunk, workspace,
                  reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  if (f32) {
+    if (events) return fail(SSD_EUNSUPPORTED, "the fp32 backward has no per-kernel events");
+    return launch_status(ssd::run_chunk_bwd_f32(a, static_cast<hipStream_t>(stream)));
+  }
   return launch_status(ssd::run_chunk_bwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t ssd_bwd_workspace_size_f32(int Bsz, int T, int H, int P, int G, int N) {
+  if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return 0;
+  return ssd::bwd_f32_workspace_bytes(Bsz, T, H, P, G, N, false);
+}
+
+size_t ssd_complex_bwd_workspace_size(int Bsz, int T, int H, int P, int G, int N) {
+  if (Bsz <= 0 || T < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return 0;
+  return ssd::bwd_f32_workspace_bytes(Bsz, T, H, P, G, N, true);
+}
+
+int ssd_complex_chunk_bwd(const float* x, const float* dt, const float* A, const float* B,
+                          const float* C, const float* dt_bias, float dt_min, float dt_max,
+                          const float* h0, const float* dy, const float* dh_final, float* dx,
+                          float* ddt, float* dA, float* dB, float* dC, float* ddt_bias, float* dh0,
+                          int Bsz, int T, int H, int P, int G, int N, int chunk, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  SSD_TRY(check_chunk_shape(Bsz, T, H, P, G, N, chunk, 1));
+  if (!((P == 64 || P == 32) && (N == 16 || N == 32 || N == 64)))
+    return fail(SSD_EUNSUPPORTED, "complex backward: (P, N) = (%d, %d) not in {32, 64} x {16, 32, 64}", P,
+                N);
+  if (chunk != 64) return fail(SSD_EUNSUPPORTED, "complex backward: chunk=%d, must be 64", chunk);
+  const bool has_tokens = T > 0;
+  SSD_TRY(check_ptr(x, "x", 16, has_tokens));
+  SSD_TRY(check_ptr(dt, "dt", 4, has_tokens));
+  SSD_TRY(check_ptr(A, "A", 8, true));
+  SSD_TRY(check_ptr(B, "B", 16, has_tokens));
+  SSD_TRY(check_ptr(C, "C", 16, has_tokens));
+  SSD_TRY(check_ptr(dt_bias, "dt_bias", 4, false));
+  SSD_TRY(check_ptr(h0, "h0", 16, false));
+  SSD_TRY(check_ptr(dy, "dy", 16, has_tokens));
+  SSD_TRY(check_ptr(dh_final, "dh_final", 16, false));
+  SSD_TRY(check_ptr(dx, "dx", 16, has_tokens));
+  SSD_TRY(check_ptr(ddt, "ddt", 4, has_tokens));
+  SSD_TRY(check_ptr(dA, "dA", 8, true));
+  SSD_TRY(check_ptr(dB, "dB", 16, has_tokens));
+  SSD_TRY(check_ptr(dC, "dC", 16, has_tokens));
+  SSD_TRY(check_ptr(ddt_bias, "ddt_bias", 4, true));
+  SSD_TRY(check_ptr(dh0, "dh0", 16, false));
+  SSD_TRY(check_clamp(dt_min, dt_max));
+  const size_t need = ssd::bwd_f32_workspace_bytes(Bsz, T, H, P, G, N, true);
+  if (!workspace || workspace_bytes < need)
+    return fail(SSD_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  SSD_TRY(check_ptr(workspace, "workspace", 256, true));
+  ssd::CplxBwdArgs a{x, dt, A, B, C, dt_bias, dt_min, dt_max, h0, dy, dh_final, dx, ddt, dA, dB, dC,
+                     ddt_bias, dh0, Bsz, T, H, P, G, N, workspace};
+  return launch_status(ssd::run_complex_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

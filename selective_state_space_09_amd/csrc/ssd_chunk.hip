@@ -64,7 +64,14 @@ struct StateBSlab : Slab<ST, N / 4, 1> {
   }
 };
 
-template <int P, int N>
+// MODE kStateFwd: S_c = sum_s e^{tot - cs_s} delta_s x_s (x) B_s and the
+// chunk's decay (the forward).  kStateFwdUnit: the same with input scale 1
+// (no delta_s on the input term: the rotated-frame form of the complex
+// recurrence).  kStateAdj: the adjoint chunk state of the backward,
+// G_c = sum_l e^{cs_l} dy_l (x) C_l (x = dy, B = C; no decay written).
+constexpr int kStateFwd = 0, kStateFwdUnit = 1, kStateAdj = 2;
+
+template <int P, int N, int MODE = kStateFwd>
 __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min, float dt_max,
@@ -107,10 +114,17 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
 
   const double cum =
       chunk_prologue(dt_raw, Lc, a_re, bias, dt_min, dt_max, dl, cs_hi, cs_lo, wsum, &tot, Q);
-  // weight of each source token to the chunk end
+  // weight of each source token to the chunk end (the adjoint: from the chunk start)
   const double total = tot;
-  if (tid < Q) wre[tid] = __expf(static_cast<float>(total - cum)) * dl[tid];  // exponent <= 0
-  if (tid == 0) {
+  if (tid < Q) {
+    if constexpr (MODE == kStateAdj)
+      wre[tid] = tid < Lc ? __expf(static_cast<float>(cum)) : 0.0f;  // exponent <= 0
+    else if constexpr (MODE == kStateFwdUnit)
+      wre[tid] = tid < Lc ? __expf(static_cast<float>(total - cum)) : 0.0f;
+    else
+      wre[tid] = __expf(static_cast<float>(total - cum)) * dl[tid];
+  }
+  if (MODE != kStateAdj && tid == 0) {
     float* dc = decay + ((static_cast<size_t>(b) * H + h) * nc + c) * 2;
     dc[0] = __expf(static_cast<float>(total));
     dc[1] = 0.0f;
@@ -447,6 +461,56 @@ static hipError_t dispatch_n(const ChunkArgs& a, hipStream_t st) {
     default: break;
   }
   return hipErrorInvalidValue;
+}
+
+// fp32 chunk-state kernel of the backward (see ssd_internal.h)
+template <int P, int N>
+static hipError_t launch_states_f32(const float* x, const float* dt, const float* A, const float* B,
+                                    const float* dt_bias, float dt_min, float dt_max, float* states,
+                                    float* decay, int Bsz, int T, int H, int G, int chunk, int mode,
+                                    hipStream_t st, const hipEvent_t* ev) {
+  const int nc = (T + chunk - 1) / chunk;
+  const int npairs = Bsz * nc;
+  const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * H;
+  if (mode == kStateFwd)
+    launch_k(nc > 0, ssd_state_kernel<P, N, kStateFwd>, dim3(blocks), dim3(kThreads), st, ev, x, dt,
+             A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
+  else if (mode == kStateFwdUnit)
+    launch_k(nc > 0, ssd_state_kernel<P, N, kStateFwdUnit>, dim3(blocks), dim3(kThreads), st, ev, x,
+             dt, A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
+  else
+    launch_k(nc > 0, ssd_state_kernel<P, N, kStateAdj>, dim3(blocks), dim3(kThreads), st, ev, x, dt,
+             A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
+  return hipGetLastError();
+}
+
+hipError_t run_states_f32(const float* x, const float* dt, const float* A, const float* B,
+                          const float* dt_bias, float dt_min, float dt_max, float* states,
+                          float* decay, int Bsz, int T, int H, int P, int G, int N, int chunk,
+                          int mode, hipStream_t st, const hipEvent_t* ev) {
+#define SSD_STATES_F32(PP, NN)                                                                     \
+  if (P == PP && N == NN)                                                                          \
+    return launch_states_f32<PP, NN>(x, dt, A, B, dt_bias, dt_min, dt_max, states, decay, Bsz, T, H, \
+                                     G, chunk, mode, st, ev);
+  SSD_STATES_F32(32, 32)
+  SSD_STATES_F32(32, 64)
+  SSD_STATES_F32(32, 128)
+  SSD_STATES_F32(64, 32)
+  SSD_STATES_F32(64, 64)
+  SSD_STATES_F32(64, 128)
+#undef SSD_STATES_F32
+  return hipErrorInvalidValue;
+}
+
+hipError_t run_pass_f32(float* states, const float* decay, const float* h0, float* h_final, int Bsz,
+                        int H, int P, int N, int nc, hipStream_t st, const hipEvent_t* ev) {
+  switch (N) {
+    case 32: launch_pass<false, 32>(states, decay, h0, h_final, Bsz, H, P, nc, st, ev); break;
+    case 64: launch_pass<false, 64>(states, decay, h0, h_final, Bsz, H, P, nc, st, ev); break;
+    case 128: launch_pass<false, 128>(states, decay, h0, h_final, Bsz, H, P, nc, st, ev); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st) {

@@ -171,6 +171,43 @@ hipError_t run_complex_decode(const DecodeArgs& a, hipStream_t st);  // D unused
 // then holds the fp32 boundary states h_in(c))
 hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_bwd_bf16(const BwdArgs& a, hipStream_t st);
+// fp32 chunk-state kernel for the backward: mode 0 forward chunk states S_c
+// and decays (input scale delta), 1 the same with input scale 1, 2 adjoint
+// chunk states G_c = sum_l e^{cs_l} x_l (x) B_l (x = dy, B = C; decay unused).
+// states (Bsz, nc, H, P, N) fp32; decay (Bsz, H, nc, 2).  P in {32, 64}, N in
+// {32, 64, 128}.
+hipError_t run_states_f32(const float* x, const float* dt, const float* A, const float* B,
+                          const float* dt_bias, float dt_min, float dt_max, float* states,
+                          float* decay, int Bsz, int T, int H, int P, int G, int N, int chunk,
+                          int mode, hipStream_t st, const hipEvent_t* ev);
+// fp32 state passing in place (h_in over S; h0, h_final may be null)
+hipError_t run_pass_f32(float* states, const float* decay, const float* h0, float* h_final, int Bsz,
+                        int H, int P, int N, int nc, hipStream_t st, const hipEvent_t* ev);
+// the fp32 backward (real form, dtype 0) and the complex backward; chunk 64
+hipError_t run_chunk_bwd_f32(const BwdArgs& a, hipStream_t st);
+size_t bwd_f32_workspace_bytes(int Bsz, int T, int H, int P, int G, int N, bool cplx);
+struct CplxBwdArgs {
+  const float* x;
+  const float* dt;
+  const float* A;  // (H, 2)
+  const float* B;  // (Bsz, T, G, N, 2)
+  const float* C;
+  const float* dt_bias;
+  float dt_min, dt_max;
+  const float* h0;        // (Bsz, H, P, N, 2) or null
+  const float* dy;        // (Bsz, T, H, P)
+  const float* dh_final;  // (Bsz, H, P, N, 2) or null
+  float* dx;
+  float* ddt;
+  float* dA;  // (H, 2)
+  float* dB;  // (Bsz, T, G, N, 2)
+  float* dC;
+  float* ddt_bias;
+  float* dh0;  // (Bsz, H, P, N, 2) or null
+  int Bsz, T, H, P, G, N;
+  void* workspace;
+};
+hipError_t run_complex_bwd(const CplxBwdArgs& a, hipStream_t st);
 size_t bwd_workspace_bytes(int Bsz, int T, int H, int P, int G, int N, int chunk);
 int bwd_heads_per_group(int H, int G);
 hipError_t run_conv1d(const ConvArgs& a, hipStream_t st);

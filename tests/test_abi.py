@@ -239,3 +239,40 @@ def test_noalloc_scratch_covers_the_bitmamba_shape():
     """The BitMamba layer shape (B2 T2048 H64 P64 N128, chunk 256) fits the
     allocation-free forward's scratch array."""
     assert ssd.ssd_workspace_size(2, 2048, 64, 64, 1, 128, 256) <= ssd.NOALLOC_SCRATCH_BYTES
+
+
+def test_f32_and_complex_backward_rejects_without_device_use():
+    """Argument checks of the float32 and complex backward run before any HIP
+    call (this host has no GPU): chunk must be 64, the (P, N) sets are
+    enforced, the workspace size is checked, pointers must be aligned."""
+    L = ssd.lib()
+
+    def f32(chunk=64, P=64, N=128, ws=1 << 40, B=GOOD):
+        rc = L.ssd_chunk_bwd(GOOD, GOOD, GOOD, B, GOOD, None, None, 0.0, 1.0, None, GOOD, None,
+                             GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None,
+                             1, 64, 2, P, 1, N, chunk, ssd.SSD_F32, GOOD, ws, None)
+        return rc, L.ssd_last_error().decode()
+    rc, msg = f32(chunk=256)
+    assert rc == ssd.SSD_EUNSUPPORTED and "chunk=256" in msg
+    rc, msg = f32(N=16)
+    assert rc == ssd.SSD_EUNSUPPORTED and "fp32 backward" in msg
+    rc, msg = f32(ws=16)
+    assert rc == ssd.SSD_EWORKSPACE
+    rc, msg = f32(B=MISALIGNED)
+    assert rc == ssd.SSD_EINVAL and "B is not 16-byte aligned" in msg
+    assert ssd.ssd_bwd_workspace_size_f32(1, 64, 2, 64, 1, 128) > 0
+
+    def cplx(chunk=64, P=64, N=64, ws=1 << 40, A=GOOD):
+        rc = L.ssd_complex_chunk_bwd(GOOD, GOOD, A, GOOD, GOOD, None, 0.0, 1.0, None, GOOD, None,
+                                     GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None,
+                                     1, 64, 2, P, 2, N, chunk, GOOD, ws, None)
+        return rc, L.ssd_last_error().decode()
+    rc, msg = cplx(chunk=128)
+    assert rc == ssd.SSD_EUNSUPPORTED and "chunk=128" in msg
+    rc, msg = cplx(P=128)
+    assert rc == ssd.SSD_EUNSUPPORTED and "complex backward" in msg
+    rc, msg = cplx(N=128)
+    assert rc == ssd.SSD_EUNSUPPORTED
+    rc, msg = cplx(ws=16)
+    assert rc == ssd.SSD_EWORKSPACE
+    assert ssd.ssd_complex_bwd_workspace_size(1, 64, 2, 64, 2, 64) > 0

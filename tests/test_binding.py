@@ -153,3 +153,16 @@ def test_packed_rejects_mismatched_shapes():
         _raises_shape(ssd.ssd_complex_chunk_fwd_packed, name, **kw)
     with pytest.raises(ValueError, match="columns"):
         ssd.ssd_complex_chunk_fwd_packed(proj[..., :-1], torch.zeros(H, 2), H, P, N)
+
+
+def test_complex_backward_rejects_mismatched_shapes():
+    kw = cplx_args()
+    kw["dy"] = torch.zeros(1, 8, 2, 16)
+    kw["dh_final"] = torch.zeros(1, 2, 16, 16, 2)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ssd.ssd_complex_chunk_bwd(**kw)
+    for name, bad in (("dy", torch.zeros(1, 8, 2, 8)), ("dh_final", torch.zeros(1, 2, 16, 16)),
+                      ("A", torch.zeros(2)), ("C", torch.zeros(1, 8, 2, 15, 2))):
+        k2 = dict(kw)
+        k2[name] = bad
+        _raises_shape(ssd.ssd_complex_chunk_bwd, name, **k2)
