@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--workload", default="bitmamba_bf16",
                     choices=["bitmamba_bf16", "long_bf16", "mamba3lite_complex", "tiny_f32",
                              "decode_f32", "decode_complex", "conv_bf16", "conv_decode_f32",
-                             "bwd_bf16", "mamba3lite_packed", "mimo_bf16"])
+                             "bwd_bf16", "bwd_complex", "mamba3lite_packed", "mimo_bf16"])
     ap.add_argument("--no-flush", action="store_true",
                     help="keep the Infinity Cache warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,6 +106,7 @@ KERNEL_SOURCES = {
     "bwd_bf16": ["ssd_bwd_bf16.hip", "ssd_chunk_bf16.hip"],
     "mamba3lite_packed": ["ssd_chunk_cplx.hip"],
     "mimo_bf16": ["ssd_linear.hip"],
+    "bwd_complex": ["ssd_bwd_f32.hip", "ssd_chunk.hip"],
 }
 
 
@@ -362,6 +363,8 @@ def main():
         return bench_conv(args, cfg)
     if cfg["kind"] == "bwd":
         return bench_bwd(args, cfg)
+    if cfg["kind"] == "bwd_complex":
+        return bench_bwd_complex(args, cfg)
     if cfg["kind"] == "mimo":
         return bench_mimo(args, cfg)
     inp = inputs.make_workload(args.workload, seed=0)
@@ -883,6 +886,150 @@ def bench_bwd(args, cfg):
             "value": reps * Bsz * T / total, "unit": "tokens/s", "cores": oracle.threads_used(),
             "kind": "oracle",
             "sample": f"the whole workload (float64 adjoint recurrence), {reps} passes in {total:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
+CPLX_BWD_KERNELS = ["ssd_cplx_rotate_kernel", "ssd_state_kernel(unit scale)", "ssd_pass_kernel",
+                    "ssd_state_kernel(adjoint)", "ssd_f32_adj_pass_kernel", "ssd_f32_col_kernel",
+                    "ssd_f32_row_kernel", "ssd_f32_const_kernel", "ssd_cplx_tau_kernel",
+                    "ssd_cplx_rho_total_kernel", "ssd_f32_dt_kernel", "ssd_f32_dt_sum_kernel",
+                    "ssd_f32_group_sum_kernel", "ssd_cplx_dh0_kernel"]
+
+
+def cplx_bwd_costs(dims):
+    """Algorithmic HBM bytes of the whole complex backward (x, dt, B, C, dy in;
+    dx, ddt, dB, dC out; complex64 B/C/dB/dC, float32 x/dy/dx) and the fp32
+    matrix flops of the two block kernels and the chunk-state kernels, in the
+    rotated frame (2N real features), 64-token chunks."""
+    Bsz, T, H, P, G, N = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N"))
+    Q, NE = 64, 2 * N
+    x = Bsz * T * H * P * 4
+    bc = Bsz * T * G * N * 8
+    units = Bsz * (T / Q) * H
+    tri = Q * (Q + 1) / 2
+    state = units * 2 * Q * P * NE
+    col = units * (2 * Q * Q * NE + 2 * Q * Q * P + 2 * tri * P + 2 * Q * P * NE * 2 + 2 * tri * NE)
+    row = units * (2 * Q * Q * NE + 2 * Q * Q * P + 2 * Q * P * NE + 2 * tri * NE)
+    return {"whole_backward": 3 * x + 4 * bc + 2 * Bsz * T * H * 4,
+            "flops": {"ssd_state_kernel(unit scale)": state, "ssd_state_kernel(adjoint)": state,
+                      "ssd_f32_col_kernel": col, "ssd_f32_row_kernel": row}}
+
+
+def bench_bwd_complex(args, cfg):
+    """Complex backward at the Mamba-3-Lite layer shape: one step = one
+    ssd_complex_chunk_bwd over the whole batch (B8 T2048 H16 P64 N64, chunk
+    64, gradients of every input through y), the 512 MiB flush read between
+    steps.  fp32 matrix products: MFMA figures against the fp32 peak."""
+    import torch
+    import selective_state_space_09_amd as ssd
+    from selective_state_space_09_amd import inputs
+    inp = inputs.make_workload(args.workload, seed=0)
+    dims = dict(inp["dims"])
+    Bsz, T, H, P, G, N = (dims[k] for k in ("Bsz", "T", "H", "P", "G", "N"))
+    Q = cfg["chunk"]
+    dev = torch.device("cuda:0")
+    d = {k: (torch.from_numpy(np.ascontiguousarray(v)).to(dev) if isinstance(v, np.ndarray) else v)
+         for k, v in inp.items()}
+    f32 = dict(dtype=torch.float32, device=dev)
+    dx = torch.empty((Bsz, T, H, P), **f32)
+    ddt = torch.empty((Bsz, T, H), **f32)
+    dA = torch.empty((H, 2), **f32)
+    dB = torch.empty((Bsz, T, G, N, 2), **f32)
+    dC = torch.empty_like(dB)
+    dbias = torch.empty(H, **f32)
+    ws = torch.empty(ssd.ssd_complex_bwd_workspace_size(Bsz, T, H, P, G, N), dtype=torch.uint8,
+                     device=dev)
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    L = ssd.lib()
+    hip = Hip()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P_ = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["dt_bias"]),
+             float(d["dt_min"]), float(d["dt_max"]), None, P_(d["dy"]), None, P_(dx), P_(ddt),
+             P_(dA), P_(dB), P_(dC), P_(dbias), None, Bsz, T, H, P, G, N, Q, P_(ws), ws.numel(), sp)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(L.ssd_last_error().decode())
+
+    n_total = args.warmup + args.steps
+    step_evs = [(hip.event(), hip.event()) for _ in range(n_total)]
+    for i in range(n_total):
+        if flush is not None:
+            flush.max()
+        a, b = step_evs[i]
+        hip.lib.hipEventRecord(a, sp)
+        check(L.ssd_complex_chunk_bwd(*fixed))
+        hip.lib.hipEventRecord(b, sp)
+    torch.cuda.synchronize()
+    per_step = [hip.elapsed_ms(*step_evs[i]) for i in range(args.warmup, n_total)]
+    n_kern = max(10, args.steps // 2)
+    nev = 2 * len(CPLX_BWD_KERNELS)
+    evs = [[hip.event() for _ in range(nev)] for _ in range(n_kern)]
+    for i in range(n_kern):
+        if flush is not None:
+            flush.max()
+        arr = (ctypes.c_void_p * nev)(*[e.value for e in evs[i]])
+        check(L.ssd_complex_chunk_bwd_ev(*fixed, arr))
+    torch.cuda.synchronize()
+    costs = cplx_bwd_costs(dims)
+    kern = {}
+    for k, name in enumerate(CPLX_BWD_KERNELS):
+        avg = float(np.mean([hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in evs]))
+        ent = {"avg_us": avg * 1e3}
+        fl = costs["flops"].get(name)
+        if fl:
+            tf = fl / (avg / 1e3) / 1e12
+            ent.update({"alg_flops": fl, "mfma_tflops": tf, "mfma_frac": tf / MFMA_PEAK_TFLOPS["f32"]})
+        kern[name] = ent
+    ms = float(np.mean(per_step))
+    dom = max(kern, key=lambda n: kern[n]["avg_us"])
+    dom_s = kern[dom]["avg_us"] / 1e6
+    whole = costs["whole_backward"]
+    achieved = whole / dom_s / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload, dom),
+            "kernel": dom, "alg_bytes": whole, "launch_us": dom_s * 1e6}
+    if "alg_flops" in kern[dom]:
+        roof["mfma"] = {"alg_flops": kern[dom]["alg_flops"], "tflops": kern[dom]["mfma_tflops"],
+                        "executed_dtype": "f32", "peak": MFMA_PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                        "frac": kern[dom]["mfma_frac"]}
+    out = {
+        "metric": "SSD complex bwd tokens/s per layer (H16 P64 N64 complex64)",
+        "value": Bsz * T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": Bsz, "seq_len": T, "heads": H, "headdim": P,
+                   "d_state": N, "ngroups": G, "chunk": Q, "complex": True,
+                   "cache": "cold (Infinity Cache flushed between steps)" if flush is not None
+                   else "warm"},
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(np.min(per_step)),
+        "roofline": roof,
+        "end_to_end": {"alg_bytes": whole, "gbs": whole / (ms / 1e3) / 1e9,
+                       "frac": whole / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        oracle.set_threads(threads)
+        # one sequence (its H recurrences) at a time, repeated to ~cpu_seconds / 3
+        one = {k: (np.ascontiguousarray(v[:1]) if isinstance(v, np.ndarray) and v.ndim >= 3 else v)
+               for k, v in inp.items()}
+        reps, total = 0, 0.0
+        while total < args.cpu_seconds / 3:
+            t0 = time.perf_counter()
+            oracle.complex_bwd(one["x"], one["dt"], one["A"], one["B"], one["C"], one["dy"],
+                               one["dt_bias"], one["dt_min"], one["dt_max"], None, None,
+                               want_dh0=False)
+            total += time.perf_counter() - t0
+            reps += 1
+        out["cpu_baseline"] = {
+            "value": reps * T / total, "unit": "tokens/s", "cores": oracle.threads_used(),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"one of the {Bsz} sequences ({H} complex recurrences of T={T}, float64 "
+                      f"adjoint), {reps} runs in {total:.2f} s; tokens/s of that sequence"}
     print(json.dumps(out), flush=True)
 
 

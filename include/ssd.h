@@ -354,11 +354,13 @@ int ssd_chunk_bwd(const void *x, const float *dt, const float *A, const void *B,
 
 /*
  * Measurement variant of ssd_chunk_bwd: identical arguments, kernels and
- * result, plus `events`, 22 hipEvent_t (passed as void*): a start/stop pair
- * bound to each of the 11 kernels' dispatches in order (chunk states, state
- * passing, adjoint chunk states, adjoint passing, dx/dB blocks, dC blocks,
- * chunk constants of da, step-size gradients per chunk, their sums per head,
- * dB sum, dC sum), or NULL.
+ * result, plus `events` (hipEvent_t passed as void*), or NULL.  SSD_BF16: 22
+ * events, a start/stop pair bound to each of the 11 kernels' dispatches in
+ * order (chunk states, state passing, adjoint chunk states, adjoint passing,
+ * dx/dB blocks, dC blocks, chunk constants of da, step-size gradients per
+ * chunk, their sums per head, dB sum, dC sum).  SSD_F32: 28 events, the 14
+ * slots of ssd_complex_chunk_bwd_ev (the complex-only slots record their pair
+ * back to back).
  */
 int ssd_chunk_bwd_ev(const void *x, const float *dt, const float *A, const void *B,
                      const void *C, const float *D, const float *dt_bias, float dt_min,
@@ -389,6 +391,21 @@ int ssd_chunk_bwd_ev(const void *x, const float *dt, const float *A, const void 
  * 256-byte aligned.  Errors as for ssd_complex_chunk_fwd.
  */
 size_t ssd_complex_bwd_workspace_size(int Bsz, int T, int H, int P, int G, int N);
+
+/* Measurement variant of ssd_complex_chunk_bwd: identical arguments, kernels
+ * and result, plus `events`, 28 hipEvent_t (passed as void*) or NULL: a
+ * start/stop pair bound to each of 14 kernel slots in order (rotation into
+ * the sequence frame, chunk states, state passing, adjoint chunk states,
+ * adjoint passing, column-side blocks, row-side blocks, chunk constants, the
+ * last token's rotation term, rho sums per chunk, step-size gradients per
+ * chunk, their sums per head, dB/dC group sums, dh0). */
+int ssd_complex_chunk_bwd_ev(const float *x, const float *dt, const float *A, const float *B,
+                             const float *C, const float *dt_bias, float dt_min, float dt_max,
+                             const float *h0, const float *dy, const float *dh_final, float *dx,
+                             float *ddt, float *dA, float *dB, float *dC, float *ddt_bias,
+                             float *dh0, int Bsz, int T, int H, int P, int G, int N, int chunk,
+                             void *workspace, size_t workspace_bytes, void *stream,
+                             void *const *events);
 
 int ssd_complex_chunk_bwd(const float *x, const float *dt, const float *A, const float *B,
                           const float *C, const float *dt_bias, float dt_min, float dt_max,

@@ -82,6 +82,8 @@ def lib():
     L.ssd_complex_chunk_bwd.restype = I
     L.ssd_complex_chunk_bwd.argtypes = [P, P, P, P, P, P, F, F, P, P, P, P, P, P, P, P, P, P,
                                         I, I, I, I, I, I, I, P, S, P]
+    L.ssd_complex_chunk_bwd_ev.restype = I
+    L.ssd_complex_chunk_bwd_ev.argtypes = L.ssd_complex_chunk_bwd.argtypes + [P]
     L.ssd_conv1d_fwd.restype = I
     L.ssd_conv1d_fwd.argtypes = [P, LL, P, P, P, I, P, P, P, P, I, I, I, I, I, I, P]
     L.ssd_conv1d_fwd_ev.restype = I

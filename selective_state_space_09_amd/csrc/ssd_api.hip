@@ -562,10 +562,7 @@ int ssd_chunk_bwd_ev(const void* x, const float* dt, const float* A, const void*
   ssd::BwdArgs a{x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, dy, dh_final, dx, ddt, dA, dB,
                  dC, dD, ddt_bias, dh0, Bsz, T, H, P, G, N, chunk, workspace,
                  reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
-  if (f32) {
-    if (events) return fail(SSD_EUNSUPPORTED, "the fp32 backward has no per-kernel events");
-    return launch_status(ssd::run_chunk_bwd_f32(a, static_cast<hipStream_t>(stream)));
-  }
+  if (f32) return launch_status(ssd::run_chunk_bwd_f32(a, static_cast<hipStream_t>(stream)));
   return launch_status(ssd::run_chunk_bwd_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -585,6 +582,18 @@ int ssd_complex_chunk_bwd(const float* x, const float* dt, const float* A, const
                           float* ddt, float* dA, float* dB, float* dC, float* ddt_bias, float* dh0,
                           int Bsz, int T, int H, int P, int G, int N, int chunk, void* workspace,
                           size_t workspace_bytes, void* stream) {
+  return ssd_complex_chunk_bwd_ev(x, dt, A, B, C, dt_bias, dt_min, dt_max, h0, dy, dh_final, dx, ddt,
+                                  dA, dB, dC, ddt_bias, dh0, Bsz, T, H, P, G, N, chunk, workspace,
+                                  workspace_bytes, stream, nullptr);
+}
+
+int ssd_complex_chunk_bwd_ev(const float* x, const float* dt, const float* A, const float* B,
+                             const float* C, const float* dt_bias, float dt_min, float dt_max,
+                             const float* h0, const float* dy, const float* dh_final, float* dx,
+                             float* ddt, float* dA, float* dB, float* dC, float* ddt_bias,
+                             float* dh0, int Bsz, int T, int H, int P, int G, int N, int chunk,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events) {
   SSD_TRY(check_chunk_shape(Bsz, T, H, P, G, N, chunk, 1));
   if (!((P == 64 || P == 32) && (N == 16 || N == 32 || N == 64)))
     return fail(SSD_EUNSUPPORTED, "complex backward: (P, N) = (%d, %d) not in {32, 64} x {16, 32, 64}", P,
@@ -614,7 +623,8 @@ int ssd_complex_chunk_bwd(const float* x, const float* dt, const float* A, const
                 workspace ? workspace_bytes : static_cast<size_t>(0));
   SSD_TRY(check_ptr(workspace, "workspace", 256, true));
   ssd::CplxBwdArgs a{x, dt, A, B, C, dt_bias, dt_min, dt_max, h0, dy, dh_final, dx, ddt, dA, dB, dC,
-                     ddt_bias, dh0, Bsz, T, H, P, G, N, workspace};
+                     ddt_bias, dh0, Bsz, T, H, P, G, N, workspace,
+                     reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
   return launch_status(ssd::run_complex_bwd(a, static_cast<hipStream_t>(stream)));
 }
 

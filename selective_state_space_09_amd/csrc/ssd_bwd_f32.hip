@@ -53,6 +53,11 @@
 //   ssd_f32_dt_sum        per head: the sums of the shares
 //   ssd_f32_group_sum     dB, dC: the heads of each group summed (complex:
 //                         rotated back first); complex dh0 interleaved
+// With measurement events, pair k (events 2k, 2k+1) is bound to: 0 rotation,
+// 1 chunk states, 2 state passing, 3 adjoint chunk states, 4 adjoint passing,
+// 5 column side, 6 row side, 7 chunk constants, 8 tau, 9 rho totals,
+// 10 step sizes, 11 their sums, 12 group sums, 13 dh0 (a kernel a form does
+// not run records its pair back to back).
 //
 // MFMA operands: 16x16x4 fp32, lane i holding A[i%16][k] and B[k][i%16] of
 // one k per instruction.  A run of four instructions takes k = 4q + j
@@ -758,7 +763,9 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
                            const float* dt_bias, float dt_min, float dt_max, const float* Beff,
                            const float* Ceff, int Geff, const float* dy, const float* D,
                            float* dx, float* ddt, float* dA, float* dD, float* ddt_bias, char* ws,
-                           const F32BwdLayout& L, int Bsz, int T, int H, hipStream_t st) {
+                           const F32BwdLayout& L, int Bsz, int T, int H, hipStream_t st,
+                           const hipEvent_t* ev) {
+  auto E = [&](int k) { return ev ? ev + 2 * k : nullptr; };
   const int nc = (T + kQ - 1) / kQ;
   const size_t tok = static_cast<size_t>(Bsz) * T * H;
   float* tv = reinterpret_cast<float*>(ws + L.tokv);
@@ -774,27 +781,25 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
   const dim3 grid(nc > 0 ? nc : 1, H, Bsz);
   constexpr bool SCALE = !CPLX;
   const bool run = nc > 0;
-  launch_k(run, ssd_f32_col_kernel<P, NE, SCALE, CPLX>, grid, dim3(kThreads), st, nullptr, x, dt, A_dec,
+  launch_k(run, ssd_f32_col_kernel<P, NE, SCALE, CPLX>, grid, dim3(kThreads), st, E(5), x, dt, A_dec,
            dt_bias, dt_min, dt_max, Beff, Ceff, dy, D, adj, dx, dBh, f2, col, xv, dyx, rhoB, T, H, Geff,
            nc);
-  launch_k(run, ssd_f32_row_kernel<P, NE, SCALE, CPLX>, grid, dim3(kThreads), st, nullptr, x, dt, A_dec,
+  launch_k(run, ssd_f32_row_kernel<P, NE, SCALE, CPLX>, grid, dim3(kThreads), st, E(6), x, dt, A_dec,
            dt_bias, dt_min, dt_max, Beff, Ceff, dy, S, dCh, f1, rw, rhoC, T, H, Geff, nc);
-  launch_k(run, ssd_f32_const_kernel, grid, dim3(kThreads), st, nullptr, adj, S, dec, cst, H, P * NE, nc);
-  if constexpr (CPLX) {
-    launch_k(true, ssd_cplx_tau_kernel, dim3(H, Bsz), dim3(kThreads), st, nullptr,
-             reinterpret_cast<const float*>(ws + L.dhfe), reinterpret_cast<const float*>(ws + L.hfe),
-             rhoB, T, H, P, NE / 2);
-    launch_k(run, ssd_cplx_rho_total_kernel, grid, dim3(kQ), st, nullptr, static_cast<const float*>(rhoB),
-             static_cast<const float*>(rhoC), reinterpret_cast<double*>(ws + L.rtot), T, H, nc);
-  }
-  launch_k(run, ssd_f32_dt_kernel<CPLX>, grid, dim3(kQ), st, nullptr, dt, A_dt, dt_bias, dt_min, dt_max,
+  launch_k(run, ssd_f32_const_kernel, grid, dim3(kThreads), st, E(7), adj, S, dec, cst, H, P * NE, nc);
+  launch_k(CPLX, ssd_cplx_tau_kernel, dim3(H, Bsz), dim3(kThreads), st, E(8),
+           reinterpret_cast<const float*>(ws + L.dhfe), reinterpret_cast<const float*>(ws + L.hfe), rhoB,
+           T, H, P, NE / 2);
+  launch_k(CPLX && run, ssd_cplx_rho_total_kernel, grid, dim3(kQ), st, E(9), static_cast<const float*>(rhoB),
+           static_cast<const float*>(rhoC), reinterpret_cast<double*>(ws + L.rtot), T, H, nc);
+  launch_k(run, ssd_f32_dt_kernel<CPLX>, grid, dim3(kQ), st, E(10), dt, A_dt, dt_bias, dt_min, dt_max,
            static_cast<const float*>(f1), static_cast<const float*>(f2), static_cast<const float*>(col),
            static_cast<const float*>(rw), static_cast<const float*>(xv), static_cast<const float*>(dyx),
            static_cast<const double*>(cst), static_cast<const float*>(rhoB), static_cast<const float*>(rhoC),
            CPLX ? reinterpret_cast<const double*>(ws + L.rtot) : nullptr,
            CPLX ? reinterpret_cast<const double*>(ws + L.u) : nullptr, ddt, part, T, H, nc);
   launch_k(true, ssd_f32_dt_sum_kernel<CPLX>, dim3((H + kThreads - 1) / kThreads), dim3(kThreads), st,
-           nullptr, static_cast<const double*>(part), dA, ddt_bias, dD, Bsz, H, nc);
+           E(11), static_cast<const double*>(part), dA, ddt_bias, dD, Bsz, H, nc);
   return hipGetLastError();
 }
 
@@ -803,6 +808,9 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
 template <int P, int N>
 static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
   const int nc = (a.T + kQ - 1) / kQ;
+  const hipEvent_t* ev = a.events;
+  auto E = [&](int k) { return ev ? ev + 2 * k : nullptr; };
+  launch_k(false, ssd_cplx_dh0_kernel, dim3(1), dim3(kThreads), st, E(0), nullptr, nullptr, size_t{0}, 0);
   const F32BwdLayout L = f32_layout(a.Bsz, a.T, a.H, P, N, false);
   char* ws = static_cast<char*>(a.workspace);
   float* S = reinterpret_cast<float*>(ws + L.S);
@@ -813,23 +821,24 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
   const float* C = static_cast<const float*>(a.C);
   const float* dy = static_cast<const float*>(a.dy);
   hipError_t e = run_states_f32(x, a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, dec, a.Bsz, a.T, a.H,
-                                P, a.G, N, kQ, 0, st, nullptr);
-  if (e == hipSuccess) e = run_pass_f32(S, dec, a.h0, nullptr, a.Bsz, a.H, P, N, nc, st, nullptr);
+                                P, a.G, N, kQ, 0, st, E(1));
+  if (e == hipSuccess) e = run_pass_f32(S, dec, a.h0, nullptr, a.Bsz, a.H, P, N, nc, st, E(2));
   if (e == hipSuccess)
     e = run_states_f32(dy, a.dt, a.A, C, a.dt_bias, a.dt_min, a.dt_max, adj, nullptr, a.Bsz, a.T, a.H, P,
-                       a.G, N, kQ, 2, st, nullptr);
+                       a.G, N, kQ, 2, st, E(3));
   if (e != hipSuccess) return e;
   launch_k(true, ssd_f32_adj_pass_kernel, dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
-           dim3(kThreads), st, nullptr, adj, static_cast<const float*>(dec), a.dh_final, a.dh0, a.H,
+           dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), a.dh_final, a.dh0, a.H,
            P * N, nc);
   e = launch_f32_core<P, N, false>(x, a.dt, a.A, a.A, a.dt_bias, a.dt_min, a.dt_max, B, C, a.G, dy, a.D,
                                    static_cast<float*>(a.dx), a.ddt, a.dA, a.dD, a.ddt_bias, ws, L, a.Bsz,
-                                   a.T, a.H, st);
+                                   a.T, a.H, st, ev);
   if (e != hipSuccess) return e;
   const size_t rows = static_cast<size_t>(a.Bsz) * a.T;
   const size_t nthreads = rows * a.G * (N / 4);
+  launch_k(false, ssd_cplx_dh0_kernel, dim3(1), dim3(kThreads), st, E(13), nullptr, nullptr, size_t{0}, 0);
   launch_k(nthreads > 0, ssd_f32_group_sum_kernel<false>,
-           dim3(static_cast<unsigned>((nthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, nullptr,
+           dim3(static_cast<unsigned>((nthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, E(12),
            reinterpret_cast<const float*>(ws + L.dBh), reinterpret_cast<const float*>(ws + L.dCh),
            static_cast<const double*>(nullptr), static_cast<const float*>(nullptr), a.dB, a.dC, rows,
            a.H, a.G, N);
@@ -850,6 +859,8 @@ template <int P, int N>
 static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   constexpr int NE = 2 * N;
   const int nc = (a.T + kQ - 1) / kQ;
+  const hipEvent_t* ev = a.events;
+  auto E = [&](int k) { return ev ? ev + 2 * k : nullptr; };
   const F32BwdLayout L = f32_layout(a.Bsz, a.T, a.H, P, N, true);
   char* ws = static_cast<char*>(a.workspace);
   float* S = reinterpret_cast<float*>(ws + L.S);
@@ -863,35 +874,34 @@ static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   float* dhfe = reinterpret_cast<float*>(ws + L.dhfe);
   float* hfe = reinterpret_cast<float*>(ws + L.hfe);
   float* dh0e = reinterpret_cast<float*>(ws + L.dh0e);
-  launch_k(true, ssd_cplx_rotate_kernel, dim3(a.H, a.Bsz), dim3(kThreads), st, nullptr, a.dt, a.A,
+  launch_k(true, ssd_cplx_rotate_kernel, dim3(a.H, a.Bsz), dim3(kThreads), st, E(0), a.dt, a.A,
            a.dt_bias, a.dt_min, a.dt_max, a.B, a.C, a.h0, a.dh_final, u, Beff, Ceff, alpha, h0e, dhfe, a.T,
            a.H, a.G, P, N);
   // the rotated-frame real problem: per-head features (G = H), decay alpha, input scale 1
   hipError_t e = run_states_f32(a.x, a.dt, alpha, Beff, a.dt_bias, a.dt_min, a.dt_max, S, dec, a.Bsz, a.T,
-                                a.H, P, a.H, NE, kQ, 1, st, nullptr);
-  if (e == hipSuccess) e = run_pass_f32(S, dec, h0e, hfe, a.Bsz, a.H, P, NE, nc, st, nullptr);
+                                a.H, P, a.H, NE, kQ, 1, st, E(1));
+  if (e == hipSuccess) e = run_pass_f32(S, dec, h0e, hfe, a.Bsz, a.H, P, NE, nc, st, E(2));
   if (e == hipSuccess)
     e = run_states_f32(a.dy, a.dt, alpha, Ceff, a.dt_bias, a.dt_min, a.dt_max, adj, nullptr, a.Bsz, a.T,
-                       a.H, P, a.H, NE, kQ, 2, st, nullptr);
+                       a.H, P, a.H, NE, kQ, 2, st, E(3));
   if (e != hipSuccess) return e;
   launch_k(true, ssd_f32_adj_pass_kernel, dim3((P * NE / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
-           dim3(kThreads), st, nullptr, adj, static_cast<const float*>(dec), static_cast<const float*>(dhfe),
+           dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), static_cast<const float*>(dhfe),
            dh0e, a.H, P * NE, nc);
   e = launch_f32_core<P, NE, true>(a.x, a.dt, alpha, a.A, a.dt_bias, a.dt_min, a.dt_max, Beff, Ceff, a.H,
                                    a.dy, nullptr, a.dx, a.ddt, a.dA, nullptr, a.ddt_bias, ws, L, a.Bsz, a.T,
-                                   a.H, st);
+                                   a.H, st, ev);
   if (e != hipSuccess) return e;
   const size_t rows = static_cast<size_t>(a.Bsz) * a.T;
   const size_t nthreads = rows * a.G * N;
   launch_k(nthreads > 0, ssd_f32_group_sum_kernel<true>,
-           dim3(static_cast<unsigned>((nthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, nullptr,
+           dim3(static_cast<unsigned>((nthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, E(12),
            reinterpret_cast<const float*>(ws + L.dBh), reinterpret_cast<const float*>(ws + L.dCh),
            static_cast<const double*>(u), a.A, a.dB, a.dC, rows, a.H, a.G, N);
-  if (a.dh0) {
-    const size_t total = static_cast<size_t>(a.Bsz) * a.H * P * N;
-    launch_k(true, ssd_cplx_dh0_kernel, dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)),
-             dim3(kThreads), st, nullptr, static_cast<const float*>(dh0e), a.dh0, total, N);
-  }
+  const size_t total = static_cast<size_t>(a.Bsz) * a.H * P * N;
+  launch_k(a.dh0 != nullptr, ssd_cplx_dh0_kernel,
+           dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)), dim3(kThreads), st, E(13),
+           static_cast<const float*>(dh0e), a.dh0, total, N);
   return hipGetLastError();
 }
 

@@ -206,6 +206,7 @@ struct CplxBwdArgs {
   float* dh0;  // (Bsz, H, P, N, 2) or null
   int Bsz, T, H, P, G, N;
   void* workspace;
+  hipEvent_t* events;  // NULL, or 28: start/stop of each of the 14 kernel slots
 };
 hipError_t run_complex_bwd(const CplxBwdArgs& a, hipStream_t st);
 size_t bwd_workspace_bytes(int Bsz, int T, int H, int P, int G, int N, int chunk);

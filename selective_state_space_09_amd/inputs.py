@@ -49,6 +49,9 @@ WORKLOADS = {
     # loss through y: seeded dy, no h0, no dh_final)
     "bwd_bf16": dict(kind="bwd", Bsz=2, T=2048, H=64, P=64, N=128, G=1, chunk=256,
                      dtype="bf16"),
+    # backward of the complex scan at the Mamba-3-Lite layer shape (loss
+    # through y: seeded dy, no h0, no dh_final), chunk 64
+    "bwd_complex": dict(kind="bwd_complex", Bsz=8, T=2048, H=16, P=64, N=64, G=16, chunk=64),
     # depthwise causal conv (K = 4, SiLU) of the BitMamba layer over its x|B|C
     # channels (4096 + 128 + 128), read from the in_proj output row (width
     # 2*4096 + 2*128 + 64 = 8512: z, x, B, C, dt) and split into the scan's inputs
@@ -282,6 +285,13 @@ def make_workload(name, seed=0, **overrides):
         dy = _normal(rng, (d["Bsz"], d["T"], d["H"], d["P"]))
         inp["dy"] = f32_to_bf16_bits(dy) if cfg.get("dtype") == "bf16" else dy
         inp["kind"] = "bwd"
+        return inp
+    if kind == "bwd_complex":
+        inp = make_complex(seed=seed, **cfg)
+        rng = np.random.default_rng(seed + 1)
+        d = inp["dims"]
+        inp["dy"] = _normal(rng, (d["Bsz"], d["T"], d["H"], d["P"]))
+        inp["kind"] = "bwd_complex"
         return inp
     if kind == "conv_decode":
         return make_conv_decode(seed=seed, **cfg)
