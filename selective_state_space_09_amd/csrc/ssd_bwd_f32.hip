@@ -38,8 +38,9 @@
 // The angles theta_t are reduced modulo 2 pi in double precision.
 //
 // Kernels (one workgroup per (chunk, head, batch) unless noted):
-//   ssd_cplx_rotate       (complex) per (batch, head): u and theta over the
-//                         sequence (fp64), B_eff, C_eff, the rotated h0 and dh_final
+//   ssd_cplx_u_local, ssd_cplx_rotate  (complex) u and theta over the sequence
+//                         (fp64: chunk sums, then each chunk adds the totals of the
+//                         earlier ones), B_eff, C_eff, the rotated h0 and dh_final
 //   chunk states, state passing, adjoint chunk states: ssd_chunk.hip's fp32
 //                         kernels (run_states_f32, run_pass_f32)
 //   ssd_f32_adj_pass      R_c in place over G_c, last chunk first; dh0
@@ -52,8 +53,11 @@
 //                         the chunk's shares of dA, ddt_bias, dD [, d beta]
 //   ssd_f32_dt_sum        per head: the sums of the shares
 //   ssd_f32_group_sum     dB, dC: the heads of each group summed (complex:
-//                         rotated back first); complex dh0 interleaved
-// With measurement events, pair k (events 2k, 2k+1) is bound to: 0 rotation,
+//                         rotated back first); complex dh0 interleaved.  When
+//                         each head has its own group the block kernels write
+//                         dB and dC directly (complex: rotated back) instead
+// With measurement events, pair k (events 2k, 2k+1) is bound to: 0 rotation
+// (from the start of the u sums to the end of the rotation),
 // 1 chunk states, 2 state passing, 3 adjoint chunk states, 4 adjoint passing,
 // 5 column side, 6 row side, 7 chunk constants, 8 tau, 9 rho totals,
 // 10 step sizes, 11 their sums, 12 group sums, 13 dh0 (a kernel a form does
@@ -128,7 +132,8 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_col_kernel(
     const float* __restrict__ Cm, const float* __restrict__ dy, const float* __restrict__ D,
     const float* __restrict__ adj, float* __restrict__ dx, float* __restrict__ dBh,
     float* __restrict__ f2o, float* __restrict__ colo, float* __restrict__ xvo,
-    float* __restrict__ dyxo, float* __restrict__ rhoB, int T, int H, int G, int nc) {
+    float* __restrict__ dyxo, float* __restrict__ rhoB, const float2* __restrict__ rot,
+    float* __restrict__ dBo, int T, int H, int G, int nc) {
   constexpr int XP = P + 4, NP = NE + 4;
   constexpr int PT = P / 16, NT = NE / 16;
   __shared__ __attribute__((aligned(16))) float Xs[kQ * XP];
@@ -247,9 +252,27 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_col_kernel(
         db[nt] = mfma_f32(Cs[(16 * lt + 4 * q + j) * NP + 16 * nt + r16], sW[lt][j], db[nt]);
   const size_t row = (r0 + s) * H + h;
   if (s < Lc) {
+    if (CPLX && dBo) {
+      // each head its own group: dB = e^{i theta} (dB_eff[n] + i dB_eff[N+n]) straight out
+      const float2 r = rot[row];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      *reinterpret_cast<f32x4*>(dBh + row * NE + 16 * nt + 4 * q) = db[nt];
+      for (int nt = 0; nt < NT / 2; ++nt) {
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xr = db[nt][i], xi = db[nt + NT / 2][i];
+          o[2 * i] = xr * r.x - xi * r.y;
+          o[2 * i + 1] = xr * r.y + xi * r.x;
+        }
+        float* dst = dBo + (row * (NE / 2) + 16 * nt + 4 * q) * 2;
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<f32x4*>(dBh + row * NE + 16 * nt + 4 * q) = db[nt];
+    }
   }
   float rb = 0.0f;
   if constexpr (CPLX) {
@@ -286,7 +309,8 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_row_kernel(
     const float* __restrict__ dt_bias, float dt_min, float dt_max, const float* __restrict__ Bm,
     const float* __restrict__ Cm, const float* __restrict__ dy, const float* __restrict__ states,
     float* __restrict__ dCh, float* __restrict__ f1o, float* __restrict__ rowo,
-    float* __restrict__ rhoC, int T, int H, int G, int nc) {
+    float* __restrict__ rhoC, const float2* __restrict__ rot, float* __restrict__ dCo, int T, int H,
+    int G, int nc) {
   constexpr int XP = P + 4, NP = NE + 4;
   constexpr int NT = NE / 16;
   __shared__ __attribute__((aligned(16))) float Xs[kQ * XP];
@@ -369,9 +393,27 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_row_kernel(
         dc[nt] = mfma_f32(Bs[(16 * st + 4 * q + j) * NP + 16 * nt + r16], sW[st][j], dc[nt]);
   const size_t row = (r0 + l) * H + h;
   if (l < Lc) {
+    if (CPLX && dCo) {
+      // each head its own group: dC = e^{-i theta} (dC_eff[n] - i dC_eff[N+n]) straight out
+      const float2 r = rot[row];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      *reinterpret_cast<f32x4*>(dCh + row * NE + 16 * nt + 4 * q) = dc[nt];
+      for (int nt = 0; nt < NT / 2; ++nt) {
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float yr = dc[nt][i], yi = -dc[nt + NT / 2][i];
+          o[2 * i] = yr * r.x + yi * r.y;
+          o[2 * i + 1] = yi * r.x - yr * r.y;
+        }
+        float* dst = dCo + (row * (NE / 2) + 16 * nt + 4 * q) * 2;
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<f32x4*>(dCh + row * NE + 16 * nt + 4 * q) = dc[nt];
+    }
   }
   float rc = 0.0f;
   if constexpr (CPLX) {
@@ -441,65 +483,81 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_const_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Complex: rotation of the inputs into the sequence frame, per (batch, head):
-// u_t (fp64 scan of delta over the sequence, 256 tokens per pass), theta_t =
-// beta u_t mod 2 pi; B_eff, C_eff (Bsz, T, H, 2N); the decay alpha of each
-// head; h0 as [Re | Im] rows; dh_final rotated by -theta at the last token.
+// Complex: rotation of the inputs into the sequence frame.  u_t = delta_1 + ..
+// + delta_t over the sequence (fp64) in two steps: each chunk's local sums and
+// total (ssd_cplx_u_local), then each chunk adds the totals of the chunks
+// before it (ssd_cplx_rotate, one workgroup per (chunk, head, batch)), forms
+// theta_t = beta u_t mod 2 pi, keeps (cos, sin) theta_t per token and head,
+// and writes B_eff, C_eff (Bsz, T, H, 2N); the last chunk's workgroup turns
+// h0 into [Re | Im] rows and dh_final, rotated by -theta at the last token,
+// likewise; the decay alpha of each head.
 // ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kQ) void ssd_cplx_u_local_kernel(
+    const float* __restrict__ dt, const float* __restrict__ dt_bias, float dt_min, float dt_max,
+    double* __restrict__ uo, double* __restrict__ ctot, int T, int H, int nc) {
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int t = c * kQ + lane;
+  const size_t row = (static_cast<size_t>(b) * T + (t < T ? t : 0)) * H + h;
+  const double d = t < T ? static_cast<double>(step_size(dt[row], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max))
+                         : 0.0;
+  const double s = wave_inclusive_sum_d(d);
+  if (t < T) uo[row] = s;
+  if (lane == kQ - 1) ctot[(static_cast<size_t>(b) * H + h) * nc + c] = s;
+}
+
 __global__ __launch_bounds__(kThreads) void ssd_cplx_rotate_kernel(
-    const float* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
-    float dt_min, float dt_max, const float* __restrict__ Bm, const float* __restrict__ Cm,
+    const float* __restrict__ A, const float* __restrict__ Bm, const float* __restrict__ Cm,
     const float* __restrict__ h0, const float* __restrict__ dh_final, double* __restrict__ uo,
-    float* __restrict__ Beff, float* __restrict__ Ceff, float* __restrict__ alpha,
-    float* __restrict__ h0e, float* __restrict__ dhfe, int T, int H, int G, int P, int N) {
-  __shared__ double wsum[4];
-  __shared__ double carry_s;
-  __shared__ float cth[kThreads], sth[kThreads];
-  const int h = blockIdx.x, b = blockIdx.y;
+    const double* __restrict__ ctot, float2* __restrict__ rot, float* __restrict__ Beff,
+    float* __restrict__ Ceff, float* __restrict__ alpha, float* __restrict__ h0e,
+    float* __restrict__ dhfe, int T, int H, int G, int P, int N, int nc) {
+  __shared__ float cth[kQ], sth[kQ];
+  __shared__ double u_last;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (H / G);
   const int tid = threadIdx.x;
+  const int t0 = c * kQ, Lc = max(0, min(kQ, T - t0));
   const float be = A[2 * h + 1];
-  const float bias = dt_bias ? dt_bias[h] : 0.0f;
-  if (tid == 0) {
-    carry_s = 0.0;
-    if (b == 0) alpha[h] = A[2 * h];
-  }
-  __syncthreads();
-  const int NE = 2 * N;
-  for (int t0 = 0; t0 < T; t0 += kThreads) {
-    const int t = t0 + tid;
-    const size_t row = static_cast<size_t>(b) * T + (t < T ? t : 0);
-    const float d = t < T ? step_size(dt[row * H + h], bias, dt_min, dt_max) : 0.0f;
-    const double carry = carry_s;
-    const double u = carry + block_inclusive_scan(static_cast<double>(d), wsum);
-    if (t < T) uo[row * H + h] = u;
-    float cs, sn;
-    rot_cs(static_cast<double>(be) * u, cs, sn);
+  const size_t bh = static_cast<size_t>(b) * H + h;
+  if (tid == 0 && b == 0 && c == 0) alpha[h] = A[2 * h];
+  if (tid < kQ) {
+    double pre = 0.0;  // totals of the earlier chunks
+    for (int cc = tid; cc < c; cc += kQ) pre += ctot[bh * nc + cc];
+    pre = __shfl(wave_inclusive_sum_d(pre), kQ - 1);
+    const size_t row = (static_cast<size_t>(b) * T + t0 + (tid < Lc ? tid : 0)) * H + h;
+    const double u = tid < Lc ? uo[row] + pre : pre;
+    float cs = 1.0f, sn = 0.0f;
+    if (tid < Lc) {
+      uo[row] = u;
+      rot_cs(static_cast<double>(be) * u, cs, sn);
+      rot[row] = make_float2(cs, sn);
+    }
     cth[tid] = cs;
     sth[tid] = sn;
-    __syncthreads();
-    if (tid == kThreads - 1) carry_s = u;
-    // rotated features of the pass's tokens: B' = B e^{-i theta}, C' = C e^{i theta}
-    const int nt = min(kThreads, T - t0);
-    for (int i = tid; i < nt * N; i += kThreads) {
-      const int tl = i / N, n = i % N;
-      const size_t rr = static_cast<size_t>(b) * T + t0 + tl;
-      const float2 bv = *reinterpret_cast<const float2*>(Bm + ((rr * G + g) * N + n) * 2);
-      const float2 cv = *reinterpret_cast<const float2*>(Cm + ((rr * G + g) * N + n) * 2);
-      const float co = cth[tl], si = sth[tl];
-      float* be_row = Beff + (rr * H + h) * NE;
-      float* ce_row = Ceff + (rr * H + h) * NE;
-      be_row[n] = bv.x * co + bv.y * si;       // Re(B e^{-i theta})
-      be_row[N + n] = bv.y * co - bv.x * si;   // Im
-      ce_row[n] = cv.x * co - cv.y * si;       // Re(C e^{i theta})
-      ce_row[N + n] = -(cv.y * co + cv.x * si);  // -Im
-    }
-    __syncthreads();
+    if (tid == (Lc > 0 ? Lc - 1 : 0)) u_last = Lc > 0 ? u : 0.0;
   }
+  __syncthreads();
+  // rotated features, two n per thread: B' = B e^{-i theta}, C' = C e^{i theta}
+  const int NE = 2 * N, half = N / 2;
+  for (int i = tid; i < Lc * half; i += kThreads) {
+    const int tl = i / half, n = 2 * (i % half);
+    const size_t rr = static_cast<size_t>(b) * T + t0 + tl;
+    const float4 bv = *reinterpret_cast<const float4*>(Bm + ((rr * G + g) * N + n) * 2);
+    const float4 cv = *reinterpret_cast<const float4*>(Cm + ((rr * G + g) * N + n) * 2);
+    const float co = cth[tl], si = sth[tl];
+    float* be_row = Beff + (rr * H + h) * NE;
+    float* ce_row = Ceff + (rr * H + h) * NE;
+    *reinterpret_cast<float2*>(be_row + n) = make_float2(bv.x * co + bv.y * si, bv.z * co + bv.w * si);
+    *reinterpret_cast<float2*>(be_row + N + n) = make_float2(bv.y * co - bv.x * si, bv.w * co - bv.z * si);
+    *reinterpret_cast<float2*>(ce_row + n) = make_float2(cv.x * co - cv.y * si, cv.z * co - cv.w * si);
+    *reinterpret_cast<float2*>(ce_row + N + n) =
+        make_float2(-(cv.y * co + cv.x * si), -(cv.w * co + cv.z * si));
+  }
+  if (c != gridDim.x - 1) return;
   // h0 -> [Re | Im] rows; dh_final -> e^{-i theta_{T-1}} dh_final as [Re | Im]
   float cl = 1.0f, sl = 0.0f;
-  if (T > 0) rot_cs(static_cast<double>(be) * carry_s, cl, sl);
-  const size_t bh = static_cast<size_t>(b) * H + h;
+  if (T > 0) rot_cs(static_cast<double>(be) * u_last, cl, sl);
   for (int i = tid; i < P * N; i += kThreads) {
     const int p = i / N, n = i % N;
     const size_t src = (bh * P * N + i) * 2;
@@ -623,18 +681,34 @@ __global__ __launch_bounds__(kQ) void ssd_f32_dt_kernel(
   }
 }
 
-// per head: dA (complex: (d alpha, d beta)), ddt_bias, dD from the chunk shares
+// per head (one workgroup each): dA (complex: (d alpha, d beta)), ddt_bias, dD
+// from the chunk shares of every sequence (fp64)
 template <bool CPLX>
 __global__ __launch_bounds__(kThreads) void ssd_f32_dt_sum_kernel(
     const double* __restrict__ part, float* __restrict__ dA, float* __restrict__ ddt_bias,
     float* __restrict__ dD, int Bsz, int H, int nc) {
-  const int h = blockIdx.x * kThreads + threadIdx.x;
-  if (h >= H) return;
+  __shared__ double ws4[4][4];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int b = 0; b < Bsz; ++b)
-    for (int c = 0; c < nc; ++c)
+  for (int i = tid; i < Bsz * nc; i += kThreads) {
+    const int b = i / nc, c = i % nc;
+    const double2* pp = reinterpret_cast<const double2*>(part + ((static_cast<size_t>(b) * H + h) * nc + c) * 4);
+    const double2 lo = pp[0], hi = pp[1];
+    s[0] += lo.x;
+    s[1] += lo.y;
+    s[2] += hi.x;
+    s[3] += hi.y;
+  }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s[k] += part[((static_cast<size_t>(b) * H + h) * nc + c) * 4 + k];
+  for (int k = 0; k < 4; ++k) {
+    s[k] = wave_inclusive_sum_d(s[k]);
+    if (lane == kWave - 1) ws4[wid][k] = s[k];
+  }
+  __syncthreads();
+  if (tid != 0) return;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s[k] = (ws4[0][k] + ws4[1][k]) + (ws4[2][k] + ws4[3][k]);
   if constexpr (CPLX) {
     dA[2 * h] = static_cast<float>(s[0]);
     dA[2 * h + 1] = static_cast<float>(s[3]);
@@ -650,9 +724,8 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_dt_sum_kernel(
 // (re, im) pairs).  One thread per (b, t, g, n) (real: 4 n).
 template <bool CPLX>
 __global__ __launch_bounds__(kThreads) void ssd_f32_group_sum_kernel(
-    const float* __restrict__ dBh, const float* __restrict__ dCh, const double* __restrict__ u,
-    const float* __restrict__ A, float* __restrict__ dB, float* __restrict__ dC, size_t rows, int H,
-    int G, int N) {
+    const float* __restrict__ dBh, const float* __restrict__ dCh, const float2* __restrict__ rot,
+    float* __restrict__ dB, float* __restrict__ dC, size_t rows, int H, int G, int N) {
   const int hpg = H / G;
   const int NE = CPLX ? 2 * N : N;
   const int per = CPLX ? N : N / 4;  // threads per (b, t, g) row
@@ -665,8 +738,8 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_group_sum_kernel(
     for (int e = 0; e < hpg; ++e) {
       const int h = g * hpg + e;
       const size_t hr = (bt * H + h) * NE;
-      float co, si;
-      rot_cs(static_cast<double>(A[2 * h + 1]) * u[bt * H + h], co, si);
+      const float2 r = rot[bt * H + h];
+      const float co = r.x, si = r.y;
       // dB = e^{i theta} (dB_eff[n] + i dB_eff[N+n]); dC = e^{-i theta} (dC_eff[n] - i dC_eff[N+n])
       const float xr = dBh[hr + k], xi = dBh[hr + N + k];
       br += xr * co - xi * si;
@@ -715,7 +788,8 @@ __global__ __launch_bounds__(kThreads) void ssd_cplx_dh0_kernel(const float* __r
 // dh_final and h_final, rho chunk totals.
 // ---------------------------------------------------------------------------
 struct F32BwdLayout {
-  size_t S, dec, adj, dBh, dCh, tokv, cst, part, u, Beff, Ceff, alpha, h0e, dhfe, hfe, rtot, dh0e, total;
+  size_t S, dec, adj, dBh, dCh, tokv, cst, part, u, rot, ctot, Beff, Ceff, alpha, h0e, dhfe, hfe, rtot, dh0e,
+      total;
 };
 static F32BwdLayout f32_layout(int Bsz, int T, int H, int P, int N, bool cplx) {
   const int NE = cplx ? 2 * N : N;
@@ -736,6 +810,8 @@ static F32BwdLayout f32_layout(int Bsz, int T, int H, int P, int N, bool cplx) {
   if (cplx) {
     const size_t hs = static_cast<size_t>(Bsz) * H * P * NE * 4;
     L.u = o;     o += up(tok * 8);
+    L.rot = o;   o += up(tok * 8);
+    L.ctot = o;  o += up(static_cast<size_t>(Bsz) * H * nc * 8);
     L.Beff = o;  o += up(tok * NE * 4);
     L.Ceff = o;  o += up(tok * NE * 4);
     L.alpha = o; o += up(static_cast<size_t>(H) * 4);
@@ -762,7 +838,8 @@ template <int P, int NE, bool CPLX>
 hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, const float* A_dt,
                            const float* dt_bias, float dt_min, float dt_max, const float* Beff,
                            const float* Ceff, int Geff, const float* dy, const float* D,
-                           float* dx, float* ddt, float* dA, float* dD, float* ddt_bias, char* ws,
+                           float* dx, float* ddt, float* dA, float* dD, float* ddt_bias, float* dBh,
+                           float* dCh, const float2* rot, float* dBo, float* dCo, char* ws,
                            const F32BwdLayout& L, int Bsz, int T, int H, hipStream_t st,
                            const hipEvent_t* ev) {
   auto E = [&](int k) { return ev ? ev + 2 * k : nullptr; };
@@ -774,18 +851,17 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
   const float* S = reinterpret_cast<const float*>(ws + L.S);
   const float* dec = reinterpret_cast<const float*>(ws + L.dec);
   const float* adj = reinterpret_cast<const float*>(ws + L.adj);
-  float* dBh = reinterpret_cast<float*>(ws + L.dBh);
-  float* dCh = reinterpret_cast<float*>(ws + L.dCh);
   double* cst = reinterpret_cast<double*>(ws + L.cst);
   double* part = reinterpret_cast<double*>(ws + L.part);
   const dim3 grid(nc > 0 ? nc : 1, H, Bsz);
   constexpr bool SCALE = !CPLX;
   const bool run = nc > 0;
   launch_k(run, ssd_f32_col_kernel<P, NE, SCALE, CPLX>, grid, dim3(kThreads), st, E(5), x, dt, A_dec,
-           dt_bias, dt_min, dt_max, Beff, Ceff, dy, D, adj, dx, dBh, f2, col, xv, dyx, rhoB, T, H, Geff,
-           nc);
+           dt_bias, dt_min, dt_max, Beff, Ceff, dy, D, adj, dx, dBh, f2, col, xv, dyx, rhoB, rot, dBo, T, H,
+           Geff, nc);
   launch_k(run, ssd_f32_row_kernel<P, NE, SCALE, CPLX>, grid, dim3(kThreads), st, E(6), x, dt, A_dec,
-           dt_bias, dt_min, dt_max, Beff, Ceff, dy, S, dCh, f1, rw, rhoC, T, H, Geff, nc);
+           dt_bias, dt_min, dt_max, Beff, Ceff, dy, S, dCh, f1, rw, rhoC, rot, dCo, T, H, Geff,
+           nc);
   launch_k(run, ssd_f32_const_kernel, grid, dim3(kThreads), st, E(7), adj, S, dec, cst, H, P * NE, nc);
   launch_k(CPLX, ssd_cplx_tau_kernel, dim3(H, Bsz), dim3(kThreads), st, E(8),
            reinterpret_cast<const float*>(ws + L.dhfe), reinterpret_cast<const float*>(ws + L.hfe), rhoB,
@@ -798,8 +874,7 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
            static_cast<const double*>(cst), static_cast<const float*>(rhoB), static_cast<const float*>(rhoC),
            CPLX ? reinterpret_cast<const double*>(ws + L.rtot) : nullptr,
            CPLX ? reinterpret_cast<const double*>(ws + L.u) : nullptr, ddt, part, T, H, nc);
-  launch_k(true, ssd_f32_dt_sum_kernel<CPLX>, dim3((H + kThreads - 1) / kThreads), dim3(kThreads), st,
-           E(11), static_cast<const double*>(part), dA, ddt_bias, dD, Bsz, H, nc);
+  launch_k(true, ssd_f32_dt_sum_kernel<CPLX>, dim3(H), dim3(kThreads), st, E(11), static_cast<const double*>(part), dA, ddt_bias, dD, Bsz, H, nc);
   return hipGetLastError();
 }
 
@@ -830,18 +905,21 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
   launch_k(true, ssd_f32_adj_pass_kernel, dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
            dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), a.dh_final, a.dh0, a.H,
            P * N, nc);
+  // each head its own group: the per-head gradients are the outputs
+  const bool direct = a.G == a.H;
+  float* dBh = direct ? a.dB : reinterpret_cast<float*>(ws + L.dBh);
+  float* dCh = direct ? a.dC : reinterpret_cast<float*>(ws + L.dCh);
   e = launch_f32_core<P, N, false>(x, a.dt, a.A, a.A, a.dt_bias, a.dt_min, a.dt_max, B, C, a.G, dy, a.D,
-                                   static_cast<float*>(a.dx), a.ddt, a.dA, a.dD, a.ddt_bias, ws, L, a.Bsz,
-                                   a.T, a.H, st, ev);
+                                   static_cast<float*>(a.dx), a.ddt, a.dA, a.dD, a.ddt_bias, dBh, dCh,
+                                   nullptr, nullptr, nullptr, ws, L, a.Bsz, a.T, a.H, st, ev);
   if (e != hipSuccess) return e;
   const size_t rows = static_cast<size_t>(a.Bsz) * a.T;
-  const size_t nthreads = rows * a.G * (N / 4);
+  const size_t nthreads = direct ? 0 : rows * a.G * (N / 4);
   launch_k(false, ssd_cplx_dh0_kernel, dim3(1), dim3(kThreads), st, E(13), nullptr, nullptr, size_t{0}, 0);
   launch_k(nthreads > 0, ssd_f32_group_sum_kernel<false>,
            dim3(static_cast<unsigned>((nthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, E(12),
            reinterpret_cast<const float*>(ws + L.dBh), reinterpret_cast<const float*>(ws + L.dCh),
-           static_cast<const double*>(nullptr), static_cast<const float*>(nullptr), a.dB, a.dC, rows,
-           a.H, a.G, N);
+           static_cast<const float2*>(nullptr), a.dB, a.dC, rows, a.H, a.G, N);
   return hipGetLastError();
 }
 
@@ -874,9 +952,29 @@ static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   float* dhfe = reinterpret_cast<float*>(ws + L.dhfe);
   float* hfe = reinterpret_cast<float*>(ws + L.hfe);
   float* dh0e = reinterpret_cast<float*>(ws + L.dh0e);
-  launch_k(true, ssd_cplx_rotate_kernel, dim3(a.H, a.Bsz), dim3(kThreads), st, E(0), a.dt, a.A,
-           a.dt_bias, a.dt_min, a.dt_max, a.B, a.C, a.h0, a.dh_final, u, Beff, Ceff, alpha, h0e, dhfe, a.T,
-           a.H, a.G, P, N);
+  float2* rot = reinterpret_cast<float2*>(ws + L.rot);
+  double* ctot = reinterpret_cast<double*>(ws + L.ctot);
+  // rotation: the pair of event slot 0 spans both kernels
+  const hipEvent_t* e0 = E(0);
+  if (nc > 0) {
+    if (e0)
+      hipExtLaunchKernelGGL(ssd_cplx_u_local_kernel, dim3(nc, a.H, a.Bsz), dim3(kQ), 0, st, e0[0], nullptr, 0,
+                            a.dt, a.dt_bias, a.dt_min, a.dt_max, u, ctot, a.T, a.H, nc);
+    else
+      hipLaunchKernelGGL(ssd_cplx_u_local_kernel, dim3(nc, a.H, a.Bsz), dim3(kQ), 0, st, a.dt, a.dt_bias,
+                         a.dt_min, a.dt_max, u, ctot, a.T, a.H, nc);
+  } else if (e0) {
+    (void)hipEventRecord(e0[0], st);
+  }
+  const dim3 rgrid(nc > 0 ? nc : 1, a.H, a.Bsz);
+  if (e0)
+    hipExtLaunchKernelGGL(ssd_cplx_rotate_kernel, rgrid, dim3(kThreads), 0, st, nullptr, e0[1], 0, a.A, a.B,
+                          a.C, a.h0, a.dh_final, u, static_cast<const double*>(ctot), rot, Beff, Ceff, alpha,
+                          h0e, dhfe, a.T, a.H, a.G, P, N, nc);
+  else
+    hipLaunchKernelGGL(ssd_cplx_rotate_kernel, rgrid, dim3(kThreads), 0, st, a.A, a.B, a.C, a.h0,
+                       a.dh_final, u, static_cast<const double*>(ctot), rot, Beff, Ceff, alpha, h0e, dhfe,
+                       a.T, a.H, a.G, P, N, nc);
   // the rotated-frame real problem: per-head features (G = H), decay alpha, input scale 1
   hipError_t e = run_states_f32(a.x, a.dt, alpha, Beff, a.dt_bias, a.dt_min, a.dt_max, S, dec, a.Bsz, a.T,
                                 a.H, P, a.H, NE, kQ, 1, st, E(1));
@@ -888,16 +986,20 @@ static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   launch_k(true, ssd_f32_adj_pass_kernel, dim3((P * NE / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
            dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), static_cast<const float*>(dhfe),
            dh0e, a.H, P * NE, nc);
+  // each head its own group: dB, dC rotated back and written by the block kernels
+  const bool direct = a.G == a.H;
   e = launch_f32_core<P, NE, true>(a.x, a.dt, alpha, a.A, a.dt_bias, a.dt_min, a.dt_max, Beff, Ceff, a.H,
-                                   a.dy, nullptr, a.dx, a.ddt, a.dA, nullptr, a.ddt_bias, ws, L, a.Bsz, a.T,
+                                   a.dy, nullptr, a.dx, a.ddt, a.dA, nullptr, a.ddt_bias,
+                                   reinterpret_cast<float*>(ws + L.dBh), reinterpret_cast<float*>(ws + L.dCh),
+                                   rot, direct ? a.dB : nullptr, direct ? a.dC : nullptr, ws, L, a.Bsz, a.T,
                                    a.H, st, ev);
   if (e != hipSuccess) return e;
   const size_t rows = static_cast<size_t>(a.Bsz) * a.T;
-  const size_t nthreads = rows * a.G * N;
+  const size_t nthreads = direct ? 0 : rows * a.G * N;
   launch_k(nthreads > 0, ssd_f32_group_sum_kernel<true>,
            dim3(static_cast<unsigned>((nthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, E(12),
            reinterpret_cast<const float*>(ws + L.dBh), reinterpret_cast<const float*>(ws + L.dCh),
-           static_cast<const double*>(u), a.A, a.dB, a.dC, rows, a.H, a.G, N);
+           static_cast<const float2*>(rot), a.dB, a.dC, rows, a.H, a.G, N);
   const size_t total = static_cast<size_t>(a.Bsz) * a.H * P * N;
   launch_k(a.dh0 != nullptr, ssd_cplx_dh0_kernel,
            dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)), dim3(kThreads), st, E(13),
