@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--workload", default="bitmamba_bf16",
                     choices=["bitmamba_bf16", "long_bf16", "mamba3lite_complex", "tiny_f32",
                              "decode_f32", "decode_complex", "conv_bf16", "conv_decode_f32",
-                             "bwd_bf16", "bwd_complex", "mamba3lite_packed", "mimo_bf16"])
+                             "bwd_bf16", "bwd_complex", "mamba3lite_packed", "mimo_bf16",
+                             "varlen_bf16"])
     ap.add_argument("--no-flush", action="store_true",
                     help="keep the Infinity Cache warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -107,6 +108,7 @@ KERNEL_SOURCES = {
     "mamba3lite_packed": ["ssd_chunk_cplx.hip"],
     "mimo_bf16": ["ssd_linear.hip"],
     "bwd_complex": ["ssd_bwd_f32.hip", "ssd_chunk.hip"],
+    "varlen_bf16": ["ssd_chunk_bf16.hip"],
 }
 
 
@@ -367,6 +369,8 @@ def main():
         return bench_bwd_complex(args, cfg)
     if cfg["kind"] == "mimo":
         return bench_mimo(args, cfg)
+    if cfg["kind"] == "varlen":
+        return bench_varlen(args, cfg)
     inp = inputs.make_workload(args.workload, seed=0)
     Q = cfg["chunk"]
     dims = dict(inp["dims"], Q=Q)
@@ -532,6 +536,124 @@ def main():
         copy_counter_reference(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, dims, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_varlen(args, cfg):
+    """Variable-length prefill: one step = one ssd_chunk_fwd_varlen call over
+    the packed batch (its three kernels, the segment-table copy included).
+    Roofline over the batch's algorithmic bytes (x, dt, B, C read once, y
+    written once for its Ttot tokens) as for the uniform forward."""
+    import torch
+    import selective_state_space_09_amd as ssd
+    from selective_state_space_09_amd import inputs
+    inp = inputs.make_workload(args.workload, seed=0, with_h0=True)
+    d0 = inp["dims"]
+    Q = cfg["chunk"]
+    Ttot, H, P, G, N = (d0[k] for k in ("Ttot", "H", "P", "G", "N"))
+    dims = dict(Bsz=1, T=Ttot, H=H, P=P, G=G, N=N, Q=Q)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    d = {k: (up(v) if isinstance(v, np.ndarray) and k != "cu_seqlens" else v) for k, v in inp.items()}
+    cu = np.ascontiguousarray(inp["cu_seqlens"], np.int32)
+    nseq = cu.size - 1
+    y = torch.empty((Ttot, H, P), dtype=torch.bfloat16, device=dev)
+    hf = torch.empty((nseq, H, P, N), dtype=torch.float32, device=dev)
+    L = ssd.lib()
+    cup = cu.ctypes.data_as(ctypes.c_void_p)
+    nbytes = int(L.ssd_varlen_workspace_size(cup, nseq, H, P, G, N, Q))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P_ = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    fixed = (P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["D"]), P_(d["dt_bias"]),
+             float(d["dt_min"]), float(d["dt_max"]), P_(d["h0"]), P_(y), P_(hf), cup, nseq, H, P, G, N, Q,
+             ssd.SSD_BF16, P_(ws), ws.numel(), sp)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(L.ssd_last_error().decode())
+
+    n_total = args.warmup + args.steps
+    n_kern = max(10, args.steps // 2)
+    step_evs = [(hip.event(), hip.event()) for _ in range(n_total)]
+    evs = [[hip.event() for _ in range(6)] for _ in range(n_kern)]
+    ev_arrays = [(ctypes.c_void_p * 6)(*[e.value for e in row]) for row in evs]
+    for i in range(n_total):
+        if flush is not None:
+            flush.max()
+        a, b = step_evs[i]
+        hip.lib.hipEventRecord(a, sp)
+        check(L.ssd_chunk_fwd_varlen(*fixed))
+        hip.lib.hipEventRecord(b, sp)
+    torch.cuda.synchronize()
+    per_step = [hip.elapsed_ms(*step_evs[i]) for i in range(args.warmup, n_total)]
+    for i in range(n_kern):
+        if flush is not None:
+            flush.max()
+        check(L.ssd_chunk_fwd_varlen_ev(*fixed, ev_arrays[i]))
+    torch.cuda.synchronize()
+    vcfg = dict(kind="real", dtype="bf16")
+    segs = kernel_segments(vcfg)
+    kern = {}
+    for n, (k0, k1) in segs.items():
+        avg = float(np.mean([hip.elapsed_ms(evs[i][k0], evs[i][k1]) for i in range(n_kern)]))
+        kern[n] = {"avg_us": avg * 1e3}
+    ms = float(np.mean(per_step))
+    alg = algorithmic_bytes(vcfg, dims)
+    dom = max(kern, key=lambda n: kern[n]["avg_us"])
+    dom_s = kern[dom]["avg_us"] / 1e6
+    achieved = alg / dom_s / 1e9
+    copy_gbs, copy_bytes = copy_reference(torch, dev, alg, flush)
+    e2e = alg / (ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC, "value": Ttot / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(per_step)), "ms_per_step_min": float(np.min(per_step)),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "sequences": [int(v) for v in np.diff(cu)], "tokens": Ttot,
+                   "heads": H, "headdim": P, "d_state": N, "ngroups": G, "chunk": Q,
+                   "cache": "cold (Infinity Cache flushed between steps)" if flush is not None else "warm"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload, dom),
+                     "kernel": dom, "alg_bytes": alg, "launch_us": dom_s * 1e6,
+                     "frac_of_copy": achieved / copy_gbs},
+        "end_to_end": {"alg_bytes": alg, "gbs": e2e, "frac": e2e / HBM_PEAK_GBS},
+        "achievable_hbm": {"kernel": "device copy (torch copy_)", "bytes_moved": copy_bytes,
+                           "gbs": copy_gbs, "frac_of_peak": copy_gbs / HBM_PEAK_GBS},
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.set_threads(len(os.sched_getaffinity(0)))
+        # the oracle on the first k heads of every sequence, k doubled until a
+        # run takes half the target
+        nh, t_run = 1, 0.0
+        while True:
+            hs = list(range(nh))
+            sub = {k: inp[k] for k in ("B", "C", "cu_seqlens", "dt_min", "dt_max")}
+            t0 = time.perf_counter()
+            oracle.fwd_varlen(np.ascontiguousarray(inp["x"][:, hs]), np.ascontiguousarray(inp["dt"][:, hs]),
+                              inp["A"][hs], sub["B"], sub["C"], sub["cu_seqlens"], inp["D"][hs],
+                              inp["dt_bias"][hs], sub["dt_min"], sub["dt_max"],
+                              np.ascontiguousarray(inp["h0"][:, hs]))
+            t_run = time.perf_counter() - t0
+            if t_run >= args.cpu_seconds / 2 or nh >= H:
+                break
+            nh = min(H, 2 * nh)
+        out["cpu_baseline"] = {"value": Ttot * (nh / H) / t_run, "unit": "tokens/s",
+                               "cores": oracle.threads_used(), "kind": "oracle",
+                               "sample": f"every sequence, the first {nh} of {H} heads, float64"}
     print(json.dumps(out), flush=True)
 
 

@@ -176,6 +176,51 @@ int ssd_chunk_fwd_ev(const void *x, const float *dt, const float *A,
                      void *workspace, size_t workspace_bytes, void *stream,
                      void *const *events);
 
+/*
+ * Variable-length batch of the real chunked forward: nseq independent
+ * sequences of different lengths packed along the token axis, each one the
+ * recurrence above from its own h0 (the batched prefill of a Mamba-2 layer
+ * whose states then continue in ssd_step_decode).
+ *   cu_seqlens (nseq + 1)   int32, HOST memory (the one host array of this
+ *                           ABI): sequence b holds the token rows
+ *                           cu_seqlens[b] .. cu_seqlens[b+1]-1;
+ *                           cu_seqlens[0] = 0, non-decreasing, Ttot =
+ *                           cu_seqlens[nseq]; empty sequences are allowed
+ *                           (their h_final is their h0).  1 <= nseq <= 65535.
+ *   x, y     (Ttot, H, P)    bfloat16 (dtype must be SSD_BF16)
+ *   dt       (Ttot, H)       float32, raw step
+ *   B, C     (Ttot, G, N)    bfloat16
+ *   A, D, dt_bias (H)        as in ssd_chunk_fwd
+ *   h0, h_final (nseq, H, P, N) float32 or NULL
+ *   workspace of at least ssd_varlen_workspace_size(cu_seqlens, ...) bytes
+ * Chunks and segments never span two sequences: every sequence is cut into
+ * chunks from its own first token, so sequence b's outputs equal those of
+ * ssd_chunk_fwd on it alone (bit for bit when both calls pick the same
+ * segment length).  The library checks cu_seqlens, builds its segment table
+ * on the host and copies it into the workspace on `stream` (a small
+ * host-to-device copy from pageable memory; cu_seqlens may be reused once the
+ * call returns).  Invalid cu_seqlens: SSD_EINVAL before any HIP call.
+ * ssd_varlen_workspace_size returns 0 for arguments the call would reject.
+ */
+size_t ssd_varlen_workspace_size(const int *cu_seqlens, int nseq, int H, int P,
+                                 int G, int N, int chunk);
+int ssd_chunk_fwd_varlen(const void *x, const float *dt, const float *A,
+                         const void *B, const void *C, const float *D,
+                         const float *dt_bias, float dt_min, float dt_max,
+                         const float *h0, void *y, float *h_final,
+                         const int *cu_seqlens, int nseq, int H, int P, int G,
+                         int N, int chunk, int dtype, void *workspace,
+                         size_t workspace_bytes, void *stream);
+/* the same with the 6 measurement events of ssd_chunk_fwd_ev */
+int ssd_chunk_fwd_varlen_ev(const void *x, const float *dt, const float *A,
+                            const void *B, const void *C, const float *D,
+                            const float *dt_bias, float dt_min, float dt_max,
+                            const float *h0, void *y, float *h_final,
+                            const int *cu_seqlens, int nseq, int H, int P,
+                            int G, int N, int chunk, int dtype, void *workspace,
+                            size_t workspace_bytes, void *stream,
+                            void *const *events);
+
 int ssd_complex_chunk_fwd_ev(const float *x, const float *dt, const float *A,
                              const float *B, const float *C,
                              const float *dt_bias, float dt_min, float dt_max,

@@ -132,6 +132,28 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=float("inf"),
     return y, hf
 
 
+def fwd_varlen(x, dt, A, B, C, cu_seqlens, D=None, dt_bias=None, dt_min=0.0,
+               dt_max=float("inf"), h0=None):
+    """Variable-length batch of the real recurrence: sequence b holds rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 of x (Ttot,H,P), dt (Ttot,H) and B/C
+    (Ttot,G,N), and is one recurrence from its own h0[b] (h0 (nseq,H,P,N) or
+    None): ``fwd`` on that slice alone.  Returns (y (Ttot,H,P), h_final
+    (nseq,H,P,N)) as float64."""
+    cu = [int(v) for v in cu_seqlens]
+    nseq = len(cu) - 1
+    Ttot, H, P = x.shape
+    N = B.shape[2]
+    y = np.empty((Ttot, H, P), np.float64)
+    hf = np.empty((nseq, H, P, N), np.float64)
+    for b in range(nseq):
+        lo, hi = cu[b], cu[b + 1]
+        yb, hb = fwd(x[None, lo:hi], dt[None, lo:hi], A, B[None, lo:hi], C[None, lo:hi], D, dt_bias,
+                     dt_min, dt_max, None if h0 is None else h0[b:b + 1])
+        y[lo:hi] = yb[0]
+        hf[b] = hb[0]
+    return y, hf
+
+
 def complex_fwd(x, dt, A, B, C, dt_bias=None, dt_min=0.0, dt_max=float("inf"),
                 h0=None):
     """Complex recurrence.  x (Bsz,T,H,P) float32, dt (Bsz,T,H), A (H,2),

@@ -53,6 +53,13 @@ def lib():
                                         I, I, I, I, I, I, I, I, P]
     L.ssd_chunk_fwd_ev.restype = I
     L.ssd_chunk_fwd_ev.argtypes = L.ssd_chunk_fwd.argtypes + [P]
+    L.ssd_varlen_workspace_size.restype = S
+    L.ssd_varlen_workspace_size.argtypes = [P, I, I, I, I, I, I]
+    L.ssd_chunk_fwd_varlen.restype = I
+    L.ssd_chunk_fwd_varlen.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P,
+                                       P, I, I, I, I, I, I, I, P, S, P]
+    L.ssd_chunk_fwd_varlen_ev.restype = I
+    L.ssd_chunk_fwd_varlen_ev.argtypes = L.ssd_chunk_fwd_varlen.argtypes + [P]
     L.ssd_complex_chunk_fwd_ev.restype = I
     L.ssd_complex_chunk_fwd_ev.argtypes = L.ssd_complex_chunk_fwd.argtypes + [P]
     L.ssd_step_decode.restype = I
@@ -209,6 +216,82 @@ def ssd_chunk_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_min=0.0, dt_max=math.
                                _ptr(dt_bias), float(dt_min), float(dt_max), _ptr(h0),
                                _ptr(y), _ptr(h_final), Bsz, T, H, P, G, N, chunk, dtype,
                                _ptr(ws), ws.numel(), _stream(stream)))
+    return (y, h_final) if h_final is not None else y
+
+
+def _cu_host(cu_seqlens):
+    """cu_seqlens as a contiguous host int32 array (the library reads it on
+    the host)."""
+    import numpy as np
+    if isinstance(cu_seqlens, torch.Tensor):
+        if cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be host memory (a list, numpy array or CPU tensor)")
+        cu_seqlens = cu_seqlens.numpy()
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int32)
+    if cu.ndim != 1 or cu.size < 2:
+        raise ValueError(f"cu_seqlens must be 1-D with at least 2 entries, got shape {cu.shape}")
+    return cu
+
+
+def ssd_varlen_workspace_size(cu_seqlens, H, P, G, N, chunk):
+    cu = _cu_host(cu_seqlens)
+    return int(lib().ssd_varlen_workspace_size(cu.ctypes.data_as(ctypes.c_void_p), cu.size - 1,
+                                               H, P, G, N, chunk))
+
+
+def ssd_chunk_fwd_varlen(x, dt, A, B, C, cu_seqlens, D=None, dt_bias=None, dt_min=0.0,
+                         dt_max=math.inf, h0=None, chunk=256, y=None, h_final=None,
+                         return_final_state=False, workspace=None, stream=None, events=None):
+    """Variable-length batch of the real forward: x (Ttot,H,P) and B, C
+    (Ttot,G,N) bfloat16, dt (Ttot,H), sequence b on the rows cu_seqlens[b] ..
+    cu_seqlens[b+1]-1 (cu_seqlens a host array of nseq+1 ints), h0 and
+    h_final (nseq,H,P,N) float32.  Returns y (and h_final when asked or
+    given)."""
+    cu = _cu_host(cu_seqlens)
+    nseq = cu.size - 1
+    _ndim(x, "x", 3)
+    _ndim(B, "B", 3)
+    Ttot, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if int(cu[-1]) != Ttot:
+        raise ValueError(f"cu_seqlens[-1] = {int(cu[-1])} but x has {Ttot} token rows")
+    _expect(B, "B", (Ttot, G, N), x)
+    _expect(C, "C", (Ttot, G, N), x)
+    _expect(dt, "dt", (Ttot, H), x)
+    _expect(A, "A", (H,), x)
+    _expect(D, "D", (H,), x)
+    _expect(dt_bias, "dt_bias", (H,), x)
+    _expect(h0, "h0", (nseq, H, P, N), x)
+    _expect(y, "y", (Ttot, H, P), x)
+    _expect(h_final, "h_final", (nseq, H, P, N), x)
+    _dev(x, "x", torch.bfloat16)
+    _dev(B, "B", torch.bfloat16)
+    _dev(C, "C", torch.bfloat16)
+    _dev(dt, "dt", torch.float32)
+    _dev(A, "A", torch.float32)
+    _dev(D, "D", torch.float32)
+    _dev(dt_bias, "dt_bias", torch.float32)
+    _dev(h0, "h0", torch.float32)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", torch.bfloat16)
+    if h_final is None and return_final_state:
+        h_final = torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device)
+    _dev(h_final, "h_final", torch.float32)
+    cup = cu.ctypes.data_as(ctypes.c_void_p)
+    nbytes = int(lib().ssd_varlen_workspace_size(cup, nseq, H, P, G, N, chunk))
+    if nbytes == 0:
+        _check(lib().ssd_chunk_fwd_varlen(None, None, None, None, None, None, None, float(dt_min),
+                                          float(dt_max), None, None, None, cup, nseq, H, P, G, N,
+                                          chunk, SSD_BF16, None, 0, None))
+    ws = _workspace(nbytes, x.device, workspace)
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), float(dt_min),
+            float(dt_max), _ptr(h0), _ptr(y), _ptr(h_final), cup, nseq, H, P, G, N, chunk, SSD_BF16,
+            _ptr(ws), ws.numel(), _stream(stream))
+    if events is None:
+        _check(lib().ssd_chunk_fwd_varlen(*args))
+    else:
+        _check(lib().ssd_chunk_fwd_varlen_ev(*args, events))
     return (y, h_final) if h_final is not None else y
 
 

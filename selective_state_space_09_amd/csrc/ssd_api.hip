@@ -185,6 +185,52 @@ int ssd_chunk_fwd(const void* x, const float* dt, const float* A, const void* B,
                           H, P, G, N, chunk, dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
+// ---- variable-length batches (bf16 real forward) ----
+
+size_t ssd_varlen_workspace_size(const int* cu_seqlens, int nseq, int H, int P, int G, int N, int chunk) {
+  if (!cu_seqlens) return 0;
+  ssd::VarlenPlan p{};
+  const char* why = nullptr;
+  if (!ssd::varlen_plan(cu_seqlens, nseq, H, chunk, p, &why)) return 0;
+  if (check_chunk_shape(1, p.Ttot, H, P, G, N, chunk, 0) != SSD_OK) return 0;
+  return ssd::bf16_varlen_layout(p, H, P, N, chunk).total + 256;
+}
+
+int ssd_chunk_fwd_varlen_ev(const void* x, const float* dt, const float* A, const void* B,
+                            const void* C, const float* D, const float* dt_bias, float dt_min,
+                            float dt_max, const float* h0, void* y, float* h_final,
+                            const int* cu_seqlens, int nseq, int H, int P, int G, int N, int chunk,
+                            int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events) {
+  if (!cu_seqlens) return fail(SSD_EINVAL, "cu_seqlens is NULL");
+  ssd::VarlenPlan p{};
+  const char* why = nullptr;
+  if (!ssd::varlen_plan(cu_seqlens, nseq, H, chunk > 0 ? chunk : 1, p, &why))
+    return fail(SSD_EINVAL, "cu_seqlens: %s", why);
+  if (dtype != SSD_BF16)
+    return fail(SSD_EUNSUPPORTED, "variable-length batches take bfloat16 x, B, C, y (dtype=%d)", dtype);
+  SSD_TRY(check_real_fwd(x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final, 1, p.Ttot, H, P,
+                         G, N, chunk, dtype));
+  const size_t need = ssd::bf16_varlen_layout(p, H, P, N, chunk).total + 256;
+  SSD_TRY(check_ptr(workspace, "workspace", 256, true));
+  if (workspace_bytes < need)
+    return fail(SSD_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  ssd::ChunkArgs a{x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final,
+                   nseq, p.Ttot, H, P, G, N, chunk, dtype, workspace,
+                   reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_chunk_varlen_bf16(a, p, cu_seqlens, static_cast<hipStream_t>(stream)));
+}
+
+int ssd_chunk_fwd_varlen(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                         const float* D, const float* dt_bias, float dt_min, float dt_max,
+                         const float* h0, void* y, float* h_final, const int* cu_seqlens, int nseq,
+                         int H, int P, int G, int N, int chunk, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return ssd_chunk_fwd_varlen_ev(x, dt, A, B, C, D, dt_bias, dt_min, dt_max, h0, y, h_final,
+                                 cu_seqlens, nseq, H, P, G, N, chunk, dtype, workspace, workspace_bytes,
+                                 stream, nullptr);
+}
+
 }  // extern "C"
 
 // ---- the allocation-free forward ----

@@ -26,6 +26,8 @@
 
 #include <type_traits>
 
+#include <vector>
+
 #include "ssd_chunk_common.h"
 
 namespace ssd {
@@ -93,7 +95,8 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min,
     float dt_max, float* __restrict__ states, float* __restrict__ decay,
-    float2* __restrict__ tok, int T, int H, int G, int Q, int nc, int K, int nseg, int npairs) {
+    float2* __restrict__ tok, int T, int H, int G, int Q, int nc, int K, int nseg, int npairs,
+    VarLen vl) {
   constexpr int NTHR = 512, WW = 8;
   constexpr int HS = 64;                    // tokens per staged quarter
   constexpr int XPn = P + 16, BPn = N + 16;  // pitches (bf16 elements)
@@ -113,21 +116,26 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float wsc[HPW][256];
   __shared__ float wpart[HPW][WW];
 
-  int b, sg, hp;
-  if (!unit_of_block(H / HPW, nseg, npairs, b, sg, hp)) return;
-  const int h0 = hp * HPW;  // first head of the workgroup
+  SegView sv;
+  if (!seg_of_block(vl, H / HPW, T, nseg, npairs, sv)) return;
+  const int b = sv.b, sg = sv.sg;
+  const int h0 = sv.h * HPW;  // first head of the workgroup
   const int g = h0 / (H / G);
+  const int ncb = (sv.T + Q - 1) / Q;       // chunks of the sequence
   const int c0 = sg * K;                    // first chunk of the segment
-  const int nck = min(K, nc - c0);          // chunks of the segment
+  const int nck = min(K, ncb - c0);         // chunks of the segment
   const int ts = c0 * Q;                    // first token
-  const int Ls = min(nck * Q, T - ts);      // tokens of the segment
+  const int Ls = min(nck * Q, sv.T - ts);   // tokens of the segment
+  // token-table chunk of the segment's first chunk (variable lengths: K slots
+  // per global segment)
+  const size_t tokc0 = vl.cu ? static_cast<size_t>(sv.gs) * K : static_cast<size_t>(b) * nc + c0;
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wid = wave_id();
   const int ng = wid % NGW, pg = wid / NGW;
 
   // ---- loads: dt of the first chunk, then the first two quarters ----
-  const size_t r0 = static_cast<size_t>(b) * T + ts;
+  const size_t r0 = sv.row0 + ts;
   float dtv[HPW];
   auto load_dt = [&](int kc) {
     const int lc = min(Q, Ls - kc * Q);
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
       lam_seg[e] *= lam;
       // (A u_l, delta_l) of every token for the output kernel (padding: delta 0)
       if (tid < Q)
-        tok[((static_cast<size_t>(b) * nc + c0 + kc) * H + h) * Q + tid] = make_float2(a_re * u, dd[e]);
+        tok[((tokc0 + kc) * H + h) * Q + tid] = make_float2(a_re * u, dd[e]);
       if (kc > 0) {
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
   // n = 32 m + 8q .. +7 (else per tile n = nt*16 + 4q .. +3)
 #pragma unroll
   for (int e = 0; e < HPW; ++e) {
-    float* dst = states + ((static_cast<size_t>(b) * nseg + sg) * H + h0 + e) * (static_cast<size_t>(P) * N);
+    float* dst = states + (static_cast<size_t>(sv.gs) * H + h0 + e) * (static_cast<size_t>(P) * N);
 #pragma unroll
     for (int j = 0; j < PTW; ++j) {
       const int pt = pg * PTW + j;
@@ -317,7 +325,9 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
         }
       }
     }
-    if (tid == 0) decay[(static_cast<size_t>(b) * H + h0 + e) * nseg + sg] = lam_seg[e];
+    if (tid == 0)
+      decay[vl.cu ? static_cast<size_t>(sv.gs) * H + h0 + e : (static_cast<size_t>(b) * H + h0 + e) * nseg + sg] =
+          lam_seg[e];
   }
 }
 
@@ -335,17 +345,23 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
 template <bool KEEP32>
 __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
     float* __restrict__ S, uint16_t* __restrict__ hin, const float* __restrict__ decay,
-    const float* __restrict__ h0, float* __restrict__ h_final, int H, int PN, int nseg) {
+    const float* __restrict__ h0, float* __restrict__ h_final, int H, int PN, int nseg_all,
+    const int* __restrict__ segstart) {
   constexpr int PF = 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const int e8 = blockIdx.x * kThreads + threadIdx.x;  // group of 8 elements
   if (e8 * 8 >= PN) return;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t sstride = static_cast<size_t>(H) * PN;  // between segments of one (b, h)
-  const size_t off = static_cast<size_t>(b) * nseg * sstride + h * static_cast<size_t>(PN) + e8 * 8;
+  // the sequence's segments: nseg_all each, or (variable lengths) its range of
+  // global segments, whose decays are stored segment-major
+  const size_t gs0 = segstart ? static_cast<size_t>(segstart[b]) : static_cast<size_t>(b) * nseg_all;
+  const int nseg = segstart ? segstart[b + 1] - segstart[b] : nseg_all;
+  const size_t off = gs0 * sstride + h * static_cast<size_t>(PN) + e8 * 8;
   float* sp = S + off;
   uint16_t* hp = hin + off;
-  const float* dc = decay + bh * nseg;
+  const float* dc = segstart ? decay + gs0 * H + h : decay + bh * nseg;
+  const int dstr = segstart ? H : 1;
   float hv[8];
   if (h0) {
     const float4 a = *reinterpret_cast<const float4*>(h0 + bh * PN + e8 * 8);
@@ -364,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
     if (j < nseg) {
       cur[j][0] = *reinterpret_cast<const float4*>(sp + j * sstride);
       cur[j][1] = *reinterpret_cast<const float4*>(sp + j * sstride + 4);
-      cd[j] = dc[j];
+      cd[j] = dc[j * dstr];
     }
   for (int s0 = 0; s0 < nseg; s0 += PF) {
     float4 nxt[PF][2];
@@ -375,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_bf16_kernel(
       if (sn < nseg) {
         nxt[j][0] = *reinterpret_cast<const float4*>(sp + sn * sstride);
         nxt[j][1] = *reinterpret_cast<const float4*>(sp + sn * sstride + 4);
-        nd[j] = dc[sn];
+        nd[j] = dc[sn * dstr];
       }
     }
 #pragma unroll
@@ -475,7 +491,7 @@ template <int P, int N, bool MULTI>
 __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const float* __restrict__ D, const float2* __restrict__ tok, const uint16_t* __restrict__ hin,
-    uint16_t* __restrict__ y, int T, int H, int G, int Q, int nc, int K, int nseg, int npairs) {
+    uint16_t* __restrict__ y, int T, int H, int G, int Q, int nc, int K, int nseg, int npairs, VarLen vl) {
   constexpr int QSM = 64;               // sub-chunk length (Q >= 64); a shorter chunk is one
   constexpr int KCP = N < 32 ? 32 : N;  // K of G^T padded to whole 32-wide MFMA steps (zeros)
   // row pitches (bf16): the B tile is read by rows (16 bytes a lane) and by the
@@ -518,13 +534,15 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
   __shared__ int sexact[256 / QSM];
   __shared__ float stau_last;
 
-  int b, sg, h;
-  if (!unit_of_block(H, nseg, npairs, b, sg, h)) return;
+  SegView sv;
+  if (!seg_of_block(vl, H, T, nseg, npairs, sv)) return;
+  const int b = sv.b, sg = sv.sg, h = sv.h;
   const int g = h / (H / G);
   const int c0 = sg * K;
-  const int nck = min(K, nc - c0);
+  const int nck = min(K, (sv.T + Q - 1) / Q - c0);
   const int ts = c0 * Q;
-  const int Ls = min(nck * Q, T - ts);
+  const int Ls = min(nck * Q, sv.T - ts);
+  const size_t tokc0 = vl.cu ? static_cast<size_t>(sv.gs) * K : static_cast<size_t>(b) * nc + c0;
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wid = wave_id();  // wave-uniform (SGPR): tile branches stay scalar
@@ -539,21 +557,21 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
   const float Dh = D ? D[h] : 0.0f;
 
   // ---- buffer descriptors of this segment's slices (rows >= Ls read as zero) ----
-  const size_t xy0 = (static_cast<size_t>(b) * T + ts) * H * P + static_cast<size_t>(h) * P;
+  const size_t xy0 = (sv.row0 + ts) * H * P + static_cast<size_t>(h) * P;
   const uint32_t xrow = static_cast<uint32_t>(H) * P * 2;
   const uint32_t xbytes = Ls > 0 ? static_cast<uint32_t>(Ls - 1) * xrow + P * 2 : 0;
   const buf_t xbuf = make_buf(x + xy0, xbytes);
   const buf_t ybuf = make_buf(y + xy0, xbytes);
-  const size_t bc0 = (static_cast<size_t>(b) * T + ts) * G * N + static_cast<size_t>(g) * N;
+  const size_t bc0 = (sv.row0 + ts) * G * N + static_cast<size_t>(g) * N;
   const uint32_t brow = static_cast<uint32_t>(G) * N * 2;
   const uint32_t bbytes = Ls > 0 ? static_cast<uint32_t>(Ls - 1) * brow + N * 2 : 0;
   const buf_t bbuf = make_buf(Bm + bc0, bbytes);
   const buf_t cbuf = make_buf(Cm + bc0, bbytes);
-  const buf_t hbuf = make_buf(hin + ((static_cast<size_t>(b) * nseg + sg) * H + h) * (static_cast<size_t>(P) * N),
+  const buf_t hbuf = make_buf(hin + (static_cast<size_t>(sv.gs) * H + h) * (static_cast<size_t>(P) * N),
                               P * N * 2);
   // token table entry of token tid of chunk kc of the segment
   auto load_tok = [&](int kc) -> float2 {
-    return tid < Q ? tok[((static_cast<size_t>(b) * nc + c0 + kc) * H + h) * Q + tid]
+    return tid < Q ? tok[((tokc0 + kc) * H + h) * Q + tid]
                    : make_float2(0.f, 0.f);
   };
 
@@ -969,12 +987,25 @@ __global__ __launch_bounds__(kThreads, MULTI ? 2 : 3) void ssd_scan_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// variable lengths: the plan's segment count, the workspace layout and the
+// device copies of the tables
+struct VarSetup {
+  int npairs;
+  Bf16FwdLayout L;
+  VarLen vl;
+};
+
 template <int P, int N>
-static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output, int K) {
-  const int nc = (a.T + a.chunk - 1) / a.chunk;
-  const int nseg = (nc + K - 1) / K;
-  const int npairs = a.Bsz * nseg;
-  const Bf16FwdLayout L = bf16_fwd_layout(a.Bsz, nc, a.H, P, N, a.chunk, K);
+static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output, int K,
+                              const VarSetup* vs = nullptr) {
+  // uniform: nc chunks and nseg segments per sequence; variable lengths: the
+  // global segments of the plan (nc, nseg unused by the kernels)
+  const int nc = vs ? 0 : (a.T + a.chunk - 1) / a.chunk;
+  const int nseg = vs ? 0 : (nc + K - 1) / K;
+  const int npairs = vs ? vs->npairs : a.Bsz * nseg;
+  const Bf16FwdLayout L = vs ? vs->L : bf16_fwd_layout(a.Bsz, nc, a.H, P, N, a.chunk, K);
+  const VarLen vl = vs ? vs->vl : VarLen{nullptr, nullptr, nullptr};
+  const bool any = npairs > 0;
   char* ws = static_cast<char*>(a.workspace);
   float* S = reinterpret_cast<float*>(ws + L.S);
   uint16_t* hin = reinterpret_cast<uint16_t*>(ws + L.Hin);
@@ -988,9 +1019,9 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_outp
   // segment states: two heads per workgroup when the heads of a group pair up
   auto state = [&](auto hpw, auto s4) {
     constexpr int HPW = decltype(hpw)::value;
-    launch_k(nc > 0, ssd_state_bf16_kernel<P, N, HPW, decltype(s4)::value>, dim3(blocks / HPW), dim3(512),
+    launch_k(any, ssd_state_bf16_kernel<P, N, HPW, decltype(s4)::value>, dim3(blocks / HPW), dim3(512),
              st, ev, x, a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, decay, tok, a.T, a.H, a.G,
-             a.chunk, nc, K, nseg, npairs);
+             a.chunk, nc, K, nseg, npairs, vl);
   };
   const bool pair = kStatePairHeads && (a.H / a.G) % 2 == 0;
   if (pair && K > 1)
@@ -1004,49 +1035,51 @@ static hipError_t launch_bf16(const ChunkArgs& a, hipStream_t st, bool with_outp
   // without the outputs (the backward's recompute, K = 1) the fp32 boundary
   // states are kept too, over the chunk states
   if (with_output)
-    launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel<false>,
+    launch_k(any || a.h_final, ssd_pass_bf16_kernel<false>,
              dim3((P * N / 8 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
              ev ? ev + 2 : nullptr, S, hin, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
-             P * N, nseg);
+             P * N, nseg, vl.segstart);
   else
-    launch_k(nc > 0 || a.h_final, ssd_pass_bf16_kernel<true>,
+    launch_k(any || a.h_final, ssd_pass_bf16_kernel<true>,
              dim3((P * N / 8 + kThreads - 1) / kThreads, a.H, a.Bsz), dim3(kThreads), st,
              ev ? ev + 2 : nullptr, S, hin, static_cast<const float*>(decay), a.h0, a.h_final, a.H,
-             P * N, nseg);
+             P * N, nseg, vl.segstart);
   if (!with_output) return hipGetLastError();
   // the kernel walks several chunks only when K > 1 (a separate build: the
   // per-chunk factor step inside its loop costs registers)
   if (K > 1)
-    launch_k(nc > 0, ssd_scan_bf16_kernel<P, N, true>, dim3(blocks), dim3(kThreads), st,
+    launch_k(any, ssd_scan_bf16_kernel<P, N, true>, dim3(blocks), dim3(kThreads), st,
              ev ? ev + 4 : nullptr, x, B, C, a.D, static_cast<const float2*>(tok),
              static_cast<const uint16_t*>(hin), static_cast<uint16_t*>(a.y), a.T, a.H, a.G,
-             a.chunk, nc, K, nseg, npairs);
+             a.chunk, nc, K, nseg, npairs, vl);
   else
-    launch_k(nc > 0, ssd_scan_bf16_kernel<P, N, false>, dim3(blocks), dim3(kThreads), st,
+    launch_k(any, ssd_scan_bf16_kernel<P, N, false>, dim3(blocks), dim3(kThreads), st,
              ev ? ev + 4 : nullptr, x, B, C, a.D, static_cast<const float2*>(tok),
              static_cast<const uint16_t*>(hin), static_cast<uint16_t*>(a.y), a.T, a.H, a.G,
-             a.chunk, nc, K, nseg, npairs);
+             a.chunk, nc, K, nseg, npairs, vl);
   return hipGetLastError();
 }
 
 template <int P>
-static hipError_t dispatch_bf16_n(const ChunkArgs& a, hipStream_t st, bool with_output, int K) {
+static hipError_t dispatch_bf16_n(const ChunkArgs& a, hipStream_t st, bool with_output, int K,
+                                  const VarSetup* vs = nullptr) {
   switch (a.N) {
-    case 16: return launch_bf16<P, 16>(a, st, with_output, K);
-    case 32: return launch_bf16<P, 32>(a, st, with_output, K);
-    case 64: return launch_bf16<P, 64>(a, st, with_output, K);
-    case 128: return launch_bf16<P, 128>(a, st, with_output, K);
+    case 16: return launch_bf16<P, 16>(a, st, with_output, K, vs);
+    case 32: return launch_bf16<P, 32>(a, st, with_output, K, vs);
+    case 64: return launch_bf16<P, 64>(a, st, with_output, K, vs);
+    case 128: return launch_bf16<P, 128>(a, st, with_output, K, vs);
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
-static hipError_t dispatch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output, int K) {
+static hipError_t dispatch_bf16(const ChunkArgs& a, hipStream_t st, bool with_output, int K,
+                                const VarSetup* vs = nullptr) {
   switch (a.P) {
-    case 16: return dispatch_bf16_n<16>(a, st, with_output, K);
-    case 32: return dispatch_bf16_n<32>(a, st, with_output, K);
-    case 64: return dispatch_bf16_n<64>(a, st, with_output, K);
-    case 128: return dispatch_bf16_n<128>(a, st, with_output, K);
+    case 16: return dispatch_bf16_n<16>(a, st, with_output, K, vs);
+    case 32: return dispatch_bf16_n<32>(a, st, with_output, K, vs);
+    case 64: return dispatch_bf16_n<64>(a, st, with_output, K, vs);
+    case 128: return dispatch_bf16_n<128>(a, st, with_output, K, vs);
     default: break;
   }
   return hipErrorInvalidValue;
@@ -1061,5 +1094,98 @@ hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st) {
 // token table and h_final of a forward call without its outputs (the backward
 // recomputes these)
 hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st) { return dispatch_bf16(a, st, false, 1); }
+
+// ---- variable-length batches ----
+
+bool varlen_plan(const int* cu, int nseq, int H, int chunk, VarlenPlan& p, const char** why) {
+  if (nseq <= 0 || nseq > 65535) {
+    *why = "nseq must be in [1, 65535]";
+    return false;
+  }
+  if (cu[0] != 0) {
+    *why = "cu_seqlens[0] must be 0";
+    return false;
+  }
+  long long nc_tot = 0;
+  int max_nc = 0;
+  for (int b = 0; b < nseq; ++b) {
+    if (cu[b + 1] < cu[b]) {
+      *why = "cu_seqlens must be non-decreasing";
+      return false;
+    }
+    const int nc = (cu[b + 1] - cu[b] + chunk - 1) / chunk;
+    nc_tot += nc;
+    max_nc = nc > max_nc ? nc : max_nc;
+  }
+  p.nseq = nseq;
+  p.Ttot = cu[nseq];
+  p.nc_tot = nc_tot;
+  p.max_nc = max_nc;
+  // the uniform rule over all chunks, then no longer than the longest sequence
+  int K = nc_tot > 2147483647LL ? 16 : bf16_segment_chunks(1, static_cast<int>(nc_tot), H, chunk);
+  while (K > 1 && K > max_nc) K /= 2;
+  p.K = K;
+  long long npairs = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const int nc = (cu[b + 1] - cu[b] + chunk - 1) / chunk;
+    npairs += (nc + K - 1) / K;
+  }
+  if ((npairs + kXCD - 1) / kXCD * kXCD * H > 2147483647LL) {
+    *why = "grid too large: the segments times H exceed 2^31 - 1 workgroups";
+    return false;
+  }
+  p.npairs = static_cast<int>(npairs);
+  return true;
+}
+
+Bf16FwdLayout bf16_varlen_layout(const VarlenPlan& p, int H, int P, int N, int chunk) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t np = static_cast<size_t>(p.npairs);
+  const size_t st = np * H * P * N;
+  Bf16FwdLayout L{};
+  size_t o = 0;
+  L.S = o;
+  o += up(st * 4);
+  L.Hin = o;
+  o += up(st * 2);
+  L.decay = o;
+  o += up(np * H * 4);
+  L.tok = o;
+  o += up(np * p.K * H * chunk * 8);
+  L.table = o;
+  o += up(np * 8 + 2 * (static_cast<size_t>(p.nseq) + 1) * 4);
+  L.total = o;
+  return L;
+}
+
+hipError_t run_chunk_varlen_bf16(const ChunkArgs& a, const VarlenPlan& p, const int* cu, hipStream_t st) {
+  const Bf16FwdLayout L = bf16_varlen_layout(p, a.H, a.P, a.N, a.chunk);
+  // the table, built here and copied into the workspace (the call returns
+  // once the copy has taken the host data)
+  std::vector<int> t(static_cast<size_t>(p.npairs) * 2 + 2 * (static_cast<size_t>(p.nseq) + 1));
+  int* seg = t.data();
+  int* segstart = seg + static_cast<size_t>(p.npairs) * 2;
+  int* cud = segstart + p.nseq + 1;
+  int j = 0;
+  for (int b = 0; b < p.nseq; ++b) {
+    segstart[b] = j;
+    const int nc = (cu[b + 1] - cu[b] + a.chunk - 1) / a.chunk;
+    for (int sg = 0; sg < (nc + p.K - 1) / p.K; ++sg, ++j) {
+      seg[2 * j] = b;
+      seg[2 * j + 1] = sg;
+    }
+  }
+  segstart[p.nseq] = j;
+  for (int b = 0; b <= p.nseq; ++b) cud[b] = cu[b];
+  char* ws = static_cast<char*>(a.workspace);
+  hipError_t e = hipMemcpyAsync(ws + L.table, t.data(), t.size() * sizeof(int), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return e;
+  const char* tb = ws + L.table;
+  const VarSetup vs{p.npairs, L,
+                    VarLen{reinterpret_cast<const int*>(tb + (static_cast<size_t>(p.npairs) * 2 + p.nseq + 1) * 4),
+                           reinterpret_cast<const int2*>(tb),
+                           reinterpret_cast<const int*>(tb + static_cast<size_t>(p.npairs) * 8)}};
+  return dispatch_bf16(a, st, true, p.K, &vs);
+}
 
 }  // namespace ssd

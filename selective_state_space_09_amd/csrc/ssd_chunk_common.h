@@ -40,6 +40,51 @@ __device__ __forceinline__ bool unit_of_block(int H, int nc, int npairs, int& b,
   return unit_coords(blockIdx.x, H, nc, npairs, b, c, h);
 }
 
+// Variable-length batches of the bf16 real forward: sequence b holds the token
+// rows cu[b] .. cu[b+1]-1 of the packed inputs; its segments (of K chunks,
+// the last one possibly shorter) are the global segments segstart[b] ..
+// segstart[b+1]-1, and seg[j] = (b, segment of b) of global segment j, or
+// (-1, -1) for the padding past the last one.  With cu == nullptr every
+// sequence has T tokens and global segment j is (j / nseg, j % nseg).
+struct VarLen {
+  const int* cu;
+  const int2* seg;
+  const int* segstart;
+};
+
+// The segment a workgroup works on: sequence b, segment sg of it, head (or
+// head group) h under the XCD-grouped order of unit_coords; gs its global
+// segment index (states, h_in); row0 the sequence's first token row, T its
+// length.  False for padding units.
+struct SegView {
+  int b, sg, h, gs, T;
+  size_t row0;
+};
+__device__ __forceinline__ bool seg_of_block(const VarLen& v, int Hu, int T, int nseg, int npairs,
+                                             SegView& s) {
+  const int id = blockIdx.x;
+  const int k = id / kXCD;
+  const int j = (id % kXCD) + kXCD * (k / Hu);
+  s.h = k % Hu;
+  if (j >= npairs) return false;
+  s.gs = j;
+  if (v.cu) {
+    const int2 e = v.seg[j];
+    if (e.x < 0) return false;
+    s.b = e.x;
+    s.sg = e.y;
+    const int r = v.cu[e.x];
+    s.row0 = static_cast<size_t>(r);
+    s.T = v.cu[e.x + 1] - r;
+  } else {
+    s.b = j / nseg;
+    s.sg = j % nseg;
+    s.row0 = static_cast<size_t>(s.b) * T;
+    s.T = T;
+  }
+  return true;
+}
+
 
 // Launch of one kernel of a forward call.  With a start/stop event pair
 // (ev != NULL) the events are bound to the kernel's own dispatch

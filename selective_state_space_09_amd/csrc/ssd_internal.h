@@ -139,6 +139,7 @@ inline int bf16_segment_chunks(int Bsz, int nc, int H, int chunk) {
 
 struct Bf16FwdLayout {
   size_t S, Hin, decay, tok, total;  // byte offsets, total bytes
+  size_t table;                      // variable lengths: seg, segstart, cu (host-built)
 };
 
 inline Bf16FwdLayout bf16_fwd_layout(int Bsz, int nc, int H, int P, int N, int chunk, int K) {
@@ -158,6 +159,28 @@ inline Bf16FwdLayout bf16_fwd_layout(int Bsz, int nc, int H, int P, int N, int c
   L.total = o;
   return L;
 }
+
+// ---------------------------------------------------------------------------
+// Variable-length batch of the bf16 real forward.  cu: the (nseq + 1) host
+// offsets of the sequences' token rows in the packed inputs (cu[0] = 0,
+// non-decreasing, cu[nseq] = Ttot).  Each sequence is cut into chunks (a last,
+// shorter one) and segments of K chunks (a last, shorter one) on its own; the
+// segments of all sequences are numbered in sequence order (global segment
+// index), and the workspace holds per global segment what the uniform layout
+// holds per (batch, segment): S, Hin (npairs, H, P, N), decay (npairs, H) --
+// segment-major --, tok (npairs * K chunks, H, chunk); then the table the
+// kernels read: seg (npairs int2: sequence, segment of it), segstart
+// (nseq + 1), cu (nseq + 1).
+// ---------------------------------------------------------------------------
+struct VarlenPlan {
+  int nseq, Ttot, K, npairs, max_nc;
+  long long nc_tot;
+};
+// false (and *why) for an invalid cu or sizes beyond the kernels' limits
+bool varlen_plan(const int* cu, int nseq, int H, int chunk, VarlenPlan& p, const char** why);
+Bf16FwdLayout bf16_varlen_layout(const VarlenPlan& p, int H, int P, int N, int chunk);
+// a.Bsz = nseq, a.T = Ttot; the table is copied into the workspace from cu
+hipError_t run_chunk_varlen_bf16(const ChunkArgs& a, const VarlenPlan& p, const int* cu, hipStream_t st);
 
 hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);

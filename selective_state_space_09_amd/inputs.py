@@ -51,6 +51,10 @@ WORKLOADS = {
                      dtype="bf16"),
     # backward of the complex scan at the Mamba-3-Lite layer shape (loss
     # through y: seeded dy, no h0, no dh_final), chunk 64
+    # a batch of six prompts of mixed lengths (4096 tokens in all) through the
+    # BitMamba layer shape: the variable-length prefill
+    "varlen_bf16": dict(kind="varlen", lengths=(1024, 517, 2048, 3, 64, 440), H=64, P=64, N=128, G=1,
+                        chunk=256, dtype="bf16"),
     "bwd_complex": dict(kind="bwd_complex", Bsz=8, T=2048, H=16, P=64, N=64, G=16, chunk=64),
     # depthwise causal conv (K = 4, SiLU) of the BitMamba layer over its x|B|C
     # channels (4096 + 128 + 128), read from the in_proj output row (width
@@ -124,6 +128,25 @@ def make_real(Bsz, T, H, P, N, G=1, dtype="f32", seed=0, with_h0=False,
     return dict(kind="real", x=x, dt=dt, A=A, B=B, C=C, D=D, dt_bias=dt_bias,
                 dt_min=DT_MIN, dt_max=DT_MAX, h0=h0, dtype=dtype,
                 dims=dict(Bsz=Bsz, T=T, H=H, P=P, G=G, N=N))
+
+
+def make_varlen(lengths, H, P, N, G=1, dtype="bf16", seed=0, with_h0=False, **kw):
+    """A variable-length batch of the real form: the sequences of ``lengths``
+    packed along the token axis (x (Ttot,H,P), dt (Ttot,H), B/C (Ttot,G,N),
+    cu_seqlens (nseq+1) int32), drawn as ``make_real`` draws one sequence of
+    Ttot tokens; h0 (nseq,H,P,N) when asked."""
+    lengths = [int(t) for t in lengths]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    Ttot = int(cu[-1])
+    inp = make_real(1, Ttot, H, P, N, G=G, dtype=dtype, seed=seed, with_h0=False, **kw)
+    for k in ("x", "dt", "B", "C"):
+        inp[k] = np.ascontiguousarray(inp[k][0])
+    rng = np.random.default_rng(seed + 7919)
+    inp["h0"] = _normal(rng, (len(lengths), H, P, N)) if with_h0 else None
+    inp["cu_seqlens"] = cu
+    inp["kind"] = "varlen"
+    inp["dims"] = dict(nseq=len(lengths), Ttot=Ttot, H=H, P=P, G=G, N=N)
+    return inp
 
 
 def make_complex(Bsz, T, H, P, N, G=None, seed=0, with_h0=False, **_ignored):
@@ -269,6 +292,10 @@ def make_workload(name, seed=0, **overrides):
         return make_real(seed=seed, **cfg)
     if kind == "complex":
         return make_complex(seed=seed, **cfg)
+    if kind == "varlen":
+        c = dict(cfg)
+        return make_varlen(c.pop("lengths"), c.pop("H"), c.pop("P"), c.pop("N"), seed=seed,
+                           **{k: v for k, v in c.items() if k not in ("kind", "chunk")})
     if kind == "complex_packed":
         inp = make_complex(seed=seed, **cfg)
         inp["proj"] = pack_complex_rows(inp, cfg.get("ld"))

@@ -276,3 +276,38 @@ def test_f32_and_complex_backward_rejects_without_device_use():
     rc, msg = cplx(ws=16)
     assert rc == ssd.SSD_EWORKSPACE
     assert ssd.ssd_complex_bwd_workspace_size(1, 64, 2, 64, 2, 64) > 0
+
+
+def test_varlen_rejects_without_device_use():
+    """The variable-length forward checks cu_seqlens (a host array) and the
+    other arguments before any HIP call (this host has no GPU)."""
+    import numpy as np
+    L = ssd.lib()
+
+    def call(cu, dtype=ssd.SSD_BF16, ws=1 << 40, chunk=256, x=GOOD):
+        cu = np.ascontiguousarray(cu, np.int32)
+        rc = L.ssd_chunk_fwd_varlen(x, GOOD, GOOD, GOOD, GOOD, None, None, 0.0, 1.0, None, GOOD, None,
+                                    cu.ctypes.data_as(ctypes.c_void_p), cu.size - 1, 4, 64, 1, 128,
+                                    chunk, dtype, GOOD, ws, None)
+        return rc, L.ssd_last_error().decode()
+    rc, msg = call([1, 5, 9])
+    assert rc == ssd.SSD_EINVAL and "cu_seqlens[0]" in msg
+    rc, msg = call([0, 5, 3])
+    assert rc == ssd.SSD_EINVAL and "non-decreasing" in msg
+    rc, msg = call([0, 5, 9], dtype=ssd.SSD_F32)
+    assert rc == ssd.SSD_EUNSUPPORTED and "bfloat16" in msg
+    rc, msg = call([0, 5, 9], ws=16)
+    assert rc == ssd.SSD_EWORKSPACE
+    rc, msg = call([0, 5, 9], chunk=48)
+    assert rc == ssd.SSD_EUNSUPPORTED and "chunk=48" in msg
+    rc, msg = call([0, 5, 9], x=MISALIGNED)
+    assert rc == ssd.SSD_EINVAL and "x is not 16-byte aligned" in msg
+    rc = L.ssd_chunk_fwd_varlen(GOOD, GOOD, GOOD, GOOD, GOOD, None, None, 0.0, 1.0, None, GOOD, None,
+                                None, 2, 4, 64, 1, 128, 256, ssd.SSD_BF16, GOOD, 1 << 40, None)
+    assert rc == ssd.SSD_EINVAL and "cu_seqlens is NULL" in L.ssd_last_error().decode()
+    assert ssd.ssd_varlen_workspace_size([0, 5, 9], 4, 64, 1, 128, 256) > 0
+    assert ssd.ssd_varlen_workspace_size([0, 5, 3], 4, 64, 1, 128, 256) == 0
+    # the segment table grows with the number of sequences, not only with Ttot
+    one = ssd.ssd_varlen_workspace_size([0, 512], 4, 64, 1, 128, 256)
+    many = ssd.ssd_varlen_workspace_size([0] + list(range(1, 513)), 4, 64, 1, 128, 256)
+    assert many > one

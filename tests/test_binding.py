@@ -166,3 +166,20 @@ def test_complex_backward_rejects_mismatched_shapes():
         k2 = dict(kw)
         k2[name] = bad
         _raises_shape(ssd.ssd_complex_chunk_bwd, name, **k2)
+
+
+def test_varlen_binding_checks_shapes_before_the_call():
+    """cu_seqlens must be host memory and agree with x's token rows; the
+    per-sequence states must have nseq rows."""
+    import numpy as np
+    x = torch.zeros((9, 4, 64), dtype=torch.bfloat16)
+    B = torch.zeros((9, 1, 128), dtype=torch.bfloat16)
+    dt = torch.zeros((9, 4))
+    A = torch.zeros(4)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        ssd.ssd_chunk_fwd_varlen(x, dt, A, B, B, [0, 5, 8])
+    with pytest.raises(ValueError, match="h0"):
+        ssd.ssd_chunk_fwd_varlen(x, dt, A, B, B, np.array([0, 5, 9]),
+                                 h0=torch.zeros((3, 4, 64, 128)))
+    with pytest.raises(ValueError, match="at least 2"):
+        ssd.ssd_chunk_fwd_varlen(x, dt, A, B, B, [9])

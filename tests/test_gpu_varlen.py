@@ -1,0 +1,156 @@
+"""GPU parity of the variable-length real forward (ssd_chunk_fwd_varlen,
+bfloat16 x/B/C/y) against the oracle's per-sequence recurrence
+(oracle.fwd_varlen), through the C ABI.
+
+Bar: the bfloat16 tolerance, 2e-2 normwise per (sequence, head) for y and
+h_final.  Also: bit-identical to the batched forward when every sequence has
+the same length, and to a call on one sequence alone when both pick the same
+segment length; and the prefill -> decode chaining of each sequence through
+its h_final.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_09_amd as ssd
+from selective_state_space_09_amd import inputs
+import _gpu
+import _metrics
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _run(inp, chunk, heads=None):
+    d = _gpu.upload(inp)
+    y, hf = ssd.ssd_chunk_fwd_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], inp["cu_seqlens"], d["D"],
+                                     d["dt_bias"], d["dt_min"], d["dt_max"], d["h0"], chunk=chunk,
+                                     return_final_state=True)
+    torch.cuda.synchronize()
+    return y, hf
+
+
+def _ref(inp, heads=None):
+    sub = dict(inp)
+    if heads is not None:
+        for k in ("x", "dt"):
+            sub[k] = np.ascontiguousarray(inp[k][:, heads])
+        for k in ("A", "D", "dt_bias"):
+            sub[k] = None if inp[k] is None else np.ascontiguousarray(inp[k][heads])
+        sub["h0"] = None if inp["h0"] is None else np.ascontiguousarray(inp["h0"][:, heads])
+    return oracle.fwd_varlen(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["cu_seqlens"],
+                             sub["D"], sub["dt_bias"], sub["dt_min"], sub["dt_max"], sub["h0"])
+
+
+def _per_sequence_err(got, ref, cu):
+    """max over sequences of the per-(sequence, head) normwise error of y"""
+    e = 0.0
+    for b in range(len(cu) - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi > lo:
+            e = max(e, _metrics.y_err(got[None, lo:hi], ref[None, lo:hi]))
+    return e
+
+
+def _check(y, hf, ref_y, ref_hf, cu, what):
+    ey = _per_sequence_err(y, ref_y, cu)
+    eh = _metrics.state_err(hf, ref_hf)
+    print(what, f"y {ey:.2e} (global {_metrics.global_err(y, ref_y):.2e})  h_final {eh:.2e}", flush=True)
+    assert ey <= TOL and eh <= TOL, (what, ey, eh)
+
+
+CASES = [
+    # lengths, H, P, N, G, chunk, with_h0
+    ([0, 1, 63, 64, 65, 300, 513, 0, 17], 4, 64, 128, 1, 256, True),  # empty, single-token, ragged
+    ([5, 200, 64, 129], 4, 64, 64, 2, 64, True),                       # two groups, chunk 64
+    ([300, 1, 77], 2, 32, 128, 2, 128, False),                         # per-head groups, no h0
+    ([16, 33, 48, 0], 2, 16, 16, 1, 16, True),                         # chunk 16, smallest tiles
+]
+
+
+@pytest.mark.parametrize("lengths,H,P,N,G,chunk,wh0", CASES)
+def test_varlen_matches_oracle(lengths, H, P, N, G, chunk, wh0):
+    what = f"varlen lengths={lengths} H={H} P={P} N={N} G={G} chunk={chunk}"
+    print(what, flush=True)
+    inp = inputs.make_varlen(lengths, H, P, N, G=G, dtype="bf16", seed=sum(lengths) + H, with_h0=wh0)
+    y, hf = _run(inp, chunk)
+    ry, rh = _ref(inp)
+    _check(_gpu.to_host64(y), _gpu.to_host64(hf), ry, rh, inp["cu_seqlens"], what)
+
+
+def test_varlen_equal_lengths_is_the_batched_forward_bit_for_bit():
+    L, nseq, H, P, N = 300, 3, 4, 64, 128
+    print("varlen equal lengths vs batched", flush=True)
+    inp = inputs.make_varlen([L] * nseq, H, P, N, dtype="bf16", seed=4, with_h0=True)
+    y, hf = _run(inp, 256)
+    d = _gpu.upload(inp)
+    rs = lambda t: t.reshape((nseq, L) + tuple(t.shape[1:]))
+    yb, hb = ssd.ssd_chunk_fwd(rs(d["x"]), rs(d["dt"]), d["A"], rs(d["B"]), rs(d["C"]), d["D"], d["dt_bias"],
+                               d["dt_min"], d["dt_max"], d["h0"], chunk=256, return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), yb.reshape(y.shape).view(torch.int16))
+    assert torch.equal(hf, hb)
+
+
+def test_varlen_long_sequences_segments():
+    """Sequences long enough that workgroups walk segments of K = 2 chunks
+    (45 517 tokens, 64 heads: 180 chunks of 256): three sampled heads against
+    the oracle in every sequence; the first sequence bit for bit against a
+    call on it alone (which picks the same K)."""
+    lengths, H, P, N = [40000, 3000, 17, 2500], 64, 64, 128
+    print(f"varlen long lengths={lengths}", flush=True)
+    inp = inputs.make_varlen(lengths, H, P, N, dtype="bf16", seed=12, with_h0=True)
+    y, hf = _run(inp, 256)
+    heads = [0, 37, 63]
+    ry, rh = _ref(inp, heads)
+    yh = _gpu.to_host64(y)[:, heads]
+    hh = _gpu.to_host64(hf)[:, heads]
+    _check(yh, hh, ry, rh, inp["cu_seqlens"], "varlen long, heads 0 37 63")
+    d = _gpu.upload(inp)
+    L0 = lengths[0]
+    one = lambda t: t[:L0][None]
+    y1, h1 = ssd.ssd_chunk_fwd(one(d["x"]), one(d["dt"]), d["A"], one(d["B"]), one(d["C"]), d["D"],
+                               d["dt_bias"], d["dt_min"], d["dt_max"], d["h0"][:1].contiguous(), chunk=256,
+                               return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:L0].view(torch.int16), y1[0].view(torch.int16))
+    assert torch.equal(hf[0], h1[0])
+
+
+def test_varlen_prefill_then_decode():
+    """Each sequence's h_final continues in the decode step: one more token
+    per sequence (float32) against the oracle on the sequences one token
+    longer (the prefill's bf16 values widened exactly)."""
+    lengths, H, P, N, G = [7, 130, 0, 64], 4, 64, 128, 1
+    print(f"varlen prefill -> decode lengths={lengths}", flush=True)
+    inp = inputs.make_varlen(lengths, H, P, N, G=G, dtype="bf16", seed=21, with_h0=True)
+    y, hf = _run(inp, 64)
+    nseq = len(lengths)
+    step = inputs.make_decode(nseq, H, P, N, G=G, seed=22)["steps"][0]  # x (nseq,H,P), dt, B, C
+    h = hf.clone()
+    yd = ssd.ssd_step_decode(h, _gpu.to_dev(step["x"]), _gpu.to_dev(step["dt"]), _gpu.to_dev(inp["A"]),
+                             _gpu.to_dev(step["B"]), _gpu.to_dev(step["C"]), _gpu.to_dev(inp["D"]),
+                             _gpu.to_dev(inp["dt_bias"]), inp["dt_min"], inp["dt_max"])
+    torch.cuda.synchronize()
+    # the oracle on the extended sequences, in float32
+    w = inputs.bf16_bits_to_f32
+    cu = inp["cu_seqlens"]
+    xs, dts, Bs, Cs = [], [], [], []
+    for b in range(nseq):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        xs += [w(inp["x"][lo:hi]), step["x"][b:b + 1]]
+        dts += [inp["dt"][lo:hi], step["dt"][b:b + 1]]
+        Bs += [w(inp["B"][lo:hi]), step["B"][b:b + 1]]
+        Cs += [w(inp["C"][lo:hi]), step["C"][b:b + 1]]
+    cu2 = np.concatenate([[0], np.cumsum(np.asarray(lengths) + 1)]).astype(np.int32)
+    ry, rh = oracle.fwd_varlen(np.concatenate(xs).astype(np.float32), np.concatenate(dts).astype(np.float32),
+                               inp["A"], np.concatenate(Bs).astype(np.float32),
+                               np.concatenate(Cs).astype(np.float32), cu2, inp["D"], inp["dt_bias"],
+                               inp["dt_min"], inp["dt_max"], inp["h0"])
+    last = ry[cu2[1:] - 1]  # (nseq, H, P)
+    ey = _metrics.y_err_bh(yd.cpu().numpy(), last)
+    eh = _metrics.state_err(h.cpu().numpy(), rh)
+    print(f"prefill -> decode: y {ey:.2e}  state {eh:.2e}", flush=True)
+    assert ey <= TOL and eh <= TOL
