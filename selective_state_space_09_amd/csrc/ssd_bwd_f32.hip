@@ -88,10 +88,10 @@ __device__ __forceinline__ float qsum(float a) {
 
 // rows [0, rows) of W-float-wide rows (src row stride `ld` floats) into an LDS
 // tile of pitch `pitch`, zeros for rows past `valid`
-template <int W>
+template <int W, int NTHR = kThreads>
 __device__ __forceinline__ void stage(float* tile, int pitch, const float* __restrict__ src, size_t ld,
                                       int rows, int valid) {
-  for (int i = threadIdx.x; i < rows * (W / 4); i += kThreads) {
+  for (int i = threadIdx.x; i < rows * (W / 4); i += NTHR) {
     const int r = i / (W / 4), v = i % (W / 4);
     const float4 val = r < valid ? *reinterpret_cast<const float4*>(src + r * ld + v * 4)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -119,14 +119,22 @@ __device__ __forceinline__ f32x4 dot_rows(const float* arow, const float* brow, 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Column side: wave w owns the 16 source tokens s = 16 w .. +15 of the chunk
-// (one per lane column).  Scores S = C.B^T and W0 = dy.x^T (rows l, columns
-// s), masked and decayed into M and W; then
-//   v^T[p][s] = e^{tot-cs_s} (R B_s)[p] + sum_l dy^T[p][l] M[l][s],
-//   dB^T[n][s] = s_s e^{tot-cs_s} (R^T x_s)[n] + sum_l C^T[n][l] W[l][s].
+// Both block kernels run eight waves (two per SIMD: the 137 KB of LDS of the
+// widest tiles leave room for one workgroup per CU), in two roles of four
+// waves; in each role wave w owns the 16 tokens 16 (w % 4) .. +15 of the
+// chunk as MFMA columns.
+// ---------------------------------------------------------------------------
+constexpr int kT8 = 512;
+
+// Column side, source token s = 16 (w % 4) + lane % 16.  Scores S = C.B^T and
+// W0 = dy.x^T (rows l, columns s), masked and decayed into M and W.
+//   role 0:  v^T[p][s] = e^{tot-cs_s} (R B_s)[p] + sum_l dy^T[p][l] M[l][s];
+//            dx, f2, col (the box terms), x.v, dy.x
+//   role 1:  dB^T[n][s] = s_s e^{tot-cs_s} (R^T x_s)[n] + sum_l C^T[n][l] W[l][s];
+//            rho_B (complex)
 // ---------------------------------------------------------------------------
 template <int P, int NE, bool SCALE, bool CPLX>
-__global__ __launch_bounds__(kThreads) void ssd_f32_col_kernel(
+__global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
     const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ dt_bias, float dt_min, float dt_max, const float* __restrict__ Bm,
     const float* __restrict__ Cm, const float* __restrict__ dy, const float* __restrict__ D,
@@ -142,93 +150,111 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_col_kernel(
   __shared__ __attribute__((aligned(16))) float Cs[kQ * NP];
   __shared__ __attribute__((aligned(16))) float Rs[P * NP];
   __shared__ float dl[kQ], cs_hi[kQ], cs_lo[kQ];
-  __shared__ double wsum[4], tot;
+  __shared__ double wsum[kT8 / kWave], tot;
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (H / G);
   const int t0 = c * kQ, Lc = min(kQ, T - t0);
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
-  const int w = wave_id();
+  const int w = wave_id(), role = w >> 2;
   const size_t r0 = static_cast<size_t>(b) * T + t0;
   const float dt_raw = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
-  stage<P>(Xs, XP, x + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  stage<P>(Ys, XP, dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  stage<NE>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
-  stage<NE>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
-  stage<NE>(Rs, NP, adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE), NE, P,
-            P);
+  stage<P, kT8>(Xs, XP, x + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
+  stage<P, kT8>(Ys, XP, dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
+  stage<NE, kT8>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  stage<NE, kT8>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  stage<NE, kT8>(Rs, NP, adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE),
+                 NE, P, P);
   chunk_prologue(dt_raw, Lc, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, dl, cs_hi, cs_lo, wsum,
                  &tot, kQ);  // (its barrier also publishes the staged tiles)
 
-  const int s = 16 * w + r16;  // this lane's source token
+  const int s = 16 * (w & 3) + r16;  // this lane's source token
   const float hs = cs_hi[s], ls = cs_lo[s];
   const float sc = SCALE ? dl[s] : (s < Lc ? 1.0f : 0.0f);
   const float fr = s < Lc ? __expf(static_cast<float>((tot - static_cast<double>(hs)) - static_cast<double>(ls)))
                           : 0.0f;  // e^{tot - cs_s} <= 1
+  const size_t row = (r0 + s) * H + h;
 
-  // scores, rows l = 16 lt + 4q + i
-  f32x4 sS[4], sW[4];
+  // W0 = dy.x^T, rows l = 16 lt + 4q + i, masked, decayed and scaled into W
+  f32x4 sW[4];
 #pragma unroll
-  for (int lt = 0; lt < 4; ++lt) {
-    sS[lt] = dot_rows<NE>(Cs + (16 * lt + r16) * NP, Bs + s * NP, f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int lt = 0; lt < 4; ++lt)
     sW[lt] = dot_rows<P>(Ys + (16 * lt + r16) * XP, Xs + s * XP, f32x4{0.f, 0.f, 0.f, 0.f});
-  }
-  float col = 0.0f;
+  float dd[4][4];  // decay of (l, s), 0 off the causal block
 #pragma unroll
   for (int lt = 0; lt < 4; ++lt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int l = 16 * lt + 4 * q + i;
       const bool ok = l >= s && l < Lc && s < Lc;
-      const float d = ok ? decay_between(cs_hi[l], cs_lo[l], hs, ls) : 0.0f;
-      const float m = d * sS[lt][i];
-      const float wv = d * sc * sW[lt][i];
-      col += l > s ? wv * sS[lt][i] : 0.0f;
-      sS[lt][i] = m;
-      sW[lt][i] = wv;
+      dd[lt][i] = ok ? decay_between(cs_hi[l], cs_lo[l], hs, ls) : 0.0f;
+      sW[lt][i] = dd[lt][i] * sc * sW[lt][i];
     }
-  col = qsum(col);
 
-  // v: boundary (R B_s), then f2, then the intra-chunk part
-  f32x4 v[PT];
+  if (role == 0) {
+    // scores S = C.B^T; the box terms; M = decayed S
+    f32x4 sS[4];
 #pragma unroll
-  for (int pt = 0; pt < PT; ++pt) {
-    v[pt] = dot_rows<NE>(Rs + (16 * pt + r16) * NP, Bs + s * NP, f32x4{0.f, 0.f, 0.f, 0.f});
-    v[pt] = v[pt] * fr;
-  }
-  float f2 = 0.0f;
+    for (int lt = 0; lt < 4; ++lt)
+      sS[lt] = dot_rows<NE>(Cs + (16 * lt + r16) * NP, Bs + s * NP, f32x4{0.f, 0.f, 0.f, 0.f});
+    float col = 0.0f;
 #pragma unroll
-  for (int pt = 0; pt < PT; ++pt)
+    for (int lt = 0; lt < 4; ++lt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f2 += Xs[s * XP + 16 * pt + 4 * q + i] * v[pt][i];
-  f2 = sc * qsum(f2);
+      for (int i = 0; i < 4; ++i) {
+        const int l = 16 * lt + 4 * q + i;
+        col += l > s ? sW[lt][i] * sS[lt][i] : 0.0f;
+        sS[lt][i] = dd[lt][i] * sS[lt][i];
+      }
+    col = qsum(col);
+    // v: boundary (R B_s), then f2, then the intra-chunk part
+    f32x4 v[PT];
 #pragma unroll
-  for (int lt = 0; lt < 4; ++lt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
-        v[pt] = mfma_f32(Ys[(16 * lt + 4 * q + j) * XP + 16 * pt + r16], sS[lt][j], v[pt]);
-  float xv = 0.0f, dyx = 0.0f;
-  const float Dh = D ? D[h] : 0.0f;
-  float* dxr = dx + ((r0 + s) * H + h) * P;
-#pragma unroll
-  for (int pt = 0; pt < PT; ++pt) {
-    float o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = 16 * pt + 4 * q + i;
-      const float xe = Xs[s * XP + p], ye = Ys[s * XP + p];
-      xv += xe * v[pt][i];
-      dyx += xe * ye;
-      o[i] = sc * v[pt][i] + Dh * ye;
+    for (int pt = 0; pt < PT; ++pt) {
+      v[pt] = dot_rows<NE>(Rs + (16 * pt + r16) * NP, Bs + s * NP, f32x4{0.f, 0.f, 0.f, 0.f});
+      v[pt] = v[pt] * fr;
     }
-    if (s < Lc) *reinterpret_cast<float4*>(dxr + 16 * pt + 4 * q) = make_float4(o[0], o[1], o[2], o[3]);
+    float f2 = 0.0f;
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f2 += Xs[s * XP + 16 * pt + 4 * q + i] * v[pt][i];
+    f2 = sc * qsum(f2);
+#pragma unroll
+    for (int lt = 0; lt < 4; ++lt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+          v[pt] = mfma_f32(Ys[(16 * lt + 4 * q + j) * XP + 16 * pt + r16], sS[lt][j], v[pt]);
+    float xv = 0.0f, dyx = 0.0f;
+    const float Dh = D ? D[h] : 0.0f;
+    float* dxr = dx + row * P;
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = 16 * pt + 4 * q + i;
+        const float xe = Xs[s * XP + p], ye = Ys[s * XP + p];
+        xv += xe * v[pt][i];
+        dyx += xe * ye;
+        o[i] = sc * v[pt][i] + Dh * ye;
+      }
+      if (s < Lc) *reinterpret_cast<float4*>(dxr + 16 * pt + 4 * q) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    xv = qsum(xv);
+    dyx = qsum(dyx);
+    if (q == 0 && s < Lc) {
+      f2o[row] = f2;
+      colo[row] = col;
+      xvo[row] = xv;
+      dyxo[row] = dyx;
+    }
+    return;
   }
-  xv = qsum(xv);
-  dyx = qsum(dyx);
 
-  // dB: boundary (R^T x_s), scaled, then the intra-chunk part
+  // role 1 -- dB: boundary (R^T x_s), scaled, then the intra-chunk part
   f32x4 db[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -250,7 +276,6 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_col_kernel(
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         db[nt] = mfma_f32(Cs[(16 * lt + 4 * q + j) * NP + 16 * nt + r16], sW[lt][j], db[nt]);
-  const size_t row = (r0 + s) * H + h;
   if (s < Lc) {
     if (CPLX && dBo) {
       // each head its own group: dB = e^{i theta} (dB_eff[n] + i dB_eff[N+n]) straight out
@@ -274,10 +299,10 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_col_kernel(
         *reinterpret_cast<f32x4*>(dBh + row * NE + 16 * nt + 4 * q) = db[nt];
     }
   }
-  float rb = 0.0f;
   if constexpr (CPLX) {
     // Im(conj(dB') B') = dB_eff[n] B_eff[N+n] - dB_eff[N+n] B_eff[n]
     constexpr int HT = NT / 2;
+    float rb = 0.0f;
 #pragma unroll
     for (int nt = 0; nt < HT; ++nt)
 #pragma unroll
@@ -286,25 +311,20 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_col_kernel(
         rb += db[nt][i] * Bs[s * NP + NE / 2 + n] - db[nt + HT][i] * Bs[s * NP + n];
       }
     rb = qsum(rb);
-  }
-  if (q == 0 && s < Lc) {
-    f2o[row] = f2;
-    colo[row] = col;
-    xvo[row] = xv;
-    dyxo[row] = dyx;
-    if constexpr (CPLX) rhoB[row] = rb;
+    if (q == 0 && s < Lc) rhoB[row] = rb;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Row side: wave w owns the 16 target tokens l = 16 w .. +15 (one per lane
-// column).  Transposed scores S^T = B.C^T and W0^T = x.dy^T (rows s, columns
-// l), masked and decayed; then
-//   dC^T[n][l] = e^{cs_l} (H_in^T dy_l)[n] + sum_s B^T[n][s] W^T[s][l],
-// f1 from the boundary part, row from the box terms.
+// Row side, target token l = 16 (w % 4) + lane % 16.  Transposed scores
+// S^T = B.C^T and W0^T = x.dy^T (rows s, columns l), masked and decayed.
+//   role 0:  the boundary part of dC^T[n][l], e^{cs_l} (H_in^T dy_l)[n]; f1;
+//            row (the box terms); after the exchange the whole dC, rho_C
+//   role 1:  the intra-chunk part sum_s B^T[n][s] W^T[s][l], handed to role 0
+//            through LDS (over the B tile, once every wave is done with it)
 // ---------------------------------------------------------------------------
 template <int P, int NE, bool SCALE, bool CPLX>
-__global__ __launch_bounds__(kThreads) void ssd_f32_row_kernel(
+__global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
     const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ dt_bias, float dt_min, float dt_max, const float* __restrict__ Bm,
     const float* __restrict__ Cm, const float* __restrict__ dy, const float* __restrict__ states,
@@ -319,36 +339,33 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_row_kernel(
   __shared__ __attribute__((aligned(16))) float Cs[kQ * NP];
   __shared__ __attribute__((aligned(16))) float Hs[P * NP];
   __shared__ float dl[kQ], cs_hi[kQ], cs_lo[kQ];
-  __shared__ double wsum[4], tot;
+  __shared__ double wsum[kT8 / kWave], tot;
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (H / G);
   const int t0 = c * kQ, Lc = min(kQ, T - t0);
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
-  const int w = wave_id();
+  const int w = wave_id(), role = w >> 2;
   const size_t r0 = static_cast<size_t>(b) * T + t0;
   const float dt_raw = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
-  stage<P>(Xs, XP, x + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  stage<P>(Ys, XP, dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  stage<NE>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
-  stage<NE>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
-  stage<NE>(Hs, NP, states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE),
-            NE, P, P);
+  stage<P, kT8>(Xs, XP, x + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
+  stage<P, kT8>(Ys, XP, dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
+  stage<NE, kT8>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  stage<NE, kT8>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  stage<NE, kT8>(Hs, NP, states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE),
+                 NE, P, P);
   chunk_prologue(dt_raw, Lc, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, dl, cs_hi, cs_lo, wsum,
                  &tot, kQ);
 
-  const int l = 16 * w + r16;  // this lane's target token
+  const int l = 16 * (w & 3) + r16;  // this lane's target token
   const float hl = cs_hi[l], ll = cs_lo[l];
-  const float fl = l < Lc ? __expf(hl + ll) : 0.0f;  // e^{cs_l} <= 1
+  const size_t row = (r0 + l) * H + h;
 
-  // transposed scores, rows s = 16 st + 4q + i
-  f32x4 sS[4], sW[4];
+  // W0^T = x.dy^T, rows s = 16 st + 4q + i, masked, decayed and scaled
+  f32x4 sW[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    sS[st] = dot_rows<NE>(Bs + (16 * st + r16) * NP, Cs + l * NP, f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int st = 0; st < 4; ++st)
     sW[st] = dot_rows<P>(Xs + (16 * st + r16) * XP, Ys + l * XP, f32x4{0.f, 0.f, 0.f, 0.f});
-  }
-  float rw = 0.0f;
 #pragma unroll
   for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -357,41 +374,66 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_row_kernel(
       const bool ok = s <= l && l < Lc && s < Lc;
       const float d = ok ? decay_between(hl, ll, cs_hi[s], cs_lo[s]) : 0.0f;
       const float sc = SCALE ? dl[s] : 1.0f;
-      const float wv = d * sc * sW[st][i];
-      rw += s < l ? wv * sS[st][i] : 0.0f;
-      sW[st][i] = wv;
+      sW[st][i] = d * sc * sW[st][i];
     }
-  rw = qsum(rw);
 
-  // dC: boundary (H_in^T dy_l) scaled by e^{cs_l}, f1, then the intra-chunk part
   f32x4 dc[NT];
+  float f1 = 0.0f, rw = 0.0f;
+  if (role == 0) {
+    f32x4 sS[4];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < 4; ++st)
+      sS[st] = dot_rows<NE>(Bs + (16 * st + r16) * NP, Cs + l * NP, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int k0 = 0; k0 < P; k0 += 16) {
-      const float4 yb = *reinterpret_cast<const float4*>(Ys + l * XP + k0 + 4 * q);
-      acc = mfma_f32(Hs[(k0 + 4 * q + 0) * NP + 16 * nt + r16], yb.x, acc);
-      acc = mfma_f32(Hs[(k0 + 4 * q + 1) * NP + 16 * nt + r16], yb.y, acc);
-      acc = mfma_f32(Hs[(k0 + 4 * q + 2) * NP + 16 * nt + r16], yb.z, acc);
-      acc = mfma_f32(Hs[(k0 + 4 * q + 3) * NP + 16 * nt + r16], yb.w, acc);
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * st + 4 * q + i;
+        rw += s < l ? sW[st][i] * sS[st][i] : 0.0f;
+      }
+    rw = qsum(rw);
+    // boundary (H_in^T dy_l) scaled by e^{cs_l}, and f1
+    const float fl = l < Lc ? __expf(hl + ll) : 0.0f;  // e^{cs_l} <= 1
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < P; k0 += 16) {
+        const float4 yb = *reinterpret_cast<const float4*>(Ys + l * XP + k0 + 4 * q);
+        acc = mfma_f32(Hs[(k0 + 4 * q + 0) * NP + 16 * nt + r16], yb.x, acc);
+        acc = mfma_f32(Hs[(k0 + 4 * q + 1) * NP + 16 * nt + r16], yb.y, acc);
+        acc = mfma_f32(Hs[(k0 + 4 * q + 2) * NP + 16 * nt + r16], yb.z, acc);
+        acc = mfma_f32(Hs[(k0 + 4 * q + 3) * NP + 16 * nt + r16], yb.w, acc);
+      }
+      dc[nt] = acc * fl;
     }
-    dc[nt] = acc * fl;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f1 += Cs[l * NP + 16 * nt + 4 * q + i] * dc[nt][i];
+    f1 = qsum(f1);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          dc[nt] = mfma_f32(Bs[(16 * st + 4 * q + j) * NP + 16 * nt + r16], sW[st][j], dc[nt]);
   }
-  float f1 = 0.0f;
+  __syncthreads();  // every wave is done with the B tile
+  float* part = Bs;  // role 1's part of dC, [l][n] at the B tile's pitch
+  if (role == 1) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f32x4*>(part + l * NP + 16 * nt + 4 * q) = dc[nt];
+  }
+  __syncthreads();
+  if (role == 1) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f1 += Cs[l * NP + 16 * nt + 4 * q + i] * dc[nt][i];
-  f1 = qsum(f1);
-#pragma unroll
-  for (int st = 0; st < 4; ++st)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        dc[nt] = mfma_f32(Bs[(16 * st + 4 * q + j) * NP + 16 * nt + r16], sW[st][j], dc[nt]);
-  const size_t row = (r0 + l) * H + h;
+  for (int nt = 0; nt < NT; ++nt) dc[nt] = dc[nt] + *reinterpret_cast<const f32x4*>(part + l * NP + 16 * nt + 4 * q);
   if (l < Lc) {
     if (CPLX && dCo) {
       // each head its own group: dC = e^{-i theta} (dC_eff[n] - i dC_eff[N+n]) straight out
@@ -856,10 +898,10 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
   const dim3 grid(nc > 0 ? nc : 1, H, Bsz);
   constexpr bool SCALE = !CPLX;
   const bool run = nc > 0;
-  launch_k(run, ssd_f32_col_kernel<P, NE, SCALE, CPLX>, grid, dim3(kThreads), st, E(5), x, dt, A_dec,
+  launch_k(run, ssd_f32_col_kernel<P, NE, SCALE, CPLX>, grid, dim3(kT8), st, E(5), x, dt, A_dec,
            dt_bias, dt_min, dt_max, Beff, Ceff, dy, D, adj, dx, dBh, f2, col, xv, dyx, rhoB, rot, dBo, T, H,
            Geff, nc);
-  launch_k(run, ssd_f32_row_kernel<P, NE, SCALE, CPLX>, grid, dim3(kThreads), st, E(6), x, dt, A_dec,
+  launch_k(run, ssd_f32_row_kernel<P, NE, SCALE, CPLX>, grid, dim3(kT8), st, E(6), x, dt, A_dec,
            dt_bias, dt_min, dt_max, Beff, Ceff, dy, S, dCh, f1, rw, rhoC, rot, dCo, T, H, Geff,
            nc);
   launch_k(run, ssd_f32_const_kernel, grid, dim3(kThreads), st, E(7), adj, S, dec, cst, H, P * NE, nc);
