@@ -69,9 +69,11 @@ struct StateBSlab : Slab<ST, N / 4, 1> {
 // (no delta_s on the input term: the rotated-frame form of the complex
 // recurrence).  kStateAdj: the adjoint chunk state of the backward,
 // G_c = sum_l e^{cs_l} dy_l (x) C_l (x = dy, B = C; no decay written).
+// NBUF = 1: one stage buffer, for chunks of at most one stage (the backward's
+// 64-token chunks): half the LDS, so that two workgroups share a CU.
 constexpr int kStateFwd = 0, kStateFwdUnit = 1, kStateAdj = 2;
 
-template <int P, int N, int MODE = kStateFwd>
+template <int P, int N, int MODE = kStateFwd, int NBUF = 2>
 __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min, float dt_max,
@@ -83,10 +85,11 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   constexpr int NTILE = (P / 16) * (N / 16);
   constexpr int TPW = (NTILE + 3) / 4;  // output tiles per wave
 
-  __shared__ __attribute__((aligned(16))) float xT[2][P * XP];
-  __shared__ __attribute__((aligned(16))) float bT[2][N * XP];
-  __shared__ float dl[256], cs_hi[256], cs_lo[256];
-  __shared__ float wre[256];
+  constexpr int TQ = NBUF == 1 ? 64 : 256;  // longest chunk
+  __shared__ __attribute__((aligned(16))) float xT[NBUF][P * XP];
+  __shared__ __attribute__((aligned(16))) float bT[NBUF][N * XP];
+  __shared__ float dl[TQ], cs_hi[TQ], cs_lo[TQ];
+  __shared__ float wre[TQ];
   __shared__ double wsum[4], tot;
 
   int b, c, h;
@@ -142,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
 
   const int ntiles = (Lc + ST - 1) / ST;
   for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    const bool more = it + 1 < ntiles;
+    const int cur = NBUF == 1 ? 0 : it & 1;
+    const bool more = NBUF > 1 && it + 1 < ntiles;
     if (more) {
       xs.load(xbase, xrow, (it + 1) * ST, Lc);
       bs.load(bbase, brow, (it + 1) * ST, Lc);
@@ -166,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
       }
     }
     if (more) {
-      xs.store(xT[cur ^ 1]);
-      bs.store(bT[cur ^ 1], wre, (it + 1) * ST, Q);
+      xs.store(xT[(cur ^ 1) % NBUF]);
+      bs.store(bT[(cur ^ 1) % NBUF], wre, (it + 1) * ST, Q);
     }
     __syncthreads();
   }
@@ -472,14 +475,15 @@ static hipError_t launch_states_f32(const float* x, const float* dt, const float
   const int nc = (T + chunk - 1) / chunk;
   const int npairs = Bsz * nc;
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * H;
+  if (chunk > 64) return hipErrorInvalidValue;  // one stage buffer holds 64 tokens
   if (mode == kStateFwd)
-    launch_k(nc > 0, ssd_state_kernel<P, N, kStateFwd>, dim3(blocks), dim3(kThreads), st, ev, x, dt,
+    launch_k(nc > 0, ssd_state_kernel<P, N, kStateFwd, 1>, dim3(blocks), dim3(kThreads), st, ev, x, dt,
              A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
   else if (mode == kStateFwdUnit)
-    launch_k(nc > 0, ssd_state_kernel<P, N, kStateFwdUnit>, dim3(blocks), dim3(kThreads), st, ev, x,
+    launch_k(nc > 0, ssd_state_kernel<P, N, kStateFwdUnit, 1>, dim3(blocks), dim3(kThreads), st, ev, x,
              dt, A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
   else
-    launch_k(nc > 0, ssd_state_kernel<P, N, kStateAdj>, dim3(blocks), dim3(kThreads), st, ev, x, dt,
+    launch_k(nc > 0, ssd_state_kernel<P, N, kStateAdj, 1>, dim3(blocks), dim3(kThreads), st, ev, x, dt,
              A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
   return hipGetLastError();
 }
