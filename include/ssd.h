@@ -328,6 +328,38 @@ int ssd_conv1d_fwd(const void *xbc, long long ld, const float *w, const float *b
                    void *stream);
 
 /*
+ * The convolution over a variable-length batch (the prefill of nseq sequences
+ * of different lengths, packed along the token axis, as for
+ * ssd_chunk_fwd_varlen): each sequence is convolved on its own, from its own
+ * state_in row, and leaves its own state_out row.
+ *   cu_seqlens (nseq + 1)  int32, HOST memory: sequence b holds the token rows
+ *                          cu_seqlens[b] .. cu_seqlens[b+1]-1 (cu_seqlens[0] =
+ *                          0, non-decreasing; empty sequences allowed: their
+ *                          state_out is their state_in); 1 <= nseq <= 65535
+ *   xbc        (Ttot, ld)  as in ssd_conv1d_fwd, Ttot = cu_seqlens[nseq]
+ *   x, B, C    (Ttot, HP), (Ttot, GN), (Ttot, GN)
+ *   state_in, state_out (nseq, 3, Ch) float32 or NULL
+ *   workspace  of ssd_conv1d_varlen_workspace_size(nseq) bytes (the device
+ *              copy of cu_seqlens, written on `stream` from pageable memory;
+ *              cu_seqlens may be reused once the call returns)
+ * Each sequence's result equals ssd_conv1d_fwd on it alone, bit for bit.
+ * Other arguments and errors as in ssd_conv1d_fwd (the 32-bit addressing
+ * limit applies to the longest sequence); invalid cu_seqlens: SSD_EINVAL.
+ */
+size_t ssd_conv1d_varlen_workspace_size(int nseq);
+int ssd_conv1d_fwd_varlen(const void *xbc, long long ld, const float *w, const float *bias,
+                          const float *state_in, int act, void *x, void *B, void *C,
+                          float *state_out, const int *cu_seqlens, int nseq, int HP, int GN,
+                          int K, int dtype, void *workspace, size_t workspace_bytes,
+                          void *stream);
+/* the same with the 2 measurement events of ssd_conv1d_fwd_ev */
+int ssd_conv1d_fwd_varlen_ev(const void *xbc, long long ld, const float *w, const float *bias,
+                             const float *state_in, int act, void *x, void *B, void *C,
+                             float *state_out, const int *cu_seqlens, int nseq, int HP, int GN,
+                             int K, int dtype, void *workspace, size_t workspace_bytes,
+                             void *stream, void *const *events);
+
+/*
  * Measurement variant of ssd_conv1d_fwd: identical arguments, kernel and
  * result, plus `events`, 2 hipEvent_t (passed as void*) bound to the kernel's
  * dispatch on `stream` (start, stop), or NULL.

@@ -260,6 +260,25 @@ def conv1d(xbc, w, bias=None, state_in=None, act=1, ch=None):
     return out, st
 
 
+def conv1d_varlen(xbc, w, cu_seqlens, bias=None, state_in=None, act=1, ch=None):
+    """The convolution over a variable-length batch: sequence b holds rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 of xbc (Ttot,ld) and is ``conv1d`` on
+    that slice alone from state_in[b] (state_in (nseq,K-1,ch) or None).
+    Returns (out (Ttot,ch), state_out (nseq,K-1,ch)) as float64."""
+    cu = [int(v) for v in cu_seqlens]
+    nseq = len(cu) - 1
+    ch = xbc.shape[1] if ch is None else int(ch)
+    K = w.shape[1]
+    out = np.empty((xbc.shape[0], ch), np.float64)
+    st = np.empty((nseq, K - 1, ch), np.float64)
+    for b in range(nseq):
+        lo, hi = cu[b], cu[b + 1]
+        ob, sb = conv1d(xbc[None, lo:hi], w, bias, None if state_in is None else state_in[b:b + 1], act, ch)
+        out[lo:hi] = ob[0]
+        st[b] = sb[0]
+    return out, st
+
+
 def conv1d_step(state, xt, w, bias=None, act=1):
     """One decode step of the convolution: the segment of length 1.  state
     (Bsz,K-1,ch) float32 inputs that preceded the token, xt (Bsz,ch) float32.

@@ -93,6 +93,12 @@ def lib():
     L.ssd_complex_chunk_bwd_ev.argtypes = L.ssd_complex_chunk_bwd.argtypes + [P]
     L.ssd_conv1d_fwd.restype = I
     L.ssd_conv1d_fwd.argtypes = [P, LL, P, P, P, I, P, P, P, P, I, I, I, I, I, I, P]
+    L.ssd_conv1d_varlen_workspace_size.restype = S
+    L.ssd_conv1d_varlen_workspace_size.argtypes = [I]
+    L.ssd_conv1d_fwd_varlen.restype = I
+    L.ssd_conv1d_fwd_varlen.argtypes = [P, LL, P, P, P, I, P, P, P, P, P, I, I, I, I, I, P, S, P]
+    L.ssd_conv1d_fwd_varlen_ev.restype = I
+    L.ssd_conv1d_fwd_varlen_ev.argtypes = L.ssd_conv1d_fwd_varlen.argtypes + [P]
     L.ssd_conv1d_fwd_ev.restype = I
     L.ssd_conv1d_fwd_ev.argtypes = L.ssd_conv1d_fwd.argtypes + [P]
     L.ssd_linear_fwd.restype = I
@@ -451,6 +457,56 @@ def _rows(t, name, ndim):
     if ndim == 3 and t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) != t.shape[1] * ld:
         raise ValueError(f"{name}: batch entries must follow each other (stride T*ld)")
     return ld
+
+
+def ssd_conv1d_fwd_varlen(xbc, w, HP, GN, cu_seqlens, bias=None, state_in=None, act=1, x=None,
+                          B=None, C=None, state_out=None, workspace=None, stream=None):
+    """The convolution over a variable-length batch: xbc (Ttot,Ch) rows (or a
+    column slice of wider rows) of nseq packed sequences, sequence b on rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 (cu_seqlens a host array of nseq+1
+    ints); state_in/state_out (nseq,3,Ch).  Returns (x, B, C, state_out)."""
+    cu = _cu_host(cu_seqlens)
+    nseq = cu.size - 1
+    _ndim(xbc, "xbc", 2)
+    Ttot, Ch = xbc.shape
+    if int(cu[-1]) != Ttot:
+        raise ValueError(f"cu_seqlens[-1] = {int(cu[-1])} but xbc has {Ttot} token rows")
+    if Ch != HP + 2 * GN:
+        raise ValueError(f"xbc has {Ch} channels, HP + 2*GN = {HP + 2 * GN}")
+    _ndim(w, "w", 2)
+    K = w.shape[1]
+    _expect(w, "w", (Ch, K), xbc)
+    _expect(bias, "bias", (Ch,), xbc)
+    _expect(state_in, "state_in", (nseq, K - 1, Ch), xbc)
+    _expect(state_out, "state_out", (nseq, K - 1, Ch), xbc)
+    _expect(x, "x", (Ttot, HP), xbc)
+    _expect(B, "B", (Ttot, GN), xbc)
+    _expect(C, "C", (Ttot, GN), xbc)
+    ld = _rows(xbc, "xbc", 2)
+    if xbc.dtype == torch.bfloat16:
+        dtype = SSD_BF16
+    elif xbc.dtype == torch.float32:
+        dtype = SSD_F32
+    else:
+        raise TypeError("xbc must be float32 or bfloat16")
+    _dev(w, "w", torch.float32)
+    _dev(bias, "bias", torch.float32)
+    _dev(state_in, "state_in", torch.float32)
+    dev = xbc.device
+    x = torch.empty((Ttot, HP), dtype=xbc.dtype, device=dev) if x is None else x
+    B = torch.empty((Ttot, GN), dtype=xbc.dtype, device=dev) if B is None else B
+    C = torch.empty((Ttot, GN), dtype=xbc.dtype, device=dev) if C is None else C
+    if state_out is None:
+        state_out = torch.empty((nseq, K - 1, Ch), dtype=torch.float32, device=dev)
+    for t, n in ((x, "x"), (B, "B"), (C, "C")):
+        _dev(t, n, xbc.dtype)
+    _dev(state_out, "state_out", torch.float32)
+    ws = _workspace(int(lib().ssd_conv1d_varlen_workspace_size(nseq)), dev, workspace)
+    _check(lib().ssd_conv1d_fwd_varlen(_ptr(xbc), ld, _ptr(w), _ptr(bias), _ptr(state_in), int(act),
+                                       _ptr(x), _ptr(B), _ptr(C), _ptr(state_out),
+                                       cu.ctypes.data_as(ctypes.c_void_p), nseq, HP, GN, K, dtype,
+                                       _ptr(ws), ws.numel(), _stream(stream)))
+    return x, B, C, state_out
 
 
 def ssd_conv1d_fwd(xbc, w, HP, GN, bias=None, state_in=None, act=1, x=None, B=None, C=None,

@@ -507,6 +507,65 @@ int ssd_conv1d_fwd_ev(const void* xbc, long long ld, const float* w, const float
   return launch_status(ssd::run_conv1d(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t ssd_conv1d_varlen_workspace_size(int nseq) {
+  if (nseq <= 0 || nseq > 65535) return 0;
+  return (static_cast<size_t>(nseq) + 1) * 4 / 256 * 256 + 256;
+}
+
+int ssd_conv1d_fwd_varlen_ev(const void* xbc, long long ld, const float* w, const float* bias,
+                             const float* state_in, int act, void* x, void* B, void* C,
+                             float* state_out, const int* cu_seqlens, int nseq, int HP, int GN, int K,
+                             int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events) {
+  if (!cu_seqlens) return fail(SSD_EINVAL, "cu_seqlens is NULL");
+  if (nseq <= 0 || nseq > 65535) return fail(SSD_EINVAL, "nseq=%d not in [1, 65535]", nseq);
+  if (cu_seqlens[0] != 0) return fail(SSD_EINVAL, "cu_seqlens: cu_seqlens[0] must be 0");
+  int Tmax = 0;
+  for (int b = 0; b < nseq; ++b) {
+    if (cu_seqlens[b + 1] < cu_seqlens[b]) return fail(SSD_EINVAL, "cu_seqlens: must be non-decreasing");
+    const int t = cu_seqlens[b + 1] - cu_seqlens[b];
+    Tmax = t > Tmax ? t : Tmax;
+  }
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_EUNSUPPORTED, "dtype=%d", dtype);
+  const int V = dtype == SSD_BF16 ? 8 : 4;
+  const long long es = dtype == SSD_BF16 ? 2 : 4;
+  SSD_TRY(check_conv_common(nseq, HP, GN, ld, K, act, V));
+  const int tt = ssd::conv_tokens_per_thread();
+  if ((static_cast<long long>(Tmax) + tt) * ld * es > 4294967295LL - 16)
+    return fail(SSD_EUNSUPPORTED, "one sequence's rows exceed 4 GiB: T=%d ld=%lld", Tmax, ld);
+  if ((static_cast<long long>(Tmax) + 4LL * tt - 1) / (4LL * tt) > 65535)
+    return fail(SSD_EUNSUPPORTED, "a sequence of T=%d is too long", Tmax);
+  const bool has_tokens = cu_seqlens[nseq] > 0;
+  SSD_TRY(check_ptr(xbc, "xbc", 16, has_tokens));
+  SSD_TRY(check_ptr(w, "w", 16, true));
+  SSD_TRY(check_ptr(bias, "bias", 16, false));
+  SSD_TRY(check_ptr(state_in, "state_in", 16, false));
+  SSD_TRY(check_ptr(state_out, "state_out", 16, false));
+  SSD_TRY(check_ptr(x, "x", 16, has_tokens));
+  SSD_TRY(check_ptr(B, "B", 16, has_tokens && GN > 0));
+  SSD_TRY(check_ptr(C, "C", 16, has_tokens && GN > 0));
+  const size_t Ch = static_cast<size_t>(HP) + 2 * static_cast<size_t>(GN);
+  const size_t sbytes = static_cast<size_t>(nseq) * 3 * Ch * 4;
+  if (overlaps(state_in, sbytes, state_out, sbytes))
+    return fail(SSD_EINVAL, "state_in and state_out overlap");
+  SSD_TRY(check_ptr(workspace, "workspace", 256, true));
+  const size_t need = ssd_conv1d_varlen_workspace_size(nseq);
+  if (workspace_bytes < need)
+    return fail(SSD_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  ssd::ConvArgs a{xbc, static_cast<int>(ld), w, bias, state_in, state_out, act, x, B, C,
+                  nseq, Tmax, HP, GN, dtype,
+                  reinterpret_cast<hipEvent_t*>(const_cast<void**>(events))};
+  return launch_status(ssd::run_conv1d_varlen(a, cu_seqlens, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int ssd_conv1d_fwd_varlen(const void* xbc, long long ld, const float* w, const float* bias,
+                          const float* state_in, int act, void* x, void* B, void* C, float* state_out,
+                          const int* cu_seqlens, int nseq, int HP, int GN, int K, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_conv1d_fwd_varlen_ev(xbc, ld, w, bias, state_in, act, x, B, C, state_out, cu_seqlens, nseq,
+                                  HP, GN, K, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
 int ssd_conv1d_step(float* state, const float* xt, long long ld, const float* w,
                     const float* bias, int act, float* x, float* B, float* C, int Bsz, int HP,
                     int GN, int K, void* stream) {

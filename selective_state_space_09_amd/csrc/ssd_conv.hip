@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void ssd_conv1d_kernel(
     const TIn* __restrict__ xbc, int ld, const float* __restrict__ w,
     const float* __restrict__ bias, const float* __restrict__ state_in, TIn* __restrict__ xo,
     TIn* __restrict__ bo, TIn* __restrict__ co, float* __restrict__ state_out, int T, int HP,
-    int GN) {
+    int GN, const int* __restrict__ cu) {
   using CV = ConvVec<TIn>;
   constexpr int V = CV::V;
   constexpr int ES = sizeof(TIn);
@@ -102,6 +102,13 @@ __global__ __launch_bounds__(256) void ssd_conv1d_kernel(
   const bool active = vec * V < Ch;
   const int c0 = active ? vec * V : 0;
   const int b = blockIdx.z;
+  // the sequence's rows: b of Bsz sequences of T tokens, or (variable
+  // lengths) the rows cu[b] .. cu[b+1]-1 of the packed batch
+  size_t row0 = static_cast<size_t>(b) * T;
+  if (cu) {
+    row0 = static_cast<size_t>(cu[b]);
+    T = cu[b + 1] - cu[b];
+  }
   const int run = blockIdx.y * kRunsPerBlock + wave_id();
   const int t0 = run * kConvTT;
   const int nruns = T > 0 ? (T + kConvTT - 1) / kConvTT : 1;
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(256) void ssd_conv1d_kernel(
 
   // the 3 positions before the run: positions >= 0 from the rows, < 0 from
   // the carried state (a NULL state is an empty range: zeros)
-  const buf_t xb = make_buf(xbc + static_cast<size_t>(b) * T * ld,
+  const buf_t xb = make_buf(xbc + row0 * ld,
                             static_cast<uint32_t>(static_cast<size_t>(T) * ld * ES));
   const buf_t sb = make_buf(state_in + static_cast<size_t>(b) * (kConvK - 1) * Ch,
                             state_in ? static_cast<uint32_t>(kConvK - 1) * Ch * 4 : 0u);
@@ -175,11 +182,11 @@ __global__ __launch_bounds__(256) void ssd_conv1d_kernel(
   }
 
   // outputs of this batch entry; rows at or past T are out of range
-  const buf_t xob = make_buf(xo + static_cast<size_t>(b) * T * HP,
+  const buf_t xob = make_buf(xo + row0 * HP,
                              static_cast<uint32_t>(static_cast<size_t>(T) * HP * ES));
-  const buf_t bob = make_buf(bo + static_cast<size_t>(b) * T * GN,
+  const buf_t bob = make_buf(bo + row0 * GN,
                              static_cast<uint32_t>(static_cast<size_t>(T) * GN * ES));
-  const buf_t cob = make_buf(co + static_cast<size_t>(b) * T * GN,
+  const buf_t cob = make_buf(co + row0 * GN,
                              static_cast<uint32_t>(static_cast<size_t>(T) * GN * ES));
   // a block whose vectors all lie in x issues one store per token; the block
   // holding the x|B|C boundary issues three, each lane's offset in range for
@@ -305,8 +312,10 @@ __global__ __launch_bounds__(256) void ssd_conv1d_step_kernel(
   }
 }
 
+// cu: the device copy of the sequence offsets (variable lengths; a.Bsz
+// sequences, a.T the longest), or NULL
 template <typename TIn>
-void launch_conv(const ConvArgs& a, hipStream_t st) {
+void launch_conv(const ConvArgs& a, hipStream_t st, const int* cu) {
   constexpr int V = ConvVec<TIn>::V;
   const int Ch = a.HP + 2 * a.GN;
   const int nvec = Ch / V;
@@ -318,10 +327,10 @@ void launch_conv(const ConvArgs& a, hipStream_t st) {
   TIn* co = static_cast<TIn*>(a.C);
   if (a.act)
     launch_k(true, ssd_conv1d_kernel<TIn, true>, grid, dim3(kThreads), st, a.events, x, a.ld, a.w,
-             a.bias, a.state_in, xo, bo, co, a.state_out, a.T, a.HP, a.GN);
+             a.bias, a.state_in, xo, bo, co, a.state_out, a.T, a.HP, a.GN, cu);
   else
     launch_k(true, ssd_conv1d_kernel<TIn, false>, grid, dim3(kThreads), st, a.events, x, a.ld,
-             a.w, a.bias, a.state_in, xo, bo, co, a.state_out, a.T, a.HP, a.GN);
+             a.w, a.bias, a.state_in, xo, bo, co, a.state_out, a.T, a.HP, a.GN, cu);
 }
 
 }  // namespace
@@ -330,9 +339,23 @@ int conv_tokens_per_thread() { return kConvTT; }
 
 hipError_t run_conv1d(const ConvArgs& a, hipStream_t st) {
   if (a.dtype == 1)
-    launch_conv<uint16_t>(a, st);
+    launch_conv<uint16_t>(a, st, nullptr);
   else
-    launch_conv<float>(a, st);
+    launch_conv<float>(a, st, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t run_conv1d_varlen(const ConvArgs& a, const int* cu, void* workspace, hipStream_t st) {
+  // the offsets go to the workspace (the call returns once the copy has the
+  // host data); a.Bsz = nseq, a.T = the longest sequence
+  hipError_t e = hipMemcpyAsync(workspace, cu, (static_cast<size_t>(a.Bsz) + 1) * sizeof(int),
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return e;
+  const int* cud = static_cast<const int*>(workspace);
+  if (a.dtype == 1)
+    launch_conv<uint16_t>(a, st, cud);
+  else
+    launch_conv<float>(a, st, cud);
   return hipGetLastError();
 }
 

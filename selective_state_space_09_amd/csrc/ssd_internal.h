@@ -183,6 +183,9 @@ Bf16FwdLayout bf16_varlen_layout(const VarlenPlan& p, int H, int P, int N, int c
 hipError_t run_chunk_varlen_bf16(const ChunkArgs& a, const VarlenPlan& p, const int* cu, hipStream_t st);
 
 hipError_t run_chunk_real(const ChunkArgs& a, hipStream_t st);
+// the convolution over a variable-length batch: a.Bsz = nseq sequences, a.T
+// the longest; cu the host offsets, copied to `workspace` ((nseq+1) ints)
+hipError_t run_conv1d_varlen(const ConvArgs& a, const int* cu, void* workspace, hipStream_t st);
 hipError_t run_chunk_real_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_complex(const ChunkArgs& a, hipStream_t st);
 // a.x = the in_proj rows (Bsz, T, ld): [x | B_re | B_im | C_re | C_im | dt], G = H

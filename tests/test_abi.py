@@ -311,3 +311,27 @@ def test_varlen_rejects_without_device_use():
     one = ssd.ssd_varlen_workspace_size([0, 512], 4, 64, 1, 128, 256)
     many = ssd.ssd_varlen_workspace_size([0] + list(range(1, 513)), 4, 64, 1, 128, 256)
     assert many > one
+
+
+def test_conv_varlen_rejects_without_device_use():
+    import numpy as np
+    L = ssd.lib()
+
+    def call(cu, ws=1 << 20, K=4, x=GOOD):
+        cu = np.ascontiguousarray(cu, np.int32)
+        rc = L.ssd_conv1d_fwd_varlen(x, 384, GOOD, None, None, 1, GOOD, GOOD, GOOD, None,
+                                     cu.ctypes.data_as(ctypes.c_void_p), cu.size - 1, 256, 64, K,
+                                     ssd.SSD_BF16, GOOD, ws, None)
+        return rc, L.ssd_last_error().decode()
+    rc, msg = call([2, 5])
+    assert rc == ssd.SSD_EINVAL and "cu_seqlens[0]" in msg
+    rc, msg = call([0, 5, 4])
+    assert rc == ssd.SSD_EINVAL and "non-decreasing" in msg
+    rc, msg = call([0, 5, 9], ws=0)
+    assert rc == ssd.SSD_EWORKSPACE
+    rc, msg = call([0, 5, 9], K=3)
+    assert rc == ssd.SSD_EUNSUPPORTED
+    rc, msg = call([0, 5, 9], x=MISALIGNED)
+    assert rc == ssd.SSD_EINVAL and "xbc" in msg
+    assert ssd.lib().ssd_conv1d_varlen_workspace_size(3) >= 16
+    assert ssd.lib().ssd_conv1d_varlen_workspace_size(0) == 0

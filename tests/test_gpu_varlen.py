@@ -154,3 +154,92 @@ def test_varlen_prefill_then_decode():
     eh = _metrics.state_err(h.cpu().numpy(), rh)
     print(f"prefill -> decode: y {ey:.2e}  state {eh:.2e}", flush=True)
     assert ey <= TOL and eh <= TOL
+
+
+# ---- the convolution over a variable-length batch ----
+
+def _conv_case(lengths, HP, GN, ld, dtype, seed):
+    d = inputs.make_conv(1, int(sum(lengths)), HP, GN, ld=ld, dtype=dtype, seed=seed, with_state=False)
+    rng = np.random.default_rng(seed + 1)
+    d["xbc"] = np.ascontiguousarray(d["xbc"][0])
+    d["state_in"] = rng.standard_normal((len(lengths), 3, HP + 2 * GN)).astype(np.float32)
+    d["cu"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return d
+
+
+def _conv_bar(got, ref, dtype, what):
+    rel, ab = (2.0 ** -8, 2e-5) if dtype == "bf16" else (2e-6, 2e-5)
+    bad = np.argwhere(np.abs(got - ref) > rel * np.abs(ref) + ab)
+    assert bad.size == 0, (what, len(bad), tuple(bad[0]))
+
+
+def _conv_gpu(d, HP, GN, act=1):
+    Ch = HP + 2 * GN
+    xb = _gpu.to_dev(d["xbc"])[:, :Ch]  # a column slice of the wider rows
+    x, B, C, so = ssd.ssd_conv1d_fwd_varlen(xb, _gpu.to_dev(d["w"]), HP, GN, d["cu"],
+                                            bias=_gpu.to_dev(d["bias"]), state_in=_gpu.to_dev(d["state_in"]),
+                                            act=act)
+    torch.cuda.synchronize()
+    return x, B, C, so
+
+
+CONV_CASES = [
+    # lengths, HP, GN, ld, dtype
+    ([0, 1, 2, 3, 5, 8, 9, 100, 17], 256, 64, 400, "bf16"),
+    ([33, 0, 70, 1], 512, 64, 640, "f32"),
+]
+
+
+@pytest.mark.parametrize("lengths,HP,GN,ld,dtype", CONV_CASES)
+def test_conv_varlen_matches_oracle(lengths, HP, GN, ld, dtype):
+    print(f"conv varlen lengths={lengths} HP={HP} GN={GN} {dtype}", flush=True)
+    d = _conv_case(lengths, HP, GN, ld, dtype, seed=len(lengths) + HP)
+    Ch = HP + 2 * GN
+    ref, rst = oracle.conv1d_varlen(d["xbc"], d["w"], d["cu"], d["bias"], d["state_in"], act=1, ch=Ch)
+    x, B, C, so = _conv_gpu(d, HP, GN)
+    _conv_bar(_gpu.to_host64(x), ref[:, :HP], dtype, "x")
+    _conv_bar(_gpu.to_host64(B), ref[:, HP:HP + GN], dtype, "B")
+    _conv_bar(_gpu.to_host64(C), ref[:, HP + GN:], dtype, "C")
+    np.testing.assert_array_equal(_gpu.to_host64(so), rst)
+
+
+def test_conv_varlen_equal_lengths_is_the_batched_conv_bit_for_bit():
+    L, nseq, HP, GN = 45, 3, 128, 32
+    print("conv varlen equal lengths vs batched", flush=True)
+    d = _conv_case([L] * nseq, HP, GN, None, "bf16", seed=8)
+    x, B, C, so = _conv_gpu(d, HP, GN)
+    xb = _gpu.to_dev(d["xbc"]).view(nseq, L, -1)
+    xr, Br, Cr, sr = ssd.ssd_conv1d_fwd(xb, _gpu.to_dev(d["w"]), HP, GN, bias=_gpu.to_dev(d["bias"]),
+                                        state_in=_gpu.to_dev(d["state_in"]), act=1)
+    torch.cuda.synchronize()
+    for a, r in ((x, xr), (B, Br), (C, Cr)):
+        assert torch.equal(a.view(torch.int16), r.reshape(a.shape).view(torch.int16))
+    assert torch.equal(so, sr)
+
+
+def test_mamba2_layer_prefill_varlen_conv_then_scan():
+    """The prefill of a Mamba-2 layer over a variable-length batch: the
+    convolution's x, B, C (bf16, packed) feed the scan directly.  Against the
+    oracle convolution, rounded to bf16, fed to the oracle scan (a value on a
+    bf16 rounding boundary may land one step apart on the two sides, far
+    inside the scan's bar)."""
+    lengths, H, P, G, N = [130, 0, 7, 300, 64], 4, 64, 1, 128
+    HP, GN = H * P, G * N
+    print(f"mamba-2 prefill varlen lengths={lengths}", flush=True)
+    d = _conv_case(lengths, HP, GN, None, "bf16", seed=31)
+    x, B, C, so = _conv_gpu(d, HP, GN)
+    r = inputs.make_varlen(lengths, H, P, N, G=G, dtype="bf16", seed=32, with_h0=True)
+    dd = _gpu.upload(r)
+    Ttot = int(d["cu"][-1])
+    y, hf = ssd.ssd_chunk_fwd_varlen(x.view(Ttot, H, P), dd["dt"], dd["A"], B.view(Ttot, G, N),
+                                     C.view(Ttot, G, N), d["cu"], dd["D"], dd["dt_bias"], r["dt_min"],
+                                     r["dt_max"], dd["h0"], chunk=64, return_final_state=True)
+    torch.cuda.synchronize()
+    out, _ = oracle.conv1d_varlen(d["xbc"], d["w"], d["cu"], d["bias"], d["state_in"], act=1)
+    q = inputs.f32_to_bf16_bits(out.astype(np.float32))
+    xr = np.ascontiguousarray(q[:, :HP]).reshape(Ttot, H, P)
+    Br = np.ascontiguousarray(q[:, HP:HP + GN]).reshape(Ttot, G, N)
+    Cr = np.ascontiguousarray(q[:, HP + GN:]).reshape(Ttot, G, N)
+    ry, rh = oracle.fwd_varlen(xr, r["dt"], r["A"], Br, Cr, d["cu"], r["D"], r["dt_bias"], r["dt_min"],
+                               r["dt_max"], r["h0"])
+    _check(_gpu.to_host64(y), _gpu.to_host64(hf), ry, rh, d["cu"], "mamba-2 prefill varlen")

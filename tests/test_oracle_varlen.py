@@ -69,3 +69,48 @@ def test_cut_and_chained_sequence_equals_the_uncut_one():
     scale = np.abs(y).max()
     assert np.abs(y2 - y[10:]).max() <= 1e-6 * scale
     assert np.abs(h2 - hf).max() <= 1e-6 * np.abs(hf).max()
+
+
+# ---- the convolution over a variable-length batch (oracle.conv1d_varlen) ----
+
+def _conv_inputs(lengths, Ch=24, seed=0):
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    xbc = rng.standard_normal((int(cu[-1]), Ch)).astype(np.float32)
+    w = rng.uniform(-0.5, 0.5, size=(Ch, 4)).astype(np.float32)
+    bias = rng.uniform(-0.5, 0.5, size=Ch).astype(np.float32)
+    st = rng.standard_normal((len(lengths), 3, Ch)).astype(np.float32)
+    return xbc, w, bias, st, cu
+
+
+def test_conv_varlen_equal_lengths_reduce_to_the_batched_form():
+    L, nseq = 11, 3
+    xbc, w, bias, st, cu = _conv_inputs([L] * nseq, seed=1)
+    out, so = oracle.conv1d_varlen(xbc, w, cu, bias, st)
+    ob, sb = oracle.conv1d(xbc.reshape(nseq, L, -1), w, bias, st)
+    np.testing.assert_array_equal(out, ob.reshape(out.shape))
+    np.testing.assert_array_equal(so, sb)
+
+
+def test_conv_varlen_sequences_do_not_interact_and_empty_keeps_state():
+    xbc, w, bias, st, cu = _conv_inputs([5, 0, 2, 7], seed=2)
+    out, so = oracle.conv1d_varlen(xbc, w, cu, bias, st)
+    np.testing.assert_array_equal(so[1], st[1].astype(np.float64))
+    x2 = xbc.copy()
+    x2[cu[2]:cu[3]] += 1.0  # the third sequence only
+    out2, so2 = oracle.conv1d_varlen(x2, w, cu, bias, st)
+    np.testing.assert_array_equal(out2[:cu[2]], out[:cu[2]])
+    np.testing.assert_array_equal(out2[cu[3]:], out[cu[3]:])
+    np.testing.assert_array_equal(so2[[0, 1, 3]], so[[0, 1, 3]])
+    assert np.abs(out2[cu[2]:cu[3]] - out[cu[2]:cu[3]]).max() > 1e-3
+
+
+def test_conv_varlen_cut_and_chained_equals_uncut():
+    """a sequence of 9 rows vs. its first 4 and last 5 as two calls chained
+    through the carried state (raw inputs, so exactly)"""
+    xbc, w, bias, st, cu = _conv_inputs([9], seed=3)
+    out, so = oracle.conv1d_varlen(xbc, w, cu, bias, st)
+    o1, s1 = oracle.conv1d_varlen(xbc[:4], w, [0, 4], bias, st)
+    o2, s2 = oracle.conv1d_varlen(xbc[4:], w, [0, 5], bias, s1.astype(np.float32))
+    np.testing.assert_array_equal(np.concatenate([o1, o2]), out)
+    np.testing.assert_array_equal(s2, so)
