@@ -654,6 +654,8 @@ def bench_varlen(args, cfg):
         out["cpu_baseline"] = {"value": Ttot * (nh / H) / t_run, "unit": "tokens/s",
                                "cores": oracle.threads_used(), "kind": "oracle",
                                "sample": f"every sequence, the first {nh} of {H} heads, float64"}
+    if args.copy_ref:
+        copy_counter_reference(torch, dev)
     print(json.dumps(out), flush=True)
 
 
@@ -1152,6 +1154,8 @@ def bench_bwd_complex(args, cfg):
             "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"one of the {Bsz} sequences ({H} complex recurrences of T={T}, float64 "
                       f"adjoint), {reps} runs in {total:.2f} s; tokens/s of that sequence"}
+    if args.copy_ref:
+        copy_counter_reference(torch, dev)
     print(json.dumps(out), flush=True)
 
 
