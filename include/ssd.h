@@ -413,7 +413,7 @@ int ssd_conv1d_step_ev(float *state, const float *xt, long long ld, const float 
  * Built for dtype SSD_BF16 with P in {32, 64}, N in {64, 128}, chunk in
  * {64, 128, 256}, and for dtype SSD_F32 (x, B, C, dy and dx float32; fp32
  * matrix products) with P in {32, 64}, N in {32, 64, 128} and chunk 64
- * (SSD_EUNSUPPORTED otherwise; the fp32 backward has no measurement events).
+ * (SSD_EUNSUPPORTED otherwise).
  * dB, dC, dh0, h0 and dh_final 16-byte aligned.  Outputs are overwritten, not
  * accumulated, and must not overlap inputs.  Errors as for ssd_chunk_fwd.
  * Workspace: ssd_bwd_workspace_size (SSD_BF16) or ssd_bwd_workspace_size_f32.
