@@ -40,7 +40,10 @@
 // Kernels (one workgroup per (chunk, head, batch) unless noted):
 //   ssd_cplx_u_local, ssd_cplx_rotate  (complex) u and theta over the sequence
 //                         (fp64: chunk sums, then each chunk adds the totals of the
-//                         earlier ones), B_eff, C_eff, the rotated h0 and dh_final
+//                         earlier ones), (cos, sin) theta per token, the rotated h0
+//                         and dh_final; B_eff and C_eff are never stored: the
+//                         chunk-state and block kernels form them from B and C as
+//                         they stage them
 //   chunk states, state passing, adjoint chunk states: ssd_chunk.hip's fp32
 //                         kernels (run_states_f32, run_pass_f32)
 //   ssd_f32_adj_pass      R_c in place over G_c, last chunk first; dh0
@@ -96,6 +99,34 @@ __device__ __forceinline__ void stage(float* tile, int pitch, const float* __res
     const float4 val = r < valid ? *reinterpret_cast<const float4*>(src + r * ld + v * 4)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
     *reinterpret_cast<float4*>(tile + r * pitch + v * 4) = val;
+  }
+}
+
+// the same for complex rows (W/2 (re, im) pairs per row), rotated per row r by
+// (cos, sin) theta = rc[r * rstride] into the W real features [Re | Im] of
+// z e^{-i theta} (CONJ = false) or [Re | -Im] of z e^{+i theta} (CONJ = true)
+template <int W, int NTHR, bool CONJ>
+__device__ __forceinline__ void stage_rot(float* tile, int pitch, const float* __restrict__ src, size_t ld,
+                                          int rows, int valid, const float2* __restrict__ rc,
+                                          size_t rstride) {
+  constexpr int NH = W / 2;
+  for (int i = threadIdx.x; i < rows * (W / 4); i += NTHR) {
+    const int r = i / (W / 4), v = i % (W / 4);
+    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+    float2 cs = make_float2(1.f, 0.f);
+    if (r < valid) {
+      val = *reinterpret_cast<const float4*>(src + r * ld + v * 4);
+      cs = rc[r * rstride];
+    }
+    float* t = tile + r * pitch + 2 * v;
+    if constexpr (!CONJ) {
+      *reinterpret_cast<float2*>(t) = make_float2(val.x * cs.x + val.y * cs.y, val.z * cs.x + val.w * cs.y);
+      *reinterpret_cast<float2*>(t + NH) = make_float2(val.y * cs.x - val.x * cs.y, val.w * cs.x - val.z * cs.y);
+    } else {
+      *reinterpret_cast<float2*>(t) = make_float2(val.x * cs.x - val.y * cs.y, val.z * cs.x - val.w * cs.y);
+      *reinterpret_cast<float2*>(t + NH) =
+          make_float2(-(val.y * cs.x + val.x * cs.y), -(val.w * cs.x + val.z * cs.y));
+    }
   }
 }
 
@@ -161,8 +192,15 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
   const float dt_raw = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
   stage<P, kT8>(Xs, XP, x + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
   stage<P, kT8>(Ys, XP, dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  stage<NE, kT8>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
-  stage<NE, kT8>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  if constexpr (CPLX) {
+    stage_rot<NE, kT8, false>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc,
+                              rot + r0 * H + h, H);
+    stage_rot<NE, kT8, true>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc,
+                             rot + r0 * H + h, H);
+  } else {
+    stage<NE, kT8>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+    stage<NE, kT8>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  }
   stage<NE, kT8>(Rs, NP, adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE),
                  NE, P, P);
   chunk_prologue(dt_raw, Lc, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, dl, cs_hi, cs_lo, wsum,
@@ -350,8 +388,15 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
   const float dt_raw = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
   stage<P, kT8>(Xs, XP, x + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
   stage<P, kT8>(Ys, XP, dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  stage<NE, kT8>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
-  stage<NE, kT8>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  if constexpr (CPLX) {
+    stage_rot<NE, kT8, false>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc,
+                              rot + r0 * H + h, H);
+    stage_rot<NE, kT8, true>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc,
+                             rot + r0 * H + h, H);
+  } else {
+    stage<NE, kT8>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+    stage<NE, kT8>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  }
   stage<NE, kT8>(Hs, NP, states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE),
                  NE, P, P);
   chunk_prologue(dt_raw, Lc, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, dl, cs_hi, cs_lo, wsum,
@@ -525,14 +570,14 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_const_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Complex: rotation of the inputs into the sequence frame.  u_t = delta_1 + ..
-// + delta_t over the sequence (fp64) in two steps: each chunk's local sums and
-// total (ssd_cplx_u_local), then each chunk adds the totals of the chunks
-// before it (ssd_cplx_rotate, one workgroup per (chunk, head, batch)), forms
-// theta_t = beta u_t mod 2 pi, keeps (cos, sin) theta_t per token and head,
-// and writes B_eff, C_eff (Bsz, T, H, 2N); the last chunk's workgroup turns
-// h0 into [Re | Im] rows and dh_final, rotated by -theta at the last token,
-// likewise; the decay alpha of each head.
+// Complex: the sequence frame.  u_t = delta_1 + .. + delta_t over the
+// sequence (fp64) in two steps: each chunk's local sums and total
+// (ssd_cplx_u_local), then each chunk adds the totals of the chunks before it
+// (ssd_cplx_rotate, one workgroup per (chunk, head, batch)) and keeps
+// (cos, sin) theta_t, theta_t = beta u_t mod 2 pi, per token and head (the
+// kernels that read B and C rotate them by it as they stage them); the last
+// chunk's workgroup turns h0 into [Re | Im] rows and dh_final, rotated by
+// -theta at the last token, likewise; the decay alpha of each head.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kQ) void ssd_cplx_u_local_kernel(
     const float* __restrict__ dt, const float* __restrict__ dt_bias, float dt_min, float dt_max,
@@ -549,15 +594,12 @@ __global__ __launch_bounds__(kQ) void ssd_cplx_u_local_kernel(
 }
 
 __global__ __launch_bounds__(kThreads) void ssd_cplx_rotate_kernel(
-    const float* __restrict__ A, const float* __restrict__ Bm, const float* __restrict__ Cm,
-    const float* __restrict__ h0, const float* __restrict__ dh_final, double* __restrict__ uo,
-    const double* __restrict__ ctot, float2* __restrict__ rot, float* __restrict__ Beff,
-    float* __restrict__ Ceff, float* __restrict__ alpha, float* __restrict__ h0e,
-    float* __restrict__ dhfe, int T, int H, int G, int P, int N, int nc) {
-  __shared__ float cth[kQ], sth[kQ];
+    const float* __restrict__ A, const float* __restrict__ h0, const float* __restrict__ dh_final,
+    double* __restrict__ uo, const double* __restrict__ ctot, float2* __restrict__ rot,
+    float* __restrict__ alpha, float* __restrict__ h0e, float* __restrict__ dhfe, int T, int H, int P,
+    int N, int nc) {
   __shared__ double u_last;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
   const int tid = threadIdx.x;
   const int t0 = c * kQ, Lc = max(0, min(kQ, T - t0));
   const float be = A[2 * h + 1];
@@ -569,34 +611,17 @@ __global__ __launch_bounds__(kThreads) void ssd_cplx_rotate_kernel(
     pre = __shfl(wave_inclusive_sum_d(pre), kQ - 1);
     const size_t row = (static_cast<size_t>(b) * T + t0 + (tid < Lc ? tid : 0)) * H + h;
     const double u = tid < Lc ? uo[row] + pre : pre;
-    float cs = 1.0f, sn = 0.0f;
     if (tid < Lc) {
       uo[row] = u;
+      float cs, sn;
       rot_cs(static_cast<double>(be) * u, cs, sn);
       rot[row] = make_float2(cs, sn);
     }
-    cth[tid] = cs;
-    sth[tid] = sn;
     if (tid == (Lc > 0 ? Lc - 1 : 0)) u_last = Lc > 0 ? u : 0.0;
   }
-  __syncthreads();
-  // rotated features, two n per thread: B' = B e^{-i theta}, C' = C e^{i theta}
-  const int NE = 2 * N, half = N / 2;
-  for (int i = tid; i < Lc * half; i += kThreads) {
-    const int tl = i / half, n = 2 * (i % half);
-    const size_t rr = static_cast<size_t>(b) * T + t0 + tl;
-    const float4 bv = *reinterpret_cast<const float4*>(Bm + ((rr * G + g) * N + n) * 2);
-    const float4 cv = *reinterpret_cast<const float4*>(Cm + ((rr * G + g) * N + n) * 2);
-    const float co = cth[tl], si = sth[tl];
-    float* be_row = Beff + (rr * H + h) * NE;
-    float* ce_row = Ceff + (rr * H + h) * NE;
-    *reinterpret_cast<float2*>(be_row + n) = make_float2(bv.x * co + bv.y * si, bv.z * co + bv.w * si);
-    *reinterpret_cast<float2*>(be_row + N + n) = make_float2(bv.y * co - bv.x * si, bv.w * co - bv.z * si);
-    *reinterpret_cast<float2*>(ce_row + n) = make_float2(cv.x * co - cv.y * si, cv.z * co - cv.w * si);
-    *reinterpret_cast<float2*>(ce_row + N + n) =
-        make_float2(-(cv.y * co + cv.x * si), -(cv.w * co + cv.z * si));
-  }
   if (c != gridDim.x - 1) return;
+  __syncthreads();
+  const int NE = 2 * N;
   // h0 -> [Re | Im] rows; dh_final -> e^{-i theta_{T-1}} dh_final as [Re | Im]
   float cl = 1.0f, sl = 0.0f;
   if (T > 0) rot_cs(static_cast<double>(be) * u_last, cl, sl);
@@ -826,12 +851,11 @@ __global__ __launch_bounds__(kThreads) void ssd_cplx_dh0_kernel(const float* __r
 // Workspace of the fp32 backward (256-byte aligned regions): chunk states
 // (recomputed; h_in over them), decays, adjoint states (R over G), per-head
 // dB and dC, per-token values (f1, f2, col, row, x.v, dy.x, rho_B, rho_C),
-// chunk constants and shares; complex: u, B_eff, C_eff, alpha, rotated h0,
+// chunk constants and shares; complex: u, (cos, sin) theta, chunk step totals, alpha, rotated h0,
 // dh_final and h_final, rho chunk totals.
 // ---------------------------------------------------------------------------
 struct F32BwdLayout {
-  size_t S, dec, adj, dBh, dCh, tokv, cst, part, u, rot, ctot, Beff, Ceff, alpha, h0e, dhfe, hfe, rtot, dh0e,
-      total;
+  size_t S, dec, adj, dBh, dCh, tokv, cst, part, u, rot, ctot, alpha, h0e, dhfe, hfe, rtot, dh0e, total;
 };
 static F32BwdLayout f32_layout(int Bsz, int T, int H, int P, int N, bool cplx) {
   const int NE = cplx ? 2 * N : N;
@@ -854,8 +878,6 @@ static F32BwdLayout f32_layout(int Bsz, int T, int H, int P, int N, bool cplx) {
     L.u = o;     o += up(tok * 8);
     L.rot = o;   o += up(tok * 8);
     L.ctot = o;  o += up(static_cast<size_t>(Bsz) * H * nc * 8);
-    L.Beff = o;  o += up(tok * NE * 4);
-    L.Ceff = o;  o += up(tok * NE * 4);
     L.alpha = o; o += up(static_cast<size_t>(H) * 4);
     L.h0e = o;   o += up(hs);
     L.dhfe = o;  o += up(hs);
@@ -878,8 +900,8 @@ namespace {
 // step sizes, their sums
 template <int P, int NE, bool CPLX>
 hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, const float* A_dt,
-                           const float* dt_bias, float dt_min, float dt_max, const float* Beff,
-                           const float* Ceff, int Geff, const float* dy, const float* D,
+                           const float* dt_bias, float dt_min, float dt_max, const float* Bin,
+                           const float* Cin, int Geff, const float* dy, const float* D,
                            float* dx, float* ddt, float* dA, float* dD, float* ddt_bias, float* dBh,
                            float* dCh, const float2* rot, float* dBo, float* dCo, char* ws,
                            const F32BwdLayout& L, int Bsz, int T, int H, hipStream_t st,
@@ -899,10 +921,10 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
   constexpr bool SCALE = !CPLX;
   const bool run = nc > 0;
   launch_k(run, ssd_f32_col_kernel<P, NE, SCALE, CPLX>, grid, dim3(kT8), st, E(5), x, dt, A_dec,
-           dt_bias, dt_min, dt_max, Beff, Ceff, dy, D, adj, dx, dBh, f2, col, xv, dyx, rhoB, rot, dBo, T, H,
+           dt_bias, dt_min, dt_max, Bin, Cin, dy, D, adj, dx, dBh, f2, col, xv, dyx, rhoB, rot, dBo, T, H,
            Geff, nc);
   launch_k(run, ssd_f32_row_kernel<P, NE, SCALE, CPLX>, grid, dim3(kT8), st, E(6), x, dt, A_dec,
-           dt_bias, dt_min, dt_max, Beff, Ceff, dy, S, dCh, f1, rw, rhoC, rot, dCo, T, H, Geff,
+           dt_bias, dt_min, dt_max, Bin, Cin, dy, S, dCh, f1, rw, rhoC, rot, dCo, T, H, Geff,
            nc);
   launch_k(run, ssd_f32_const_kernel, grid, dim3(kThreads), st, E(7), adj, S, dec, cst, H, P * NE, nc);
   launch_k(CPLX, ssd_cplx_tau_kernel, dim3(H, Bsz), dim3(kThreads), st, E(8),
@@ -938,11 +960,11 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
   const float* C = static_cast<const float*>(a.C);
   const float* dy = static_cast<const float*>(a.dy);
   hipError_t e = run_states_f32(x, a.dt, a.A, B, a.dt_bias, a.dt_min, a.dt_max, S, dec, a.Bsz, a.T, a.H,
-                                P, a.G, N, kQ, 0, st, E(1));
+                                P, a.G, N, kQ, 0, nullptr, st, E(1));
   if (e == hipSuccess) e = run_pass_f32(S, dec, a.h0, nullptr, a.Bsz, a.H, P, N, nc, st, E(2));
   if (e == hipSuccess)
     e = run_states_f32(dy, a.dt, a.A, C, a.dt_bias, a.dt_min, a.dt_max, adj, nullptr, a.Bsz, a.T, a.H, P,
-                       a.G, N, kQ, 2, st, E(3));
+                       a.G, N, kQ, 2, nullptr, st, E(3));
   if (e != hipSuccess) return e;
   launch_k(true, ssd_f32_adj_pass_kernel, dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
            dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), a.dh_final, a.dh0, a.H,
@@ -987,8 +1009,6 @@ static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   float* dec = reinterpret_cast<float*>(ws + L.dec);
   float* adj = reinterpret_cast<float*>(ws + L.adj);
   double* u = reinterpret_cast<double*>(ws + L.u);
-  float* Beff = reinterpret_cast<float*>(ws + L.Beff);
-  float* Ceff = reinterpret_cast<float*>(ws + L.Ceff);
   float* alpha = reinterpret_cast<float*>(ws + L.alpha);
   float* h0e = reinterpret_cast<float*>(ws + L.h0e);
   float* dhfe = reinterpret_cast<float*>(ws + L.dhfe);
@@ -1010,27 +1030,28 @@ static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   }
   const dim3 rgrid(nc > 0 ? nc : 1, a.H, a.Bsz);
   if (e0)
-    hipExtLaunchKernelGGL(ssd_cplx_rotate_kernel, rgrid, dim3(kThreads), 0, st, nullptr, e0[1], 0, a.A, a.B,
-                          a.C, a.h0, a.dh_final, u, static_cast<const double*>(ctot), rot, Beff, Ceff, alpha,
-                          h0e, dhfe, a.T, a.H, a.G, P, N, nc);
+    hipExtLaunchKernelGGL(ssd_cplx_rotate_kernel, rgrid, dim3(kThreads), 0, st, nullptr, e0[1], 0, a.A, a.h0,
+                          a.dh_final, u, static_cast<const double*>(ctot), rot, alpha, h0e, dhfe, a.T, a.H, P,
+                          N, nc);
   else
-    hipLaunchKernelGGL(ssd_cplx_rotate_kernel, rgrid, dim3(kThreads), 0, st, a.A, a.B, a.C, a.h0,
-                       a.dh_final, u, static_cast<const double*>(ctot), rot, Beff, Ceff, alpha, h0e, dhfe,
-                       a.T, a.H, a.G, P, N, nc);
-  // the rotated-frame real problem: per-head features (G = H), decay alpha, input scale 1
-  hipError_t e = run_states_f32(a.x, a.dt, alpha, Beff, a.dt_bias, a.dt_min, a.dt_max, S, dec, a.Bsz, a.T,
-                                a.H, P, a.H, NE, kQ, 1, st, E(1));
+    hipLaunchKernelGGL(ssd_cplx_rotate_kernel, rgrid, dim3(kThreads), 0, st, a.A, a.h0, a.dh_final, u,
+                       static_cast<const double*>(ctot), rot, alpha, h0e, dhfe, a.T, a.H, P, N, nc);
+  // the rotated-frame real problem: 2N features (B and C rotated as they are
+  // staged), decay alpha, input scale 1
+  const float2* rotc = rot;
+  hipError_t e = run_states_f32(a.x, a.dt, alpha, a.B, a.dt_bias, a.dt_min, a.dt_max, S, dec, a.Bsz, a.T,
+                                a.H, P, a.G, NE, kQ, 3, rotc, st, E(1));
   if (e == hipSuccess) e = run_pass_f32(S, dec, h0e, hfe, a.Bsz, a.H, P, NE, nc, st, E(2));
   if (e == hipSuccess)
-    e = run_states_f32(a.dy, a.dt, alpha, Ceff, a.dt_bias, a.dt_min, a.dt_max, adj, nullptr, a.Bsz, a.T,
-                       a.H, P, a.H, NE, kQ, 2, st, E(3));
+    e = run_states_f32(a.dy, a.dt, alpha, a.C, a.dt_bias, a.dt_min, a.dt_max, adj, nullptr, a.Bsz, a.T,
+                       a.H, P, a.G, NE, kQ, 4, rotc, st, E(3));
   if (e != hipSuccess) return e;
   launch_k(true, ssd_f32_adj_pass_kernel, dim3((P * NE / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
            dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), static_cast<const float*>(dhfe),
            dh0e, a.H, P * NE, nc);
   // each head its own group: dB, dC rotated back and written by the block kernels
   const bool direct = a.G == a.H;
-  e = launch_f32_core<P, NE, true>(a.x, a.dt, alpha, a.A, a.dt_bias, a.dt_min, a.dt_max, Beff, Ceff, a.H,
+  e = launch_f32_core<P, NE, true>(a.x, a.dt, alpha, a.A, a.dt_bias, a.dt_min, a.dt_max, a.B, a.C, a.G,
                                    a.dy, nullptr, a.dx, a.ddt, a.dA, nullptr, a.ddt_bias,
                                    reinterpret_cast<float*>(ws + L.dBh), reinterpret_cast<float*>(ws + L.dCh),
                                    rot, direct ? a.dB : nullptr, direct ? a.dC : nullptr, ws, L, a.Bsz, a.T,

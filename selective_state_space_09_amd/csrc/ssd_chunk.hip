@@ -35,6 +35,8 @@
 // HBM latency of stage i+1 overlaps the MFMA work of stage i (double-buffered
 // LDS, one barrier per stage).
 
+#include <type_traits>
+
 #include "ssd_chunk_common.h"
 
 namespace ssd {
@@ -46,6 +48,40 @@ namespace ssd {
 // B slab -> bT[k][s - s0] = w_s B_s[k] (transposed, weighted).
 template <int ST, int N>
 struct StateBSlab : Slab<ST, N / 4, 1> {
+  // complex rows (N / 2 values as (re, im) pairs) rotated per token into the
+  // N real features [Re | Im] of z e^{-i theta} (CONJ = false: B) or
+  // [Re | -Im] of z e^{+i theta} (CONJ = true: C); rc[s] = (cos, sin) theta_s
+  template <bool CONJ>
+  __device__ __forceinline__ void store_rot(float* bT, const float* wre, const float2* rc, int s0,
+                                            int Q) const {
+    constexpr int XP = ST + Pad<float>::row;
+    constexpr int NH = N / 2;
+#pragma unroll
+    for (int i = 0; i < this->PER; ++i) {
+      const int it = threadIdx.x + i * kThreads;
+      if (it >= this->ITEMS) break;
+      const int ng = it % (N / 4), sl = it / (N / 4);
+      const int s = s0 + sl;
+      const float w = s < Q ? wre[s] : 0.f;
+      const float2 r = s < Q ? rc[s] : make_float2(1.f, 0.f);
+      const uint4 u = this->v[i][0];
+      const float re0 = __uint_as_float(u.x), im0 = __uint_as_float(u.y);
+      const float re1 = __uint_as_float(u.z), im1 = __uint_as_float(u.w);
+      const int n = 2 * ng;
+      if constexpr (!CONJ) {
+        bT[(n + 0) * XP + sl] = w * (re0 * r.x + im0 * r.y);
+        bT[(n + 1) * XP + sl] = w * (re1 * r.x + im1 * r.y);
+        bT[(NH + n + 0) * XP + sl] = w * (im0 * r.x - re0 * r.y);
+        bT[(NH + n + 1) * XP + sl] = w * (im1 * r.x - re1 * r.y);
+      } else {
+        bT[(n + 0) * XP + sl] = w * (re0 * r.x - im0 * r.y);
+        bT[(n + 1) * XP + sl] = w * (re1 * r.x - im1 * r.y);
+        bT[(NH + n + 0) * XP + sl] = -w * (im0 * r.x + re0 * r.y);
+        bT[(NH + n + 1) * XP + sl] = -w * (im1 * r.x + re1 * r.y);
+      }
+    }
+  }
+
   __device__ __forceinline__ void store(float* bT, const float* wre, int s0, int Q) const {
     constexpr int XP = ST + Pad<float>::row;
 #pragma unroll
@@ -69,16 +105,23 @@ struct StateBSlab : Slab<ST, N / 4, 1> {
 // (no delta_s on the input term: the rotated-frame form of the complex
 // recurrence).  kStateAdj: the adjoint chunk state of the backward,
 // G_c = sum_l e^{cs_l} dy_l (x) C_l (x = dy, B = C; no decay written).
+// kStateCplxUnit, kStateCplxAdj: kStateFwdUnit and kStateAdj on complex rows
+// (B or C as N / 2 (re, im) pairs) rotated into the sequence frame as they are
+// staged: features [Re B e^{-i theta} | Im B e^{-i theta}], resp.
+// [Re C e^{i theta} | -Im C e^{i theta}], with theta per token from `rot`.
 // NBUF = 1: one stage buffer, for chunks of at most one stage (the backward's
 // 64-token chunks): half the LDS, so that two workgroups share a CU.
-constexpr int kStateFwd = 0, kStateFwdUnit = 1, kStateAdj = 2;
+constexpr int kStateFwd = 0, kStateFwdUnit = 1, kStateAdj = 2, kStateCplxUnit = 3, kStateCplxAdj = 4;
 
 template <int P, int N, int MODE = kStateFwd, int NBUF = 2>
 __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ dt_bias, float dt_min, float dt_max,
     float* __restrict__ states, float* __restrict__ decay, int T, int H, int G, int Q, int nc,
-    int npairs) {
+    int npairs, const float2* __restrict__ rot) {
+  constexpr bool kCplx = MODE == kStateCplxUnit || MODE == kStateCplxAdj;
+  constexpr bool kAdj = MODE == kStateAdj || MODE == kStateCplxAdj;
+  constexpr bool kUnit = MODE == kStateFwdUnit || MODE == kStateCplxUnit;
   // stage length: 64 tokens unless two buffers of that size overflow LDS
   constexpr int ST = 2 * (P + N) * (64 + Pad<float>::row) * 4 + 8192 <= kLdsBytes ? 64 : 32;
   constexpr int XP = ST + Pad<float>::row;
@@ -90,6 +133,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   __shared__ __attribute__((aligned(16))) float bT[NBUF][N * XP];
   __shared__ float dl[TQ], cs_hi[TQ], cs_lo[TQ];
   __shared__ float wre[TQ];
+  __shared__ float2 rcs[kCplx ? TQ : 1];
   __shared__ double wsum[4], tot;
 
   int b, c, h;
@@ -115,26 +159,33 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   xs.load(xbase, xrow, 0, Lc);
   bs.load(bbase, brow, 0, Lc);
 
+  if constexpr (kCplx) {
+    static_assert(NBUF == 1, "complex rows: one stage");
+    if (tid < Q) rcs[tid] = tid < Lc ? rot[dt_base + static_cast<size_t>(tid) * H] : make_float2(1.f, 0.f);
+  }
   const double cum =
       chunk_prologue(dt_raw, Lc, a_re, bias, dt_min, dt_max, dl, cs_hi, cs_lo, wsum, &tot, Q);
   // weight of each source token to the chunk end (the adjoint: from the chunk start)
   const double total = tot;
   if (tid < Q) {
-    if constexpr (MODE == kStateAdj)
+    if constexpr (kAdj)
       wre[tid] = tid < Lc ? __expf(static_cast<float>(cum)) : 0.0f;  // exponent <= 0
-    else if constexpr (MODE == kStateFwdUnit)
+    else if constexpr (kUnit)
       wre[tid] = tid < Lc ? __expf(static_cast<float>(total - cum)) : 0.0f;
     else
       wre[tid] = __expf(static_cast<float>(total - cum)) * dl[tid];
   }
-  if (MODE != kStateAdj && tid == 0) {
+  if (!kAdj && tid == 0) {
     float* dc = decay + ((static_cast<size_t>(b) * H + h) * nc + c) * 2;
     dc[0] = __expf(static_cast<float>(total));
     dc[1] = 0.0f;
   }
   __syncthreads();
   xs.store(xT[0]);
-  bs.store(bT[0], wre, 0, Q);
+  if constexpr (kCplx)
+    bs.template store_rot<MODE == kStateCplxAdj>(bT[0], wre, rcs, 0, Q);
+  else
+    bs.store(bT[0], wre, 0, Q);
   __syncthreads();
 
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
@@ -444,7 +495,8 @@ static hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st) {
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
   const hipEvent_t* ev = a.events;
   launch_k(nc > 0, ssd_state_kernel<P, N>, dim3(blocks), dim3(kThreads), st, ev, x, a.dt, a.A, B,
-           a.dt_bias, a.dt_min, a.dt_max, states, decay, a.T, a.H, a.G, a.chunk, nc, npairs);
+           a.dt_bias, a.dt_min, a.dt_max, states, decay, a.T, a.H, a.G, a.chunk, nc, npairs,
+           static_cast<const float2*>(nullptr));
   launch_pass<false, N>(states, decay, a.h0, a.h_final, a.Bsz, a.H, P, nc, st,
                         ev ? ev + 2 : nullptr);
   launch_k(nc > 0, ssd_scan_kernel<P, N>, dim3(blocks), dim3(kThreads), st, ev ? ev + 4 : nullptr,
@@ -471,31 +523,35 @@ template <int P, int N>
 static hipError_t launch_states_f32(const float* x, const float* dt, const float* A, const float* B,
                                     const float* dt_bias, float dt_min, float dt_max, float* states,
                                     float* decay, int Bsz, int T, int H, int G, int chunk, int mode,
-                                    hipStream_t st, const hipEvent_t* ev) {
+                                    const float2* rot, hipStream_t st, const hipEvent_t* ev) {
   const int nc = (T + chunk - 1) / chunk;
   const int npairs = Bsz * nc;
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * H;
   if (chunk > 64) return hipErrorInvalidValue;  // one stage buffer holds 64 tokens
-  if (mode == kStateFwd)
-    launch_k(nc > 0, ssd_state_kernel<P, N, kStateFwd, 1>, dim3(blocks), dim3(kThreads), st, ev, x, dt,
-             A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
-  else if (mode == kStateFwdUnit)
-    launch_k(nc > 0, ssd_state_kernel<P, N, kStateFwdUnit, 1>, dim3(blocks), dim3(kThreads), st, ev, x,
-             dt, A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
-  else
-    launch_k(nc > 0, ssd_state_kernel<P, N, kStateAdj, 1>, dim3(blocks), dim3(kThreads), st, ev, x, dt,
-             A, B, dt_bias, dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs);
+  auto go = [&](auto m) {
+    constexpr int M = decltype(m)::value;
+    launch_k(nc > 0, ssd_state_kernel<P, N, M, 1>, dim3(blocks), dim3(kThreads), st, ev, x, dt, A, B, dt_bias,
+             dt_min, dt_max, states, decay, T, H, G, chunk, nc, npairs, rot);
+  };
+  switch (mode) {
+    case kStateFwd: go(std::integral_constant<int, kStateFwd>{}); break;
+    case kStateFwdUnit: go(std::integral_constant<int, kStateFwdUnit>{}); break;
+    case kStateAdj: go(std::integral_constant<int, kStateAdj>{}); break;
+    case kStateCplxUnit: go(std::integral_constant<int, kStateCplxUnit>{}); break;
+    case kStateCplxAdj: go(std::integral_constant<int, kStateCplxAdj>{}); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t run_states_f32(const float* x, const float* dt, const float* A, const float* B,
                           const float* dt_bias, float dt_min, float dt_max, float* states,
                           float* decay, int Bsz, int T, int H, int P, int G, int N, int chunk,
-                          int mode, hipStream_t st, const hipEvent_t* ev) {
+                          int mode, const float2* rot, hipStream_t st, const hipEvent_t* ev) {
 #define SSD_STATES_F32(PP, NN)                                                                     \
   if (P == PP && N == NN)                                                                          \
     return launch_states_f32<PP, NN>(x, dt, A, B, dt_bias, dt_min, dt_max, states, decay, Bsz, T, H, \
-                                     G, chunk, mode, st, ev);
+                                     G, chunk, mode, rot, st, ev);
   SSD_STATES_F32(32, 32)
   SSD_STATES_F32(32, 64)
   SSD_STATES_F32(32, 128)

@@ -197,15 +197,18 @@ hipError_t run_complex_decode(const DecodeArgs& a, hipStream_t st);  // D unused
 // then holds the fp32 boundary states h_in(c))
 hipError_t run_chunk_states_bf16(const ChunkArgs& a, hipStream_t st);
 hipError_t run_chunk_bwd_bf16(const BwdArgs& a, hipStream_t st);
-// fp32 chunk-state kernel for the backward: mode 0 forward chunk states S_c
-// and decays (input scale delta), 1 the same with input scale 1, 2 adjoint
-// chunk states G_c = sum_l e^{cs_l} x_l (x) B_l (x = dy, B = C; decay unused).
-// states (Bsz, nc, H, P, N) fp32; decay (Bsz, H, nc, 2).  P in {32, 64}, N in
-// {32, 64, 128}.
+// fp32 chunk-state kernel for the backward (chunk <= 64): mode 0 forward
+// chunk states S_c and decays (input scale delta), 1 the same with input
+// scale 1, 2 adjoint chunk states G_c = sum_l e^{cs_l} x_l (x) B_l (x = dy,
+// B = C; decay unused); 3 and 4 are 1 and 2 on complex rows (B or C as N/2
+// (re, im) pairs per group row, N the real feature count) rotated per token by
+// rot (Bsz, T, H) = (cos, sin) theta into [Re B e^{-i theta} | Im ..] (3) or
+// [Re C e^{i theta} | -Im ..] (4).  states (Bsz, nc, H, P, N) fp32; decay
+// (Bsz, H, nc, 2).  P in {32, 64}, N in {32, 64, 128}.
 hipError_t run_states_f32(const float* x, const float* dt, const float* A, const float* B,
                           const float* dt_bias, float dt_min, float dt_max, float* states,
                           float* decay, int Bsz, int T, int H, int P, int G, int N, int chunk,
-                          int mode, hipStream_t st, const hipEvent_t* ev);
+                          int mode, const float2* rot, hipStream_t st, const hipEvent_t* ev);
 // fp32 state passing in place (h_in over S; h0, h_final may be null)
 hipError_t run_pass_f32(float* states, const float* decay, const float* h0, float* h_final, int Bsz,
                         int H, int P, int N, int nc, hipStream_t st, const hipEvent_t* ev);
