@@ -1013,9 +1013,12 @@ def bench_bwd(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+# the 14 event slots of ssd_complex_chunk_bwd_ev; None: a slot no kernel fills
+# (the chunk constants form inside the adjoint passing), and the group sums
+# run only when a group holds several heads
 CPLX_BWD_KERNELS = ["ssd_cplx_rotate_kernel", "ssd_state_kernel(unit scale)", "ssd_pass_kernel",
                     "ssd_state_kernel(adjoint)", "ssd_f32_adj_pass_kernel", "ssd_f32_col_kernel",
-                    "ssd_f32_row_kernel", "ssd_f32_const_kernel", "ssd_cplx_tau_kernel",
+                    "ssd_f32_row_kernel", None, "ssd_cplx_tau_kernel",
                     "ssd_cplx_rho_total_kernel", "ssd_f32_dt_kernel", "ssd_f32_dt_sum_kernel",
                     "ssd_f32_group_sum_kernel", "ssd_cplx_dh0_kernel"]
 
@@ -1099,6 +1102,8 @@ def bench_bwd_complex(args, cfg):
     costs = cplx_bwd_costs(dims)
     kern = {}
     for k, name in enumerate(CPLX_BWD_KERNELS):
+        if name is None or (name == "ssd_f32_group_sum_kernel" and G == H):
+            continue
         avg = float(np.mean([hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in evs]))
         ent = {"avg_us": avg * 1e3}
         fl = costs["flops"].get(name)

@@ -473,7 +473,8 @@ size_t ssd_complex_bwd_workspace_size(int Bsz, int T, int H, int P, int G, int N
  * and result, plus `events`, 28 hipEvent_t (passed as void*) or NULL: a
  * start/stop pair bound to each of 14 kernel slots in order (rotation into
  * the sequence frame, chunk states, state passing, adjoint chunk states,
- * adjoint passing, column-side blocks, row-side blocks, chunk constants, the
+ * adjoint passing (which also forms the chunk constants), column-side blocks,
+ * row-side blocks, chunk constants (an empty pair), the
  * last token's rotation term, rho sums per chunk, step-size gradients per
  * chunk, their sums per head, dB/dC group sums, dh0). */
 int ssd_complex_chunk_bwd_ev(const float *x, const float *dt, const float *A, const float *B,

@@ -46,10 +46,10 @@
 //                         they stage them
 //   chunk states, state passing, adjoint chunk states: ssd_chunk.hip's fp32
 //                         kernels (run_states_f32, run_pass_f32)
-//   ssd_f32_adj_pass      R_c in place over G_c, last chunk first; dh0
+//   ssd_f32_adj_pass      R_c in place over G_c, last chunk first; dh0; the
+//                         shares of the chunk constants <R_c, H_in(c)>
 //   ssd_f32_col           v, dx, dB (per head), f2, col, x.v, dy.x [, rho_B]
 //   ssd_f32_row           dC (per head), f1, row [, rho_C]
-//   ssd_f32_const         e^{tot} <R_c, H_in(c)>
 //   ssd_cplx_tau          (complex) the last token's rho term of h_final
 //   ssd_cplx_rho_total    (complex) rho summed over each chunk
 //   ssd_f32_dt            fp64 scans of f1, f2, col - row [, rho]: da, ddt and
@@ -62,7 +62,8 @@
 // With measurement events, pair k (events 2k, 2k+1) is bound to: 0 rotation
 // (from the start of the u sums to the end of the rotation),
 // 1 chunk states, 2 state passing, 3 adjoint chunk states, 4 adjoint passing,
-// 5 column side, 6 row side, 7 chunk constants, 8 tau, 9 rho totals,
+// 5 column side, 6 row side, 7 chunk constants (formed inside the adjoint
+// passing: recorded back to back), 8 tau, 9 rho totals,
 // 10 step sizes, 11 their sums, 12 group sums, 13 dh0 (a kernel a form does
 // not run records its pair back to back).
 //
@@ -524,49 +525,48 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
 
 // ---------------------------------------------------------------------------
 // Adjoint passing, last chunk first: R_{nc-1} = dh_final, R_{c-1} = lambda_c
-// R_c + G_c, dh0 = R_{-1}; R_c over G_c.  One thread per 4 elements.
+// R_c + G_c, dh0 = R_{-1}; R_c over G_c.  One thread per 4 elements, a
+// workgroup per 1024 elements of one (batch, head).  On the way it forms its
+// share of each chunk's constant <R_c, H_in(c)> (H_in over the forward states,
+// fp64 sums): cpart[(b, h, c) * nblk + block], summed and scaled by e^{tot}
+// where the step-size gradients use them.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ssd_f32_adj_pass_kernel(
     float* __restrict__ adj, const float* __restrict__ decay, const float* __restrict__ dh_final,
-    float* __restrict__ dh0, int H, int PN, int nc) {
+    float* __restrict__ dh0, const float* __restrict__ states, double* __restrict__ cpart, int H, int PN,
+    int nc) {
+  __shared__ double ws4[kThreads / kWave];
   const int h = blockIdx.y, b = blockIdx.z;
-  const int e4 = blockIdx.x * kThreads + threadIdx.x;
-  if (e4 * 4 >= PN) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int e4 = blockIdx.x * kThreads + tid;
+  const bool in = e4 * 4 < PN;
+  const int nblk = gridDim.x;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t cstride = static_cast<size_t>(H) * PN;
-  float* base = adj + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e4 * 4;
+  const size_t off = static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + (in ? e4 * 4 : 0);
+  float* base = adj + off;
+  const float* hb = states + off;
   const float* dc = decay + bh * nc * 2;
-  float4 r = dh_final ? *reinterpret_cast<const float4*>(dh_final + bh * PN + e4 * 4)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 r = in && dh_final ? *reinterpret_cast<const float4*>(dh_final + bh * PN + e4 * 4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int cc = nc - 1; cc >= 0; --cc) {
-    const float4 gv = *reinterpret_cast<const float4*>(base + cc * cstride);
+    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f), hv = gv;
+    if (in) {
+      gv = *reinterpret_cast<const float4*>(base + cc * cstride);
+      hv = *reinterpret_cast<const float4*>(hb + cc * cstride);
+      *reinterpret_cast<float4*>(base + cc * cstride) = r;
+    }
+    double part = static_cast<double>(r.x * hv.x + r.y * hv.y) + static_cast<double>(r.z * hv.z + r.w * hv.w);
+    part = wave_inclusive_sum_d(part);
+    if (lane == kWave - 1) ws4[wid] = part;
+    __syncthreads();
+    if (tid == 0)
+      cpart[(bh * nc + cc) * nblk + blockIdx.x] = (ws4[0] + ws4[1]) + (ws4[2] + ws4[3]);
+    __syncthreads();
     const float l = dc[2 * cc];
-    *reinterpret_cast<float4*>(base + cc * cstride) = r;
     r = make_float4(l * r.x + gv.x, l * r.y + gv.y, l * r.z + gv.z, l * r.w + gv.w);
   }
-  if (dh0) *reinterpret_cast<float4*>(dh0 + bh * PN + e4 * 4) = r;
-}
-
-// chunk constants e^{tot} <R_c, H_in(c)> (fp64 sum)
-__global__ __launch_bounds__(kThreads) void ssd_f32_const_kernel(
-    const float* __restrict__ adj, const float* __restrict__ states, const float* __restrict__ decay,
-    double* __restrict__ cst, int H, int PN, int nc) {
-  __shared__ double ws4[4];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
-  const size_t bh = static_cast<size_t>(b) * H + h;
-  const size_t slot = ((static_cast<size_t>(b) * nc + c) * H + h) * PN;
-  double sum = 0.0;
-  for (int i = tid * 4; i < PN; i += kThreads * 4) {
-    const float4 r = *reinterpret_cast<const float4*>(adj + slot + i);
-    const float4 s = *reinterpret_cast<const float4*>(states + slot + i);
-    sum += static_cast<double>(r.x * s.x + r.y * s.y) + static_cast<double>(r.z * s.z + r.w * s.w);
-  }
-  sum = wave_inclusive_sum_d(sum);
-  if (lane == kWave - 1) ws4[wid] = sum;
-  __syncthreads();
-  if (tid == 0)
-    cst[bh * nc + c] = static_cast<double>(decay[(bh * nc + c) * 2]) * ((ws4[0] + ws4[1]) + (ws4[2] + ws4[3]));
+  if (in && dh0) *reinterpret_cast<float4*>(dh0 + bh * PN + e4 * 4) = r;
 }
 
 // ---------------------------------------------------------------------------
@@ -688,13 +688,17 @@ __global__ __launch_bounds__(kQ) void ssd_f32_dt_kernel(
     const float* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
     float dt_min, float dt_max, const float* __restrict__ f1, const float* __restrict__ f2,
     const float* __restrict__ colp, const float* __restrict__ rowp, const float* __restrict__ xv,
-    const float* __restrict__ dyx, const double* __restrict__ cst, const float* __restrict__ rhoB,
-    const float* __restrict__ rhoC, const double* __restrict__ rtot, const double* __restrict__ u,
-    float* __restrict__ ddt, double* __restrict__ part, int T, int H, int nc) {
+    const float* __restrict__ dyx, const double* __restrict__ cpart, const float* __restrict__ decay,
+    int nblk, const float* __restrict__ rhoB, const float* __restrict__ rhoC, const double* __restrict__ rtot,
+    const double* __restrict__ u, float* __restrict__ ddt, double* __restrict__ part, int T, int H, int nc) {
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t bhc = bh * nc + c;
+  // the chunk constant e^{tot} <R_c, H_in(c)> from the adjoint passing's shares
+  double cst_c = 0.0;
+  for (int k = 0; k < nblk; ++k) cst_c += cpart[bhc * nblk + k];
+  cst_c *= static_cast<double>(decay[bhc * 2]);
   const int t = c * kQ + lane;
   const bool in = t < T;
   const size_t row = (static_cast<size_t>(b) * T + (in ? t : 0)) * H + h;
@@ -717,7 +721,7 @@ __global__ __launch_bounds__(kQ) void ssd_f32_dt_kernel(
   }
   double sA = 0.0, sBias = 0.0, sD = 0.0, sBeta = 0.0;
   if (in) {
-    const double da = box + f1_suffix + f2_prefix + cst[bhc];
+    const double da = box + f1_suffix + f2_prefix + cst_c;
     const float z = dt[row] + bias;
     const float d = step_size(dt[row], bias, dt_min, dt_max);
     const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
@@ -871,7 +875,7 @@ static F32BwdLayout f32_layout(int Bsz, int T, int H, int P, int N, bool cplx) {
   L.dBh = o;  o += up(tok * NE * 4);
   L.dCh = o;  o += up(tok * NE * 4);
   L.tokv = o; o += up(tok * 4 * 8);
-  L.cst = o;  o += up(static_cast<size_t>(Bsz) * H * nc * 8);
+  L.cst = o;  o += up(static_cast<size_t>(Bsz) * H * nc * 8 * ((P * NE / 4 + kThreads - 1) / kThreads));
   L.part = o; o += up(static_cast<size_t>(Bsz) * H * nc * 32);
   if (cplx) {
     const size_t hs = static_cast<size_t>(Bsz) * H * P * NE * 4;
@@ -926,7 +930,9 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
   launch_k(run, ssd_f32_row_kernel<P, NE, SCALE, CPLX>, grid, dim3(kT8), st, E(6), x, dt, A_dec,
            dt_bias, dt_min, dt_max, Bin, Cin, dy, S, dCh, f1, rw, rhoC, rot, dCo, T, H, Geff,
            nc);
-  launch_k(run, ssd_f32_const_kernel, grid, dim3(kThreads), st, E(7), adj, S, dec, cst, H, P * NE, nc);
+  // (the chunk constants come from the adjoint passing: slot 7 records back to back)
+  launch_k(false, ssd_f32_dt_sum_kernel<CPLX>, dim3(1), dim3(kThreads), st, E(7), nullptr, nullptr, nullptr,
+           nullptr, 0, 0, 0);
   launch_k(CPLX, ssd_cplx_tau_kernel, dim3(H, Bsz), dim3(kThreads), st, E(8),
            reinterpret_cast<const float*>(ws + L.dhfe), reinterpret_cast<const float*>(ws + L.hfe), rhoB,
            T, H, P, NE / 2);
@@ -935,7 +941,8 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
   launch_k(run, ssd_f32_dt_kernel<CPLX>, grid, dim3(kQ), st, E(10), dt, A_dt, dt_bias, dt_min, dt_max,
            static_cast<const float*>(f1), static_cast<const float*>(f2), static_cast<const float*>(col),
            static_cast<const float*>(rw), static_cast<const float*>(xv), static_cast<const float*>(dyx),
-           static_cast<const double*>(cst), static_cast<const float*>(rhoB), static_cast<const float*>(rhoC),
+           static_cast<const double*>(cst), dec, (P * NE / 4 + kThreads - 1) / kThreads,
+           static_cast<const float*>(rhoB), static_cast<const float*>(rhoC),
            CPLX ? reinterpret_cast<const double*>(ws + L.rtot) : nullptr,
            CPLX ? reinterpret_cast<const double*>(ws + L.u) : nullptr, ddt, part, T, H, nc);
   launch_k(true, ssd_f32_dt_sum_kernel<CPLX>, dim3(H), dim3(kThreads), st, E(11), static_cast<const double*>(part), dA, ddt_bias, dD, Bsz, H, nc);
@@ -967,8 +974,8 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
                        a.G, N, kQ, 2, nullptr, st, E(3));
   if (e != hipSuccess) return e;
   launch_k(true, ssd_f32_adj_pass_kernel, dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
-           dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), a.dh_final, a.dh0, a.H,
-           P * N, nc);
+           dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), a.dh_final, a.dh0,
+           static_cast<const float*>(S), reinterpret_cast<double*>(ws + L.cst), a.H, P * N, nc);
   // each head its own group: the per-head gradients are the outputs
   const bool direct = a.G == a.H;
   float* dBh = direct ? a.dB : reinterpret_cast<float*>(ws + L.dBh);
@@ -1048,7 +1055,7 @@ static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   launch_k(true, ssd_f32_adj_pass_kernel, dim3((P * NE / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
            dim3(kThreads), st, E(4), adj, static_cast<const float*>(dec), static_cast<const float*>(dhfe),
-           dh0e, a.H, P * NE, nc);
+           dh0e, static_cast<const float*>(S), reinterpret_cast<double*>(ws + L.cst), a.H, P * NE, nc);
   // each head its own group: dB, dC rotated back and written by the block kernels
   const bool direct = a.G == a.H;
   e = launch_f32_core<P, NE, true>(a.x, a.dt, alpha, a.A, a.dt_bias, a.dt_min, a.dt_max, a.B, a.C, a.G,
