@@ -131,6 +131,66 @@ __device__ __forceinline__ void stage_rot(float* tile, int pitch, const float* _
   }
 }
 
+// A tile of ROWS rows of W floats staged in two phases, so that every load of
+// a workgroup's tiles is in flight before the first wait: load() into
+// registers (rows at or past `valid` as zeros), then store() into LDS at
+// `pitch` (store_rot: complex rows rotated as stage_rot does, with the rows'
+// (cos, sin) loaded beside them).
+template <int W, int ROWS, int NTHR>
+struct TileRegs {
+  static constexpr int VPR = W / 4;
+  static constexpr int ITEMS = ROWS * VPR;
+  static constexpr int PER = (ITEMS + NTHR - 1) / NTHR;
+  float4 v[PER];
+  float2 cs[PER];
+  __device__ __forceinline__ void load(const float* __restrict__ src, size_t ld, int valid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHR;
+      const int r = it / VPR, c4 = it % VPR;
+      v[i] = (ITEMS % NTHR == 0 || it < ITEMS) && r < valid
+                 ? *reinterpret_cast<const float4*>(src + r * ld + c4 * 4)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void load_rot(const float2* __restrict__ rc, size_t rstride, int valid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHR;
+      const int r = it / VPR;
+      cs[i] = (ITEMS % NTHR == 0 || it < ITEMS) && r < valid ? rc[r * rstride] : make_float2(1.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void store(float* tile, int pitch) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHR;
+      if (ITEMS % NTHR == 0 || it < ITEMS)
+        *reinterpret_cast<float4*>(tile + (it / VPR) * pitch + (it % VPR) * 4) = v[i];
+    }
+  }
+  template <bool CONJ>
+  __device__ __forceinline__ void store_rot(float* tile, int pitch, const float2 (&rcs)[PER]) const {
+    constexpr int NH = W / 2;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHR;
+      if (!(ITEMS % NTHR == 0 || it < ITEMS)) continue;
+      const float4 val = v[i];
+      const float2 c = rcs[i];
+      float* t = tile + (it / VPR) * pitch + 2 * (it % VPR);
+      if constexpr (!CONJ) {
+        *reinterpret_cast<float2*>(t) = make_float2(val.x * c.x + val.y * c.y, val.z * c.x + val.w * c.y);
+        *reinterpret_cast<float2*>(t + NH) = make_float2(val.y * c.x - val.x * c.y, val.w * c.x - val.z * c.y);
+      } else {
+        *reinterpret_cast<float2*>(t) = make_float2(val.x * c.x - val.y * c.y, val.z * c.x - val.w * c.y);
+        *reinterpret_cast<float2*>(t + NH) =
+            make_float2(-(val.y * c.x + val.x * c.y), -(val.w * c.x + val.z * c.y));
+      }
+    }
+  }
+};
+
 // acc += A . B over k in [0, K): A rows `arow` (k contiguous), B rows `brow`
 // (k contiguous), 4 k per lane group per float4
 template <int K>
@@ -191,19 +251,28 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
   const int w = wave_id(), role = w >> 2;
   const size_t r0 = static_cast<size_t>(b) * T + t0;
   const float dt_raw = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
-  stage<P, kT8>(Xs, XP, x + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  stage<P, kT8>(Ys, XP, dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  if constexpr (CPLX) {
-    stage_rot<NE, kT8, false>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc,
-                              rot + r0 * H + h, H);
-    stage_rot<NE, kT8, true>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc,
-                             rot + r0 * H + h, H);
-  } else {
-    stage<NE, kT8>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
-    stage<NE, kT8>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  {
+    // every tile's loads first, then the LDS stores
+    TileRegs<P, kQ, kT8> tx, ty;
+    TileRegs<NE, kQ, kT8> tb, tc;
+    TileRegs<NE, P, kT8> tr;
+    tx.load(x + (r0 * H + h) * P, static_cast<size_t>(H) * P, Lc);
+    ty.load(dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, Lc);
+    tb.load(Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, Lc);
+    tc.load(Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, Lc);
+    tr.load(adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE), NE, P);
+    if constexpr (CPLX) tb.load_rot(rot + r0 * H + h, H, Lc);
+    tx.store(Xs, XP);
+    ty.store(Ys, XP);
+    if constexpr (CPLX) {
+      tb.template store_rot<false>(Bs, NP, tb.cs);
+      tc.template store_rot<true>(Cs, NP, tb.cs);
+    } else {
+      tb.store(Bs, NP);
+      tc.store(Cs, NP);
+    }
+    tr.store(Rs, NP);
   }
-  stage<NE, kT8>(Rs, NP, adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE),
-                 NE, P, P);
   chunk_prologue(dt_raw, Lc, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, dl, cs_hi, cs_lo, wsum,
                  &tot, kQ);  // (its barrier also publishes the staged tiles)
 
@@ -387,19 +456,28 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
   const int w = wave_id(), role = w >> 2;
   const size_t r0 = static_cast<size_t>(b) * T + t0;
   const float dt_raw = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
-  stage<P, kT8>(Xs, XP, x + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  stage<P, kT8>(Ys, XP, dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, kQ, Lc);
-  if constexpr (CPLX) {
-    stage_rot<NE, kT8, false>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc,
-                              rot + r0 * H + h, H);
-    stage_rot<NE, kT8, true>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc,
-                             rot + r0 * H + h, H);
-  } else {
-    stage<NE, kT8>(Bs, NP, Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
-    stage<NE, kT8>(Cs, NP, Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, kQ, Lc);
+  {
+    // every tile's loads first, then the LDS stores
+    TileRegs<P, kQ, kT8> tx, ty;
+    TileRegs<NE, kQ, kT8> tb, tc;
+    TileRegs<NE, P, kT8> th;
+    tx.load(x + (r0 * H + h) * P, static_cast<size_t>(H) * P, Lc);
+    ty.load(dy + (r0 * H + h) * P, static_cast<size_t>(H) * P, Lc);
+    tb.load(Bm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, Lc);
+    tc.load(Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, Lc);
+    th.load(states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE), NE, P);
+    if constexpr (CPLX) tb.load_rot(rot + r0 * H + h, H, Lc);
+    tx.store(Xs, XP);
+    ty.store(Ys, XP);
+    if constexpr (CPLX) {
+      tb.template store_rot<false>(Bs, NP, tb.cs);
+      tc.template store_rot<true>(Cs, NP, tb.cs);
+    } else {
+      tb.store(Bs, NP);
+      tc.store(Cs, NP);
+    }
+    th.store(Hs, NP);
   }
-  stage<NE, kT8>(Hs, NP, states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE),
-                 NE, P, P);
   chunk_prologue(dt_raw, Lc, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, dl, cs_hi, cs_lo, wsum,
                  &tot, kQ);
 
