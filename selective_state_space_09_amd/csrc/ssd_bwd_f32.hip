@@ -90,52 +90,13 @@ __device__ __forceinline__ float qsum(float a) {
   return __uint_as_float(h[0]) + __uint_as_float(h[1]);
 }
 
-// rows [0, rows) of W-float-wide rows (src row stride `ld` floats) into an LDS
-// tile of pitch `pitch`, zeros for rows past `valid`
-template <int W, int NTHR = kThreads>
-__device__ __forceinline__ void stage(float* tile, int pitch, const float* __restrict__ src, size_t ld,
-                                      int rows, int valid) {
-  for (int i = threadIdx.x; i < rows * (W / 4); i += NTHR) {
-    const int r = i / (W / 4), v = i % (W / 4);
-    const float4 val = r < valid ? *reinterpret_cast<const float4*>(src + r * ld + v * 4)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(tile + r * pitch + v * 4) = val;
-  }
-}
-
-// the same for complex rows (W/2 (re, im) pairs per row), rotated per row r by
-// (cos, sin) theta = rc[r * rstride] into the W real features [Re | Im] of
-// z e^{-i theta} (CONJ = false) or [Re | -Im] of z e^{+i theta} (CONJ = true)
-template <int W, int NTHR, bool CONJ>
-__device__ __forceinline__ void stage_rot(float* tile, int pitch, const float* __restrict__ src, size_t ld,
-                                          int rows, int valid, const float2* __restrict__ rc,
-                                          size_t rstride) {
-  constexpr int NH = W / 2;
-  for (int i = threadIdx.x; i < rows * (W / 4); i += NTHR) {
-    const int r = i / (W / 4), v = i % (W / 4);
-    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-    float2 cs = make_float2(1.f, 0.f);
-    if (r < valid) {
-      val = *reinterpret_cast<const float4*>(src + r * ld + v * 4);
-      cs = rc[r * rstride];
-    }
-    float* t = tile + r * pitch + 2 * v;
-    if constexpr (!CONJ) {
-      *reinterpret_cast<float2*>(t) = make_float2(val.x * cs.x + val.y * cs.y, val.z * cs.x + val.w * cs.y);
-      *reinterpret_cast<float2*>(t + NH) = make_float2(val.y * cs.x - val.x * cs.y, val.w * cs.x - val.z * cs.y);
-    } else {
-      *reinterpret_cast<float2*>(t) = make_float2(val.x * cs.x - val.y * cs.y, val.z * cs.x - val.w * cs.y);
-      *reinterpret_cast<float2*>(t + NH) =
-          make_float2(-(val.y * cs.x + val.x * cs.y), -(val.w * cs.x + val.z * cs.y));
-    }
-  }
-}
-
-// A tile of ROWS rows of W floats staged in two phases, so that every load of
-// a workgroup's tiles is in flight before the first wait: load() into
-// registers (rows at or past `valid` as zeros), then store() into LDS at
-// `pitch` (store_rot: complex rows rotated as stage_rot does, with the rows'
-// (cos, sin) loaded beside them).
+// A tile of ROWS rows of W floats (source row stride `ld` floats) staged in two
+// phases, so that every load of a workgroup's tiles is in flight before the
+// first wait: load() into registers (rows at or past `valid` as zeros), then
+// store() into LDS at `pitch`.  For complex rows (W/2 (re, im) pairs per row),
+// load_rot() fetches each row's (cos, sin) theta and store_rot() writes the W
+// real features [Re | Im] of z e^{-i theta} (CONJ = false) or [Re | -Im] of
+// z e^{+i theta} (CONJ = true).
 template <int W, int ROWS, int NTHR>
 struct TileRegs {
   static constexpr int VPR = W / 4;
