@@ -83,46 +83,6 @@ __device__ __forceinline__ void split8(uint4 v, float f, uint4& hi, uint4& lo) {
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-// Copies an fp32 (ROWS, 8 * VPR) tile from a buffer (row r at byte r *
-// row_bytes) into two LDS bf16 tiles of pitch `pitch`: its leading part
-// round(v) into `hi` and the remainder round(v - round(v)) into `lo`.
-template <int VPR, int ROWS>
-__device__ __forceinline__ void stage_rows_split(uint16_t* hi, uint16_t* lo, int pitch, buf_t src,
-                                                 uint32_t row_bytes) {
-  constexpr int ITEMS = 2 * VPR * ROWS;  // 16-byte (4-float) pieces
-#pragma unroll
-  for (int it0 = 0; it0 < ITEMS; it0 += kThreads) {
-    const int it = it0 + static_cast<int>(threadIdx.x);
-    if (ITEMS % kThreads == 0 || it < ITEMS) {
-      const int v = it % (2 * VPR), r = it / (2 * VPR);
-      const uint4 u = buf_load16(src, static_cast<uint32_t>(r) * row_bytes + v * 16);
-      uint32_t h0, l0, h1, l1;
-      split_bf16x2(__uint_as_float(u.x), __uint_as_float(u.y), h0, l0);
-      split_bf16x2(__uint_as_float(u.z), __uint_as_float(u.w), h1, l1);
-      *reinterpret_cast<uint2*>(hi + r * pitch + v * 4) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(lo + r * pitch + v * 4) = make_uint2(l0, l1);
-    }
-  }
-}
-
-// Copies `rows` rows of `VPR` 16-byte vectors from a buffer (row r at byte
-// r * row_bytes) into an LDS tile of pitch `pitch` bf16; rows past the
-// buffer's range arrive as zero.  256 threads.
-template <int VPR, int ROWS>
-__device__ __forceinline__ void stage_rows(uint16_t* tile, int pitch, buf_t src, uint32_t row_bytes,
-                                           int row0) {
-  constexpr int ITEMS = VPR * ROWS;
-#pragma unroll
-  for (int it0 = 0; it0 < ITEMS; it0 += kThreads) {
-    const int it = it0 + static_cast<int>(threadIdx.x);
-    if (ITEMS % kThreads == 0 || it < ITEMS) {
-      const int v = it % VPR, r = it / VPR;
-      *reinterpret_cast<uint4*>(tile + r * pitch + v * 8) =
-          buf_load16(src, static_cast<uint32_t>(row0 + r) * row_bytes + v * 16);
-    }
-  }
-}
-
 // writes rows held in registers (a BufSlab of the same shape) into an LDS tile
 template <int ROWS, int VPR>
 __device__ __forceinline__ void put_rows(uint16_t* tile, int pitch, const BufSlab<ROWS, VPR, kThreads>& q) {
@@ -131,6 +91,27 @@ __device__ __forceinline__ void put_rows(uint16_t* tile, int pitch, const BufSla
     const int it = static_cast<int>(threadIdx.x) + i * kThreads;
     if (q.ITEMS % kThreads == 0 || it < q.ITEMS)
       *reinterpret_cast<uint4*>(tile + (it / VPR) * pitch + (it % VPR) * 8) = q.v[i];
+  }
+}
+
+// writes fp32 rows held in registers (a BufSlab of 4-float pieces) into two
+// LDS bf16 tiles of pitch `pitch`: the leading part round(v) into `hi` and the
+// remainder round(v - round(v)) into `lo`
+template <int ROWS, int VPR>
+__device__ __forceinline__ void put_rows_split(uint16_t* hi, uint16_t* lo, int pitch,
+                                               const BufSlab<ROWS, VPR, kThreads>& q) {
+#pragma unroll
+  for (int i = 0; i < q.PER; ++i) {
+    const int it = static_cast<int>(threadIdx.x) + i * kThreads;
+    if (q.ITEMS % kThreads == 0 || it < q.ITEMS) {
+      const int v = it % VPR, r = it / VPR;
+      const uint4 u = q.v[i];
+      uint32_t h0, l0, h1, l1;
+      split_bf16x2(__uint_as_float(u.x), __uint_as_float(u.y), h0, l0);
+      split_bf16x2(__uint_as_float(u.z), __uint_as_float(u.w), h1, l1);
+      *reinterpret_cast<uint2*>(hi + r * pitch + v * 4) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(lo + r * pitch + v * 4) = make_uint2(l0, l1);
+    }
   }
 }
 
@@ -205,12 +186,17 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
   const int wid = wave_id();
   const size_t r0 = static_cast<size_t>(b) * T + t0;
   const float2* tk = tok + ((static_cast<size_t>(b) * nc + c) * H + h) * Q;
-  if (tid < Q) wl[tid] = tid < Lc ? __expf(tk[tid].x) : 0.0f;
   const uint32_t yrow = static_cast<uint32_t>(H) * P * 2, crow = static_cast<uint32_t>(G) * N * 2;
   const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
                               static_cast<uint32_t>(Lc - 1) * yrow + P * 2);
   const buf_t cbuf = make_buf(Cm + r0 * G * N + static_cast<size_t>(g) * N,
                               static_cast<uint32_t>(Lc - 1) * crow + N * 2);
+  // the C and dy rows of the next block, loaded one block ahead
+  BufSlab<kBlk, N / 8, kThreads> cq;
+  BufSlab<kBlk, P / 8, kThreads> yq;
+  cq.load(cbuf, crow, 0);
+  yq.load(ybuf, yrow, 0);
+  if (tid < Q) wl[tid] = tid < Lc ? __expf(tk[tid].x) : 0.0f;
   f32x4 acc[NTW][PT];
 #pragma unroll
   for (int i = 0; i < NTW; ++i)
@@ -219,19 +205,23 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
 
   for (int l0 = 0; l0 < Lc; l0 += kBlk) {
     __syncthreads();  // wl written / previous block consumed
-    stage_rows<N / 8, kBlk>(cl, CP, cbuf, crow, l0);
+    put_rows(cl, CP, cq);
     // dy rows scaled by e^{cs_l}
 #pragma unroll
-    for (int it0 = 0; it0 < kBlk * (P / 8); it0 += kThreads) {
-      const int it = it0 + tid;
-      if ((kBlk * (P / 8)) % kThreads == 0 || it < kBlk * (P / 8)) {
+    for (int i = 0; i < yq.PER; ++i) {
+      const int it = tid + i * kThreads;
+      if (yq.ITEMS % kThreads == 0 || it < yq.ITEMS) {
         const int v = it % (P / 8), r = it / (P / 8);
         const float w = l0 + r < Q ? wl[l0 + r] : 0.0f;
         uint4 hi, lo;
-        split8(buf_load16(ybuf, static_cast<uint32_t>(l0 + r) * yrow + v * 16), w, hi, lo);
+        split8(yq.v[i], w, hi, lo);
         *reinterpret_cast<uint4*>(yl + r * YP + v * 8) = hi;
         *reinterpret_cast<uint4*>(ylo + r * YP + v * 8) = lo;
       }
+    }
+    if (l0 + kBlk < Lc) {
+      cq.load(cbuf, crow, l0 + kBlk);
+      yq.load(ybuf, yrow, l0 + kBlk);
     }
     __syncthreads();
 #pragma unroll
@@ -403,6 +393,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
   __shared__ __attribute__((aligned(16))) float cs2[256];  // cs_l log2(e) of the chunk's tokens
   __shared__ float dlt[256];                               // delta_l
   __shared__ float rows[2][4][kBlk];  // per l-block parity and wave: row share of each row l
+  __shared__ float dsh;                // D of the head
 
   const int nb = (Q + kBlk - 1) / kBlk;
   const int hpg = H / G;
@@ -421,30 +412,54 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
   const buf_t cbuf = make_buf(Cm + r0 * G * N + static_cast<size_t>(g) * N,
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
-  stage_rows<N / 8, kBlk>(Bs, NP, bbuf, brow, s0);
+  const int nlb = (Lc - s0 + kBlk - 1) / kBlk;
+  auto rows_of = [&](const uint16_t* base, int hh) {
+    return make_buf(base + r0 * H * P + static_cast<size_t>(hh) * P, static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
+  };
+  // Each step's tiles pass through registers: all of its loads are issued
+  // before the barrier that frees their LDS tiles, and stored after it.
+  // (Loading them one step ahead instead costs the 36 registers that keep a
+  // second wave on each SIMD: 150 against 95 us at the BitMamba shape.)
+  BufSlab<kBlk, P / 8, kThreads> xq;
+  BufSlab<P, N / 4, kThreads> rq;
+  BufSlab<kBlk, N / 8, kThreads> cq;
+  BufSlab<kBlk, P / 8, kThreads> yq;
+  float2 tq = make_float2(0.f, 0.f);
+  float dq = 0.0f;
+  auto load_head = [&](int hh) {
+    xq.load(rows_of(x, hh), xrow, s0);
+    rq.load(make_buf(adj + ((static_cast<size_t>(b) * nc + c) * H + hh) * (static_cast<size_t>(P) * N),
+                     static_cast<uint32_t>(P) * N * 4),
+            N * 4, 0);
+    if (tid < Q) tq = tok[((static_cast<size_t>(b) * nc + c) * H + hh) * Q + tid];
+    if (D != nullptr && tid == 0) dq = D[hh];
+  };
+  auto load_lblock = [&](int hh, int lb) {
+    cq.load(cbuf, brow, s0 + lb * kBlk);
+    yq.load(rows_of(dy, hh), xrow, s0 + lb * kBlk);
+  };
+  {
+    BufSlab<kBlk, N / 8, kThreads> bq;
+    bq.load(bbuf, brow, s0);
+    put_rows(Bs, NP, bq);
+  }
 
   f32x4 dB[NT];  // dB^T[n][s]: lane holds column s = sl, rows n = 16 nt + 4q + i
 #pragma unroll
   for (int i = 0; i < NT; ++i) dB[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int sl = s0 + 16 * w + r16;  // this lane's source token (score, v^T and dB^T columns)
-  const int nlb = (Lc - s0 + kBlk - 1) / kBlk;
 
   for (int e = 0; e < HPG; ++e) {
     const int h = h0 + e;
-    const buf_t xbuf = make_buf(x + r0 * H * P + static_cast<size_t>(h) * P,
-                                static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
-    const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
-                                static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
-    const buf_t rbuf = make_buf(adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
-                                static_cast<uint32_t>(P) * N * 4);
+    load_head(h);
     __syncthreads();  // previous head done with Xs, Rs, cs2, dlt, Ys, Cs
-    stage_rows<P / 8, kBlk>(Xs, XP, xbuf, xrow, s0);
-    stage_rows_split<N / 8, P>(Rs, Cs, NP, rbuf, N * 4);
+    put_rows(Xs, XP, xq);
+    put_rows_split(Rs, Cs, NP, rq);
     if (tid < Q) {
-      const float2 t2 = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
-      cs2[tid] = t2.x * kLog2e;
-      dlt[tid] = t2.y;
+      cs2[tid] = tq.x * kLog2e;
+      dlt[tid] = tq.y;
     }
+    if (tid == 0) dsh = dq;
     __syncthreads();
     // every decay factor below is 2^(cs2_l - cs2_s) <= 1 (l >= s)
     const float tot = cs2[Q - 1];
@@ -529,10 +544,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     };
     for (int lb = nlb - 1; lb >= 0; --lb) {
       const int l0 = s0 + lb * kBlk;
+      load_lblock(h, lb);
       __syncthreads();
+      put_rows(Cs, NP, cq);
+      put_rows(Ys, XP, yq);
+      // (after the waits for this block's rows: a store before them would be waited for too)
       if (lb + 1 < nlb) flush_rows(lb + 1);
-      stage_rows<N / 8, kBlk>(Cs, NP, cbuf, brow, l0);
-      stage_rows<P / 8, kBlk>(Ys, XP, ybuf, xrow, l0);
       __syncthreads();
       // score tiles of this wave's 16 columns s: lane holds s = sl, l = l0 + 16 lt + 4q + i
       f32x4 s1[4], s2[4];
@@ -639,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
 
     // outputs of head h: lane holds row s = sl, p = 32 hh + 8q .. +7 of each pair;
     // Ys now holds the dy rows of the s block (the last l block was the diagonal)
-    const float Dh = D ? D[h] : 0.0f;
+    const float Dh = dsh;  // (the D load went with the head's other loads)
     const buf_t dxbuf = make_buf(dx + r0 * H * P + static_cast<size_t>(h) * P,
                                  static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
     {
@@ -729,7 +746,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
   const buf_t cbuf = make_buf(Cm + r0 * G * N + static_cast<size_t>(g) * N,
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
-  stage_rows<N / 8, kBlk>(Cs, NP, cbuf, brow, l0);
 
   f32x4 dCg[NT];
 #pragma unroll
@@ -745,20 +761,33 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
   BufSlab<kBlk, N / 8, kThreads> bq;
   xq.load(xbufh(h0), xrow, 0);
   bq.load(bbuf, brow, 0);
+  {
+    BufSlab<kBlk, N / 8, kThreads> cq;
+    cq.load(cbuf, brow, l0);
+    put_rows(Cs, NP, cq);
+  }
 
   for (int e = 0; e < HPG; ++e) {
     const int h = h0 + e;
-    const buf_t ybuf = make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P,
-                                static_cast<uint32_t>(Lc - 1) * xrow + P * 2);
-    const buf_t hbuf = make_buf(states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
-                                static_cast<uint32_t>(P) * N * 4);
-    __syncthreads();
-    stage_rows<P / 8, kBlk>(Ys, XP, ybuf, xrow, l0);
-    stage_rows_split<N / 8, P>(Hs, Bs, NP, hbuf, N * 4);
-    if (tid < Q) {
-      const float2 t2 = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
-      cs2[tid] = t2.x * kLog2e;
-      dlt[tid] = t2.y;
+    {
+      // the head's dy rows, h_in(c) and token table: every load issued before
+      // the barrier that frees their tiles
+      BufSlab<kBlk, P / 8, kThreads> yq;
+      BufSlab<P, N / 4, kThreads> hq;
+      float2 t2 = make_float2(0.f, 0.f);
+      if (tid < Q) t2 = tok[((static_cast<size_t>(b) * nc + c) * H + h) * Q + tid];
+      yq.load(make_buf(dy + r0 * H * P + static_cast<size_t>(h) * P, static_cast<uint32_t>(Lc - 1) * xrow + P * 2),
+              xrow, l0);
+      hq.load(make_buf(states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * N),
+                       static_cast<uint32_t>(P) * N * 4),
+              N * 4, 0);
+      __syncthreads();
+      put_rows(Ys, XP, yq);
+      put_rows_split(Hs, Bs, NP, hq);
+      if (tid < Q) {
+        cs2[tid] = t2.x * kLog2e;
+        dlt[tid] = t2.y;
+      }
     }
     __syncthreads();
     // every decay factor below is 2^(cs2_l - cs2_s) <= 1 (s <= l)
