@@ -92,8 +92,10 @@ __device__ __forceinline__ float qsum(float a) {
 
 // A tile of ROWS rows of W floats (source row stride `ld` floats) staged in two
 // phases, so that every load of a workgroup's tiles is in flight before the
-// first wait: load() into registers (rows at or past `valid` as zeros), then
-// store() into LDS at `pitch`.  For complex rows (W/2 (re, im) pairs per row),
+// first wait: load() into registers, then store() into LDS at `pitch`, rows at
+// or past `valid` (>= 1) as zeros.  The loads are unconditional (a row past
+// `valid` reads row valid - 1, zeroed at the store): a load under a branch
+// ends in a wait for it where the branch joins.  For complex rows (W/2 (re, im) pairs per row),
 // load_rot() fetches each row's (cos, sin) theta and store_rot() writes the W
 // real features [Re | Im] of z e^{-i theta} (CONJ = false) or [Re | -Im] of
 // z e^{+i theta} (CONJ = true).
@@ -104,22 +106,25 @@ struct TileRegs {
   static constexpr int PER = (ITEMS + NTHR - 1) / NTHR;
   float4 v[PER];
   float2 cs[PER];
+  int valid_;
+  __device__ __forceinline__ float4 val(int i) const {
+    return (threadIdx.x + i * NTHR) / VPR < valid_ ? v[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   __device__ __forceinline__ void load(const float* __restrict__ src, size_t ld, int valid) {
+    valid_ = valid;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int it = threadIdx.x + i * NTHR;
-      const int r = it / VPR, c4 = it % VPR;
-      v[i] = (ITEMS % NTHR == 0 || it < ITEMS) && r < valid
-                 ? *reinterpret_cast<const float4*>(src + r * ld + c4 * 4)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int r = min(it / VPR, valid - 1), c4 = it % VPR;
+      if (ITEMS % NTHR == 0 || it < ITEMS) v[i] = *reinterpret_cast<const float4*>(src + r * ld + c4 * 4);
     }
   }
   __device__ __forceinline__ void load_rot(const float2* __restrict__ rc, size_t rstride, int valid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int it = threadIdx.x + i * NTHR;
-      const int r = it / VPR;
-      cs[i] = (ITEMS % NTHR == 0 || it < ITEMS) && r < valid ? rc[r * rstride] : make_float2(1.f, 0.f);
+      const int r = min(it / VPR, valid - 1);
+      if (ITEMS % NTHR == 0 || it < ITEMS) cs[i] = rc[r * rstride];
     }
   }
   __device__ __forceinline__ void store(float* tile, int pitch) const {
@@ -127,7 +132,7 @@ struct TileRegs {
     for (int i = 0; i < PER; ++i) {
       const int it = threadIdx.x + i * NTHR;
       if (ITEMS % NTHR == 0 || it < ITEMS)
-        *reinterpret_cast<float4*>(tile + (it / VPR) * pitch + (it % VPR) * 4) = v[i];
+        *reinterpret_cast<float4*>(tile + (it / VPR) * pitch + (it % VPR) * 4) = val(i);
     }
   }
   template <bool CONJ>
@@ -137,7 +142,7 @@ struct TileRegs {
     for (int i = 0; i < PER; ++i) {
       const int it = threadIdx.x + i * NTHR;
       if (!(ITEMS % NTHR == 0 || it < ITEMS)) continue;
-      const float4 val = v[i];
+      const float4 val = this->val(i);  // zero past `valid`, whatever its rotation
       const float2 c = rcs[i];
       float* t = tile + (it / VPR) * pitch + 2 * (it % VPR);
       if constexpr (!CONJ) {
@@ -211,9 +216,20 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int w = wave_id(), role = w >> 2;
   const size_t r0 = static_cast<size_t>(b) * T + t0;
-  const float dt_raw = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
+  const int s = 16 * (w & 3) + r16;  // this lane's source token
+  const size_t row = (r0 + s) * H + h;
+  // The loads come in the order they are waited for (a wait for one load also
+  // waits for those issued before it): the step sizes and per-head values the
+  // prologue needs, this lane's rotation (the complex dB), then every tile
+  // into registers; the prologue's scans run while the tiles arrive.
+  // (unconditional loads of clamped rows: the prologue ignores dt past Lc, and
+  // the rotation is used only for s < Lc)
+  const float dt_raw = dt[(r0 + min(tid, Lc - 1)) * H + h];
+  const float a_h = A[h], bias_h = dt_bias ? dt_bias[h] : 0.0f;
+  const float Dh = D ? D[h] : 0.0f;
+  float2 rs = make_float2(1.0f, 0.0f);
+  if (CPLX && dBo != nullptr) rs = rot[(r0 + min(s, Lc - 1)) * H + h];
   {
-    // every tile's loads first, then the LDS stores
     TileRegs<P, kQ, kT8> tx, ty;
     TileRegs<NE, kQ, kT8> tb, tc;
     TileRegs<NE, P, kT8> tr;
@@ -223,6 +239,7 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
     tc.load(Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, Lc);
     tr.load(adj + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE), NE, P);
     if constexpr (CPLX) tb.load_rot(rot + r0 * H + h, H, Lc);
+    chunk_prologue(dt_raw, Lc, a_h, bias_h, dt_min, dt_max, dl, cs_hi, cs_lo, wsum, &tot, kQ);
     tx.store(Xs, XP);
     ty.store(Ys, XP);
     if constexpr (CPLX) {
@@ -234,15 +251,12 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
     }
     tr.store(Rs, NP);
   }
-  chunk_prologue(dt_raw, Lc, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, dl, cs_hi, cs_lo, wsum,
-                 &tot, kQ);  // (its barrier also publishes the staged tiles)
+  __syncthreads();
 
-  const int s = 16 * (w & 3) + r16;  // this lane's source token
   const float hs = cs_hi[s], ls = cs_lo[s];
   const float sc = SCALE ? dl[s] : (s < Lc ? 1.0f : 0.0f);
   const float fr = s < Lc ? __expf(static_cast<float>((tot - static_cast<double>(hs)) - static_cast<double>(ls)))
                           : 0.0f;  // e^{tot - cs_s} <= 1
-  const size_t row = (r0 + s) * H + h;
 
   // W0 = dy.x^T, rows l = 16 lt + 4q + i, masked, decayed and scaled into W
   f32x4 sW[4];
@@ -297,7 +311,6 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
         for (int pt = 0; pt < PT; ++pt)
           v[pt] = mfma_f32(Ys[(16 * lt + 4 * q + j) * XP + 16 * pt + r16], sS[lt][j], v[pt]);
     float xv = 0.0f, dyx = 0.0f;
-    const float Dh = D ? D[h] : 0.0f;
     float* dxr = dx + row * P;
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
@@ -348,7 +361,7 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
   if (s < Lc) {
     if (CPLX && dBo) {
       // each head its own group: dB = e^{i theta} (dB_eff[n] + i dB_eff[N+n]) straight out
-      const float2 r = rot[row];
+      const float2 r = rs;
 #pragma unroll
       for (int nt = 0; nt < NT / 2; ++nt) {
         float o[8];
@@ -416,9 +429,14 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int w = wave_id(), role = w >> 2;
   const size_t r0 = static_cast<size_t>(b) * T + t0;
-  const float dt_raw = tid < Lc ? dt[(r0 + tid) * H + h] : 0.0f;
+  const int l = 16 * (w & 3) + r16;  // this lane's target token
+  const size_t row = (r0 + l) * H + h;
+  // loads in the order they are waited for, as in the column kernel
+  const float dt_raw = dt[(r0 + min(tid, Lc - 1)) * H + h];
+  const float a_h = A[h], bias_h = dt_bias ? dt_bias[h] : 0.0f;
+  float2 rl = make_float2(1.0f, 0.0f);
+  if (CPLX && dCo != nullptr) rl = rot[(r0 + min(l, Lc - 1)) * H + h];
   {
-    // every tile's loads first, then the LDS stores
     TileRegs<P, kQ, kT8> tx, ty;
     TileRegs<NE, kQ, kT8> tb, tc;
     TileRegs<NE, P, kT8> th;
@@ -428,6 +446,7 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
     tc.load(Cm + (r0 * G + g) * NE, static_cast<size_t>(G) * NE, Lc);
     th.load(states + ((static_cast<size_t>(b) * nc + c) * H + h) * (static_cast<size_t>(P) * NE), NE, P);
     if constexpr (CPLX) tb.load_rot(rot + r0 * H + h, H, Lc);
+    chunk_prologue(dt_raw, Lc, a_h, bias_h, dt_min, dt_max, dl, cs_hi, cs_lo, wsum, &tot, kQ);
     tx.store(Xs, XP);
     ty.store(Ys, XP);
     if constexpr (CPLX) {
@@ -439,12 +458,9 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
     }
     th.store(Hs, NP);
   }
-  chunk_prologue(dt_raw, Lc, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, dl, cs_hi, cs_lo, wsum,
-                 &tot, kQ);
+  __syncthreads();
 
-  const int l = 16 * (w & 3) + r16;  // this lane's target token
   const float hl = cs_hi[l], ll = cs_lo[l];
-  const size_t row = (r0 + l) * H + h;
 
   // W0^T = x.dy^T, rows s = 16 st + 4q + i, masked, decayed and scaled
   f32x4 sW[4];
@@ -522,7 +538,7 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
   if (l < Lc) {
     if (CPLX && dCo) {
       // each head its own group: dC = e^{-i theta} (dC_eff[n] - i dC_eff[N+n]) straight out
-      const float2 r = rot[row];
+      const float2 r = rl;
 #pragma unroll
       for (int nt = 0; nt < NT / 2; ++nt) {
         float o[8];
