@@ -134,8 +134,16 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
   const int wid = wave_id();
   const int ng = wid % NGW, pg = wid / NGW;
 
-  // ---- loads: dt of the first chunk, then the first two quarters ----
+  // ---- loads: the heads' A and dt bias, dt of the first chunk, then the
+  // first two quarters (the per-head values loaded once, first: a wait for a
+  // load also waits for every load issued before it) ----
   const size_t r0 = sv.row0 + ts;
+  float a_h[HPW], bias_h[HPW];
+#pragma unroll
+  for (int e = 0; e < HPW; ++e) {
+    a_h[e] = A[h0 + e];
+    bias_h[e] = dt_bias ? dt_bias[h0 + e] : 0.0f;
+  }
   float dtv[HPW];
   auto load_dt = [&](int kc) {
     const int lc = min(Q, Ls - kc * Q);
@@ -186,8 +194,7 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
     float dd[HPW], uu[HPW];
 #pragma unroll
     for (int e = 0; e < HPW; ++e) {
-      const float bias = dt_bias ? dt_bias[h0 + e] : 0.0f;
-      dd[e] = tid < lc ? step_size(dtv[e], bias, dt_min, dt_max) : 0.0f;
+      dd[e] = tid < lc ? step_size(dtv[e], bias_h[e], dt_min, dt_max) : 0.0f;
       uu[e] = wave_inclusive_sum(dd[e]);
       if (lane == kWave - 1) wpart[e][wid] = uu[e];
     }
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(512, 4) void ssd_state_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < HPW; ++e) {
       const int h = h0 + e;
-      const float a_re = A[h];
+      const float a_re = a_h[e];
       float before = 0.0f, total = 0.0f;
 #pragma unroll
       for (int w = 0; w < WW; ++w) {
