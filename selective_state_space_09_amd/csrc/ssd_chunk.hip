@@ -48,12 +48,25 @@ namespace ssd {
 // B slab -> bT[k][s - s0] = w_s B_s[k] (transposed, weighted).
 template <int ST, int N>
 struct StateBSlab : Slab<ST, N / 4, 1> {
+  // complex rows: each item's (cos, sin) theta_s, loaded beside the rows
+  // (rot[s * stride] for token s; rows past Lc (>= 1) read row Lc - 1, whose
+  // weight is zero)
+  float2 rc[Slab<ST, N / 4, 1>::PER];
+  __device__ __forceinline__ void load_rot(const float2* __restrict__ rot, size_t stride, int s0, int Lc) {
+#pragma unroll
+    for (int i = 0; i < this->PER; ++i) {
+      const int it = threadIdx.x + i * kThreads;
+      if (this->ITEMS % kThreads == 0 || it < this->ITEMS)
+        rc[i] = rot[static_cast<size_t>(min(s0 + it / (N / 4), Lc - 1)) * stride];
+    }
+  }
+
   // complex rows (N / 2 values as (re, im) pairs) rotated per token into the
   // N real features [Re | Im] of z e^{-i theta} (CONJ = false: B) or
-  // [Re | -Im] of z e^{+i theta} (CONJ = true: C); rc[s] = (cos, sin) theta_s
+  // [Re | -Im] of z e^{+i theta} (CONJ = true: C), with the rotations of
+  // load_rot
   template <bool CONJ>
-  __device__ __forceinline__ void store_rot(float* bT, const float* wre, const float2* rc, int s0,
-                                            int Q) const {
+  __device__ __forceinline__ void store_rot(float* bT, const float* wre, int s0, int Q) const {
     constexpr int XP = ST + Pad<float>::row;
     constexpr int NH = N / 2;
 #pragma unroll
@@ -63,7 +76,7 @@ struct StateBSlab : Slab<ST, N / 4, 1> {
       const int ng = it % (N / 4), sl = it / (N / 4);
       const int s = s0 + sl;
       const float w = s < Q ? wre[s] : 0.f;
-      const float2 r = s < Q ? rc[s] : make_float2(1.f, 0.f);
+      const float2 r = rc[i];
       const uint4 u = this->v[i][0];
       const float re0 = __uint_as_float(u.x), im0 = __uint_as_float(u.y);
       const float re1 = __uint_as_float(u.z), im1 = __uint_as_float(u.w);
@@ -133,7 +146,6 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   __shared__ __attribute__((aligned(16))) float bT[NBUF][N * XP];
   __shared__ float dl[TQ], cs_hi[TQ], cs_lo[TQ];
   __shared__ float wre[TQ];
-  __shared__ float2 rcs[kCplx ? TQ : 1];
   __shared__ double wsum[4], tot;
 
   int b, c, h;
@@ -147,21 +159,24 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
 
   // issue the first global loads before any arithmetic
   const size_t dt_base = (static_cast<size_t>(b) * T + t0) * H + h;
-  const float dt_raw = tid < Lc ? dt[dt_base + static_cast<size_t>(tid) * H] : 0.0f;
+  const float dt_raw = dt[dt_base + static_cast<size_t>(min(tid, Lc - 1)) * H];  // (ignored past Lc)
   const char* xbase = reinterpret_cast<const char*>(
       x + (static_cast<size_t>(b) * T + t0) * H * P + static_cast<size_t>(h) * P);
   const size_t xrow = static_cast<size_t>(H) * P * sizeof(float);
   const char* bbase = reinterpret_cast<const char*>(
       Bm + (static_cast<size_t>(b) * T + t0) * G * N + static_cast<size_t>(g) * N);
   const size_t brow = static_cast<size_t>(G) * N * sizeof(float);
+  // (dt ahead of the slab loads in the issue order: the prologue waits for it,
+  // and a wait for a load also waits for every load issued before it)
+  __builtin_amdgcn_sched_barrier(0);
+  // (rows past the chunk read clamped: their weights w_s are zero)
   XSlabF32<ST, P> xs;
   StateBSlab<ST, N> bs;
-  xs.load(xbase, xrow, 0, Lc);
-  bs.load(bbase, brow, 0, Lc);
-
+  xs.load_clamped(xbase, xrow, 0, Lc);
+  bs.load_clamped(bbase, brow, 0, Lc);
   if constexpr (kCplx) {
     static_assert(NBUF == 1, "complex rows: one stage");
-    if (tid < Q) rcs[tid] = tid < Lc ? rot[dt_base + static_cast<size_t>(tid) * H] : make_float2(1.f, 0.f);
+    bs.load_rot(rot + dt_base, H, 0, Lc);
   }
   const double cum =
       chunk_prologue(dt_raw, Lc, a_re, bias, dt_min, dt_max, dl, cs_hi, cs_lo, wsum, &tot, Q);
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   __syncthreads();
   xs.store(xT[0]);
   if constexpr (kCplx)
-    bs.template store_rot<MODE == kStateCplxAdj>(bT[0], wre, rcs, 0, Q);
+    bs.template store_rot<MODE == kStateCplxAdj>(bT[0], wre, 0, Q);
   else
     bs.store(bT[0], wre, 0, Q);
   __syncthreads();
@@ -199,8 +214,8 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     const int cur = NBUF == 1 ? 0 : it & 1;
     const bool more = NBUF > 1 && it + 1 < ntiles;
     if (more) {
-      xs.load(xbase, xrow, (it + 1) * ST, Lc);
-      bs.load(bbase, brow, (it + 1) * ST, Lc);
+      xs.load_clamped(xbase, xrow, (it + 1) * ST, Lc);
+      bs.load_clamped(bbase, brow, (it + 1) * ST, Lc);
     }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {

@@ -120,7 +120,10 @@ __device__ __forceinline__ double chunk_prologue(float dt_raw, int Lc, float a_r
                                                  float lo, float hi, float* dl, float* cs_hi,
                                                  float* cs_lo, double* wsum, double* tot, int Q) {
   const int l = threadIdx.x;
-  const float d = l < Lc ? step_size(dt_raw, bias, lo, hi) : 0.0f;
+  // (computed in every lane, then selected: a use under a branch would pull
+  // the caller's dt load into that branch, behind every load issued before it)
+  const float dv = step_size(dt_raw, bias, lo, hi);
+  const float d = l < Lc ? dv : 0.0f;
   const double cum = block_inclusive_scan(static_cast<double>(a_re) * static_cast<double>(d), wsum);
   if (l < Q) {
     dl[l] = d;
@@ -164,6 +167,24 @@ struct Slab {
         if (it < ITEMS && s < Lc)
           val = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(s) * row_bytes + vv * 16);
         v[i][r] = val;
+      }
+    }
+  }
+
+  // the same with rows at or past Lc (>= 1) read as row Lc - 1 instead of
+  // zero: no load under a branch (which ends in a wait for it where the
+  // branch joins), for callers whose products weight those rows by zero
+  __device__ __forceinline__ void load_clamped(const char* __restrict__ base, size_t row_bytes, int s0,
+                                               int Lc) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * kThreads;
+      const int vv = it % VPR, rg = it / VPR;
+#pragma unroll
+      for (int r = 0; r < RPI; ++r) {
+        const int s = min(s0 + rg * RPI + r, Lc - 1);
+        if (ITEMS % kThreads == 0 || it < ITEMS)
+          v[i][r] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(s) * row_bytes + vv * 16);
       }
     }
   }
