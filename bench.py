@@ -1016,7 +1016,7 @@ def bench_bwd(args, cfg):
 # the 14 event slots of ssd_complex_chunk_bwd_ev; None: a slot no kernel fills
 # (the chunk constants form inside the adjoint passing), and the group sums
 # run only when a group holds several heads
-CPLX_BWD_KERNELS = ["ssd_cplx_rotate_kernel", "ssd_state_kernel(unit scale)", "ssd_pass_kernel",
+CPLX_BWD_KERNELS = ["ssd_cplx_frame_kernel", "ssd_state_kernel(unit scale)", "ssd_pass_kernel",
                     "ssd_state_kernel(adjoint)", "ssd_f32_adj_pass_kernel", "ssd_f32_col_kernel",
                     "ssd_f32_row_kernel", None, "ssd_cplx_tau_kernel",
                     "ssd_cplx_rho_total_kernel", "ssd_f32_dt_kernel", "ssd_f32_dt_sum_kernel",

@@ -38,12 +38,11 @@
 // The angles theta_t are reduced modulo 2 pi in double precision.
 //
 // Kernels (one workgroup per (chunk, head, batch) unless noted):
-//   ssd_cplx_u_local, ssd_cplx_rotate  (complex) u and theta over the sequence
-//                         (fp64: chunk sums, then each chunk adds the totals of the
-//                         earlier ones), (cos, sin) theta per token, the rotated h0
-//                         and dh_final; B_eff and C_eff are never stored: the
-//                         chunk-state and block kernels form them from B and C as
-//                         they stage them
+//   ssd_cplx_frame      (complex; one workgroup per (head, batch)) u and theta
+//                         over the sequence (an fp64 scan), (cos, sin) theta per
+//                         token, the rotated h0 and dh_final; B_eff and C_eff are
+//                         never stored: the chunk-state and block kernels form them
+//                         from B and C as they stage them
 //   chunk states, state passing, adjoint chunk states: ssd_chunk.hip's fp32
 //                         kernels (run_states_f32, run_pass_f32)
 //   ssd_f32_adj_pass      R_c in place over G_c, last chunk first; dh0; the
@@ -625,61 +624,68 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_adj_pass_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Complex: the sequence frame.  u_t = delta_1 + .. + delta_t over the
-// sequence (fp64) in two steps: each chunk's local sums and total
-// (ssd_cplx_u_local), then each chunk adds the totals of the chunks before it
-// (ssd_cplx_rotate, one workgroup per (chunk, head, batch)) and keeps
-// (cos, sin) theta_t, theta_t = beta u_t mod 2 pi, per token and head (the
-// kernels that read B and C rotate them by it as they stage them); the last
-// chunk's workgroup turns h0 into [Re | Im] rows and dh_final, rotated by
-// -theta at the last token, likewise; the decay alpha of each head.
+// Complex: the sequence frame, one workgroup per (head, batch).  u_t =
+// delta_1 + .. + delta_t over the sequence (fp64: each thread sums 8
+// consecutive tokens, one block scan per 2048 tokens, carried from block to
+// block) and (cos, sin) theta_t, theta_t = beta u_t mod 2 pi, per token
+// and head (the kernels that read B and C rotate them by it as they stage
+// them); then h0 as [Re | Im] rows and dh_final, rotated by -theta at the last
+// token, likewise; the decay alpha of each head.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kQ) void ssd_cplx_u_local_kernel(
+__global__ __launch_bounds__(kThreads) void ssd_cplx_frame_kernel(
     const float* __restrict__ dt, const float* __restrict__ dt_bias, float dt_min, float dt_max,
-    double* __restrict__ uo, double* __restrict__ ctot, int T, int H, int nc) {
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int t = c * kQ + lane;
-  const size_t row = (static_cast<size_t>(b) * T + (t < T ? t : 0)) * H + h;
-  const double d = t < T ? static_cast<double>(step_size(dt[row], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max))
-                         : 0.0;
-  const double s = wave_inclusive_sum_d(d);
-  if (t < T) uo[row] = s;
-  if (lane == kQ - 1) ctot[(static_cast<size_t>(b) * H + h) * nc + c] = s;
-}
-
-__global__ __launch_bounds__(kThreads) void ssd_cplx_rotate_kernel(
     const float* __restrict__ A, const float* __restrict__ h0, const float* __restrict__ dh_final,
-    double* __restrict__ uo, const double* __restrict__ ctot, float2* __restrict__ rot,
-    float* __restrict__ alpha, float* __restrict__ h0e, float* __restrict__ dhfe, int T, int H, int P,
-    int N, int nc) {
-  __shared__ double u_last;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int t0 = c * kQ, Lc = max(0, min(kQ, T - t0));
+    double* __restrict__ uo, float2* __restrict__ rot, float* __restrict__ alpha, float* __restrict__ h0e,
+    float* __restrict__ dhfe, int T, int H, int P, int N) {
+  constexpr int TPT = 8;  // consecutive tokens per thread in a block of kThreads * TPT
+  __shared__ double wtot[kThreads / kWave];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
   const float be = A[2 * h + 1];
+  const float bias = dt_bias ? dt_bias[h] : 0.0f;
+  if (tid == 0 && b == 0) alpha[h] = A[2 * h];
   const size_t bh = static_cast<size_t>(b) * H + h;
-  if (tid == 0 && b == 0 && c == 0) alpha[h] = A[2 * h];
-  if (tid < kQ) {
-    double pre = 0.0;  // totals of the earlier chunks
-    for (int cc = tid; cc < c; cc += kQ) pre += ctot[bh * nc + cc];
-    pre = __shfl(wave_inclusive_sum_d(pre), kQ - 1);
-    const size_t row = (static_cast<size_t>(b) * T + t0 + (tid < Lc ? tid : 0)) * H + h;
-    const double u = tid < Lc ? uo[row] + pre : pre;
-    if (tid < Lc) {
-      uo[row] = u;
-      float cs, sn;
-      rot_cs(static_cast<double>(be) * u, cs, sn);
-      rot[row] = make_float2(cs, sn);
+  double carry = 0.0;  // u of the tokens before the block
+  for (int tb = 0; tb < T; tb += TPT * kThreads) {
+    const int t0 = tb + TPT * tid;  // this thread's first token
+    float dv[TPT];
+#pragma unroll
+    for (int r = 0; r < TPT; ++r)  // (clamped rows: no load under a branch)
+      dv[r] = dt[(static_cast<size_t>(b) * T + min(t0 + r, T - 1)) * H + h];
+    double us[TPT], run = 0.0;  // this thread's inclusive sums
+#pragma unroll
+    for (int r = 0; r < TPT; ++r) {
+      run += t0 + r < T ? static_cast<double>(step_size(dv[r], bias, dt_min, dt_max)) : 0.0;
+      us[r] = run;
     }
-    if (tid == (Lc > 0 ? Lc - 1 : 0)) u_last = Lc > 0 ? u : 0.0;
+    const double incl = wave_inclusive_sum_d(run);
+    if (lane == kWave - 1) wtot[wid] = incl;
+    __syncthreads();
+    double before = carry + (incl - run), total = carry;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      const double pw = wtot[w];
+      before += w < wid ? pw : 0.0;
+      total += pw;
+    }
+    __syncthreads();  // (wtot is rewritten by the next block)
+#pragma unroll
+    for (int r = 0; r < TPT; ++r) {
+      if (t0 + r < T) {
+        const double u = before + us[r];
+        const size_t row = (static_cast<size_t>(b) * T + t0 + r) * H + h;
+        uo[row] = u;
+        float cs, sn;
+        rot_cs(static_cast<double>(be) * u, cs, sn);
+        rot[row] = make_float2(cs, sn);
+      }
+    }
+    carry = total;
   }
-  if (c != gridDim.x - 1) return;
-  __syncthreads();
-  const int NE = 2 * N;
   // h0 -> [Re | Im] rows; dh_final -> e^{-i theta_{T-1}} dh_final as [Re | Im]
   float cl = 1.0f, sl = 0.0f;
-  if (T > 0) rot_cs(static_cast<double>(be) * u_last, cl, sl);
+  if (T > 0) rot_cs(static_cast<double>(be) * carry, cl, sl);
+  const int NE = 2 * N;
   for (int i = tid; i < P * N; i += kThreads) {
     const int p = i / N, n = i % N;
     const size_t src = (bh * P * N + i) * 2;
@@ -910,11 +916,11 @@ __global__ __launch_bounds__(kThreads) void ssd_cplx_dh0_kernel(const float* __r
 // Workspace of the fp32 backward (256-byte aligned regions): chunk states
 // (recomputed; h_in over them), decays, adjoint states (R over G), per-head
 // dB and dC, per-token values (f1, f2, col, row, x.v, dy.x, rho_B, rho_C),
-// chunk constants and shares; complex: u, (cos, sin) theta, chunk step totals, alpha, rotated h0,
+// chunk constants and shares; complex: u, (cos, sin) theta, alpha, rotated h0,
 // dh_final and h_final, rho chunk totals.
 // ---------------------------------------------------------------------------
 struct F32BwdLayout {
-  size_t S, dec, adj, dBh, dCh, tokv, cst, part, u, rot, ctot, alpha, h0e, dhfe, hfe, rtot, dh0e, total;
+  size_t S, dec, adj, dBh, dCh, tokv, cst, part, u, rot, alpha, h0e, dhfe, hfe, rtot, dh0e, total;
 };
 static F32BwdLayout f32_layout(int Bsz, int T, int H, int P, int N, bool cplx) {
   const int NE = cplx ? 2 * N : N;
@@ -936,7 +942,6 @@ static F32BwdLayout f32_layout(int Bsz, int T, int H, int P, int N, bool cplx) {
     const size_t hs = static_cast<size_t>(Bsz) * H * P * NE * 4;
     L.u = o;     o += up(tok * 8);
     L.rot = o;   o += up(tok * 8);
-    L.ctot = o;  o += up(static_cast<size_t>(Bsz) * H * nc * 8);
     L.alpha = o; o += up(static_cast<size_t>(H) * 4);
     L.h0e = o;   o += up(hs);
     L.dhfe = o;  o += up(hs);
@@ -1077,27 +1082,9 @@ static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   float* hfe = reinterpret_cast<float*>(ws + L.hfe);
   float* dh0e = reinterpret_cast<float*>(ws + L.dh0e);
   float2* rot = reinterpret_cast<float2*>(ws + L.rot);
-  double* ctot = reinterpret_cast<double*>(ws + L.ctot);
-  // rotation: the pair of event slot 0 spans both kernels
-  const hipEvent_t* e0 = E(0);
-  if (nc > 0) {
-    if (e0)
-      hipExtLaunchKernelGGL(ssd_cplx_u_local_kernel, dim3(nc, a.H, a.Bsz), dim3(kQ), 0, st, e0[0], nullptr, 0,
-                            a.dt, a.dt_bias, a.dt_min, a.dt_max, u, ctot, a.T, a.H, nc);
-    else
-      hipLaunchKernelGGL(ssd_cplx_u_local_kernel, dim3(nc, a.H, a.Bsz), dim3(kQ), 0, st, a.dt, a.dt_bias,
-                         a.dt_min, a.dt_max, u, ctot, a.T, a.H, nc);
-  } else if (e0) {
-    (void)hipEventRecord(e0[0], st);
-  }
-  const dim3 rgrid(nc > 0 ? nc : 1, a.H, a.Bsz);
-  if (e0)
-    hipExtLaunchKernelGGL(ssd_cplx_rotate_kernel, rgrid, dim3(kThreads), 0, st, nullptr, e0[1], 0, a.A, a.h0,
-                          a.dh_final, u, static_cast<const double*>(ctot), rot, alpha, h0e, dhfe, a.T, a.H, P,
-                          N, nc);
-  else
-    hipLaunchKernelGGL(ssd_cplx_rotate_kernel, rgrid, dim3(kThreads), 0, st, a.A, a.h0, a.dh_final, u,
-                       static_cast<const double*>(ctot), rot, alpha, h0e, dhfe, a.T, a.H, P, N, nc);
+  // the sequence frame (event slot 0)
+  launch_k(true, ssd_cplx_frame_kernel, dim3(a.H, a.Bsz), dim3(kThreads), st, E(0), a.dt, a.dt_bias, a.dt_min,
+           a.dt_max, a.A, a.h0, a.dh_final, u, rot, alpha, h0e, dhfe, a.T, a.H, P, N);
   // the rotated-frame real problem: 2N features (B and C rotated as they are
   // staged), decay alpha, input scale 1
   const float2* rotc = rot;
