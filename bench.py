@@ -845,7 +845,7 @@ def cpu_baseline_conv(inp, target_s):
 
 BWD_KERNELS = ["ssd_state_bf16_kernel", "ssd_pass_bf16_kernel", "ssd_adj_state_kernel",
                "ssd_adj_pass_kernel", "ssd_bwd_dxdb_kernel", "ssd_bwd_dc_kernel",
-               "ssd_bwd_const_kernel", "ssd_bwd_dt_kernel", "ssd_bwd_dt_sum_kernel",
+               None, "ssd_bwd_dt_kernel", "ssd_bwd_dt_sum_kernel",
                "ssd_bwd_reduce_kernel(dB)", "ssd_bwd_reduce_kernel(dC)"]
 
 
@@ -870,7 +870,8 @@ def bwd_kernel_costs(dims, nparts):
         "ssd_state_bf16_kernel": (x + bc + Bsz * T * H * 4 + st + dec + tok, units * 2 * Q * P * N),
         "ssd_pass_bf16_kernel": (2 * st + dec, 0),
         "ssd_adj_state_kernel": (x + bc + tok + st, units * 2 * Q * P * N),
-        "ssd_adj_pass_kernel": (2 * st + dec, 0),
+        # G in, R out, h_in in (the chunk constants' shares)
+        "ssd_adj_pass_kernel": (3 * st + dec, 0),
         # x, dy, B, C, tok, R in; dx, x.v, dy.x, f2, col, row shares, dB partials out
         "ssd_bwd_dxdb_kernel": (3 * x + 2 * bc + tok + st + 4 * pt + pt * (nb + 1) / 2 + part,
                                 units * (2 * tri * P * 2 + 2 * tri * N + 2 * Q * N * P * 2)
@@ -878,7 +879,6 @@ def bwd_kernel_costs(dims, nparts):
         # x, dy, B, C, tok, h_in in; f1, dC partials out
         "ssd_bwd_dc_kernel": (2 * x + 2 * bc + tok + st + pt + part,
                               units * (2 * tri * P + 2 * tri * N + 2 * Q * P * N)),
-        "ssd_bwd_const_kernel": (2 * st + dec, 0),
         "ssd_bwd_dt_kernel": (Bsz * T * H * 4 + 6 * pt + pt * (nb + 1) / 2, 0),
         "ssd_bwd_dt_sum_kernel": (Bsz * H * nc * 24 + H * 12, 0),
         "ssd_bwd_reduce_kernel(dB)": (part + out, 0),
@@ -954,6 +954,8 @@ def bench_bwd(args, cfg):
     costs = bwd_kernel_costs(dims, nparts)
     kern = {}
     for k, name in enumerate(BWD_KERNELS):
+        if name is None:  # (the chunk constants: formed by the adjoint passing)
+            continue
         avg = float(np.mean([hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in evs]))
         nb_, fl = costs[name]
         ent = {"avg_us": avg * 1e3, "own_io_bytes": nb_, "own_io_gbs": nb_ / (avg / 1e3) / 1e9}

@@ -432,10 +432,11 @@ int ssd_chunk_bwd(const void *x, const float *dt, const float *A, const void *B,
 /*
  * Measurement variant of ssd_chunk_bwd: identical arguments, kernels and
  * result, plus `events` (hipEvent_t passed as void*), or NULL.  SSD_BF16: 22
- * events, a start/stop pair bound to each of the 11 kernels' dispatches in
- * order (chunk states, state passing, adjoint chunk states, adjoint passing,
- * dx/dB blocks, dC blocks, chunk constants of da, step-size gradients per
- * chunk, their sums per head, dB sum, dC sum).  SSD_F32: 28 events, the 14
+ * events, a start/stop pair bound to each of 11 kernel slots in order (chunk
+ * states, state passing, adjoint chunk states, adjoint passing (which also
+ * forms the chunk constants of da), dx/dB blocks, dC blocks, chunk constants
+ * (an empty pair, recorded back to back), step-size gradients per chunk,
+ * their sums per head, dB sum, dC sum).  SSD_F32: 28 events, the 14
  * slots of ssd_complex_chunk_bwd_ev (the complex-only slots record their pair
  * back to back).
  */

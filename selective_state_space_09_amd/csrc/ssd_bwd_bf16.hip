@@ -278,47 +278,72 @@ __global__ __launch_bounds__(kThreads) void ssd_adj_state_kernel(
 // ---------------------------------------------------------------------------
 // Adjoint passing, last chunk first:  R_{nc-1} = dh_final,
 // R_{c-1} = lambda_c R_c + G_c,  dh0 = R_{-1}.  R_c overwrites G_c in place
-// (fp32, after G_c is consumed).  One thread per 4 consecutive n.
+// (fp32, after G_c is consumed).  One thread per 4 consecutive n; the chunks
+// in groups of 8 whose loads are issued together.  Beside it, the chunk
+// constants of da, e^{tot_c} <R_c, H_in(c)> (the term shared by every step of
+// chunk c): each workgroup reads H_in(c) with R_c and writes its fp64 share
+// of the inner product per chunk, cpart[(b, h, c) * nblk + block], which the
+// step-size kernel sums and scales.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ssd_adj_pass_kernel(
     float* __restrict__ adj, const float* __restrict__ decay, const float* __restrict__ dh_final,
-    float* __restrict__ dh0, int H, int PN, int nc) {
+    float* __restrict__ dh0, const float* __restrict__ states, double* __restrict__ cpart, int H, int PN,
+    int nc) {
   constexpr int PF = 8;
+  __shared__ double ws[PF][kThreads / kWave];
   const int h = blockIdx.y, b = blockIdx.z;
-  const int e4 = blockIdx.x * kThreads + threadIdx.x;
-  if (e4 * 4 >= PN) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int e4 = blockIdx.x * kThreads + tid;
+  const bool in = e4 * 4 < PN;
+  const int nblk = gridDim.x;
   const size_t bh = static_cast<size_t>(b) * H + h;
   const size_t cstride = static_cast<size_t>(H) * PN;
-  float* base = adj + static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + e4 * 4;
+  const size_t off = static_cast<size_t>(b) * nc * cstride + h * static_cast<size_t>(PN) + (in ? e4 * 4 : 0);
+  float* base = adj + off;
+  const float* hb = states + off;
   const float* dc = decay + bh * nc;
-  float4 r = dh_final ? *reinterpret_cast<const float4*>(dh_final + bh * PN + e4 * 4)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 r = in && dh_final ? *reinterpret_cast<const float4*>(dh_final + bh * PN + e4 * 4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c1 = nc; c1 > 0; c1 -= PF) {  // chunks c1-1 down to c1-PF
-    float4 gv[PF];
+    float4 gv[PF], hv[PF];
     float ld[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int cc = c1 - 1 - j;
-      if (cc >= 0) {
+      gv[j] = hv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      ld[j] = 0.0f;
+      if (cc >= 0 && in) {
         gv[j] = *reinterpret_cast<const float4*>(base + cc * cstride);
-        ld[j] = dc[cc];
+        hv[j] = *reinterpret_cast<const float4*>(hb + cc * cstride);
+      }
+      if (cc >= 0) ld[j] = dc[cc];
+    }
+    double part[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int cc = c1 - 1 - j;
+      // R_c = r here: its share of <R_c, H_in(c)>, then the update
+      part[j] = static_cast<double>(r.x * hv[j].x + r.y * hv[j].y) +
+                static_cast<double>(r.z * hv[j].z + r.w * hv[j].w);
+      if (cc >= 0) {
+        if (in) *reinterpret_cast<float4*>(base + cc * cstride) = r;
+        const float l = ld[j];
+        r = make_float4(l * r.x + gv[j].x, l * r.y + gv[j].y, l * r.z + gv[j].z, l * r.w + gv[j].w);
       }
     }
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int cc = c1 - 1 - j;
-      if (cc >= 0) {
-        const float4 hold = r;
-        const float l = ld[j];
-        r.x = l * r.x + gv[j].x;
-        r.y = l * r.y + gv[j].y;
-        r.z = l * r.z + gv[j].z;
-        r.w = l * r.w + gv[j].w;
-        *reinterpret_cast<float4*>(base + cc * cstride) = hold;
-      }
+      double v = part[j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+      if (lane == 0) ws[j][wid] = v;
     }
+    __syncthreads();
+    if (tid < PF && c1 - 1 - tid >= 0)
+      cpart[(bh * nc + (c1 - 1 - tid)) * nblk + blockIdx.x] = (ws[tid][0] + ws[tid][1]) + (ws[tid][2] + ws[tid][3]);
+    __syncthreads();  // (ws is rewritten by the next group of chunks)
   }
-  if (dh0) *reinterpret_cast<float4*>(dh0 + bh * PN + e4 * 4) = r;
+  if (in && dh0) *reinterpret_cast<float4*>(dh0 + bh * PN + e4 * 4) = r;
 }
 
 // Work unit of the two block kernels: (b, chunk, 64-token block, head group).
@@ -908,41 +933,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Chunk constants: e^{tot_c} <R_c, H_in(c)> (the term of da shared by every
-// step of chunk c), fp32 states, one workgroup per (chunk, head, batch).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void ssd_bwd_const_kernel(
-    const float* __restrict__ adj, const float* __restrict__ states,
-    const float* __restrict__ decay, double* __restrict__ cst, int H, int PN, int nc) {
-  __shared__ double ws4[4];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
-  const size_t bh = static_cast<size_t>(b) * H + h;
-  const size_t slot = ((static_cast<size_t>(b) * nc + c) * H + h) * PN;
-  double s = 0.0;
-  for (int i = tid * 8; i < PN; i += kThreads * 8) {
-    const float4 r0 = *reinterpret_cast<const float4*>(adj + slot + i);
-    const float4 r1 = *reinterpret_cast<const float4*>(adj + slot + i + 4);
-    const float4 h0v = *reinterpret_cast<const float4*>(states + slot + i);
-    const float4 h1v = *reinterpret_cast<const float4*>(states + slot + i + 4);
-    float acc = r0.x * h0v.x;
-    acc = fmaf(r0.y, h0v.y, acc);
-    acc = fmaf(r0.z, h0v.z, acc);
-    acc = fmaf(r0.w, h0v.w, acc);
-    acc = fmaf(r1.x, h1v.x, acc);
-    acc = fmaf(r1.y, h1v.y, acc);
-    acc = fmaf(r1.z, h1v.z, acc);
-    acc = fmaf(r1.w, h1v.w, acc);
-    s += acc;
-  }
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
-  if (lane == 0) ws4[wid] = s;
-  __syncthreads();
-  if (tid == 0)
-    cst[bh * nc + c] = static_cast<double>(decay[bh * nc + c]) * (ws4[0] + ws4[1] + ws4[2] + ws4[3]);
-}
-
-// ---------------------------------------------------------------------------
 // Step-size gradients, one workgroup per (chunk, head, batch), thread l =
 // token l of the chunk:
 //   da_l = box_l + sum_{l' >= l} f1_l' + sum_{s < l} f2_s + e^{tot} <R_c, H_in>,
@@ -956,9 +946,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
     const float* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
     float dt_min, float dt_max, const float* __restrict__ f1, const float* __restrict__ f2,
     const float* __restrict__ colp, const float* __restrict__ rowp, const float* __restrict__ xv,
-    const float* __restrict__ dyx,
-    const double* __restrict__ cst, float* __restrict__ ddt, double* __restrict__ part, int Bsz,
-    int T, int H, int Q, int nc) {
+    const float* __restrict__ dyx, const double* __restrict__ cpart, const float* __restrict__ decay,
+    int nblk, float* __restrict__ ddt, double* __restrict__ part, int Bsz, int T, int H, int Q, int nc) {
   __shared__ double wsum[3][4];
   __shared__ double red[3][4];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -967,6 +956,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
   const float bias = dt_bias ? dt_bias[h] : 0.0f;
   const size_t BTH = static_cast<size_t>(Bsz) * T * H;
   const size_t bhc = (static_cast<size_t>(b) * H + h) * nc + c;
+  // the chunk constant e^{tot_c} <R_c, H_in(c)>: the adjoint passing's shares
+  double cst = 0.0;
+  for (int k = 0; k < nblk; ++k) cst += cpart[bhc * nblk + k];
+  cst *= static_cast<double>(decay[bhc]);
   const int t = c * Q + tid;
   const bool in = tid < Q && t < T;
   const size_t row = (static_cast<size_t>(b) * T + (in ? t : 0)) * H + h;
@@ -1004,7 +997,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
   const double box = sc[2] + before[2] - gv;
   double sA = 0.0, sBias = 0.0, sD = 0.0;
   if (in) {
-    const double da = box + f1_suffix + f2_prefix + cst[bhc];
+    const double da = box + f1_suffix + f2_prefix + cst;
     const float z = dt[row] + bias;
     const float d = step_size(dt[row], bias, dt_min, dt_max);
     const float xvt = xv[row];
@@ -1104,8 +1097,8 @@ static BwdLayout bwd_layout(int Bsz, int T, int H, int P, int G, int N, int chun
   o += up(tok);
   L.row = o;
   o += up(tok * ((chunk + kBlk - 1) / kBlk));
-  L.cst = o;
-  o += up(static_cast<size_t>(Bsz) * H * nc * 8);
+  L.cst = o;  // the adjoint passing's shares of the chunk constants, per workgroup
+  o += up(static_cast<size_t>(Bsz) * H * nc * 8 * ((P * N / 4 + kThreads - 1) / kThreads));
   L.dtp = o;
   o += up(static_cast<size_t>(Bsz) * H * nc * 3 * 8);
   const int nparts = (H / G) / bwd_heads_per_group(H, G);
@@ -1174,8 +1167,11 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const unsigned blocks = static_cast<unsigned>((npairs + kXCD - 1) / kXCD) * kXCD * a.H;
   launch_k(nc > 0, ssd_adj_state_kernel<P, N>, dim3(blocks), dim3(kThreads), st, ev ? ev + 4 : nullptr,
            dy, C, tok, adj, a.T, a.H, a.G, Q, nc, npairs);
-  launch_k(true, ssd_adj_pass_kernel, dim3((P * N / 4 + kThreads - 1) / kThreads, a.H, a.Bsz),
-           dim3(kThreads), st, ev ? ev + 6 : nullptr, adj, decay, a.dh_final, a.dh0, a.H, P * N, nc);
+  // the adjoint passing also forms each chunk's constant, as per-workgroup shares
+  const int nblk = (P * N / 4 + kThreads - 1) / kThreads;
+  double* cpart = reinterpret_cast<double*>(ws + L.cst);
+  launch_k(true, ssd_adj_pass_kernel, dim3(nblk, a.H, a.Bsz), dim3(kThreads), st, ev ? ev + 6 : nullptr, adj,
+           decay, a.dh_final, a.dh0, states, cpart, a.H, P * N, nc);
   const int HPG = bwd_heads_per_group(a.H, a.G);
   const int nb = (Q + kBlk - 1) / kBlk;
   const unsigned bblocks = static_cast<unsigned>(nb) * units_per_rank(a.H / HPG, nc, a.Bsz);
@@ -1184,17 +1180,16 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
            dyx, f2, col, rowp, dBp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
   launch_k(nc > 0, ssd_bwd_dc_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 10 : nullptr,
            x, B, C, dy, tok, states, f1, dCp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
-  double* cst = reinterpret_cast<double*>(ws + L.cst);
-  launch_k(nc > 0, ssd_bwd_const_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
-           ev ? ev + 12 : nullptr, static_cast<const float*>(adj), states, decay, cst, a.H, P * N,
-           nc);
+  // (the chunk constants' slot: an empty pair, recorded back to back)
+  launch_k(false, ssd_bwd_reduce_kernel, dim3(1), dim3(kThreads), st, ev ? ev + 12 : nullptr,
+           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), size_t{0}, 0);
   double* dtp = reinterpret_cast<double*>(ws + L.dtp);
   launch_k(nc > 0, ssd_bwd_dt_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
            ev ? ev + 14 : nullptr, a.dt, a.A, a.dt_bias, a.dt_min, a.dt_max, static_cast<const float*>(f1),
            static_cast<const float*>(f2), static_cast<const float*>(col), static_cast<const float*>(rowp),
            static_cast<const float*>(xv),
-           static_cast<const float*>(dyx), static_cast<const double*>(cst), a.ddt, dtp, a.Bsz, a.T, a.H,
-           Q, nc);
+           static_cast<const float*>(dyx), static_cast<const double*>(cpart), decay, nblk, a.ddt, dtp, a.Bsz,
+           a.T, a.H, Q, nc);
   launch_k(true, ssd_bwd_dt_sum_kernel, dim3((a.H + kThreads - 1) / kThreads), dim3(kThreads), st,
            ev ? ev + 16 : nullptr, static_cast<const double*>(dtp), a.dA, a.ddt_bias, a.dD, a.Bsz, a.H,
            nc);
