@@ -206,6 +206,7 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
   __shared__ __attribute__((aligned(16))) float Bs[kQ * NP];
   __shared__ __attribute__((aligned(16))) float Cs[kQ * NP];
   __shared__ __attribute__((aligned(16))) float Rs[P * NP];
+  __shared__ float Ws[4][16][kWave];  // role 1's W tiles, per wave (w % 4), value and lane
   __shared__ float dl[kQ], cs_hi[kQ], cs_lo[kQ];
   __shared__ double wsum[kT8 / kWave], tot;
 
@@ -257,11 +258,6 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
   const float fr = s < Lc ? __expf(static_cast<float>((tot - static_cast<double>(hs)) - static_cast<double>(ls)))
                           : 0.0f;  // e^{tot - cs_s} <= 1
 
-  // W0 = dy.x^T, rows l = 16 lt + 4q + i, masked, decayed and scaled into W
-  f32x4 sW[4];
-#pragma unroll
-  for (int lt = 0; lt < 4; ++lt)
-    sW[lt] = dot_rows<P>(Ys + (16 * lt + r16) * XP, Xs + s * XP, f32x4{0.f, 0.f, 0.f, 0.f});
   float dd[4][4];  // decay of (l, s), 0 off the causal block
 #pragma unroll
   for (int lt = 0; lt < 4; ++lt)
@@ -270,8 +266,23 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
       const int l = 16 * lt + 4 * q + i;
       const bool ok = l >= s && l < Lc && s < Lc;
       dd[lt][i] = ok ? decay_between(cs_hi[l], cs_lo[l], hs, ls) : 0.0f;
-      sW[lt][i] = dd[lt][i] * sc * sW[lt][i];
     }
+  // W0 = dy.x^T, rows l = 16 lt + 4q + i, masked, decayed and scaled into W:
+  // role 1 forms it and hands it to role 0 through LDS (one barrier, each role
+  // reaching it after its first products)
+  f32x4 sW[4];
+  if (role == 1) {
+#pragma unroll
+    for (int lt = 0; lt < 4; ++lt)
+      sW[lt] = dot_rows<P>(Ys + (16 * lt + r16) * XP, Xs + s * XP, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int lt = 0; lt < 4; ++lt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sW[lt][i] = dd[lt][i] * sc * sW[lt][i];
+        Ws[w & 3][4 * lt + i][lane] = sW[lt][i];
+      }
+  }
 
   if (role == 0) {
     // scores S = C.B^T; the box terms; M = decayed S
@@ -279,13 +290,14 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
 #pragma unroll
     for (int lt = 0; lt < 4; ++lt)
       sS[lt] = dot_rows<NE>(Cs + (16 * lt + r16) * NP, Bs + s * NP, f32x4{0.f, 0.f, 0.f, 0.f});
+    __syncthreads();  // (the W tiles of role 1)
     float col = 0.0f;
 #pragma unroll
     for (int lt = 0; lt < 4; ++lt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int l = 16 * lt + 4 * q + i;
-        col += l > s ? sW[lt][i] * sS[lt][i] : 0.0f;
+        col += l > s ? Ws[w & 3][4 * lt + i][lane] * sS[lt][i] : 0.0f;
         sS[lt][i] = dd[lt][i] * sS[lt][i];
       }
     col = qsum(col);
@@ -350,6 +362,7 @@ __global__ __launch_bounds__(kT8) void ssd_f32_col_kernel(
     }
     db[nt] = acc * (sc * fr);
   }
+  __syncthreads();  // (role 0 takes the W tiles)
 #pragma unroll
   for (int lt = 0; lt < 4; ++lt)
 #pragma unroll
@@ -419,6 +432,7 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
   __shared__ __attribute__((aligned(16))) float Bs[kQ * NP];
   __shared__ __attribute__((aligned(16))) float Cs[kQ * NP];
   __shared__ __attribute__((aligned(16))) float Hs[P * NP];
+  __shared__ float Ws[4][16][kWave];  // role 1's W^T tiles, per wave (w % 4), value and lane
   __shared__ float dl[kQ], cs_hi[kQ], cs_lo[kQ];
   __shared__ double wsum[kT8 / kWave], tot;
 
@@ -461,21 +475,26 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
 
   const float hl = cs_hi[l], ll = cs_lo[l];
 
-  // W0^T = x.dy^T, rows s = 16 st + 4q + i, masked, decayed and scaled
+  // W0^T = x.dy^T, rows s = 16 st + 4q + i, masked, decayed and scaled: role 1
+  // forms it and hands it to role 0 through LDS (one barrier, each role
+  // reaching it after its first products)
   f32x4 sW[4];
+  if (role == 1) {
 #pragma unroll
-  for (int st = 0; st < 4; ++st)
-    sW[st] = dot_rows<P>(Xs + (16 * st + r16) * XP, Ys + l * XP, f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int st = 0; st < 4; ++st)
+      sW[st] = dot_rows<P>(Xs + (16 * st + r16) * XP, Ys + l * XP, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-  for (int st = 0; st < 4; ++st)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = 16 * st + 4 * q + i;
-      const bool ok = s <= l && l < Lc && s < Lc;
-      const float d = ok ? decay_between(hl, ll, cs_hi[s], cs_lo[s]) : 0.0f;
-      const float sc = SCALE ? dl[s] : 1.0f;
-      sW[st][i] = d * sc * sW[st][i];
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * st + 4 * q + i;
+        const bool ok = s <= l && l < Lc && s < Lc;
+        const float d = ok ? decay_between(hl, ll, cs_hi[s], cs_lo[s]) : 0.0f;
+        const float sc = SCALE ? dl[s] : 1.0f;
+        sW[st][i] = d * sc * sW[st][i];
+        Ws[w & 3][4 * st + i][lane] = sW[st][i];
+      }
+  }
 
   f32x4 dc[NT];
   float f1 = 0.0f, rw = 0.0f;
@@ -484,12 +503,13 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
 #pragma unroll
     for (int st = 0; st < 4; ++st)
       sS[st] = dot_rows<NE>(Bs + (16 * st + r16) * NP, Cs + l * NP, f32x4{0.f, 0.f, 0.f, 0.f});
+    __syncthreads();  // (the W^T tiles of role 1)
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 16 * st + 4 * q + i;
-        rw += s < l ? sW[st][i] * sS[st][i] : 0.0f;
+        rw += s < l ? Ws[w & 3][4 * st + i][lane] * sS[st][i] : 0.0f;
       }
     rw = qsum(rw);
     // boundary (H_in^T dy_l) scaled by e^{cs_l}, and f1
@@ -513,6 +533,7 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
       for (int i = 0; i < 4; ++i) f1 += Cs[l * NP + 16 * nt + 4 * q + i] * dc[nt][i];
     f1 = qsum(f1);
   } else {
+    __syncthreads();  // (role 0 takes the W^T tiles)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) dc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
