@@ -846,7 +846,7 @@ def cpu_baseline_conv(inp, target_s):
 BWD_KERNELS = ["ssd_state_bf16_kernel", "ssd_pass_bf16_kernel", "ssd_adj_state_kernel",
                "ssd_adj_pass_kernel", "ssd_bwd_dxdb_kernel", "ssd_bwd_dc_kernel",
                None, "ssd_bwd_dt_kernel", "ssd_bwd_dt_sum_kernel",
-               "ssd_bwd_reduce_kernel(dB)", "ssd_bwd_reduce_kernel(dC)"]
+               "ssd_bwd_reduce_kernel(dB, dC)", None]
 
 
 def bwd_kernel_costs(dims, nparts):
@@ -881,8 +881,7 @@ def bwd_kernel_costs(dims, nparts):
                               units * (2 * tri * P + 2 * tri * N + 2 * Q * P * N)),
         "ssd_bwd_dt_kernel": (Bsz * T * H * 4 + 6 * pt + pt * (nb + 1) / 2, 0),
         "ssd_bwd_dt_sum_kernel": (Bsz * H * nc * 24 + H * 12, 0),
-        "ssd_bwd_reduce_kernel(dB)": (part + out, 0),
-        "ssd_bwd_reduce_kernel(dC)": (part + out, 0),
+        "ssd_bwd_reduce_kernel(dB, dC)": (2 * (part + out), 0),
         # x, dy in and dx out; B, C in; dt in and ddt out; dB, dC out (fp32)
         "whole_backward": (3 * x + 2 * bc + Bsz * T * H * 8 + 2 * out, 0),
     }

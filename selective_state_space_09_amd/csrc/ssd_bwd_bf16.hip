@@ -1039,12 +1039,17 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_sum_kernel(
   dD[h] = static_cast<float>(s[2]);
 }
 
-// dB (or dC) = sum of the nparts head-group partials, float4 at a time
-__global__ __launch_bounds__(kThreads) void ssd_bwd_reduce_kernel(const float* __restrict__ part,
-                                                                  float* __restrict__ out,
-                                                                  size_t n4, int nparts) {
+// dB and dC = sums of their nparts head-group partials, float4 at a time
+// (blockIdx.y 0: dB, 1: dC; one launch for both)
+__global__ __launch_bounds__(kThreads) void ssd_bwd_reduce_kernel(const float* __restrict__ partB,
+                                                                  float* __restrict__ outB,
+                                                                  const float* __restrict__ partC,
+                                                                  float* __restrict__ outC, size_t n4,
+                                                                  int nparts) {
   const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= n4) return;
+  const float* part = blockIdx.y == 0 ? partB : partC;
+  float* out = blockIdx.y == 0 ? outB : outC;
   const float4* p = reinterpret_cast<const float4*>(part);
   float4 s = p[i];
   for (int k = 1; k < nparts; ++k) {
@@ -1182,7 +1187,8 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
            x, B, C, dy, tok, states, f1, dCp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
   // (the chunk constants' slot: an empty pair, recorded back to back)
   launch_k(false, ssd_bwd_reduce_kernel, dim3(1), dim3(kThreads), st, ev ? ev + 12 : nullptr,
-           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), size_t{0}, 0);
+           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), static_cast<const float*>(nullptr),
+           static_cast<float*>(nullptr), size_t{0}, 0);
   double* dtp = reinterpret_cast<double*>(ws + L.dtp);
   launch_k(nc > 0, ssd_bwd_dt_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
            ev ? ev + 14 : nullptr, a.dt, a.A, a.dt_bias, a.dt_min, a.dt_max, static_cast<const float*>(f1),
@@ -1196,10 +1202,13 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const size_t n4 = static_cast<size_t>(a.Bsz) * a.T * a.G * N / 4;
   const int nparts = (a.H / a.G) / HPG;
   const unsigned rblocks = static_cast<unsigned>((n4 + kThreads - 1) / kThreads);
-  launch_k(n4 > 0, ssd_bwd_reduce_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(kThreads), st,
-           ev ? ev + 18 : nullptr, static_cast<const float*>(dBp), a.dB, n4, nparts);
-  launch_k(n4 > 0, ssd_bwd_reduce_kernel, dim3(rblocks > 0 ? rblocks : 1), dim3(kThreads), st,
-           ev ? ev + 20 : nullptr, static_cast<const float*>(dCp), a.dC, n4, nparts);
+  // dB and dC in one launch (slot dB sum; slot dC sum: an empty pair)
+  launch_k(n4 > 0, ssd_bwd_reduce_kernel, dim3(rblocks > 0 ? rblocks : 1, 2), dim3(kThreads), st,
+           ev ? ev + 18 : nullptr, static_cast<const float*>(dBp), a.dB, static_cast<const float*>(dCp), a.dC,
+           n4, nparts);
+  launch_k(false, ssd_bwd_reduce_kernel, dim3(1), dim3(kThreads), st, ev ? ev + 20 : nullptr,
+           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), static_cast<const float*>(nullptr),
+           static_cast<float*>(nullptr), size_t{0}, 0);
   return hipGetLastError();
 }
 
