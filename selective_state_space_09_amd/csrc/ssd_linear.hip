@@ -7,9 +7,10 @@
 // 3.1: these projections run in bf16 under autocast, fp32 accumulation).
 //
 // One workgroup per 128 x 128 output tile (4 waves, 2 x 2, each 64 x 64), K in
-// steps of 64 staged through LDS (rows K-contiguous for both operands, so the
-// matrix-core fragments are plain 16-byte row reads), the next step's tiles
-// loaded into registers while the current one is multiplied.  x may be fp32
+// steps of 64 staged through two LDS sets (rows K-contiguous for both
+// operands, so the matrix-core fragments are plain 16-byte row reads): step s
+// is multiplied from one set while step s + 1, loaded into registers a step
+// earlier, is written into the other, one barrier per step.  x may be fp32
 // (rounded to bf16, nearest even, as it is staged) or bf16; W is bf16.
 //
 // The product is formed transposed, Z^T[n][m] = W[n][.] x[m][.]: a lane's
@@ -35,8 +36,10 @@ template <bool XF32, bool ZF32>
 __global__ __launch_bounds__(kThreads, 2) void ssd_linear_kernel(
     const void* __restrict__ xv, const uint16_t* __restrict__ W, void* __restrict__ zv, int M,
     int K, int Nout, int mblocks, int nblocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t xl[kLinBM * kLinPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t wl[kLinBN * kLinPitch];
+  // two LDS sets: step s is multiplied from one while step s + 1 is staged
+  // into the other (one barrier per step; 80 KB: two workgroups per CU)
+  __shared__ __attribute__((aligned(16))) uint16_t xl[2][kLinBM * kLinPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t wl[2][kLinBN * kLinPitch];
 
   // tile of this workgroup: the row blocks are spread over the XCDs, and the
   // output blocks of one row block follow each other on its XCD
@@ -78,24 +81,24 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_linear_kernel(
       wr[i] = buf_load16(wbuf, static_cast<uint32_t>(it / WVPR) * wrow + k0 * 2 + (it % WVPR) * 16);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < XVPT; ++i) {
       const int it = tid + i * kThreads;
       const int row = it / XVPR, v = it % XVPR;
       if constexpr (XF32) {
         const uint4 u = xr[i];
-        *reinterpret_cast<uint2*>(xl + row * kLinPitch + v * 4) =
+        *reinterpret_cast<uint2*>(xl[buf] + row * kLinPitch + v * 4) =
             make_uint2(pack_bf16x2(__uint_as_float(u.x), __uint_as_float(u.y)),
                        pack_bf16x2(__uint_as_float(u.z), __uint_as_float(u.w)));
       } else {
-        *reinterpret_cast<uint4*>(xl + row * kLinPitch + v * 8) = xr[i];
+        *reinterpret_cast<uint4*>(xl[buf] + row * kLinPitch + v * 8) = xr[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < WVPT; ++i) {
       const int it = tid + i * kThreads;
-      *reinterpret_cast<uint4*>(wl + (it / WVPR) * kLinPitch + (it % WVPR) * 8) = wr[i];
+      *reinterpret_cast<uint4*>(wl[buf] + (it / WVPR) * kLinPitch + (it % WVPR) * 8) = wr[i];
     }
   };
 
@@ -107,11 +110,17 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_linear_kernel(
 
   const int nsteps = K / kLinBK;
   load(0);
+  stage(0);
+  if (nsteps > 1) load(kLinBK);
+  __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
-    __syncthreads();  // every wave is done with the previous step's tiles
-    stage();
-    __syncthreads();
-    if (s + 1 < nsteps) load((s + 1) * kLinBK);
+    const int cur = s & 1;
+    // step s + 1 into the other set (its last reads were step s - 1's, before
+    // the previous barrier), then the loads of step s + 2
+    if (s + 1 < nsteps) {
+      stage(cur ^ 1);
+      if (s + 2 < nsteps) load((s + 2) * kLinBK);
+    }
 #pragma unroll
     for (int ks = 0; ks < kLinBK; ks += 32) {
       uint4 af[4], bf[4];
@@ -119,17 +128,18 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_linear_kernel(
       for (int t = 0; t < 4; ++t) {
         // n tile t of the wave: pair t / 2, half t % 2, permuted rows
         const int nl = wn * 64 + 32 * (t >> 1) + 4 * (t & 1) + 8 * (r16 >> 2) + (r16 & 3);
-        af[t] = *reinterpret_cast<const uint4*>(wl + nl * kLinPitch + ks + 8 * q);
+        af[t] = *reinterpret_cast<const uint4*>(wl[cur] + nl * kLinPitch + ks + 8 * q);
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        bf[mt] = *reinterpret_cast<const uint4*>(xl + (wm * 64 + mt * 16 + r16) * kLinPitch + ks + 8 * q);
+        bf[mt] = *reinterpret_cast<const uint4*>(xl[cur] + (wm * 64 + mt * 16 + r16) * kLinPitch + ks + 8 * q);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           acc[t][mt] = mfma_bf16(as_bf16x8(af[t]), as_bf16x8(bf[mt]), acc[t][mt]);
     }
+    __syncthreads();  // step s + 1's set complete; step s's set free
   }
 
   // z rows out: lane holds row m = mb*128 + wm*64 + mt*16 + r16 and, per pair of
