@@ -601,7 +601,8 @@ __global__ __launch_bounds__(kT8) void ssd_f32_row_kernel(
 // ---------------------------------------------------------------------------
 // Adjoint passing, last chunk first: R_{nc-1} = dh_final, R_{c-1} = lambda_c
 // R_c + G_c, dh0 = R_{-1}; R_c over G_c.  One thread per 4 elements, a
-// workgroup per 1024 elements of one (batch, head).  On the way it forms its
+// workgroup per 1024 elements of one (batch, head), the chunks in groups of 8
+// whose loads are issued together.  On the way it forms its
 // share of each chunk's constant <R_c, H_in(c)> (H_in over the forward states,
 // fp64 sums): cpart[(b, h, c) * nblk + block], summed and scaled by e^{tot}
 // where the step-size gradients use them.
@@ -610,7 +611,8 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_adj_pass_kernel(
     float* __restrict__ adj, const float* __restrict__ decay, const float* __restrict__ dh_final,
     float* __restrict__ dh0, const float* __restrict__ states, double* __restrict__ cpart, int H, int PN,
     int nc) {
-  __shared__ double ws4[kThreads / kWave];
+  constexpr int PF = 8;  // chunks whose loads are issued together
+  __shared__ double ws[PF][kThreads / kWave];
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int e4 = blockIdx.x * kThreads + tid;
@@ -624,22 +626,44 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_adj_pass_kernel(
   const float* dc = decay + bh * nc * 2;
   float4 r = in && dh_final ? *reinterpret_cast<const float4*>(dh_final + bh * PN + e4 * 4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int cc = nc - 1; cc >= 0; --cc) {
-    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f), hv = gv;
-    if (in) {
-      gv = *reinterpret_cast<const float4*>(base + cc * cstride);
-      hv = *reinterpret_cast<const float4*>(hb + cc * cstride);
-      *reinterpret_cast<float4*>(base + cc * cstride) = r;
+  for (int c1 = nc; c1 > 0; c1 -= PF) {  // chunks c1-1 down to c1-PF
+    float4 gv[PF], hv[PF];
+    float ld[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int cc = c1 - 1 - j;
+      gv[j] = hv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      ld[j] = 0.0f;
+      if (cc >= 0 && in) {
+        gv[j] = *reinterpret_cast<const float4*>(base + cc * cstride);
+        hv[j] = *reinterpret_cast<const float4*>(hb + cc * cstride);
+      }
+      if (cc >= 0) ld[j] = dc[2 * cc];
     }
-    double part = static_cast<double>(r.x * hv.x + r.y * hv.y) + static_cast<double>(r.z * hv.z + r.w * hv.w);
-    part = wave_inclusive_sum_d(part);
-    if (lane == kWave - 1) ws4[wid] = part;
+    double part[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int cc = c1 - 1 - j;
+      // R_c = r here: its share of <R_c, H_in(c)>, then the update
+      part[j] = static_cast<double>(r.x * hv[j].x + r.y * hv[j].y) +
+                static_cast<double>(r.z * hv[j].z + r.w * hv[j].w);
+      if (cc >= 0) {
+        if (in) *reinterpret_cast<float4*>(base + cc * cstride) = r;
+        const float l = ld[j];
+        r = make_float4(l * r.x + gv[j].x, l * r.y + gv[j].y, l * r.z + gv[j].z, l * r.w + gv[j].w);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      double v = part[j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+      if (lane == 0) ws[j][wid] = v;
+    }
     __syncthreads();
-    if (tid == 0)
-      cpart[(bh * nc + cc) * nblk + blockIdx.x] = (ws4[0] + ws4[1]) + (ws4[2] + ws4[3]);
-    __syncthreads();
-    const float l = dc[2 * cc];
-    r = make_float4(l * r.x + gv.x, l * r.y + gv.y, l * r.z + gv.z, l * r.w + gv.w);
+    if (tid < PF && c1 - 1 - tid >= 0)
+      cpart[(bh * nc + (c1 - 1 - tid)) * nblk + blockIdx.x] = (ws[tid][0] + ws[tid][1]) + (ws[tid][2] + ws[tid][3]);
+    __syncthreads();  // (ws is rewritten by the next group of chunks)
   }
   if (in && dh0) *reinterpret_cast<float4*>(dh0 + bh * PN + e4 * 4) = r;
 }
