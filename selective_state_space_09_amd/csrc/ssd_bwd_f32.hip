@@ -670,20 +670,21 @@ __global__ __launch_bounds__(kThreads) void ssd_f32_adj_pass_kernel(
 
 // ---------------------------------------------------------------------------
 // Complex: the sequence frame, one workgroup per (head, batch).  u_t =
-// delta_1 + .. + delta_t over the sequence (fp64: each thread sums 8
+// delta_1 + .. + delta_t over the sequence (fp64: each of 1024 threads sums 2
 // consecutive tokens, one block scan per 2048 tokens, carried from block to
 // block) and (cos, sin) theta_t, theta_t = beta u_t mod 2 pi, per token
 // and head (the kernels that read B and C rotate them by it as they stage
 // them); then h0 as [Re | Im] rows and dh_final, rotated by -theta at the last
 // token, likewise; the decay alpha of each head.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void ssd_cplx_frame_kernel(
+constexpr int kFrameThreads = 1024;
+__global__ __launch_bounds__(kFrameThreads) void ssd_cplx_frame_kernel(
     const float* __restrict__ dt, const float* __restrict__ dt_bias, float dt_min, float dt_max,
     const float* __restrict__ A, const float* __restrict__ h0, const float* __restrict__ dh_final,
     double* __restrict__ uo, float2* __restrict__ rot, float* __restrict__ alpha, float* __restrict__ h0e,
     float* __restrict__ dhfe, int T, int H, int P, int N) {
-  constexpr int TPT = 8;  // consecutive tokens per thread in a block of kThreads * TPT
-  __shared__ double wtot[kThreads / kWave];
+  constexpr int TPT = 2;  // consecutive tokens per thread in a block of kFrameThreads * TPT
+  __shared__ double wtot[kFrameThreads / kWave];
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid / kWave;
   const float be = A[2 * h + 1];
@@ -691,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void ssd_cplx_frame_kernel(
   if (tid == 0 && b == 0) alpha[h] = A[2 * h];
   const size_t bh = static_cast<size_t>(b) * H + h;
   double carry = 0.0;  // u of the tokens before the block
-  for (int tb = 0; tb < T; tb += TPT * kThreads) {
+  for (int tb = 0; tb < T; tb += TPT * kFrameThreads) {
     const int t0 = tb + TPT * tid;  // this thread's first token
     float dv[TPT];
 #pragma unroll
@@ -708,7 +709,7 @@ __global__ __launch_bounds__(kThreads) void ssd_cplx_frame_kernel(
     __syncthreads();
     double before = carry + (incl - run), total = carry;
 #pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
+    for (int w = 0; w < kFrameThreads / kWave; ++w) {
       const double pw = wtot[w];
       before += w < wid ? pw : 0.0;
       total += pw;
@@ -731,7 +732,7 @@ __global__ __launch_bounds__(kThreads) void ssd_cplx_frame_kernel(
   float cl = 1.0f, sl = 0.0f;
   if (T > 0) rot_cs(static_cast<double>(be) * carry, cl, sl);
   const int NE = 2 * N;
-  for (int i = tid; i < P * N; i += kThreads) {
+  for (int i = tid; i < P * N; i += kFrameThreads) {
     const int p = i / N, n = i % N;
     const size_t src = (bh * P * N + i) * 2;
     const size_t dst = bh * P * NE + static_cast<size_t>(p) * NE;
@@ -1128,7 +1129,7 @@ static hipError_t launch_cplx_bwd(const CplxBwdArgs& a, hipStream_t st) {
   float* dh0e = reinterpret_cast<float*>(ws + L.dh0e);
   float2* rot = reinterpret_cast<float2*>(ws + L.rot);
   // the sequence frame (event slot 0)
-  launch_k(true, ssd_cplx_frame_kernel, dim3(a.H, a.Bsz), dim3(kThreads), st, E(0), a.dt, a.dt_bias, a.dt_min,
+  launch_k(true, ssd_cplx_frame_kernel, dim3(a.H, a.Bsz), dim3(kFrameThreads), st, E(0), a.dt, a.dt_bias, a.dt_min,
            a.dt_max, a.A, a.h0, a.dh_final, u, rot, alpha, h0e, dhfe, a.T, a.H, P, N);
   // the rotated-frame real problem: 2N features (B and C rotated as they are
   // staged), decay alpha, input scale 1
