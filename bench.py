@@ -96,19 +96,20 @@ class Hip:
 # files hash the same.
 DEVICE_HEADERS = ["ssd_chunk_common.h", "ssd_device.h"]
 KERNEL_SOURCES = {
-    "bitmamba_bf16": ["ssd_chunk_bf16.hip"],
-    "long_bf16": ["ssd_chunk_bf16.hip"],
+    # (ssd_internal.h: the segment length the bf16 forward launches with)
+    "bitmamba_bf16": ["ssd_chunk_bf16.hip", "ssd_internal.h"],
+    "long_bf16": ["ssd_chunk_bf16.hip", "ssd_internal.h"],
     "tiny_f32": ["ssd_chunk.hip"],
     "mamba3lite_complex": ["ssd_chunk_cplx.hip"],
     "decode_f32": ["ssd_decode.hip"],
     "decode_complex": ["ssd_decode.hip"],
     "conv_bf16": ["ssd_conv.hip"],
     "conv_decode_f32": ["ssd_conv.hip"],
-    "bwd_bf16": ["ssd_bwd_bf16.hip", "ssd_chunk_bf16.hip"],
+    "bwd_bf16": ["ssd_bwd_bf16.hip", "ssd_chunk_bf16.hip", "ssd_internal.h"],
     "mamba3lite_packed": ["ssd_chunk_cplx.hip"],
     "mimo_bf16": ["ssd_linear.hip"],
     "bwd_complex": ["ssd_bwd_f32.hip", "ssd_chunk.hip"],
-    "varlen_bf16": ["ssd_chunk_bf16.hip"],
+    "varlen_bf16": ["ssd_chunk_bf16.hip", "ssd_internal.h"],
 }
 
 

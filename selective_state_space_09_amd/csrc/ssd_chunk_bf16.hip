@@ -1128,8 +1128,11 @@ bool varlen_plan(const int* cu, int nseq, int H, int chunk, VarlenPlan& p, const
   p.Ttot = cu[nseq];
   p.nc_tot = nc_tot;
   p.max_nc = max_nc;
-  // the uniform rule over all chunks, then no longer than the longest sequence
-  int K = nc_tot > 2147483647LL ? 16 : bf16_segment_chunks(1, static_cast<int>(nc_tot), H, chunk);
+  // the rule over all chunks (the variable-length target), then no longer than
+  // the longest sequence
+  int K = nc_tot > 2147483647LL
+              ? 16
+              : bf16_segment_chunks(1, static_cast<int>(nc_tot), H, chunk, kSegTargetUnitsVarlen);
   while (K > 1 && K > max_nc) K /= 2;
   p.K = K;
   long long npairs = 0;

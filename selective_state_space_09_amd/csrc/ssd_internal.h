@@ -120,20 +120,24 @@ inline size_t workspace_cplx_token_floats(int Bsz, int nc, int H, int chunk) {
 //   decay fp32 (Bsz, H, nseg)        each segment's decay factor
 //   tok   float2 (Bsz, nc, H, chunk) per token: A u_l (cumulative step from
 //                                    the chunk start times A) and delta_l
-// nseg = ceil(nc / K).  K is 1 while the (batch, chunk, head) units fill the
-// chip on their own, else the largest power of two (<= 16) that leaves at
-// least kSegTargetUnits workgroups; chunks below 64 tokens always use K = 1.
+// nseg = ceil(nc / K).  K is the largest power of two (<= 16, <= nc) that
+// leaves at least `target` (batch, segment, head) workgroups; chunks below 64
+// tokens always use K = 1.  Uniform batches: 512, one round of the
+// multi-chunk output kernel at two workgroups per CU (at the BitMamba shape
+// K = 2: 63.7 -> 60.3 us per step, against 1024 single-chunk workgroups in
+// 1.33 rounds at three per CU; at T65536 K = 16: 606 -> 586 us).
+// Variable-length batches: 2048 over all their chunks (sequences of uneven
+// length leave segments of uneven length; the six-prompt batch runs 92 us at
+// K = 1 against 102 us at K = 2).
 // ---------------------------------------------------------------------------
-#ifndef SSD_SEG_TARGET_UNITS
-#define SSD_SEG_TARGET_UNITS 2048
-#endif
-constexpr long long kSegTargetUnits = SSD_SEG_TARGET_UNITS;
+constexpr long long kSegTargetUnits = 512;
+constexpr long long kSegTargetUnitsVarlen = 2048;
 
-inline int bf16_segment_chunks(int Bsz, int nc, int H, int chunk) {
+inline int bf16_segment_chunks(int Bsz, int nc, int H, int chunk, long long target = kSegTargetUnits) {
   if (chunk < 64) return 1;
   const long long units = static_cast<long long>(Bsz) * nc * H;
   int K = 1;
-  while (K < 16 && 2 * K <= nc && units / (2LL * K) >= kSegTargetUnits) K *= 2;
+  while (K < 16 && 2 * K <= nc && units / (2LL * K) >= target) K *= 2;
   return K;
 }
 

@@ -451,7 +451,7 @@ def test_mixed_decay_modes():
 # bf16 segments: output and state workgroups that walk several chunks
 # --------------------------------------------------------------------------
 
-def _segment_chunks(Bsz, T, H, Q, target=2048):
+def _segment_chunks(Bsz, T, H, Q, target=512):
     """Chunks per workgroup the bf16 forward picks for a shape (the rule the
     library states with its workspace layout): 1 below 64-token chunks, else
     the largest power of two <= 16 leaving >= `target` workgroups."""
@@ -466,12 +466,14 @@ def _segment_chunks(Bsz, T, H, Q, target=2048):
 
 SEGMENT_CASES = [
     # Bsz, T, H, P, N, G, Q, h0, steep
-    (2, 2048, 64, 16, 16, 1, 64, True, False),     # K = 2
-    (4, 4000, 64, 16, 32, 2, 64, True, False),     # K = 4, ragged last segment and chunk
-    (1, 8192, 64, 32, 64, 1, 64, False, False),    # K = 4
-    (4, 2100, 64, 16, 16, 1, 64, True, True),      # K = 4, exact-mode sub-chunks mixed in
-    (1, 16384, 64, 16, 16, 1, 128, True, False),   # K = 4 at chunk 128
-    (1, 70000, 64, 16, 16, 4, 256, True, True),    # K = 8 at chunk 256, steep, ragged
+    (1, 2048, 32, 16, 16, 1, 64, True, False),     # K = 2
+    (2, 1000, 64, 16, 32, 2, 64, True, True),      # K = 4, ragged last chunk, steep
+    (2, 2048, 64, 16, 16, 1, 64, True, False),     # K = 8
+    (4, 4000, 64, 16, 32, 2, 64, True, False),     # K = 16, ragged last segment and chunk
+    (1, 8192, 64, 32, 64, 1, 64, False, False),    # K = 16
+    (4, 2100, 64, 16, 16, 1, 64, True, True),      # K = 16, exact-mode sub-chunks mixed in
+    (1, 16384, 64, 16, 16, 1, 128, True, False),   # K = 16 at chunk 128
+    (1, 70000, 64, 16, 16, 4, 256, True, True),    # K = 16 at chunk 256, steep, ragged
 ]
 
 
@@ -497,7 +499,7 @@ def test_real_segments(case):
 
 
 @pytest.mark.parametrize("shape", [(1, 300, 2, 64, 128, 1, 256), (4, 4096, 64, 16, 16, 1, 256)],
-                         ids=["K1", "K2"])
+                         ids=["K1", "K8"])
 def test_pivot_gap_below_fp32_range(shape):
     """A decay of e^-1.8 per token (A = -18, every step 0.1): each half
     sub-chunk decays by e^-57.6, inside the factored form's e^60 bound, so no
