@@ -83,7 +83,8 @@ const char *ssd_last_error(void);
  * chunk-boundary states as fp32, (Bsz, nc, H, P, N) real or (Bsz, nc, H, P, 2N)
  * complex with nc = ceil(T / chunk), plus one decay factor per (b, h, chunk),
  * plus for the real form one (exponent, step size) float pair per token and
- * head.  (The bf16 real path keeps its chunk and boundary states as bf16.)
+ * head.  (The bf16 real path keeps its chunk states in fp32 too, and beside
+ * them the bf16 copy of each boundary state that its output kernel reads.)
  * Returns 0 for sizes the library rejects, among them any whose 1-D grid
  * would exceed 2^31 - 1 workgroups (ceil(Bsz * nc / 8) * 8 * H) or whose
  * chunk of token rows exceeds 4 GiB (chunk * H * P * 4 or chunk * G * N * 8).

@@ -41,13 +41,13 @@
 //   forward recompute   chunk states, boundary states h_in(c) (fp32) and the
 //                       per-token (cs, delta) table (the forward's kernels)
 //   ssd_adj_state       G_c per (batch, chunk, head), MFMA over tokens
-//   ssd_adj_pass        R_c in place over G_c, dh0
+//   ssd_adj_pass        R_c in place over G_c, dh0, and the chunk constants
+//                       e^{tot} <R_c, H_in(c)> as fp64 shares
 //   ssd_bwd_dxdb        per (batch, chunk, 64-token column block s, head
 //                       group): v, dx, x.v, dy.x, f2, col, the block's
 //                       share of row, and dB summed over the group
 //   ssd_bwd_dc          per (batch, chunk, 64-token row block l, head group):
 //                       dC summed over the group, f1 per head
-//   ssd_bwd_const       per (chunk, head, batch): e^{tot} <R_c, H_in>
 //   ssd_bwd_dt          per (chunk, head, batch): the prefix / suffix sums of
 //                       col - row, f2 / f1 inside the chunk (fp64), da, ddt, the chunk's
 //                       shares of dA, ddt_bias, dD
@@ -432,6 +432,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int w = wave_id();
   const size_t r0 = static_cast<size_t>(b) * T + t0;
+  // per-token values for the step-size kernel: token-contiguous per (batch, head)
+  auto head_row = [&](int hh) { return (static_cast<size_t>(b) * H + hh) * T + t0; };
   const uint32_t xrow = static_cast<uint32_t>(H) * P * 2, brow = static_cast<uint32_t>(G) * N * 2;
   const buf_t bbuf = make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N,
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     // f2_s = delta_s x_s . (e^{tot-cs_s} R_c B_s): the R part of x.v, before the rest
     {
       const float part = group_total(xdot(Xs + sr * XP));
-      if (q == 0 && sl < Lc) f2o[(r0 + sl) * H + h] = dl_s * part;
+      if (q == 0 && sl < Lc) f2o[head_row(h) + sl] = dl_s * part;
     }
     // boundary part of dB: delta_s e^{tot-cs_s} (x_s R)[n] (B columns s = this lane's sl),
     // x_s R from the exact x rows and both parts of R, scaled in fp32
@@ -565,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
       const int l0 = s0 + lb * kBlk;
       const float(*rw)[kBlk] = rows[lb & 1];
       if (tid < kBlk && l0 + tid < Lc)
-        rowp[static_cast<size_t>(j) * BTH + (r0 + l0 + tid) * H + h] = rw[0][tid] + rw[1][tid] + rw[2][tid] + rw[3][tid];
+        rowp[static_cast<size_t>(j) * BTH + head_row(h) + l0 + tid] = rw[0][tid] + rw[1][tid] + rw[2][tid] + rw[3][tid];
     };
     for (int lb = nlb - 1; lb >= 0; --lb) {
       const int l0 = s0 + lb * kBlk;
@@ -676,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
     flush_rows(0);
     {
       const float ct = group_total(col);
-      if (q == 0 && sl < Lc) colp[(r0 + sl) * H + h] = ct;
+      if (q == 0 && sl < Lc) colp[head_row(h) + sl] = ct;
     }
 
     // outputs of head h: lane holds row s = sl, p = 32 hh + 8q .. +7 of each pair;
@@ -708,8 +710,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dxdb_kernel(
       pxv = group_total(pxv);
       pdx = group_total(pdx);
       if (q == 0 && sl < Lc) {
-        xv[(r0 + sl) * H + h] = pxv;
-        dyx[(r0 + sl) * H + h] = pdx;
+        xv[head_row(h) + sl] = pxv;
+        dyx[head_row(h) + sl] = pdx;
       }
     }
   }
@@ -766,6 +768,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int w = wave_id();
   const size_t r0 = static_cast<size_t>(b) * T + t0;
+  // per-token values for the step-size kernel: token-contiguous per (batch, head)
+  auto head_row = [&](int hh) { return (static_cast<size_t>(b) * H + hh) * T + t0; };
   const uint32_t xrow = static_cast<uint32_t>(H) * P * 2, brow = static_cast<uint32_t>(G) * N * 2;
   const buf_t bbuf = make_buf(Bm + r0 * G * N + static_cast<size_t>(g) * N,
                               static_cast<uint32_t>(Lc - 1) * brow + N * 2);
@@ -851,7 +855,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dc_kernel(
               bf16_bits_to_f32(cc.y & 0xFFFFu) * dC[nt][2] + bf16_bits_to_f32(cc.y >> 16) * dC[nt][3];
       }
       pd = group_total(pd);
-      if (q == 0 && ll < Lc) f1o[(r0 + ll) * H + h] = pd;
+      if (q == 0 && ll < Lc) f1o[head_row(h) + ll] = pd;
     }
     for (int sb = 0; sb <= ib; ++sb) {
       const int s0 = sb * kBlk;
@@ -962,17 +966,19 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
   cst *= static_cast<double>(decay[bhc]);
   const int t = c * Q + tid;
   const bool in = tid < Q && t < T;
-  const size_t row = (static_cast<size_t>(b) * T + (in ? t : 0)) * H + h;
-  const double f1v = in ? static_cast<double>(f1[row]) : 0.0;
-  const double f2v = in ? static_cast<double>(f2[row]) : 0.0;
+  const size_t row = (static_cast<size_t>(b) * T + (in ? t : 0)) * H + h;  // dt, ddt: (B, T, H)
+  // the kernels' per-token values: token-contiguous per (batch, head)
+  const size_t hrow = (static_cast<size_t>(b) * H + h) * T + (in ? t : 0);
+  const double f1v = in ? static_cast<double>(f1[hrow]) : 0.0;
+  const double f2v = in ? static_cast<double>(f2[hrow]) : 0.0;
   double gv = 0.0;  // col_u - row_u of this token
   if (in) {
     // the shares of the column blocks jb <= this token's block (at most 4:
     // Q <= 256), all loads issued together
     float rs[4];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) rs[jb] = jb <= tid / kBlk ? rowp[static_cast<size_t>(jb) * BTH + row] : 0.0f;
-    gv = static_cast<double>(colp[row]);
+    for (int jb = 0; jb < 4; ++jb) rs[jb] = jb <= tid / kBlk ? rowp[static_cast<size_t>(jb) * BTH + hrow] : 0.0f;
+    gv = static_cast<double>(colp[hrow]);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) gv -= rs[jb];
   }
@@ -1000,7 +1006,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
     const double da = box + f1_suffix + f2_prefix + cst;
     const float z = dt[row] + bias;
     const float d = step_size(dt[row], bias, dt_min, dt_max);
-    const float xvt = xv[row];
+    const float xvt = xv[hrow];
     const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
     const bool pass = sp >= dt_min && sp <= dt_max;
     const double dd = static_cast<double>(a_re) * da + xvt;
@@ -1008,7 +1014,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
     ddt[row] = static_cast<float>(gz);
     sA = static_cast<double>(d) * da;
     sBias = gz;
-    sD = dyx[row];
+    sD = dyx[hrow];
   }
   // wave sums by DPP scans (the total lands in the last lane)
   sA = wave_inclusive_sum_d(sA);
