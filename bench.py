@@ -846,8 +846,8 @@ def cpu_baseline_conv(inp, target_s):
 
 BWD_KERNELS = ["ssd_state_bf16_kernel", "ssd_pass_bf16_kernel", "ssd_adj_state_kernel",
                "ssd_adj_pass_kernel", "ssd_bwd_dxdb_kernel", "ssd_bwd_dc_kernel",
-               None, "ssd_bwd_dt_kernel", "ssd_bwd_dt_sum_kernel",
-               "ssd_bwd_reduce_kernel(dB, dC)", None]
+               None, "ssd_bwd_dt_kernel", None,
+               "ssd_bwd_reduce_kernel(dB, dC, dA)", None]
 
 
 def bwd_kernel_costs(dims, nparts):
@@ -881,8 +881,8 @@ def bwd_kernel_costs(dims, nparts):
         "ssd_bwd_dc_kernel": (2 * x + 2 * bc + tok + st + pt + part,
                               units * (2 * tri * P + 2 * tri * N + 2 * Q * P * N)),
         "ssd_bwd_dt_kernel": (Bsz * T * H * 4 + 6 * pt + pt * (nb + 1) / 2, 0),
-        "ssd_bwd_dt_sum_kernel": (Bsz * H * nc * 24 + H * 12, 0),
-        "ssd_bwd_reduce_kernel(dB, dC)": (2 * (part + out), 0),
+        # dB, dC partials in, dB, dC out; the per-head sums of the chunk shares
+        "ssd_bwd_reduce_kernel(dB, dC, dA)": (2 * (part + out) + Bsz * H * nc * 24 + H * 12, 0),
         # x, dy in and dx out; B, C in; dt in and ddt out; dB, dC out (fp32)
         "whole_backward": (3 * x + 2 * bc + Bsz * T * H * 8 + 2 * out, 0),
     }
@@ -954,7 +954,7 @@ def bench_bwd(args, cfg):
     costs = bwd_kernel_costs(dims, nparts)
     kern = {}
     for k, name in enumerate(BWD_KERNELS):
-        if name is None:  # (the chunk constants: formed by the adjoint passing)
+        if name is None:  # (a slot whose work runs in another slot's launch)
             continue
         avg = float(np.mean([hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in evs]))
         nb_, fl = costs[name]

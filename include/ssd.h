@@ -437,7 +437,9 @@ int ssd_chunk_bwd(const void *x, const float *dt, const float *A, const void *B,
  * states, state passing, adjoint chunk states, adjoint passing (which also
  * forms the chunk constants of da), dx/dB blocks, dC blocks, chunk constants
  * (an empty pair, recorded back to back), step-size gradients per chunk,
- * their sums per head, dB and dC sums (one launch), an empty pair).  SSD_F32: 28 events, the 14
+ * their sums per head (an empty pair: they run in the next slot's launch),
+ * the sums of dB and dC and the per-head sums (one launch), an empty pair).
+ * SSD_F32: 28 events, the 14
  * slots of ssd_complex_chunk_bwd_ev (the complex-only slots record their pair
  * back to back).
  */

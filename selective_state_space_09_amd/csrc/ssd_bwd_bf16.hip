@@ -1029,30 +1029,28 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_dt_kernel(
   if (tid < 3) part[bhc * 3 + tid] = red[tid][0] + red[tid][1] + red[tid][2] + red[tid][3];
 }
 
-// dA, ddt_bias, dD: per head, the sums of the chunk shares over batch and chunks
-__global__ __launch_bounds__(kThreads) void ssd_bwd_dt_sum_kernel(
-    const double* __restrict__ part, float* __restrict__ dA, float* __restrict__ ddt_bias,
-    float* __restrict__ dD, int Bsz, int H, int nc) {
-  const int h = blockIdx.x * kThreads + threadIdx.x;
-  if (h >= H) return;
-  double s[3] = {0.0, 0.0, 0.0};
-  for (int b = 0; b < Bsz; ++b)
-    for (int c = 0; c < nc; ++c)
-#pragma unroll
-      for (int k = 0; k < 3; ++k) s[k] += part[(((static_cast<size_t>(b) * H + h) * nc + c) * 3) + k];
-  dA[h] = static_cast<float>(s[0]);
-  ddt_bias[h] = static_cast<float>(s[1]);
-  dD[h] = static_cast<float>(s[2]);
-}
-
-// dB and dC = sums of their nparts head-group partials, float4 at a time
-// (blockIdx.y 0: dB, 1: dC; one launch for both)
-__global__ __launch_bounds__(kThreads) void ssd_bwd_reduce_kernel(const float* __restrict__ partB,
-                                                                  float* __restrict__ outB,
-                                                                  const float* __restrict__ partC,
-                                                                  float* __restrict__ outC, size_t n4,
-                                                                  int nparts) {
+// The sums after the step-size kernel, one launch: blockIdx.y 0 and 1, dB and
+// dC as the sums of their nparts head-group partials, float4 at a time; 2, per
+// head, dA, ddt_bias and dD as the sums of the chunk shares over batch and
+// chunks (fp64)
+__global__ __launch_bounds__(kThreads) void ssd_bwd_reduce_kernel(
+    const float* __restrict__ partB, float* __restrict__ outB, const float* __restrict__ partC,
+    float* __restrict__ outC, size_t n4, int nparts, const double* __restrict__ dtp,
+    float* __restrict__ dA, float* __restrict__ ddt_bias, float* __restrict__ dD, int Bsz, int H,
+    int nc) {
   const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (blockIdx.y == 2) {
+    if (i >= static_cast<size_t>(H)) return;
+    double s[3] = {0.0, 0.0, 0.0};
+    for (int b = 0; b < Bsz; ++b)
+      for (int c = 0; c < nc; ++c)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) s[k] += dtp[(((static_cast<size_t>(b) * H + i) * nc + c) * 3) + k];
+    dA[i] = static_cast<float>(s[0]);
+    ddt_bias[i] = static_cast<float>(s[1]);
+    dD[i] = static_cast<float>(s[2]);
+    return;
+  }
   if (i >= n4) return;
   const float* part = blockIdx.y == 0 ? partB : partC;
   float* out = blockIdx.y == 0 ? outB : outC;
@@ -1192,9 +1190,7 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   launch_k(nc > 0, ssd_bwd_dc_kernel<P, N>, dim3(bblocks), dim3(kThreads), st, ev ? ev + 10 : nullptr,
            x, B, C, dy, tok, states, f1, dCp, a.Bsz, a.T, a.H, a.G, Q, nc, HPG);
   // (the chunk constants' slot: an empty pair, recorded back to back)
-  launch_k(false, ssd_bwd_reduce_kernel, dim3(1), dim3(kThreads), st, ev ? ev + 12 : nullptr,
-           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), static_cast<const float*>(nullptr),
-           static_cast<float*>(nullptr), size_t{0}, 0);
+  empty_slot(st, ev ? ev + 12 : nullptr);
   double* dtp = reinterpret_cast<double*>(ws + L.dtp);
   launch_k(nc > 0, ssd_bwd_dt_kernel, dim3(nc > 0 ? nc : 1, a.H, a.Bsz), dim3(kThreads), st,
            ev ? ev + 14 : nullptr, a.dt, a.A, a.dt_bias, a.dt_min, a.dt_max, static_cast<const float*>(f1),
@@ -1202,19 +1198,17 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
            static_cast<const float*>(xv),
            static_cast<const float*>(dyx), static_cast<const double*>(cpart), decay, nblk, a.ddt, dtp, a.Bsz,
            a.T, a.H, Q, nc);
-  launch_k(true, ssd_bwd_dt_sum_kernel, dim3((a.H + kThreads - 1) / kThreads), dim3(kThreads), st,
-           ev ? ev + 16 : nullptr, static_cast<const double*>(dtp), a.dA, a.ddt_bias, a.dD, a.Bsz, a.H,
-           nc);
+  // (the per-head sums' slot: an empty pair; they run in the launch below)
   const size_t n4 = static_cast<size_t>(a.Bsz) * a.T * a.G * N / 4;
   const int nparts = (a.H / a.G) / HPG;
-  const unsigned rblocks = static_cast<unsigned>((n4 + kThreads - 1) / kThreads);
-  // dB and dC in one launch (slot dB sum; slot dC sum: an empty pair)
-  launch_k(n4 > 0, ssd_bwd_reduce_kernel, dim3(rblocks > 0 ? rblocks : 1, 2), dim3(kThreads), st,
+  empty_slot(st, ev ? ev + 16 : nullptr);
+  // dB, dC and the per-head sums in one launch (slot 9; slot 10: an empty pair)
+  const size_t rblocks = std::max((n4 + kThreads - 1) / kThreads,
+                                  static_cast<size_t>((a.H + kThreads - 1) / kThreads));
+  launch_k(true, ssd_bwd_reduce_kernel, dim3(static_cast<unsigned>(rblocks), 3), dim3(kThreads), st,
            ev ? ev + 18 : nullptr, static_cast<const float*>(dBp), a.dB, static_cast<const float*>(dCp), a.dC,
-           n4, nparts);
-  launch_k(false, ssd_bwd_reduce_kernel, dim3(1), dim3(kThreads), st, ev ? ev + 20 : nullptr,
-           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), static_cast<const float*>(nullptr),
-           static_cast<float*>(nullptr), size_t{0}, 0);
+           n4, nparts, static_cast<const double*>(dtp), a.dA, a.ddt_bias, a.dD, a.Bsz, a.H, nc);
+  empty_slot(st, ev ? ev + 20 : nullptr);
   return hipGetLastError();
 }
 
