@@ -1066,6 +1066,14 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_reduce_kernel(
   reinterpret_cast<float4*>(out)[i] = s;
 }
 
+// An event slot with no kernel of its own: its pair recorded back to back.
+inline void empty_slot(hipStream_t st, const hipEvent_t* ev) {
+  if (ev) {
+    (void)hipEventRecord(ev[0], st);
+    (void)hipEventRecord(ev[1], st);
+  }
+}
+
 // heads per workgroup of the block kernels: the largest divisor of H/G up to
 // 4 (1024 workgroups per block kernel at the BitMamba shape; more heads per
 // workgroup share staging but leave too few workgroups to fill the CUs)

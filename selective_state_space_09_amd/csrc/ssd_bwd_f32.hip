@@ -1037,7 +1037,8 @@ hipError_t launch_f32_core(const float* x, const float* dt, const float* A_dec, 
            dt_bias, dt_min, dt_max, Bin, Cin, dy, S, dCh, f1, rw, rhoC, rot, dCo, T, H, Geff,
            nc);
   // (the chunk constants come from the adjoint passing: slot 7 records back to back)
-  empty_slot(st, E(7));
+  launch_k(false, ssd_f32_dt_sum_kernel<CPLX>, dim3(1), dim3(kThreads), st, E(7), nullptr, nullptr, nullptr,
+           nullptr, 0, 0, 0);
   launch_k(CPLX, ssd_cplx_tau_kernel, dim3(H, Bsz), dim3(kThreads), st, E(8),
            reinterpret_cast<const float*>(ws + L.dhfe), reinterpret_cast<const float*>(ws + L.hfe), rhoB,
            T, H, P, NE / 2);
@@ -1061,7 +1062,7 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
   const int nc = (a.T + kQ - 1) / kQ;
   const hipEvent_t* ev = a.events;
   auto E = [&](int k) { return ev ? ev + 2 * k : nullptr; };
-  empty_slot(st, E(0));
+  launch_k(false, ssd_cplx_dh0_kernel, dim3(1), dim3(kThreads), st, E(0), nullptr, nullptr, size_t{0}, 0);
   const F32BwdLayout L = f32_layout(a.Bsz, a.T, a.H, P, N, false);
   char* ws = static_cast<char*>(a.workspace);
   float* S = reinterpret_cast<float*>(ws + L.S);
@@ -1091,7 +1092,7 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const size_t rows = static_cast<size_t>(a.Bsz) * a.T;
   const size_t nthreads = direct ? 0 : rows * a.G * (N / 4);
-  empty_slot(st, E(13));
+  launch_k(false, ssd_cplx_dh0_kernel, dim3(1), dim3(kThreads), st, E(13), nullptr, nullptr, size_t{0}, 0);
   launch_k(nthreads > 0, ssd_f32_group_sum_kernel<false>,
            dim3(static_cast<unsigned>((nthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, E(12),
            reinterpret_cast<const float*>(ws + L.dBh), reinterpret_cast<const float*>(ws + L.dCh),

@@ -106,14 +106,6 @@ inline void launch_k(bool run, F kernel, dim3 grid, dim3 block, hipStream_t st,
     hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
 }
 
-// An event slot with no kernel of its own: its pair recorded back to back.
-inline void empty_slot(hipStream_t st, const hipEvent_t* ev) {
-  if (ev) {
-    (void)hipEventRecord(ev[0], st);
-    (void)hipEventRecord(ev[1], st);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Per-chunk prologue of the fp32 kernels: step sizes and cumulative decay
 // exponents.
