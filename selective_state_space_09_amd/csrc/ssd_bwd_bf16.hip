@@ -51,8 +51,8 @@
 //   ssd_bwd_dt          per (chunk, head, batch): the prefix / suffix sums of
 //                       col - row, f2 / f1 inside the chunk (fp64), da, ddt, the chunk's
 //                       shares of dA, ddt_bias, dD
-//   ssd_bwd_dt_sum      dA, ddt_bias, dD: the sums of the shares
-//   ssd_bwd_reduce      sums of the head-group partials of dB and dC.
+//   ssd_bwd_reduce      sums of the head-group partials of dB and dC, and
+//                       dA, ddt_bias, dD as the sums of the chunk shares.
 // Every factor e^{cs_l - cs_s} (l >= s), e^{cs_l} and e^{tot - cs_s} is at
 // most 1 (A < 0), so each is evaluated directly per element.
 
